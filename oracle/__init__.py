@@ -1,0 +1,238 @@
+"""fp64 CPU oracle for the batched SSM decode step (checkpoint + record buffer).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  It shares no code with the GPU path and never imports it.
+
+The arithmetic lives in ``replay_oracle.c`` (plain loops, double precision,
+OpenMP over independent (row, head) tiles); this module only marshals numpy
+arrays into it.  ``bytemodel.py`` holds the traffic model.  Each C function
+cites the passage of the pages it follows.
+
+Array conventions (one tile = one (row, head) pair, tiles flattened):
+    S, C       float64 [n, d_v, d_k]   state / checkpoint, row-major
+    q, k       float64 [n, d_k]
+    v, out     float64 [n, d_v]
+    lam, beta  float64 [n]             log-decay (alpha = exp(lam)), GDN beta
+    rec_lam    float64 [n, cap]        buffered log-decays
+    rec_x      float64 [n, cap, d_v]   buffered values (v, or GDN's corrected d)
+    rec_k      float64 [n, cap, d_k]   buffered keys
+    w          int32   [n]             records held per tile
+    flush      uint8   [n]             this step's flush decision
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+MAMBA2 = 0
+GDN = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "replay_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_U8P = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+
+
+def _opt(ptr_type):
+    """ndpointer that also accepts None (NULL)."""
+
+    class _Opt(ptr_type):
+        @classmethod
+        def from_param(cls, obj):
+            if obj is None:
+                return None
+            return ptr_type.from_param(obj)
+
+    return _Opt
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str = _LIB):
+        if not os.path.exists(path):
+            if path != _LIB:
+                raise FileNotFoundError(path)
+            build()
+        self.path = path
+        lib = ctypes.CDLL(path)
+        i64, i32, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        lib.oc_conventional_step.argtypes = [c_int, i64, c_int, c_int, _F64P, _F64P, _F64P, _F64P,
+                                             _F64P, _opt(_F64P), _opt(_U8P), _F64P]
+        lib.oc_conventional_step.restype = None
+        lib.oc_replay_step.argtypes = [c_int, i64, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P,
+                                       _I32P, _U8P, _F64P, _F64P, _F64P, _F64P, _opt(_F64P),
+                                       _opt(_U8P), _F64P]
+        lib.oc_replay_step.restype = i64
+        lib.oc_replay_fold.argtypes = [i64, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P, _I32P,
+                                       _opt(_U8P)]
+        lib.oc_replay_fold.restype = None
+        lib.oc_cursor_run.argtypes = [c_int, i32, i64, _opt(_U8P), _I32P, _U8P]
+        lib.oc_cursor_run.restype = None
+        lib.oc_num_threads.restype = c_int
+        lib.oc_set_num_threads.argtypes = [c_int]
+        self.lib = lib
+
+    # -- threads ---------------------------------------------------------
+    def num_threads(self) -> int:
+        return int(self.lib.oc_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oc_set_num_threads(int(n))
+
+    # -- steps -----------------------------------------------------------
+    def conventional_step(self, form, S, q, k, v, lam, beta=None, active=None):
+        n, dv, dk = S.shape
+        out = np.zeros((n, dv), np.float64)
+        _check(S, q, k, v, lam, beta, n, dv, dk)
+        self.lib.oc_conventional_step(int(form), n, dv, dk, S, q, k, v, lam, beta,
+                                      _u8(active), out)
+        return out
+
+    def replay_step(self, form, C, rec_lam, rec_x, rec_k, w, flush, q, k, v, lam, beta=None,
+                    active=None):
+        n, dv, dk = C.shape
+        cap = rec_lam.shape[1]
+        assert rec_x.shape == (n, cap, dv) and rec_k.shape == (n, cap, dk)
+        assert w.dtype == np.int32 and w.shape == (n,)
+        _check(C, q, k, v, lam, beta, n, dv, dk)
+        out = np.zeros((n, dv), np.float64)
+        ovf = self.lib.oc_replay_step(int(form), n, dv, dk, cap, C, rec_lam, rec_x, rec_k, w,
+                                      _u8(flush), q, k, v, lam, beta, _u8(active), out)
+        if ovf:
+            raise ValueError(f"{ovf} tiles would overflow the record buffer (cap={cap})")
+        return out
+
+    def replay_fold(self, C, rec_lam, rec_x, rec_k, w, mask=None):
+        n, dv, dk = C.shape
+        cap = rec_lam.shape[1]
+        self.lib.oc_replay_fold(n, dv, dk, cap, C, rec_lam, rec_x, rec_k, w, _u8(mask))
+
+    def cursor_run(self, L, w0, n_steps, forced=None):
+        w = np.zeros(n_steps, np.int32)
+        f = np.zeros(n_steps, np.uint8)
+        self.lib.oc_cursor_run(int(L), int(w0), int(n_steps), _u8(forced), w, f)
+        return w, f.astype(bool)
+
+
+def _u8(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a).astype(np.uint8))
+
+
+def _check(S, q, k, v, lam, beta, n, dv, dk):
+    for a in (S, q, k, v, lam) + ((beta,) if beta is not None else ()):
+        assert a.dtype == np.float64 and a.flags.c_contiguous
+    assert q.shape == (n, dk) and k.shape == (n, dk) and v.shape == (n, dv)
+    assert lam.shape == (n,)
+    assert beta is None or beta.shape == (n,)
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built from this directory's source (built on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+class ConventionalModel:
+    """Conventional decode for B rows x H heads, fp64 state in memory."""
+
+    def __init__(self, form, B, H, dv, dk, S0=None, oracle=None):
+        self.o = oracle or get()
+        self.form, self.B, self.H, self.dv, self.dk = form, B, H, dv, dk
+        n = B * H
+        self.S = np.zeros((n, dv, dk)) if S0 is None else np.ascontiguousarray(S0, np.float64).reshape(n, dv, dk).copy()
+
+    def step(self, q, k, v, lam, beta=None, active_rows=None):
+        """q, k: [B, H, dk]; v: [B, H, dv]; lam, beta: [B, H].  Returns o [B, H, dv]."""
+        B, H = self.B, self.H
+        act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
+        n = B * H
+        out = self.o.conventional_step(self.form, self.S, _vec(q, n), _vec(k, n), _vec(v, n),
+                                       _scal(lam, n), None if beta is None else _scal(beta, n),
+                                       act)
+        return out.reshape(B, H, self.dv)
+
+    def state(self):
+        return self.S.reshape(self.B, self.H, self.dv, self.dk)
+
+
+class ReplayModel:
+    """Checkpoint + record buffer for B rows x H heads, fp64, buffer of L - 1 slots."""
+
+    def __init__(self, form, B, H, dv, dk, L, oracle=None):
+        self.o = oracle or get()
+        self.form, self.B, self.H, self.dv, self.dk, self.L = form, B, H, dv, dk, L
+        n = B * H
+        cap = max(L - 1, 0)
+        self.cap = cap
+        self.C = np.zeros((n, dv, dk))
+        self.rec_lam = np.zeros((n, cap))
+        self.rec_x = np.zeros((n, cap, dv))
+        self.rec_k = np.zeros((n, cap, dk))
+        self.w = np.zeros(n, np.int32)
+
+    def set_row(self, b, C, rec_lam, rec_x, rec_k, w):
+        """Load one row's checkpoint [H, dv, dk] and its first w records."""
+        H = self.H
+        sl = slice(b * H, (b + 1) * H)
+        self.C[sl] = C
+        self.rec_lam[sl] = 0.0
+        self.rec_x[sl] = 0.0
+        self.rec_k[sl] = 0.0
+        if w:
+            self.rec_lam[sl, :w] = rec_lam[:, :w]
+            self.rec_x[sl, :w] = rec_x[:, :w]
+            self.rec_k[sl, :w] = rec_k[:, :w]
+        self.w[sl] = w
+
+    def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None):
+        """flush_rows: [B] bools.  Returns o [B, H, dv]."""
+        B, H = self.B, self.H
+        fl = np.repeat(np.asarray(flush_rows, bool), H)
+        act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
+        n = B * H
+        out = self.o.replay_step(self.form, self.C, self.rec_lam, self.rec_x, self.rec_k, self.w,
+                                 fl, _vec(q, n), _vec(k, n), _vec(v, n), _scal(lam, n),
+                                 None if beta is None else _scal(beta, n), act)
+        return out.reshape(B, H, self.dv)
+
+    def fold(self, rows_mask):
+        mask = np.repeat(np.asarray(rows_mask, bool), self.H)
+        self.o.replay_fold(self.C, self.rec_lam, self.rec_x, self.rec_k, self.w, mask)
+
+    def checkpoint(self):
+        return self.C.reshape(self.B, self.H, self.dv, self.dk)
+
+    def records_held(self):
+        return self.w.reshape(self.B, self.H)
+
+
+def _vec(a, n):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(n, -1))
+
+
+def _scal(a, n):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(n))

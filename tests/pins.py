@@ -1,0 +1,314 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with the fact it checks.  ``test_oracle.py`` runs
+them on the real oracle; ``test_oracle_mutants.py`` runs them on copies of the
+oracle with planted mistakes and requires every mistake to be caught.
+
+Sources of the facts (pages):
+  [blog] "ReplaySSM: an SSM decoder that writes its state once every 16
+         tokens": recurrence ("Why a fixed-size state is not cheap to
+         decode"), the unrolled identity ("The identity"), the output-only
+         bracketing ("Output without a state"), the delta-rule expansion
+         ("The delta-rule wrinkle").
+  [pr]   vLLM pull request "[Kernel] ReplaySSM: cache SSM inputs for faster
+         Gated DeltaNet standard decode": cursor and flush rule ("CUDA graphs
+         and continuous batching").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+M2, GDN = oracle.MAMBA2, oracle.GDN
+
+
+def _tok(form, seed, step, B, H, dv, dk, a_lo=1.0, a_hi=8.0):
+    t = workloads.tokens(form, seed, step, B, H, dv, dk, "f32", a_lo, a_hi)
+    f = lambda x: x.double().numpy()
+    return f(t.q), f(t.k), f(t.v), f(t.lam), (None if t.beta is None else f(t.beta))
+
+
+def _rel(a, b):
+    """max |a - b| / max |b| over the last axis, worst case over the rest."""
+    a, b = np.asarray(a), np.asarray(b)
+    num = np.abs(a - b).reshape(-1, a.shape[-1]).max(-1)
+    den = np.maximum(np.abs(b).reshape(-1, b.shape[-1]).max(-1), 1e-300)
+    return float((num / den).max())
+
+
+def run_both(orc, form, B, H, dv, dk, L, n_steps, seed=0, a_lo=1.0, a_hi=8.0, forced=None,
+             check_flush_state=True):
+    """Run the conventional and the checkpoint + buffer routes side by side.
+
+    Returns (max output relative deviation, max flushed-state deviation,
+    number of flush steps).  Both routes start from a zero state; the flush
+    schedule comes from the oracle's cursor."""
+    conv = oracle.ConventionalModel(form, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(form, B, H, dv, dk, L, oracle=orc)
+    ws, fls = orc.cursor_run(L, 0, n_steps, forced)
+    worst_o, worst_s, n_flush = 0.0, 0.0, 0
+    for s in range(n_steps):
+        q, k, v, lam, beta = _tok(form, seed, s, B, H, dv, dk, a_lo, a_hi)
+        assert np.all(rep.w == ws[s]), "replay route holds a different number of records than the cursor"
+        o_c = conv.step(q, k, v, lam, beta)
+        o_r = rep.step(q, k, v, lam, np.full(B, fls[s]), beta)
+        worst_o = max(worst_o, _rel(o_r, o_c))
+        if fls[s]:
+            n_flush += 1
+            if check_flush_state:
+                worst_s = max(worst_s, _rel(rep.checkpoint(), conv.state()))
+    return worst_o, worst_s, n_flush
+
+
+# ---------------------------------------------------------------- identity --
+def pin_identity_mamba2_tiny(orc):
+    """[blog] "The identity": both sides are the same matrix; outputs agree up
+    to floating-point order.  Tiny Mamba-2 workload: batch 2, 4 heads, 16x32,
+    L=4, 64 steps from zero (16 flushes)."""
+    o, s, nf = run_both(orc, M2, 2, 4, 16, 32, 4, 64)
+    assert nf == 16
+    assert o < 1e-12 and s < 1e-12, (o, s)
+
+
+def pin_identity_mamba2_long_memory(orc):
+    """Same identity with slowly decaying heads (a ~ U[0.001, 0.01]), where the
+    checkpoint term stays dominant and an error in it cannot hide."""
+    o, s, _ = run_both(orc, M2, 2, 4, 16, 32, 4, 64, seed=3, a_lo=0.001, a_hi=0.01)
+    assert o < 1e-12 and s < 1e-12, (o, s)
+
+
+def pin_identity_gdn_tiny(orc):
+    """[pr] reviewer comment: S_{t-1} q and S_{t-1} k rebuilt from checkpoint
+    plus buffer equal the conventional delta-rule state's."""
+    o, s, nf = run_both(orc, GDN, 2, 4, 16, 32, 4, 64, seed=1)
+    assert nf == 16
+    assert o < 1e-12 and s < 1e-12, (o, s)
+
+
+def pin_identity_long_window(orc):
+    """L=16 (the pages' default) and forced flushes at irregular steps."""
+    forced = np.zeros(80, np.uint8)
+    forced[[5, 6, 30, 51]] = 1
+    for form in (M2, GDN):
+        o, s, nf = run_both(orc, form, 1, 2, 16, 32, 16, 80, seed=7, forced=forced)
+        assert nf >= 4
+        assert o < 1e-12 and s < 1e-12, (form, o, s)
+
+
+# ---------------------------------------------------------- special cases --
+def pin_single_step_from_zero(orc):
+    """One update from a zero state: o = (v k^T) q = v (k^T q) ([blog]
+    "Output without a state").  For Gated DeltaNet the zero state makes the
+    corrected value beta v, so o = beta v (k . q)."""
+    B, H, dv, dk = 2, 3, 16, 32
+    for form in (M2, GDN):
+        q, k, v, lam, beta = _tok(form, 11, 0, B, H, dv, dk)
+        want = v * np.einsum("bhc,bhc->bh", k, q)[..., None]
+        if form == GDN:
+            want = want * beta[..., None]
+        conv = oracle.ConventionalModel(form, B, H, dv, dk, oracle=orc)
+        got_c = conv.step(q, k, v, lam, beta)
+        for fl in (False, True):
+            rep = oracle.ReplayModel(form, B, H, dv, dk, 4, oracle=orc)
+            got_r = rep.step(q, k, v, lam, np.full(B, fl), beta)
+            assert _rel(got_r, want) < 1e-13, (form, fl)
+        assert _rel(got_c, want) < 1e-13, form
+
+
+def pin_no_decay_is_plain_sum(orc):
+    """alpha = 1 (lam = 0): the state is the plain sum of outer products."""
+    B, H, dv, dk, n = 1, 2, 16, 32, 9
+    conv = oracle.ConventionalModel(M2, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(M2, B, H, dv, dk, 4, oracle=orc)
+    ws, fls = orc.cursor_run(4, 0, n)
+    acc = np.zeros((B, H, dv, dk))
+    for s in range(n):
+        q, k, v, lam, _ = _tok(M2, 5, s, B, H, dv, dk)
+        lam = np.zeros_like(lam)
+        acc += np.einsum("bhi,bhc->bhic", v, k)
+        want = np.einsum("bhic,bhc->bhi", acc, q)
+        assert _rel(conv.step(q, k, v, lam), want) < 1e-12
+        assert _rel(rep.step(q, k, v, lam, np.full(B, fls[s])), want) < 1e-12
+        assert _rel(conv.state(), acc) < 1e-12
+
+
+def pin_constant_decay_geometric(orc):
+    """Constant alpha: S_t = sum_{j<=t} alpha^{t-j} v_j k_j^T (the unrolled
+    recurrence with gamma_{j+1:t} = alpha^{t-j})."""
+    B, H, dv, dk, n, L = 1, 2, 16, 32, 11, 4
+    alpha = 0.8
+    conv = oracle.ConventionalModel(M2, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+    ws, fls = orc.cursor_run(L, 0, n)
+    vs, ks = [], []
+    for s in range(n):
+        q, k, v, lam, _ = _tok(M2, 6, s, B, H, dv, dk)
+        lam = np.full_like(lam, np.log(alpha))
+        vs.append(v)
+        ks.append(k)
+        S = sum(alpha ** (s - j) * np.einsum("bhi,bhc->bhic", vs[j], ks[j]) for j in range(s + 1))
+        want = np.einsum("bhic,bhc->bhi", S, q)
+        assert _rel(conv.step(q, k, v, lam), want) < 1e-12, s
+        assert _rel(rep.step(q, k, v, lam, np.full(B, fls[s])), want) < 1e-12, s
+
+
+def pin_full_forgetting(orc):
+    """alpha = 0 (lam = -inf): S_t = v_t k_t^T and the checkpoint and buffer
+    contribute nothing."""
+    B, H, dv, dk = 1, 2, 16, 32
+    conv = oracle.ConventionalModel(M2, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(M2, B, H, dv, dk, 4, oracle=orc)
+    ws, fls = orc.cursor_run(4, 0, 7)
+    for s in range(7):
+        q, k, v, lam, _ = _tok(M2, 8, s, B, H, dv, dk)
+        if s in (2, 5):
+            lam = np.full_like(lam, -np.inf)
+            want = v * np.einsum("bhc,bhc->bh", k, q)[..., None]
+        o_c = conv.step(q, k, v, lam)
+        o_r = rep.step(q, k, v, lam, np.full(B, fls[s]))
+        assert _rel(o_r, o_c) < 1e-12
+        if s in (2, 5):
+            assert _rel(o_c, want) < 1e-13 and _rel(o_r, want) < 1e-13
+
+
+def pin_gdn_product_form(orc):
+    """[blog] "The delta-rule wrinkle": the conventional Gated DeltaNet update
+    equals the product form S_t = alpha S_{t-1} (I - beta k k^T) + beta v k^T,
+    evaluated here with plain matrix products."""
+    B, H, dv, dk = 2, 2, 16, 32
+    conv = oracle.ConventionalModel(GDN, B, H, dv, dk, oracle=orc)
+    S = np.zeros((B, H, dv, dk))
+    I = np.eye(dk)
+    for s in range(6):
+        q, k, v, lam, beta = _tok(GDN, 9, s, B, H, dv, dk)
+        k = k * 1.3  # off the unit sphere so that the k k^T term is not special
+        o = conv.step(q, k, v, lam, beta)
+        for b in range(B):
+            for h in range(H):
+                a, bt = np.exp(lam[b, h]), beta[b, h]
+                P = I - bt * np.outer(k[b, h], k[b, h])
+                S[b, h] = a * S[b, h] @ P + bt * np.outer(v[b, h], k[b, h])
+        assert _rel(conv.state(), S) < 1e-12, s
+        assert _rel(o, np.einsum("bhic,bhc->bhi", S, q)) < 1e-12, s
+
+
+def pin_gdn_unit_key_stores_value(orc):
+    """Gated DeltaNet with beta = 1 and |k| = 1: the update overwrites the
+    state's response to k with v, S_t k_t = v_t, for any alpha and prior state
+    (expand alpha S (I - k k^T) k + v k^T k)."""
+    B, H, dv, dk, L = 2, 2, 16, 32, 4
+    conv = oracle.ConventionalModel(GDN, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(GDN, B, H, dv, dk, L, oracle=orc)
+    ws, fls = orc.cursor_run(L, 0, 9)
+    for s in range(9):
+        q, k, v, lam, beta = _tok(GDN, 10, s, B, H, dv, dk)
+        k = k / np.linalg.norm(k, axis=-1, keepdims=True)  # exactly unit in fp64
+        beta = np.ones_like(beta)
+        conv.step(q, k, v, lam, beta)
+        rep.step(q, k, v, lam, np.full(B, fls[s]), beta)
+        Sk = np.einsum("bhic,bhc->bhi", conv.state(), k)
+        assert _rel(Sk, v) < 1e-12, s
+        if fls[s]:
+            assert _rel(np.einsum("bhic,bhc->bhi", rep.checkpoint(), k), v) < 1e-12, s
+
+
+def pin_gdn_zero_beta_only_decays(orc):
+    """Gated DeltaNet with beta = 0 writes nothing: S_t = alpha S_{t-1}, and the
+    buffered corrected values are zero."""
+    B, H, dv, dk, L = 1, 2, 16, 32, 4
+    conv = oracle.ConventionalModel(GDN, B, H, dv, dk, oracle=orc)
+    rep = oracle.ReplayModel(GDN, B, H, dv, dk, L, oracle=orc)
+    ws, fls = orc.cursor_run(L, 0, 12)
+    for s in range(12):
+        q, k, v, lam, beta = _tok(GDN, 12, s, B, H, dv, dk)
+        if s >= 5:
+            beta = np.zeros_like(beta)
+        before = conv.state().copy()
+        o_c = conv.step(q, k, v, lam, beta)
+        o_r = rep.step(q, k, v, lam, np.full(B, fls[s]), beta)
+        if s >= 5:
+            want = np.exp(lam)[..., None, None] * before
+            assert _rel(conv.state(), want) < 1e-13, s
+            assert _rel(o_c, np.einsum("bhic,bhc->bhi", want, q)) < 1e-12
+        assert _rel(o_r, o_c) < 1e-12, s
+        if s == 10:  # steps 8, 9, 10 are buffered, all with beta = 0
+            assert np.all(rep.w == 3)
+            assert np.all(rep.rec_x[:, :3] == 0.0)
+
+
+# ------------------------------------------------------------------- fold --
+def pin_fold_materialises_state(orc):
+    """A token-less fold of w records gives the conventional state after
+    those w tokens ([blog] "The identity" with h = w); folding nothing leaves
+    the checkpoint unchanged; decoding continues identically afterwards."""
+    B, H, dv, dk, L = 2, 2, 16, 32, 8
+    for form in (M2, GDN):
+        conv = oracle.ConventionalModel(form, B, H, dv, dk, oracle=orc)
+        rep = oracle.ReplayModel(form, B, H, dv, dk, L, oracle=orc)
+        for s in range(13):
+            q, k, v, lam, beta = _tok(form, 13, s, B, H, dv, dk)
+            conv.step(q, k, v, lam, beta)
+            rep.step(q, k, v, lam, rep.records_held()[:, 0] == L - 1, beta)
+            if s in (4, 9):
+                rep.fold(np.array([True, s == 9]))
+                sel = [0] if s == 4 else [0, 1]
+                assert _rel(rep.checkpoint()[sel], conv.state()[sel]) < 1e-12, (form, s)
+                assert np.all(rep.records_held()[sel] == 0)
+        rep.fold(np.array([True, True]))
+        assert _rel(rep.checkpoint(), conv.state()) < 1e-12
+        after = rep.checkpoint().copy()
+        rep.fold(np.array([True, True]))  # no records left: unchanged
+        assert np.array_equal(rep.checkpoint(), after)
+        for s in range(13, 20):  # decoding continues from the folded state
+            q, k, v, lam, beta = _tok(form, 13, s, B, H, dv, dk)
+            o_c = conv.step(q, k, v, lam, beta)
+            o_r = rep.step(q, k, v, lam, rep.records_held()[:, 0] == L - 1, beta)
+            assert _rel(o_r, o_c) < 1e-12, (form, s)
+
+
+# ----------------------------------------------------------------- cursor --
+def pin_cursor_closed_form(orc):
+    """[pr] "CUDA graphs and continuous batching": without forcing, the write
+    position after n steps from w0 is (w0 + n) mod L, a row flushes when it
+    reaches L - 1, and n steps hold floor((w0 + n) / L) flushes."""
+    for L in (1, 2, 4, 16, 33, 64):
+        for w0 in sorted({0, min(1, L - 1), L // 2, L - 1}):
+            n = 5 * L + 3
+            w, f = orc.cursor_run(L, w0, n)
+            assert np.array_equal(w, (w0 + np.arange(n)) % L), (L, w0)
+            assert np.array_equal(f, w == L - 1)
+            assert int(f.sum()) == (w0 + n) // L
+    w, f = orc.cursor_run(4, 0, 64)
+    assert list(np.nonzero(f)[0]) == list(range(3, 64, 4))
+
+
+def pin_cursor_forced_flush(orc):
+    """A forced flush (prefix-cache align mode, [pr] "What this PR adds")
+    empties the buffer at once: the next step writes position 0."""
+    forced = np.zeros(20, np.uint8)
+    forced[[2, 3, 11]] = 1
+    w, f = orc.cursor_run(16, 0, 20, forced)
+    assert list(w[:6]) == [0, 1, 2, 0, 0, 1]
+    assert list(np.nonzero(f)[0]) == [2, 3, 11]
+    assert w[12] == 0 and w[19] == 7
+
+
+ALL_PINS = [
+    pin_identity_mamba2_tiny,
+    pin_identity_mamba2_long_memory,
+    pin_identity_gdn_tiny,
+    pin_identity_long_window,
+    pin_single_step_from_zero,
+    pin_no_decay_is_plain_sum,
+    pin_constant_decay_geometric,
+    pin_full_forgetting,
+    pin_gdn_product_form,
+    pin_gdn_unit_key_stores_value,
+    pin_gdn_zero_beta_only_decays,
+    pin_fold_materialises_state,
+    pin_cursor_closed_form,
+    pin_cursor_forced_flush,
+]

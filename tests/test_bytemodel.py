@@ -1,0 +1,69 @@
+"""The traffic model against the figures the pages print (tests/golden/byte_model_facts.txt)."""
+import os
+
+import pytest
+
+from oracle import bytemodel as bm
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "byte_model_facts.txt")
+
+
+def _facts():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, args, value, tol, cite = [x.strip() for x in line.split("|")]
+        rows.append((name, [float(a) if "." in a else int(a) for a in args.split()], float(value),
+                     float(tol), cite))
+    return rows
+
+
+def _eval(name, a):
+    if name == "layer_state_bytes":
+        return bm.layer_state_bytes(*a)
+    if name == "stack_state_bytes":
+        return a[0] * bm.layer_state_bytes(*a[1:])
+    if name == "batch_state_bytes":
+        return a[0] * a[1] * bm.layer_state_bytes(*a[2:])
+    if name == "state_term_ratio":
+        return bm.state_term_ratio(*a)
+    if name == "traffic_ratio":
+        return bm.traffic_ratio(*a)
+    if name == "state_over_record":
+        return bm.state_bytes(*a) / bm.record_bytes(a[0], a[1])
+    if name == "optimal_window":
+        dv, dk, eb, T, abar = a
+        return bm.optimal_window(bm.state_bytes(dv, dk, eb) / bm.record_bytes(dv, dk), T, abar)
+    if name == "output_only_shrink":
+        return bm.output_only_shrink(*a)
+    if name == "grouped_record_bytes":
+        return bm.grouped_record_bytes(*a)
+    if name in ("grouped_mib_per_token", "grouped_ratio"):
+        L, H, dv, dk, G, eb = a
+        m = bm.layer_state_bytes(H, dv, dk, eb)
+        per_token = bm.replay_window_bytes(L, m, bm.grouped_record_bytes(H, dv, dk, G)) / L
+        if name == "grouped_mib_per_token":
+            return per_token / 2**20
+        return per_token / (bm.conventional_window_bytes(L, m) / L)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("fact", _facts(), ids=lambda f: f[0])
+def test_printed_fact(fact):
+    name, args, value, tol, cite = fact
+    got = _eval(name, args)
+    assert abs(got - value) <= tol, f"{name}{tuple(args)} = {got}, pages print {value} ({cite})"
+
+
+def test_window_totals_by_counting():
+    """Count one window step by step (step i reads the i-1 records before it,
+    non-flush steps write one record, every step reads the state, the last
+    writes it) and compare with the closed form."""
+    for L in (1, 2, 4, 8, 16, 32):
+        m, r = 1000, 7
+        reads = sum(m + (i - 1) * r for i in range(1, L + 1))
+        writes = (L - 1) * r + m
+        assert reads + writes == bm.replay_window_bytes(L, m, r)
+        assert bm.conventional_window_bytes(L, m) == 2 * L * m

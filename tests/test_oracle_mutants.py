@@ -1,0 +1,92 @@
+"""Every plausible mistake planted in the oracle must fail at least one pin.
+
+Each case copies oracle/replay_oracle.c, applies one textual change (a dropped
+term, a wrong sign, an off-by-one index, a swapped operand), compiles the copy
+on the CPU with gcc into a temporary directory and runs all pins against it.
+The real oracle source is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "replay_oracle.c")
+
+MUTANTS = [
+    ("conv_drop_decay",
+     "St[(int64_t)i * dk + c] = alpha * St[(int64_t)i * dk + c] + d[i] * kt[c];",
+     "St[(int64_t)i * dk + c] = St[(int64_t)i * dk + c] + d[i] * kt[c];"),
+    ("conv_gdn_sign",
+     "d[i] = beta[t] * (vt[i] - alpha * a[i]);",
+     "d[i] = beta[t] * (vt[i] + alpha * a[i]);"),
+    ("conv_gdn_drop_alpha_in_correction",
+     "d[i] = beta[t] * (vt[i] - alpha * a[i]);",
+     "d[i] = beta[t] * (vt[i] - a[i]);"),
+    ("conv_gdn_drop_beta",
+     "d[i] = beta[t] * (vt[i] - alpha * a[i]);",
+     "d[i] = (vt[i] - alpha * a[i]);"),
+    ("matvec_wrong_stride",
+     "for (int i = 0; i < dv; ++i) y[i] = dot(S + (int64_t)i * dk, x, dk);",
+     "for (int i = 0; i < dv; ++i) y[i] = dot(S + (int64_t)i, x, dk);"),
+    ("replay_gamma_off_by_one",
+     "o += gamma_range(alpha1, j + 1, h) * xt[(int64_t)(j - 1) * dv + i] * dotq[j];",
+     "o += gamma_range(alpha1, j, h) * xt[(int64_t)(j - 1) * dv + i] * dotq[j];"),
+    ("replay_checkpoint_gamma_short",
+     "const double gh = gamma_range(alpha1, 1, h);",
+     "const double gh = gamma_range(alpha1, 1, h - 1);"),
+    ("replay_drop_current_token",
+     "o += vt[i] * kq; /* j = h: gamma_{h+1:h} = 1 */",
+     "/* dropped */"),
+    ("replay_ckpt_gemv_with_k",
+     "matvec(Ct, qt, dv, dk, cq);",
+     "matvec(Ct, kt, dv, dk, cq);"),
+    ("replay_flush_drop_current",
+     "s += vt[i] * kt[c];",
+     "/* dropped */"),
+    ("replay_flush_gamma_off_by_one",
+     "s += gamma_range(alpha1, j + 1, h) * xt[(int64_t)(j - 1) * dv + i] *",
+     "s += gamma_range(alpha1, j + 2, h) * xt[(int64_t)(j - 1) * dv + i] *"),
+    ("replay_gdn_key_dots_swapped",
+     "sk += r * dotk[j] * dj;",
+     "sk += r * dotq[j] * dj;"),
+    ("replay_gdn_drop_alpha_out",
+     "ot[i] = alpha * sq + d[i] * kq;",
+     "ot[i] = sq + d[i] * kq;"),
+    ("replay_gdn_flush_drop_alpha",
+     "Ct[(int64_t)i * dk + c] = alpha * s + d[i] * kt[c];",
+     "Ct[(int64_t)i * dk + c] = s + d[i] * kt[c];"),
+    ("replay_gdn_T_includes_current",
+     "const double T = gamma_range(alpha1, 1, wt);",
+     "const double T = gamma_range(alpha1, 1, wt) * alpha;"),
+    ("replay_append_wrong_slot",
+     "lamt[wt] = lam[t];\n                    memcpy(xt + (int64_t)wt * dv, vt,",
+     "lamt[wt] = lam[t];\n                    memcpy(xt + (int64_t)(wt > 0 ? wt - 1 : 0) * dv, vt,"),
+    ("fold_gamma_short",
+     "const double gw = gamma_range(alpha1, 1, wt);",
+     "const double gw = gamma_range(alpha1, 2, wt);"),
+    ("cursor_flush_late",
+     "const int f = (w == L - 1) || (forced && forced[s]);",
+     "const int f = (w == L) || (forced && forced[s]);"),
+    ("cursor_force_ignored",
+     "const int f = (w == L - 1) || (forced && forced[s]);",
+     "const int f = (w == L - 1);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut_src = tmp_path / "mutant.c"
+    mut_src.write_text(src.replace(old, new))
+    lib = oracle.build(str(mut_src), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
