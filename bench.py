@@ -1,0 +1,287 @@
+"""Benchmark: checkpoint + buffer decode step vs conventional decode step.
+
+    python bench.py [--steps K] [--warmup W] [--workload nemotron|gdn] [--batch B]
+                    [--L L] [--state f32|f16] [--pools P] [--no-cpu-baseline]
+
+Default workload: one Mamba-2 layer at the Nemotron-3-Super shape (128 heads,
+d_v=64, d_k=128, fp32 state, 4 MiB per sequence), batch 256, L=16, bf16
+v/k/q, fp16 records, fp32 log-decay.  A step is one pass of the whole hot
+path over the batch: host cursor/flush metadata, its async upload, and one
+kernel launch that serves flush and non-flush rows.  K defaults to 64 (four
+windows of 16 tokens) after W=16 warm-up steps.
+
+Inputs are seeded synthetic tensors (16 distinct token batches, cycled),
+resident in HBM before the timed region.  P independent state pools (default
+4, like P layers of a model) are used in rotation so that consecutive steps
+never find their state in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is the decode steps/s of the checkpoint +
+buffer path (wall clock over K steps); the conventional kernel is timed the
+same way under "conventional".  "roofline" describes the dominant kernel
+(the checkpoint + buffer step): algorithmic bytes per launch / mean launch
+time from HIP events on the launch stream, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode steps/s + achieved HBM TB/s (% peak), replay vs conventional at bs=256"
+
+WORKLOADS = {
+    "nemotron": dict(form=0, H=128, dv=64, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16"),
+    "gdn": dict(form=1, H=32, dv=128, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16"),
+}
+
+_ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+# ----------------------------------------------------------- byte accounting --
+def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay"):
+    """Algorithmic HBM bytes of one launch over B rows at cursor w.
+
+    Checkpoint + buffer step, per (row, head): read the checkpoint (d_v d_k
+    state elements) and the w buffered records (x: d_v, k: d_k record
+    elements, one fp32 log-decay each); a non-flush row writes one record, a
+    flush row writes the checkpoint back.  Conventional step: read and write
+    the state.  Both: read q, k (d_k), v (d_v) in the io dtype, the fp32
+    log-decay (and beta for Gated DeltaNet), write the fp32 output (d_v); per
+    row, read the block id (4 bytes) plus, for the checkpoint + buffer
+    step, the cursor and flag (5 bytes)."""
+    ms = dv * dk * _ES[state]
+    r = dv * _ES[rec] + dk * _ES[rec] + 4
+    io_b = (2 * dk + dv) * _ES[io] + 4 + (4 if form == 1 else 0) + 4 * dv
+    if kind == "conventional":
+        return B * (H * (2 * ms + io_b) + 4)
+    per_head = ms + w * r + (ms if flush else r) + io_b
+    return B * (H * per_head + 9)
+
+
+def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay"):
+    return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind) for w in range(L))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("rs_kernels.hip", "rs_api.cpp", "rs_internal.h"):
+        h.update(open(os.path.join(ROOT, "linear_attention_decode_replay_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_key: str):
+    """HBM traffic per launch measured with rocprofv3 counters, if a summary
+    for the current kernel source exists under profiles/."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload_key)
+    if not entry or entry.get("kernel_source") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------- CPU baseline --
+def cpu_baseline(cfg, n_steps=16, rows=None):
+    """The fp64 oracle (both routes) on the host cores, one window of steps
+    over a bounded sample of rows; reported as steps/s of the full batch."""
+    import oracle
+    import workloads
+    o = oracle.get()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    o.set_num_threads(threads)
+    B = rows or cfg["B"]
+    toks = [workloads.tokens(cfg["form"], 7, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
+            for s in range(n_steps)]
+    f64 = [(t.q.double().numpy(), t.k.double().numpy(), t.v.double().numpy(), t.lam.double().numpy(),
+            None if t.beta is None else t.beta.double().numpy()) for t in toks]
+    w, fl = o.cursor_run(cfg["L"], 0, n_steps)
+    rep = oracle.ReplayModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"])
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        q, k, v, lam, beta = f64[s]
+        rep.step(q, k, v, lam, np.full(B, fl[s]), beta)
+    t_rep = time.perf_counter() - t0
+    del rep
+    conv = oracle.ConventionalModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"])
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        q, k, v, lam, beta = f64[s]
+        conv.step(q, k, v, lam, beta)
+    t_conv = time.perf_counter() - t0
+    scale = B / cfg["B"]
+    return {
+        "value": round(n_steps * scale / t_rep, 4),
+        "unit": "steps/s",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle, checkpoint+buffer route, {n_steps} steps (one window) over "
+                   f"{B} of {cfg['B']} rows x {cfg['H']} heads; conventional route "
+                   f"{round(n_steps * scale / t_conv, 4)} steps/s; {t_rep + t_conv:.1f} s of CPU time"),
+    }
+
+
+# ------------------------------------------------------------------------ GPU --
+def run_gpu(cfg, steps, warmup, n_pools, kind):
+    import torch
+    import linear_attention_decode_replay_amd as rs
+    import workloads
+    from linear_attention_decode_replay_amd.state import DecodeLayer
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"])
+    B = cfg["B"]
+    layers = []
+    for p in range(n_pools):
+        d = DecodeLayer(lay, B, B, dev)
+        for b in range(B):
+            d.assign(b, b)
+        d.reset_rows(range(B))
+        layers.append(d)
+    n_inputs = 16
+    ios, keep = [], []
+    for s in range(n_inputs):
+        t = workloads.tokens(cfg["form"], 11, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
+        q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
+        beta = t.beta.to(dev) if t.beta is not None else None
+        out = torch.empty((B, cfg["H"], cfg["dv"]), dtype=torch.float32, device=dev)
+        keep.append((q, k, v, lam, beta, out))
+        ios.append(rs.make_io(q, k, v, lam, out, beta))
+    torch.cuda.synchronize()
+
+    def one(s, events=None):
+        d = layers[s % n_pools]
+        io = ios[s % n_inputs]
+        if kind == "replay":
+            wp, fl = d.step(io, events=events)
+            return int(wp[0]), bool(fl[0])
+        d.conventional_step(io, events=events)
+        return None, None
+
+    for s in range(warmup):
+        one(s)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    cursors = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        cursors.append(one(warmup + i, ev[i]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times_ms = [a.elapsed_time(b) for a, b in ev]
+    errs = sum(int(d.err.item()) for d in layers)
+    if errs:
+        raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
+    nbytes = [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"],
+                         w or 0, bool(f), kind) for (w, f) in cursors]
+    by_pos = {}
+    if kind == "replay":
+        for (w, f), t in zip(cursors, times_ms):
+            key = "flush" if f else f"w{w}"
+            by_pos.setdefault(key, []).append(t)
+    return {
+        "wall_s": wall,
+        "steps_per_s": steps / wall,
+        "ms_per_step": 1e3 * wall / steps,
+        "kernel_ms_mean": float(np.mean(times_ms)),
+        "bytes_per_launch_mean": float(np.mean(nbytes)),
+        "achieved_gbs": float(np.sum(nbytes) / (np.sum(times_ms) * 1e-3) / 1e9),
+        "by_position_us": {k: round(1e3 * float(np.mean(v)), 1) for k, v in sorted(by_pos.items())},
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="nemotron", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--L", type=int, default=None)
+    ap.add_argument("--state", default=None, choices=["f32", "f16"])
+    ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decode step exchanges no data between GPUs, so each "
+              f"GPU runs its own rows or heads independently (--gpus {args.gpus} is not supported).",
+              file=sys.stderr)
+        return 2
+    cfg = dict(WORKLOADS[args.workload])
+    if args.batch:
+        cfg["B"] = args.batch
+    if args.L:
+        cfg["L"] = args.L
+    if args.state:
+        cfg["state"] = args.state
+
+    rep = run_gpu(cfg, args.steps, args.warmup, args.pools, "replay")
+    conv = run_gpu(cfg, args.steps, args.warmup, args.pools, "conventional")
+
+    wb_r = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"])
+    wb_c = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"], "conventional")
+    form_name = "mamba2" if cfg["form"] == 0 else "gdn"
+    workload = (f"{form_name} layer, {cfg['H']} heads, d_v={cfg['dv']}, d_k={cfg['dk']}, {cfg['state']} state, "
+                f"{cfg['rec']} records, {cfg['io']} q/k/v, batch {cfg['B']}, L={cfg['L']}")
+    key = f"{args.workload}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    traffic = load_traffic(key)
+    achieved = rep["achieved_gbs"]
+    line = {
+        "metric": METRIC,
+        "value": round(rep["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rep["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "global_batch": cfg["B"], "seq_len": None, "heads": cfg["H"],
+                   "d_v": cfg["dv"], "d_k": cfg["dk"], "L": cfg["L"], "state_dtype": cfg["state"],
+                   "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": args.pools,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_replay_step", "bytes_per_launch": round(rep["bytes_per_launch_mean"]),
+                     "launch_us": round(1e3 * rep["kernel_ms_mean"], 2)},
+        "replay": {"steps_per_s": round(rep["steps_per_s"], 2), "kernel_us": round(1e3 * rep["kernel_ms_mean"], 2),
+                   "kernel_steps_per_s": round(1e3 / rep["kernel_ms_mean"], 2),
+                   "achieved_tbs": round(achieved / 1e3, 3), "pct_peak": round(100 * achieved / HBM_PEAK_GBS, 1),
+                   "us_by_cursor": rep["by_position_us"]},
+        "conventional": {"steps_per_s": round(conv["steps_per_s"], 2), "kernel_us": round(1e3 * conv["kernel_ms_mean"], 2),
+                         "kernel_steps_per_s": round(1e3 / conv["kernel_ms_mean"], 2),
+                         "achieved_tbs": round(conv["achieved_gbs"] / 1e3, 3),
+                         "pct_peak": round(100 * conv["achieved_gbs"] / HBM_PEAK_GBS, 1)},
+        "speedup_replay_vs_conventional": round(conv["kernel_ms_mean"] / rep["kernel_ms_mean"], 3),
+        "speedup_wall": round(rep["steps_per_s"] / conv["steps_per_s"], 3),
+        "algorithmic_bytes_ratio": round(wb_r / wb_c, 4),
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, rows=args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

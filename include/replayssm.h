@@ -1,0 +1,239 @@
+/*
+ * replayssm.h -- C ABI of the batched SSM decode step served from a checkpoint
+ * state plus a buffer of the last per-token records, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (blog "ReplaySSM: an SSM decoder that writes its state once
+ * every 16 tokens", sections "The identity" and "Output without a state"):
+ * per head, the recurrent state S_t (d_v x d_k) of
+ *     S_t = alpha_t S_{t-1} + x_t k_t^T,   o_t = S_t q_t
+ * is kept as a checkpoint C plus the records (lam_j = log alpha_j, x_j, k_j)
+ * of the tokens seen since C was written.  With w records buffered,
+ *     S_t = gamma C + sum_j gamma_j x_j k_j^T + x_t k_t^T,
+ * gamma and gamma_j being products of the alphas after the checkpoint and
+ * after record j.  For Mamba-2 x_t = v_t.  For Gated DeltaNet (blog section
+ * "The delta-rule wrinkle") x_t is the corrected value
+ *     d_t = beta_t (v_t - alpha_t S_{t-1} k_t),
+ * where S_{t-1} k_t and S_{t-1} q_t are both rebuilt from the checkpoint and
+ * the records (vLLM pull request "[Kernel] ReplaySSM: cache SSM inputs for
+ * faster Gated DeltaNet standard decode", reviewer comment on the
+ * output-only route).
+ *
+ * A non-flush step reads C, computes o_t and appends one record.  A flush
+ * step (every L-th token of a row, or when forced) folds the records and the
+ * current token into C, writes C once and empties the buffer.
+ *
+ * Conventions for every function below:
+ *   - Memory: the caller owns all host and device memory, including the
+ *     block pool.  The library allocates nothing and keeps no mutable global
+ *     state; it may be called from several host threads.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL means
+ *     the default stream) and never synchronise the host.  All device
+ *     pointers must stay valid until the work on `stream` has completed.
+ *   - Errors: each function returns an rs_status.  Arguments are validated on
+ *     the host before anything is launched; on error nothing is launched and
+ *     rs_last_error() describes the problem.  Per-row metadata lives on the
+ *     device, so its checks happen in the kernels: a tile whose block id or
+ *     cursor is out of range is skipped (no reads, no writes) and counted in
+ *     rs_batch.err_count when that pointer is non-NULL.
+ *   - Pointer alignment: pool 256 bytes; q, k, v, out, log_decay, beta
+ *     16 bytes; q/k/v strides must keep every (row, head) vector 16-byte
+ *     aligned.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RS_OK = 0,
+    RS_EINVAL = -1,        /* bad argument: NULL/misaligned pointer, bad size or stride */
+    RS_EUNSUPPORTED = -2,  /* valid request with no compiled kernel (shape or dtype)  */
+    RS_EHIP = -3           /* the HIP runtime reported an error at launch             */
+} rs_status;
+
+typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2 } rs_dtype;
+
+typedef enum {
+    RS_MAMBA2 = 0,  /* S_t = alpha S_{t-1} + v k^T                       */
+    RS_GDN = 1      /* Gated DeltaNet: S_t = alpha S_{t-1} + d k^T, d as above */
+} rs_form;
+
+/*
+ * One SSM layer.  Supported (d_v, d_k): (16, 32), (64, 128), (128, 128).
+ * L: buffer length in tokens, 1..64 (the pages' default is 16); a row holds
+ *    at most L - 1 records, and its L-th token is a flush.
+ * state_dtype:  RS_F32 or RS_F16 (checkpoint / conventional state).
+ * record_dtype: RS_F32 or RS_F16 (buffered x and k; the log-decay is fp32).
+ * io_dtype:     RS_F32, RS_F16 or RS_BF16 (q, k, v inputs).
+ */
+typedef struct {
+    int32_t form;
+    int32_t n_heads;
+    int32_t d_v;
+    int32_t d_k;
+    int32_t L;
+    int32_t state_dtype;
+    int32_t record_dtype;
+    int32_t io_dtype;
+} rs_layer;
+
+/*
+ * Byte layout of one paged block = the whole per-request state of one layer
+ * (vLLM pull request above, "Paged cache layout": checkpoint and record
+ * buffers live in the request's paged block behind its block table).
+ * Offsets are from the block start; every region starts 256-byte aligned.
+ *   ckpt     [n_heads][d_v][d_k]    state_dtype, row-major per head
+ *   rec_x    [n_heads][slots][d_v]  record_dtype
+ *   rec_k    [n_heads][slots][d_k]  record_dtype
+ *   rec_lam  [n_heads][slots]       fp32 log-decay
+ * slots = L - 1.  block_bytes is a multiple of 256.
+ */
+typedef struct {
+    int64_t ckpt_off;
+    int64_t rec_x_off;
+    int64_t rec_k_off;
+    int64_t rec_lam_off;
+    int64_t block_bytes;
+    int32_t slots;
+    int32_t reserved;
+} rs_block_layout;
+
+/* Host, pure.  Fills *out for `layer`.  RS_EINVAL / RS_EUNSUPPORTED on a bad
+ * or uncompiled layer (the same checks as the device calls). */
+int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
+
+/*
+ * One decode batch.  All arrays are device memory with n_rows entries.
+ *   pool        n_blocks * block_bytes bytes (rs_block_layout_get).
+ *   block_table row -> block id in [0, n_blocks); -1 marks a padding row,
+ *               which is neither read nor written (its outputs are left as
+ *               they were).
+ *   write_pos   records held by the row, 0..L-1 (the write cursor of the
+ *               vLLM pull request, "CUDA graphs and continuous batching").
+ *   flush       nonzero: this step folds the row into its checkpoint.  A row
+ *               at write_pos == L-1 flushes whatever its flag says.  May be
+ *               NULL (no forced flushes).
+ *   err_count   optional (may be NULL): incremented once per (row, head) tile
+ *               skipped because its block id or cursor was out of range.
+ */
+typedef struct {
+    int32_t n_rows;
+    int32_t reserved;
+    int64_t n_blocks;
+    void* pool;
+    const int32_t* block_table;
+    const int32_t* write_pos;
+    const uint8_t* flush;
+    int32_t* err_count;
+} rs_batch;
+
+/*
+ * One token per row.  q, k: [n_rows][n_heads][d_k]; v: [n_rows][n_heads][d_v],
+ * all io_dtype, unit stride along the last dimension, row and head strides in
+ * ELEMENTS (so strided views into a wider projection output work).
+ * log_decay: [n_rows][n_heads] fp32, lam = log alpha <= 0 (Mamba-2) or the
+ * gate g (Gated DeltaNet); -inf is allowed and means alpha = 0.
+ * beta: [n_rows][n_heads] fp32, Gated DeltaNet only (NULL for Mamba-2).
+ * out:  [n_rows][n_heads][d_v] fp32, contiguous; written for non-padding rows.
+ */
+typedef struct {
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t q_row_stride, q_head_stride;
+    int64_t k_row_stride, k_head_stride;
+    int64_t v_row_stride, v_head_stride;
+    const float* log_decay;
+    const float* beta;
+    float* out;
+} rs_step_io;
+
+/*
+ * Checkpoint + buffer decode step (blog, "The identity" and "Output without a
+ * state"; vLLM pull request, "Core concept").  One launch serves every row:
+ *   non-flush row: out = S_t q_t rebuilt from the checkpoint and the w
+ *                  buffered records; record w <- (lam, x, k) cast to
+ *                  record_dtype (round to nearest even); checkpoint untouched.
+ *   flush row:     out as above; checkpoint <- S_t (the records and the
+ *                  current token folded in), stored once in state_dtype
+ *                  (round to nearest even); no record is written.  The caller
+ *                  then sets the row's write_pos to 0.
+ * Buffer slots >= write_pos are never read.
+ */
+int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
+                       hipStream_t stream);
+
+/*
+ * Token-less flush: for every non-padding row whose flush flag is set, fold
+ * its write_pos records into its checkpoint (S = gamma C + sum_j gamma_j x_j
+ * k_j^T, blog "The identity" with h = write_pos).  Rows whose flag is clear
+ * are untouched.  This materialises the exact state at any step: before a row
+ * is retired or preempted, or at a prefix-cache block boundary (vLLM pull
+ * request, "What this PR adds", align mode).  batch->flush must not be NULL.
+ */
+int replay_flush(const rs_layer* layer, const rs_batch* batch, hipStream_t stream);
+
+/*
+ * Conventional decode step (blog, "Why a fixed-size state is not cheap to
+ * decode"; "The delta-rule wrinkle" for Gated DeltaNet): the checkpoint
+ * region of each block holds the full state S, which is read, updated and
+ * written back on every step; out = S_t q_t.  write_pos and flush are
+ * ignored (may be NULL); record_dtype is unused.
+ */
+int conventional_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
+                             hipStream_t stream);
+
+/*
+ * Zero the checkpoint of every non-padding row whose mask entry (device
+ * uint8 [n_rows]) is nonzero: the state of a request that joins the batch.
+ * Its write_pos must start at 0; stale records need no clearing because
+ * slots at or beyond write_pos are never read (vLLM pull request, "CUDA
+ * graphs and continuous batching").  Implemented as a kernel, not a memset,
+ * so it may be captured in a HIP graph.
+ */
+int replay_state_reset(const rs_layer* layer, const rs_batch* batch, const uint8_t* mask,
+                       hipStream_t stream);
+
+/*
+ * Host metadata for one step (vLLM pull request, "CUDA graphs and continuous
+ * batching": the write position is the row's decode step counted from its
+ * anchor, modulo L; a row flushes at position L-1 or when a flush is forced,
+ * e.g. on the step that completes a prefix-cache block).  Host arrays of
+ * n_rows:
+ *   steps_since_anchor  in:  decode steps since the row's anchor; < 0 = pad row
+ *   force_flush         in:  nonzero forces a flush this step (may be NULL)
+ *   write_pos           out: steps_since_anchor mod L (0 for pad rows)
+ *   flush               out: 1 if the row flushes this step (0 for pad rows)
+ * The caller copies write_pos and flush to the device.  RS_EINVAL on NULL
+ * output pointers, n_rows < 0 or L outside 1..64.
+ */
+int rs_meta_step(int32_t L, int32_t n_rows, const int32_t* steps_since_anchor,
+                 const uint8_t* force_flush, int32_t* write_pos, uint8_t* flush);
+
+/*
+ * Host: advance the per-row anchors after a step: a row that flushed is
+ * re-anchored (0), any other live row counts one more step; pad rows (< 0)
+ * stay as they are.  Re-anchoring a resumed or re-joined row is the caller
+ * setting its entry to 0 (after replay_flush or replay_state_reset).
+ */
+int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, const uint8_t* flush);
+
+/* Host: RS_OK if a kernel is compiled for this layer, else the reason code. */
+int rs_layer_supported(const rs_layer* layer);
+
+/* Host: description of the last error raised on the calling thread ("" if none). */
+const char* rs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */

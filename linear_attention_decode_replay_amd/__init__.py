@@ -1,0 +1,243 @@
+"""Batched SSM decode step served from a checkpoint plus a record buffer, on
+MI355X (gfx950).
+
+This package is a thin ctypes binding over ``libreplayssm.so`` (C ABI in
+``include/replayssm.h``).  It only marshals arguments: every step of the
+decode path runs in the HIP kernels.  PyTorch supplies device memory and the
+stream.  If the library is missing, importing this package raises
+ImportError; there is no fallback.
+
+Entry points (same names and meaning as the C ABI):
+    replay_decode_step, replay_flush, conventional_decode_step,
+    replay_state_reset, rs_meta_step, rs_meta_advance, block_layout,
+    layer_supported.
+Struct builders: layer(), make_batch(), make_io(); device memory helper:
+Pool (allocates the paged block pool with torch and exposes typed views).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayssm.so")
+
+MAMBA2, GDN = 0, 1
+F32, F16, BF16 = 0, 1, 2
+RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
+
+_c = ctypes
+_vp = _c.c_void_p
+
+
+class RsLayer(_c.Structure):
+    _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
+                ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
+                ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32)]
+
+
+class RsBlockLayout(_c.Structure):
+    _fields_ = [("ckpt_off", _c.c_int64), ("rec_x_off", _c.c_int64), ("rec_k_off", _c.c_int64),
+                ("rec_lam_off", _c.c_int64), ("block_bytes", _c.c_int64), ("slots", _c.c_int32),
+                ("reserved", _c.c_int32)]
+
+
+class RsBatch(_c.Structure):
+    _fields_ = [("n_rows", _c.c_int32), ("reserved", _c.c_int32), ("n_blocks", _c.c_int64),
+                ("pool", _vp), ("block_table", _vp), ("write_pos", _vp), ("flush", _vp),
+                ("err_count", _vp)]
+
+
+class RsStepIO(_c.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp),
+                ("q_row_stride", _c.c_int64), ("q_head_stride", _c.c_int64),
+                ("k_row_stride", _c.c_int64), ("k_head_stride", _c.c_int64),
+                ("v_row_stride", _c.c_int64), ("v_head_stride", _c.c_int64),
+                ("log_decay", _vp), ("beta", _vp), ("out", _vp)]
+
+
+class ReplaySSMError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"replayssm error {code}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m linear_attention_decode_replay_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = _c.CDLL(_LIB_PATH)
+    P = _c.POINTER
+    lib.rs_block_layout_get.argtypes = [P(RsLayer), P(RsBlockLayout)]
+    lib.rs_layer_supported.argtypes = [P(RsLayer)]
+    for name in ("replay_decode_step", "conventional_decode_step"):
+        getattr(lib, name).argtypes = [P(RsLayer), P(RsBatch), P(RsStepIO), _vp]
+    lib.replay_flush.argtypes = [P(RsLayer), P(RsBatch), _vp]
+    lib.replay_state_reset.argtypes = [P(RsLayer), P(RsBatch), _vp, _vp]
+    lib.rs_meta_step.argtypes = [_c.c_int32, _c.c_int32, _vp, _vp, _vp, _vp]
+    lib.rs_meta_advance.argtypes = [_c.c_int32, _c.c_int32, _vp, _vp]
+    lib.rs_last_error.restype = _c.c_char_p
+    for name in ("rs_block_layout_get", "rs_layer_supported", "replay_decode_step",
+                 "conventional_decode_step", "replay_flush", "replay_state_reset", "rs_meta_step",
+                 "rs_meta_advance"):
+        getattr(lib, name).restype = _c.c_int
+    return lib
+
+
+_lib = _load()
+LIBRARY_PATH = _LIB_PATH
+
+
+def _check(rc: int) -> None:
+    if rc != RS_OK:
+        raise ReplaySSMError(rc, _lib.rs_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.rs_last_error().decode()
+
+
+# ------------------------------------------------------------------ structs --
+_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
+
+
+def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
+          record_dtype="f16", io_dtype="bf16") -> RsLayer:
+    code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
+    return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
+                   code(record_dtype), code(io_dtype))
+
+
+def block_layout(lay: RsLayer) -> RsBlockLayout:
+    out = RsBlockLayout()
+    _check(_lib.rs_block_layout_get(_c.byref(lay), _c.byref(out)))
+    return out
+
+
+def layer_supported(lay: RsLayer) -> int:
+    return int(_lib.rs_layer_supported(_c.byref(lay)))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def make_batch(pool, n_blocks: int, block_table, write_pos=None, flush=None, err_count=None) -> RsBatch:
+    """pool: uint8 device tensor; block_table/write_pos: int32 [n_rows];
+    flush: uint8 [n_rows]; err_count: int32 [1].  The tensors must outlive
+    the launches that use the returned struct."""
+    return RsBatch(int(block_table.numel()), 0, int(n_blocks), _ptr(pool), _ptr(block_table),
+                   _ptr(write_pos), _ptr(flush), _ptr(err_count))
+
+
+def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:
+    """q, k: [n_rows, n_heads, d_k]; v: [n_rows, n_heads, d_v] (any row/head
+    strides, unit last stride); log_decay, beta: fp32 [n_rows, n_heads]
+    contiguous; out: fp32 [n_rows, n_heads, d_v] contiguous."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be [rows, heads, d] with unit last stride")
+    for name, t in (("log_decay", log_decay), ("beta", beta), ("out", out)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return RsStepIO(_ptr(q), _ptr(k), _ptr(v), q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+                    v.stride(0), v.stride(1), _ptr(log_decay), _ptr(beta), _ptr(out))
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ------------------------------------------------------------- entry points --
+def replay_decode_step(lay: RsLayer, batch: RsBatch, io: RsStepIO, stream=None) -> None:
+    _check(_lib.replay_decode_step(_c.byref(lay), _c.byref(batch), _c.byref(io), _stream(stream)))
+
+
+def replay_flush(lay: RsLayer, batch: RsBatch, stream=None) -> None:
+    _check(_lib.replay_flush(_c.byref(lay), _c.byref(batch), _stream(stream)))
+
+
+def conventional_decode_step(lay: RsLayer, batch: RsBatch, io: RsStepIO, stream=None) -> None:
+    _check(_lib.conventional_decode_step(_c.byref(lay), _c.byref(batch), _c.byref(io), _stream(stream)))
+
+
+def replay_state_reset(lay: RsLayer, batch: RsBatch, mask, stream=None) -> None:
+    _check(_lib.replay_state_reset(_c.byref(lay), _c.byref(batch), _ptr(mask), _stream(stream)))
+
+
+def rs_meta_step(L: int, steps_since_anchor: np.ndarray, force_flush: np.ndarray | None = None):
+    """Host metadata for one step.  Returns (write_pos int32, flush uint8)."""
+    s = np.ascontiguousarray(steps_since_anchor, dtype=np.int32)
+    n = s.shape[0]
+    f = None if force_flush is None else np.ascontiguousarray(force_flush, dtype=np.uint8)
+    wp = np.zeros(n, np.int32)
+    fl = np.zeros(n, np.uint8)
+    _check(_lib.rs_meta_step(int(L), n, s.ctypes.data, None if f is None else f.ctypes.data,
+                             wp.ctypes.data, fl.ctypes.data))
+    return wp, fl
+
+
+def rs_meta_advance(L: int, steps_since_anchor: np.ndarray, flush: np.ndarray) -> None:
+    """In place on an int32 contiguous array."""
+    assert steps_since_anchor.dtype == np.int32 and steps_since_anchor.flags.c_contiguous
+    f = np.ascontiguousarray(flush, dtype=np.uint8)
+    _check(_lib.rs_meta_advance(int(L), steps_since_anchor.shape[0], steps_since_anchor.ctypes.data,
+                                f.ctypes.data))
+
+
+# ------------------------------------------------------------ device memory --
+class Pool:
+    """The paged block pool of one layer, allocated with torch on a device,
+    with typed views of each region (memory plumbing for callers and tests)."""
+
+    def __init__(self, lay: RsLayer, n_blocks: int, device="cuda"):
+        import torch
+        self.layer = lay
+        self.layout = block_layout(lay)
+        self.n_blocks = int(n_blocks)
+        self.block_bytes = int(self.layout.block_bytes)
+        self.raw = torch.empty((self.n_blocks, self.block_bytes), dtype=torch.uint8, device=device)
+        self._tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+
+    def _region(self, off, nbytes, dtype, shape):
+        return self.raw[:, off:off + nbytes].view(dtype).view(self.n_blocks, *shape)
+
+    def ckpt(self):
+        """[n_blocks, H, d_v, d_k] in the state dtype."""
+        L = self.layer
+        dt = self._tdt[L.state_dtype]
+        es = 4 if L.state_dtype == F32 else 2
+        n = L.n_heads * L.d_v * L.d_k
+        return self._region(self.layout.ckpt_off, n * es, dt, (L.n_heads, L.d_v, L.d_k))
+
+    def rec_x(self):
+        """[n_blocks, H, slots, d_v] in the record dtype."""
+        L, s = self.layer, self.layout.slots
+        es = 4 if L.record_dtype == F32 else 2
+        return self._region(self.layout.rec_x_off, L.n_heads * s * L.d_v * es,
+                            self._tdt[L.record_dtype], (L.n_heads, s, L.d_v))
+
+    def rec_k(self):
+        """[n_blocks, H, slots, d_k] in the record dtype."""
+        L, s = self.layer, self.layout.slots
+        es = 4 if L.record_dtype == F32 else 2
+        return self._region(self.layout.rec_k_off, L.n_heads * s * L.d_k * es,
+                            self._tdt[L.record_dtype], (L.n_heads, s, L.d_k))
+
+    def rec_lam(self):
+        """[n_blocks, H, slots] fp32."""
+        import torch
+        L, s = self.layer, self.layout.slots
+        return self._region(self.layout.rec_lam_off, L.n_heads * s * 4, torch.float32, (L.n_heads, s))
+
+
+__all__ = [
+    "MAMBA2", "GDN", "F32", "F16", "BF16", "RsLayer", "RsBlockLayout", "RsBatch", "RsStepIO",
+    "ReplaySSMError", "layer", "block_layout", "layer_supported", "make_batch", "make_io",
+    "replay_decode_step", "replay_flush", "conventional_decode_step", "replay_state_reset",
+    "rs_meta_step", "rs_meta_advance", "last_error", "Pool", "LIBRARY_PATH",
+]

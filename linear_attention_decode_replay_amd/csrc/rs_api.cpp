@@ -1,0 +1,263 @@
+// Host side of the C ABI declared in replayssm.h: argument validation, the
+// paged block layout, the per-row cursor/flush metadata and kernel launch.
+// No allocation, no global mutable state (the error text is thread-local).
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "replayssm.h"
+#include "rs_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return RS_OK;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dtype_bytes(int dt) { return dt == RS_F32 ? 4 : 2; }
+
+const int kMaxL = 64;
+const size_t kMaxLds = 64 * 1024;
+
+int check_layer(const rs_layer* L, rs::Kind kind) {
+    if (!L) return fail(RS_EINVAL, "layer is NULL");
+    if (L->form != RS_MAMBA2 && L->form != RS_GDN) return fail(RS_EINVAL, "unknown form %d", L->form);
+    if (L->n_heads < 1) return fail(RS_EINVAL, "n_heads must be >= 1 (got %d)", L->n_heads);
+    if (L->d_v < 1 || L->d_k < 1) return fail(RS_EINVAL, "d_v and d_k must be >= 1");
+    if (L->L < 1 || L->L > kMaxL) return fail(RS_EINVAL, "L must be in 1..%d (got %d)", kMaxL, L->L);
+    for (int dt : {L->state_dtype, L->record_dtype, L->io_dtype})
+        if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return fail(RS_EINVAL, "unknown dtype %d", dt);
+    if (L->state_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 state is not supported");
+    if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
+    if (!rs::compiled(kind, *L))
+        return fail(RS_EUNSUPPORTED, "no kernel for d_v=%d d_k=%d (supported: 16x32, 64x128, 128x128)",
+                    L->d_v, L->d_k);
+    if (rs::lds_bytes(kind, *L) > kMaxLds)
+        return fail(RS_EUNSUPPORTED, "buffer of L=%d records needs %zu bytes of LDS (> %zu)", L->L,
+                    rs::lds_bytes(kind, *L), kMaxLds);
+    return RS_OK;
+}
+
+void layout_of(const rs_layer& L, rs_block_layout* o) {
+    const int64_t slots = L.L - 1;
+    const int64_t H = L.n_heads;
+    const int64_t sb = dtype_bytes(L.state_dtype), rb = dtype_bytes(L.record_dtype);
+    o->ckpt_off = 0;
+    o->rec_x_off = align_up(H * L.d_v * L.d_k * sb, 256);
+    o->rec_k_off = align_up(o->rec_x_off + H * slots * L.d_v * rb, 256);
+    o->rec_lam_off = align_up(o->rec_k_off + H * slots * L.d_k * rb, 256);
+    o->block_bytes = align_up(o->rec_lam_off + H * slots * 4, 256);
+    o->slots = (int32_t)slots;
+    o->reserved = 0;
+}
+
+int check_batch(const rs_layer& L, const rs_batch* b, bool needs_cursor, bool needs_flush) {
+    if (!b) return fail(RS_EINVAL, "batch is NULL");
+    if (b->n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
+    if (b->n_rows == 0) return RS_OK;
+    if ((int64_t)b->n_rows * L.n_heads > 0x7fffffffLL)
+        return fail(RS_EINVAL, "n_rows * n_heads exceeds the launch grid");
+    if (b->n_blocks < 1) return fail(RS_EINVAL, "n_blocks must be >= 1");
+    if (!b->pool || !aligned(b->pool, 256)) return fail(RS_EINVAL, "pool must be non-NULL and 256-byte aligned");
+    if (!b->block_table) return fail(RS_EINVAL, "block_table is NULL");
+    if (needs_cursor && !b->write_pos) return fail(RS_EINVAL, "write_pos is NULL");
+    if (needs_flush && !b->flush) return fail(RS_EINVAL, "flush is NULL");
+    if (b->err_count && !aligned(b->err_count, 4)) return fail(RS_EINVAL, "err_count is misaligned");
+    return RS_OK;
+}
+
+int check_vec(const char* name, const void* p, int64_t rs, int64_t hs, int d, int elem) {
+    if (!p) return fail(RS_EINVAL, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(RS_EINVAL, "%s must be 16-byte aligned", name);
+    if ((rs * elem) % 16 || (hs * elem) % 16)
+        return fail(RS_EINVAL, "%s strides (%lld, %lld elements) must keep 16-byte alignment", name,
+                    (long long)rs, (long long)hs);
+    if (hs < d || rs < 0) return fail(RS_EINVAL, "%s strides (%lld, %lld) overlap a %d-vector", name,
+                                      (long long)rs, (long long)hs, d);
+    return RS_OK;
+}
+
+int check_io(const rs_layer& L, const rs_batch& b, const rs_step_io* io) {
+    if (!io) return fail(RS_EINVAL, "io is NULL");
+    if (b.n_rows == 0) return RS_OK;
+    const int e = dtype_bytes(L.io_dtype);
+    int rc;
+    if ((rc = check_vec("q", io->q, io->q_row_stride, io->q_head_stride, L.d_k, e))) return rc;
+    if ((rc = check_vec("k", io->k, io->k_row_stride, io->k_head_stride, L.d_k, e))) return rc;
+    if ((rc = check_vec("v", io->v, io->v_row_stride, io->v_head_stride, L.d_v, e))) return rc;
+    if (b.n_rows > 1) {
+        if (io->q_row_stride < (int64_t)L.n_heads * io->q_head_stride ||
+            io->k_row_stride < (int64_t)L.n_heads * io->k_head_stride ||
+            io->v_row_stride < (int64_t)L.n_heads * io->v_head_stride)
+            return fail(RS_EINVAL, "row strides overlap the heads of the previous row");
+    }
+    if (!io->log_decay || !aligned(io->log_decay, 16)) return fail(RS_EINVAL, "log_decay must be non-NULL and 16-byte aligned");
+    if (L.form == RS_GDN && (!io->beta || !aligned(io->beta, 16)))
+        return fail(RS_EINVAL, "beta must be non-NULL and 16-byte aligned for Gated DeltaNet");
+    if (!io->out || !aligned(io->out, 16)) return fail(RS_EINVAL, "out must be non-NULL and 16-byte aligned");
+    return RS_OK;
+}
+
+rs::StepParams params(const rs_layer& L, const rs_batch& b) {
+    rs_block_layout lay;
+    layout_of(L, &lay);
+    rs::StepParams p{};
+    p.pool = static_cast<char*>(b.pool);
+    p.block_bytes = lay.block_bytes;
+    p.n_blocks = b.n_blocks;
+    p.ckpt_off = lay.ckpt_off;
+    p.recx_off = lay.rec_x_off;
+    p.reck_off = lay.rec_k_off;
+    p.reclam_off = lay.rec_lam_off;
+    p.block_table = b.block_table;
+    p.write_pos = b.write_pos;
+    p.flush = b.flush;
+    p.err = b.err_count;
+    p.n_rows = b.n_rows;
+    p.n_heads = L.n_heads;
+    p.L = L.L;
+    p.slots = lay.slots;
+    return p;
+}
+
+void set_io(rs::StepParams& p, const rs_step_io& io) {
+    p.q = io.q;
+    p.k = io.k;
+    p.v = io.v;
+    p.qs_r = io.q_row_stride;
+    p.qs_h = io.q_head_stride;
+    p.ks_r = io.k_row_stride;
+    p.ks_h = io.k_head_stride;
+    p.vs_r = io.v_row_stride;
+    p.vs_h = io.v_head_stride;
+    p.lam = io.log_decay;
+    p.beta = io.beta;
+    p.out = io.out;
+}
+
+int do_launch(rs::Kind kind, const rs_layer& L, const rs::StepParams& p, hipStream_t stream) {
+    (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
+    const hipError_t e = rs::launch(kind, L, p, stream);
+    if (e != hipSuccess) return fail(RS_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out) {
+    int rc = check_layer(layer, rs::Kind::ReplayStep);
+    if (rc) return rc;
+    if (!out) return fail(RS_EINVAL, "out is NULL");
+    layout_of(*layer, out);
+    return ok();
+}
+
+int rs_layer_supported(const rs_layer* layer) {
+    int rc = check_layer(layer, rs::Kind::ReplayStep);
+    if (rc) return rc;
+    rc = check_layer(layer, rs::Kind::ConventionalStep);
+    return rc ? rc : ok();
+}
+
+int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
+                       hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::ReplayStep))) return rc;
+    if ((rc = check_batch(*layer, batch, true, false))) return rc;
+    if ((rc = check_io(*layer, *batch, io))) return rc;
+    if (batch->n_rows == 0) return ok();
+    rs::StepParams p = params(*layer, *batch);
+    set_io(p, *io);
+    return do_launch(rs::Kind::ReplayStep, *layer, p, stream);
+}
+
+int replay_flush(const rs_layer* layer, const rs_batch* batch, hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::Flush))) return rc;
+    if ((rc = check_batch(*layer, batch, true, true))) return rc;
+    if (batch->n_rows == 0) return ok();
+    const rs::StepParams p = params(*layer, *batch);
+    return do_launch(rs::Kind::Flush, *layer, p, stream);
+}
+
+int conventional_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
+                             hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::ConventionalStep))) return rc;
+    if ((rc = check_batch(*layer, batch, false, false))) return rc;
+    if ((rc = check_io(*layer, *batch, io))) return rc;
+    if (batch->n_rows == 0) return ok();
+    rs::StepParams p = params(*layer, *batch);
+    p.write_pos = nullptr;
+    p.flush = nullptr;
+    set_io(p, *io);
+    return do_launch(rs::Kind::ConventionalStep, *layer, p, stream);
+}
+
+int replay_state_reset(const rs_layer* layer, const rs_batch* batch, const uint8_t* mask,
+                       hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::Reset))) return rc;
+    if ((rc = check_batch(*layer, batch, false, false))) return rc;
+    if (batch->n_rows == 0) return ok();
+    if (!mask) return fail(RS_EINVAL, "mask is NULL");
+    rs::StepParams p = params(*layer, *batch);
+    p.mask = mask;
+    return do_launch(rs::Kind::Reset, *layer, p, stream);
+}
+
+int rs_meta_step(int32_t L, int32_t n_rows, const int32_t* steps_since_anchor,
+                 const uint8_t* force_flush, int32_t* write_pos, uint8_t* flush) {
+    if (L < 1 || L > kMaxL) return fail(RS_EINVAL, "L must be in 1..%d (got %d)", kMaxL, L);
+    if (n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
+    if (n_rows == 0) return ok();
+    if (!steps_since_anchor || !write_pos || !flush) return fail(RS_EINVAL, "NULL array");
+    for (int32_t r = 0; r < n_rows; ++r) {
+        const int32_t n = steps_since_anchor[r];
+        if (n < 0) {
+            write_pos[r] = 0;
+            flush[r] = 0;
+            continue;
+        }
+        const int32_t w = n % L;
+        write_pos[r] = w;
+        flush[r] = (uint8_t)((w == L - 1) || (force_flush && force_flush[r]));
+    }
+    return ok();
+}
+
+int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, const uint8_t* flush) {
+    if (L < 1 || L > kMaxL) return fail(RS_EINVAL, "L must be in 1..%d (got %d)", kMaxL, L);
+    if (n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
+    if (n_rows == 0) return ok();
+    if (!steps_since_anchor || !flush) return fail(RS_EINVAL, "NULL array");
+    for (int32_t r = 0; r < n_rows; ++r) {
+        if (steps_since_anchor[r] < 0) continue;
+        steps_since_anchor[r] = flush[r] ? 0 : steps_since_anchor[r] + 1;
+    }
+    return ok();
+}
+
+const char* rs_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal interface between the host entry points (rs_api.cpp) and the
+// kernels (rs_kernels.hip).  Not installed; the public ABI is replayssm.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "replayssm.h"
+
+namespace rs {
+
+// Everything a launch needs, passed to the kernels by value.
+struct StepParams {
+    char* pool;
+    int64_t block_bytes;
+    int64_t n_blocks;
+    int64_t ckpt_off, recx_off, reck_off, reclam_off;
+    const int32_t* block_table;
+    const int32_t* write_pos;
+    const uint8_t* flush;   // per-row flag (replay step, token-less flush)
+    const uint8_t* mask;    // per-row mask (state reset)
+    int32_t* err;
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t qs_r, qs_h, ks_r, ks_h, vs_r, vs_h;
+    const float* lam;
+    const float* beta;
+    float* out;
+    int32_t n_rows, n_heads, L, slots;
+};
+
+enum class Kind { ReplayStep, ConventionalStep, Flush, Reset };
+
+// Dynamic LDS bytes a launch of `kind` needs for this layer (0 if none).
+size_t lds_bytes(Kind kind, const rs_layer& layer);
+
+// True if a kernel of `kind` is compiled for this layer.
+bool compiled(Kind kind, const rs_layer& layer);
+
+// Launch; returns hipSuccess or the launch error.
+hipError_t launch(Kind kind, const rs_layer& layer, const StepParams& p, hipStream_t stream);
+
+}  // namespace rs

@@ -74,7 +74,7 @@ class Oracle:
         lib = ctypes.CDLL(path)
         i64, i32, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
         lib.oc_conventional_step.argtypes = [c_int, i64, c_int, c_int, _F64P, _F64P, _F64P, _F64P,
-                                             _F64P, _opt(_F64P), _opt(_U8P), _F64P]
+                                             _F64P, _opt(_F64P), _opt(_U8P), _F64P, _opt(_F64P)]
         lib.oc_conventional_step.restype = None
         lib.oc_replay_step.argtypes = [c_int, i64, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P,
                                        _I32P, _U8P, _F64P, _F64P, _F64P, _F64P, _opt(_F64P),
@@ -97,13 +97,15 @@ class Oracle:
         self.lib.oc_set_num_threads(int(n))
 
     # -- steps -----------------------------------------------------------
-    def conventional_step(self, form, S, q, k, v, lam, beta=None, active=None):
+    def conventional_step(self, form, S, q, k, v, lam, beta=None, active=None, want_x=False):
+        """Returns out, or (out, x) with x the value written into the state."""
         n, dv, dk = S.shape
         out = np.zeros((n, dv), np.float64)
+        x = np.zeros((n, dv), np.float64) if want_x else None
         _check(S, q, k, v, lam, beta, n, dv, dk)
         self.lib.oc_conventional_step(int(form), n, dv, dk, S, q, k, v, lam, beta,
-                                      _u8(active), out)
-        return out
+                                      _u8(active), out, x)
+        return (out, x) if want_x else out
 
     def replay_step(self, form, C, rec_lam, rec_x, rec_k, w, flush, q, k, v, lam, beta=None,
                     active=None):
@@ -165,15 +167,18 @@ class ConventionalModel:
         n = B * H
         self.S = np.zeros((n, dv, dk)) if S0 is None else np.ascontiguousarray(S0, np.float64).reshape(n, dv, dk).copy()
 
-    def step(self, q, k, v, lam, beta=None, active_rows=None):
-        """q, k: [B, H, dk]; v: [B, H, dv]; lam, beta: [B, H].  Returns o [B, H, dv]."""
+    def step(self, q, k, v, lam, beta=None, active_rows=None, want_x=False):
+        """q, k: [B, H, dk]; v: [B, H, dv]; lam, beta: [B, H].  Returns o [B, H, dv]
+        (and, with want_x, the value x [B, H, dv] written into the state)."""
         B, H = self.B, self.H
         act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
         n = B * H
-        out = self.o.conventional_step(self.form, self.S, _vec(q, n), _vec(k, n), _vec(v, n),
+        res = self.o.conventional_step(self.form, self.S, _vec(q, n), _vec(k, n), _vec(v, n),
                                        _scal(lam, n), None if beta is None else _scal(beta, n),
-                                       act)
-        return out.reshape(B, H, self.dv)
+                                       act, want_x)
+        if want_x:
+            return res[0].reshape(B, H, self.dv), res[1].reshape(B, H, self.dv)
+        return res.reshape(B, H, self.dv)
 
     def state(self):
         return self.S.reshape(self.B, self.H, self.dv, self.dk)

@@ -82,12 +82,13 @@ static void matvec(const double* S, const double* x, int dv, int dk, double* y) 
  *
  * Arrays: S [n][dv][dk]; q, k [n][dk]; v, out [n][dv]; lam, beta [n]
  * (beta ignored for Mamba-2, may be NULL).  active [n] may be NULL (= all);
- * inactive tiles are left untouched.
+ * inactive tiles are left untouched.  xout [n][dv], if not NULL, receives
+ * the value written into the state this step (v, or the corrected d).
  */
 void oc_conventional_step(int form, int64_t n, int dv, int dk, double* S,
                           const double* q, const double* k, const double* v,
                           const double* lam, const double* beta,
-                          const uint8_t* active, double* out) {
+                          const uint8_t* active, double* out, double* xout) {
 #pragma omp parallel
     {
         double* a = (double*)malloc(sizeof(double) * (size_t)dv);
@@ -111,6 +112,7 @@ void oc_conventional_step(int form, int64_t n, int dv, int dk, double* S,
                 for (int c = 0; c < dk; ++c)
                     St[(int64_t)i * dk + c] = alpha * St[(int64_t)i * dk + c] + d[i] * kt[c];
             matvec(St, qt, dv, dk, out + t * dv);            /* o_t = S_t q_t */
+            if (xout) memcpy(xout + t * dv, d, sizeof(double) * (size_t)dv);
         }
         free(a);
         free(d);

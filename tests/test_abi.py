@@ -1,0 +1,169 @@
+"""C ABI on the CPU: symbols, block layout, validation, host metadata.
+
+No GPU work here: device entry points are only called with arguments that
+fail host-side validation or with n_rows == 0 (which launches nothing)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_decode_replay_amd as rs
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "replayssm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert {"replay_decode_step", "replay_flush", "conventional_decode_step", "replay_state_reset",
+            "rs_block_layout_get", "rs_meta_step", "rs_meta_advance", "rs_last_error"} <= set(names)
+    lib = ctypes.CDLL(rs.LIBRARY_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in replayssm.h but not exported"
+
+
+def _c2(**kw):
+    args = dict(form=rs.MAMBA2, n_heads=128, d_v=64, d_k=128, L=16, state_dtype="f32",
+                record_dtype="f16", io_dtype="bf16")
+    args.update(kw)
+    return rs.layer(**args)
+
+
+def test_block_layout_nemotron_layer():
+    lay = rs.block_layout(_c2())
+    assert lay.ckpt_off == 0
+    assert lay.rec_x_off == 4 * 2**20            # the 4 MiB checkpoint
+    assert lay.slots == 15
+    assert lay.rec_k_off == lay.rec_x_off + 128 * 15 * 64 * 2
+    assert lay.rec_lam_off == lay.rec_k_off + 128 * 15 * 128 * 2
+    assert lay.block_bytes == lay.rec_lam_off + 128 * 15 * 4   # already 256-aligned
+    for off in (lay.rec_x_off, lay.rec_k_off, lay.rec_lam_off, lay.block_bytes):
+        assert off % 256 == 0
+
+
+@pytest.mark.parametrize("L", [1, 2, 16, 64])
+@pytest.mark.parametrize("shape", [(16, 32), (64, 128), (128, 128)])
+@pytest.mark.parametrize("sdt,rdt", [("f32", "f32"), ("f16", "f16"), ("f32", "f16")])
+def test_block_layout_regions_disjoint(L, shape, sdt, rdt):
+    dv, dk = shape
+    layer = _c2(n_heads=3, d_v=dv, d_k=dk, L=L, state_dtype=sdt, record_dtype=rdt)
+    if rs.layer_supported(layer) != rs.RS_OK:
+        pytest.skip(rs.last_error())
+    lay = rs.block_layout(layer)
+    sb, rb = (4 if sdt == "f32" else 2), (4 if rdt == "f32" else 2)
+    ends = [(lay.ckpt_off, 3 * dv * dk * sb), (lay.rec_x_off, 3 * (L - 1) * dv * rb),
+            (lay.rec_k_off, 3 * (L - 1) * dk * rb), (lay.rec_lam_off, 3 * (L - 1) * 4)]
+    for (a, na), (b, _) in zip(ends, ends[1:]):
+        assert a + na <= b
+    assert ends[-1][0] + ends[-1][1] <= lay.block_bytes and lay.block_bytes % 256 == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(L=0), rs.RS_EINVAL), (dict(L=65), rs.RS_EINVAL), (dict(form=7), rs.RS_EINVAL),
+    (dict(n_heads=0), rs.RS_EINVAL), (dict(d_v=32, d_k=32), rs.RS_EUNSUPPORTED),
+    (dict(state_dtype="bf16"), rs.RS_EUNSUPPORTED), (dict(io_dtype=9), rs.RS_EINVAL),
+    (dict(d_v=128, d_k=128, L=64, record_dtype="f32"), rs.RS_EUNSUPPORTED),
+])
+def test_layer_validation(bad, code):
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.block_layout(_c2(**bad))
+    assert e.value.code == code
+    assert rs.last_error()
+
+
+def test_empty_batch_launches_nothing():
+    layer = _c2()
+    empty = rs.RsBatch(0, 0, 1, None, None, None, None, None)
+    io = rs.RsStepIO()
+    rs.replay_decode_step(layer, empty, io, stream=0)
+    rs.conventional_decode_step(layer, empty, io, stream=0)
+    rs.replay_flush(layer, empty, stream=0)
+    rs.replay_state_reset(layer, empty, None, stream=0)
+
+
+def test_device_calls_reject_bad_arguments_on_host():
+    layer = _c2()
+    buf = (ctypes.c_uint8 * 512)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    batch = rs.RsBatch(4, 0, 4, None, base, base, None, None)      # NULL pool
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_decode_step(layer, batch, rs.RsStepIO(), stream=0)
+    assert e.value.code == rs.RS_EINVAL and "pool" in rs.last_error()
+    batch = rs.RsBatch(4, 0, 4, base + 8, base, base, None, None)  # misaligned pool
+    with pytest.raises(rs.ReplaySSMError):
+        rs.replay_decode_step(layer, batch, rs.RsStepIO(), stream=0)
+    batch = rs.RsBatch(4, 0, 4, base, base, base, None, None)
+    io = rs.RsStepIO(base, base, base, 128 * 128, 128, 128 * 128, 128, 128 * 64, 64, base, None, base)
+    io.q = base + 8                                                # misaligned q
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_decode_step(layer, batch, io, stream=0)
+    assert "q" in rs.last_error()
+    io.q = base
+    io.k_head_stride = 100                                         # head stride < d_k
+    with pytest.raises(rs.ReplaySSMError):
+        rs.replay_decode_step(layer, batch, io, stream=0)
+    io.k_head_stride = 128
+    with pytest.raises(rs.ReplaySSMError) as e:                    # GDN needs beta
+        rs.replay_decode_step(_c2(form=rs.GDN), batch, io, stream=0)
+    assert "beta" in rs.last_error()
+    with pytest.raises(rs.ReplaySSMError):                         # token-less flush needs flags
+        rs.replay_flush(layer, batch, stream=0)
+    with pytest.raises(rs.ReplaySSMError):                         # reset needs a mask
+        rs.replay_state_reset(layer, batch, None, stream=0)
+
+
+# ------------------------------------------------------------ host metadata --
+def _run_meta(L, n_steps, w0, forced=None):
+    """Drive rs_meta_step / rs_meta_advance for one row over n_steps."""
+    anchor = np.array([w0], np.int32)
+    ws, fs = [], []
+    for s in range(n_steps):
+        f = None if forced is None else np.array([forced[s]], np.uint8)
+        wp, fl = rs.rs_meta_step(L, anchor, f)
+        ws.append(int(wp[0]))
+        fs.append(bool(fl[0]))
+        rs.rs_meta_advance(L, anchor, fl)
+    return np.array(ws, np.int32), np.array(fs)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 16, 64])
+def test_meta_matches_oracle_cursor(L):
+    orc = oracle.get()
+    rng = np.random.default_rng(L)
+    for w0 in sorted({0, L // 2, L - 1}):
+        for forced in (None, (rng.random(3 * L + 7) < 0.15).astype(np.uint8)):
+            w, f = _run_meta(L, 3 * L + 7, w0, forced)
+            ow, of = orc.cursor_run(L, w0, 3 * L + 7, forced)
+            assert np.array_equal(w, ow) and np.array_equal(f, of), (L, w0)
+
+
+def test_meta_cases():
+    """Fresh decode, flush boundary, buffer wrap, resume re-anchor, pad rows
+    and per-row independence in one batch."""
+    L = 16
+    anchor = np.array([0, 14, 15, 40, -1, 3], np.int32)   # row 3: anchor counted past L (wraps)
+    force = np.array([0, 0, 0, 0, 1, 1], np.uint8)        # pad row ignores its force flag
+    wp, fl = rs.rs_meta_step(L, anchor, force)
+    assert list(wp) == [0, 14, 15, 8, 0, 3]
+    assert list(fl) == [0, 0, 1, 0, 0, 1]
+    rs.rs_meta_advance(L, anchor, fl)
+    assert list(anchor) == [1, 15, 0, 41, -1, 0]
+    # resume after preemption: the caller re-anchors the row at 0
+    anchor[3] = 0
+    wp, fl = rs.rs_meta_step(L, anchor)
+    assert wp[3] == 0 and fl[3] == 0 and wp[1] == 15 and fl[1] == 1
+
+
+def test_meta_rejects_bad_arguments():
+    with pytest.raises(rs.ReplaySSMError):
+        rs.rs_meta_step(0, np.zeros(3, np.int32))
+    with pytest.raises(rs.ReplaySSMError):
+        rs.rs_meta_step(65, np.zeros(3, np.int32))

@@ -1,0 +1,36 @@
+"""bench.py's algorithmic byte accounting against the oracle's traffic model."""
+import pytest
+
+import bench
+from oracle import bytemodel as bm
+
+
+@pytest.mark.parametrize("name", sorted(bench.WORKLOADS))
+@pytest.mark.parametrize("L", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("state", ["f32", "f16"])
+def test_window_bytes_match_model(name, L, state):
+    c = dict(bench.WORKLOADS[name])
+    c["L"], c["state"] = L, state
+    args = (c["form"], c["H"], c["dv"], c["dk"], c["B"], c["state"], c["rec"], c["io"])
+    io = (2 * c["dk"] + c["dv"]) * 2 + 4 + (4 if c["form"] == 1 else 0) + 4 * c["dv"]
+    ms = bm.state_bytes(c["dv"], c["dk"], 4 if state == "f32" else 2)
+    rec = bm.record_bytes(c["dv"], c["dk"])   # fp16 x and k, fp32 decay
+    per_row_meta = 9 * c["B"] * L
+    got = bench.window_bytes(*args, L) - c["B"] * c["H"] * L * io - per_row_meta
+    assert got == c["B"] * c["H"] * bm.replay_window_bytes(L, ms, rec)
+    got_c = bench.window_bytes(*args, L, "conventional") - c["B"] * c["H"] * L * io - 4 * c["B"] * L
+    assert got_c == c["B"] * c["H"] * bm.conventional_window_bytes(L, ms)
+
+
+def test_headline_ratio():
+    """The headline workload's algorithmic traffic ratio, inputs included: the
+    state + record part is the blog's 0.581; q/k/v/out add a little."""
+    c = bench.WORKLOADS["nemotron"]
+    args = (c["form"], c["H"], c["dv"], c["dk"], c["B"], c["state"], c["rec"], c["io"], c["L"])
+    r = bench.window_bytes(*args) / bench.window_bytes(*args, "conventional")
+    assert 0.581 < r < 0.60
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err

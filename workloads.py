@@ -4,9 +4,10 @@ Shared by the tests, the smoke check and the benchmark, and by both the GPU
 path and the CPU oracle.  This module draws random numbers and casts them to
 the input dtypes; it contains none of the decode arithmetic.
 
-Every generator is a pure function of (seed, step, shape): numpy's
-``default_rng([seed, stream, step])`` makes each step's draw independent of
-how many earlier steps were generated, so a test can regenerate step s alone.
+Every generator is a pure function of (seed, step, shape): each draw uses a
+torch CPU generator seeded from numpy's SeedSequence([seed, stream, step]),
+so a step's inputs do not depend on how many earlier steps were generated
+(a test can regenerate step s alone) nor on the thread count.
 
 Input recipes (the workloads the pages measure on):
   * Mamba-2 form: v, k, q ~ N(0, 1); log-decay lam = -softplus(x) * a with
@@ -35,12 +36,15 @@ def torch_dtype(name: str) -> torch.dtype:
     return _TORCH_DT[name]
 
 
-def _softplus(x: np.ndarray) -> np.ndarray:
+def _softplus(x):
+    if isinstance(x, torch.Tensor):
+        return torch.logaddexp(torch.zeros_like(x), x)
     return np.logaddexp(0.0, x)
 
 
-def _sigmoid(x: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-x))
+def _gen(*key: int) -> torch.Generator:
+    seed = int(np.random.SeedSequence(list(key)).generate_state(1, dtype=np.uint64)[0] >> 1)
+    return torch.Generator().manual_seed(seed)
 
 
 def head_decay_scale(seed: int, H: int, a_lo: float = 1.0, a_hi: float = 8.0) -> np.ndarray:
@@ -60,30 +64,28 @@ class Tokens:
 
 def mamba2_tokens(seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str = "f32",
                   a_lo: float = 1.0, a_hi: float = 8.0) -> Tokens:
-    rng = np.random.default_rng([seed, _S_TOKENS, step])
-    q = rng.standard_normal((B, H, dk), dtype=np.float32)
-    k = rng.standard_normal((B, H, dk), dtype=np.float32)
-    v = rng.standard_normal((B, H, dv), dtype=np.float32)
-    x = rng.standard_normal((B, H))
-    a = head_decay_scale(seed, H, a_lo, a_hi)
-    lam = (-_softplus(x) * a[None, :]).astype(np.float32)
+    g = _gen(seed, _S_TOKENS, step)
     dt = _TORCH_DT[io]
-    return Tokens(torch.from_numpy(q).to(dt), torch.from_numpy(k).to(dt),
-                  torch.from_numpy(v).to(dt), torch.from_numpy(lam), None)
+    q = torch.randn((B, H, dk), generator=g).to(dt)
+    k = torch.randn((B, H, dk), generator=g).to(dt)
+    v = torch.randn((B, H, dv), generator=g).to(dt)
+    x = torch.randn((B, H), generator=g, dtype=torch.float64)
+    a = torch.from_numpy(head_decay_scale(seed, H, a_lo, a_hi))
+    lam = (-_softplus(x) * a[None, :]).float()
+    return Tokens(q, k, v, lam, None)
 
 
 def gdn_tokens(seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str = "bf16") -> Tokens:
-    rng = np.random.default_rng([seed, _S_TOKENS, step])
-    q = rng.standard_normal((B, H, dk))
-    k = rng.standard_normal((B, H, dk))
-    q /= np.linalg.norm(q, axis=-1, keepdims=True)
-    k /= np.linalg.norm(k, axis=-1, keepdims=True)
-    v = rng.standard_normal((B, H, dv))
-    beta = _sigmoid(rng.standard_normal((B, H))).astype(np.float32)
-    lam = (-_softplus(rng.standard_normal((B, H)))).astype(np.float32)
+    g = _gen(seed, _S_TOKENS, step)
     dt = _TORCH_DT[io]
-    return Tokens(torch.from_numpy(q).to(dt), torch.from_numpy(k).to(dt),
-                  torch.from_numpy(v).to(dt), torch.from_numpy(lam), torch.from_numpy(beta))
+    q = torch.randn((B, H, dk), generator=g, dtype=torch.float64)
+    k = torch.randn((B, H, dk), generator=g, dtype=torch.float64)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(dt)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(dt)
+    v = torch.randn((B, H, dv), generator=g).to(dt)
+    beta = torch.sigmoid(torch.randn((B, H), generator=g, dtype=torch.float64)).float()
+    lam = (-_softplus(torch.randn((B, H), generator=g, dtype=torch.float64))).float()
+    return Tokens(q, k, v, lam, beta)
 
 
 def tokens(form: int, seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str,
