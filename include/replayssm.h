@@ -38,7 +38,10 @@
  *     rs_batch.err_count when that pointer is non-NULL.
  *   - Pointer alignment: pool 256 bytes; q, k, v, out, log_decay, beta
  *     16 bytes; q/k/v strides must keep every (row, head) vector 16-byte
- *     aligned.
+ *     aligned; block_table, write_pos, flush and reset masks 4 bytes (the
+ *     byte arrays are read in aligned 32-bit words, never past the word that
+ *     holds the last entry).
+ *   - Sizes: n_rows <= 65535 per launch.
  */
 #ifndef REPLAYSSM_H
 #define REPLAYSSM_H

@@ -64,6 +64,11 @@ class ReplaySSMError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime (same SONAME as ROCm's).  Loading torch
+    # first makes the dynamic linker bind this library to that same runtime
+    # instance, so torch's device memory and stream handles are valid here.
+    # Loaded the other way round, the process would hold two HIP runtimes.
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run `python -m linear_attention_decode_replay_amd.build` "
                           "(or __graft_entry__.build()) first")

@@ -73,13 +73,15 @@ int check_batch(const rs_layer& L, const rs_batch* b, bool needs_cursor, bool ne
     if (!b) return fail(RS_EINVAL, "batch is NULL");
     if (b->n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
     if (b->n_rows == 0) return RS_OK;
-    if ((int64_t)b->n_rows * L.n_heads > 0x7fffffffLL)
-        return fail(RS_EINVAL, "n_rows * n_heads exceeds the launch grid");
+    if (b->n_rows > 65535) return fail(RS_EINVAL, "n_rows must be <= 65535 (got %d)", b->n_rows);
     if (b->n_blocks < 1) return fail(RS_EINVAL, "n_blocks must be >= 1");
     if (!b->pool || !aligned(b->pool, 256)) return fail(RS_EINVAL, "pool must be non-NULL and 256-byte aligned");
-    if (!b->block_table) return fail(RS_EINVAL, "block_table is NULL");
+    if (!b->block_table || !aligned(b->block_table, 4))
+        return fail(RS_EINVAL, "block_table must be non-NULL and 4-byte aligned");
     if (needs_cursor && !b->write_pos) return fail(RS_EINVAL, "write_pos is NULL");
+    if (b->write_pos && !aligned(b->write_pos, 4)) return fail(RS_EINVAL, "write_pos must be 4-byte aligned");
     if (needs_flush && !b->flush) return fail(RS_EINVAL, "flush is NULL");
+    if (b->flush && !aligned(b->flush, 4)) return fail(RS_EINVAL, "flush must be 4-byte aligned");
     if (b->err_count && !aligned(b->err_count, 4)) return fail(RS_EINVAL, "err_count is misaligned");
     return RS_OK;
 }
@@ -220,7 +222,7 @@ int replay_state_reset(const rs_layer* layer, const rs_batch* batch, const uint8
     if ((rc = check_layer(layer, rs::Kind::Reset))) return rc;
     if ((rc = check_batch(*layer, batch, false, false))) return rc;
     if (batch->n_rows == 0) return ok();
-    if (!mask) return fail(RS_EINVAL, "mask is NULL");
+    if (!mask || !aligned(mask, 4)) return fail(RS_EINVAL, "mask must be non-NULL and 4-byte aligned");
     rs::StepParams p = params(*layer, *batch);
     p.mask = mask;
     return do_launch(rs::Kind::Reset, *layer, p, stream);

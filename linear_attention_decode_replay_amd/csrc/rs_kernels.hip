@@ -111,17 +111,17 @@ __device__ __forceinline__ u32x4 pack16(const float* in) {
 
 // ------------------------------------------------------- lane-group sums --
 // Sum N per-lane values over an aligned group of lanes (offsets OFF, OFF/2,
-// ..., 1; gl = lane index within the group).  While more than one value is
+// ..., 1; gl = lane index within the group).  While more than KEEP values are
 // left, the lane whose OFF bit is set keeps the upper half of its values,
 // its partner the lower half, and each adds the partner's copy of the half
-// it keeps; with one value left, plain butterflies finish.  Afterwards the
-// first xsum_left<N,G>() entries of v hold complete sums of original indices
-// xsum_base<N,G>(gl) + i, identical across the lanes that differ only in
-// xsum_dup_mask<N,G>() bits.
-template <int N, int OFF>
+// it keeps; once KEEP values are left, plain butterflies finish.  Afterwards
+// the first xsum_left<N,G,KEEP>() entries of v hold complete sums of the
+// contiguous original indices xsum_base<N,G,KEEP>(gl) + i, identical across
+// the lanes that differ only in xsum_dup_mask<N,G,KEEP>() bits.
+template <int N, int OFF, int KEEP = 1>
 __device__ __forceinline__ void xsum(float* v, int gl) {
     if constexpr (OFF > 0) {
-        if constexpr (N > 1) {
+        if constexpr (N > KEEP) {
             const bool up = (gl & OFF) != 0;
 #pragma unroll
             for (int i = 0; i < N / 2; ++i) {
@@ -129,37 +129,38 @@ __device__ __forceinline__ void xsum(float* v, int gl) {
                 const float keep = up ? v[i + N / 2] : v[i];
                 v[i] = keep + __shfl_xor(send, OFF);
             }
-            xsum<N / 2, OFF / 2>(v, gl);
+            xsum<N / 2, OFF / 2, KEEP>(v, gl);
         } else {
-            v[0] += __shfl_xor(v[0], OFF);
-            xsum<1, OFF / 2>(v, gl);
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], OFF);
+            xsum<N, OFF / 2, KEEP>(v, gl);
         }
     }
 }
 
-template <int N, int G>
+template <int N, int G, int KEEP = 1>
 constexpr int xsum_left() {
     int n = N;
-    for (int o = G / 2; o > 0 && n > 1; o >>= 1) n /= 2;
+    for (int o = G / 2; o > 0 && n > KEEP; o >>= 1) n /= 2;
     return n;
 }
 
-template <int N, int G>
+template <int N, int G, int KEEP = 1>
 __device__ __forceinline__ int xsum_base(int gl) {
     int n = N, b = 0;
 #pragma unroll
-    for (int o = G / 2; o > 0 && n > 1; o >>= 1) {
+    for (int o = G / 2; o > 0 && n > KEEP; o >>= 1) {
         if (gl & o) b += n / 2;
         n /= 2;
     }
     return b;
 }
 
-template <int N, int G>
+template <int N, int G, int KEEP = 1>
 constexpr int xsum_dup_mask() {
     int n = N, m = 0;
     for (int o = G / 2; o > 0; o >>= 1) {
-        if (n > 1) n /= 2;
+        if (n > KEEP) n /= 2;
         else m |= o;
     }
     return m;
@@ -174,101 +175,128 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // ------------------------------------------------------------ tile shape --
-template <int DV, int DK, class TS>
+// A (row, head) tile of d_v x d_k state is covered by SPLIT workgroups, each
+// owning DVW = d_v / SPLIT consecutive state rows (everything the step does is
+// row-local except the record dot products, which each workgroup recomputes).
+template <int DV, int DK, class TS, int SPLIT>
 struct Tile {
     using S = typename TS::S;
+    static constexpr int DVW = DV / SPLIT;                     // state rows per workgroup
     static constexpr int VEC = 16 / (int)sizeof(S);           // state elements per 16 B
     static constexpr int LPR = DK / VEC;                       // lanes per state row
-    static constexpr int LOADS = DV * LPR;                     // 16-B chunks per tile
-    static constexpr int NT = LOADS >= 2048 ? 256 : (LOADS >= 512 ? 128 : 64);
+    static constexpr int LOADS = DVW * LPR;                    // 16-B chunks per workgroup
+    static constexpr int NT = LOADS / 4 >= 256 ? 256 : (LOADS / 4 >= 128 ? 128 : 64);
     static constexpr int RPP = NT / LPR;                       // rows per pass
-    static constexpr int NR = DV / RPP;                        // passes per thread
+    static constexpr int NR = DVW / RPP;                       // passes per thread
+    static_assert(DV % SPLIT == 0, "split");
     static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "lane group");
-    static_assert(NT % LPR == 0 && DV % RPP == 0 && NR >= 1, "tile split");
+    static_assert(NT % LPR == 0 && DVW % RPP == 0 && NR >= 1, "tile split");
     static_assert((NR & (NR - 1)) == 0, "passes must be a power of two");
+    static_assert(NT >= DVW && NT >= 64, "one thread per owned row, one full wave");
 };
 
 constexpr int kMamba2 = RS_MAMBA2;
 constexpr int kGdn = RS_GDN;
 
 struct TileIds {
-    int row, head;
+    int row, head, part;
     int64_t tile;
 };
 
+// Grid: x = head * SPLIT + part, y = row (the workgroups of one row are
+// consecutive).
+template <int SPLIT>
 __device__ __forceinline__ TileIds tile_ids(const StepParams& p) {
     TileIds t;
-    t.tile = blockIdx.x;
-    t.row = (int)(t.tile / p.n_heads);
-    t.head = (int)(t.tile - (int64_t)t.row * p.n_heads);
+    t.head = (int)blockIdx.x / SPLIT;
+    t.part = (int)blockIdx.x % SPLIT;
+    t.row = (int)blockIdx.y;
+    t.tile = (int64_t)t.row * p.n_heads + t.head;
     return t;
+}
+
+// A row's flag byte, read as the 32-bit word that holds it (the array is
+// 4-byte aligned, checked on the host): a uniform address, so this is a
+// scalar load that issues together with the rest of the row metadata.  The
+// word never leaves the 4-byte-aligned span of the flag itself.
+__device__ __forceinline__ bool row_flag(const uint8_t* flags, int row) {
+    const uint32_t word = reinterpret_cast<const uint32_t*>(flags)[row >> 2];
+    return ((word >> (8 * (row & 3))) & 0xffu) != 0;
 }
 
 __device__ __forceinline__ void count_error(const StepParams& p) {
     if (threadIdx.x == 0 && p.err) atomicAdd(p.err, 1);
 }
 
-// LDS carve-up shared by the step and flush kernels.
+// Streamed state and records are read or written once per step and are far
+// larger than the caches, so they use non-temporal accesses (measured on
+// MI355X: a 128-bit read stream moves from ~6.4 to ~7.2 TB/s, an in-place
+// read-modify-write from ~5.3 to ~5.5-5.9 TB/s).
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// LDS carve-up shared by the step and flush kernels (DVW = rows owned).
 template <class R>
 struct Lds {
-    R* k;         // [slots][DK] buffered keys
-    R* x;         // [slots][DV] buffered values
-    float* lam;   // [L]  buffered log-decays
-    float* e;     // [L]  per-record decay weight
-    float* cq;    // [L]  k_j . q
-    float* ck;    // [L]  k_j . k (Gated DeltaNet)
-    float* y;     // [DV] C q
-    float* yk;    // [DV] C k (Gated DeltaNet)
-    float* v;     // [DV] current v
-    float* u;     // [DV] current corrected value d (Gated DeltaNet)
-    float* sc;    // [4]  G, k . q
+    R* k;         // [slots][DK]  buffered keys
+    R* x;         // [slots][DVW] buffered values, owned rows
+    float* e;     // [L]   per-record decay weight
+    float* cq;    // [L]   k_j . q
+    float* ck;    // [L]   k_j . k (Gated DeltaNet)
+    float* v;     // [DVW] current v, owned rows
+    float* u;     // [DVW] current corrected value d (Gated DeltaNet)
+    float* sc;    // [4]   G, k . q
 };
 
-template <int DV, int DK, class R>
+template <int DVW, int DK, class R>
 __device__ __forceinline__ Lds<R> carve(char* smem, int slots, int L) {
     Lds<R> s;
     s.k = reinterpret_cast<R*>(smem);
     s.x = s.k + (int64_t)slots * DK;
-    float* f = reinterpret_cast<float*>(s.x + (int64_t)slots * DV);
-    s.lam = f;
-    s.e = s.lam + L;
+    float* f = reinterpret_cast<float*>(s.x + (int64_t)slots * DVW);
+    s.e = f;
     s.cq = s.e + L;
     s.ck = s.cq + L;
-    s.y = s.ck + L;
-    s.yk = s.y + DV;
-    s.v = s.yk + DV;
-    s.u = s.v + DV;
-    s.sc = s.u + DV;
+    s.v = s.ck + L;
+    s.u = s.v + DVW;
+    s.sc = s.u + DVW;
     return s;
 }
 
-template <int DV, int DK, class R>
+template <int DVW, int DK, class R>
 constexpr size_t lds_need(int slots, int L) {
-    return (size_t)slots * (DK + DV) * sizeof(R) + sizeof(float) * (4 * (size_t)L + 4 * DV + 4);
+    return (size_t)slots * (DK + DVW) * sizeof(R) + sizeof(float) * (3 * (size_t)L + 2 * DVW + 4);
 }
 
-// Copy records 0..w-1 (keys then values) into LDS in 16-byte chunks.  The
-// first RC chunks per thread are loaded by rec_issue() before the caller
-// issues its checkpoint loads and written by rec_commit() afterwards; any
-// remainder (only when w * record bytes exceeds RC * NT * 16) is copied by
-// rec_commit() directly.
-template <int DV, int DK, class R, int NT, int RC>
+// Copy records 0..w-1 into LDS in 16-byte chunks: keys (d_k each, contiguous
+// in the buffer) then the owned DVW entries of each value record (stride d_v).
+// issue() loads the first RC chunks per thread before the caller issues its
+// checkpoint loads; commit() writes them to LDS afterwards and copies any
+// remainder (only when w records exceed RC * NT chunks) directly.
+template <int DV, int DVW, int DK, class R, int NT, int RC>
 struct RecordCopy {
-    static constexpr int KCH = DK * (int)sizeof(R) / 16;
-    static constexpr int XCH = DV * (int)sizeof(R) / 16;
-    static_assert(DK * sizeof(R) % 16 == 0 && DV * sizeof(R) % 16 == 0, "record rows");
+    static constexpr int KCH = DK * (int)sizeof(R) / 16;   // chunks per key record
+    static constexpr int XCH = DVW * (int)sizeof(R) / 16;  // chunks per owned value record
+    static constexpr int XE = 16 / (int)sizeof(R);         // elements per chunk
+    static_assert(DK * sizeof(R) % 16 == 0 && DVW * sizeof(R) % 16 == 0, "record rows");
     u32x4 buf[RC];
     int nk, n;
 
+    __device__ __forceinline__ const R* src(const R* rk, const R* rx, int i) const {
+        if (i < nk) return rk + (int64_t)i * XE;
+        const int t = i - nk, j = t / XCH;
+        return rx + (int64_t)j * DV + (t - j * XCH) * XE;
+    }
     __device__ __forceinline__ void issue(const R* rk, const R* rx, int w) {
         nk = w * KCH;
         n = nk + w * XCH;
+        if (n > 0) {  // uniform; loads clamped into range instead of predicated
 #pragma unroll
-        for (int u = 0; u < RC; ++u) {
-            const int i = u * NT + (int)threadIdx.x;
-            if (i < n)
-                buf[u] = i < nk ? reinterpret_cast<const u32x4*>(rk)[i]
-                                : reinterpret_cast<const u32x4*>(rx)[i - nk];
+            for (int u = 0; u < RC; ++u) buf[u] = ld_stream(src(rk, rx, min(u * NT + (int)threadIdx.x, n - 1)));
         }
     }
     __device__ __forceinline__ void commit(const R* rk, const R* rx, R* sk, R* sx) {
@@ -281,87 +309,131 @@ struct RecordCopy {
             }
         }
         for (int i = RC * NT + (int)threadIdx.x; i < n; i += NT) {
-            if (i < nk) reinterpret_cast<u32x4*>(sk)[i] = reinterpret_cast<const u32x4*>(rk)[i];
-            else reinterpret_cast<u32x4*>(sx)[i - nk] = reinterpret_cast<const u32x4*>(rx)[i - nk];
+            const u32x4 c = ld_stream(src(rk, rx, i));
+            if (i < nk) reinterpret_cast<u32x4*>(sk)[i] = c;
+            else reinterpret_cast<u32x4*>(sx)[i - nk] = c;
         }
     }
 };
 
-// Decay weights: thread j < w writes e_j = exp(base + sum_{j<l<w} lam_l);
-// thread w writes G = exp(base + sum_{l<w} lam_l) to sc[0].
-__device__ __forceinline__ void decay_weights(float* lam, float* e, float* sc, int w, float base) {
-    const int j = threadIdx.x;
-    if (j <= w) {
-        float acc = base;
-        for (int l = (j == w ? 0 : j + 1); l < w; ++l) acc += lam[l];
-        if (j < w) e[j] = expf(acc);
-        else sc[0] = expf(acc);
+// Decay weights by a suffix scan over the lanes of wave 0, lane j holding
+// lam_j for j < w (the buffer holds at most 63 records, so one wave covers
+// it):  lane j < w writes e[j] = exp(base + sum_{j<l<w} lam_l), lane 0 writes
+// sc[0] = G = exp(base + sum_{l<w} lam_l).  Every exponent is a sum of
+// log-decays (<= 0), never a ratio of products.
+__device__ __forceinline__ void decay_weights(float lam_j, float* e, float* sc, int w, float base) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        float s = lane < w ? lam_j : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {  // inclusive suffix sum over lanes >= lane
+            const float t = __shfl_down(s, off);
+            if (lane + off < 64) s += t;
+        }
+        float after = __shfl_down(s, 1);  // sum over lanes > lane
+        if (lane == 63) after = 0.f;
+        if (lane < w) e[lane] = expf(base + after);
+        if (lane == 0) sc[0] = expf(base + s);
+    }
+}
+
+// Cast N floats to the record type and store them (N * sizeof(R) bytes,
+// aligned to that size up to 16).
+template <class T, int N>
+__device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const float* in) {
+    using S = typename T::S;
+    constexpr int BYTES = N * (int)sizeof(S);
+    S tmp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) tmp[i] = from_f<T>(in[i]);
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+        for (int i = 0; i < BYTES / 16; ++i) {
+            u32x4 r;
+            __builtin_memcpy(&r, reinterpret_cast<const char*>(tmp) + 16 * i, 16);
+            reinterpret_cast<u32x4*>(p)[i] = r;
+        }
+    } else if constexpr (BYTES == 8) {
+        u32x2 r;
+        __builtin_memcpy(&r, tmp, 8);
+        *reinterpret_cast<u32x2*>(p) = r;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) p[i] = tmp[i];
     }
 }
 
 // ----------------------------------------------------- replay decode step --
-template <int FORM, int DV, int DK, class TS, class TR, class TI>
-__global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_step(const StepParams p) {
-    using T = Tile<DV, DK, TS>;
+// Order of work inside a workgroup:
+//   1. row metadata (flag loaded first, consumed last);
+//   2. small loads (token chunks, buffered decays and records), then the
+//      checkpoint stream, so that waiting for the small loads never waits for
+//      the stream;
+//   3. records to LDS, barrier; decay weights and record dot products while
+//      the checkpoint is still in flight; barrier;
+//   4. per-lane partial sums of G (C q) plus this lane's share of the record
+//      terms (lane c of a row's lane group takes records c, c + LPR, ...),
+//      then one lane-group reduction that yields the output rows directly;
+//   5. non-flush: append the record from registers; flush: fold and store.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT>
+__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(const StepParams p) {
+    using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
     using R = typename TR::S;
     using I = typename TI::S;
-    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR;
-    constexpr int NV = FORM == kGdn ? 2 * NR : NR;  // row sums per thread
+    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr int KEEP = FORM == kGdn ? 2 : 1;  // Gated DeltaNet keeps (C q, C k) of a row together
+    constexpr int NV = KEEP * NR;
 
-    const TileIds id = tile_ids(p);
+    const TileIds id = tile_ids<SPLIT>(p);
+    // Without a flag array the (always present) cursor array is read in its
+    // place and the result discarded, so that the load is unconditional.
+    const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
+    const bool flag = row_flag(fsrc, id.row) && p.flush;
     const int blk = p.block_table[id.row];
-    if (blk < 0) return;  // padding row
     const int w = p.write_pos[id.row];
-    if (blk >= p.n_blocks || w < 0 || w > p.slots) {
-        count_error(p);
+    const bool pad = blk < 0;
+    const bool bad = !pad && (blk >= p.n_blocks || w < 0 || w > p.slots);
+    if (pad || bad) {
+        if (bad) count_error(p);
         return;
     }
-    const bool fl = (w == p.slots) || (p.flush && p.flush[id.row]);
 
     const int tid = threadIdx.x;
     const int cc = tid % LPR;  // column chunk
     const int rg = tid / LPR;  // row within a pass
+    const int row0 = id.part * DVW;
 
     char* base = p.pool + (int64_t)blk * p.block_bytes;
-    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK);
-    R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV;
+    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     float* rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
     const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
     const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
-    const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
+    const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
     const float lam = p.lam[id.tile];
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const Lds<R> s = carve<DV, DK, R>(smem, p.slots, p.L);
+    const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
 
-    // Records first (small), then the checkpoint stream, then the token.
-    RecordCopy<DV, DK, R, NT, 2> rec;
-    rec.issue(rk, rx, w);
-    u32x4 cb[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        cb[r] = *reinterpret_cast<const u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     float qv[VEC], kv[VEC];
     load_f<TI, VEC>(qp + cc * VEC, qv);
     load_f<TI, VEC>(kp + cc * VEC, kv);
-    for (int i = tid; i < DV; i += NT) s.v[i] = to_f<TI>(vp[i]);
-    if (tid < w) s.lam[tid] = rl[tid];
+    const float vi = to_f<TI>(vp[min(tid, DVW - 1)]);
+    float lam_j = 0.f;
+    if (w > 0) lam_j = rl[min(tid, w - 1)];
+    RecordCopy<DV, DVW, DK, R, NT, 2> rec;
+    rec.issue(rk, rx, w);
+    u32x4 cb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
 
-    // Non-flush append of what does not depend on the state: lam and k for
-    // both forms, and v for Mamba-2 (Gated DeltaNet appends d further down).
-    if (!fl) {
-        for (int i = tid; i < DK; i += NT) rk[(int64_t)w * DK + i] = from_f<TR>(to_f<TI>(kp[i]));
-        if constexpr (FORM == kMamba2)
-            for (int i = tid; i < DV; i += NT) rx[(int64_t)w * DV + i] = from_f<TR>(to_f<TI>(vp[i]));
-        if (tid == 0) rl[w] = lam;
-    }
-
+    if (tid < DVW) s.v[tid] = vi;
     rec.commit(rk, rx, s.k, s.x);
     __syncthreads();
 
-    decay_weights(s.lam, s.e, s.sc, w, FORM == kMamba2 ? lam : 0.0f);
+    decay_weights(lam_j, s.e, s.sc, w, FORM == kMamba2 ? lam : 0.0f);
 
     // Record dot products: lane group rg takes records rg, rg + RPP, ...;
     // index w stands for the current token (k . q).
@@ -392,8 +464,10 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_step(const St
             }
         }
     }
+    __syncthreads();
 
-    // Checkpoint GEMV: C q (and C k for Gated DeltaNet) from one register copy.
+    const float G = s.sc[0];
+    const float kq = s.sc[1];
     float cf[NR][VEC];
 #pragma unroll
     for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
@@ -406,53 +480,71 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_step(const St
             a += cf[r][c] * qv[c];
             if constexpr (FORM == kGdn) b += cf[r][c] * kv[c];
         }
-        acc[r] = a;
-        if constexpr (FORM == kGdn) acc[NR + r] = b;
-    }
-    xsum<NV, LPR / 2>(acc, cc);
-    {
-        constexpr int left = xsum_left<NV, LPR>();
-        const int b0 = xsum_base<NV, LPR>(cc);
-        if ((cc & xsum_dup_mask<NV, LPR>()) == 0) {
-#pragma unroll
-            for (int i = 0; i < left; ++i) {
-                const int idx = b0 + i;
-                const int r = idx % NR;
-                float* dst = (FORM == kGdn && idx >= NR) ? s.yk : s.y;
-                dst[r * RPP + rg] = acc[i];
-            }
-        }
-    }
-    __syncthreads();
-
-    const float G = s.sc[0];
-    const float kq = s.sc[1];
-    const float alpha = expf(lam);  // used by Gated DeltaNet only
-    for (int i = tid; i < DV; i += NT) {
-        float* o = p.out + id.tile * DV;
         if constexpr (FORM == kMamba2) {
-            float acc_o = G * s.y[i];
-            for (int j = 0; j < w; ++j) acc_o += (s.e[j] * s.cq[j]) * to_f<TR>(s.x[(int64_t)j * DV + i]);
-            acc_o += kq * s.v[i];
-            o[i] = acc_o;
+            acc[r] = G * a;
         } else {
-            float aq = G * s.y[i], ak = G * s.yk[i];
-            for (int j = 0; j < w; ++j) {
-                const float xj = to_f<TR>(s.x[(int64_t)j * DV + i]);
-                aq += (s.e[j] * s.cq[j]) * xj;
-                ak += (s.e[j] * s.ck[j]) * xj;
+            acc[2 * r] = G * a;
+            acc[2 * r + 1] = G * b;
+        }
+    }
+    for (int j = cc; j < w; j += LPR) {
+        const float wq = s.e[j] * s.cq[j];
+        const float wk = FORM == kGdn ? s.e[j] * s.ck[j] : 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float xj = to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
+            if constexpr (FORM == kMamba2) {
+                acc[r] += wq * xj;
+            } else {
+                acc[2 * r] += wq * xj;
+                acc[2 * r + 1] += wk * xj;
             }
-            const float d = p.beta[id.tile] * (s.v[i] - alpha * ak);
-            o[i] = alpha * aq + kq * d;
-            if (fl) s.u[i] = d;
-            else rx[(int64_t)w * DV + i] = from_f<TR>(d);
+        }
+    }
+    if constexpr (FORM == kMamba2) {
+        if (cc == LPR - 1) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r] += kq * s.v[r * RPP + rg];
+        }
+    }
+    xsum<NV, LPR / 2, KEEP>(acc, cc);
+
+    const bool fl = (w == p.slots) || flag;
+    const float alpha = expf(lam);  // Gated DeltaNet only
+    float* o = p.out + id.tile * DV + row0;
+    {
+        constexpr int left = xsum_left<NV, LPR, KEEP>();
+        const int b0 = xsum_base<NV, LPR, KEEP>(cc);
+        if ((cc & xsum_dup_mask<NV, LPR, KEEP>()) == 0) {
+            if constexpr (FORM == kMamba2) {
+#pragma unroll
+                for (int i = 0; i < left; ++i) o[(b0 + i) * RPP + rg] = acc[i];
+            } else {
+                const float bt = p.beta[id.tile];
+#pragma unroll
+                for (int i = 0; i < left; i += 2) {
+                    const int row = ((b0 + i) / 2) * RPP + rg;
+                    const float d = bt * (s.v[row] - alpha * acc[i + 1]);
+                    o[row] = alpha * acc[i] + kq * d;
+                    if (fl) s.u[row] = d;
+                    else rx[(int64_t)w * DV + row] = from_f<TR>(d);
+                }
+            }
         }
     }
 
-    if (!fl) return;  // uniform across the workgroup
+    if (!fl) {  // uniform across the workgroup
+        if (id.part == 0) {
+            if (tid == 0) rl[w] = lam;
+            if (rg == 0) store_f<TR, VEC>(rk + (int64_t)w * DK + cc * VEC, kv);
+        }
+        if constexpr (FORM == kMamba2)
+            if (tid < DVW) rx[(int64_t)w * DV + tid] = from_f<TR>(vi);
+        return;
+    }
 
     // Flush: fold records and the current token into the registers holding
-    // the tile, store once.
+    // the owned rows, store once.
     //   Mamba-2:  C' = G C + sum_j e_j x_j k_j^T + v k^T
     //   GDN:      C' = alpha P C + sum_j alpha p_j d_j k_j^T + d k^T
     if constexpr (FORM == kGdn) __syncthreads();  // d in LDS
@@ -471,26 +563,26 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_step(const St
         const float ej = ge * s.e[j];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float f = ej * to_f<TR>(s.x[(int64_t)j * DV + r * RPP + rg]);
+            const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
 #pragma unroll
             for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
         }
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-        *reinterpret_cast<u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC) = pack16<TS>(cf[r]);
+    for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
 }
 
 // ------------------------------------------------ conventional decode step --
-template <int FORM, int DV, int DK, class TS, class TI>
-__global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_conventional_step(const StepParams p) {
-    using T = Tile<DV, DK, TS>;
+template <int FORM, int DV, int DK, class TS, class TI, int SPLIT>
+__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_step(const StepParams p) {
+    using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
     using I = typename TI::S;
-    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR;
-    constexpr int NV = FORM == kGdn ? 2 * NR : NR;
+    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr int KEEP = FORM == kGdn ? 2 : 1;
+    constexpr int NV = KEEP * NR;
 
-    const TileIds id = tile_ids(p);
+    const TileIds id = tile_ids<SPLIT>(p);
     const int blk = p.block_table[id.row];
     if (blk < 0) return;
     if (blk >= p.n_blocks) {
@@ -500,29 +592,34 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_conventional_step(co
     const int tid = threadIdx.x;
     const int cc = tid % LPR;
     const int rg = tid / LPR;
+    const int row0 = id.part * DVW;
 
     char* base = p.pool + (int64_t)blk * p.block_bytes;
-    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK);
+    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
     const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
-    const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
+    const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
 
-    __shared__ float s_y[DV], s_yk[DV], s_u[DV];
+    __shared__ float s_v[DVW], s_u[DVW];
 
-    u32x4 cb[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        cb[r] = *reinterpret_cast<const u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     float qv[VEC], kv[VEC];
     load_f<TI, VEC>(qp + cc * VEC, qv);
     load_f<TI, VEC>(kp + cc * VEC, kv);
+    const float vi = to_f<TI>(vp[min(tid, DVW - 1)]);
+    u32x4 cb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     const float alpha = expf(p.lam[id.tile]);
+    if (tid < DVW) s_v[tid] = vi;
 
     float kq = 0.f;
 #pragma unroll
     for (int c = 0; c < VEC; ++c) kq += kv[c] * qv[c];
     kq = group_sum<LPR>(kq);
+    __syncthreads();
 
+    // o = S_t q = alpha (S_{t-1} q) + (k . q) u, with u = v (Mamba-2) or the
+    // corrected value d = beta (v - alpha S_{t-1} k) (Gated DeltaNet).
     float cf[NR][VEC];
 #pragma unroll
     for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
@@ -535,57 +632,61 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_conventional_step(co
             a += cf[r][c] * qv[c];
             if constexpr (FORM == kGdn) b += cf[r][c] * kv[c];
         }
-        acc[r] = a;
-        if constexpr (FORM == kGdn) acc[NR + r] = b;
+        if constexpr (FORM == kMamba2) {
+            acc[r] = alpha * a;
+            if (cc == LPR - 1) acc[r] += kq * s_v[r * RPP + rg];
+        } else {
+            acc[2 * r] = a;
+            acc[2 * r + 1] = b;
+        }
     }
-    xsum<NV, LPR / 2>(acc, cc);
+    xsum<NV, LPR / 2, KEEP>(acc, cc);
+    float* o = p.out + id.tile * DV + row0;
     {
-        constexpr int left = xsum_left<NV, LPR>();
-        const int b0 = xsum_base<NV, LPR>(cc);
-        if ((cc & xsum_dup_mask<NV, LPR>()) == 0) {
+        constexpr int left = xsum_left<NV, LPR, KEEP>();
+        const int b0 = xsum_base<NV, LPR, KEEP>(cc);
+        if ((cc & xsum_dup_mask<NV, LPR, KEEP>()) == 0) {
+            if constexpr (FORM == kMamba2) {
 #pragma unroll
-            for (int i = 0; i < left; ++i) {
-                const int idx = b0 + i;
-                float* dst = (FORM == kGdn && idx >= NR) ? s_yk : s_y;
-                dst[(idx % NR) * RPP + rg] = acc[i];
+                for (int i = 0; i < left; ++i) o[(b0 + i) * RPP + rg] = acc[i];
+            } else {
+                const float bt = p.beta[id.tile];
+#pragma unroll
+                for (int i = 0; i < left; i += 2) {
+                    const int row = ((b0 + i) / 2) * RPP + rg;
+                    const float d = bt * (s_v[row] - alpha * acc[i + 1]);
+                    o[row] = alpha * acc[i] + kq * d;
+                    s_u[row] = d;
+                }
             }
         }
     }
-    __syncthreads();
-
-    // o = S_t q = alpha (S_{t-1} q) + (k . q) u, with u = v (Mamba-2) or the
-    // corrected value d = beta (v - alpha S_{t-1} k) (Gated DeltaNet).
-    for (int i = tid; i < DV; i += NT) {
-        const float vi = to_f<TI>(vp[i]);
-        float ui = vi;
-        if constexpr (FORM == kGdn) ui = p.beta[id.tile] * (vi - alpha * s_yk[i]);
-        p.out[id.tile * DV + i] = alpha * s_y[i] + kq * ui;
-        s_u[i] = ui;
-    }
-    __syncthreads();
+    if constexpr (FORM == kGdn) __syncthreads();  // d in LDS
 
     // S_t = alpha S_{t-1} + u k^T, stored every step.
+    const float* u = FORM == kMamba2 ? s_v : s_u;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const float ur = s_u[r * RPP + rg];
+        const float ur = u[r * RPP + rg];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) cf[r][c] = alpha * cf[r][c] + ur * kv[c];
-        *reinterpret_cast<u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC) = pack16<TS>(cf[r]);
+        st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
     }
 }
 
 // ------------------------------------------------------ token-less flush --
-template <int DV, int DK, class TS, class TR>
-__global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_flush(const StepParams p) {
-    using T = Tile<DV, DK, TS>;
+template <int DV, int DK, class TS, class TR, int SPLIT>
+__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(const StepParams p) {
+    using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
     using R = typename TR::S;
-    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR;
+    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
 
-    const TileIds id = tile_ids(p);
+    const TileIds id = tile_ids<SPLIT>(p);
+    const bool flag = row_flag(p.flush, id.row);
     const int blk = p.block_table[id.row];
-    if (blk < 0 || !p.flush[id.row]) return;
     const int w = p.write_pos[id.row];
+    if (blk < 0 || !flag) return;
     if (blk >= p.n_blocks || w < 0 || w > p.slots) {
         count_error(p);
         return;
@@ -595,25 +696,24 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_flush(const S
     const int tid = threadIdx.x;
     const int cc = tid % LPR;
     const int rg = tid / LPR;
+    const int row0 = id.part * DVW;
     char* base = p.pool + (int64_t)blk * p.block_bytes;
-    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK);
-    const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV;
+    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     const float* rl = reinterpret_cast<const float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const Lds<R> s = carve<DV, DK, R>(smem, p.slots, p.L);
+    const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
 
-    RecordCopy<DV, DK, R, NT, 2> rec;
+    const float lam_j = rl[min(tid, w - 1)];
+    RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
     u32x4 cb[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-        cb[r] = *reinterpret_cast<const u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
-    if (tid < w) s.lam[tid] = rl[tid];
+    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     rec.commit(rk, rx, s.k, s.x);
-    __syncthreads();
-    decay_weights(s.lam, s.e, s.sc, w, 0.0f);
+    decay_weights(lam_j, s.e, s.sc, w, 0.0f);
     __syncthreads();
 
     // C' = G C + sum_j e_j x_j k_j^T  with G = exp(sum_{l<w} lam_l).
@@ -631,34 +731,47 @@ __global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_replay_flush(const S
         const float ej = s.e[j];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float f = ej * to_f<TR>(s.x[(int64_t)j * DV + r * RPP + rg]);
+            const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
 #pragma unroll
             for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
         }
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-        *reinterpret_cast<u32x4*>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC) = pack16<TS>(cf[r]);
+    for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
 }
 
 // ------------------------------------------------------------ state reset --
-template <int DV, int DK, class TS>
-__global__ __launch_bounds__((Tile<DV, DK, TS>::NT)) void k_state_reset(const StepParams p) {
-    using T = Tile<DV, DK, TS>;
+template <int DV, int DK, class TS, int SPLIT>
+__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(const StepParams p) {
+    using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
-    constexpr int NT = T::NT, NR = T::NR;
-    const TileIds id = tile_ids(p);
+    constexpr int NT = T::NT, NR = T::NR, DVW = T::DVW;
+    const TileIds id = tile_ids<SPLIT>(p);
+    const bool m = row_flag(p.mask, id.row);
     const int blk = p.block_table[id.row];
-    if (blk < 0 || !p.mask[id.row]) return;
+    if (blk < 0 || !m) return;
     if (blk >= p.n_blocks) {
         count_error(p);
         return;
     }
     S* ck = reinterpret_cast<S*>(p.pool + (int64_t)blk * p.block_bytes + p.ckpt_off) +
-            (int64_t)id.head * (DV * DK);
+            (int64_t)id.head * (DV * DK) + (int64_t)id.part * DVW * DK;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < NR; ++r) reinterpret_cast<u32x4*>(ck)[r * NT + threadIdx.x] = z;
+    for (int r = 0; r < NR; ++r) st_stream(reinterpret_cast<u32x4*>(ck) + r * NT + threadIdx.x, z);
+}
+
+// How many workgroups share one (row, head) tile.  Measured on MI355X: a
+// read-modify-write stream is fastest at 16 KiB per workgroup; a read-only
+// stream is insensitive between 16 and 32 KiB.
+template <int KIND, int DV, int DK, class TS>
+constexpr int split_for() {
+    constexpr int tile_bytes = DV * DK * (int)sizeof(typename TS::S);
+    if constexpr (KIND == (int)Kind::ReplayStep) {
+        return tile_bytes >= 65536 ? 2 : 1;
+    } else {
+        return tile_bytes >= 65536 ? 4 : (tile_bytes >= 32768 ? 2 : 1);
+    }
 }
 
 // -------------------------------------------------------------- dispatch --
@@ -696,6 +809,11 @@ struct Dispatch {
     hipStream_t stream;
     hipError_t err = hipSuccess;
 
+    template <int SPLIT>
+    dim3 grid() const {
+        return dim3(p ? (unsigned)(p->n_heads * SPLIT) : 1u, p ? (unsigned)p->n_rows : 1u);
+    }
+
     bool run() {
         const int slots = L.L - 1;
         bool ok = false;
@@ -703,21 +821,24 @@ struct Dispatch {
             constexpr int DV = decltype(dv_c)::value, DK = decltype(dk_c)::value;
             with_state(L.state_dtype, [&](auto ts) {
                 using TS = decltype(ts);
-                using T = Tile<DV, DK, TS>;
-                const dim3 block(T::NT);
-                const dim3 grid(p ? (unsigned)((int64_t)p->n_rows * p->n_heads) : 1u);
                 if (kind == Kind::Reset) {
+                    constexpr int SP = split_for<(int)Kind::Reset, DV, DK, TS>();
                     ok = true;
-                    if (p) hipLaunchKernelGGL((k_state_reset<DV, DK, TS>), grid, block, 0, stream, *p);
+                    if (p)
+                        hipLaunchKernelGGL((k_state_reset<DV, DK, TS, SP>), grid<SP>(),
+                                           dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
                     return;
                 }
                 if (kind == Kind::ConventionalStep) {
+                    constexpr int SP = split_for<(int)Kind::ConventionalStep, DV, DK, TS>();
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
                         with_io(L.io_dtype, [&](auto ti) {
                             using TI = decltype(ti);
                             ok = true;
-                            if (p) hipLaunchKernelGGL((k_conventional_step<FORM, DV, DK, TS, TI>), grid, block, 0, stream, *p);
+                            if (p)
+                                hipLaunchKernelGGL((k_conventional_step<FORM, DV, DK, TS, TI, SP>), grid<SP>(),
+                                                   dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
                         });
                     });
                     return;
@@ -725,18 +846,25 @@ struct Dispatch {
                 with_record(L.record_dtype, [&](auto tr) {
                     using TR = decltype(tr);
                     using R = typename TR::S;
-                    const size_t lds = lds_need<DV, DK, R>(slots, L.L);
                     if (kind == Kind::Flush) {
+                        constexpr int SP = split_for<(int)Kind::Flush, DV, DK, TS>();
+                        const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                         ok = true;
-                        if (p) hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR>), grid, block, lds, stream, *p);
+                        if (p)
+                            hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR, SP>), grid<SP>(),
+                                               dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
                         return;
                     }
+                    constexpr int SP = split_for<(int)Kind::ReplayStep, DV, DK, TS>();
+                    const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
                         with_io(L.io_dtype, [&](auto ti) {
                             using TI = decltype(ti);
                             ok = true;
-                            if (p) hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI>), grid, block, lds, stream, *p);
+                            if (p)
+                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP>), grid<SP>(),
+                                                   dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
                         });
                     });
                 });
@@ -749,11 +877,12 @@ struct Dispatch {
 
 }  // namespace
 
+// Upper bound over the splits (a workgroup owning all d_v rows).
 size_t lds_bytes(Kind kind, const rs_layer& layer) {
     if (kind != Kind::ReplayStep && kind != Kind::Flush) return 0;
     const int slots = layer.L - 1;
     const size_t rb = layer.record_dtype == RS_F32 ? 4 : 2;
-    return (size_t)slots * (layer.d_k + layer.d_v) * rb + sizeof(float) * (4 * (size_t)layer.L + 4 * layer.d_v + 4);
+    return (size_t)slots * (layer.d_k + layer.d_v) * rb + sizeof(float) * (3 * (size_t)layer.L + 2 * layer.d_v + 4);
 }
 
 bool compiled(Kind kind, const rs_layer& layer) {
