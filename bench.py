@@ -205,6 +205,79 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     }
 
 
+def calibrate_copy(mib: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, three times: its
+    FETCH_SIZE / WRITE_SIZE readings give the scale of those counters."""
+    import torch
+    n = mib * 2**20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _read_counter_csv(path):
+    """Per-dispatch counter values from a rocprofv3 counter_collection.csv:
+    returns [(kernel_name, counter_name, value)]."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("kernel_name") or ""
+            cname = r.get("Counter_Name") or r.get("Counter-Name") or ""
+            val = r.get("Counter_Value") or r.get("Counter-Value") or "0"
+            rows.append((name, cname, float(val)))
+    return rows
+
+
+def summarize_counters(args, fetch_csv, write_csv):
+    """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
+    (known bytes of the calibration copy) / (its reading), then averaged per
+    launch of the checkpoint + buffer kernel and of the conventional kernel."""
+    out = {}
+    mib = args.calibrate_copy
+    if not mib:
+        raise SystemExit("--summarize-counters needs --calibrate-copy MIB (the size used in the profiled run)")
+    res = {}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        per = {}
+        for name, cname, val in _read_counter_csv(path):
+            per.setdefault(name, []).append(val)
+        # the calibration copy is the largest copy dispatch of the run (three of them)
+        copy = sorted((v for n, vs in per.items() if "copy" in n.lower() and "rs::" not in n for v in vs),
+                      reverse=True)[:3]
+        if not copy or copy[-1] * 1024 < 0.25 * mib * 2**20:
+            raise SystemExit(f"no calibration copy of ~{mib} MiB found in {path}")
+        scale = mib * 2**20 / (float(np.median(copy)) * 1024)
+        res[label] = {"scale": scale,
+                      "replay": float(np.mean([v for n, vs in per.items() if "k_replay_step" in n for v in vs])) * 1024 * scale,
+                      "conventional": float(np.mean([v for n, vs in per.items() if "k_conventional_step" in n for v in vs])) * 1024 * scale}
+    cfg = dict(WORKLOADS[args.workload])
+    if args.batch:
+        cfg["B"] = args.batch
+    if args.L:
+        cfg["L"] = args.L
+    if args.state:
+        cfg["state"] = args.state
+    key = f"{args.workload}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    entry = {"kernel_source": kernel_source_hash(),
+             "bytes_per_launch": round(res["fetch"]["replay"] + res["write"]["replay"]),
+             "replay": {"fetch": round(res["fetch"]["replay"]), "write": round(res["write"]["replay"])},
+             "conventional": {"fetch": round(res["fetch"]["conventional"]), "write": round(res["write"]["conventional"]),
+                              "bytes_per_launch": round(res["fetch"]["conventional"] + res["write"]["conventional"])},
+             "scale": {"fetch": round(res["fetch"]["scale"], 4), "write": round(res["write"]["scale"], 4)},
+             "calibration_copy_mib": mib}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[key] = entry
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({key: entry}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,7 +290,14 @@ def main(argv=None):
     ap.add_argument("--pools", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (scale for rocprofv3 byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
+                         "into per-launch HBM bytes in profiles/counters.json and print them; runs nothing on the GPU")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        return summarize_counters(args, *args.summarize_counters)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step exchanges no data between GPUs, so each "
@@ -232,6 +312,8 @@ def main(argv=None):
     if args.state:
         cfg["state"] = args.state
 
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
     rep = run_gpu(cfg, args.steps, args.warmup, args.pools, "replay")
     conv = run_gpu(cfg, args.steps, args.warmup, args.pools, "conventional")
 

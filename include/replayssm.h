@@ -126,6 +126,12 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               NULL (no forced flushes).
  *   err_count   optional (may be NULL): incremented once per (row, head) tile
  *               skipped because its block id or cursor was out of range.
+ *   next_write_pos  optional (may be NULL), replay_decode_step only: receives
+ *               each non-padding row's cursor for the next step, 0 after a
+ *               flush and write_pos + 1 otherwise (the host rule of
+ *               rs_meta_advance).  Passing it as the next step's write_pos
+ *               lets a caller skip the per-step host -> device copy while
+ *               the batch is unchanged.  Must not alias write_pos.
  */
 typedef struct {
     int32_t n_rows;
@@ -136,6 +142,7 @@ typedef struct {
     const int32_t* write_pos;
     const uint8_t* flush;
     int32_t* err_count;
+    int32_t* next_write_pos;
 } rs_batch;
 
 /*

@@ -46,7 +46,7 @@ class RsBlockLayout(_c.Structure):
 class RsBatch(_c.Structure):
     _fields_ = [("n_rows", _c.c_int32), ("reserved", _c.c_int32), ("n_blocks", _c.c_int64),
                 ("pool", _vp), ("block_table", _vp), ("write_pos", _vp), ("flush", _vp),
-                ("err_count", _vp)]
+                ("err_count", _vp), ("next_write_pos", _vp)]
 
 
 class RsStepIO(_c.Structure):
@@ -128,12 +128,13 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def make_batch(pool, n_blocks: int, block_table, write_pos=None, flush=None, err_count=None) -> RsBatch:
-    """pool: uint8 device tensor; block_table/write_pos: int32 [n_rows];
-    flush: uint8 [n_rows]; err_count: int32 [1].  The tensors must outlive
-    the launches that use the returned struct."""
+def make_batch(pool, n_blocks: int, block_table, write_pos=None, flush=None, err_count=None,
+               next_write_pos=None) -> RsBatch:
+    """pool: uint8 device tensor; block_table/write_pos/next_write_pos: int32
+    [n_rows]; flush: uint8 [n_rows]; err_count: int32 [1].  The tensors must
+    outlive the launches that use the returned struct."""
     return RsBatch(int(block_table.numel()), 0, int(n_blocks), _ptr(pool), _ptr(block_table),
-                   _ptr(write_pos), _ptr(flush), _ptr(err_count))
+                   _ptr(write_pos), _ptr(flush), _ptr(err_count), _ptr(next_write_pos))
 
 
 def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:

@@ -83,6 +83,10 @@ int check_batch(const rs_layer& L, const rs_batch* b, bool needs_cursor, bool ne
     if (needs_flush && !b->flush) return fail(RS_EINVAL, "flush is NULL");
     if (b->flush && !aligned(b->flush, 4)) return fail(RS_EINVAL, "flush must be 4-byte aligned");
     if (b->err_count && !aligned(b->err_count, 4)) return fail(RS_EINVAL, "err_count is misaligned");
+    if (b->next_write_pos && !aligned(b->next_write_pos, 4))
+        return fail(RS_EINVAL, "next_write_pos must be 4-byte aligned");
+    if (b->next_write_pos && b->next_write_pos == b->write_pos)
+        return fail(RS_EINVAL, "next_write_pos must not alias write_pos");
     return RS_OK;
 }
 
@@ -133,6 +137,7 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.write_pos = b.write_pos;
     p.flush = b.flush;
     p.err = b.err_count;
+    p.next_wp = nullptr;
     p.n_rows = b.n_rows;
     p.n_heads = L.n_heads;
     p.L = L.L;
@@ -189,6 +194,7 @@ int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_st
     if ((rc = check_io(*layer, *batch, io))) return rc;
     if (batch->n_rows == 0) return ok();
     rs::StepParams p = params(*layer, *batch);
+    p.next_wp = batch->next_write_pos;
     set_io(p, *io);
     return do_launch(rs::Kind::ReplayStep, *layer, p, stream);
 }

@@ -21,6 +21,7 @@ struct StepParams {
     const uint8_t* flush;   // per-row flag (replay step, token-less flush)
     const uint8_t* mask;    // per-row mask (state reset)
     int32_t* err;
+    int32_t* next_wp;       // replay step: next cursor per row (optional)
     const void* q;
     const void* k;
     const void* v;

@@ -510,6 +510,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     xsum<NV, LPR / 2, KEEP>(acc, cc);
 
     const bool fl = (w == p.slots) || flag;
+    if (p.next_wp && id.head == 0 && id.part == 0 && tid == 0) p.next_wp[id.row] = fl ? 0 : w + 1;
     const float alpha = expf(lam);  // Gated DeltaNet only
     float* o = p.out + id.tile * DV + row0;
     {
@@ -761,17 +762,15 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(c
     for (int r = 0; r < NR; ++r) st_stream(reinterpret_cast<u32x4*>(ck) + r * NT + threadIdx.x, z);
 }
 
-// How many workgroups share one (row, head) tile.  Measured on MI355X: a
-// read-modify-write stream is fastest at 16 KiB per workgroup; a read-only
-// stream is insensitive between 16 and 32 KiB.
-template <int KIND, int DV, int DK, class TS>
+// How many workgroups share one (row, head) tile: at most 8192 state elements
+// (32 floats per thread at 256 threads) per workgroup.  Measured on MI355X:
+// with more, the extra registers cost occupancy (Gated DeltaNet's fp16 128x128
+// tile: 5.2 TB/s unsplit, 5.8 TB/s split in two); below it, splitting further
+// only repeats the record dot products.
+template <int DV, int DK>
 constexpr int split_for() {
-    constexpr int tile_bytes = DV * DK * (int)sizeof(typename TS::S);
-    if constexpr (KIND == (int)Kind::ReplayStep) {
-        return tile_bytes >= 65536 ? 2 : 1;
-    } else {
-        return tile_bytes >= 65536 ? 4 : (tile_bytes >= 32768 ? 2 : 1);
-    }
+    constexpr int s = DV * DK / 8192;
+    return s < 1 ? 1 : s;
 }
 
 // -------------------------------------------------------------- dispatch --
@@ -822,7 +821,7 @@ struct Dispatch {
             with_state(L.state_dtype, [&](auto ts) {
                 using TS = decltype(ts);
                 if (kind == Kind::Reset) {
-                    constexpr int SP = split_for<(int)Kind::Reset, DV, DK, TS>();
+                    constexpr int SP = split_for<DV, DK>();
                     ok = true;
                     if (p)
                         hipLaunchKernelGGL((k_state_reset<DV, DK, TS, SP>), grid<SP>(),
@@ -830,7 +829,7 @@ struct Dispatch {
                     return;
                 }
                 if (kind == Kind::ConventionalStep) {
-                    constexpr int SP = split_for<(int)Kind::ConventionalStep, DV, DK, TS>();
+                    constexpr int SP = split_for<DV, DK>();
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
                         with_io(L.io_dtype, [&](auto ti) {
@@ -847,7 +846,7 @@ struct Dispatch {
                     using TR = decltype(tr);
                     using R = typename TR::S;
                     if (kind == Kind::Flush) {
-                        constexpr int SP = split_for<(int)Kind::Flush, DV, DK, TS>();
+                        constexpr int SP = split_for<DV, DK>();
                         const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                         ok = true;
                         if (p)
@@ -855,7 +854,7 @@ struct Dispatch {
                                                dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
                         return;
                     }
-                    constexpr int SP = split_for<(int)Kind::ReplayStep, DV, DK, TS>();
+                    constexpr int SP = split_for<DV, DK>();
                     const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;

@@ -9,14 +9,17 @@ last anchored), and drives the C ABI once per step:
      SSM inputs for faster Gated DeltaNet standard decode", section "CUDA
      graphs and continuous batching": position = steps since anchor mod L,
      flush at position L-1 or when forced);
-  2. the block table, positions and flags are copied host -> device
-     asynchronously from pinned staging buffers (no device -> host sync);
-  3. one kernel launch serves flush and non-flush rows alike;
-  4. ``rs_meta_advance`` re-anchors the rows that flushed.
+  2. one kernel launch serves flush and non-flush rows alike;
+  3. ``rs_meta_advance`` re-anchors the rows that flushed.
 
-A ring of staging buffers lets the host run several steps ahead of the
-device; a buffer is reused only after the event recorded behind its copy
-has completed.
+The device keeps its own copy of the cursors: each replay step writes every
+row's next cursor (0 after a flush, else w + 1, the rule of step 3) into the
+second of two cursor arrays, and the next step reads it.  Host and device
+therefore stay equal by construction, and the host copies metadata to the
+device (one asynchronous copy from pinned memory, no device -> host sync)
+only when it changes: a slot joins or retires, a flush is forced (and on the
+step after, to clear the flag), or rows are re-anchored.  In steady decoding
+a step is a single kernel launch.
 """
 from __future__ import annotations
 
@@ -27,12 +30,30 @@ from . import (Pool, RsLayer, conventional_decode_step, make_batch, replay_decod
                replay_flush, replay_state_reset, rs_meta_advance, rs_meta_step)
 
 
+def _layout(n: int):
+    """Byte offsets of the per-row arrays in one metadata buffer, each 4-byte
+    aligned: block_table int32, flush uint8, mask uint8, cursor0 int32,
+    cursor1 int32."""
+    n4 = (n + 3) // 4 * 4
+    off = {"bt": 0, "fl": 4 * n, "mk": 4 * n + n4, "c0": 4 * n + 2 * n4, "c1": 8 * n + 2 * n4}
+    return off, 12 * n + 2 * n4
+
+
+def _views(buf: torch.Tensor, n: int):
+    off, _ = _layout(n)
+    return (buf[off["bt"]:off["bt"] + 4 * n].view(torch.int32), buf[off["fl"]:off["fl"] + n],
+            buf[off["mk"]:off["mk"] + n], buf[off["c0"]:off["c0"] + 4 * n].view(torch.int32),
+            buf[off["c1"]:off["c1"] + 4 * n].view(torch.int32))
+
+
 class _Stage:
+    """Pinned host image of the metadata buffer (one upload in flight)."""
+
     def __init__(self, n: int):
-        self.wp = torch.zeros(n, dtype=torch.int32, pin_memory=True)
-        self.fl = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
-        self.bt = torch.zeros(n, dtype=torch.int32, pin_memory=True)
-        self.mask = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
+        _, size = _layout(n)
+        self.buf = torch.zeros(size, dtype=torch.uint8, pin_memory=True)
+        self.bt, self.fl, self.mk, c0, c1 = (t.numpy() for t in _views(self.buf, n))
+        self.c = (c0, c1)
         self.event = None
 
 
@@ -41,21 +62,25 @@ class DecodeLayer:
                  staging: int = 4):
         self.layer = lay
         self.L = int(lay.L)
-        self.n_slots = int(n_slots)
+        self.n_slots = n = int(n_slots)
         self.pool = Pool(lay, n_blocks or n_slots, device)
         self.device = self.pool.raw.device
-        self.anchor = np.full(self.n_slots, -1, np.int32)   # -1: empty slot (padding row)
-        self.blocks = np.full(self.n_slots, -1, np.int32)
-        dev = self.device
-        self.block_table = torch.full((self.n_slots,), -1, dtype=torch.int32, device=dev)
-        self.write_pos = torch.zeros(self.n_slots, dtype=torch.int32, device=dev)
-        self.flush = torch.zeros(self.n_slots, dtype=torch.uint8, device=dev)
-        self.mask = torch.zeros(self.n_slots, dtype=torch.uint8, device=dev)
-        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        self._stages = [_Stage(self.n_slots) for _ in range(staging)]
+        self.anchor = np.full(n, -1, np.int32)   # -1: empty slot (padding row)
+        self.blocks = np.full(n, -1, np.int32)
+        _, size = _layout(n)
+        self.meta = torch.zeros(size, dtype=torch.uint8, device=self.device)
+        self.block_table, self.flush, self.mask, c0, c1 = _views(self.meta, n)
+        self.cursor = (c0, c1)
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        # batch[i] reads cursor i and writes the next cursors into cursor 1-i
+        self.batch = [make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.cursor[i],
+                                 self.flush, self.err, next_write_pos=self.cursor[1 - i]) for i in (0, 1)]
+        self._cur = 0
+        self._stages = [_Stage(n) for _ in range(staging)]
         self._next = 0
-        self.batch = make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.write_pos,
-                                self.flush, self.err)
+        self._dirty = True          # device metadata differs from the host's
+        self._forced_last = False   # the device flag array holds forced flags
+        self.uploads = 0
 
     # ---------------------------------------------------------- bookkeeping --
     def assign(self, slot: int, block: int, steps_since_anchor: int = 0) -> None:
@@ -64,33 +89,45 @@ class DecodeLayer:
             raise ValueError(f"block {block} outside the pool of {self.pool.n_blocks}")
         self.blocks[slot] = block
         self.anchor[slot] = steps_since_anchor
+        self._dirty = True
 
     def retire(self, slot: int) -> None:
         self.blocks[slot] = -1
         self.anchor[slot] = -1
+        self._dirty = True
 
     def live(self) -> np.ndarray:
         return self.blocks >= 0
 
+    def device_cursor(self) -> np.ndarray:
+        """The device's cursors for the next step (synchronises; for tests)."""
+        torch.cuda.synchronize(self.device)
+        return self.cursor[self._cur].cpu().numpy()
+
     # ------------------------------------------------------------- transfers --
-    def _upload(self, stream, wp=None, fl=None, mask=None) -> None:
+    def _upload(self, stream, wp, flags=None, mask=None) -> None:
+        """One async host -> device copy of block table, flags, mask and the
+        current cursor array."""
         st = self._stages[self._next]
         self._next = (self._next + 1) % len(self._stages)
         if st.event is not None:
-            st.event.synchronize()
-        st.bt.numpy()[:] = self.blocks
+            st.event.synchronize()  # the previous copy out of this buffer is done
+        st.bt[:] = self.blocks
+        st.fl[:] = 0 if flags is None else flags
+        st.mk[:] = 0 if mask is None else mask
+        st.c[self._cur][:] = wp
+        off, _ = _layout(self.n_slots)
         with torch.cuda.stream(stream):
-            self.block_table.copy_(st.bt, non_blocking=True)
-            if wp is not None:
-                st.wp.numpy()[:] = wp
-                st.fl.numpy()[:] = fl
-                self.write_pos.copy_(st.wp, non_blocking=True)
-                self.flush.copy_(st.fl, non_blocking=True)
-            if mask is not None:
-                st.mask.numpy()[:] = mask
-                self.mask.copy_(st.mask, non_blocking=True)
+            if self._cur == 0:
+                end = off["c1"]
+                self.meta[:end].copy_(st.buf[:end], non_blocking=True)
+            else:
+                self.meta[:off["c0"]].copy_(st.buf[:off["c0"]], non_blocking=True)
+                end = off["c1"] + 4 * self.n_slots
+                self.meta[off["c1"]:end].copy_(st.buf[off["c1"]:end], non_blocking=True)
             st.event = torch.cuda.Event()
             st.event.record(stream)
+        self.uploads += 1
 
     # ----------------------------------------------------------------- steps --
     def step(self, io, force: np.ndarray | None = None, stream=None, events=None):
@@ -99,21 +136,33 @@ class DecodeLayer:
         recorded on the stream right around the kernel launch."""
         stream = stream or torch.cuda.current_stream(self.device)
         wp, fl = rs_meta_step(self.L, self.anchor, force)
-        self._upload(stream, wp, fl)
+        forced = None
+        if force is not None:
+            forced = (np.asarray(force, bool) & self.live()).astype(np.uint8)
+            if not forced.any():
+                forced = None
+        if self._dirty or forced is not None or self._forced_last:
+            self._upload(stream, wp, forced)
+            self._forced_last = forced is not None
+            self._dirty = False
         if events:
             events[0].record(stream)
-        replay_decode_step(self.layer, self.batch, io, stream)
+        replay_decode_step(self.layer, self.batch[self._cur], io, stream)
         if events:
             events[1].record(stream)
+        self._cur ^= 1
         rs_meta_advance(self.L, self.anchor, fl)
         return wp, fl
 
     def conventional_step(self, io, stream=None, events=None) -> None:
         stream = stream or torch.cuda.current_stream(self.device)
-        self._upload(stream)
+        if self._dirty:
+            wp, _ = rs_meta_step(self.L, self.anchor)
+            self._upload(stream, wp)
+            self._dirty = False
         if events:
             events[0].record(stream)
-        conventional_decode_step(self.layer, self.batch, io, stream)
+        conventional_decode_step(self.layer, self.batch[self._cur], io, stream)
         if events:
             events[1].record(stream)
 
@@ -126,8 +175,9 @@ class DecodeLayer:
         sel &= self.live()
         wp, _ = rs_meta_step(self.L, self.anchor)
         self._upload(stream, wp, sel.astype(np.uint8))
-        replay_flush(self.layer, self.batch, stream)
+        replay_flush(self.layer, self.batch[self._cur], stream)
         self.anchor[sel] = 0
+        self._dirty = True
 
     def reset_rows(self, rows, stream=None) -> None:
         """Zero the checkpoint of the given slots (new requests) and anchor
@@ -136,6 +186,8 @@ class DecodeLayer:
         sel = np.zeros(self.n_slots, bool)
         sel[np.asarray(rows, dtype=np.int64)] = True
         sel &= self.live()
-        self._upload(stream, mask=sel.astype(np.uint8))
-        replay_state_reset(self.layer, self.batch, self.mask, stream)
+        wp, _ = rs_meta_step(self.L, self.anchor)
+        self._upload(stream, wp, mask=sel.astype(np.uint8))
+        replay_state_reset(self.layer, self.batch[self._cur], self.mask, stream)
         self.anchor[sel] = 0
+        self._dirty = True

@@ -135,8 +135,12 @@ def run_case(c: Case, dev="cuda") -> dict:
         if conv is not None:
             out_c = torch.full((c.B, c.H, c.dv), float("nan"), device=dev)
             conv.conventional_step(rs.make_io(q, k, v, lam, out_c, beta))
-        # host metadata is bit-exact against the oracle's cursor
+        # host metadata is bit-exact against the oracle's cursor, and the
+        # cursors the kernel wrote for the next step equal the host's
         assert wp[0] == want_w[s] and bool(fl[0]) == bool(want_f[s]), (s, wp[0], fl[0])
+        nxt = rep.device_cursor()
+        lv = rep.live()
+        assert np.array_equal(nxt[lv], rep.anchor[lv] % c.L), f"device cursor, step {s}"
         for b in live_rows[1:]:
             assert wp[b] == s % c.L and bool(fl[b]) == (s % c.L == c.L - 1), (s, b)
         for b in c.pad_rows:
