@@ -7,8 +7,9 @@ Default workload: one Mamba-2 layer at the Nemotron-3-Super shape (128 heads,
 d_v=64, d_k=128, fp32 state, 4 MiB per sequence), batch 256, L=16, bf16
 v/k/q, fp16 records, fp32 log-decay.  A step is one pass of the whole hot
 path over the batch: host cursor/flush metadata, its async upload, and one
-kernel launch that serves flush and non-flush rows.  K defaults to 64 (four
-windows of 16 tokens) after W=16 warm-up steps.
+kernel launch that serves flush and non-flush rows.  K defaults to 64 after
+W=64 warm-up steps: with 4 state pools in rotation both are exactly one
+window of 16 tokens per pool, so every cursor position is weighted equally.
 
 Inputs are seeded synthetic tensors (16 distinct token batches, cycled),
 resident in HBM before the timed region.  P independent state pools (default
@@ -282,7 +283,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="nemotron", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--L", type=int, default=None)

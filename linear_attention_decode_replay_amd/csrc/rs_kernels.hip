@@ -224,8 +224,9 @@ __device__ __forceinline__ bool row_flag(const uint8_t* flags, int row) {
     return ((word >> (8 * (row & 3))) & 0xffu) != 0;
 }
 
-__device__ __forceinline__ void count_error(const StepParams& p) {
-    if (threadIdx.x == 0 && p.err) atomicAdd(p.err, 1);
+// Counted once per (row, head) tile, by the workgroup owning its first rows.
+__device__ __forceinline__ void count_error(const StepParams& p, const TileIds& id) {
+    if (threadIdx.x == 0 && id.part == 0 && p.err) atomicAdd(p.err, 1);
 }
 
 // Streamed state and records are read or written once per step and are far
@@ -395,7 +396,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     const bool pad = blk < 0;
     const bool bad = !pad && (blk >= p.n_blocks || w < 0 || w > p.slots);
     if (pad || bad) {
-        if (bad) count_error(p);
+        if (bad) count_error(p, id);
         return;
     }
 
@@ -587,7 +588,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
     const int blk = p.block_table[id.row];
     if (blk < 0) return;
     if (blk >= p.n_blocks) {
-        count_error(p);
+        count_error(p, id);
         return;
     }
     const int tid = threadIdx.x;
@@ -689,7 +690,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(
     const int w = p.write_pos[id.row];
     if (blk < 0 || !flag) return;
     if (blk >= p.n_blocks || w < 0 || w > p.slots) {
-        count_error(p);
+        count_error(p, id);
         return;
     }
     if (w == 0) return;  // nothing buffered: the checkpoint is the state
@@ -752,7 +753,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(c
     const int blk = p.block_table[id.row];
     if (blk < 0 || !m) return;
     if (blk >= p.n_blocks) {
-        count_error(p);
+        count_error(p, id);
         return;
     }
     S* ck = reinterpret_cast<S*>(p.pool + (int64_t)blk * p.block_bytes + p.ckpt_off) +
