@@ -206,6 +206,133 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     }
 
 
+# ------------------------------------------------------------------- suite --
+def _inputs(cfg, B, n, dev, seed=11):
+    import linear_attention_decode_replay_amd as rs
+    import torch
+    import workloads
+    ios, keep = [], []
+    for s in range(n):
+        t = workloads.tokens(cfg["form"], seed, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
+        q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
+        beta = t.beta.to(dev) if t.beta is not None else None
+        out = torch.empty((B, cfg["H"], cfg["dv"]), dtype=torch.float32, device=dev)
+        keep.append((q, k, v, lam, beta, out))
+        ios.append(rs.make_io(q, k, v, lam, out, beta))
+    return ios, keep
+
+
+def _layer_stack(cfg, B, n_layers, dev):
+    import linear_attention_decode_replay_amd as rs
+    from linear_attention_decode_replay_amd.state import DecodeLayer
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"])
+    layers = []
+    for _ in range(n_layers):
+        d = DecodeLayer(lay, B, B, dev)
+        for b in range(B):
+            d.assign(b, b)
+        d.reset_rows(range(B))
+        layers.append(d)
+    return layers
+
+
+def suite_gdn_sweep(out, steps=32):
+    """Gated DeltaNet, 32 heads, 128x128, L=16: replay vs conventional kernel
+    time per launch over batch sizes, fp32 and fp16 state.  A 512 MiB write
+    between launches (outside the timed events) leaves every launch cold."""
+    import torch
+    dev = torch.device("cuda", 0)
+    scrub = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+    for state in ("f32", "f16"):
+        for B in (1, 8, 32, 128, 256, 512):
+            cfg = dict(WORKLOADS["gdn"], B=B, state=state)
+            ios, keep = _inputs(cfg, B, 16, dev)
+            res = {}
+            for kind in ("replay", "conventional"):
+                d = _layer_stack(cfg, B, 1, dev)[0]
+                times, nbytes = [], []
+                for s in range(16 + steps):
+                    scrub.fill_(s & 0xff)
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    if kind == "replay":
+                        wp, fl = d.step(ios[s % 16], events=ev)
+                        w, f = int(wp[0]), bool(fl[0])
+                    else:
+                        d.conventional_step(ios[s % 16], events=ev)
+                        w, f = 0, False
+                    if s >= 16:
+                        times.append(ev)
+                        nbytes.append(step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, state, cfg["rec"],
+                                                 cfg["io"], w, f, kind))
+                torch.cuda.synchronize()
+                us = float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e3
+                res[kind] = {"us": round(us, 2), "tbs": round(float(np.mean(nbytes)) / (us * 1e-6) / 1e12, 3)}
+                del d
+            line = {"suite": "gdn_batch_sweep", "state": state, "batch": B, "L": 16,
+                    "replay_us": res["replay"]["us"], "replay_tbs": res["replay"]["tbs"],
+                    "conventional_us": res["conventional"]["us"], "conventional_tbs": res["conventional"]["tbs"],
+                    "speedup": round(res["conventional"]["us"] / res["replay"]["us"], 3)}
+            print(json.dumps(line), file=out, flush=True)
+            del ios, keep
+            torch.cuda.empty_cache()
+
+
+def suite_stack(out, n_layers=40):
+    """40 Mamba-2 layers at the Nemotron-3-Super shape, batch 256: time and
+    algorithmic bytes of one decode step over all layers (one launch per
+    layer), replay for L in {8, 16, 32} with fp32 and fp16 checkpoints, and
+    the conventional step with fp32 and fp16 state.  Two windows timed after
+    one window of warm-up."""
+    import torch
+    dev = torch.device("cuda", 0)
+    base = dict(WORKLOADS["nemotron"])
+    ios, keep = _inputs(base, base["B"], 16, dev)
+    results = {}
+    runs = [("conventional", 16, "f32"), ("conventional", 16, "f16")]
+    runs += [("replay", L, st) for st in ("f32", "f16") for L in (8, 16, 32)]
+    for kind, L, state in runs:
+        cfg = dict(base, L=L, state=state)
+        layers = _layer_stack(cfg, base["B"], n_layers, dev)
+        n_warm, n_time = L, 2 * L
+        nbytes = 0
+        for s in range(n_warm + n_time):
+            if s == n_warm:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            for li, d in enumerate(layers):
+                io = ios[(s + li) % 16]
+                if kind == "replay":
+                    wp, fl = d.step(io)
+                    w, f = int(wp[0]), bool(fl[0])
+                else:
+                    d.conventional_step(io)
+                    w, f = 0, False
+                if s >= n_warm:
+                    nbytes += step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], state, cfg["rec"],
+                                         cfg["io"], w, f, kind)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / n_time
+        gb = nbytes / n_time / 1e9
+        results[(kind, L, state)] = ms
+        line = {"suite": "stack40", "kind": kind, "L": L if kind == "replay" else None, "state": state,
+                "ms_per_step": round(ms, 3), "wall_ms_per_step": round(1e3 * wall / n_time, 3),
+                "gb_per_step": round(gb, 3), "tbs": round(gb / ms, 3)}
+        print(json.dumps(line), file=out, flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    for (kind, L, state), ms in results.items():
+        if kind == "replay":
+            line = {"suite": "stack40_ratio", "L": L, "state": state,
+                    "speedup_vs_conventional_f32": round(results[("conventional", 16, "f32")] / ms, 3),
+                    "speedup_vs_conventional_f16": round(results[("conventional", 16, "f16")] / ms, 3)}
+            print(json.dumps(line), file=out, flush=True)
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain device-to-device copy of `mib` MiB, three times: its
     FETCH_SIZE / WRITE_SIZE readings give the scale of those counters."""
@@ -293,12 +420,24 @@ def main(argv=None):
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (scale for rocprofv3 byte counters)")
+    ap.add_argument("--suite", metavar="PATH",
+                    help="instead of the one-line benchmark, run the Gated DeltaNet batch sweep and the "
+                         "40-layer stack and write JSON lines to PATH")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                          "into per-launch HBM bytes in profiles/counters.json and print them; runs nothing on the GPU")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         return summarize_counters(args, *args.summarize_counters)
+    if args.suite:
+        if args.gpus != 1:
+            print("the suite runs on one GPU", file=sys.stderr)
+            return 2
+        with open(args.suite, "w") as out:
+            suite_gdn_sweep(out)
+            suite_stack(out)
+        print(open(args.suite).read(), end="")
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step exchanges no data between GPUs, so each "
