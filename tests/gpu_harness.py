@@ -122,7 +122,7 @@ def run_case(c: Case, dev="cuda") -> dict:
     want_w, want_f = orc.cursor_run(c.L, 0, c.steps, forced)
     rdt = workloads.torch_dtype(c.rec_dt)
     err = {"out_replay": 0.0, "out_conv": 0.0, "ckpt_flush": 0.0, "state_conv": 0.0, "ring_x": 0.0,
-           "flushes": 0}
+           "out_replay_step": 0.0, "flushes": 0}
     for s in range(c.steps):
         tok = workloads.tokens(c.form, c.seed, s, c.B, c.H, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
         q, k, v = _device_tokens(tok, c.strided, dev)
@@ -152,6 +152,9 @@ def run_case(c: Case, dev="cuda") -> dict:
         torch.cuda.synchronize()
         got_r = out_r[sample].double().cpu().numpy()
         err["out_replay"] = max(err["out_replay"], rel_err(got_r, o_ref))
+        # the same, normalised by the whole step's output instead of each tile's
+        err["out_replay_step"] = max(err["out_replay_step"],
+                                     float(np.abs(got_r - o_ref).max() / max(np.abs(o_ref).max(), 1e-300)))
         if conv is not None:
             got_c = out_c[sample].double().cpu().numpy()
             err["out_conv"] = max(err["out_conv"], rel_err(got_c, o_ref))
