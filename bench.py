@@ -238,11 +238,13 @@ def _layer_stack(cfg, B, n_layers, dev):
 
 def suite_gdn_sweep(out, steps=32):
     """Gated DeltaNet, 32 heads, 128x128, L=16: replay vs conventional kernel
-    time per launch over batch sizes, fp32 and fp16 state.  A 512 MiB write
-    between launches (outside the timed events) leaves every launch cold."""
+    time per launch over batch sizes, fp32 and fp16 state.  Reading a 1 GiB
+    buffer between launches (outside the timed events) evicts the state from
+    the 256 MB Infinity Cache and the L2s without leaving dirty lines behind,
+    so every launch is cold."""
     import torch
     dev = torch.device("cuda", 0)
-    scrub = torch.empty(512 * 2**20, dtype=torch.uint8, device=dev)
+    scrub = torch.ones(2**28, dtype=torch.int32, device=dev)
     for state in ("f32", "f16"):
         for B in (1, 8, 32, 128, 256, 512):
             cfg = dict(WORKLOADS["gdn"], B=B, state=state)
@@ -252,7 +254,7 @@ def suite_gdn_sweep(out, steps=32):
                 d = _layer_stack(cfg, B, 1, dev)[0]
                 times, nbytes = [], []
                 for s in range(16 + steps):
-                    scrub.fill_(s & 0xff)
+                    scrub.sum()
                     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     if kind == "replay":
                         wp, fl = d.step(ios[s % 16], events=ev)

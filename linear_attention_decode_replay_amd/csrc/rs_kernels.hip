@@ -774,7 +774,53 @@ constexpr int split_for() {
     return s < 1 ? 1 : s;
 }
 
+// Whether Tile<DV, DK, TS, SPLIT> is a valid decomposition (the conditions
+// its static_asserts check, plus at least 8 owned rows so that an owned value
+// record is a whole number of 16-byte chunks).
+template <int DV, int DK, class TS, int SPLIT>
+constexpr bool tile_ok() {
+    if (SPLIT < 1 || DV % SPLIT) return false;
+    const int dvw = DV / SPLIT;
+    const int vec = 16 / (int)sizeof(typename TS::S);
+    const int lpr = DK / vec;
+    const int loads = dvw * lpr;
+    const int nt = loads / 4 >= 256 ? 256 : (loads / 4 >= 128 ? 128 : 64);
+    if (lpr < 1 || lpr > 64 || (lpr & (lpr - 1)) || nt % lpr) return false;
+    const int rpp = nt / lpr;
+    if (dvw % rpp) return false;
+    const int nr = dvw / rpp;
+    return nr >= 1 && (nr & (nr - 1)) == 0 && nt >= dvw && dvw >= 8;
+}
+
+// A wider split for grids too small to fill the chip: up to 8x the base.
+template <int DV, int DK, class TS>
+constexpr int wide_split() {
+    constexpr int b = split_for<DV, DK>();
+    if constexpr (tile_ok<DV, DK, TS, 8 * b>()) return 8 * b;
+    else if constexpr (tile_ok<DV, DK, TS, 4 * b>()) return 4 * b;
+    else if constexpr (tile_ok<DV, DK, TS, 2 * b>()) return 2 * b;
+    else return b;
+}
+
+// Read-modify-write launches (conventional step, token-less flush) with fewer
+// workgroups than this (4 per compute unit) use the wide split: a small batch
+// is bound by each workgroup's latency, not by bandwidth.
+constexpr int64_t kFillWorkgroups = 1024;
+
 // -------------------------------------------------------------- dispatch --
+template <int DV, int DK, class TS, class F>
+void with_split(const StepParams* p, F&& f) {
+    constexpr int base = split_for<DV, DK>();
+    constexpr int wide = wide_split<DV, DK, TS>();
+    if constexpr (wide != base) {
+        if (p && (int64_t)p->n_rows * p->n_heads * base < kFillWorkgroups) {
+            f(std::integral_constant<int, wide>{});
+            return;
+        }
+    }
+    f(std::integral_constant<int, base>{});
+}
+
 template <class F>
 bool with_state(int dt, F&& f) {
     if (dt == RS_F32) { f(tF32{}); return true; }
@@ -830,15 +876,17 @@ struct Dispatch {
                     return;
                 }
                 if (kind == Kind::ConventionalStep) {
-                    constexpr int SP = split_for<DV, DK>();
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
                         with_io(L.io_dtype, [&](auto ti) {
                             using TI = decltype(ti);
                             ok = true;
                             if (p)
-                                hipLaunchKernelGGL((k_conventional_step<FORM, DV, DK, TS, TI, SP>), grid<SP>(),
-                                                   dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
+                                with_split<DV, DK, TS>(p, [&](auto sp_c) {
+                                    constexpr int SP = decltype(sp_c)::value;
+                                    hipLaunchKernelGGL((k_conventional_step<FORM, DV, DK, TS, TI, SP>), grid<SP>(),
+                                                       dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
+                                });
                         });
                     });
                     return;
@@ -847,24 +895,31 @@ struct Dispatch {
                     using TR = decltype(tr);
                     using R = typename TR::S;
                     if (kind == Kind::Flush) {
-                        constexpr int SP = split_for<DV, DK>();
-                        const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                         ok = true;
                         if (p)
-                            hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR, SP>), grid<SP>(),
-                                               dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
+                            with_split<DV, DK, TS>(p, [&](auto sp_c) {
+                                constexpr int SP = decltype(sp_c)::value;
+                                const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR, SP>), grid<SP>(),
+                                                   dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
+                            });
                         return;
                     }
-                    constexpr int SP = split_for<DV, DK>();
-                    const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
                         with_io(L.io_dtype, [&](auto ti) {
                             using TI = decltype(ti);
                             ok = true;
-                            if (p)
+                            if (p) {
+                                // The replay step keeps the base split at any batch:
+                                // measured, a wider split at small batch repeats the
+                                // record work in more workgroups and is slower
+                                // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
+                                constexpr int SP = split_for<DV, DK>();
+                                const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
                                 hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP>), grid<SP>(),
                                                    dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
+                            }
                         });
                     });
                 });
