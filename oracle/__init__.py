@@ -235,6 +235,53 @@ class ReplayModel:
         return self.w.reshape(self.B, self.H)
 
 
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to fp16 / bf16 (round to nearest even, the
+    libraries' casts) and return them as float64."""
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+class TwoCopyReplayModel(ReplayModel):
+    """Checkpoint + buffer with two checkpoint copies (blog "The precision
+    argument, derived"): the recurrence copy C is exact (float64) and is read
+    only by flushes; the read copy C_lo is C rounded to `read_dtype` at each
+    flush, from the same unrounded fold, and is what non-flush steps read.
+    Mamba-2 form."""
+
+    def __init__(self, B, H, dv, dk, L, read_dtype="f16", oracle=None):
+        super().__init__(MAMBA2, B, H, dv, dk, L, oracle)
+        self.read_dtype = read_dtype
+        self.C_lo = np.zeros_like(self.C)
+
+    def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None):
+        B, H = self.B, self.H
+        n = B * H
+        fl = np.repeat(np.asarray(flush_rows, bool), H)
+        act = np.ones(n, bool) if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
+        args = (_vec(q, n), _vec(k, n), _vec(v, n), _scal(lam, n), None)
+        # non-flush rows: output from the read copy, record appended
+        out = self.o.replay_step(MAMBA2, self.C_lo, self.rec_lam, self.rec_x, self.rec_k, self.w, fl, *args,
+                                 act & ~fl)
+        # flush rows: fold from the recurrence copy, then re-round the read copy
+        out += self.o.replay_step(MAMBA2, self.C, self.rec_lam, self.rec_x, self.rec_k, self.w, fl, *args,
+                                  act & fl)
+        f = act & fl
+        self.C_lo[f] = round_to(self.C[f], self.read_dtype)
+        return out.reshape(B, H, self.dv)
+
+    def fold(self, rows_mask):
+        super().fold(rows_mask)
+        mask = np.repeat(np.asarray(rows_mask, bool), self.H)
+        self.C_lo[mask] = round_to(self.C[mask], self.read_dtype)
+
+
 def _vec(a, n):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(n, -1))
 

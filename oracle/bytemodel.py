@@ -5,7 +5,10 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE (see the package docstring).
 All formulas follow the blog "ReplaySSM: an SSM decoder that writes its state
 once every 16 tokens", section "The identity" (state and record terms of one
 window), "Output without a state" (shrink of the state-building term) and
-"Why 16" (the window-length optimum).  Units are bytes per head unless a
+"Why 16" (the window-length optimum); the two-copy window follows the review
+"ReplaySSM, checked", section "The precision argument, derived" (non-flush
+steps read only the read copy; a flush reads the recurrence copy and writes
+both).  Units are bytes per head unless a
 function says otherwise.
 """
 from __future__ import annotations
@@ -40,6 +43,14 @@ def replay_window_bytes(L: int, m_state: int, rec: int) -> int:
     i - 1 records before it (L (L - 1) / 2 in total) and L - 1 records are
     written."""
     return (L + 1) * m_state + rec * (L * (L - 1) // 2 + (L - 1))
+
+
+def two_copy_window_bytes(L: int, m_hi: int, m_lo: int, rec: int) -> int:
+    """Checkpoint + buffer with a recurrence copy (m_hi bytes) and a read copy
+    (m_lo bytes): the L - 1 non-flush steps read the read copy, the flush
+    reads the recurrence copy and writes both; records as in
+    replay_window_bytes."""
+    return (L - 1) * m_lo + m_hi + (m_hi + m_lo) + rec * (L * (L - 1) // 2 + (L - 1))
 
 
 def state_term_ratio(L: int) -> float:

@@ -296,6 +296,65 @@ def pin_cursor_forced_flush(orc):
     assert w[12] == 0 and w[19] == 7
 
 
+# ------------------------------------------------- two-precision checkpoint --
+def pin_two_copy_read_error_is_one_rounding(orc):
+    """[blog] "The precision argument, derived": with an exact recurrence copy
+    and a read copy rounded once per flush, a non-flush step h positions into
+    the window outputs o_t + gamma_h eps_m q_t, eps_m = C_lo - C; a flush step
+    reads the recurrence copy and is exact.  Checked against the exact
+    checkpoint + buffer route on the same inputs, with eps_m one fp16
+    rounding of the last checkpoint."""
+    B, H, dv, dk, L = 2, 3, 16, 32, 4
+    exact = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+    two = oracle.TwoCopyReplayModel(B, H, dv, dk, L, "f16", oracle=orc)
+    ws, fls = orc.cursor_run(L, 0, 40)
+    since = np.zeros((B, H))  # log of gamma_h: decays since the checkpoint, current token included
+    for s in range(40):
+        q, k, v, lam, _ = _tok(M2, 21, s, B, H, dv, dk, 0.001, 0.01)
+        since = since + lam
+        eps = (two.C_lo - two.C).reshape(B, H, dv, dk)
+        o_e = exact.step(q, k, v, lam, np.full(B, fls[s]))
+        o_t = two.step(q, k, v, lam, np.full(B, fls[s]))
+        if fls[s]:
+            assert _rel(o_t, o_e) < 1e-12, s
+            since = np.zeros((B, H))
+        else:
+            want = np.exp(since)[..., None] * np.einsum("bhic,bhc->bhi", eps, q)
+            d = o_t - o_e
+            scale = np.abs(o_e).max()
+            assert np.abs(d - want).max() <= 1e-12 * scale, s
+        # the read copy is one rounding of the recurrence copy
+        C = two.C
+        assert np.all(np.abs(two.C_lo - C) <= np.abs(C) * 2.0**-11 + 2.0**-25), s
+        assert _rel(two.C.reshape(B, H, dv, dk), exact.checkpoint()) < 1e-12
+
+
+def pin_two_copy_error_does_not_accumulate(orc):
+    """The read error stays at one rounding over many windows, while a single
+    checkpoint rounded at every flush (and fed back) drifts further: long-memory
+    heads, 50 windows."""
+    B, H, dv, dk, L, steps = 1, 4, 16, 32, 8, 400
+    exact = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+    two = oracle.TwoCopyReplayModel(B, H, dv, dk, L, "f16", oracle=orc)
+    single = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)  # its checkpoint re-rounded at each flush
+    ws, fls = orc.cursor_run(L, 0, steps)
+    err_two, err_single = [], []
+    for s in range(steps):
+        q, k, v, lam, _ = _tok(M2, 22, s, B, H, dv, dk, 0.0005, 0.001)
+        o_e = exact.step(q, k, v, lam, np.full(B, fls[s]))
+        o_t = two.step(q, k, v, lam, np.full(B, fls[s]))
+        o_s = single.step(q, k, v, lam, np.full(B, fls[s]))
+        if fls[s]:
+            single.C[:] = oracle.round_to(single.C, "f16")
+        scale = np.abs(o_e).max()
+        err_two.append(np.abs(o_t - o_e).max() / scale)
+        err_single.append(np.abs(o_s - o_e).max() / scale)
+    late_two, late_single = max(err_two[-50:]), max(err_single[-50:])
+    assert late_two < 2.0**-10, late_two          # about one fp16 rounding
+    assert max(err_two[-50:]) < 3 * max(err_two[50:100])  # not growing
+    assert late_single > 2 * late_two, (late_single, late_two)
+
+
 ALL_PINS = [
     pin_identity_mamba2_tiny,
     pin_identity_mamba2_long_memory,
@@ -311,4 +370,6 @@ ALL_PINS = [
     pin_fold_materialises_state,
     pin_cursor_closed_form,
     pin_cursor_forced_flush,
+    pin_two_copy_read_error_is_one_rounding,
+    pin_two_copy_error_does_not_accumulate,
 ]

@@ -90,3 +90,45 @@ def test_mutant_is_caught(tmp_path, name, old, new):
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# ------------------------------------------------ two-copy model mutants --
+def _broken_two_copy(kind):
+    """A TwoCopyReplayModel with one planted mistake (Python level)."""
+    import numpy as np
+    from oracle import MAMBA2, TwoCopyReplayModel, _scal, _vec, round_to
+
+    class Broken(TwoCopyReplayModel):
+        def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None):
+            B, H = self.B, self.H
+            n = B * H
+            fl = np.repeat(np.asarray(flush_rows, bool), H)
+            act = np.ones(n, bool)
+            args = (_vec(q, n), _vec(k, n), _vec(v, n), _scal(lam, n), None)
+            read = self.C if kind == "nonflush_reads_recurrence_copy" else self.C_lo
+            fold = self.C_lo if kind == "flush_folds_read_copy" else self.C
+            out = self.o.replay_step(MAMBA2, read, self.rec_lam, self.rec_x, self.rec_k, self.w, fl, *args,
+                                     act & ~fl)
+            out += self.o.replay_step(MAMBA2, fold, self.rec_lam, self.rec_x, self.rec_k, self.w, fl, *args,
+                                      act & fl)
+            if kind == "flush_folds_read_copy":
+                self.C[fl] = fold[fl]
+            if kind != "read_copy_not_refreshed":
+                self.C_lo[fl] = round_to(self.C[fl], self.read_dtype)
+            return out.reshape(B, H, self.dv)
+
+    return Broken
+
+
+@pytest.mark.parametrize("kind", ["nonflush_reads_recurrence_copy", "flush_folds_read_copy",
+                                  "read_copy_not_refreshed"])
+def test_two_copy_mutant_is_caught(monkeypatch, kind):
+    import pins
+    monkeypatch.setattr(oracle, "TwoCopyReplayModel", _broken_two_copy(kind))
+    caught = []
+    for pin in (pins.pin_two_copy_read_error_is_one_rounding, pins.pin_two_copy_error_does_not_accumulate):
+        try:
+            pin(oracle.get())
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"two-copy mutant {kind} passed both pins"
