@@ -40,15 +40,15 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode steps/s + achieved HBM TB/s (% peak), replay vs conventional at bs=256"
 
 WORKLOADS = {
-    "nemotron": dict(form=0, H=128, dv=64, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16"),
-    "gdn": dict(form=1, H=32, dv=128, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16"),
+    "nemotron": dict(form=0, H=128, dv=64, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16", read=None),
+    "gdn": dict(form=1, H=32, dv=128, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16", read=None),
 }
 
 _ES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 # ----------------------------------------------------------- byte accounting --
-def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay"):
+def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay", read=None):
     """Algorithmic HBM bytes of one launch over B rows at cursor w.
 
     Checkpoint + buffer step, per (row, head): read the checkpoint (d_v d_k
@@ -58,18 +58,24 @@ def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay"):
     the state.  Both: read q, k (d_k), v (d_v) in the io dtype, the fp32
     log-decay (and beta for Gated DeltaNet), write the fp32 output (d_v); per
     row, read the block id (4 bytes) plus, for the checkpoint + buffer
-    step, the cursor and flag (5 bytes)."""
+    step, the cursor and flag (5 bytes).  With a two-precision checkpoint
+    (`read` = the read copy's dtype) a non-flush row reads the read copy, a
+    flush row reads the recurrence copy and writes both."""
     ms = dv * dk * _ES[state]
     r = dv * _ES[rec] + dk * _ES[rec] + 4
     io_b = (2 * dk + dv) * _ES[io] + 4 + (4 if form == 1 else 0) + 4 * dv
     if kind == "conventional":
         return B * (H * (2 * ms + io_b) + 4)
-    per_head = ms + w * r + (ms if flush else r) + io_b
+    if read:
+        ml = dv * dk * _ES[read]
+        per_head = (ms + ms + ml if flush else ml + r) + w * r + io_b
+    else:
+        per_head = ms + w * r + (ms if flush else r) + io_b
     return B * (H * per_head + 9)
 
 
-def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay"):
-    return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind) for w in range(L))
+def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay", read=None):
+    return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind, read) for w in range(L))
 
 
 def kernel_source_hash() -> str:
@@ -77,6 +83,11 @@ def kernel_source_hash() -> str:
     for f in ("rs_kernels.hip", "rs_api.cpp", "rs_internal.h"):
         h.update(open(os.path.join(ROOT, "linear_attention_decode_replay_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def workload_key(name, cfg) -> str:
+    key = f"{name}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    return key + (f"-read{cfg['read']}" if cfg.get("read") else "")
 
 
 def load_traffic(workload_key: str):
@@ -110,7 +121,10 @@ def cpu_baseline(cfg, n_steps=16, rows=None):
     f64 = [(t.q.double().numpy(), t.k.double().numpy(), t.v.double().numpy(), t.lam.double().numpy(),
             None if t.beta is None else t.beta.double().numpy()) for t in toks]
     w, fl = o.cursor_run(cfg["L"], 0, n_steps)
-    rep = oracle.ReplayModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"])
+    if cfg.get("read"):
+        rep = oracle.TwoCopyReplayModel(B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["read"])
+    else:
+        rep = oracle.ReplayModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"])
     t0 = time.perf_counter()
     for s in range(n_steps):
         q, k, v, lam, beta = f64[s]
@@ -144,7 +158,9 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"])
+    # the conventional step has one state copy whatever the replay layout
+    read = cfg["read"] if kind == "replay" else None
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"], read)
     B = cfg["B"]
     layers = []
     for p in range(n_pools):
@@ -189,7 +205,7 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     if errs:
         raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
     nbytes = [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"],
-                         w or 0, bool(f), kind) for (w, f) in cursors]
+                         w or 0, bool(f), kind, cfg["read"]) for (w, f) in cursors]
     by_pos = {}
     if kind == "replay":
         for (w, f), t in zip(cursors, times_ms):
@@ -225,7 +241,8 @@ def _inputs(cfg, B, n, dev, seed=11):
 def _layer_stack(cfg, B, n_layers, dev):
     import linear_attention_decode_replay_amd as rs
     from linear_attention_decode_replay_amd.state import DecodeLayer
-    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"])
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"],
+                   cfg["read"])
     layers = []
     for _ in range(n_layers):
         d = DecodeLayer(lay, B, B, dev)
@@ -282,7 +299,8 @@ def suite_gdn_sweep(out, steps=32):
 def suite_stack(out, n_layers=40):
     """40 Mamba-2 layers at the Nemotron-3-Super shape, batch 256: time and
     algorithmic bytes of one decode step over all layers (one launch per
-    layer), replay for L in {8, 16, 32} with fp32 and fp16 checkpoints, and
+    layer), replay for L in {8, 16, 32} with fp32 and fp16 checkpoints, replay
+    at L=16 with an fp32 recurrence copy and an fp16 or bf16 read copy, and
     the conventional step with fp32 and fp16 state.  Two windows timed after
     one window of warm-up."""
     import torch
@@ -290,10 +308,11 @@ def suite_stack(out, n_layers=40):
     base = dict(WORKLOADS["nemotron"])
     ios, keep = _inputs(base, base["B"], 16, dev)
     results = {}
-    runs = [("conventional", 16, "f32"), ("conventional", 16, "f16")]
-    runs += [("replay", L, st) for st in ("f32", "f16") for L in (8, 16, 32)]
-    for kind, L, state in runs:
-        cfg = dict(base, L=L, state=state)
+    runs = [("conventional", 16, "f32", None), ("conventional", 16, "f16", None)]
+    runs += [("replay", L, st, None) for st in ("f32", "f16") for L in (8, 16, 32)]
+    runs += [("replay", 16, "f32", rd) for rd in ("f16", "bf16")]
+    for kind, L, state, read in runs:
+        cfg = dict(base, L=L, state=state, read=read)
         layers = _layer_stack(cfg, base["B"], n_layers, dev)
         n_warm, n_time = L, 2 * L
         nbytes = 0
@@ -313,25 +332,26 @@ def suite_stack(out, n_layers=40):
                     w, f = 0, False
                 if s >= n_warm:
                     nbytes += step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], state, cfg["rec"],
-                                         cfg["io"], w, f, kind)
+                                         cfg["io"], w, f, kind, read)
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = e0.elapsed_time(e1) / n_time
         gb = nbytes / n_time / 1e9
-        results[(kind, L, state)] = ms
+        results[(kind, L, state, read)] = ms
         line = {"suite": "stack40", "kind": kind, "L": L if kind == "replay" else None, "state": state,
+                "read_copy": read,
                 "ms_per_step": round(ms, 3), "wall_ms_per_step": round(1e3 * wall / n_time, 3),
                 "gb_per_step": round(gb, 3), "tbs": round(gb / ms, 3)}
         print(json.dumps(line), file=out, flush=True)
         del layers
         torch.cuda.empty_cache()
-    for (kind, L, state), ms in results.items():
+    for (kind, L, state, read), ms in results.items():
         if kind == "replay":
-            line = {"suite": "stack40_ratio", "L": L, "state": state,
-                    "speedup_vs_conventional_f32": round(results[("conventional", 16, "f32")] / ms, 3),
-                    "speedup_vs_conventional_f16": round(results[("conventional", 16, "f16")] / ms, 3)}
+            line = {"suite": "stack40_ratio", "L": L, "state": state, "read_copy": read,
+                    "speedup_vs_conventional_f32": round(results[("conventional", 16, "f32", None)] / ms, 3),
+                    "speedup_vs_conventional_f16": round(results[("conventional", 16, "f16", None)] / ms, 3)}
             print(json.dumps(line), file=out, flush=True)
 
 
@@ -390,7 +410,8 @@ def summarize_counters(args, fetch_csv, write_csv):
         cfg["L"] = args.L
     if args.state:
         cfg["state"] = args.state
-    key = f"{args.workload}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    cfg["read"] = args.read
+    key = workload_key(args.workload, cfg)
     entry = {"kernel_source": kernel_source_hash(),
              "bytes_per_launch": round(res["fetch"]["replay"] + res["write"]["replay"]),
              "replay": {"fetch": round(res["fetch"]["replay"]), "write": round(res["write"]["replay"])},
@@ -417,6 +438,8 @@ def main(argv=None):
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--L", type=int, default=None)
     ap.add_argument("--state", default=None, choices=["f32", "f16"])
+    ap.add_argument("--read", default=None, choices=["f16", "bf16"],
+                    help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy")
     ap.add_argument("--pools", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
@@ -453,18 +476,21 @@ def main(argv=None):
         cfg["L"] = args.L
     if args.state:
         cfg["state"] = args.state
+    cfg["read"] = args.read
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
     rep = run_gpu(cfg, args.steps, args.warmup, args.pools, "replay")
     conv = run_gpu(cfg, args.steps, args.warmup, args.pools, "conventional")
 
-    wb_r = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"])
+    wb_r = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"],
+                        read=cfg["read"])
     wb_c = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"], "conventional")
     form_name = "mamba2" if cfg["form"] == 0 else "gdn"
-    workload = (f"{form_name} layer, {cfg['H']} heads, d_v={cfg['dv']}, d_k={cfg['dk']}, {cfg['state']} state, "
+    state_desc = f"{cfg['state']} state" + (f" + {cfg['read']} read copy" if cfg["read"] else "")
+    workload = (f"{form_name} layer, {cfg['H']} heads, d_v={cfg['dv']}, d_k={cfg['dk']}, {state_desc}, "
                 f"{cfg['rec']} records, {cfg['io']} q/k/v, batch {cfg['B']}, L={cfg['L']}")
-    key = f"{args.workload}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    key = workload_key(args.workload, cfg)
     traffic = load_traffic(key)
     achieved = rep["achieved_gbs"]
     line = {
@@ -482,6 +508,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": workload, "global_batch": cfg["B"], "seq_len": None, "heads": cfg["H"],
                    "d_v": cfg["dv"], "d_k": cfg["dk"], "L": cfg["L"], "state_dtype": cfg["state"],
+                   "read_copy_dtype": cfg["read"],
                    "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": args.pools,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -76,6 +76,15 @@ typedef enum {
  * state_dtype:  RS_F32 or RS_F16 (checkpoint / conventional state).
  * record_dtype: RS_F32 or RS_F16 (buffered x and k; the log-decay is fp32).
  * io_dtype:     RS_F32, RS_F16 or RS_BF16 (q, k, v inputs).
+ * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16 or
+ *               RS_BF16 for a two-precision checkpoint (blog "The precision
+ *               argument, derived"): state_dtype RS_F32 is the recurrence
+ *               copy, read by flushes only; a second copy in read_dtype is
+ *               what non-flush steps read.  A flush folds from the
+ *               recurrence copy and rewrites both copies from the same
+ *               unrounded values, so the read copy's rounding never enters
+ *               the recurrence.  Mamba-2 form only (RS_EUNSUPPORTED for GDN:
+ *               its buffered corrections would carry the read copy's error).
  */
 typedef struct {
     int32_t form;
@@ -86,6 +95,7 @@ typedef struct {
     int32_t state_dtype;
     int32_t record_dtype;
     int32_t io_dtype;
+    int32_t read_dtype;
 } rs_layer;
 
 /*
@@ -97,6 +107,8 @@ typedef struct {
  *   rec_x    [n_heads][slots][d_v]  record_dtype
  *   rec_k    [n_heads][slots][d_k]  record_dtype
  *   rec_lam  [n_heads][slots]       fp32 log-decay
+ *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
+ *                                   ckpt_lo_off is 0 otherwise)
  * slots = L - 1.  block_bytes is a multiple of 256.
  */
 typedef struct {
@@ -107,6 +119,7 @@ typedef struct {
     int64_t block_bytes;
     int32_t slots;
     int32_t reserved;
+    int64_t ckpt_lo_off;
 } rs_block_layout;
 
 /* Host, pure.  Fills *out for `layer`.  RS_EINVAL / RS_EUNSUPPORTED on a bad
@@ -176,7 +189,10 @@ typedef struct {
  *                  current token folded in), stored once in state_dtype
  *                  (round to nearest even); no record is written.  The caller
  *                  then sets the row's write_pos to 0.
- * Buffer slots >= write_pos are never read.
+ * Buffer slots >= write_pos are never read.  With a two-precision checkpoint
+ * a non-flush row reads only the read copy (its output differs from the
+ * single-checkpoint output by G (C_lo - C) q, one rounding of the last
+ * checkpoint); a flush row reads the recurrence copy and writes both.
  */
 int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
                        hipStream_t stream);
@@ -184,7 +200,8 @@ int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_st
 /*
  * Token-less flush: for every non-padding row whose flush flag is set, fold
  * its write_pos records into its checkpoint (S = gamma C + sum_j gamma_j x_j
- * k_j^T, blog "The identity" with h = write_pos).  Rows whose flag is clear
+ * k_j^T, blog "The identity" with h = write_pos; from and into the recurrence
+ * copy, the read copy rewritten from the same values).  Rows whose flag is clear
  * are untouched.  This materialises the exact state at any step: before a row
  * is retired or preempted, or at a prefix-cache block boundary (vLLM pull
  * request, "What this PR adds", align mode).  batch->flush must not be NULL.
@@ -196,14 +213,16 @@ int replay_flush(const rs_layer* layer, const rs_batch* batch, hipStream_t strea
  * decode"; "The delta-rule wrinkle" for Gated DeltaNet): the checkpoint
  * region of each block holds the full state S, which is read, updated and
  * written back on every step; out = S_t q_t.  write_pos and flush are
- * ignored (may be NULL); record_dtype is unused.
+ * ignored (may be NULL); record_dtype is unused.  With a two-precision layer
+ * it works on the recurrence copy alone and leaves the read copy untouched.
  */
 int conventional_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_step_io* io,
                              hipStream_t stream);
 
 /*
- * Zero the checkpoint of every non-padding row whose mask entry (device
- * uint8 [n_rows]) is nonzero: the state of a request that joins the batch.
+ * Zero the checkpoint (both copies of a two-precision checkpoint) of every
+ * non-padding row whose mask entry (device uint8 [n_rows]) is nonzero: the
+ * state of a request that joins the batch.
  * Its write_pos must start at 0; stale records need no clearing because
  * slots at or beyond write_pos are never read (vLLM pull request, "CUDA
  * graphs and continuous batching").  Implemented as a kernel, not a memset,

@@ -34,13 +34,13 @@ _vp = _c.c_void_p
 class RsLayer(_c.Structure):
     _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
                 ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
-                ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32)]
+                ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32)]
 
 
 class RsBlockLayout(_c.Structure):
     _fields_ = [("ckpt_off", _c.c_int64), ("rec_x_off", _c.c_int64), ("rec_k_off", _c.c_int64),
                 ("rec_lam_off", _c.c_int64), ("block_bytes", _c.c_int64), ("slots", _c.c_int32),
-                ("reserved", _c.c_int32)]
+                ("reserved", _c.c_int32), ("ckpt_lo_off", _c.c_int64)]
 
 
 class RsBatch(_c.Structure):
@@ -108,10 +108,12 @@ _DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
 
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
-          record_dtype="f16", io_dtype="bf16") -> RsLayer:
+          record_dtype="f16", io_dtype="bf16", read_dtype=None) -> RsLayer:
+    """read_dtype: None for a single checkpoint, "f16" / "bf16" for a
+    two-precision checkpoint (fp32 recurrence copy + read copy)."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
-                   code(record_dtype), code(io_dtype))
+                   code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype))
 
 
 def block_layout(lay: RsLayer) -> RsBlockLayout:
@@ -233,6 +235,15 @@ class Pool:
         es = 4 if L.record_dtype == F32 else 2
         return self._region(self.layout.rec_k_off, L.n_heads * s * L.d_k * es,
                             self._tdt[L.record_dtype], (L.n_heads, s, L.d_k))
+
+    def ckpt_lo(self):
+        """[n_blocks, H, d_v, d_k] read copy of a two-precision checkpoint."""
+        L = self.layer
+        if L.read_dtype < 0 or L.read_dtype == L.state_dtype:
+            raise ValueError("this layer has a single checkpoint")
+        es = 4 if L.read_dtype == F32 else 2
+        return self._region(self.layout.ckpt_lo_off, L.n_heads * L.d_v * L.d_k * es, self._tdt[L.read_dtype],
+                            (L.n_heads, L.d_v, L.d_k))
 
     def rec_lam(self):
         """[n_blocks, H, slots] fp32."""

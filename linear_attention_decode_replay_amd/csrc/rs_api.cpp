@@ -35,6 +35,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int dtype_bytes(int dt) { return dt == RS_F32 ? 4 : 2; }
 
 const int kMaxL = 64;
+
+bool two_precision(const rs_layer& L) { return L.read_dtype >= 0 && L.read_dtype != L.state_dtype; }
 const size_t kMaxLds = 64 * 1024;
 
 int check_layer(const rs_layer* L, rs::Kind kind) {
@@ -46,6 +48,14 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
     for (int dt : {L->state_dtype, L->record_dtype, L->io_dtype})
         if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return fail(RS_EINVAL, "unknown dtype %d", dt);
     if (L->state_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 state is not supported");
+    if (L->read_dtype < -1 || L->read_dtype > RS_BF16) return fail(RS_EINVAL, "unknown read dtype %d", L->read_dtype);
+    if (two_precision(*L)) {
+        if (L->form != RS_MAMBA2)
+            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: Mamba-2 form only (a GDN read copy would "
+                                         "leak into the buffered corrected values)");
+        if (L->state_dtype != RS_F32 || (L->read_dtype != RS_F16 && L->read_dtype != RS_BF16))
+            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy with an fp16 or bf16 read copy");
+    }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
     if (!rs::compiled(kind, *L))
         return fail(RS_EUNSUPPORTED, "no kernel for d_v=%d d_k=%d (supported: 16x32, 64x128, 128x128)",
@@ -65,6 +75,11 @@ void layout_of(const rs_layer& L, rs_block_layout* o) {
     o->rec_k_off = align_up(o->rec_x_off + H * slots * L.d_v * rb, 256);
     o->rec_lam_off = align_up(o->rec_k_off + H * slots * L.d_k * rb, 256);
     o->block_bytes = align_up(o->rec_lam_off + H * slots * 4, 256);
+    o->ckpt_lo_off = 0;
+    if (two_precision(L)) {
+        o->ckpt_lo_off = o->block_bytes;
+        o->block_bytes = align_up(o->ckpt_lo_off + H * L.d_v * L.d_k * dtype_bytes(L.read_dtype), 256);
+    }
     o->slots = (int32_t)slots;
     o->reserved = 0;
 }
@@ -133,6 +148,7 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.recx_off = lay.rec_x_off;
     p.reck_off = lay.rec_k_off;
     p.reclam_off = lay.rec_lam_off;
+    p.ckpt_lo_off = lay.ckpt_lo_off;
     p.block_table = b.block_table;
     p.write_pos = b.write_pos;
     p.flush = b.flush;

@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rs_internal.h"
 
 namespace rs {
@@ -61,6 +63,13 @@ template <> __device__ __forceinline__ float to_f<tBF16>(uint16_t x) {
 template <class T> __device__ __forceinline__ typename T::S from_f(float x);
 template <> __device__ __forceinline__ float from_f<tF32>(float x) { return x; }
 template <> __device__ __forceinline__ _Float16 from_f<tF16>(float x) { return (_Float16)x; }
+// bf16 keeps the top 16 bits of the float; round to nearest even on the
+// discarded 16 (NaN stays a quiet NaN).
+template <> __device__ __forceinline__ uint16_t from_f<tBF16>(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
 
 // Load N consecutive elements (N * sizeof(S) bytes, naturally aligned to
 // that size up to 16) and widen them to float.
@@ -107,6 +116,25 @@ __device__ __forceinline__ u32x4 pack16(const float* in) {
     u32x4 r;
     __builtin_memcpy(&r, tmp, 16);
     return r;
+}
+
+// N elements of T held as N * sizeof(T) / 16 sixteen-byte chunks.
+template <class T, int N>
+__device__ __forceinline__ void unpack_n(const u32x4* in, float* out) {
+    using S = typename T::S;
+    S tmp[N];
+    __builtin_memcpy(tmp, in, sizeof(tmp));
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f<T>(tmp[i]);
+}
+
+template <class T, int N>
+__device__ __forceinline__ void pack_n(const float* in, u32x4* out) {
+    using S = typename T::S;
+    S tmp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) tmp[i] = from_f<T>(in[i]);
+    __builtin_memcpy(out, tmp, sizeof(tmp));
 }
 
 // ------------------------------------------------------- lane-group sums --
@@ -238,6 +266,16 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+template <int C>
+__device__ __forceinline__ void ld_stream_n(const void* p, u32x4* out) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) out[c] = ld_stream(reinterpret_cast<const u32x4*>(p) + c);
+}
+template <int C>
+__device__ __forceinline__ void st_stream_n(void* p, const u32x4* in) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) st_stream(reinterpret_cast<u32x4*>(p) + c, in[c]);
 }
 
 // LDS carve-up shared by the step and flush kernels (DVW = rows owned).
@@ -376,15 +414,25 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 //      terms (lane c of a row's lane group takes records c, c + LPR, ...),
 //      then one lane-group reduction that yields the output rows directly;
 //   5. non-flush: append the record from registers; flush: fold and store.
-template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT>
-__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(const StepParams p) {
-    using T = Tile<DV, DK, TS, SPLIT>;
+//
+// Two-precision checkpoint (TL != TS; blog "The precision argument,
+// derived"): the block holds the recurrence copy (TS) and a read copy (TL).
+// Non-flush rows stream only the read copy; a flush row loads the recurrence
+// copy, folds in fp32 and stores both copies, each cast from the same
+// unrounded values.  Threads are laid out by the read type, so a flush row
+// moves HPC = sizeof(TS) / sizeof(TL) chunks per lane chunk of the read copy.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL>
+__global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(const StepParams p) {
+    using T = Tile<DV, DK, TL, SPLIT>;
     using S = typename TS::S;
+    using RL = typename TL::S;
     using R = typename TR::S;
     using I = typename TI::S;
     constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
     constexpr int KEEP = FORM == kGdn ? 2 : 1;  // Gated DeltaNet keeps (C q, C k) of a row together
     constexpr int NV = KEEP * NR;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr int HPC = VEC * (int)sizeof(S) / 16;  // recurrence-copy chunks per lane chunk
 
     const TileIds id = tile_ids<SPLIT>(p);
     // Without a flag array the (always present) cursor array is read in its
@@ -407,6 +455,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
 
     char* base = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     float* rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
@@ -414,6 +463,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
     const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
     const float lam = p.lam[id.tile];
+    const bool fl = (w == p.slots) || flag;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
@@ -426,9 +476,14 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     if (w > 0) lam_j = rl[min(tid, w - 1)];
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
-    u32x4 cb[NR];
+    u32x4 cb[NR * HPC];
+    if (!TWO || fl) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+        for (int r = 0; r < NR; ++r) ld_stream_n<HPC>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, &cb[r * HPC]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) cb[r * HPC] = ld_stream(cl + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+    }
 
     if (tid < DVW) s.v[tid] = vi;
     rec.commit(rk, rx, s.k, s.x);
@@ -470,8 +525,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     const float G = s.sc[0];
     const float kq = s.sc[1];
     float cf[NR][VEC];
+    if (!TWO || fl) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+        for (int r = 0; r < NR; ++r) unpack_n<TS, VEC>(&cb[r * HPC], cf[r]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) unpack_n<TL, VEC>(&cb[r * HPC], cf[r]);
+    }
     float acc[NV];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -510,7 +570,6 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
     }
     xsum<NV, LPR / 2, KEEP>(acc, cc);
 
-    const bool fl = (w == p.slots) || flag;
     if (p.next_wp && id.head == 0 && id.part == 0 && tid == 0) p.next_wp[id.row] = fl ? 0 : w + 1;
     const float alpha = expf(lam);  // Gated DeltaNet only
     float* o = p.out + id.tile * DV + row0;
@@ -571,7 +630,17 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_step(c
         }
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+    for (int r = 0; r < NR; ++r) {
+        const int64_t off = (int64_t)(r * RPP + rg) * DK + cc * VEC;
+        u32x4 hp[HPC];
+        pack_n<TS, VEC>(cf[r], hp);
+        st_stream_n<HPC>(ck + off, hp);
+        if constexpr (TWO) {
+            u32x4 lo;
+            pack_n<TL, VEC>(cf[r], &lo);
+            st_stream(cl + off, lo);
+        }
+    }
 }
 
 // ------------------------------------------------ conventional decode step --
@@ -580,7 +649,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
     using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
     using I = typename TI::S;
-    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr int VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
     constexpr int KEEP = FORM == kGdn ? 2 : 1;
     constexpr int NV = KEEP * NR;
 
@@ -677,12 +746,17 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 }
 
 // ------------------------------------------------------ token-less flush --
-template <int DV, int DK, class TS, class TR, int SPLIT>
-__global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(const StepParams p) {
-    using T = Tile<DV, DK, TS, SPLIT>;
+// Fold the w buffered records into the (recurrence) checkpoint; with a
+// two-precision checkpoint the read copy is rewritten from the same values.
+template <int DV, int DK, class TS, class TR, int SPLIT, class TL>
+__global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(const StepParams p) {
+    using T = Tile<DV, DK, TL, SPLIT>;
     using S = typename TS::S;
+    using RL = typename TL::S;
     using R = typename TR::S;
     constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr int HPC = VEC * (int)sizeof(S) / 16;
 
     const TileIds id = tile_ids<SPLIT>(p);
     const bool flag = row_flag(p.flush, id.row);
@@ -701,6 +775,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(
     const int row0 = id.part * DVW;
     char* base = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     const float* rl = reinterpret_cast<const float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
@@ -711,9 +786,9 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(
     const float lam_j = rl[min(tid, w - 1)];
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
-    u32x4 cb[NR];
+    u32x4 cb[NR * HPC];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+    for (int r = 0; r < NR; ++r) ld_stream_n<HPC>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, &cb[r * HPC]);
     rec.commit(rk, rx, s.k, s.x);
     decay_weights(lam_j, s.e, s.sc, w, 0.0f);
     __syncthreads();
@@ -723,7 +798,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(
     float cf[NR][VEC];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        unpack16<TS>(cb[r], cf[r]);
+        unpack_n<TS, VEC>(&cb[r * HPC], cf[r]);
 #pragma unroll
         for (int c = 0; c < VEC; ++c) cf[r][c] *= G;
     }
@@ -739,15 +814,28 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_replay_flush(
         }
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+    for (int r = 0; r < NR; ++r) {
+        const int64_t off = (int64_t)(r * RPP + rg) * DK + cc * VEC;
+        u32x4 hp[HPC];
+        pack_n<TS, VEC>(cf[r], hp);
+        st_stream_n<HPC>(ck + off, hp);
+        if constexpr (TWO) {
+            u32x4 lo;
+            pack_n<TL, VEC>(cf[r], &lo);
+            st_stream(cl + off, lo);
+        }
+    }
 }
 
 // ------------------------------------------------------------ state reset --
-template <int DV, int DK, class TS, int SPLIT>
+// Zero the checkpoint (both copies of a two-precision checkpoint).
+template <int DV, int DK, class TS, int SPLIT, class TL>
 __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(const StepParams p) {
     using T = Tile<DV, DK, TS, SPLIT>;
     using S = typename TS::S;
+    using RL = typename TL::S;
     constexpr int NT = T::NT, NR = T::NR, DVW = T::DVW;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
     const TileIds id = tile_ids<SPLIT>(p);
     const bool m = row_flag(p.mask, id.row);
     const int blk = p.block_table[id.row];
@@ -756,11 +844,18 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(c
         count_error(p, id);
         return;
     }
-    S* ck = reinterpret_cast<S*>(p.pool + (int64_t)blk * p.block_bytes + p.ckpt_off) +
-            (int64_t)id.head * (DV * DK) + (int64_t)id.part * DVW * DK;
+    char* base = p.pool + (int64_t)blk * p.block_bytes;
+    const int64_t elem0 = (int64_t)id.head * (DV * DK) + (int64_t)id.part * DVW * DK;
+    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + elem0;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < NR; ++r) st_stream(reinterpret_cast<u32x4*>(ck) + r * NT + threadIdx.x, z);
+    if constexpr (TWO) {
+        // the read copy's owned rows are DVW * DK * sizeof(RL) bytes
+        constexpr int CH = DVW * DK * (int)sizeof(RL) / 16;
+        RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + elem0;
+        for (int i = threadIdx.x; i < CH; i += NT) st_stream(reinterpret_cast<u32x4*>(cl) + i, z);
+    }
 }
 
 // How many workgroups share one (row, head) tile: at most 8192 state elements
@@ -848,6 +943,18 @@ bool with_form(int form, F&& f) {
     return false;
 }
 
+// The read copy's type: the state type itself (one checkpoint), or fp16 /
+// bf16 for a two-precision checkpoint over an fp32 recurrence copy.
+template <class TS, class F>
+bool with_read(int read_dt, int state_dt, F&& f) {
+    if (read_dt < 0 || read_dt == state_dt) { f(TS{}); return true; }
+    if constexpr (std::is_same<TS, tF32>::value) {
+        if (read_dt == RS_F16) { f(tF16{}); return true; }
+        if (read_dt == RS_BF16) { f(tBF16{}); return true; }
+    }
+    return false;
+}
+
 struct Dispatch {
     Kind kind;
     const rs_layer& L;
@@ -867,14 +974,6 @@ struct Dispatch {
             constexpr int DV = decltype(dv_c)::value, DK = decltype(dk_c)::value;
             with_state(L.state_dtype, [&](auto ts) {
                 using TS = decltype(ts);
-                if (kind == Kind::Reset) {
-                    constexpr int SP = split_for<DV, DK>();
-                    ok = true;
-                    if (p)
-                        hipLaunchKernelGGL((k_state_reset<DV, DK, TS, SP>), grid<SP>(),
-                                           dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
-                    return;
-                }
                 if (kind == Kind::ConventionalStep) {
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
@@ -891,34 +990,50 @@ struct Dispatch {
                     });
                     return;
                 }
-                with_record(L.record_dtype, [&](auto tr) {
-                    using TR = decltype(tr);
-                    using R = typename TR::S;
-                    if (kind == Kind::Flush) {
+                with_read<TS>(L.read_dtype, L.state_dtype, [&](auto tl) {
+                    using TL = decltype(tl);
+                    constexpr bool TWO = !std::is_same<TS, TL>::value;
+                    if (kind == Kind::Reset) {
+                        constexpr int SP = split_for<DV, DK>();
                         ok = true;
                         if (p)
-                            with_split<DV, DK, TS>(p, [&](auto sp_c) {
-                                constexpr int SP = decltype(sp_c)::value;
-                                const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
-                                hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR, SP>), grid<SP>(),
-                                                   dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
-                            });
+                            hipLaunchKernelGGL((k_state_reset<DV, DK, TS, SP, TL>), grid<SP>(),
+                                               dim3(Tile<DV, DK, TS, SP>::NT), 0, stream, *p);
                         return;
                     }
-                    with_form(L.form, [&](auto f_c) {
-                        constexpr int FORM = decltype(f_c)::value;
-                        with_io(L.io_dtype, [&](auto ti) {
-                            using TI = decltype(ti);
+                    with_record(L.record_dtype, [&](auto tr) {
+                        using TR = decltype(tr);
+                        using R = typename TR::S;
+                        if (kind == Kind::Flush) {
                             ok = true;
-                            if (p) {
-                                // The replay step keeps the base split at any batch:
-                                // measured, a wider split at small batch repeats the
-                                // record work in more workgroups and is slower
-                                // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
-                                constexpr int SP = split_for<DV, DK>();
-                                const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
-                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP>), grid<SP>(),
-                                                   dim3(Tile<DV, DK, TS, SP>::NT), lds, stream, *p);
+                            if (p)
+                                with_split<DV, DK, TL>(p, [&](auto sp_c) {
+                                    constexpr int SP = decltype(sp_c)::value;
+                                    const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                    hipLaunchKernelGGL((k_replay_flush<DV, DK, TS, TR, SP, TL>), grid<SP>(),
+                                                       dim3(Tile<DV, DK, TL, SP>::NT), lds, stream, *p);
+                                });
+                            return;
+                        }
+                        with_form(L.form, [&](auto f_c) {
+                            constexpr int FORM = decltype(f_c)::value;
+                            if constexpr (TWO && FORM != kMamba2) {
+                                return;  // two-precision checkpoint: Mamba-2 form only
+                            } else {
+                                with_io(L.io_dtype, [&](auto ti) {
+                                    using TI = decltype(ti);
+                                    ok = true;
+                                    if (p) {
+                                        // The replay step keeps the base split at any batch:
+                                        // measured, a wider split at small batch repeats the
+                                        // record work in more workgroups and is slower
+                                        // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
+                                        constexpr int SP = split_for<DV, DK>();
+                                        const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                        hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
+                                                           dim3(Tile<DV, DK, TL, SP>::NT), lds, stream, *p);
+                                    }
+                                });
                             }
                         });
                     });

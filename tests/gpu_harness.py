@@ -70,12 +70,13 @@ class Case:
     strided: bool = False            # q/k/v as strided views of wider buffers
     check_conventional: bool = True
     force_every: int = 0             # > 0: force a flush on row 0 every n steps
+    read_dt: str | None = None       # two-precision checkpoint: read copy dtype
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"{f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} steps={self.steps} "
-                f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} strided={self.strided} "
-                f"pad={self.pad_rows} seed={self.seed}")
+                f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
+                f"strided={self.strided} pad={self.pad_rows} seed={self.seed}")
 
 
 def _device_tokens(tok, strided: bool, dev):
@@ -97,7 +98,7 @@ def run_case(c: Case, dev="cuda") -> dict:
     Returns the worst errors seen; raises AssertionError on any bit-exact
     mismatch (cursor, flush flag, copied record fields, untouched pad rows)."""
     say(f"[case] {c.name()}")
-    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt)
     n_blocks = c.n_blocks or (c.B + 3)
     rep = DecodeLayer(lay, c.B, n_blocks, dev)
     conv = DecodeLayer(lay, c.B, n_blocks, dev) if c.check_conventional else None
@@ -115,6 +116,8 @@ def run_case(c: Case, dev="cuda") -> dict:
     sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live_rows]
     ns = len(sample)
     ref = oracle.ConventionalModel(c.form, ns, c.H, c.dv, c.dk)
+    # a two-precision checkpoint is compared with the oracle's two-copy model
+    ref_two = oracle.TwoCopyReplayModel(ns, c.H, c.dv, c.dk, c.L, c.read_dt) if c.read_dt else None
     orc = oracle.get()
     forced = np.zeros(c.steps, np.uint8)
     if c.force_every:
@@ -122,7 +125,7 @@ def run_case(c: Case, dev="cuda") -> dict:
     want_w, want_f = orc.cursor_run(c.L, 0, c.steps, forced)
     rdt = workloads.torch_dtype(c.rec_dt)
     err = {"out_replay": 0.0, "out_conv": 0.0, "ckpt_flush": 0.0, "state_conv": 0.0, "ring_x": 0.0,
-           "out_replay_step": 0.0, "flushes": 0}
+           "out_replay_step": 0.0, "out_replay_vs_exact": 0.0, "flushes": 0}
     for s in range(c.steps):
         tok = workloads.tokens(c.form, c.seed, s, c.B, c.H, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
         q, k, v = _device_tokens(tok, c.strided, dev)
@@ -151,10 +154,18 @@ def run_case(c: Case, dev="cuda") -> dict:
                                 want_x=True)
         torch.cuda.synchronize()
         got_r = out_r[sample].double().cpu().numpy()
-        err["out_replay"] = max(err["out_replay"], rel_err(got_r, o_ref))
+        if ref_two is not None:
+            o_two = ref_two.step(tok.q[sample].double().numpy(), tok.k[sample].double().numpy(),
+                                 tok.v[sample].double().numpy(), tok.lam[sample].double().numpy(),
+                                 np.asarray(fl)[sample].astype(bool))
+            err["out_replay_vs_exact"] = max(err["out_replay_vs_exact"], rel_err(got_r, o_ref))
+            o_ref_replay = o_two
+        else:
+            o_ref_replay = o_ref
+        err["out_replay"] = max(err["out_replay"], rel_err(got_r, o_ref_replay))
         # the same, normalised by the whole step's output instead of each tile's
         err["out_replay_step"] = max(err["out_replay_step"],
-                                     float(np.abs(got_r - o_ref).max() / max(np.abs(o_ref).max(), 1e-300)))
+                                     float(np.abs(got_r - o_ref_replay).max() / max(np.abs(o_ref_replay).max(), 1e-300)))
         if conv is not None:
             got_c = out_c[sample].double().cpu().numpy()
             err["out_conv"] = max(err["out_conv"], rel_err(got_c, o_ref))
@@ -179,8 +190,12 @@ def run_case(c: Case, dev="cuda") -> dict:
         flushed = [i for i, b in enumerate(sample) if fl[b]]
         if flushed:
             err["flushes"] += 1
-            ck = rep.pool.ckpt()[blk[flushed]].double().cpu().numpy()
+            ckt = rep.pool.ckpt()[blk[flushed]]
+            ck = ckt.double().cpu().numpy()
             err["ckpt_flush"] = max(err["ckpt_flush"], rel_err(ck, ref.state()[flushed], 2))
+            if c.read_dt:  # the read copy is the RNE cast of the same values, bit for bit
+                lo = rep.pool.ckpt_lo()[blk[flushed]].cpu()
+                assert torch.equal(lo, ckt.cpu().to(workloads.torch_dtype(c.read_dt))), f"read copy, step {s}"
         if conv is not None and (s % 8 == 7 or s == c.steps - 1):
             st = conv.pool.ckpt()[blk].double().cpu().numpy()
             err["state_conv"] = max(err["state_conv"], rel_err(st, ref.state(), 2))

@@ -22,6 +22,21 @@ def test_window_bytes_match_model(name, L, state):
     assert got_c == c["B"] * c["H"] * bm.conventional_window_bytes(L, ms)
 
 
+@pytest.mark.parametrize("L", [1, 2, 8, 16, 32])
+@pytest.mark.parametrize("read", ["f16", "bf16"])
+def test_two_copy_window_bytes_match_model(L, read):
+    c = dict(bench.WORKLOADS["nemotron"])
+    args = (c["form"], c["H"], c["dv"], c["dk"], c["B"], "f32", c["rec"], c["io"])
+    io = (2 * c["dk"] + c["dv"]) * 2 + 4 + 4 * c["dv"]
+    m_hi = bm.state_bytes(c["dv"], c["dk"], 4)
+    m_lo = bm.state_bytes(c["dv"], c["dk"], 2)
+    rec = bm.record_bytes(c["dv"], c["dk"])
+    got = bench.window_bytes(*args, L, read=read) - c["B"] * c["H"] * L * io - 9 * c["B"] * L
+    assert got == c["B"] * c["H"] * bm.two_copy_window_bytes(L, m_hi, m_lo, rec)
+    # a read copy as wide as the recurrence copy costs one more write per window
+    assert bm.two_copy_window_bytes(L, m_hi, m_hi, rec) == bm.replay_window_bytes(L, m_hi, rec) + m_hi
+
+
 def test_headline_ratio():
     """The headline workload's algorithmic traffic ratio, inputs included: the
     state + record part is the blog's 0.581; q/k/v/out add a little."""

@@ -8,7 +8,7 @@ padding rows (untouched)."""
 import pytest
 
 import linear_attention_decode_replay_amd as rs
-from gpu_harness import Case, assert_within, run_case, tolerance
+from gpu_harness import TOL_F32, TOL_LOW, Case, assert_within, run_case, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -80,3 +80,24 @@ def test_gdn_batch_sweep(B, state_dt):
     sample = sorted({0, B // 3, B // 2, B - 1})
     _go(Case(form=rs.GDN, B=B, H=32, dv=128, dk=128, L=16, steps=20, state_dt=state_dt,
              rec_dt="f16", io_dt="bf16", sample=sample, seed=50 + B))
+
+
+@pytest.mark.parametrize("read_dt", ["f16", "bf16"])
+@pytest.mark.parametrize("rec_dt,io", [("f32", "f32"), ("f16", "bf16")])
+def test_two_precision_checkpoint_tiny(read_dt, rec_dt, io):
+    """fp32 recurrence copy + fp16/bf16 read copy (Mamba-2), tiny heads with
+    strided inputs, padding and forced flushes; compared with the oracle's
+    two-copy model (outputs) and its exact recurrence (flushed checkpoints)."""
+    err = run_case(Case(B=5, pad_rows=[3], strided=True, force_every=5, rec_dt=rec_dt, io_dt=io,
+                        read_dt=read_dt, seed=60))
+    assert_within(err, TOL_LOW)
+    assert err["ckpt_flush"] <= TOL_F32  # the recurrence copy is fp32
+
+
+@pytest.mark.parametrize("read_dt", ["f16", "bf16"])
+def test_two_precision_checkpoint_nemotron(read_dt):
+    """The Nemotron-3-Super layer at batch 256 with a two-precision checkpoint."""
+    err = run_case(Case(B=256, H=128, dv=64, dk=128, L=16, steps=40, state_dt="f32", rec_dt="f16",
+                        io_dt="bf16", read_dt=read_dt, sample=[0, 100, 255], n_blocks=260, seed=61))
+    assert_within(err, TOL_LOW)
+    assert err["ckpt_flush"] <= TOL_F32 and err["flushes"] == 2
