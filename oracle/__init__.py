@@ -28,6 +28,8 @@ import subprocess
 
 import numpy as np
 
+from .formats import half_ulp, round_to  # noqa: F401  (read-copy roundings)
+
 MAMBA2 = 0
 GDN = 1
 
@@ -235,25 +237,13 @@ class ReplayModel:
         return self.w.reshape(self.B, self.H)
 
 
-def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to fp16 / bf16 (round to nearest even, the
-    libraries' casts) and return them as float64."""
-    if dtype == "f16":
-        return x.astype(np.float16).astype(np.float64)
-    if dtype == "bf16":
-        import torch
-        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
-    if dtype == "f32":
-        return x.astype(np.float32).astype(np.float64)
-    raise ValueError(dtype)
-
-
 class TwoCopyReplayModel(ReplayModel):
-    """Checkpoint + buffer with two checkpoint copies (blog "The precision
-    argument, derived"): the recurrence copy C is exact (float64) and is read
-    only by flushes; the read copy C_lo is C rounded to `read_dtype` at each
-    flush, from the same unrounded fold, and is what non-flush steps read.
-    Mamba-2 form."""
+    """Checkpoint + buffer with two checkpoint copies (review "ReplaySSM,
+    checked", section "The precision argument, derived"): the recurrence copy
+    C is exact (float64) and is read only by flushes; the read copy C_lo is C
+    rounded to `read_dtype` (formats.round_to: f16, bf16 or e4m3 with a
+    power-of-two scale per state row) at each flush, from the same unrounded
+    fold, and is what non-flush steps read.  Mamba-2 form."""
 
     def __init__(self, B, H, dv, dk, L, read_dtype="f16", oracle=None):
         super().__init__(MAMBA2, B, H, dv, dk, L, oracle)
@@ -280,6 +270,19 @@ class TwoCopyReplayModel(ReplayModel):
         super().fold(rows_mask)
         mask = np.repeat(np.asarray(rows_mask, bool), self.H)
         self.C_lo[mask] = round_to(self.C[mask], self.read_dtype)
+
+    def read_error_bound(self, q, lam):
+        """Before step(q, ..., lam, ...): per output component, the most the
+        read copy can move a non-flush output, gamma_h sum_c u_ic |q_c| with
+        u = half an ulp of the recurrence copy in the read format and
+        gamma_h = exp(buffered log-decays + lam) [B, H, dv]."""
+        B, H = self.B, self.H
+        n = B * H
+        q = _vec(q, n)
+        held = np.arange(self.cap)[None, :] < self.w[:, None]
+        g = np.exp((self.rec_lam * held).sum(axis=1) + _scal(lam, n))
+        u = half_ulp(self.C, self.read_dtype)
+        return (g[:, None] * np.einsum("nic,nc->ni", u, np.abs(q))).reshape(B, H, self.dv)
 
 
 def _vec(a, n):

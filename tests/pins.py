@@ -14,6 +14,11 @@ Sources of the facts (pages):
   [pr]   vLLM pull request "[Kernel] ReplaySSM: cache SSM inputs for faster
          Gated DeltaNet standard decode": cursor and flush rule ("CUDA graphs
          and continuous batching").
+  [rev]  review "ReplaySSM, checked": two checkpoint copies ("The precision
+         argument, derived").
+  [ofp8] Open Compute Project "OCP 8-bit Floating Point Specification
+         (OFP8)": the E4M3 encoding (bias 7, no infinities, max 448,
+         subnormals m/8 * 2^-6); the format is not on the pages.
 """
 from __future__ import annotations
 
@@ -298,35 +303,43 @@ def pin_cursor_forced_flush(orc):
 
 # ------------------------------------------------- two-precision checkpoint --
 def pin_two_copy_read_error_is_one_rounding(orc):
-    """[blog] "The precision argument, derived": with an exact recurrence copy
+    """[rev] "The precision argument, derived": with an exact recurrence copy
     and a read copy rounded once per flush, a non-flush step h positions into
     the window outputs o_t + gamma_h eps_m q_t, eps_m = C_lo - C; a flush step
     reads the recurrence copy and is exact.  Checked against the exact
-    checkpoint + buffer route on the same inputs, with eps_m one fp16
-    rounding of the last checkpoint."""
+    checkpoint + buffer route on the same inputs for each read format, with
+    eps_m one rounding of the last checkpoint (within half an ulp of it), and
+    the model's error bound gamma_h sum |u| |q| holding and not loose."""
     B, H, dv, dk, L = 2, 3, 16, 32, 4
-    exact = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
-    two = oracle.TwoCopyReplayModel(B, H, dv, dk, L, "f16", oracle=orc)
-    ws, fls = orc.cursor_run(L, 0, 40)
-    since = np.zeros((B, H))  # log of gamma_h: decays since the checkpoint, current token included
-    for s in range(40):
-        q, k, v, lam, _ = _tok(M2, 21, s, B, H, dv, dk, 0.001, 0.01)
-        since = since + lam
-        eps = (two.C_lo - two.C).reshape(B, H, dv, dk)
-        o_e = exact.step(q, k, v, lam, np.full(B, fls[s]))
-        o_t = two.step(q, k, v, lam, np.full(B, fls[s]))
-        if fls[s]:
-            assert _rel(o_t, o_e) < 1e-12, s
-            since = np.zeros((B, H))
-        else:
-            want = np.exp(since)[..., None] * np.einsum("bhic,bhc->bhi", eps, q)
-            d = o_t - o_e
-            scale = np.abs(o_e).max()
-            assert np.abs(d - want).max() <= 1e-12 * scale, s
-        # the read copy is one rounding of the recurrence copy
-        C = two.C
-        assert np.all(np.abs(two.C_lo - C) <= np.abs(C) * 2.0**-11 + 2.0**-25), s
-        assert _rel(two.C.reshape(B, H, dv, dk), exact.checkpoint()) < 1e-12
+    for dt in ("f16", "bf16", "e4m3"):
+        exact = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+        two = oracle.TwoCopyReplayModel(B, H, dv, dk, L, dt, oracle=orc)
+        ws, fls = orc.cursor_run(L, 0, 40)
+        since = np.zeros((B, H))  # log of gamma_h: decays since the checkpoint, current token included
+        tight = 0.0
+        for s in range(40):
+            q, k, v, lam, _ = _tok(M2, 21, s, B, H, dv, dk, 0.001, 0.01)
+            since = since + lam
+            eps = (two.C_lo - two.C).reshape(B, H, dv, dk)
+            bound = two.read_error_bound(q, lam)
+            o_e = exact.step(q, k, v, lam, np.full(B, fls[s]))
+            o_t = two.step(q, k, v, lam, np.full(B, fls[s]))
+            if fls[s]:
+                assert _rel(o_t, o_e) < 1e-12, (dt, s)
+                since = np.zeros((B, H))
+            else:
+                want = np.exp(since)[..., None] * np.einsum("bhic,bhc->bhi", eps, q)
+                d = o_t - o_e
+                scale = np.abs(o_e).max()
+                assert np.abs(d - want).max() <= 1e-12 * scale, (dt, s)
+                assert np.all(np.abs(d) <= bound * (1 + 1e-9) + 1e-12 * scale), (dt, s)
+                if s > 4:
+                    tight = max(tight, float((np.abs(d) / np.maximum(bound, 1e-300)).max()))
+            # the read copy is one rounding of the recurrence copy
+            C = two.C
+            assert np.all(np.abs(two.C_lo - C) <= oracle.half_ulp(C, dt)), (dt, s)
+            assert _rel(two.C.reshape(B, H, dv, dk), exact.checkpoint()) < 1e-12
+        assert tight > 0.05, (dt, tight)
 
 
 def pin_two_copy_error_does_not_accumulate(orc):
@@ -355,6 +368,59 @@ def pin_two_copy_error_does_not_accumulate(orc):
     assert late_single > 2 * late_two, (late_single, late_two)
 
 
+def pin_e4m3_matches_library_cast(orc):
+    """[ofp8] E4M3 codes with round to nearest even: equal to torch's
+    float8_e4m3fn cast (a library routine) on fp32 values spread over the
+    whole finite range, ties and subnormals included; decoding equals the
+    library's for all 256 codes."""
+    import torch
+    from oracle import formats
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(20000) * np.exp2(rng.uniform(-14, 9, 20000))
+    ties = np.array([1 + 1 / 16, 1 + 3 / 16, 2.0**-9 * 1.5, 2.0**-9 * 2.5, 2.0**-10, 416.0, 240.0 + 8])
+    x = np.concatenate([x, ties, -ties, [0.0, -0.0, 448.0, -448.0]])
+    x = x[np.abs(x) <= 448].astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(formats.e4m3_encode(x), want)
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    ours = formats.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib)) and np.array_equal(ours[~np.isnan(lib)], lib[~np.isnan(lib)])
+
+
+def pin_e4m3_spec_values(orc):
+    """[ofp8] Values the specification fixes: max normal 448 = S.1111.110,
+    min normal 2^-6 = S.0001.000, max subnormal 7/8 2^-6, min subnormal 2^-9,
+    1.0 = S.0111.000; halfway cases go to the even mantissa."""
+    from oracle import formats
+    enc = lambda v: int(formats.e4m3_encode(np.array([v]))[0])
+    assert enc(448.0) == 0x7E and enc(-448.0) == 0xFE
+    assert enc(2.0**-6) == 0x08 and enc(0.875 * 2.0**-6) == 0x07 and enc(2.0**-9) == 0x01
+    assert enc(1.0) == 0x38 and enc(-2.0) == 0xC0 and enc(0.0) == 0x00
+    assert enc(1 + 1 / 16) == 0x38 and enc(1 + 3 / 16) == 0x3A      # ties to even
+    assert enc(2.0**-10) == 0x00 and enc(3 * 2.0**-10) == 0x02       # subnormal ties
+    assert enc(0.9375 * 2.0**-6) == 0x08                             # rounds up into the normals
+    assert np.isnan(formats.e4m3_decode(np.array([0x7F]))[0])
+
+
+def pin_read_rounding_within_half_ulp(orc):
+    """Every read format: round_to moves a value by at most half an ulp of
+    its representation, the bound is reached (not loose), and an E4M3 row's
+    power-of-two scale is the smallest that keeps the row within 448."""
+    from oracle import formats
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((400, 64)) * np.exp2(rng.uniform(-12, 12, (400, 1)))
+    for dt in ("f16", "bf16", "e4m3"):
+        u = formats.half_ulp(x, dt)
+        d = np.abs(formats.round_to(x, dt) - x)
+        assert np.all(d <= u), dt
+        assert (d / u).max() > 0.9, dt
+    e = formats.e4m3_row_exponent(x)
+    amax = np.abs(x).max(axis=1)
+    assert np.all(np.ldexp(amax, -e) <= 448.0) and np.all(np.ldexp(amax, -(e - 1)) > 448.0)
+    assert formats.e4m3_row_exponent(np.zeros((1, 8)))[0] == formats.E4M3_MIN_EXP
+
+
 ALL_PINS = [
     pin_identity_mamba2_tiny,
     pin_identity_mamba2_long_memory,
@@ -372,4 +438,7 @@ ALL_PINS = [
     pin_cursor_forced_flush,
     pin_two_copy_read_error_is_one_rounding,
     pin_two_copy_error_does_not_accumulate,
+    pin_e4m3_matches_library_cast,
+    pin_e4m3_spec_values,
+    pin_read_rounding_within_half_ulp,
 ]

@@ -132,3 +132,68 @@ def test_two_copy_mutant_is_caught(monkeypatch, kind):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"two-copy mutant {kind} passed both pins"
+
+
+# ---------------------------------------------- read-format mutants --
+def _format_mutants():
+    import numpy as np
+    from oracle import formats as F
+    enc, rexp, hu = F.e4m3_encode, F.e4m3_row_exponent, F.half_ulp
+
+    def truncating_encode(y):
+        # rounds toward zero instead of to nearest even
+        y = np.asarray(y, np.float64)
+        a = np.abs(y)
+        fr, ex = np.frexp(np.maximum(a, 2.0**-6))
+        E = ex - 1
+        q = np.where(a < 2.0**-6, 2.0**-9, np.ldexp(1.0, (E - 3).astype(np.int32)))
+        code = np.where(a < 2.0**-6, np.floor(a / q), (E + 7) * 8 + np.floor(a / q) - 8).astype(np.int64)
+        return (np.minimum(code, 0x7E) | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+    def fnuz_encode(y):
+        # the other common E4M3 variant: exponent bias 8
+        return enc(np.asarray(y, np.float64) * 2.0)
+
+    return {
+        "e4m3_truncates": ("e4m3_encode", truncating_encode),
+        "e4m3_bias_8": ("e4m3_encode", fnuz_encode),
+        "row_exponent_one_low": ("e4m3_row_exponent", lambda x: rexp(x) - 1),
+        "row_exponent_not_minimal": ("e4m3_row_exponent", lambda x: rexp(x) + 1),
+        "half_ulp_too_big": ("half_ulp", lambda x, dt: 2 * hu(x, dt)),
+        "half_ulp_too_small": ("half_ulp", lambda x, dt: 0.5 * hu(x, dt)),
+    }
+
+
+@pytest.mark.parametrize("kind", sorted(_format_mutants()))
+def test_format_mutant_is_caught(monkeypatch, kind):
+    import pins
+    from oracle import formats
+    name, fn = _format_mutants()[kind]
+    monkeypatch.setattr(formats, name, fn)
+    if name == "half_ulp":
+        monkeypatch.setattr(oracle, "half_ulp", fn)
+    caught = []
+    for pin in (pins.pin_e4m3_matches_library_cast, pins.pin_e4m3_spec_values,
+                pins.pin_read_rounding_within_half_ulp, pins.pin_two_copy_read_error_is_one_rounding):
+        try:
+            pin(oracle.get())
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"format mutant {kind} passed every pin"
+
+
+def test_two_copy_bound_without_decay_is_caught(monkeypatch):
+    """read_error_bound that forgets gamma_h (too loose on decayed steps)."""
+    import numpy as np
+    import pins
+    from oracle import TwoCopyReplayModel, _vec, half_ulp
+
+    class Broken(TwoCopyReplayModel):
+        def read_error_bound(self, q, lam):
+            n = self.B * self.H
+            u = half_ulp(self.C, self.read_dtype)
+            return np.einsum("nic,nc->ni", u, np.abs(_vec(q, n))).reshape(self.B, self.H, self.dv) * 50.0
+
+    monkeypatch.setattr(oracle, "TwoCopyReplayModel", Broken)
+    with pytest.raises(AssertionError):
+        pins.pin_two_copy_read_error_is_one_rounding(oracle.get())
