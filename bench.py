@@ -67,11 +67,19 @@ def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay", read
     if kind == "conventional":
         return B * (H * (2 * ms + io_b) + 4)
     if read:
-        ml = dv * dk * _ES[read]
+        ml = read_copy_bytes(dv, dk, read)
         per_head = (ms + ms + ml if flush else ml + r) + w * r + io_b
     else:
         per_head = ms + w * r + (ms if flush else r) + io_b
     return B * (H * per_head + 9)
+
+
+def read_copy_bytes(dv, dk, read):
+    """One head's read copy: d_v d_k elements, plus an fp32 scale per state
+    row for E4M3."""
+    if read == "e4m3":
+        return dv * dk + 4 * dv
+    return dv * dk * _ES[read]
 
 
 def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay", read=None):
@@ -107,15 +115,19 @@ def load_traffic(workload_key: str):
 
 
 # --------------------------------------------------------------- CPU baseline --
-def cpu_baseline(cfg, n_steps=16, rows=None):
-    """The fp64 oracle (both routes) on the host cores, one window of steps
-    over a bounded sample of rows; reported as steps/s of the full batch."""
+def cpu_baseline(cfg, n_steps=None, rows=None, min_seconds=10.0, max_windows=32):
+    """The fp64 oracle (both routes) on the host cores over a bounded sample:
+    `rows` rows (default all), whole windows of L steps repeated until the
+    checkpoint + buffer route has run `min_seconds` (at most `max_windows`
+    windows), after one untimed window; reported as steps/s of the full
+    batch."""
     import oracle
     import workloads
     o = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     o.set_num_threads(threads)
     B = rows or cfg["B"]
+    n_steps = n_steps or cfg["L"]
     toks = [workloads.tokens(cfg["form"], 7, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
             for s in range(n_steps)]
     f64 = [(t.q.double().numpy(), t.k.double().numpy(), t.v.double().numpy(), t.lam.double().numpy(),
@@ -125,27 +137,39 @@ def cpu_baseline(cfg, n_steps=16, rows=None):
         rep = oracle.TwoCopyReplayModel(B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["read"])
     else:
         rep = oracle.ReplayModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"])
+    def window(model, replay):
+        for s in range(n_steps):
+            q, k, v, lam, beta = f64[s]
+            if replay:
+                model.step(q, k, v, lam, np.full(B, fl[s]), beta)
+            else:
+                model.step(q, k, v, lam, beta)
+
+    window(rep, True)  # untimed: first touch of the model's memory
+    n_win = 0
     t0 = time.perf_counter()
-    for s in range(n_steps):
-        q, k, v, lam, beta = f64[s]
-        rep.step(q, k, v, lam, np.full(B, fl[s]), beta)
+    while n_win < max_windows and (n_win == 0 or time.perf_counter() - t0 < min_seconds):
+        window(rep, True)
+        n_win += 1
     t_rep = time.perf_counter() - t0
     del rep
     conv = oracle.ConventionalModel(cfg["form"], B, cfg["H"], cfg["dv"], cfg["dk"])
+    window(conv, False)
     t0 = time.perf_counter()
-    for s in range(n_steps):
-        q, k, v, lam, beta = f64[s]
-        conv.step(q, k, v, lam, beta)
+    for _ in range(n_win):
+        window(conv, False)
     t_conv = time.perf_counter() - t0
     scale = B / cfg["B"]
+    total = n_win * n_steps
+    route = "two-copy checkpoint+buffer" if cfg.get("read") else "checkpoint+buffer"
     return {
-        "value": round(n_steps * scale / t_rep, 4),
+        "value": round(total * scale / t_rep, 4),
         "unit": "steps/s",
         "cores": o.num_threads(),
         "kind": "oracle",
-        "sample": (f"fp64 oracle, checkpoint+buffer route, {n_steps} steps (one window) over "
+        "sample": (f"fp64 oracle, {route} route, {total} steps ({n_win} windows of {n_steps}) over "
                    f"{B} of {cfg['B']} rows x {cfg['H']} heads; conventional route "
-                   f"{round(n_steps * scale / t_conv, 4)} steps/s; {t_rep + t_conv:.1f} s of CPU time"),
+                   f"{round(total * scale / t_conv, 4)} steps/s; {t_rep + t_conv:.1f} s of CPU time"),
     }
 
 
@@ -300,7 +324,7 @@ def suite_stack(out, n_layers=40):
     """40 Mamba-2 layers at the Nemotron-3-Super shape, batch 256: time and
     algorithmic bytes of one decode step over all layers (one launch per
     layer), replay for L in {8, 16, 32} with fp32 and fp16 checkpoints, replay
-    at L=16 with an fp32 recurrence copy and an fp16 or bf16 read copy, and
+    at L=16 with an fp32 recurrence copy and an fp16, bf16 or E4M3 read copy, and
     the conventional step with fp32 and fp16 state.  Two windows timed after
     one window of warm-up."""
     import torch
@@ -310,7 +334,7 @@ def suite_stack(out, n_layers=40):
     results = {}
     runs = [("conventional", 16, "f32", None), ("conventional", 16, "f16", None)]
     runs += [("replay", L, st, None) for st in ("f32", "f16") for L in (8, 16, 32)]
-    runs += [("replay", 16, "f32", rd) for rd in ("f16", "bf16")]
+    runs += [("replay", 16, "f32", rd) for rd in ("f16", "bf16", "e4m3")]
     for kind, L, state, read in runs:
         cfg = dict(base, L=L, state=state, read=read)
         layers = _layer_stack(cfg, base["B"], n_layers, dev)
@@ -438,7 +462,7 @@ def main(argv=None):
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--L", type=int, default=None)
     ap.add_argument("--state", default=None, choices=["f32", "f16"])
-    ap.add_argument("--read", default=None, choices=["f16", "bf16"],
+    ap.add_argument("--read", default=None, choices=["f16", "bf16", "e4m3"],
                     help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy")
     ap.add_argument("--pools", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")

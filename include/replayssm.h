@@ -62,7 +62,9 @@ typedef enum {
     RS_EHIP = -3           /* the HIP runtime reported an error at launch             */
 } rs_status;
 
-typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2 } rs_dtype;
+/* RS_E4M3: OCP 8-bit floating point E4M3 (Open Compute Project "OCP 8-bit
+ * Floating Point Specification (OFP8)"), valid only as a read_dtype. */
+typedef enum { RS_F32 = 0, RS_F16 = 1, RS_BF16 = 2, RS_E4M3 = 3 } rs_dtype;
 
 typedef enum {
     RS_MAMBA2 = 0,  /* S_t = alpha S_{t-1} + v k^T                       */
@@ -76,15 +78,20 @@ typedef enum {
  * state_dtype:  RS_F32 or RS_F16 (checkpoint / conventional state).
  * record_dtype: RS_F32 or RS_F16 (buffered x and k; the log-decay is fp32).
  * io_dtype:     RS_F32, RS_F16 or RS_BF16 (q, k, v inputs).
- * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16 or
- *               RS_BF16 for a two-precision checkpoint (blog "The precision
- *               argument, derived"): state_dtype RS_F32 is the recurrence
- *               copy, read by flushes only; a second copy in read_dtype is
- *               what non-flush steps read.  A flush folds from the
- *               recurrence copy and rewrites both copies from the same
+ * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16,
+ *               RS_BF16 or RS_E4M3 for a two-precision checkpoint (blog "The
+ *               precision argument, derived"): state_dtype RS_F32 is the
+ *               recurrence copy, read by flushes only; a second copy in
+ *               read_dtype is what non-flush steps read.  A flush folds from
+ *               the recurrence copy and rewrites both copies from the same
  *               unrounded values, so the read copy's rounding never enters
  *               the recurrence.  Mamba-2 form only (RS_EUNSUPPORTED for GDN:
  *               its buffered corrections would carry the read copy's error).
+ *               All roundings are to nearest even.  An RS_E4M3 read copy
+ *               scales each state row (the d_k entries of one output
+ *               component) by its own power of two 2^e, e the smallest
+ *               integer with max|row| * 2^-e <= 448 (and at least -100): it
+ *               stores E4M3(row * 2^-e) and the fp32 scale 2^e.
  */
 typedef struct {
     int32_t form;
@@ -109,6 +116,8 @@ typedef struct {
  *   rec_lam  [n_heads][slots]       fp32 log-decay
  *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
  *                                   ckpt_lo_off is 0 otherwise)
+ *   ckpt_sc  [n_heads][d_v]         fp32 row scales of an RS_E4M3 read copy
+ *                                   (ckpt_scale_off is 0 otherwise)
  * slots = L - 1.  block_bytes is a multiple of 256.
  */
 typedef struct {
@@ -120,6 +129,7 @@ typedef struct {
     int32_t slots;
     int32_t reserved;
     int64_t ckpt_lo_off;
+    int64_t ckpt_scale_off;
 } rs_block_layout;
 
 /* Host, pure.  Fills *out for `layer`.  RS_EINVAL / RS_EUNSUPPORTED on a bad

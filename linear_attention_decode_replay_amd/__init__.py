@@ -24,7 +24,7 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayssm.so")
 
 MAMBA2, GDN = 0, 1
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, E4M3 = 0, 1, 2, 3
 RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
 
 _c = ctypes
@@ -40,7 +40,7 @@ class RsLayer(_c.Structure):
 class RsBlockLayout(_c.Structure):
     _fields_ = [("ckpt_off", _c.c_int64), ("rec_x_off", _c.c_int64), ("rec_k_off", _c.c_int64),
                 ("rec_lam_off", _c.c_int64), ("block_bytes", _c.c_int64), ("slots", _c.c_int32),
-                ("reserved", _c.c_int32), ("ckpt_lo_off", _c.c_int64)]
+                ("reserved", _c.c_int32), ("ckpt_lo_off", _c.c_int64), ("ckpt_scale_off", _c.c_int64)]
 
 
 class RsBatch(_c.Structure):
@@ -104,13 +104,14 @@ def last_error() -> str:
 
 
 # ------------------------------------------------------------------ structs --
-_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
+_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
 
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
           record_dtype="f16", io_dtype="bf16", read_dtype=None) -> RsLayer:
-    """read_dtype: None for a single checkpoint, "f16" / "bf16" for a
-    two-precision checkpoint (fp32 recurrence copy + read copy)."""
+    """read_dtype: None for a single checkpoint, "f16" / "bf16" / "e4m3" for
+    a two-precision checkpoint (fp32 recurrence copy + read copy; E4M3 with a
+    power-of-two scale per state row)."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
                    code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype))
@@ -237,13 +238,23 @@ class Pool:
                             self._tdt[L.record_dtype], (L.n_heads, s, L.d_k))
 
     def ckpt_lo(self):
-        """[n_blocks, H, d_v, d_k] read copy of a two-precision checkpoint."""
+        """[n_blocks, H, d_v, d_k] read copy of a two-precision checkpoint
+        (E4M3: the raw codes as uint8)."""
+        import torch
         L = self.layer
         if L.read_dtype < 0 or L.read_dtype == L.state_dtype:
             raise ValueError("this layer has a single checkpoint")
-        es = 4 if L.read_dtype == F32 else 2
-        return self._region(self.layout.ckpt_lo_off, L.n_heads * L.d_v * L.d_k * es, self._tdt[L.read_dtype],
+        es, dt = {F16: (2, torch.float16), BF16: (2, torch.bfloat16), E4M3: (1, torch.uint8)}[L.read_dtype]
+        return self._region(self.layout.ckpt_lo_off, L.n_heads * L.d_v * L.d_k * es, dt,
                             (L.n_heads, L.d_v, L.d_k))
+
+    def ckpt_scale(self):
+        """[n_blocks, H, d_v] fp32 row scales of an E4M3 read copy."""
+        import torch
+        L = self.layer
+        if L.read_dtype != E4M3:
+            raise ValueError("this layer has no scaled read copy")
+        return self._region(self.layout.ckpt_scale_off, L.n_heads * L.d_v * 4, torch.float32, (L.n_heads, L.d_v))
 
     def rec_lam(self):
         """[n_blocks, H, slots] fp32."""
@@ -253,7 +264,7 @@ class Pool:
 
 
 __all__ = [
-    "MAMBA2", "GDN", "F32", "F16", "BF16", "RsLayer", "RsBlockLayout", "RsBatch", "RsStepIO",
+    "MAMBA2", "GDN", "F32", "F16", "BF16", "E4M3", "RsLayer", "RsBlockLayout", "RsBatch", "RsStepIO",
     "ReplaySSMError", "layer", "block_layout", "layer_supported", "make_batch", "make_io",
     "replay_decode_step", "replay_flush", "conventional_decode_step", "replay_state_reset",
     "rs_meta_step", "rs_meta_advance", "last_error", "Pool", "LIBRARY_PATH",

@@ -32,7 +32,7 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int dtype_bytes(int dt) { return dt == RS_F32 ? 4 : 2; }
+int dtype_bytes(int dt) { return dt == RS_F32 ? 4 : (dt == RS_E4M3 ? 1 : 2); }
 
 const int kMaxL = 64;
 
@@ -48,18 +48,22 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
     for (int dt : {L->state_dtype, L->record_dtype, L->io_dtype})
         if (dt != RS_F32 && dt != RS_F16 && dt != RS_BF16) return fail(RS_EINVAL, "unknown dtype %d", dt);
     if (L->state_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 state is not supported");
-    if (L->read_dtype < -1 || L->read_dtype > RS_BF16) return fail(RS_EINVAL, "unknown read dtype %d", L->read_dtype);
+    if (L->read_dtype < -1 || L->read_dtype > RS_E4M3) return fail(RS_EINVAL, "unknown read dtype %d", L->read_dtype);
     if (two_precision(*L)) {
         if (L->form != RS_MAMBA2)
             return fail(RS_EUNSUPPORTED, "two-precision checkpoint: Mamba-2 form only (a GDN read copy would "
                                          "leak into the buffered corrected values)");
-        if (L->state_dtype != RS_F32 || (L->read_dtype != RS_F16 && L->read_dtype != RS_BF16))
-            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy with an fp16 or bf16 read copy");
+        if (L->state_dtype != RS_F32)
+            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy only");
     }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
-    if (!rs::compiled(kind, *L))
+    if (!rs::compiled(kind, *L)) {
+        if (L->read_dtype == RS_E4M3)
+            return fail(RS_EUNSUPPORTED, "no kernel for an E4M3 read copy with d_v=%d d_k=%d (supported: 64x128, "
+                                         "128x128)", L->d_v, L->d_k);
         return fail(RS_EUNSUPPORTED, "no kernel for d_v=%d d_k=%d (supported: 16x32, 64x128, 128x128)",
                     L->d_v, L->d_k);
+    }
     if (rs::lds_bytes(kind, *L) > kMaxLds)
         return fail(RS_EUNSUPPORTED, "buffer of L=%d records needs %zu bytes of LDS (> %zu)", L->L,
                     rs::lds_bytes(kind, *L), kMaxLds);
@@ -76,9 +80,14 @@ void layout_of(const rs_layer& L, rs_block_layout* o) {
     o->rec_lam_off = align_up(o->rec_k_off + H * slots * L.d_k * rb, 256);
     o->block_bytes = align_up(o->rec_lam_off + H * slots * 4, 256);
     o->ckpt_lo_off = 0;
+    o->ckpt_scale_off = 0;
     if (two_precision(L)) {
         o->ckpt_lo_off = o->block_bytes;
         o->block_bytes = align_up(o->ckpt_lo_off + H * L.d_v * L.d_k * dtype_bytes(L.read_dtype), 256);
+        if (L.read_dtype == RS_E4M3) {
+            o->ckpt_scale_off = o->block_bytes;
+            o->block_bytes = align_up(o->ckpt_scale_off + H * L.d_v * 4, 256);
+        }
     }
     o->slots = (int32_t)slots;
     o->reserved = 0;
@@ -149,6 +158,7 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.reck_off = lay.rec_k_off;
     p.reclam_off = lay.rec_lam_off;
     p.ckpt_lo_off = lay.ckpt_lo_off;
+    p.ckpt_sc_off = lay.ckpt_scale_off;
     p.block_table = b.block_table;
     p.write_pos = b.write_pos;
     p.flush = b.flush;

@@ -17,6 +17,7 @@ struct StepParams {
     int64_t n_blocks;
     int64_t ckpt_off, recx_off, reck_off, reclam_off;
     int64_t ckpt_lo_off;    // read copy of a two-precision checkpoint (else unused)
+    int64_t ckpt_sc_off;    // per-row scales of an E4M3 read copy (else unused)
     const int32_t* block_table;
     const int32_t* write_pos;
     const uint8_t* flush;   // per-row flag (replay step, token-less flush)

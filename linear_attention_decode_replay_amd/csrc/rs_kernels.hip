@@ -50,6 +50,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct tF32 { using S = float; };
 struct tF16 { using S = _Float16; };
 struct tBF16 { using S = uint16_t; };
+// OCP E4M3 codes: the read copy of a two-precision checkpoint only, each state
+// row scaled by a power of two (kScaled).
+struct tE4M3 { using S = uint8_t; };
+template <class T> constexpr bool kScaled = false;
+template <> constexpr bool kScaled<tE4M3> = true;
 
 template <class T> __device__ __forceinline__ float to_f(typename T::S x);
 template <> __device__ __forceinline__ float to_f<tF32>(float x) { return x; }
@@ -118,14 +123,30 @@ __device__ __forceinline__ u32x4 pack16(const float* in) {
     return r;
 }
 
-// N elements of T held as N * sizeof(T) / 16 sixteen-byte chunks.
+// N elements of T held as N * sizeof(T) / 16 sixteen-byte chunks.  E4M3
+// codes widen exactly (every code is an fp32 value), two per instruction;
+// the row's scale is applied by the caller.
 template <class T, int N>
 __device__ __forceinline__ void unpack_n(const u32x4* in, float* out) {
     using S = typename T::S;
-    S tmp[N];
-    __builtin_memcpy(tmp, in, sizeof(tmp));
+    if constexpr (kScaled<T>) {
+        static_assert(N % 16 == 0, "whole chunks of codes");
 #pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = to_f<T>(tmp[i]);
+        for (int i = 0; i < N / 4; ++i) {
+            const int word = (int)in[i / 4][i % 4];
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+            out[4 * i] = lo[0];
+            out[4 * i + 1] = lo[1];
+            out[4 * i + 2] = hi[0];
+            out[4 * i + 3] = hi[1];
+        }
+    } else {
+        S tmp[N];
+        __builtin_memcpy(tmp, in, sizeof(tmp));
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = to_f<T>(tmp[i]);
+    }
 }
 
 template <class T, int N>
@@ -135,6 +156,55 @@ __device__ __forceinline__ void pack_n(const float* in, u32x4* out) {
 #pragma unroll
     for (int i = 0; i < N; ++i) tmp[i] = from_f<T>(in[i]);
     __builtin_memcpy(out, tmp, sizeof(tmp));
+}
+
+// One state row of E4M3 read copy (OCP 8-bit floating point specification:
+// bias 7, largest finite 448).  The row's N * G values are spread over an
+// aligned group of G lanes, N per lane.  Its scale is 2^e with e the smallest
+// integer such that max|x| * 2^-e <= 448 (at least -100): with amax = f 2^E,
+// f in [1, 2), that is e = E - 8, or E - 7 when f > 1.75, read off the bits
+// of amax.  Scaling by 2^-e is exact (v_ldexp_f32), so the only rounding is
+// the conversion to E4M3, to nearest even; no scaled value exceeds 448.
+// Writes N codes to `codes` and returns the scale 2^e.
+template <int N, int G>
+__device__ __forceinline__ float encode_e4m3_row(const float* x, u32x4* codes) {
+    static_assert(N % 16 == 0, "whole chunks of codes");
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < N; ++c) amax = fmaxf(amax, fabsf(x[c]));
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const uint32_t b = __float_as_uint(amax);
+    int e = (int)((b >> 23) & 0xffu) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+    e = max(e, -100);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * i], -e),
+                                                __builtin_amdgcn_ldexpf(x[4 * i + 1], -e), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * i + 2], -e),
+                                            __builtin_amdgcn_ldexpf(x[4 * i + 3], -e), w, true);
+        codes[i / 4][i % 4] = (uint32_t)w;
+    }
+    return __builtin_amdgcn_ldexpf(1.0f, e);
+}
+
+// Store one lane's share of a read-copy row (VEC values at `dst`); for a
+// scaled format, lane 0 of the row's lane group also stores the row scale.
+template <class TL, int VEC, int LPR>
+__device__ __forceinline__ void store_read_row(const float* x, typename TL::S* dst, float* scale, int cc) {
+    if constexpr (kScaled<TL>) {
+        u32x4 codes[VEC / 16];
+        const float sc = encode_e4m3_row<VEC, LPR>(x, codes);
+#pragma unroll
+        for (int i = 0; i < VEC / 16; ++i) __builtin_nontemporal_store(codes[i], reinterpret_cast<u32x4*>(dst) + i);
+        if (cc == 0) *scale = sc;
+    } else {
+        u32x4 lo[VEC * sizeof(typename TL::S) / 16];
+        pack_n<TL, VEC>(x, lo);
+#pragma unroll
+        for (int i = 0; i < (int)(VEC * sizeof(typename TL::S) / 16); ++i)
+            __builtin_nontemporal_store(lo[i], reinterpret_cast<u32x4*>(dst) + i);
+    }
 }
 
 // ------------------------------------------------------- lane-group sums --
@@ -213,7 +283,10 @@ struct Tile {
     static constexpr int VEC = 16 / (int)sizeof(S);           // state elements per 16 B
     static constexpr int LPR = DK / VEC;                       // lanes per state row
     static constexpr int LOADS = DVW * LPR;                    // 16-B chunks per workgroup
-    static constexpr int NT = LOADS / 4 >= 256 ? 256 : (LOADS / 4 >= 128 ? 128 : 64);
+    // at least 4 chunks per thread, 2 for an E4M3 read copy (whose flush rows
+    // hold 4 fp32 recurrence-copy chunks per code chunk)
+    static constexpr int PER = kScaled<TS> ? 2 : 4;
+    static constexpr int NT = LOADS / PER >= 256 ? 256 : (LOADS / PER >= 128 ? 128 : 64);
     static constexpr int RPP = NT / LPR;                       // rows per pass
     static constexpr int NR = DVW / RPP;                       // passes per thread
     static_assert(DV % SPLIT == 0, "split");
@@ -432,6 +505,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     constexpr int KEEP = FORM == kGdn ? 2 : 1;  // Gated DeltaNet keeps (C q, C k) of a row together
     constexpr int NV = KEEP * NR;
     constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr bool SC = kScaled<TL>;                // read copy with per-row scales
     constexpr int HPC = VEC * (int)sizeof(S) / 16;  // recurrence-copy chunks per lane chunk
 
     const TileIds id = tile_ids<SPLIT>(p);
@@ -456,6 +530,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     char* base = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;  // row scales
     R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     float* rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
@@ -476,6 +551,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     if (w > 0) lam_j = rl[min(tid, w - 1)];
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
+    float rsc[NR];  // scales of the owned read-copy rows (scaled formats)
+    if constexpr (SC) {
+        if (!fl) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) rsc[r] = cs[r * RPP + rg];
+        }
+    }
     u32x4 cb[NR * HPC];
     if (!TWO || fl) {
 #pragma unroll
@@ -542,6 +624,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
             if constexpr (FORM == kGdn) b += cf[r][c] * kv[c];
         }
         if constexpr (FORM == kMamba2) {
+            if constexpr (SC) a = fl ? a : rsc[r] * a;
             acc[r] = G * a;
         } else {
             acc[2 * r] = G * a;
@@ -635,11 +718,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
         u32x4 hp[HPC];
         pack_n<TS, VEC>(cf[r], hp);
         st_stream_n<HPC>(ck + off, hp);
-        if constexpr (TWO) {
-            u32x4 lo;
-            pack_n<TL, VEC>(cf[r], &lo);
-            st_stream(cl + off, lo);
-        }
+        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + off, cs + r * RPP + rg, cc);
     }
 }
 
@@ -776,6 +855,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     char* base = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+    float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;
     const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
     const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
     const float* rl = reinterpret_cast<const float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
@@ -819,11 +899,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
         u32x4 hp[HPC];
         pack_n<TS, VEC>(cf[r], hp);
         st_stream_n<HPC>(ck + off, hp);
-        if constexpr (TWO) {
-            u32x4 lo;
-            pack_n<TL, VEC>(cf[r], &lo);
-            st_stream(cl + off, lo);
-        }
+        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + off, cs + r * RPP + rg, cc);
     }
 }
 
@@ -855,6 +931,10 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_state_reset(c
         constexpr int CH = DVW * DK * (int)sizeof(RL) / 16;
         RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + elem0;
         for (int i = threadIdx.x; i < CH; i += NT) st_stream(reinterpret_cast<u32x4*>(cl) + i, z);
+        if constexpr (kScaled<TL>) {
+            float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + id.part * DVW;
+            if ((int)threadIdx.x < DVW) cs[threadIdx.x] = 0.f;
+        }
     }
 }
 
@@ -879,7 +959,8 @@ constexpr bool tile_ok() {
     const int vec = 16 / (int)sizeof(typename TS::S);
     const int lpr = DK / vec;
     const int loads = dvw * lpr;
-    const int nt = loads / 4 >= 256 ? 256 : (loads / 4 >= 128 ? 128 : 64);
+    const int per = kScaled<TS> ? 2 : 4;
+    const int nt = loads / per >= 256 ? 256 : (loads / per >= 128 ? 128 : 64);
     if (lpr < 1 || lpr > 64 || (lpr & (lpr - 1)) || nt % lpr) return false;
     const int rpp = nt / lpr;
     if (dvw % rpp) return false;
@@ -944,13 +1025,18 @@ bool with_form(int form, F&& f) {
 }
 
 // The read copy's type: the state type itself (one checkpoint), or fp16 /
-// bf16 for a two-precision checkpoint over an fp32 recurrence copy.
-template <class TS, class F>
+// bf16 / E4M3 for a two-precision checkpoint over an fp32 recurrence copy.
+// E4M3 needs a head of at least one wave of 16-byte code chunks (64 x 128
+// and 128 x 128; not 16 x 32).
+template <int DV, int DK, class TS, class F>
 bool with_read(int read_dt, int state_dt, F&& f) {
     if (read_dt < 0 || read_dt == state_dt) { f(TS{}); return true; }
     if constexpr (std::is_same<TS, tF32>::value) {
         if (read_dt == RS_F16) { f(tF16{}); return true; }
         if (read_dt == RS_BF16) { f(tBF16{}); return true; }
+        if constexpr (tile_ok<DV, DK, tE4M3, split_for<DV, DK>()>()) {
+            if (read_dt == RS_E4M3) { f(tE4M3{}); return true; }
+        }
     }
     return false;
 }
@@ -990,7 +1076,7 @@ struct Dispatch {
                     });
                     return;
                 }
-                with_read<TS>(L.read_dtype, L.state_dtype, [&](auto tl) {
+                with_read<DV, DK, TS>(L.read_dtype, L.state_dtype, [&](auto tl) {
                     using TL = decltype(tl);
                     constexpr bool TWO = !std::is_same<TS, TL>::value;
                     if (kind == Kind::Reset) {

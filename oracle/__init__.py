@@ -238,8 +238,8 @@ class ReplayModel:
 
 
 class TwoCopyReplayModel(ReplayModel):
-    """Checkpoint + buffer with two checkpoint copies (review "ReplaySSM,
-    checked", section "The precision argument, derived"): the recurrence copy
+    """Checkpoint + buffer with two checkpoint copies (blog, section "The
+    precision argument, derived"): the recurrence copy
     C is exact (float64) and is read only by flushes; the read copy C_lo is C
     rounded to `read_dtype` (formats.round_to: f16, bf16 or e4m3 with a
     power-of-two scale per state row) at each flush, from the same unrounded

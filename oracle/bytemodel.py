@@ -5,10 +5,9 @@ TEST INFRASTRUCTURE, NOT PRODUCT CODE (see the package docstring).
 All formulas follow the blog "ReplaySSM: an SSM decoder that writes its state
 once every 16 tokens", section "The identity" (state and record terms of one
 window), "Output without a state" (shrink of the state-building term) and
-"Why 16" (the window-length optimum); the two-copy window follows the review
-"ReplaySSM, checked", section "The precision argument, derived" (non-flush
-steps read only the read copy; a flush reads the recurrence copy and writes
-both).  Units are bytes per head unless a
+"Why 16" (the window-length optimum); the two-copy window follows section
+"The precision argument, derived" (non-flush steps read only the read copy;
+a flush reads the recurrence copy and writes both).  Units are bytes per head unless a
 function says otherwise.
 """
 from __future__ import annotations

@@ -2,11 +2,12 @@
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE (see the package docstring).
 
-A two-precision checkpoint (review "ReplaySSM, checked", section "The
-precision argument, derived") keeps a read copy that is one rounding of the
-recurrence copy.  This module defines that rounding for each read format,
-and the largest error it can make (half a unit in the last place), which is
-what bounds a non-flush step's output error.
+A two-precision checkpoint (blog "ReplaySSM: an SSM decoder that writes its
+state once every 16 tokens", section "The precision argument, derived")
+keeps a read copy that is one rounding of the recurrence copy.  This module
+defines that rounding for each read format, and the largest error it can
+make (half a unit in the last place), which is what bounds a non-flush
+step's output error.
 
   f16, bf16   IEEE binary16 / bfloat16, round to nearest even (the libraries'
               casts).

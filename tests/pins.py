@@ -10,12 +10,11 @@ Sources of the facts (pages):
          tokens": recurrence ("Why a fixed-size state is not cheap to
          decode"), the unrolled identity ("The identity"), the output-only
          bracketing ("Output without a state"), the delta-rule expansion
-         ("The delta-rule wrinkle").
+         ("The delta-rule wrinkle"), two checkpoint copies ("The precision
+         argument, derived").
   [pr]   vLLM pull request "[Kernel] ReplaySSM: cache SSM inputs for faster
          Gated DeltaNet standard decode": cursor and flush rule ("CUDA graphs
          and continuous batching").
-  [rev]  review "ReplaySSM, checked": two checkpoint copies ("The precision
-         argument, derived").
   [ofp8] Open Compute Project "OCP 8-bit Floating Point Specification
          (OFP8)": the E4M3 encoding (bias 7, no infinities, max 448,
          subnormals m/8 * 2^-6); the format is not on the pages.
@@ -303,7 +302,7 @@ def pin_cursor_forced_flush(orc):
 
 # ------------------------------------------------- two-precision checkpoint --
 def pin_two_copy_read_error_is_one_rounding(orc):
-    """[rev] "The precision argument, derived": with an exact recurrence copy
+    """[blog] "The precision argument, derived": with an exact recurrence copy
     and a read copy rounded once per flush, a non-flush step h positions into
     the window outputs o_t + gamma_h eps_m q_t, eps_m = C_lo - C; a flush step
     reads the recurrence copy and is exact.  Checked against the exact

@@ -23,13 +23,14 @@ def test_window_bytes_match_model(name, L, state):
 
 
 @pytest.mark.parametrize("L", [1, 2, 8, 16, 32])
-@pytest.mark.parametrize("read", ["f16", "bf16"])
+@pytest.mark.parametrize("read", ["f16", "bf16", "e4m3"])
 def test_two_copy_window_bytes_match_model(L, read):
     c = dict(bench.WORKLOADS["nemotron"])
     args = (c["form"], c["H"], c["dv"], c["dk"], c["B"], "f32", c["rec"], c["io"])
     io = (2 * c["dk"] + c["dv"]) * 2 + 4 + 4 * c["dv"]
     m_hi = bm.state_bytes(c["dv"], c["dk"], 4)
-    m_lo = bm.state_bytes(c["dv"], c["dk"], 2)
+    # E4M3: one byte per element plus an fp32 scale per state row
+    m_lo = bm.state_bytes(c["dv"], c["dk"], 1) + 4 * c["dv"] if read == "e4m3" else bm.state_bytes(c["dv"], c["dk"], 2)
     rec = bm.record_bytes(c["dv"], c["dk"])
     got = bench.window_bytes(*args, L, read=read) - c["B"] * c["H"] * L * io - 9 * c["B"] * L
     assert got == c["B"] * c["H"] * bm.two_copy_window_bytes(L, m_hi, m_lo, rec)
