@@ -115,7 +115,13 @@ typedef struct {
  *   rec_k    [n_heads][slots][d_k]  record_dtype
  *   rec_lam  [n_heads][slots]       fp32 log-decay
  *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
- *                                   ckpt_lo_off is 0 otherwise)
+ *                                   ckpt_lo_off is 0 otherwise), each row of
+ *                                   d_k elements in lane order: with n read
+ *                                   elements per 16 bytes, stored position p
+ *                                   (chunk c = p / n, e = p mod n) holds
+ *                                   column 4 (c + (d_k / n) floor(e / 4)) +
+ *                                   e mod 4, so that both copies are read
+ *                                   and written with contiguous accesses
  *   ckpt_sc  [n_heads][d_v]         fp32 row scales of an RS_E4M3 read copy
  *                                   (ckpt_scale_off is 0 otherwise)
  * slots = L - 1.  block_bytes is a multiple of 256.

@@ -198,6 +198,17 @@ def rs_meta_advance(L: int, steps_since_anchor: np.ndarray, flush: np.ndarray) -
                                 f.ctypes.data))
 
 
+def read_copy_columns(lay: RsLayer) -> np.ndarray:
+    """For a two-precision layer: the column held by each stored position of
+    a read-copy row.  With n read elements per 16 bytes, position p (chunk
+    c = p // n, e = p % n) holds column 4 (c + (d_k // n) (e // 4)) + e % 4
+    (4 = fp32 recurrence-copy elements per 16 bytes)."""
+    n = {F16: 8, BF16: 8, E4M3: 16}[lay.read_dtype]
+    p = np.arange(lay.d_k)
+    c, e = p // n, p % n
+    return 4 * (c + (lay.d_k // n) * (e // 4)) + e % 4
+
+
 # ------------------------------------------------------------ device memory --
 class Pool:
     """The paged block pool of one layer, allocated with torch on a device,
@@ -248,6 +259,11 @@ class Pool:
         return self._region(self.layout.ckpt_lo_off, L.n_heads * L.d_v * L.d_k * es, dt,
                             (L.n_heads, L.d_v, L.d_k))
 
+    def ckpt_lo_columns(self):
+        """Column of each stored position of a read-copy row (the read copy
+        keeps each row in lane order; ckpt_lo()[..., i] is column cols[i])."""
+        return read_copy_columns(self.layer)
+
     def ckpt_scale(self):
         """[n_blocks, H, d_v] fp32 row scales of an E4M3 read copy."""
         import torch
@@ -267,5 +283,5 @@ __all__ = [
     "MAMBA2", "GDN", "F32", "F16", "BF16", "E4M3", "RsLayer", "RsBlockLayout", "RsBatch", "RsStepIO",
     "ReplaySSMError", "layer", "block_layout", "layer_supported", "make_batch", "make_io",
     "replay_decode_step", "replay_flush", "conventional_decode_step", "replay_state_reset",
-    "rs_meta_step", "rs_meta_advance", "last_error", "Pool", "LIBRARY_PATH",
+    "rs_meta_step", "rs_meta_advance", "last_error", "Pool", "LIBRARY_PATH", "read_copy_columns",
 ]

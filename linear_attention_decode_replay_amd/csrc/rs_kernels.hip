@@ -340,17 +340,6 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
-template <int C>
-__device__ __forceinline__ void ld_stream_n(const void* p, u32x4* out) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) out[c] = ld_stream(reinterpret_cast<const u32x4*>(p) + c);
-}
-template <int C>
-__device__ __forceinline__ void st_stream_n(void* p, const u32x4* in) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) st_stream(reinterpret_cast<u32x4*>(p) + c, in[c]);
-}
-
 // LDS carve-up shared by the step and flush kernels (DVW = rows owned).
 template <class R>
 struct Lds {
@@ -492,8 +481,17 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // derived"): the block holds the recurrence copy (TS) and a read copy (TL).
 // Non-flush rows stream only the read copy; a flush row loads the recurrence
 // copy, folds in fp32 and stores both copies, each cast from the same
-// unrounded values.  Threads are laid out by the read type, so a flush row
-// moves HPC = sizeof(TS) / sizeof(TL) chunks per lane chunk of the read copy.
+// unrounded values.  Threads are laid out by the read type: lane chunk cc of
+// a row is one 16-byte read-copy chunk and HPC = sizeof(TS) / sizeof(TL)
+// recurrence-copy chunks, which are chunks cc, cc + LPR, cc + 2 LPR, ... of
+// the row, so that every load and store instruction of a wave covers
+// contiguous memory (measured on MI355X: lanes that own consecutive chunks
+// instead cut streaming writes from 5.6 to 2.3 TB/s at two chunks per lane
+// and to 1.1 TB/s at four).  The read copy stores each row in the same lane
+// order: its chunk cc holds the columns EPC (cc + LPR h) + i (h < HPC,
+// i < EPC, EPC = recurrence-copy elements per 16 bytes).  q, k and buffered
+// keys are read in that order too, so every dot product is unchanged.  With
+// a single checkpoint HPC = 1 and the order is the natural one.
 template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL>
 __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(const StepParams p) {
     using T = Tile<DV, DK, TL, SPLIT>;
@@ -507,6 +505,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     constexpr bool TWO = !std::is_same<TS, TL>::value;
     constexpr bool SC = kScaled<TL>;                // read copy with per-row scales
     constexpr int HPC = VEC * (int)sizeof(S) / 16;  // recurrence-copy chunks per lane chunk
+    constexpr int EPC = VEC / HPC;                  // elements per recurrence-copy chunk
 
     const TileIds id = tile_ids<SPLIT>(p);
     // Without a flag array the (always present) cursor array is read in its
@@ -543,9 +542,15 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
 
+    // column of element h * EPC + i of this lane's share of a row
+    const int col0 = EPC * cc;
+    auto col = [col0](int h) { return col0 + EPC * LPR * h; };
     float qv[VEC], kv[VEC];
-    load_f<TI, VEC>(qp + cc * VEC, qv);
-    load_f<TI, VEC>(kp + cc * VEC, kv);
+#pragma unroll
+    for (int h = 0; h < HPC; ++h) {
+        load_f<TI, EPC>(qp + col(h), qv + h * EPC);
+        load_f<TI, EPC>(kp + col(h), kv + h * EPC);
+    }
     const float vi = to_f<TI>(vp[min(tid, DVW - 1)]);
     float lam_j = 0.f;
     if (w > 0) lam_j = rl[min(tid, w - 1)];
@@ -561,7 +566,11 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     u32x4 cb[NR * HPC];
     if (!TWO || fl) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) ld_stream_n<HPC>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, &cb[r * HPC]);
+        for (int r = 0; r < NR; ++r) {
+            const S* rowp = ck + (int64_t)(r * RPP + rg) * DK + col0;
+#pragma unroll
+            for (int h = 0; h < HPC; ++h) cb[r * HPC + h] = ld_stream(rowp + EPC * LPR * h);
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < NR; ++r) cb[r * HPC] = ld_stream(cl + (int64_t)(r * RPP + rg) * DK + cc * VEC);
@@ -580,7 +589,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
         const int j = it * RPP + rg;
         float kj[VEC];
         if (j < w) {
-            load_f<TR, VEC>(s.k + (int64_t)j * DK + cc * VEC, kj);
+#pragma unroll
+            for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(s.k + (int64_t)j * DK + col(h), kj + h * EPC);
         } else {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) kj[c] = kv[c];
@@ -680,7 +690,11 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     if (!fl) {  // uniform across the workgroup
         if (id.part == 0) {
             if (tid == 0) rl[w] = lam;
-            if (rg == 0) store_f<TR, VEC>(rk + (int64_t)w * DK + cc * VEC, kv);
+            if (rg == 0) {
+                R* kd = rk + (int64_t)w * DK + col0;
+#pragma unroll
+                for (int h = 0; h < HPC; ++h) store_f<TR, EPC>(kd + EPC * LPR * h, kv + h * EPC);
+            }
         }
         if constexpr (FORM == kMamba2)
             if (tid < DVW) rx[(int64_t)w * DV + tid] = from_f<TR>(vi);
@@ -703,7 +717,9 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     }
     for (int j = 0; j < w; ++j) {
         float kj[VEC];
-        load_f<TR, VEC>(s.k + (int64_t)j * DK + cc * VEC, kj);
+        const R* kr = s.k + (int64_t)j * DK + col0;
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(kr + EPC * LPR * h, kj + h * EPC);
         const float ej = ge * s.e[j];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -714,11 +730,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const int64_t off = (int64_t)(r * RPP + rg) * DK + cc * VEC;
+        const int64_t rowoff = (int64_t)(r * RPP + rg) * DK;
         u32x4 hp[HPC];
         pack_n<TS, VEC>(cf[r], hp);
-        st_stream_n<HPC>(ck + off, hp);
-        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + off, cs + r * RPP + rg, cc);
+        S* rowp = ck + rowoff + col0;
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) st_stream(rowp + EPC * LPR * h, hp[h]);
+        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + rowoff + cc * VEC, cs + r * RPP + rg, cc);
     }
 }
 
@@ -835,7 +853,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     using R = typename TR::S;
     constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
     constexpr bool TWO = !std::is_same<TS, TL>::value;
-    constexpr int HPC = VEC * (int)sizeof(S) / 16;
+    constexpr int HPC = VEC * (int)sizeof(S) / 16;  // lane order as in k_replay_step
+    constexpr int EPC = VEC / HPC;
 
     const TileIds id = tile_ids<SPLIT>(p);
     const bool flag = row_flag(p.flush, id.row);
@@ -863,12 +882,16 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
 
+    const int col0 = EPC * cc;
+    auto col = [col0](int h) { return col0 + EPC * LPR * h; };
     const float lam_j = rl[min(tid, w - 1)];
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
     u32x4 cb[NR * HPC];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) ld_stream_n<HPC>(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, &cb[r * HPC]);
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) cb[r * HPC + h] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + col(h));
     rec.commit(rk, rx, s.k, s.x);
     decay_weights(lam_j, s.e, s.sc, w, 0.0f);
     __syncthreads();
@@ -884,7 +907,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     }
     for (int j = 0; j < w; ++j) {
         float kj[VEC];
-        load_f<TR, VEC>(s.k + (int64_t)j * DK + cc * VEC, kj);
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(s.k + (int64_t)j * DK + col(h), kj + h * EPC);
         const float ej = s.e[j];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -895,11 +919,12 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const int64_t off = (int64_t)(r * RPP + rg) * DK + cc * VEC;
+        const int64_t rowoff = (int64_t)(r * RPP + rg) * DK;
         u32x4 hp[HPC];
         pack_n<TS, VEC>(cf[r], hp);
-        st_stream_n<HPC>(ck + off, hp);
-        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + off, cs + r * RPP + rg, cc);
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) st_stream(ck + rowoff + col(h), hp[h]);
+        if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + rowoff + cc * VEC, cs + r * RPP + rg, cc);
     }
 }
 

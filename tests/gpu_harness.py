@@ -212,11 +212,14 @@ def run_case(c: Case, dev="cuda") -> dict:
                 lo = rep.pool.ckpt_lo()[blk[flushed]].cpu().numpy()
                 sc = rep.pool.ckpt_scale()[blk[flushed]].cpu().numpy()
                 codes, e = oracle_formats.e4m3_quantize_rows(ckt.cpu().double().numpy())
+                codes = codes[..., rep.pool.ckpt_lo_columns()]  # stored in lane order
                 assert np.array_equal(lo, codes), f"E4M3 codes, step {s}: {np.sum(lo != codes)} differ"
                 assert np.array_equal(sc, np.ldexp(1.0, e).astype(np.float32)), f"E4M3 scales, step {s}"
             elif c.read_dt:  # the read copy is the RNE cast of the same values, bit for bit
                 lo = rep.pool.ckpt_lo()[blk[flushed]].cpu()
-                assert torch.equal(lo, ckt.cpu().to(workloads.torch_dtype(c.read_dt))), f"read copy, step {s}"
+                cols = torch.as_tensor(rep.pool.ckpt_lo_columns())  # stored in lane order
+                want = ckt.cpu()[..., cols].to(workloads.torch_dtype(c.read_dt))
+                assert torch.equal(lo, want), f"read copy, step {s}"
         if conv is not None and (s % 8 == 7 or s == c.steps - 1):
             st = conv.pool.ckpt()[blk].double().cpu().numpy()
             err["state_conv"] = max(err["state_conv"], rel_err(st, ref.state(), 2))
