@@ -20,7 +20,10 @@ Prints ONE JSON line.  `value` is the decode steps/s of the checkpoint +
 buffer path (wall clock over K steps); the conventional kernel is timed the
 same way under "conventional".  "roofline" describes the dominant kernel
 (the checkpoint + buffer step): algorithmic bytes per launch / mean launch
-time from HIP events on the launch stream, against 8 TB/s.
+time, where the mean is the time between one pair of HIP events recorded on
+the launch stream around the K timed launches, divided by K; against
+8 TB/s.  The per-cursor times ("us_by_cursor") come from one more window per
+pool after the timed region, with events around each launch.
 """
 from __future__ import annotations
 
@@ -216,32 +219,41 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     for s in range(warmup):
         one(s)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # Timed region: K back-to-back steps, bracketed by one pair of HIP events
+    # on the launch stream (no event between launches, so none of their
+    # overhead lands inside a launch).
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cursors = []
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        cursors.append(one(warmup + i, ev[i]))
+        cursors.append(one(warmup + i))
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    times_ms = [a.elapsed_time(b) for a, b in ev]
+    region_ms = start.elapsed_time(end)
     errs = sum(int(d.err.item()) for d in layers)
     if errs:
         raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
     nbytes = [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"],
                          w or 0, bool(f), kind, cfg["read"]) for (w, f) in cursors]
+    # Breakdown by cursor position (after the timed region, not part of it):
+    # one more window per pool with events around every launch.
     by_pos = {}
     if kind == "replay":
-        for (w, f), t in zip(cursors, times_ms):
-            key = "flush" if f else f"w{w}"
-            by_pos.setdefault(key, []).append(t)
+        n_brk = cfg["L"] * n_pools
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_brk)]
+        brk = [one(warmup + steps + i, ev[i]) for i in range(n_brk)]
+        torch.cuda.synchronize()
+        for (w, f), (a, b) in zip(brk, ev):
+            by_pos.setdefault("flush" if f else f"w{w}", []).append(a.elapsed_time(b))
     return {
         "wall_s": wall,
         "steps_per_s": steps / wall,
         "ms_per_step": 1e3 * wall / steps,
-        "kernel_ms_mean": float(np.mean(times_ms)),
+        "kernel_ms_mean": region_ms / steps,
         "bytes_per_launch_mean": float(np.mean(nbytes)),
-        "achieved_gbs": float(np.sum(nbytes) / (np.sum(times_ms) * 1e-3) / 1e9),
+        "achieved_gbs": float(np.sum(nbytes) / (region_ms * 1e-3) / 1e9),
         "by_position_us": {k: round(1e3 * float(np.mean(v)), 1) for k, v in sorted(by_pos.items())},
     }
 
