@@ -87,6 +87,13 @@ class Oracle:
         lib.oc_replay_fold.restype = None
         lib.oc_cursor_run.argtypes = [c_int, i32, i64, _opt(_U8P), _I32P, _U8P]
         lib.oc_cursor_run.restype = None
+        lib.oc_spec_verify.argtypes = [i64, c_int, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P, _I32P,
+                                       _U8P, _F64P, _F64P, _F64P, _F64P, _opt(_U8P), _F64P]
+        lib.oc_spec_verify.restype = i64
+        lib.oc_spec_commit.argtypes = [i64, _I32P, _I32P, _opt(_U8P)]
+        lib.oc_spec_commit.restype = None
+        lib.oc_spec_cursor_run.argtypes = [c_int, c_int, i32, i64, _I32P, _opt(_U8P), _I32P, _U8P]
+        lib.oc_spec_cursor_run.restype = None
         lib.oc_num_threads.restype = c_int
         lib.oc_set_num_threads.argtypes = [c_int]
         self.lib = lib
@@ -133,6 +140,35 @@ class Oracle:
         f = np.zeros(n_steps, np.uint8)
         self.lib.oc_cursor_run(int(L), int(w0), int(n_steps), _u8(forced), w, f)
         return w, f.astype(bool)
+
+    # -- speculative verify (Mamba-2 form) ---------------------------------
+    def spec_verify(self, C, rec_lam, rec_x, rec_k, h, flush, q, k, v, lam, active=None):
+        """q, k: [n, T, dk]; v: [n, T, dv]; lam: [n, T].  Returns out [n, T, dv]."""
+        n, dv, dk = C.shape
+        cap = rec_lam.shape[1]
+        T = q.shape[1]
+        assert rec_x.shape == (n, cap, dv) and rec_k.shape == (n, cap, dk)
+        assert h.dtype == np.int32 and h.shape == (n,)
+        for a in (C, q, k, v, lam):
+            assert a.dtype == np.float64 and a.flags.c_contiguous
+        assert q.shape == (n, T, dk) and k.shape == (n, T, dk) and v.shape == (n, T, dv) and lam.shape == (n, T)
+        out = np.zeros((n, T, dv), np.float64)
+        ovf = self.lib.oc_spec_verify(n, dv, dk, cap, T, C, rec_lam, rec_x, rec_k, h, _u8(flush), q, k, v, lam,
+                                      _u8(active), out)
+        if ovf:
+            raise ValueError(f"{ovf} tiles would overflow the record ring (cap={cap}, T={T})")
+        return out
+
+    def spec_commit(self, h, accepted, active=None):
+        self.lib.oc_spec_commit(h.shape[0], h, np.ascontiguousarray(accepted, np.int32), _u8(active))
+
+    def spec_cursor_run(self, L, T, h0, accepted, forced=None):
+        accepted = np.ascontiguousarray(accepted, np.int32)
+        n_steps = accepted.shape[0]
+        h = np.zeros(n_steps, np.int32)
+        f = np.zeros(n_steps, np.uint8)
+        self.lib.oc_spec_cursor_run(int(L), int(T), int(h0), int(n_steps), accepted, _u8(forced), h, f)
+        return h, f.astype(bool)
 
 
 def _u8(a):
@@ -283,6 +319,91 @@ class TwoCopyReplayModel(ReplayModel):
         g = np.exp((self.rec_lam * held).sum(axis=1) + _scal(lam, n))
         u = half_ulp(self.C, self.read_dtype)
         return (g[:, None] * np.einsum("nic,nc->ni", u, np.abs(q))).reshape(B, H, self.dv)
+
+
+class SpecReplayModel:
+    """Speculative verify from a checkpoint plus a ring of L committed records
+    (blog, "Speculative decoding: rollback becomes a pointer"), B rows x H
+    heads, fp64, Mamba-2 form.  verify() computes the T draft outputs and
+    stores the drafts as records behind the committed ones (after folding the
+    committed records on flush rows); commit() advances the committed pointer."""
+
+    def __init__(self, B, H, dv, dk, L, T, oracle=None):
+        self.o = oracle or get()
+        self.B, self.H, self.dv, self.dk, self.L, self.T = B, H, dv, dk, L, T
+        n = B * H
+        self.cap = L
+        self.C = np.zeros((n, dv, dk))
+        self.rec_lam = np.zeros((n, L))
+        self.rec_x = np.zeros((n, L, dv))
+        self.rec_k = np.zeros((n, L, dk))
+        self.h = np.zeros(n, np.int32)
+
+    def verify(self, q, k, v, lam, flush_rows, active_rows=None):
+        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam: [B, H, T]; flush_rows [B].
+        Returns o [B, H, T, dv]."""
+        B, H, T = self.B, self.H, self.T
+        n = B * H
+        fl = np.repeat(np.asarray(flush_rows, bool), H)
+        act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
+        f = lambda a, d: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T, d))
+        out = self.o.spec_verify(self.C, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, f(q, self.dk),
+                                 f(k, self.dk), f(v, self.dv),
+                                 np.ascontiguousarray(np.asarray(lam, np.float64).reshape(n, T)), act)
+        return out.reshape(B, H, T, self.dv)
+
+    def commit(self, accepted_rows, active_rows=None):
+        acc = np.repeat(np.asarray(accepted_rows, np.int32), self.H)
+        act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), self.H)
+        self.o.spec_commit(self.h, acc, act)
+
+    def fold(self, rows_mask):
+        """Token-less flush of the committed records (the standard step's fold)."""
+        mask = np.repeat(np.asarray(rows_mask, bool), self.H)
+        self.o.replay_fold(self.C, self.rec_lam, self.rec_x, self.rec_k, self.h, mask)
+
+    def committed(self):
+        return self.h.reshape(self.B, self.H)
+
+    def checkpoint(self):
+        return self.C.reshape(self.B, self.H, self.dv, self.dk)
+
+
+class SpecTokenByToken:
+    """The definition a speculative verify must reproduce: the conventional
+    recurrence run token by token.  The committed state S advances only by
+    accepted drafts; verify() runs the T drafts on a copy of S and returns
+    every draft's output (Mamba-2 form)."""
+
+    def __init__(self, B, H, dv, dk, T, S0=None, oracle=None):
+        self.conv = ConventionalModel(MAMBA2, B, H, dv, dk, S0, oracle)
+        self.B, self.H, self.dv, self.dk, self.T = B, H, dv, dk, T
+        self._drafts = None
+
+    def verify(self, q, k, v, lam):
+        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam: [B, H, T]."""
+        q, k, v, lam = (np.asarray(a, np.float64) for a in (q, k, v, lam))
+        S = self.conv.S.copy()
+        outs = []
+        for i in range(self.T):
+            outs.append(self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i]))
+        committed = self.conv.S
+        self.conv.S = S  # the committed state is unchanged until commit()
+        self._drafts = (q, k, v, lam)
+        del committed
+        return np.stack(outs, axis=2)
+
+    def commit(self, accepted_rows):
+        """Advance each row's committed state by its first `accepted` drafts."""
+        q, k, v, lam = self._drafts
+        acc = np.asarray(accepted_rows)
+        for i in range(self.T):
+            rows = acc > i
+            if rows.any():
+                self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i], active_rows=rows)
+
+    def state(self):
+        return self.conv.state()
 
 
 def _vec(a, n):

@@ -79,3 +79,34 @@ def grouped_record_bytes(n_heads: int, d_v: int, d_k: int, n_groups: int) -> int
     d_v-wide 16-bit value row plus a 4-byte step size, per key group one
     d_k-wide 16-bit key ("The identity", paragraph on the released kernel)."""
     return n_heads * (2 * d_v + 4) + n_groups * 2 * d_k
+
+
+# ------------------------------------------------------ speculative verify --
+def snapshot_verify_step_bytes(T: int, m_state: int) -> int:
+    """The snapshot scheme the blog compares against ("Speculative decoding:
+    rollback becomes a pointer"): one state read and one state snapshot
+    written per draft, T + 1 state transfers per verify step."""
+    return (T + 1) * m_state
+
+
+def plain_decode_token_bytes(m_state: int) -> int:
+    """Plain (conventional) decoding: the state read and written per token."""
+    return 2 * m_state
+
+
+def spec_replay_state_bytes_per_token(L: int, T: int, accepted: int, m_state: int,
+                                      n_steps: int = 100000) -> float:
+    """State bytes per committed token of checkpoint + ring verification with
+    T drafts per step, every step accepting `accepted` of them, in steady
+    state: every step reads the checkpoint once; a step whose h committed
+    records leave no room for T more (h + T > L) also writes it.  Counted
+    step by step over n_steps after a warm-up of 4 L steps."""
+    h, reads, writes, tokens = 0, 0, 0, 0
+    for s in range(4 * L + n_steps):
+        flush = h + T > L
+        if s >= 4 * L:
+            reads += 1
+            writes += int(flush)
+            tokens += accepted
+        h = (0 if flush else h) + accepted
+    return (reads + writes) * m_state / tokens

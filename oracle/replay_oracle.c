@@ -17,6 +17,9 @@
  *           Gated DeltaNet standard decode", sections "Core concept",
  *           "CUDA graphs and continuous batching", and the reviewer's comment
  *           giving S_{t-1} q_t and S_{t-1} k_t from checkpoint plus buffer.
+ *   [nv]    NVIDIA technical blog "ReplaySSM: Rethinking state storage for
+ *           faster hybrid model decoding", section "Benefit 2: Simplify
+ *           rollback and speed up verification".
  *
  * Notation.  One tile is one (request row, head).  Its state S is d_v x d_k,
  * stored row-major: S[i*d_k + c].  A token brings v (d_v), k (d_k), q (d_k),
@@ -318,5 +321,125 @@ void oc_cursor_run(int L, int32_t w0, int64_t n_steps, const uint8_t* forced,
         w_out[s] = w;
         flush_out[s] = (uint8_t)f;
         w = f ? 0 : w + 1;
+    }
+}
+
+/*
+ * Speculative verify step, Mamba-2 form ([blog] "Speculative decoding:
+ * rollback becomes a pointer"; [nv] "Benefit 2: Simplify rollback and speed
+ * up verification").  Per tile: checkpoint C, h committed records
+ * j = 1..h (lam_j, x_j, k_j) in slots 0..h-1 of a buffer of `cap` slots, and
+ * T draft tokens i = 1..T with (lam^d_i, v_i, k_i, q_i).  The output for
+ * draft i is the state after the committed records and drafts 1..i, applied
+ * to q_i ([nv]: one read of the checkpoint for all T queries, K^T Q, D the
+ * cumulative decays of the draft positions, W a causally masked matrix of
+ * decays):
+ *     o_i = gamma_{1:h} D_i (C q_i) + sum_{j=1..h} gamma_{j+1:h} D_i (k_j . q_i) x_j
+ *         + sum_{m=1..i} W_{im} (k_m . q_i) v_m
+ *     D_i = prod_{l=1..i} alpha^d_l,   W_{im} = prod_{l=m+1..i} alpha^d_l (m <= i).
+ * flush [n] is decided before acceptance is known; a flushing tile folds
+ * only its committed records,
+ *     C <- gamma_{1:h} C + sum_j gamma_{j+1:h} x_j k_j^T,   h <- 0,
+ * and every tile then stores its T drafts as records in slots h..h+T-1
+ * ([blog]: the drafts are appended behind the committed records; records
+ * past the committed pointer are ignored and later overwritten).  Accepting
+ * drafts is oc_spec_commit.  Inputs: q, k [n][T][dk]; v, out [n][T][dv];
+ * lam [n][T].  Returns the number of tiles whose drafts would not fit the
+ * ring (h + T > cap without a flush, or T > cap); those tiles are left
+ * untouched.
+ */
+int64_t oc_spec_verify(int64_t n, int dv, int dk, int cap, int T, double* C, double* rec_lam,
+                       double* rec_x, double* rec_k, int32_t* h, const uint8_t* flush,
+                       const double* q, const double* k, const double* v, const double* lam,
+                       const uint8_t* active, double* out) {
+    int64_t overflow = 0;
+#pragma omp parallel reduction(+ : overflow)
+    {
+        double* ac = (double*)malloc(sizeof(double) * (size_t)(cap + 2)); /* committed alphas, 1-indexed */
+        double* ad = (double*)malloc(sizeof(double) * (size_t)(T + 2));   /* draft alphas, 1-indexed */
+        double* cq = (double*)malloc(sizeof(double) * (size_t)dv);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n; ++t) {
+            if (active && !active[t]) continue;
+            const int ht = h[t];
+            const int base = flush[t] ? 0 : ht; /* first slot of this step's drafts */
+            if (base + T > cap) { overflow += 1; continue; }
+            double* Ct = C + t * (int64_t)dv * dk;
+            double* lamt = rec_lam + t * (int64_t)cap;
+            double* xt = rec_x + t * (int64_t)cap * dv;
+            double* krt = rec_k + t * (int64_t)cap * dk;
+            const double* qt = q + t * (int64_t)T * dk;
+            const double* kt = k + t * (int64_t)T * dk;
+            const double* vt = v + t * (int64_t)T * dv;
+            const double* lt = lam + t * (int64_t)T;
+            double* ot = out + t * (int64_t)T * dv;
+            for (int j = 1; j <= ht; ++j) ac[j] = exp(lamt[j - 1]);
+            for (int i = 1; i <= T; ++i) ad[i] = exp(lt[i - 1]);
+            const double gh = gamma_range(ac, 1, ht);
+            for (int i = 1; i <= T; ++i) {
+                const double* qi = qt + (int64_t)(i - 1) * dk;
+                const double Di = gamma_range(ad, 1, i);
+                matvec(Ct, qi, dv, dk, cq);
+                for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] = gh * Di * cq[r];
+                for (int j = 1; j <= ht; ++j) {
+                    const double wgt = gamma_range(ac, j + 1, ht) * Di * dot(krt + (int64_t)(j - 1) * dk, qi, dk);
+                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * xt[(int64_t)(j - 1) * dv + r];
+                }
+                for (int m = 1; m <= i; ++m) {
+                    const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);
+                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * vt[(int64_t)(m - 1) * dv + r];
+                }
+            }
+            if (flush[t]) {
+                for (int r = 0; r < dv; ++r)
+                    for (int c = 0; c < dk; ++c) {
+                        double s = gh * Ct[(int64_t)r * dk + c];
+                        for (int j = 1; j <= ht; ++j)
+                            s += gamma_range(ac, j + 1, ht) * xt[(int64_t)(j - 1) * dv + r] * krt[(int64_t)(j - 1) * dk + c];
+                        Ct[(int64_t)r * dk + c] = s;
+                    }
+                h[t] = 0;
+            }
+            for (int i = 0; i < T; ++i) {
+                lamt[base + i] = lt[i];
+                memcpy(xt + (int64_t)(base + i) * dv, vt + (int64_t)i * dv, sizeof(double) * (size_t)dv);
+                memcpy(krt + (int64_t)(base + i) * dk, kt + (int64_t)i * dk, sizeof(double) * (size_t)dk);
+            }
+        }
+        free(ac);
+        free(ad);
+        free(cq);
+    }
+    return overflow;
+}
+
+/*
+ * Commit after a speculative verify ([blog]: "after sampling advances the
+ * committed pointer by a"): h <- h + accepted for each selected tile.  The
+ * verify step has already set h to 0 on a flushing tile.
+ */
+void oc_spec_commit(int64_t n, int32_t* h, const int32_t* accepted, const uint8_t* active) {
+    for (int64_t t = 0; t < n; ++t)
+        if (!active || active[t]) h[t] += accepted[t];
+}
+
+/*
+ * Committed-pointer run of one row under speculative decoding with T drafts
+ * per step and a ring of L committed records ([blog]: flush when h + T > L,
+ * known before the step runs), simulated by counting what the ring holds:
+ *   step s:  flush_s = (h + T > L) or forced_s;  emits (h, flush_s);
+ *            then h = (flush_s ? 0 : h) + accepted_s.
+ * forced may be NULL.
+ */
+void oc_spec_cursor_run(int L, int T, int32_t h0, int64_t n_steps, const int32_t* accepted,
+                        const uint8_t* forced, int32_t* h_out, uint8_t* flush_out) {
+    int32_t hc = h0;
+    for (int64_t s = 0; s < n_steps; ++s) {
+        int held = hc;          /* records the ring holds before the drafts */
+        int room = L - held;    /* committed slots left */
+        const int f = (room < T) || (forced && forced[s]);
+        h_out[s] = hc;
+        flush_out[s] = (uint8_t)f;
+        hc = (f ? 0 : hc) + accepted[s];
     }
 }

@@ -18,6 +18,10 @@ Sources of the facts (pages):
   [ofp8] Open Compute Project "OCP 8-bit Floating Point Specification
          (OFP8)": the E4M3 encoding (bias 7, no infinities, max 448,
          subnormals m/8 * 2^-6); the format is not on the pages.
+  [nv]   NVIDIA technical blog "ReplaySSM: Rethinking state storage for
+         faster hybrid model decoding", section "Benefit 2: Simplify rollback
+         and speed up verification" (speculative verify); with [blog]
+         "Speculative decoding: rollback becomes a pointer".
 """
 from __future__ import annotations
 
@@ -420,6 +424,149 @@ def pin_read_rounding_within_half_ulp(orc):
     assert formats.e4m3_row_exponent(np.zeros((1, 8)))[0] == formats.E4M3_MIN_EXP
 
 
+# ------------------------------------------------------ speculative verify --
+def _spec_tok(seed, step, B, H, T, dv, dk, a_lo=0.05, a_hi=1.0):
+    """T draft tokens per row: q, k [B, H, T, dk], v [B, H, T, dv], lam [B, H, T]."""
+    toks = [_tok(M2, seed, 1000 * step + i, B, H, dv, dk, a_lo, a_hi) for i in range(T)]
+    st = lambda idx: np.stack([t[idx] for t in toks], axis=2)
+    return st(0), st(1), st(2), st(3)
+
+
+def run_spec(orc, B, H, dv, dk, L, T, n_steps, accept, seed=0, a_lo=0.05, a_hi=1.0):
+    """Speculative verify against the token-by-token recurrence.  accept(s)
+    gives the accepted counts [B] of step s.  Returns (max output deviation,
+    max deviation of a flushed checkpoint from the committed state, number of
+    flushing row-steps)."""
+    spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc)
+    ref = oracle.SpecTokenByToken(B, H, dv, dk, T, oracle=orc)
+    h = np.zeros(B, np.int32)
+    worst_o = worst_s = 0.0
+    n_flush = 0
+    for s in range(n_steps):
+        q, k, v, lam = _spec_tok(seed, s, B, H, T, dv, dk, a_lo, a_hi)
+        fl = np.array([orc.spec_cursor_run(L, T, int(h[b]), np.zeros(1, np.int32))[1][0] for b in range(B)])
+        assert np.array_equal(spec.committed()[:, 0], h), "the ring holds a different committed count"
+        o_s = spec.verify(q, k, v, lam, fl)
+        o_r = ref.verify(q, k, v, lam)
+        worst_o = max(worst_o, _rel(o_s, o_r))
+        if fl.any():
+            n_flush += int(fl.sum())
+            worst_s = max(worst_s, _rel(spec.checkpoint()[fl], ref.state()[fl]))
+        a = np.asarray(accept(s), np.int32)
+        spec.commit(a)
+        ref.commit(a)
+        h = np.where(fl, 0, h) + a
+    return worst_o, worst_s, n_flush
+
+
+def pin_spec_identity(orc):
+    """[nv] "Benefit 2" / [blog] "Speculative decoding": the T outputs of one
+    verify, from one checkpoint read, K^T Q and the causal decay matrix, are
+    the outputs of running the drafts token by token; committing a drafts
+    advances the pointer; a flush folds only committed records, and the
+    folded checkpoint equals the committed state.  T = 1, 2, 4 with random
+    accepted counts 0..T (several flushes per row)."""
+    rng = np.random.default_rng(5)
+    for T in (1, 2, 4):
+        o, st, nf = run_spec(orc, 3, 2, 8, 12, 8, T, 30, lambda s: rng.integers(0, T + 1, 3), seed=T)
+        assert nf >= 3, (T, nf)
+        assert o < 1e-12 and st < 1e-12, (T, o, st)
+
+
+def pin_spec_long_memory(orc):
+    """Same identity with slowly decaying heads (the checkpoint term dominant)."""
+    o, st, nf = run_spec(orc, 2, 2, 8, 12, 16, 4, 24, lambda s: np.full(2, 4), seed=9, a_lo=0.001, a_hi=0.01)
+    assert nf >= 4 and o < 1e-12 and st < 1e-12, (o, st, nf)
+
+
+def pin_spec_causal(orc):
+    """Draft i's output depends on drafts 1..i only (W is causally masked):
+    changing drafts after i leaves o_1..o_i bit-identical."""
+    B, H, dv, dk, L, T = 2, 2, 8, 12, 16, 4
+    outs = []
+    for variant in range(2):
+        spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc)
+        for s in range(3):
+            q, k, v, lam = _spec_tok(21, s, B, H, T, dv, dk)
+            if s == 2 and variant:
+                k[:, :, 2:] *= -3.0
+                v[:, :, 2:] += 1.0
+                lam[:, :, 2:] *= 0.5
+            o = spec.verify(q, k, v, lam, np.zeros(B, bool))
+            spec.commit(np.full(B, 2))
+        outs.append(o)
+    assert np.array_equal(outs[0][:, :, :2], outs[1][:, :, :2])
+    assert not np.allclose(outs[0][:, :, 2:], outs[1][:, :, 2:])
+
+
+def pin_spec_rejected_drafts_never_read(orc):
+    """[blog]: records past the committed pointer are ignored and overwritten.
+    Poisoning the rejected drafts' records with NaN after each commit changes
+    no later output, checkpoint or committed record."""
+    B, H, dv, dk, L, T = 2, 2, 8, 12, 8, 4
+    rng = np.random.default_rng(3)
+    acc = [rng.integers(0, T + 1, B) for _ in range(14)]
+    runs = []
+    for poison in (False, True):
+        spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc)
+        h = np.zeros(B, np.int32)
+        outs = []
+        for s in range(14):
+            q, k, v, lam = _spec_tok(33, s, B, H, T, dv, dk)
+            fl = h + T > L
+            outs.append(spec.verify(q, k, v, lam, fl))
+            spec.commit(acc[s])
+            h = np.where(fl, 0, h) + acc[s]
+            if poison:
+                for b in range(B):
+                    sl = slice(b * H, (b + 1) * H)
+                    spec.rec_x[sl, h[b]:] = np.nan
+                    spec.rec_k[sl, h[b]:] = np.nan
+                    spec.rec_lam[sl, h[b]:] = np.nan
+        runs.append((np.stack(outs), spec.checkpoint().copy()))
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
+
+
+def pin_spec_T1_is_standard_decode(orc):
+    """With one draft per step, all accepted, a verify is a plain decode step:
+    its outputs equal the standard checkpoint + buffer step's (a textbook
+    reduction of the draft sum to the current-token term)."""
+    B, H, dv, dk, L = 2, 3, 8, 12, 6
+    spec = oracle.SpecReplayModel(B, H, dv, dk, L, 1, oracle=orc)
+    rep = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+    h = np.zeros(B, np.int32)
+    for s in range(20):
+        q, k, v, lam = _spec_tok(41, s, B, H, 1, dv, dk)
+        o_s = spec.verify(q, k, v, lam, h + 1 > L)[:, :, 0]
+        o_r = rep.step(q[:, :, 0], k[:, :, 0], v[:, :, 0], lam[:, :, 0], rep.records_held()[:, 0] == L - 1)
+        assert _rel(o_s, o_r) < 1e-12, s
+        h = np.where(h + 1 > L, 0, h) + 1
+        spec.commit(np.ones(B, np.int32))
+
+
+def pin_spec_cursor(orc):
+    """[blog] "Speculative decoding": flush when h + T > L (h committed
+    records before the step), h <- (flush ? 0 : h) + a.  The vLLM fork's
+    form, next_is_flush = (new_wp + 2 T > L + T) for a ring of L + T, is the
+    same rule.  All accepted (a = T = 4, L = 16): h = 0, 4, 8, 12, 16, then
+    every fourth step flushes; every draft rejected (a = 1): a flush every 13
+    steps (at h = 13)."""
+    L, T = 16, 4
+    for hp in range(L + 1):
+        for t in range(1, L + 1):
+            _, f = orc.spec_cursor_run(L, t, hp, np.zeros(1, np.int32))
+            assert bool(f[0]) == (hp + 2 * t > L + t), (hp, t)
+    h, f = orc.spec_cursor_run(L, T, 0, np.full(21, T))
+    assert list(h[:9]) == [0, 4, 8, 12, 16, 4, 8, 12, 16]
+    assert list(np.nonzero(f)[0]) == [4, 8, 12, 16, 20]
+    h, f = orc.spec_cursor_run(L, T, 0, np.ones(40, np.int32))
+    assert list(np.nonzero(f)[0]) == [13, 26, 39] and h[13] == 13 and h[14] == 1
+    forced = np.zeros(6, np.uint8)
+    forced[2] = 1
+    h, f = orc.spec_cursor_run(L, T, 0, np.full(6, 2), forced)
+    assert list(h) == [0, 2, 4, 2, 4, 6] and list(np.nonzero(f)[0]) == [2]
+
+
 ALL_PINS = [
     pin_identity_mamba2_tiny,
     pin_identity_mamba2_long_memory,
@@ -440,4 +587,10 @@ ALL_PINS = [
     pin_e4m3_matches_library_cast,
     pin_e4m3_spec_values,
     pin_read_rounding_within_half_ulp,
+    pin_spec_identity,
+    pin_spec_long_memory,
+    pin_spec_causal,
+    pin_spec_rejected_drafts_never_read,
+    pin_spec_T1_is_standard_decode,
+    pin_spec_cursor,
 ]

@@ -47,6 +47,11 @@ def _eval(name, a):
         if name == "grouped_mib_per_token":
             return per_token / 2**20
         return per_token / (bm.conventional_window_bytes(L, m) / L)
+    if name == "snapshot_mib_per_token":
+        T, a, H, dv, dk, eb = a
+        return bm.snapshot_verify_step_bytes(T, bm.layer_state_bytes(H, dv, dk, eb)) / a / 2**20
+    if name == "plain_mib_per_token":
+        return bm.plain_decode_token_bytes(bm.layer_state_bytes(*a)) / 2**20
     raise KeyError(name)
 
 
@@ -67,3 +72,20 @@ def test_window_totals_by_counting():
         writes = (L - 1) * r + m
         assert reads + writes == bm.replay_window_bytes(L, m, r)
         assert bm.conventional_window_bytes(L, m) == 2 * L * m
+
+
+def test_spec_state_bytes_closed_form():
+    """Checkpoint + ring verification, L = 16, T = 4 (blog, "Speculative
+    decoding: rollback becomes a pointer"): with every draft accepted a cycle
+    is 4 steps (h = 4, 8, 12, 16, the last flushing) committing 16 tokens:
+    5 state transfers per 16 tokens; with one token committed per step a
+    flush comes every 13 steps: 14 transfers per 13 tokens.  (The blog's
+    interactive widget prints 1.30 and 4.47 MiB for these cases; its
+    accounting is not stated in the text, so those two figures are not
+    reproduced here.)"""
+    m = bm.layer_state_bytes(128, 64, 128, 4)
+    assert bm.spec_replay_state_bytes_per_token(16, 4, 4, m, 4000) == 5 * m / 16
+    got = bm.spec_replay_state_bytes_per_token(16, 4, 1, m, 13 * 300)
+    assert abs(got - 14 * m / 13) < 1e-9 * m
+    # both far below the snapshot scheme (5 and 20 MiB) and plain decoding (8 MiB)
+    assert 5 * m / 16 < bm.snapshot_verify_step_bytes(4, m) / 4 < bm.plain_decode_token_bytes(m)

@@ -72,6 +72,27 @@ MUTANTS = [
     ("cursor_force_ignored",
      "const int f = (w == L - 1) || (forced && forced[s]);",
      "const int f = (w == L - 1);"),
+    ("spec_no_causal_mask",
+     "for (int m = 1; m <= i; ++m) {",
+     "for (int m = 1; m <= T; ++m) {"),
+    ("spec_draft_decay_short",
+     "const double Di = gamma_range(ad, 1, i);",
+     "const double Di = gamma_range(ad, 1, i - 1);"),
+    ("spec_W_off_by_one",
+     "const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);",
+     "const double wgt = gamma_range(ad, m, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);"),
+    ("spec_committed_drop_draft_decay",
+     "const double wgt = gamma_range(ac, j + 1, ht) * Di * dot(krt + (int64_t)(j - 1) * dk, qi, dk);",
+     "const double wgt = gamma_range(ac, j + 1, ht) * dot(krt + (int64_t)(j - 1) * dk, qi, dk);"),
+    ("spec_drafts_after_flushed_records",
+     "const int base = flush[t] ? 0 : ht;",
+     "const int base = ht;"),
+    ("spec_flush_rule_inclusive",
+     "const int f = (room < T) || (forced && forced[s]);",
+     "const int f = (room <= T) || (forced && forced[s]);"),
+    ("spec_commit_one_short",
+     "if (!active || active[t]) h[t] += accepted[t];",
+     "if (!active || active[t]) h[t] += accepted[t] > 0 ? accepted[t] - 1 : 0;"),
 ]
 
 
