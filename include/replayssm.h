@@ -78,6 +78,13 @@ typedef enum {
  * state_dtype:  RS_F32 or RS_F16 (checkpoint / conventional state).
  * record_dtype: RS_F32 or RS_F16 (buffered x and k; the log-decay is fp32).
  * io_dtype:     RS_F32, RS_F16 or RS_BF16 (q, k, v inputs).
+ * spec_T:       0 for standard decoding.  T in {1, 2, 4, 8} (T <= L) makes a
+ *               speculative layer (blog "Speculative decoding: rollback
+ *               becomes a pointer"): its ring holds up to L committed records
+ *               and each step verifies T draft tokens per row with
+ *               replay_spec_verify; replay_decode_step rejects it.  Mamba-2
+ *               form, single fp32 or fp16 checkpoint, (d_v, d_k) = (16, 32)
+ *               or (64, 128).
  * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16,
  *               RS_BF16 or RS_E4M3 for a two-precision checkpoint (blog "The
  *               precision argument, derived"): state_dtype RS_F32 is the
@@ -103,6 +110,8 @@ typedef struct {
     int32_t record_dtype;
     int32_t io_dtype;
     int32_t read_dtype;
+    int32_t spec_T;   /* 0: standard decoding; 1, 2, 4 or 8: speculative layer,
+                         see replay_spec_verify */
 } rs_layer;
 
 /*
@@ -124,7 +133,8 @@ typedef struct {
  *                                   and written with contiguous accesses
  *   ckpt_sc  [n_heads][d_v]         fp32 row scales of an RS_E4M3 read copy
  *                                   (ckpt_scale_off is 0 otherwise)
- * slots = L - 1.  block_bytes is a multiple of 256.
+ * slots = L - 1 (a speculative layer: slots = L).  block_bytes is a multiple
+ * of 256.
  */
 typedef struct {
     int64_t ckpt_off;
@@ -270,6 +280,80 @@ int rs_meta_step(int32_t L, int32_t n_rows, const int32_t* steps_since_anchor,
  * setting its entry to 0 (after replay_flush or replay_state_reset).
  */
 int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, const uint8_t* flush);
+
+/*
+ * Speculative decoding (blog "Speculative decoding: rollback becomes a
+ * pointer"; NVIDIA technical blog "ReplaySSM: Rethinking state storage for
+ * faster hybrid model decoding", "Benefit 2: Simplify rollback and speed up
+ * verification").  A row of a speculative layer holds a checkpoint C and h
+ * committed records (batch->write_pos = h, 0..L).  One verify step takes T
+ * draft tokens per row, (lam_i, v_i, k_i, q_i), i = 1..T, and computes the
+ * output every draft would have if drafts 1..i were accepted:
+ *     o_i = D_i (G C q_i + sum_j g_j (k_j . q_i) v_j) + sum_{m<=i} W_im (k_m . q_i) v_m
+ * with G, g_j the decay products of the committed records after the
+ * checkpoint and after record j, D_i the product of the draft decays 1..i
+ * and W_im the product of draft decays m+1..i (a causal mask).  The
+ * checkpoint is read once for all T queries and no state is formed.  The T
+ * drafts are stored as records behind the committed ones (slots h..h+T-1).
+ * A row whose ring has no room for T more records (h + T > L), or whose flag
+ * is set, flushes first: its h committed records (only those) are folded into
+ * the checkpoint, which is written once, and the drafts are stored from slot
+ * 0.  This needs no acceptance count, so it happens in the same launch.
+ * After sampling, replay_spec_commit advances each row's committed count by
+ * the number of drafts accepted; records past it are never read and get
+ * overwritten.
+ *
+ * q, k: [n_rows][T][n_heads][d_k]; v: [n_rows][T][n_heads][d_v], io_dtype,
+ * unit stride along the last dimension, row / token / head strides in
+ * elements; log_decay: [n_rows][T][n_heads] fp32 contiguous; out:
+ * [n_rows][T][n_heads][d_v] fp32 contiguous.
+ */
+typedef struct {
+    const void* q;
+    const void* k;
+    const void* v;
+    int64_t q_row_stride, q_token_stride, q_head_stride;
+    int64_t k_row_stride, k_token_stride, k_head_stride;
+    int64_t v_row_stride, v_token_stride, v_head_stride;
+    const float* log_decay;
+    float* out;
+} rs_spec_io;
+
+/*
+ * Verify step of a speculative layer (layer->spec_T = T).  batch->write_pos:
+ * committed records per row; batch->flush: may be NULL, a nonzero entry
+ * forces the row to flush; batch->next_write_pos is not used.  Padding rows
+ * (block id -1) are neither read nor written.  A row whose metadata is out of
+ * range is skipped and counted in err_count.
+ */
+int replay_spec_verify(const rs_layer* layer, const rs_batch* batch, const rs_spec_io* io,
+                       hipStream_t stream);
+
+/*
+ * Commit after a verify step, on the device: for every non-padding row,
+ * h' = (flushed ? 0 : h) + accepted[row], where flushed is the verify's
+ * decision for that row (its flag, or h + T > L); writes h' to
+ * batch->next_write_pos and next_flush[row] = (h' + T > L).  Passing
+ * (next_write_pos, next_flush) as the next verify's (write_pos, flush) keeps
+ * the cursor on the device.  accepted: device int32 [n_rows], 0..T; a row
+ * with another value commits nothing and is counted in err_count.
+ * batch->next_write_pos and next_flush must not alias write_pos / flush.
+ */
+int replay_spec_commit(const rs_layer* layer, const rs_batch* batch, const int32_t* accepted,
+                       uint8_t* next_flush, hipStream_t stream);
+
+/*
+ * Host mirror of the speculative cursor, for callers that keep it on the
+ * host.  rs_spec_meta_step: flush[r] = 1 if committed[r] + T > L or
+ * force[r] != 0 (force may be NULL), 0 for padding rows (committed < 0).
+ * rs_spec_meta_advance: committed[r] = (flush[r] ? 0 : committed[r]) +
+ * accepted[r] for non-padding rows, in place.  RS_EINVAL on NULL arrays,
+ * n_rows < 0, L outside 1..64 or T outside 1..L.
+ */
+int rs_spec_meta_step(int32_t L, int32_t T, int32_t n_rows, const int32_t* committed,
+                      const uint8_t* force, uint8_t* flush);
+int rs_spec_meta_advance(int32_t L, int32_t T, int32_t n_rows, int32_t* committed,
+                         const uint8_t* flush, const int32_t* accepted);
 
 /* Host: RS_OK if a kernel is compiled for this layer, else the reason code. */
 int rs_layer_supported(const rs_layer* layer);

@@ -9,9 +9,10 @@ ImportError; there is no fallback.
 
 Entry points (same names and meaning as the C ABI):
     replay_decode_step, replay_flush, conventional_decode_step,
-    replay_state_reset, rs_meta_step, rs_meta_advance, block_layout,
-    layer_supported.
-Struct builders: layer(), make_batch(), make_io(); device memory helper:
+    replay_state_reset, rs_meta_step, rs_meta_advance, replay_spec_verify,
+    replay_spec_commit, rs_spec_meta_step, rs_spec_meta_advance,
+    block_layout, layer_supported.
+Struct builders: layer(), make_batch(), make_io(), make_spec_io(); device memory helper:
 Pool (allocates the paged block pool with torch and exposes typed views).
 """
 from __future__ import annotations
@@ -34,7 +35,8 @@ _vp = _c.c_void_p
 class RsLayer(_c.Structure):
     _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
                 ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
-                ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32)]
+                ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32),
+                ("spec_T", _c.c_int32)]
 
 
 class RsBlockLayout(_c.Structure):
@@ -55,6 +57,14 @@ class RsStepIO(_c.Structure):
                 ("k_row_stride", _c.c_int64), ("k_head_stride", _c.c_int64),
                 ("v_row_stride", _c.c_int64), ("v_head_stride", _c.c_int64),
                 ("log_decay", _vp), ("beta", _vp), ("out", _vp)]
+
+
+class RsSpecIO(_c.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp),
+                ("q_row_stride", _c.c_int64), ("q_token_stride", _c.c_int64), ("q_head_stride", _c.c_int64),
+                ("k_row_stride", _c.c_int64), ("k_token_stride", _c.c_int64), ("k_head_stride", _c.c_int64),
+                ("v_row_stride", _c.c_int64), ("v_token_stride", _c.c_int64), ("v_head_stride", _c.c_int64),
+                ("log_decay", _vp), ("out", _vp)]
 
 
 class ReplaySSMError(RuntimeError):
@@ -82,10 +92,15 @@ def _load():
     lib.replay_state_reset.argtypes = [P(RsLayer), P(RsBatch), _vp, _vp]
     lib.rs_meta_step.argtypes = [_c.c_int32, _c.c_int32, _vp, _vp, _vp, _vp]
     lib.rs_meta_advance.argtypes = [_c.c_int32, _c.c_int32, _vp, _vp]
+    lib.replay_spec_verify.argtypes = [P(RsLayer), P(RsBatch), P(RsSpecIO), _vp]
+    lib.replay_spec_commit.argtypes = [P(RsLayer), P(RsBatch), _vp, _vp, _vp]
+    lib.rs_spec_meta_step.argtypes = [_c.c_int32, _c.c_int32, _c.c_int32, _vp, _vp, _vp]
+    lib.rs_spec_meta_advance.argtypes = [_c.c_int32, _c.c_int32, _c.c_int32, _vp, _vp, _vp]
     lib.rs_last_error.restype = _c.c_char_p
     for name in ("rs_block_layout_get", "rs_layer_supported", "replay_decode_step",
                  "conventional_decode_step", "replay_flush", "replay_state_reset", "rs_meta_step",
-                 "rs_meta_advance"):
+                 "rs_meta_advance", "replay_spec_verify", "replay_spec_commit", "rs_spec_meta_step",
+                 "rs_spec_meta_advance"):
         getattr(lib, name).restype = _c.c_int
     return lib
 
@@ -108,13 +123,15 @@ _DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
 
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
-          record_dtype="f16", io_dtype="bf16", read_dtype=None) -> RsLayer:
+          record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0) -> RsLayer:
     """read_dtype: None for a single checkpoint, "f16" / "bf16" / "e4m3" for
     a two-precision checkpoint (fp32 recurrence copy + read copy; E4M3 with a
-    power-of-two scale per state row)."""
+    power-of-two scale per state row).  spec_T: 0 for standard decoding, T
+    for a speculative layer verifying T drafts per step."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
-                   code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype))
+                   code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype),
+                   int(spec_T))
 
 
 def block_layout(lay: RsLayer) -> RsBlockLayout:
@@ -154,6 +171,21 @@ def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:
                     v.stride(0), v.stride(1), _ptr(log_decay), _ptr(beta), _ptr(out))
 
 
+def make_spec_io(q, k, v, log_decay, out) -> RsSpecIO:
+    """q, k: [n_rows, T, n_heads, d_k]; v: [n_rows, T, n_heads, d_v] (any
+    row/token/head strides, unit last stride); log_decay: fp32
+    [n_rows, T, n_heads] contiguous; out: fp32 [n_rows, T, n_heads, d_v]
+    contiguous."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be [rows, T, heads, d] with unit last stride")
+    for name, t in (("log_decay", log_decay), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return RsSpecIO(_ptr(q), _ptr(k), _ptr(v), q.stride(0), q.stride(1), q.stride(2), k.stride(0), k.stride(1),
+                    k.stride(2), v.stride(0), v.stride(1), v.stride(2), _ptr(log_decay), _ptr(out))
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -176,6 +208,35 @@ def conventional_decode_step(lay: RsLayer, batch: RsBatch, io: RsStepIO, stream=
 
 def replay_state_reset(lay: RsLayer, batch: RsBatch, mask, stream=None) -> None:
     _check(_lib.replay_state_reset(_c.byref(lay), _c.byref(batch), _ptr(mask), _stream(stream)))
+
+
+def replay_spec_verify(lay: RsLayer, batch: RsBatch, io: RsSpecIO, stream=None) -> None:
+    _check(_lib.replay_spec_verify(_c.byref(lay), _c.byref(batch), _c.byref(io), _stream(stream)))
+
+
+def replay_spec_commit(lay: RsLayer, batch: RsBatch, accepted, next_flush, stream=None) -> None:
+    """accepted: int32 device [n_rows]; next_flush: uint8 device [n_rows]."""
+    _check(_lib.replay_spec_commit(_c.byref(lay), _c.byref(batch), _ptr(accepted), _ptr(next_flush),
+                                   _stream(stream)))
+
+
+def rs_spec_meta_step(L: int, T: int, committed: np.ndarray, force: np.ndarray | None = None) -> np.ndarray:
+    """Host mirror: this step's flush flags (uint8) for the committed counts."""
+    h = np.ascontiguousarray(committed, dtype=np.int32)
+    f = None if force is None else np.ascontiguousarray(force, dtype=np.uint8)
+    out = np.zeros(h.shape[0], np.uint8)
+    _check(_lib.rs_spec_meta_step(int(L), int(T), h.shape[0], h.ctypes.data, None if f is None else f.ctypes.data,
+                                  out.ctypes.data))
+    return out
+
+
+def rs_spec_meta_advance(L: int, T: int, committed: np.ndarray, flush: np.ndarray, accepted: np.ndarray) -> None:
+    """Host mirror of the commit, in place on an int32 contiguous array."""
+    assert committed.dtype == np.int32 and committed.flags.c_contiguous
+    f = np.ascontiguousarray(flush, dtype=np.uint8)
+    a = np.ascontiguousarray(accepted, dtype=np.int32)
+    _check(_lib.rs_spec_meta_advance(int(L), int(T), committed.shape[0], committed.ctypes.data, f.ctypes.data,
+                                     a.ctypes.data))
 
 
 def rs_meta_step(L: int, steps_since_anchor: np.ndarray, force_flush: np.ndarray | None = None):
@@ -284,4 +345,6 @@ __all__ = [
     "ReplaySSMError", "layer", "block_layout", "layer_supported", "make_batch", "make_io",
     "replay_decode_step", "replay_flush", "conventional_decode_step", "replay_state_reset",
     "rs_meta_step", "rs_meta_advance", "last_error", "Pool", "LIBRARY_PATH", "read_copy_columns",
+    "RsSpecIO", "make_spec_io", "replay_spec_verify", "replay_spec_commit", "rs_spec_meta_step",
+    "rs_spec_meta_advance",
 ]

@@ -57,7 +57,24 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
             return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy only");
     }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
+    const bool spec_kind = kind == rs::Kind::SpecVerify || kind == rs::Kind::SpecCommit;
+    if (L->spec_T != 0) {
+        const int T = L->spec_T;
+        if (T < 1 || T > L->L) return fail(RS_EINVAL, "spec_T must be in 1..L (got %d, L=%d)", T, L->L);
+        if (T != 1 && T != 2 && T != 4 && T != 8)
+            return fail(RS_EUNSUPPORTED, "spec_T must be 1, 2, 4 or 8 (got %d)", T);
+        if (L->form != RS_MAMBA2) return fail(RS_EUNSUPPORTED, "speculative verify: Mamba-2 form only");
+        if (two_precision(*L))
+            return fail(RS_EUNSUPPORTED, "speculative verify: single checkpoint only (no read copy)");
+        if (kind == rs::Kind::ReplayStep)
+            return fail(RS_EINVAL, "a speculative layer (spec_T=%d) is stepped with replay_spec_verify", T);
+    } else if (spec_kind) {
+        return fail(RS_EINVAL, "replay_spec_verify / replay_spec_commit need a speculative layer (spec_T > 0)");
+    }
     if (!rs::compiled(kind, *L)) {
+        if (spec_kind)
+            return fail(RS_EUNSUPPORTED, "no speculative kernel for d_v=%d d_k=%d (supported: 16x32, 64x128)",
+                        L->d_v, L->d_k);
         if (L->read_dtype == RS_E4M3)
             return fail(RS_EUNSUPPORTED, "no kernel for an E4M3 read copy with d_v=%d d_k=%d (supported: 64x128, "
                                          "128x128)", L->d_v, L->d_k);
@@ -71,7 +88,9 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
 }
 
 void layout_of(const rs_layer& L, rs_block_layout* o) {
-    const int64_t slots = L.L - 1;
+    // a speculative ring holds up to L committed records; a standard buffer
+    // L - 1 (the L-th token of a window flushes without being stored)
+    const int64_t slots = L.spec_T > 0 ? L.L : L.L - 1;
     const int64_t H = L.n_heads;
     const int64_t sb = dtype_bytes(L.state_dtype), rb = dtype_bytes(L.record_dtype);
     o->ckpt_off = 0;
@@ -193,12 +212,18 @@ int do_launch(rs::Kind kind, const rs_layer& L, const rs::StepParams& p, hipStre
     return ok();
 }
 
+// The step kind that defines a layer: standard decoding, or the verify step
+// of a speculative layer.
+rs::Kind step_kind(const rs_layer* layer) {
+    return layer && layer->spec_T != 0 ? rs::Kind::SpecVerify : rs::Kind::ReplayStep;
+}
+
 }  // namespace
 
 extern "C" {
 
 int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out) {
-    int rc = check_layer(layer, rs::Kind::ReplayStep);
+    int rc = check_layer(layer, step_kind(layer));
     if (rc) return rc;
     if (!out) return fail(RS_EINVAL, "out is NULL");
     layout_of(*layer, out);
@@ -206,7 +231,7 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out) {
 }
 
 int rs_layer_supported(const rs_layer* layer) {
-    int rc = check_layer(layer, rs::Kind::ReplayStep);
+    int rc = check_layer(layer, step_kind(layer));
     if (rc) return rc;
     rc = check_layer(layer, rs::Kind::ConventionalStep);
     return rc ? rc : ok();
@@ -289,6 +314,90 @@ int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, cons
         if (steps_since_anchor[r] < 0) continue;
         steps_since_anchor[r] = flush[r] ? 0 : steps_since_anchor[r] + 1;
     }
+    return ok();
+}
+
+int replay_spec_verify(const rs_layer* layer, const rs_batch* batch, const rs_spec_io* io, hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::SpecVerify))) return rc;
+    if ((rc = check_batch(*layer, batch, true, false))) return rc;
+    if (!io) return fail(RS_EINVAL, "io is NULL");
+    if (batch->n_rows == 0) return ok();
+    const int T = layer->spec_T, e = dtype_bytes(layer->io_dtype);
+    struct { const char* name; const void* p; int64_t rs, ts, hs; int d; } v3[] = {
+        {"q", io->q, io->q_row_stride, io->q_token_stride, io->q_head_stride, layer->d_k},
+        {"k", io->k, io->k_row_stride, io->k_token_stride, io->k_head_stride, layer->d_k},
+        {"v", io->v, io->v_row_stride, io->v_token_stride, io->v_head_stride, layer->d_v}};
+    for (const auto& a : v3) {
+        if ((rc = check_vec(a.name, a.p, a.rs, a.hs, a.d, e))) return rc;
+        if ((a.ts * e) % 16) return fail(RS_EINVAL, "%s token stride must keep 16-byte alignment", a.name);
+        if (a.ts < (int64_t)layer->n_heads * a.hs)
+            return fail(RS_EINVAL, "%s token stride overlaps the heads of the previous token", a.name);
+        if (batch->n_rows > 1 && a.rs < (int64_t)T * a.ts)
+            return fail(RS_EINVAL, "%s row stride overlaps the tokens of the previous row", a.name);
+    }
+    if (!io->log_decay || !aligned(io->log_decay, 16))
+        return fail(RS_EINVAL, "log_decay must be non-NULL and 16-byte aligned");
+    if (!io->out || !aligned(io->out, 16)) return fail(RS_EINVAL, "out must be non-NULL and 16-byte aligned");
+    rs::StepParams p = params(*layer, *batch);
+    p.spec_T = T;
+    p.q = io->q;
+    p.k = io->k;
+    p.v = io->v;
+    p.qs_r = io->q_row_stride;
+    p.qs_t = io->q_token_stride;
+    p.qs_h = io->q_head_stride;
+    p.ks_r = io->k_row_stride;
+    p.ks_t = io->k_token_stride;
+    p.ks_h = io->k_head_stride;
+    p.vs_r = io->v_row_stride;
+    p.vs_t = io->v_token_stride;
+    p.vs_h = io->v_head_stride;
+    p.lam = io->log_decay;
+    p.out = io->out;
+    return do_launch(rs::Kind::SpecVerify, *layer, p, stream);
+}
+
+int replay_spec_commit(const rs_layer* layer, const rs_batch* batch, const int32_t* accepted, uint8_t* next_flush,
+                       hipStream_t stream) {
+    int rc;
+    if ((rc = check_layer(layer, rs::Kind::SpecCommit))) return rc;
+    if ((rc = check_batch(*layer, batch, true, false))) return rc;
+    if (batch->n_rows == 0) return ok();
+    if (!accepted || !aligned(accepted, 4)) return fail(RS_EINVAL, "accepted must be non-NULL and 4-byte aligned");
+    if (!batch->next_write_pos) return fail(RS_EINVAL, "next_write_pos is NULL");
+    if (!next_flush) return fail(RS_EINVAL, "next_flush is NULL");
+    if (batch->flush && (const void*)batch->flush == (const void*)next_flush)
+        return fail(RS_EINVAL, "next_flush must not alias flush");
+    rs::StepParams p = params(*layer, *batch);
+    p.spec_T = layer->spec_T;
+    p.next_wp = batch->next_write_pos;
+    p.accepted = accepted;
+    p.next_flush = next_flush;
+    return do_launch(rs::Kind::SpecCommit, *layer, p, stream);
+}
+
+int rs_spec_meta_step(int32_t L, int32_t T, int32_t n_rows, const int32_t* committed, const uint8_t* force,
+                      uint8_t* flush) {
+    if (L < 1 || L > kMaxL) return fail(RS_EINVAL, "L must be in 1..%d (got %d)", kMaxL, L);
+    if (T < 1 || T > L) return fail(RS_EINVAL, "T must be in 1..L (got %d)", T);
+    if (n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
+    if (n_rows == 0) return ok();
+    if (!committed || !flush) return fail(RS_EINVAL, "NULL array");
+    for (int32_t r = 0; r < n_rows; ++r)
+        flush[r] = (uint8_t)(committed[r] >= 0 && (committed[r] + T > L || (force && force[r])));
+    return ok();
+}
+
+int rs_spec_meta_advance(int32_t L, int32_t T, int32_t n_rows, int32_t* committed, const uint8_t* flush,
+                         const int32_t* accepted) {
+    if (L < 1 || L > kMaxL) return fail(RS_EINVAL, "L must be in 1..%d (got %d)", kMaxL, L);
+    if (T < 1 || T > L) return fail(RS_EINVAL, "T must be in 1..L (got %d)", T);
+    if (n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
+    if (n_rows == 0) return ok();
+    if (!committed || !flush || !accepted) return fail(RS_EINVAL, "NULL array");
+    for (int32_t r = 0; r < n_rows; ++r)
+        if (committed[r] >= 0) committed[r] = (flush[r] ? 0 : committed[r]) + accepted[r];
     return ok();
 }
 

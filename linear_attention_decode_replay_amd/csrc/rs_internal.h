@@ -32,9 +32,14 @@ struct StepParams {
     const float* beta;
     float* out;
     int32_t n_rows, n_heads, L, slots;
+    // speculative verify / commit
+    int32_t spec_T;
+    int64_t qs_t, ks_t, vs_t;  // token strides (elements)
+    const int32_t* accepted;   // commit: drafts accepted per row
+    uint8_t* next_flush;       // commit: next step's flag per row
 };
 
-enum class Kind { ReplayStep, ConventionalStep, Flush, Reset };
+enum class Kind { ReplayStep, ConventionalStep, Flush, Reset, SpecVerify, SpecCommit };
 
 // Dynamic LDS bytes a launch of `kind` needs for this layer (0 if none).
 size_t lds_bytes(Kind kind, const rs_layer& layer);

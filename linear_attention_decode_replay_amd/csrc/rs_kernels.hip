@@ -928,6 +928,373 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     }
 }
 
+// ------------------------------------------------ speculative verify step --
+// One workgroup per (row, head) tile (split 1 only: a flushing row rewrites
+// record slots 0..T-1 that it has just read, which another workgroup of the
+// same tile could still be reading).  T draft tokens per row.  Order of work:
+//   1. small loads (draft q, k, v and log-decays, the committed records and
+//      their decays), then the checkpoint stream;
+//   2. drafts and records to LDS; barrier; log-decay sums of the committed
+//      records (suffix sums, wave 0) and of the drafts (prefix sums); barrier;
+//   3. K^T Q: lane group rg takes keys rg, rg + RPP, ... (committed records,
+//      then drafts) against all T queries, one lane-group reduction per key;
+//      each (key, query) product is scaled by its decay weight, zero where a
+//      draft comes after the query (the causal mask); barrier;
+//   4. per lane: T x NR partial sums of the checkpoint GEMV for all T queries
+//      plus this lane's share of the weighted record and draft terms, then
+//      one lane-group reduction yielding the T output rows;
+//   5. flush rows fold the committed records into the registers holding the
+//      tile and store it once; every row stores its drafts as records behind
+//      the committed ones (from slot 0 after a flush).
+// Every decay weight is the exponential of a sum of log-decays (<= 0).
+template <class R>
+struct SpecLds {
+    R* kc;        // [slots][DK] committed keys
+    R* xc;        // [slots][DV] committed values
+    float* qd;    // [T][DK] draft queries
+    float* kd;    // [T][DK] draft keys
+    float* vd;    // [T][DV] draft values
+    float* lamd;  // [T] draft log-decays
+    float* lsc;   // [slots] sum of the committed log-decays after record j
+    float* ec;    // [slots] exp(lsc)
+    float* cum;   // [T] sum of the draft log-decays 1..i
+    float* gck;   // [T] checkpoint weight of draft i
+    float* wq;    // [(slots + T) * T] weighted key . query products
+    float* sc;    // [4] total committed log-decay, its exponential
+};
+
+template <int DV, int DK, class R>
+__device__ __forceinline__ SpecLds<R> spec_carve(char* smem, int slots, int T) {
+    SpecLds<R> s;
+    s.kc = reinterpret_cast<R*>(smem);
+    s.xc = s.kc + (int64_t)slots * DK;
+    float* f = reinterpret_cast<float*>(s.xc + (int64_t)slots * DV);
+    s.qd = f;
+    s.kd = s.qd + T * DK;
+    s.vd = s.kd + T * DK;
+    s.lamd = s.vd + T * DV;
+    s.lsc = s.lamd + T;
+    s.ec = s.lsc + slots;
+    s.cum = s.ec + slots;
+    s.gck = s.cum + T;
+    s.wq = s.gck + T;
+    s.sc = s.wq + (slots + T) * T;
+    return s;
+}
+
+size_t spec_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes) {
+    return (size_t)slots * (dk + dv) * rec_bytes +
+           sizeof(float) * (2 * (size_t)T * dk + (size_t)T * dv + T + 2 * (size_t)slots + 2 * (size_t)T +
+                            ((size_t)slots + T) * T + 4);
+}
+
+// Raw 4-element load (io type) into 32-bit words; the conversion to float
+// happens when the words are used, so the load does not wait.
+template <class TI>
+struct Raw4 {
+    static constexpr int W = 4 * (int)sizeof(typename TI::S) / 4;
+    uint32_t w[W];
+    __device__ __forceinline__ void load(const typename TI::S* p) {
+        if constexpr (W == 4) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+            w[0] = r[0]; w[1] = r[1]; w[2] = r[2]; w[3] = r[3];
+        } else {
+            const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+            w[0] = r[0]; w[1] = r[1];
+        }
+    }
+    __device__ __forceinline__ void to(float* out) const {
+        typename TI::S tmp[4];
+        __builtin_memcpy(tmp, w, sizeof(tmp));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = to_f<TI>(tmp[i]);
+    }
+};
+
+template <int DV, int DK, class TS, class TR, class TI, int T>
+__global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const StepParams p) {
+    using Tl = Tile<DV, DK, TS, 1>;
+    using S = typename TS::S;
+    using R = typename TR::S;
+    using I = typename TI::S;
+    constexpr int NT = Tl::NT, VEC = Tl::VEC, LPR = Tl::LPR, RPP = Tl::RPP, NR = Tl::NR;
+    constexpr int NV = T * NR;                        // partial sums per lane: (draft, owned row)
+    constexpr int QN = (T * DK / 4 + NT - 1) / NT;    // 4-element pieces of draft q / k per thread
+    constexpr int VN = (T * DV + NT - 1) / NT;        // draft v elements per thread
+    constexpr int KCH = DK * (int)sizeof(R) / 16, XCH = DV * (int)sizeof(R) / 16, XE = 16 / (int)sizeof(R);
+    constexpr int RC = 2;                             // record chunks per thread in registers
+    static_assert(DK % 4 == 0 && VEC % 4 == 0, "4-element pieces");
+
+    const TileIds id = tile_ids<1>(p);
+    const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
+    const bool flag = row_flag(fsrc, id.row) && p.flush;
+    const int blk = p.block_table[id.row];
+    const int h = p.write_pos[id.row];
+    const bool pad = blk < 0;
+    const bool bad = !pad && (blk >= p.n_blocks || h < 0 || h > p.slots);
+    if (pad || bad) {
+        if (bad) count_error(p, id);
+        return;
+    }
+    const bool fl = flag || (h + T > p.L);  // no room for T more records: flush first
+    const int base = fl ? 0 : h;            // slot of this step's first draft
+    const int tid = threadIdx.x;
+    const int cc = tid % LPR;
+    const int rg = tid / LPR;
+
+    char* bp = p.pool + (int64_t)blk * p.block_bytes;
+    S* ck = reinterpret_cast<S*>(bp + p.ckpt_off) + (int64_t)id.head * (DV * DK);
+    R* rx = reinterpret_cast<R*>(bp + p.recx_off) + (int64_t)id.head * p.slots * DV;
+    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    float* rl = reinterpret_cast<float*>(bp + p.reclam_off) + (int64_t)id.head * p.slots;
+    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
+    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const I* vb = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
+    const int64_t tok0 = (int64_t)id.row * T;  // this row's first token in [row][T] arrays
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const SpecLds<R> s = spec_carve<DV, DK, R>(smem, p.slots, T);
+
+    // 1. small loads, then the checkpoint stream
+    Raw4<TI> qr[QN], kr[QN];
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = min((u * NT + tid) * 4, T * DK - 4);  // clamped: every thread loads
+        const int i = e / DK, c = e - i * DK;
+        qr[u].load(qb + i * p.qs_t + c);
+        kr[u].load(kb + i * p.ks_t + c);
+    }
+    I vr[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) {
+        const int e = min(u * NT + tid, T * DV - 1);
+        const int i = e / DV;
+        vr[u] = vb[i * p.vs_t + (e - i * DV)];
+    }
+    const float lam_d = p.lam[(tok0 + min(tid, T - 1)) * p.n_heads + id.head];
+    float lam_c = 0.f;
+    if (h > 0) lam_c = rl[min(tid, h - 1)];
+    // committed records: keys [h][DK] then values [h][DV], 16-byte chunks
+    const int nk = h * KCH, nrec = nk + h * XCH;
+    auto rsrc = [&](int i) -> const R* {
+        if (i < nk) return rk + (int64_t)i * XE;
+        const int t2 = i - nk, j = t2 / XCH;
+        return rx + (int64_t)j * DV + (t2 - j * XCH) * XE;
+    };
+    auto rdst = [&](int i) -> u32x4* {
+        return i < nk ? reinterpret_cast<u32x4*>(s.kc) + i : reinterpret_cast<u32x4*>(s.xc) + (i - nk);
+    };
+    u32x4 rb[RC];
+    if (nrec > 0) {
+#pragma unroll
+        for (int u = 0; u < RC; ++u) rb[u] = ld_stream(rsrc(min(u * NT + tid, nrec - 1)));
+    }
+    // records beyond RC chunks per thread (long rings only) are copied before
+    // the checkpoint stream is issued, so that waiting for them never waits
+    // for the stream
+    for (int i = RC * NT + tid; i < nrec; i += NT) *rdst(i) = ld_stream(rsrc(i));
+    u32x4 cb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+
+    // 2. to LDS
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = (u * NT + tid) * 4;
+        if (e < T * DK) {
+            qr[u].to(s.qd + e);
+            kr[u].to(s.kd + e);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < VN; ++u)
+        if (u * NT + tid < T * DV) s.vd[u * NT + tid] = to_f<TI>(vr[u]);
+    if (tid < T) s.lamd[tid] = lam_d;
+#pragma unroll
+    for (int u = 0; u < RC; ++u)
+        if (u * NT + tid < nrec) *rdst(u * NT + tid) = rb[u];
+    __syncthreads();
+
+    if (tid < 64) {
+        // committed records: lane j < h gets sum_{j<l<h} lam_l; lane 0 the total
+        const int lane = tid;
+        float sfx = lane < h ? lam_c : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {  // inclusive suffix sum over lanes >= lane
+            const float t = __shfl_down(sfx, off);
+            if (lane + off < 64) sfx += t;
+        }
+        float after = __shfl_down(sfx, 1);
+        if (lane == 63) after = 0.f;
+        if (lane < h) {
+            s.lsc[lane] = after;
+            s.ec[lane] = expf(after);
+        }
+        if (lane == 0) {
+            s.sc[0] = sfx;
+            s.sc[1] = expf(sfx);
+        }
+        if (lane < T) {  // drafts: sum of the log-decays 1..lane
+            float c = 0.f;
+            for (int m = 0; m <= lane; ++m) c += s.lamd[m];
+            s.cum[lane] = c;
+        }
+    }
+    __syncthreads();
+
+    // 3. weighted K^T Q
+    float qv[T][VEC];
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) qv[i][c] = s.qd[i * DK + cc * VEC + c];
+    if (tid < T) s.gck[tid] = expf(s.sc[0] + s.cum[tid]);
+    const int nkeys = h + T;
+    for (int j0 = 0; j0 < nkeys; j0 += RPP) {
+        const int j = j0 + rg;
+        float kj[VEC];
+        if (j < h) {
+            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+        } else {
+            const int m = min(j - h, T - 1);
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) kj[c] = s.kd[m * DK + cc * VEC + c];
+        }
+        float part[T];
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) a += kj[c] * qv[i][c];
+            part[i] = a;
+        }
+        xsum<T, LPR / 2, 1>(part, cc);
+        constexpr int left = xsum_left<T, LPR, 1>();
+        if (j < nkeys && (cc & xsum_dup_mask<T, LPR, 1>()) == 0) {
+            const int b0 = xsum_base<T, LPR, 1>(cc);
+#pragma unroll
+            for (int k = 0; k < left; ++k) {
+                const int i = b0 + k;
+                float wgt;
+                if (j < h) {
+                    wgt = expf(s.lsc[j] + s.cum[i]);
+                } else {
+                    const int m = j - h;
+                    float sm = 0.f;
+                    for (int l = m + 1; l <= i; ++l) sm += s.lamd[l];
+                    wgt = m <= i ? expf(sm) : 0.f;  // drafts after query i are masked
+                }
+                s.wq[j * T + i] = wgt * part[k];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4. outputs
+    float cf[NR][VEC];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+        const float g = s.gck[i];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) a += cf[r][c] * qv[i][c];
+            acc[i * NR + r] = g * a;
+        }
+    }
+    for (int j = cc; j < nkeys; j += LPR) {
+        float xj[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            xj[r] = j < h ? to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]) : s.vd[(j - h) * DV + r * RPP + rg];
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            const float wg = s.wq[j * T + i];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[i * NR + r] += wg * xj[r];
+        }
+    }
+    xsum<NV, LPR / 2, 1>(acc, cc);
+    {
+        constexpr int left = xsum_left<NV, LPR, 1>();
+        if ((cc & xsum_dup_mask<NV, LPR, 1>()) == 0) {
+            const int b0 = xsum_base<NV, LPR, 1>(cc);
+#pragma unroll
+            for (int k = 0; k < left; ++k) {
+                const int v = b0 + k, i = v / NR, r = v - i * NR;
+                p.out[((tok0 + i) * p.n_heads + id.head) * DV + r * RPP + rg] = acc[k];
+            }
+        }
+    }
+
+    // 5. flush: fold the committed records (only those), store once
+    if (fl) {  // uniform
+        const float G = s.sc[1];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) cf[r][c] *= G;
+        for (int j = 0; j < h; ++j) {
+            float kj[VEC];
+            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+            const float ej = s.ec[j];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float f = ej * to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+    }
+    // drafts become records base .. base + T - 1
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = (u * NT + tid) * 4;
+        if (e < T * DK) {
+            const int i = e / DK, c = e - i * DK;
+            store_f<TR, 4>(rk + (int64_t)(base + i) * DK + c, s.kd + e);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < VN; ++u) {
+        const int e = u * NT + tid;
+        if (e < T * DV) {
+            const int i = e / DV;
+            rx[(int64_t)(base + i) * DV + (e - i * DV)] = from_f<TR>(s.vd[e]);
+        }
+    }
+    if (tid < T) rl[base + tid] = s.lamd[tid];
+}
+
+// Commit after a verify: one thread per row (see replay_spec_commit).
+__global__ __launch_bounds__(256) void k_spec_commit(const StepParams p) {
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= p.n_rows) return;
+    const int blk = p.block_table[row];
+    if (blk < 0) return;
+    const int h = p.write_pos[row];
+    const int T = p.spec_T;
+    if (blk >= p.n_blocks || h < 0 || h > p.slots) {
+        if (p.err) atomicAdd(p.err, 1);
+        return;
+    }
+    const bool fl = (p.flush && p.flush[row]) || (h + T > p.L);
+    int a = p.accepted[row];
+    if (a < 0 || a > T) {
+        if (p.err) atomicAdd(p.err, 1);
+        a = 0;
+    }
+    const int hn = (fl ? 0 : h) + a;
+    p.next_wp[row] = hn;
+    p.next_flush[row] = (uint8_t)(hn + T > p.L ? 1 : 0);
+}
+
 // ------------------------------------------------------------ state reset --
 // Zero the checkpoint (both copies of a two-precision checkpoint).
 template <int DV, int DK, class TS, int SPLIT, class TL>
@@ -1043,6 +1410,14 @@ bool with_shape(int dv, int dk, F&& f) {
     return false;
 }
 template <class F>
+bool with_spec_T(int T, F&& f) {
+    if (T == 1) { f(std::integral_constant<int, 1>{}); return true; }
+    if (T == 2) { f(std::integral_constant<int, 2>{}); return true; }
+    if (T == 4) { f(std::integral_constant<int, 4>{}); return true; }
+    if (T == 8) { f(std::integral_constant<int, 8>{}); return true; }
+    return false;
+}
+template <class F>
 bool with_form(int form, F&& f) {
     if (form == RS_MAMBA2) { f(std::integral_constant<int, kMamba2>{}); return true; }
     if (form == RS_GDN) { f(std::integral_constant<int, kGdn>{}); return true; }
@@ -1099,6 +1474,33 @@ struct Dispatch {
                                 });
                         });
                     });
+                    return;
+                }
+                if (kind == Kind::SpecVerify) {
+                    if constexpr (tile_ok<DV, DK, TS, 1>() && split_for<DV, DK>() == 1) {
+                        with_record(L.record_dtype, [&](auto tr) {
+                            using TR = decltype(tr);
+                            with_io(L.io_dtype, [&](auto ti) {
+                                using TI = decltype(ti);
+                                with_spec_T(L.spec_T, [&](auto t_c) {
+                                    constexpr int T = decltype(t_c)::value;
+                                    ok = true;
+                                    if (p) {
+                                        const size_t lds = spec_lds_bytes(L.L, T, DV, DK, (int)sizeof(typename TR::S));
+                                        hipLaunchKernelGGL((k_spec_verify<DV, DK, TS, TR, TI, T>), grid<1>(),
+                                                           dim3(Tile<DV, DK, TS, 1>::NT), lds, stream, *p);
+                                    }
+                                });
+                            });
+                        });
+                    }
+                    return;
+                }
+                if (kind == Kind::SpecCommit) {
+                    ok = true;
+                    if (p)
+                        hipLaunchKernelGGL(k_spec_commit, dim3((unsigned)((p->n_rows + 255) / 256)), dim3(256), 0,
+                                           stream, *p);
                     return;
                 }
                 with_read<DV, DK, TS>(L.read_dtype, L.state_dtype, [&](auto tl) {
@@ -1160,8 +1562,10 @@ struct Dispatch {
 
 // Upper bound over the splits (a workgroup owning all d_v rows).
 size_t lds_bytes(Kind kind, const rs_layer& layer) {
+    if (kind == Kind::SpecVerify)
+        return spec_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, layer.record_dtype == RS_F32 ? 4 : 2);
     if (kind != Kind::ReplayStep && kind != Kind::Flush) return 0;
-    const int slots = layer.L - 1;
+    const int slots = layer.spec_T > 0 ? layer.L : layer.L - 1;
     const size_t rb = layer.record_dtype == RS_F32 ? 4 : 2;
     return (size_t)slots * (layer.d_k + layer.d_v) * rb + sizeof(float) * (3 * (size_t)layer.L + 2 * layer.d_v + 4);
 }

@@ -27,7 +27,8 @@ import numpy as np
 import torch
 
 from . import (Pool, RsLayer, conventional_decode_step, make_batch, replay_decode_step,
-               replay_flush, replay_state_reset, rs_meta_advance, rs_meta_step)
+               replay_flush, replay_spec_commit, replay_spec_verify, replay_state_reset, rs_meta_advance,
+               rs_meta_step)
 
 
 def _layout(n: int):
@@ -191,3 +192,76 @@ class DecodeLayer:
         replay_state_reset(self.layer, self.batch[self._cur], self.mask, stream)
         self.anchor[sel] = 0
         self._dirty = True
+
+
+class SpecDecodeLayer:
+    """Host-side state of one speculative layer (rs_layer.spec_T = T) for a
+    batch of request slots: the pool, the block table and, on the device, two
+    (committed count, flush flag) array pairs.  verify() reads one pair;
+    commit(accepted) writes the other from the device-side accepted counts
+    (blog "Speculative decoding: rollback becomes a pointer": the commit runs
+    on the device and sets the next step's flag), so a decode loop never
+    copies the cursor back to the host.  Joining or leaving rows is an upload
+    of the block table with the new rows' counts set to 0."""
+
+    def __init__(self, lay: RsLayer, n_slots: int, n_blocks: int | None = None, device="cuda"):
+        if lay.spec_T < 1:
+            raise ValueError("SpecDecodeLayer needs a speculative layer (spec_T > 0)")
+        self.layer = lay
+        self.L, self.T = int(lay.L), int(lay.spec_T)
+        self.n_slots = n = int(n_slots)
+        self.pool = Pool(lay, n_blocks or n_slots, device)
+        self.device = self.pool.raw.device
+        self.blocks = np.full(n, -1, np.int32)
+        self.block_table = torch.full((n,), -1, dtype=torch.int32, device=self.device)
+        # (committed, flag) pairs; the byte arrays are padded to a multiple of 4
+        n4 = (n + 3) // 4 * 4
+        self.committed = [torch.zeros(n, dtype=torch.int32, device=self.device) for _ in range(2)]
+        self.flag = [torch.zeros(n4, dtype=torch.uint8, device=self.device) for _ in range(2)]
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self._cur = 0
+        self.batch = [make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.committed[i],
+                                 self.flag[i], self.err, next_write_pos=self.committed[1 - i]) for i in (0, 1)]
+
+    def assign(self, slot: int, block: int) -> None:
+        if not 0 <= block < self.pool.n_blocks:
+            raise ValueError(f"block {block} outside the pool of {self.pool.n_blocks}")
+        self.blocks[slot] = block
+
+    def retire(self, slot: int) -> None:
+        self.blocks[slot] = -1
+
+    def upload(self, rows=None, stream=None) -> None:
+        """Copy the block table to the device; `rows` (joining slots) start
+        with 0 committed records, a zero checkpoint and no flag."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(stream):
+            self.block_table.copy_(torch.from_numpy(self.blocks))
+            if rows is not None:
+                sel = torch.zeros(self.n_slots, dtype=torch.bool)
+                sel[torch.as_tensor(list(rows), dtype=torch.long)] = True
+                sel = sel.to(self.device)
+                self.committed[self._cur].masked_fill_(sel, 0)
+                self.flag[self._cur][:self.n_slots].masked_fill_(sel, 0)
+                mask = torch.zeros(self.flag[0].numel(), dtype=torch.uint8, device=self.device)
+                mask[:self.n_slots] = sel.to(torch.uint8)
+                replay_state_reset(self.layer, self.batch[self._cur], mask, stream)
+
+    def verify(self, io, stream=None, events=None) -> None:
+        stream = stream or torch.cuda.current_stream(self.device)
+        if events:
+            events[0].record(stream)
+        replay_spec_verify(self.layer, self.batch[self._cur], io, stream)
+        if events:
+            events[1].record(stream)
+
+    def commit(self, accepted, stream=None) -> None:
+        """accepted: int32 device tensor [n_slots] (0..T)."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        replay_spec_commit(self.layer, self.batch[self._cur], accepted, self.flag[1 - self._cur], stream)
+        self._cur ^= 1
+
+    def device_committed(self):
+        """(committed counts, flags) the next verify will read (synchronises)."""
+        torch.cuda.synchronize(self.device)
+        return (self.committed[self._cur].cpu().numpy(), self.flag[self._cur][:self.n_slots].cpu().numpy())

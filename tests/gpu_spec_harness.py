@@ -1,0 +1,137 @@
+"""Drive the speculative verify path (HIP, through the C ABI) and the fp64
+oracle side by side on the same inputs.
+
+Every step checks, on the sampled rows: the committed counts and flags the
+device holds for the step against the host mirror (bit-exact); the T outputs
+against the oracle's verify route and against running the drafts token by
+token (tolerance); checkpoints written by flushing rows against the
+committed state (tolerance); the drafts stored as records (bit-exact copies
+of the inputs, cast to nearest even); padding rows untouched.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import linear_attention_decode_replay_amd as rs
+import oracle
+import workloads
+from gpu_harness import rel_err, say
+from linear_attention_decode_replay_amd.state import SpecDecodeLayer
+
+
+@dataclass
+class SpecCase:
+    B: int = 2
+    H: int = 4
+    dv: int = 16
+    dk: int = 32
+    L: int = 8
+    T: int = 4
+    steps: int = 40
+    state_dt: str = "f32"
+    rec_dt: str = "f32"
+    io_dt: str = "f32"
+    seed: int = 0
+    a_lo: float = 0.05
+    a_hi: float = 1.0
+    accept: str = "random"           # accepted counts: random / all / one / none
+    sample: list | None = None       # rows checked against the oracle (None: all)
+    pad_rows: list = field(default_factory=list)
+    strided: bool = False            # q/k/v as strided views of wider buffers
+    force_row0_every: int = 0        # > 0: force a flush on row 0 every n steps
+
+    def name(self):
+        return (f"spec B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
+                f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} accept={self.accept} "
+                f"strided={self.strided} pad={self.pad_rows} seed={self.seed}")
+
+
+def _device(t: torch.Tensor, strided: bool, dev):
+    if not strided:
+        return t.to(dev)
+    B, T, H, d = t.shape
+    wide = torch.full((B, T + 1, H + 2, d + 8), float("nan"), dtype=t.dtype, device=dev)
+    view = wide[:, 1:, 2:, 8:]
+    view.copy_(t.to(dev))
+    return view
+
+
+def run_spec_case(c: SpecCase, dev="cuda") -> dict:
+    say(f"[case] {c.name()}")
+    lay = rs.layer(rs.MAMBA2, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T)
+    n_blocks = c.B + 3
+    d = SpecDecodeLayer(lay, c.B, n_blocks, dev)
+    d.pool.raw.fill_(0xFF)  # NaN in every dtype: a slot read before it is written shows up
+    blocks = workloads.shuffled_blocks(c.seed, c.B, n_blocks)
+    live = [b for b in range(c.B) if b not in c.pad_rows]
+    for b in live:
+        d.assign(b, int(blocks[b]))
+    d.upload(rows=live)
+    sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live]
+    ns = len(sample)
+    spec = oracle.SpecReplayModel(ns, c.H, c.dv, c.dk, c.L, c.T)
+    ref = oracle.SpecTokenByToken(ns, c.H, c.dv, c.dk, c.T)
+    h = np.full(c.B, -1, np.int32)
+    h[live] = 0
+    rdt = workloads.torch_dtype(c.rec_dt)
+    err = {"out_spec": 0.0, "out_vs_tokens": 0.0, "ckpt_flush": 0.0, "flushes": 0, "accepted": 0}
+    for s in range(c.steps):
+        tok = workloads.spec_tokens(c.seed, s, c.B, c.H, c.T, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
+        force = np.zeros(c.B, np.uint8)
+        if c.force_row0_every and (s + 1) % c.force_row0_every == 0 and 0 in live:
+            force[0] = 1
+        fl = rs.rs_spec_meta_step(c.L, c.T, h, force)
+        if force.any():  # a forced flag is the caller's to set on the device
+            d.flag[d._cur][:c.B].copy_(torch.from_numpy(fl.copy()).to(dev))
+        # the device holds exactly the host mirror's counts and flags
+        dh, dflag = d.device_committed()
+        assert np.array_equal(dh[live], h[live]), f"device committed counts, step {s}"
+        assert np.array_equal(dflag[live].astype(bool), fl[live].astype(bool)), f"device flags, step {s}"
+        q, k, v = (_device(t, c.strided, dev) for t in (tok.q, tok.k, tok.v))
+        lam = tok.lam.to(dev)
+        out = torch.full((c.B, c.T, c.H, c.dv), float("nan"), device=dev)
+        d.verify(rs.make_spec_io(q, k, v, lam, out))
+        # oracle routes on the sampled rows, tile-major [rows, H, T, d]
+        tm = lambda t: t[sample].double().numpy().transpose(0, 2, 1, 3)
+        q64, k64, v64 = tm(tok.q), tm(tok.k), tm(tok.v)
+        lam64 = tok.lam[sample].double().numpy().transpose(0, 2, 1)
+        flr = fl[sample].astype(bool)
+        o_spec = spec.verify(q64, k64, v64, lam64, flr)
+        o_tok = ref.verify(q64, k64, v64, lam64)
+        torch.cuda.synchronize()
+        got = out[sample].double().cpu().numpy().transpose(0, 2, 1, 3)
+        err["out_spec"] = max(err["out_spec"], rel_err(got, o_spec))
+        err["out_vs_tokens"] = max(err["out_vs_tokens"], rel_err(got, o_tok))
+        for b in c.pad_rows:
+            assert torch.isnan(out[b]).all(), f"padding row {b} written, step {s}"
+        blk = torch.as_tensor(blocks[sample], device=dev, dtype=torch.long)
+        # drafts stored as records from slot (flushed ? 0 : h)
+        base = np.where(fl[sample] != 0, 0, h[sample])
+        for i_row, b in enumerate(sample):
+            sl = torch.arange(int(base[i_row]), int(base[i_row]) + c.T, device=dev)
+            got_k = d.pool.rec_k()[blk[i_row], :, sl].cpu()          # [H, T, dk]
+            assert torch.equal(got_k, tok.k[b].transpose(0, 1).to(rdt)), f"k records, row {b}, step {s}"
+            got_v = d.pool.rec_x()[blk[i_row], :, sl].cpu()
+            assert torch.equal(got_v, tok.v[b].transpose(0, 1).to(rdt)), f"v records, row {b}, step {s}"
+            got_l = d.pool.rec_lam()[blk[i_row], :, sl].cpu()
+            assert torch.equal(got_l, tok.lam[b].transpose(0, 1)), f"lam records, row {b}, step {s}"
+        flushed = [i for i, b in enumerate(sample) if fl[b]]
+        if flushed:
+            err["flushes"] += len(flushed)
+            ck = d.pool.ckpt()[blk[flushed]].double().cpu().numpy()
+            err["ckpt_flush"] = max(err["ckpt_flush"], rel_err(ck, ref.state()[flushed], 2))
+        a = workloads.spec_accepted(c.seed, s, c.B, c.T, c.accept)
+        a[c.pad_rows] = 0
+        d.commit(torch.from_numpy(a).to(dev))
+        spec.commit(a[sample])
+        ref.commit(a[sample])
+        rs.rs_spec_meta_advance(c.L, c.T, h, fl, a)
+        err["accepted"] += int(a[live].sum())
+    dh, dflag = d.device_committed()
+    assert np.array_equal(dh[live], h[live]), "device committed counts after the last commit"
+    assert int(d.err.item()) == 0, f"{int(d.err.item())} tiles or rows flagged by the kernels' checks"
+    say(f"[errors] {c.name()}: " + ", ".join(f"{k}={v:.3g}" for k, v in err.items()))
+    return err

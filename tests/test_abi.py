@@ -167,3 +167,95 @@ def test_meta_rejects_bad_arguments():
         rs.rs_meta_step(0, np.zeros(3, np.int32))
     with pytest.raises(rs.ReplaySSMError):
         rs.rs_meta_step(65, np.zeros(3, np.int32))
+
+
+# ----------------------------------------------------- speculative layers --
+def test_spec_block_layout_ring_of_L():
+    """A speculative layer's ring holds L committed records (the standard
+    buffer L - 1)."""
+    lay = rs.block_layout(_c2(spec_T=4))
+    assert lay.slots == 16
+    assert lay.rec_k_off == lay.rec_x_off + 128 * 16 * 64 * 2
+    assert lay.block_bytes == lay.rec_lam_off + 128 * 16 * 4
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(spec_T=3), rs.RS_EUNSUPPORTED), (dict(spec_T=8, L=4), rs.RS_EINVAL),
+    (dict(spec_T=-1), rs.RS_EINVAL), (dict(spec_T=4, form=rs.GDN), rs.RS_EUNSUPPORTED),
+    (dict(spec_T=4, d_v=128, d_k=128), rs.RS_EUNSUPPORTED),
+    (dict(spec_T=4, read_dtype="f16"), rs.RS_EUNSUPPORTED),
+])
+def test_spec_layer_validation(bad, code):
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.block_layout(_c2(**bad))
+    assert e.value.code == code and rs.last_error()
+
+
+def test_spec_device_calls_reject_bad_arguments_on_host():
+    spec, std = _c2(spec_T=4), _c2()
+    buf = (ctypes.c_uint8 * 1024)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    batch = rs.RsBatch(4, 0, 4, base, base, base, None, None, base + 256)
+    io = rs.RsSpecIO(base, base, base, 4 * 128 * 128, 128 * 128, 128, 4 * 128 * 128, 128 * 128, 128,
+                     4 * 128 * 64, 128 * 64, 64, base, base)
+    with pytest.raises(rs.ReplaySSMError) as e:                    # standard step on a speculative layer
+        rs.replay_decode_step(spec, batch, rs.RsStepIO(), stream=0)
+    assert e.value.code == rs.RS_EINVAL
+    with pytest.raises(rs.ReplaySSMError) as e:                    # verify on a standard layer
+        rs.replay_spec_verify(std, batch, io, stream=0)
+    assert e.value.code == rs.RS_EINVAL
+    io.q_token_stride = 100                                        # tokens overlap
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_spec_verify(spec, batch, io, stream=0)
+    assert "token stride" in rs.last_error()
+    io.q_token_stride = 128 * 128
+    io.k_row_stride = 2 * 128 * 128                                # rows overlap T tokens
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_spec_verify(spec, batch, io, stream=0)
+    assert "row stride" in rs.last_error()
+    acc = (ctypes.c_int32 * 4)()
+    nf = (ctypes.c_uint8 * 4)()
+    with pytest.raises(rs.ReplaySSMError):                         # accepted NULL
+        rs._check(rs._lib.replay_spec_commit(ctypes.byref(spec), ctypes.byref(batch), None,
+                                              ctypes.addressof(nf), None))
+    nb = rs.RsBatch(4, 0, 4, base, base, base, None, None, None)
+    with pytest.raises(rs.ReplaySSMError) as e:                    # next_write_pos NULL
+        rs._check(rs._lib.replay_spec_commit(ctypes.byref(spec), ctypes.byref(nb), ctypes.addressof(acc),
+                                              ctypes.addressof(nf), None))
+    assert "next_write_pos" in rs.last_error()
+    empty = rs.RsBatch(0, 0, 1, None, None, None, None, None)
+    rs.replay_spec_verify(spec, empty, rs.RsSpecIO(), stream=0)    # nothing to launch
+
+
+@pytest.mark.parametrize("L,T", [(8, 1), (8, 4), (16, 4), (16, 8), (64, 8)])
+def test_spec_meta_matches_oracle_cursor(L, T):
+    """Host flush rule and commit, bit-exact against the oracle's own
+    derivation of the speculative cursor, with random accepted counts and
+    forced flushes."""
+    orc = oracle.get()
+    rng = np.random.default_rng(L * 10 + T)
+    n = 6 * L
+    acc = rng.integers(0, T + 1, n).astype(np.int32)
+    forced = (rng.random(n) < 0.1).astype(np.uint8)
+    for h0 in sorted({0, L // 2, L - T + 1 if L - T + 1 >= 0 else 0}):
+        h = np.array([h0], np.int32)
+        hs, fs = [], []
+        for s in range(n):
+            fl = rs.rs_spec_meta_step(L, T, h, forced[s:s + 1])
+            hs.append(int(h[0]))
+            fs.append(bool(fl[0]))
+            rs.rs_spec_meta_advance(L, T, h, fl, acc[s:s + 1])
+        oh, of = orc.spec_cursor_run(L, T, h0, acc, forced)
+        assert np.array_equal(np.array(hs), oh) and np.array_equal(np.array(fs), of), (L, T, h0)
+
+
+def test_spec_meta_pad_rows_and_bad_arguments():
+    h = np.array([-1, 12, 13], np.int32)
+    fl = rs.rs_spec_meta_step(16, 4, h, np.array([1, 0, 0], np.uint8))
+    assert list(fl) == [0, 0, 1]
+    rs.rs_spec_meta_advance(16, 4, h, fl, np.array([3, 4, 2], np.int32))
+    assert list(h) == [-1, 16, 2]
+    with pytest.raises(rs.ReplaySSMError):
+        rs.rs_spec_meta_step(16, 17, h)
+    with pytest.raises(rs.ReplaySSMError):
+        rs.rs_spec_meta_step(16, 0, h)

@@ -1,0 +1,104 @@
+"""Speculative verify on the GPU (through the C ABI) against the fp64 oracle.
+
+Gates (the decode path's): 1e-4 of each tile's largest output when inputs,
+records and state are fp32; 2e-2 with fp16/bf16 anywhere.  Committed counts,
+flags and the stored draft records are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_decode_replay_amd as rs
+from gpu_harness import TOL_F32, TOL_LOW, say
+from gpu_spec_harness import SpecCase, run_spec_case
+from linear_attention_decode_replay_amd.state import SpecDecodeLayer
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(err, tol):
+    assert err["out_spec"] <= tol, err
+    assert err["out_vs_tokens"] <= tol, err
+    assert err["ckpt_flush"] <= tol, err
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_spec_tiny_fp32(T):
+    """Tiny shapes, everything fp32, random accepted counts 0..T, L = 8."""
+    err = run_spec_case(SpecCase(T=T, steps=40, seed=T))
+    assert err["flushes"] >= 4
+    _check(err, TOL_F32)
+
+
+@pytest.mark.parametrize("accept", ["all", "one", "none"])
+def test_spec_accept_policies(accept):
+    """Every draft accepted (a flush every L / T steps), one token per step,
+    and nothing accepted (the ring never grows, no flush)."""
+    err = run_spec_case(SpecCase(T=4, L=16, steps=36, accept=accept, seed=11))
+    if accept == "none":
+        assert err["flushes"] == 0 and err["accepted"] == 0
+    else:
+        assert err["flushes"] >= 2
+    _check(err, TOL_F32)
+
+
+def test_spec_long_memory():
+    """Slowly decaying heads: the checkpoint term dominates every output."""
+    err = run_spec_case(SpecCase(T=4, L=8, steps=30, a_lo=0.001, a_hi=0.01, seed=3))
+    _check(err, TOL_F32)
+
+
+def test_spec_strided_padding_forced_lowprec():
+    """bf16 inputs as strided views, fp16 records, a padding row, a forced
+    flush on row 0 every 5 steps."""
+    err = run_spec_case(SpecCase(B=4, T=4, L=8, steps=30, rec_dt="f16", io_dt="bf16", strided=True,
+                                 pad_rows=[2], force_row0_every=5, seed=4))
+    _check(err, TOL_LOW)
+
+
+@pytest.mark.parametrize("state_dt", ["f32", "f16"])
+def test_spec_nemotron_shape(state_dt):
+    """Nemotron-3-Super layer shape: 128 heads, 64 x 128, batch 256, L = 16,
+    T = 4, bf16 inputs, fp16 records; 4 rows sampled through the oracle (all
+    heads), every row on the GPU."""
+    err = run_spec_case(SpecCase(B=256, H=128, dv=64, dk=128, L=16, T=4, steps=16, state_dt=state_dt,
+                                 rec_dt="f16", io_dt="bf16", a_lo=1.0, a_hi=8.0, sample=[0, 77, 128, 255],
+                                 seed=21))
+    assert err["flushes"] >= 1
+    _check(err, TOL_LOW)
+
+
+def test_spec_T8_nemotron_shape():
+    err = run_spec_case(SpecCase(B=64, H=128, dv=64, dk=128, L=16, T=8, steps=12, rec_dt="f16", io_dt="bf16",
+                                 a_lo=1.0, a_hi=8.0, sample=[0, 63], seed=22))
+    _check(err, TOL_LOW)
+
+
+def test_spec_commit_rejects_out_of_range_accept():
+    """An accepted count outside 0..T commits nothing for that row and is
+    counted; the other rows commit normally."""
+    lay = rs.layer(rs.MAMBA2, 2, 16, 32, 8, "f32", "f32", "f32", None, 4)
+    d = SpecDecodeLayer(lay, 3, 3, "cuda")
+    for b in range(3):
+        d.assign(b, b)
+    d.upload(rows=range(3))
+    q = torch.randn(3, 4, 2, 32, device="cuda")
+    out = torch.empty(3, 4, 2, 16, device="cuda")
+    lam = -torch.rand(3, 4, 2, device="cuda")
+    d.verify(rs.make_spec_io(q, q, q[..., :16].contiguous(), lam, out))
+    d.commit(torch.tensor([2, 5, -1], dtype=torch.int32, device="cuda"))
+    h, fl = d.device_committed()
+    assert list(h) == [2, 0, 0] and list(fl) == [0, 0, 0]
+    assert int(d.err.item()) == 2
+    say("[spec] out-of-range accepted counts rejected")
+
+
+def test_spec_layer_rejects_standard_step():
+    lay = rs.layer(rs.MAMBA2, 2, 16, 32, 8, "f32", "f32", "f32", None, 4)
+    d = SpecDecodeLayer(lay, 2, 2, "cuda")
+    io = rs.make_io(torch.zeros(2, 2, 32, device="cuda"), torch.zeros(2, 2, 32, device="cuda"),
+                    torch.zeros(2, 2, 16, device="cuda"), torch.zeros(2, 2, device="cuda"),
+                    torch.zeros(2, 2, 16, device="cuda"))
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_decode_step(lay, d.batch[0], io)
+    assert e.value.code == rs.RS_EINVAL

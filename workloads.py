@@ -175,3 +175,34 @@ def shuffled_blocks(seed: int, n_rows: int, n_blocks: int) -> np.ndarray:
     """A block table mapping each row to a distinct block, in shuffled order."""
     rng = np.random.default_rng([seed, _S_POOL])
     return rng.permutation(n_blocks)[:n_rows].astype(np.int32)
+
+
+@dataclass
+class SpecTokens:
+    q: torch.Tensor      # [B, T, H, dk] io dtype
+    k: torch.Tensor      # [B, T, H, dk] io dtype
+    v: torch.Tensor      # [B, T, H, dv] io dtype
+    lam: torch.Tensor    # [B, T, H] float32
+
+
+def spec_tokens(seed: int, step: int, B: int, H: int, T: int, dv: int, dk: int, io: str = "bf16",
+                a_lo: float = 1.0, a_hi: float = 8.0) -> SpecTokens:
+    """T draft tokens per row for speculative step `step` (Mamba-2 recipe);
+    draft i of step s is the Mamba-2 token of step T s + i, so the same
+    per-head decay scales apply."""
+    toks = [mamba2_tokens(seed, T * step + i, B, H, dv, dk, io, a_lo, a_hi) for i in range(T)]
+    st = lambda name: torch.stack([getattr(t, name) for t in toks], dim=1).contiguous()
+    return SpecTokens(st("q"), st("k"), st("v"), st("lam"))
+
+
+def spec_accepted(seed: int, step: int, B: int, T: int, policy: str = "random") -> np.ndarray:
+    """Accepted draft counts per row for one verify step: "random" (uniform
+    0..T), "all" (T), "one" (1) or "none" (0)."""
+    if policy == "all":
+        return np.full(B, T, np.int32)
+    if policy == "one":
+        return np.ones(B, np.int32)
+    if policy == "none":
+        return np.zeros(B, np.int32)
+    rng = np.random.default_rng([seed, _S_SCHED, 7919, step])
+    return rng.integers(0, T + 1, size=B).astype(np.int32)
