@@ -391,6 +391,124 @@ def suite_stack(out, n_layers=40):
             print(json.dumps(line), file=out, flush=True)
 
 
+def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush):
+    """Algorithmic HBM bytes of one speculative verify launch (rows with h
+    committed records, flushing or not) plus its commit launch.  Per (row,
+    head): read the checkpoint and the h committed records, read T draft
+    tokens (q, k, v, log-decay), write T records and T fp32 outputs; a
+    flushing row also writes the checkpoint.  Per row: block id, count and
+    flag read by the verify; the commit reads block id, count, flag and the
+    accepted count and writes the next count and flag."""
+    h = np.asarray(h)
+    flush = np.asarray(flush, bool)
+    ms = dv * dk * _ES[state]
+    r = (dv + dk) * _ES[rec] + 4
+    tok = (2 * dk + dv) * _ES[io] + 4
+    per_head = ms + h * r + T * (tok + r + 4 * dv) + np.where(flush, ms, 0)
+    return float(np.sum(H * per_head + 9) + B * 18)
+
+
+def suite_spec(out, steps=48, n_pools=4):
+    """Speculative verify at the Nemotron-3-Super layer shape, batch 256,
+    L = 16, fp32 checkpoint, fp16 records, bf16 inputs, T in {4, 8}, with
+    every draft accepted, one token per step, and uniform 0..T acceptance.
+    One step = one verify launch + one commit launch (the committed counts
+    stay on the device); time per step from one pair of HIP events around
+    the timed steps; 4 state pools in rotation (cold caches).  Reported per
+    committed token next to the standard replay step and the conventional
+    step measured the same way."""
+    import torch
+    import linear_attention_decode_replay_amd as rs
+    import workloads
+    from linear_attention_decode_replay_amd.state import SpecDecodeLayer
+    dev = torch.device("cuda", 0)
+    base = dict(WORKLOADS["nemotron"])
+    B, H, dv, dk, L = base["B"], base["H"], base["dv"], base["dk"], base["L"]
+    # standard steps for reference (one token per row per step)
+    ios, keep = _inputs(base, B, 16, dev)
+    ref_us = {}
+    for kind in ("replay", "conventional"):
+        layers = _layer_stack(base, B, n_pools, dev)
+        n_warm, n_time = L * n_pools, 2 * L * n_pools
+        for s in range(n_warm + n_time):
+            if s == n_warm:
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            d = layers[s % n_pools]
+            if kind == "replay":
+                d.step(ios[s % 16])
+            else:
+                d.conventional_step(ios[s % 16])
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ref_us[kind] = 1e3 * e0.elapsed_time(e1) / n_time
+        del layers
+        torch.cuda.empty_cache()
+    del ios, keep
+    for T in (4, 8):
+        lay = rs.layer(0, H, dv, dk, L, "f32", "f16", "bf16", None, T)
+        drafts = []
+        for s in range(8):
+            t = workloads.spec_tokens(11, s, B, H, T, dv, dk, "bf16")
+            q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
+            o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+            drafts.append(((q, k, v, lam, o), rs.make_spec_io(q, k, v, lam, o)))
+        for policy in ("all", "one", "random"):
+            pools = []
+            for _ in range(n_pools):
+                d = SpecDecodeLayer(lay, B, B, dev)
+                for b in range(B):
+                    d.assign(b, b)
+                d.upload(rows=range(B))
+                pools.append(d)
+            acc = [torch.from_numpy(workloads.spec_accepted(3, s, B, T, policy)).to(dev) for s in range(steps)]
+            acc_host = [a.cpu().numpy() for a in acc]
+            hmirror = [np.zeros(B, np.int32) for _ in range(n_pools)]
+            n_warm = steps // 2
+            nbytes, tokens, n_flush = 0.0, 0, 0
+            for s in range(n_warm + steps):
+                if s == n_warm:
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                pi = s % n_pools
+                d, hm = pools[pi], hmirror[pi]
+                a = acc_host[s % steps]
+                fl = rs.rs_spec_meta_step(L, T, hm)
+                if s >= n_warm:
+                    nbytes += spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl)
+                    tokens += int(a.sum())
+                    n_flush += int(fl.sum())
+                d.verify(drafts[s % 8][1])
+                d.commit(acc[s % steps])
+                rs.rs_spec_meta_advance(L, T, hm, fl, a)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / steps
+            errs = sum(int(d.err.item()) for d in pools)
+            if errs:
+                raise RuntimeError(f"{errs} tiles or rows flagged by the speculative kernels' checks")
+            gb = nbytes / steps / 1e9
+            tok_per_row = tokens / steps / B
+            line = {"suite": "spec_verify", "T": T, "accept": policy, "batch": B, "L": L,
+                    "us_per_step": round(us, 2), "gb_per_step": round(gb, 4), "tbs": round(gb / (us * 1e-6) / 1e3, 3),
+                    "committed_tokens_per_row_step": round(tok_per_row, 3),
+                    "flush_fraction": round(n_flush / (steps * B), 4),
+                    "us_per_committed_token": round(us / tok_per_row, 2) if tokens else None,
+                    "replay_step_us": round(ref_us["replay"], 2), "conventional_step_us": round(ref_us["conventional"], 2),
+                    "speedup_per_token_vs_replay": round(ref_us["replay"] / (us / tok_per_row), 3) if tokens else None,
+                    "speedup_per_token_vs_conventional":
+                        round(ref_us["conventional"] / (us / tok_per_row), 3) if tokens else None}
+            print(json.dumps(line), file=out, flush=True)
+            del pools
+            torch.cuda.empty_cache()
+        del drafts
+        torch.cuda.empty_cache()
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain device-to-device copy of `mib` MiB, three times: its
     FETCH_SIZE / WRITE_SIZE readings give the scale of those counters."""
@@ -484,6 +602,8 @@ def main(argv=None):
     ap.add_argument("--suite", metavar="PATH",
                     help="instead of the one-line benchmark, run the Gated DeltaNet batch sweep and the "
                          "40-layer stack and write JSON lines to PATH")
+    ap.add_argument("--suite-only", choices=["gdn", "stack", "spec"], default=None,
+                    help="with --suite: run one part of it")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                          "into per-launch HBM bytes in profiles/counters.json and print them; runs nothing on the GPU")
@@ -495,8 +615,12 @@ def main(argv=None):
             print("the suite runs on one GPU", file=sys.stderr)
             return 2
         with open(args.suite, "w") as out:
-            suite_gdn_sweep(out)
-            suite_stack(out)
+            if args.suite_only in (None, "gdn"):
+                suite_gdn_sweep(out)
+            if args.suite_only in (None, "stack"):
+                suite_stack(out)
+            if args.suite_only in (None, "spec"):
+                suite_spec(out)
         print(open(args.suite).read(), end="")
         return 0
 

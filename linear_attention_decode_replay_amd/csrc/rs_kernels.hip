@@ -158,6 +158,9 @@ __device__ __forceinline__ void pack_n(const float* in, u32x4* out) {
     __builtin_memcpy(out, tmp, sizeof(tmp));
 }
 
+template <int G>
+__device__ __forceinline__ void group_max(float& x);  // below, with the other lane-group reductions
+
 // One state row of E4M3 read copy (OCP 8-bit floating point specification:
 // bias 7, largest finite 448).  The row's N * G values are spread over an
 // aligned group of G lanes, N per lane.  Its scale is 2^e with e the smallest
@@ -172,8 +175,7 @@ __device__ __forceinline__ float encode_e4m3_row(const float* x, u32x4* codes) {
     float amax = 0.f;
 #pragma unroll
     for (int c = 0; c < N; ++c) amax = fmaxf(amax, fabsf(x[c]));
-#pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    group_max<G>(amax);
     const uint32_t b = __float_as_uint(amax);
     int e = (int)((b >> 23) & 0xffu) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
     e = max(e, -100);
@@ -208,6 +210,29 @@ __device__ __forceinline__ void store_read_row(const float* x, typename TL::S* d
 }
 
 // ------------------------------------------------------- lane-group sums --
+// Partner exchange for the butterfly sums below, inside aligned groups of
+// 2 * OFF lanes.  The sums only need, at level OFF, a pairing of each lane
+// with one lane of the other half of its aligned group of 2 * OFF lanes (the
+// lanes of a pair agree on every higher bit, so they hold the same partial
+// sums, and each lane keeps the half selected by its own OFF bit).  That
+// allows the cheap cross-lane forms of CDNA: DPP quad permutations for
+// OFF = 1, 2 (lane ^ 1, lane ^ 2), DPP row half-mirror for OFF = 4 (lane i
+// with 7 - i in its group of 8), DPP row mirror for OFF = 8 (i with 15 - i in
+// its row of 16), and an LDS-free swizzle for OFF = 16 (lane ^ 16 in its
+// group of 32); all are register moves, not LDS permutations.
+template <int OFF>
+__device__ __forceinline__ float xpartner(float x) {
+    const int v = __float_as_int(x);
+    int r;
+    if constexpr (OFF == 1) r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+    else if constexpr (OFF == 2) r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (OFF == 4) r = __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    else if constexpr (OFF == 8) r = __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    else if constexpr (OFF == 16) r = __builtin_amdgcn_ds_swizzle(v, 0x401F);  // and 0x1f, xor 0x10
+    else r = __float_as_int(__shfl_xor(x, OFF));
+    return __int_as_float(r);
+}
+
 // Sum N per-lane values over an aligned group of lanes (offsets OFF, OFF/2,
 // ..., 1; gl = lane index within the group).  While more than KEEP values are
 // left, the lane whose OFF bit is set keeps the upper half of its values,
@@ -225,12 +250,12 @@ __device__ __forceinline__ void xsum(float* v, int gl) {
             for (int i = 0; i < N / 2; ++i) {
                 const float send = up ? v[i] : v[i + N / 2];
                 const float keep = up ? v[i + N / 2] : v[i];
-                v[i] = keep + __shfl_xor(send, OFF);
+                v[i] = keep + xpartner<OFF>(send);
             }
             xsum<N / 2, OFF / 2, KEEP>(v, gl);
         } else {
 #pragma unroll
-            for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], OFF);
+            for (int i = 0; i < N; ++i) v[i] += xpartner<OFF>(v[i]);
             xsum<N, OFF / 2, KEEP>(v, gl);
         }
     }
@@ -267,9 +292,20 @@ constexpr int xsum_dup_mask() {
 // Plain butterfly sum of one value over the group; every lane gets the sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if constexpr (G > 1) {
+        x += xpartner<G / 2>(x);
+        x = group_sum<G / 2>(x);
+    }
     return x;
+}
+
+// Butterfly maximum over the group, in place; every lane gets the maximum.
+template <int G>
+__device__ __forceinline__ void group_max(float& x) {
+    if constexpr (G > 1) {
+        x = fmaxf(x, xpartner<G / 2>(x));
+        group_max<G / 2>(x);
+    }
 }
 
 // ------------------------------------------------------------ tile shape --
