@@ -44,6 +44,9 @@ METRIC = "decode steps/s + achieved HBM TB/s (% peak), replay vs conventional at
 
 WORKLOADS = {
     "nemotron": dict(form=0, H=128, dv=64, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16", read=None),
+    # the same layer with the released grouped-key layout: 8 key groups of 16 heads
+    "nemotron-grouped": dict(form=0, H=128, dv=64, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16",
+                             read=None, groups=8),
     "gdn": dict(form=1, H=32, dv=128, dk=128, B=256, L=16, state="f32", rec="f16", io="bf16", read=None),
 }
 
@@ -51,7 +54,7 @@ _ES = {"f32": 4, "f16": 2, "bf16": 2}
 
 
 # ----------------------------------------------------------- byte accounting --
-def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay", read=None):
+def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay", read=None, groups=0):
     """Algorithmic HBM bytes of one launch over B rows at cursor w.
 
     Checkpoint + buffer step, per (row, head): read the checkpoint (d_v d_k
@@ -63,10 +66,13 @@ def step_bytes(form, H, dv, dk, B, state, rec, io, w, flush, kind="replay", read
     row, read the block id (4 bytes) plus, for the checkpoint + buffer
     step, the cursor and flag (5 bytes).  With a two-precision checkpoint
     (`read` = the read copy's dtype) a non-flush row reads the read copy, a
-    flush row reads the recurrence copy and writes both."""
+    flush row reads the recurrence copy and writes both.  With `groups` key
+    groups (0: a key per head) the key record and the q, k inputs of a group
+    are counted once, spread over its heads."""
+    hg = H // groups if groups else 1
     ms = dv * dk * _ES[state]
-    r = dv * _ES[rec] + dk * _ES[rec] + 4
-    io_b = (2 * dk + dv) * _ES[io] + 4 + (4 if form == 1 else 0) + 4 * dv
+    r = dv * _ES[rec] + dk * _ES[rec] / hg + 4
+    io_b = (2 * dk / hg + dv) * _ES[io] + 4 + (4 if form == 1 else 0) + 4 * dv
     if kind == "conventional":
         return B * (H * (2 * ms + io_b) + 4)
     if read:
@@ -85,8 +91,8 @@ def read_copy_bytes(dv, dk, read):
     return dv * dk * _ES[read]
 
 
-def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay", read=None):
-    return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind, read) for w in range(L))
+def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay", read=None, groups=0):
+    return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind, read, groups) for w in range(L))
 
 
 def kernel_source_hash() -> str:
@@ -98,6 +104,8 @@ def kernel_source_hash() -> str:
 
 def workload_key(name, cfg) -> str:
     key = f"{name}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
+    if cfg.get("groups"):
+        key += f"-g{cfg['groups']}"
     return key + (f"-read{cfg['read']}" if cfg.get("read") else "")
 
 
@@ -187,7 +195,9 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     torch.cuda.set_device(dev)
     # the conventional step has one state copy whatever the replay layout
     read = cfg["read"] if kind == "replay" else None
-    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"], read)
+    groups = cfg.get("groups", 0)
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"], read,
+                   0, groups)
     B = cfg["B"]
     layers = []
     for p in range(n_pools):
@@ -200,6 +210,9 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     ios, keep = [], []
     for s in range(n_inputs):
         t = workloads.tokens(cfg["form"], 11, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
+        if groups:  # the group's key and query: those drawn for its first head
+            hg = cfg["H"] // groups
+            t = workloads.Tokens(t.q[:, ::hg].contiguous(), t.k[:, ::hg].contiguous(), t.v, t.lam, t.beta)
         q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
         beta = t.beta.to(dev) if t.beta is not None else None
         out = torch.empty((B, cfg["H"], cfg["dv"]), dtype=torch.float32, device=dev)
@@ -236,7 +249,7 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     if errs:
         raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
     nbytes = [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"],
-                         w or 0, bool(f), kind, cfg["read"]) for (w, f) in cursors]
+                         w or 0, bool(f), kind, cfg["read"], groups) for (w, f) in cursors]
     # Breakdown by cursor position (after the timed region, not part of it):
     # one more window per pool with events around every launch.
     by_pos = {}
@@ -643,12 +656,15 @@ def main(argv=None):
     rep = run_gpu(cfg, args.steps, args.warmup, args.pools, "replay")
     conv = run_gpu(cfg, args.steps, args.warmup, args.pools, "conventional")
 
+    groups = cfg.get("groups", 0)
     wb_r = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"],
-                        read=cfg["read"])
-    wb_c = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"], "conventional")
+                        read=cfg["read"], groups=groups)
+    wb_c = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"],
+                        "conventional", groups=groups)
     form_name = "mamba2" if cfg["form"] == 0 else "gdn"
     state_desc = f"{cfg['state']} state" + (f" + {cfg['read']} read copy" if cfg["read"] else "")
-    workload = (f"{form_name} layer, {cfg['H']} heads, d_v={cfg['dv']}, d_k={cfg['dk']}, {state_desc}, "
+    keys = f", keys shared by {groups} groups" if groups else ""
+    workload = (f"{form_name} layer, {cfg['H']} heads{keys}, d_v={cfg['dv']}, d_k={cfg['dk']}, {state_desc}, "
                 f"{cfg['rec']} records, {cfg['io']} q/k/v, batch {cfg['B']}, L={cfg['L']}")
     key = workload_key(args.workload, cfg)
     traffic = load_traffic(key)
@@ -670,6 +686,7 @@ def main(argv=None):
                    "d_v": cfg["dv"], "d_k": cfg["dk"], "L": cfg["L"], "state_dtype": cfg["state"],
                    "read_copy_dtype": cfg["read"],
                    "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": args.pools,
+                   "key_groups": groups or cfg["H"],
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

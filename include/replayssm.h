@@ -85,6 +85,13 @@ typedef enum {
  *               replay_spec_verify; replay_decode_step rejects it.  Mamba-2
  *               form, single fp32 or fp16 checkpoint, (d_v, d_k) = (16, 32)
  *               or (64, 128).
+ * n_groups:     0 or n_heads for a key and a query per head.  A divisor
+ *               G < n_heads shares one key and one query among each run of
+ *               n_heads / G consecutive heads, the released grouped-key
+ *               layout (blog "The identity", the paragraph on the released
+ *               kernel: values and decays per value head, keys per group):
+ *               q and k inputs are [n_rows][G][d_k] and the ring keeps one
+ *               key record per group.  Standard decoding only (spec_T = 0).
  * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16,
  *               RS_BF16 or RS_E4M3 for a two-precision checkpoint (blog "The
  *               precision argument, derived"): state_dtype RS_F32 is the
@@ -112,6 +119,8 @@ typedef struct {
     int32_t read_dtype;
     int32_t spec_T;   /* 0: standard decoding; 1, 2, 4 or 8: speculative layer,
                          see replay_spec_verify */
+    int32_t n_groups; /* 0 (= n_heads): one key and query per head; else the
+                         number of key groups, see below */
 } rs_layer;
 
 /*
@@ -121,7 +130,8 @@ typedef struct {
  * Offsets are from the block start; every region starts 256-byte aligned.
  *   ckpt     [n_heads][d_v][d_k]    state_dtype, row-major per head
  *   rec_x    [n_heads][slots][d_v]  record_dtype
- *   rec_k    [n_heads][slots][d_k]  record_dtype
+ *   rec_k    [n_groups][slots][d_k] record_dtype (n_groups = n_heads
+ *                                   unless the layer groups its keys)
  *   rec_lam  [n_heads][slots]       fp32 log-decay
  *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
  *                                   ckpt_lo_off is 0 otherwise), each row of
@@ -185,9 +195,11 @@ typedef struct {
 } rs_batch;
 
 /*
- * One token per row.  q, k: [n_rows][n_heads][d_k]; v: [n_rows][n_heads][d_v],
- * all io_dtype, unit stride along the last dimension, row and head strides in
- * ELEMENTS (so strided views into a wider projection output work).
+ * One token per row.  q, k: [n_rows][n_heads][d_k] ([n_rows][n_groups][d_k]
+ * for a layer with grouped keys, the "head" stride then being the group
+ * stride); v: [n_rows][n_heads][d_v]; all io_dtype, unit stride along the
+ * last dimension, row and head strides in ELEMENTS (so strided views into a
+ * wider projection output work).
  * log_decay: [n_rows][n_heads] fp32, lam = log alpha <= 0 (Mamba-2) or the
  * gate g (Gated DeltaNet); -inf is allowed and means alpha = 0.
  * beta: [n_rows][n_heads] fp32, Gated DeltaNet only (NULL for Mamba-2).

@@ -36,7 +36,7 @@ class RsLayer(_c.Structure):
     _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
                 ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
                 ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32),
-                ("spec_T", _c.c_int32)]
+                ("spec_T", _c.c_int32), ("n_groups", _c.c_int32)]
 
 
 class RsBlockLayout(_c.Structure):
@@ -123,15 +123,17 @@ _DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
 
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
-          record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0) -> RsLayer:
+          record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0, n_groups: int = 0) -> RsLayer:
     """read_dtype: None for a single checkpoint, "f16" / "bf16" / "e4m3" for
     a two-precision checkpoint (fp32 recurrence copy + read copy; E4M3 with a
     power-of-two scale per state row).  spec_T: 0 for standard decoding, T
-    for a speculative layer verifying T drafts per step."""
+    for a speculative layer verifying T drafts per step.  n_groups: 0 for a
+    key and query per head, else the number of key groups (q, k inputs then
+    [rows, n_groups, d_k], one key record per group)."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
                    code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype),
-                   int(spec_T))
+                   int(spec_T), int(n_groups))
 
 
 def block_layout(lay: RsLayer) -> RsBlockLayout:
@@ -303,11 +305,13 @@ class Pool:
                             self._tdt[L.record_dtype], (L.n_heads, s, L.d_v))
 
     def rec_k(self):
-        """[n_blocks, H, slots, d_k] in the record dtype."""
+        """[n_blocks, G, slots, d_k] in the record dtype (G = key groups,
+        n_heads unless the layer groups its keys)."""
         L, s = self.layer, self.layout.slots
         es = 4 if L.record_dtype == F32 else 2
-        return self._region(self.layout.rec_k_off, L.n_heads * s * L.d_k * es,
-                            self._tdt[L.record_dtype], (L.n_heads, s, L.d_k))
+        G = L.n_groups if L.n_groups > 0 else L.n_heads
+        return self._region(self.layout.rec_k_off, G * s * L.d_k * es,
+                            self._tdt[L.record_dtype], (G, s, L.d_k))
 
     def ckpt_lo(self):
         """[n_blocks, H, d_v, d_k] read copy of a two-precision checkpoint

@@ -37,6 +37,9 @@ int dtype_bytes(int dt) { return dt == RS_F32 ? 4 : (dt == RS_E4M3 ? 1 : 2); }
 const int kMaxL = 64;
 
 bool two_precision(const rs_layer& L) { return L.read_dtype >= 0 && L.read_dtype != L.state_dtype; }
+
+// Key groups: n_groups, or one per head.
+int groups_of(const rs_layer& L) { return L.n_groups > 0 ? L.n_groups : L.n_heads; }
 const size_t kMaxLds = 64 * 1024;
 
 int check_layer(const rs_layer* L, rs::Kind kind) {
@@ -57,6 +60,10 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
             return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy only");
     }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
+    if (L->n_groups < 0 || (L->n_groups > 0 && L->n_heads % L->n_groups != 0))
+        return fail(RS_EINVAL, "n_groups (%d) must be 0 or divide n_heads (%d)", L->n_groups, L->n_heads);
+    if (L->spec_T != 0 && groups_of(*L) != L->n_heads)
+        return fail(RS_EUNSUPPORTED, "speculative verify: one key per head only (n_groups = 0)");
     const bool spec_kind = kind == rs::Kind::SpecVerify || kind == rs::Kind::SpecCommit;
     if (L->spec_T != 0) {
         const int T = L->spec_T;
@@ -96,7 +103,7 @@ void layout_of(const rs_layer& L, rs_block_layout* o) {
     o->ckpt_off = 0;
     o->rec_x_off = align_up(H * L.d_v * L.d_k * sb, 256);
     o->rec_k_off = align_up(o->rec_x_off + H * slots * L.d_v * rb, 256);
-    o->rec_lam_off = align_up(o->rec_k_off + H * slots * L.d_k * rb, 256);
+    o->rec_lam_off = align_up(o->rec_k_off + (int64_t)groups_of(L) * slots * L.d_k * rb, 256);
     o->block_bytes = align_up(o->rec_lam_off + H * slots * 4, 256);
     o->ckpt_lo_off = 0;
     o->ckpt_scale_off = 0;
@@ -149,12 +156,12 @@ int check_io(const rs_layer& L, const rs_batch& b, const rs_step_io* io) {
     if (b.n_rows == 0) return RS_OK;
     const int e = dtype_bytes(L.io_dtype);
     int rc;
+    const int64_t G = groups_of(L);
     if ((rc = check_vec("q", io->q, io->q_row_stride, io->q_head_stride, L.d_k, e))) return rc;
     if ((rc = check_vec("k", io->k, io->k_row_stride, io->k_head_stride, L.d_k, e))) return rc;
     if ((rc = check_vec("v", io->v, io->v_row_stride, io->v_head_stride, L.d_v, e))) return rc;
     if (b.n_rows > 1) {
-        if (io->q_row_stride < (int64_t)L.n_heads * io->q_head_stride ||
-            io->k_row_stride < (int64_t)L.n_heads * io->k_head_stride ||
+        if (io->q_row_stride < G * io->q_head_stride || io->k_row_stride < G * io->k_head_stride ||
             io->v_row_stride < (int64_t)L.n_heads * io->v_head_stride)
             return fail(RS_EINVAL, "row strides overlap the heads of the previous row");
     }
@@ -187,6 +194,7 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.n_heads = L.n_heads;
     p.L = L.L;
     p.slots = lay.slots;
+    p.heads_per_group = L.n_heads / groups_of(L);
     return p;
 }
 

@@ -32,6 +32,7 @@ struct StepParams {
     const float* beta;
     float* out;
     int32_t n_rows, n_heads, L, slots;
+    int32_t heads_per_group;   // heads sharing one key / query (1: per-head keys)
     // speculative verify / commit
     int32_t spec_T;
     int64_t qs_t, ks_t, vs_t;  // token strides (elements)

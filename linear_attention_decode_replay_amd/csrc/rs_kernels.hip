@@ -567,10 +567,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;  // row scales
     R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
-    R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    // keys and queries per group of heads_per_group heads (1: per head)
+    const int grp = id.head / p.heads_per_group;
+    const bool key_owner = id.head == grp * p.heads_per_group;  // appends the group's key
+    R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.slots * DK;
     float* rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
-    const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
-    const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
+    const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
     const float lam = p.lam[id.tile];
     const bool fl = (w == p.slots) || flag;
@@ -726,7 +729,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     if (!fl) {  // uniform across the workgroup
         if (id.part == 0) {
             if (tid == 0) rl[w] = lam;
-            if (rg == 0) {
+            if (rg == 0 && key_owner) {
                 R* kd = rk + (int64_t)w * DK + col0;
 #pragma unroll
                 for (int h = 0; h < HPC; ++h) store_f<TR, EPC>(kd + EPC * LPR * h, kv + h * EPC);
@@ -800,8 +803,9 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 
     char* base = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
-    const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
-    const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const int grp = id.head / p.heads_per_group;
+    const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
+    const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
 
     __shared__ float s_v[DVW], s_u[DVW];
@@ -912,7 +916,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;
     const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
-    const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)(id.head / p.heads_per_group) * p.slots * DK;
     const float* rl = reinterpret_cast<const float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];

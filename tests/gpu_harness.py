@@ -72,19 +72,34 @@ class Case:
     check_conventional: bool = True
     force_every: int = 0             # > 0: force a flush on row 0 every n steps
     read_dt: str | None = None       # two-precision checkpoint: read copy dtype
+    groups: int = 0                  # key groups (0: a key and query per head)
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"{f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
-                f"strided={self.strided} pad={self.pad_rows} seed={self.seed}")
+                f"strided={self.strided} pad={self.pad_rows} groups={self.groups} seed={self.seed}")
 
 
-def _device_tokens(tok, strided: bool, dev):
+def grouped(tok, hg: int):
+    """Tokens of a layer whose keys and queries are shared by groups of hg
+    heads: the group takes the key and query drawn for its first head, and
+    every head of the group sees them (what the oracle, which works per head,
+    is given).  Returns (per-head tokens, group q [B, G, dk], group k)."""
+    if hg == 1:
+        return tok, tok.q, tok.k
+    qg, kg = tok.q[:, ::hg].contiguous(), tok.k[:, ::hg].contiguous()
+    full = workloads.Tokens(qg.repeat_interleave(hg, dim=1), kg.repeat_interleave(hg, dim=1), tok.v, tok.lam,
+                            tok.beta)
+    return full, qg, kg
+
+
+def _device_tokens(tok, strided: bool, dev, qk=None):
+    q_in, k_in = qk if qk is not None else (tok.q, tok.k)
     if not strided:
-        return tok.q.to(dev), tok.k.to(dev), tok.v.to(dev)
+        return q_in.to(dev), k_in.to(dev), tok.v.to(dev)
     out = []
-    for t in (tok.q, tok.k, tok.v):
+    for t in (q_in, k_in, tok.v):
         B, H, d = t.shape
         wide = torch.full((B, H + 1, d + 8), float("nan"), dtype=t.dtype, device=dev)
         view = wide[:, 1:, 8:]
@@ -99,7 +114,8 @@ def run_case(c: Case, dev="cuda") -> dict:
     Returns the worst errors seen; raises AssertionError on any bit-exact
     mismatch (cursor, flush flag, copied record fields, untouched pad rows)."""
     say(f"[case] {c.name()}")
-    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt, 0, c.groups)
+    hg = c.H // c.groups if c.groups else 1
     n_blocks = c.n_blocks or (c.B + 3)
     rep = DecodeLayer(lay, c.B, n_blocks, dev)
     conv = DecodeLayer(lay, c.B, n_blocks, dev) if c.check_conventional else None
@@ -129,7 +145,8 @@ def run_case(c: Case, dev="cuda") -> dict:
            "out_replay_step": 0.0, "out_replay_vs_exact": 0.0, "flushes": 0}
     for s in range(c.steps):
         tok = workloads.tokens(c.form, c.seed, s, c.B, c.H, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
-        q, k, v = _device_tokens(tok, c.strided, dev)
+        tok, qg, kg = grouped(tok, hg)
+        q, k, v = _device_tokens(tok, c.strided, dev, (qg, kg))
         lam = tok.lam.to(dev)
         beta = tok.beta.to(dev) if tok.beta is not None else None
         out_r = torch.full((c.B, c.H, c.dv), float("nan"), device=dev)
@@ -191,8 +208,8 @@ def run_case(c: Case, dev="cuda") -> dict:
             rows = [sample[i] for i in nonflush]
             bsel = blk[nonflush]
             slots = torch.as_tensor(wp[rows].astype(np.int64), device=dev)
-            got_k = rep.pool.rec_k()[bsel, :, slots].cpu()
-            assert torch.equal(got_k, tok.k[rows].to(rdt)), f"k record, step {s}"
+            got_k = rep.pool.rec_k()[bsel, :, slots].cpu()   # one key record per group
+            assert torch.equal(got_k, kg[rows].to(rdt)), f"k record, step {s}"
             got_l = rep.pool.rec_lam()[bsel, :, slots].cpu()
             assert torch.equal(got_l, tok.lam[rows]), f"lam record, step {s}"
             got_x = rep.pool.rec_x()[bsel, :, slots].cpu()

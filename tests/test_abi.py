@@ -259,3 +259,35 @@ def test_spec_meta_pad_rows_and_bad_arguments():
         rs.rs_spec_meta_step(16, 17, h)
     with pytest.raises(rs.ReplaySSMError):
         rs.rs_spec_meta_step(16, 0, h)
+
+
+# ------------------------------------------------------------ grouped keys --
+def test_grouped_block_layout():
+    """128 heads in 8 key groups: the key ring holds 8 x 15 records."""
+    lay = rs.block_layout(_c2(n_groups=8))
+    assert lay.rec_k_off == lay.rec_x_off + 128 * 15 * 64 * 2
+    assert lay.rec_lam_off == lay.rec_k_off + 8 * 15 * 128 * 2
+    per = rs.block_layout(_c2())
+    assert per.rec_lam_off - per.rec_k_off == 16 * (lay.rec_lam_off - lay.rec_k_off)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_groups=3), rs.RS_EINVAL), (dict(n_groups=-1), rs.RS_EINVAL),
+    (dict(n_groups=8, spec_T=4), rs.RS_EUNSUPPORTED),
+])
+def test_grouped_layer_validation(bad, code):
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.block_layout(_c2(**bad))
+    assert e.value.code == code
+
+
+def test_grouped_io_strides():
+    """q / k rows of a grouped layer hold n_groups vectors."""
+    layer = _c2(n_groups=8)
+    buf = (ctypes.c_uint8 * 512)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    batch = rs.RsBatch(4, 0, 4, base, base, base, None, None)
+    io = rs.RsStepIO(base, base, base, 8 * 128, 128, 7 * 128, 128, 128 * 64, 64, base, None, base)
+    with pytest.raises(rs.ReplaySSMError) as e:                    # k rows shorter than 8 groups
+        rs.replay_decode_step(layer, batch, io, stream=0)
+    assert "row strides" in rs.last_error()

@@ -50,3 +50,22 @@ def test_headline_ratio():
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("L", [1, 4, 16, 32])
+def test_grouped_window_bytes_match_model(L):
+    """Grouped keys (8 groups of 16 heads): the per-head share of a layer
+    record is the blog's 18,944-byte released record over 128 heads; q and k
+    inputs are read once per group."""
+    c = dict(bench.WORKLOADS["nemotron-grouped"])
+    H, G = c["H"], c["groups"]
+    args = (c["form"], H, c["dv"], c["dk"], c["B"], c["state"], c["rec"], c["io"])
+    io = (2 * c["dk"] / (H // G) + c["dv"]) * 2 + 4 + 4 * c["dv"]
+    ms = bm.state_bytes(c["dv"], c["dk"], 4)
+    rec = bm.grouped_record_bytes(H, c["dv"], c["dk"], G) / H
+    got = bench.window_bytes(*args, L, groups=G) - c["B"] * H * L * io - 9 * c["B"] * L
+    assert got == pytest.approx(c["B"] * H * bm.replay_window_bytes(L, ms, rec), rel=1e-12)
+    conv = bench.window_bytes(*args, L, "conventional", groups=G) - c["B"] * H * L * io - 4 * c["B"] * L
+    assert conv == pytest.approx(c["B"] * H * bm.conventional_window_bytes(L, ms), rel=1e-12)
+    if L == 16:  # the blog's "about 0.55 of conventional traffic"
+        assert abs(got / conv - 0.5503) < 5e-4

@@ -143,3 +143,37 @@ def test_two_precision_checkpoint_nemotron(read_dt):
                         a_hi=a[1], seed=61))
     _check_two_precision(err, read_dt)
     assert err["flushes"] == 2
+
+
+# ------------------------------------------------------------ grouped keys --
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+def test_grouped_keys_tiny(form):
+    """Keys and queries shared by pairs of heads (the released grouped-key
+    layout): one key record per group, values and decays per head; fp32."""
+    err = _go(Case(form=form, H=4, groups=2, seed=70))
+    assert err["flushes"] == 16
+
+
+def test_grouped_keys_strided_pad_forced_lowprec():
+    _go(Case(B=5, H=6, groups=3, pad_rows=[1], n_blocks=9, strided=True, force_every=5, state_dt="f32",
+             rec_dt="f16", io_dt="bf16", seed=71))
+
+
+def test_grouped_keys_two_precision():
+    err = run_case(Case(H=4, groups=2, read_dt="f16", seed=72))
+    assert err["out_replay"] <= TOL_LOW and err["ckpt_flush"] <= TOL_F32
+
+
+def test_grouped_keys_nemotron_layer():
+    """The Nemotron-3-Super Mamba-2 layer as released: 128 heads in 8 key
+    groups, 64x128, fp32 state, batch 256, L = 16, bf16 inputs, fp16 records;
+    40 steps, 4 rows sampled."""
+    err = _go(Case(B=256, H=128, groups=8, dv=64, dk=128, L=16, steps=40, state_dt="f32", rec_dt="f16",
+                   io_dt="bf16", sample=[0, 99, 160, 255], n_blocks=260, seed=73))
+    assert err["flushes"] == 2
+
+
+def test_grouped_keys_gdn_production():
+    """Gated DeltaNet 128x128 with 2 value heads per key head."""
+    _go(Case(form=rs.GDN, B=16, H=32, groups=16, dv=128, dk=128, L=16, steps=20, rec_dt="f16", io_dt="bf16",
+             sample=[0, 15], seed=74))
