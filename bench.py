@@ -522,6 +522,97 @@ def suite_spec(out, steps=48, n_pools=4):
         torch.cuda.empty_cache()
 
 
+def suite_continuous(out, steps=200, n_layers=4):
+    """Continuous batching at the Nemotron-3-Super layer shape: 256 request
+    slots over a shuffled pool of 384 blocks, rows starting mid-window (cursor
+    U{0..15}), each live row retiring with p = 1/32 per step and each empty
+    slot taking a new row with p = 1/2 (a joining row's checkpoint is zeroed
+    by replay_state_reset, inside the timed region).  n_layers independent
+    layer pools share the schedule, as the layers of one model do, so that no
+    launch finds its state in the caches.  Reports the per-launch time
+    distribution (events around each launch) and the average over the whole
+    run (one event pair), for the checkpoint + buffer step and for the
+    conventional step on the same schedule."""
+    import torch
+    import linear_attention_decode_replay_amd as rs
+    import workloads
+    from linear_attention_decode_replay_amd.state import DecodeLayer
+    dev = torch.device("cuda", 0)
+    cfg = dict(WORKLOADS["nemotron"])
+    B, H, dv, dk, L, NB = cfg["B"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], 384
+    lay = rs.layer(0, H, dv, dk, L, cfg["state"], cfg["rec"], cfg["io"])
+    ios, keep = _inputs(cfg, B, 16, dev)
+    blocks0, w0s, events = workloads.continuous_schedule(17, B, steps, NB)
+    ms_state = dv * dk * _ES[cfg["state"]]
+    rec = (dv + dk) * _ES[cfg["rec"]] + 4
+    io_b = (2 * dk + dv) * _ES[cfg["io"]] + 4 + 4 * dv
+    for kind in ("replay", "conventional"):
+        layers = []
+        for _ in range(n_layers):
+            d = DecodeLayer(lay, B, NB, dev)
+            for slot in range(B):
+                d.assign(slot, int(blocks0[slot]))
+            d.reset_rows(range(B))
+            for slot in range(B):  # mid-window starts (the records' values do not matter for timing)
+                d.assign(slot, int(blocks0[slot]), int(w0s[slot]))
+            layers.append(d)
+        torch.cuda.synchronize()
+        per_launch, flush_frac, live_rows, nbytes = [], [], [], 0.0
+        ev = []
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(steps):
+            e = events[s]
+            for d in layers:
+                for slot in e.retire:
+                    d.retire(slot)
+                for slot, b in e.join:
+                    d.assign(slot, int(b))
+                if e.join:
+                    d.reset_rows([slot for slot, _ in e.join])
+            for li, d in enumerate(layers):
+                pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                io = ios[(s + li) % 16]
+                if kind == "replay":
+                    wp, fl = d.step(io, events=pair)
+                    live = d.live()
+                    if li == 0:
+                        flush_frac.append(float(np.mean(fl[live])) if live.any() else 0.0)
+                        live_rows.append(int(live.sum()))
+                    f = fl[live].astype(bool)
+                    w = wp[live]
+                    nbytes += float(np.sum(H * (ms_state + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
+                    nbytes += 4.0 * int((~live).sum())
+                else:
+                    d.conventional_step(io, events=pair)
+                    live = d.live()
+                    nbytes += float(live.sum()) * (H * (2 * ms_state + io_b) + 4) + 4.0 * int((~live).sum())
+                ev.append(pair)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        torch.cuda.synchronize()
+        per_launch = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        total_us = e0.elapsed_time(e1) * 1e3
+        errs = sum(int(d.err.item()) for d in layers)
+        if errs:
+            raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
+        n = steps * n_layers
+        line = {"suite": "continuous_batching", "kind": kind, "slots": B, "pool_blocks": NB, "steps": steps,
+                "layers": n_layers, "us_per_launch_region": round(total_us / n, 2),
+                "us_per_launch_mean": round(float(per_launch.mean()), 2),
+                "us_per_launch_p50": round(float(np.percentile(per_launch, 50)), 2),
+                "us_per_launch_p90": round(float(np.percentile(per_launch, 90)), 2),
+                "us_per_launch_max": round(float(per_launch.max()), 2),
+                "gb_per_launch": round(nbytes / n / 1e9, 4),
+                "tbs_region": round(nbytes / (total_us * 1e-6) / 1e12, 3)}
+        if kind == "replay":
+            line["flushing_rows_mean"] = round(float(np.mean(flush_frac)), 4)
+            line["live_rows_mean"] = round(float(np.mean(live_rows)), 1)
+        print(json.dumps(line), file=out, flush=True)
+        del layers
+        torch.cuda.empty_cache()
+
+
 def calibrate_copy(mib: int) -> None:
     """A plain device-to-device copy of `mib` MiB, three times: its
     FETCH_SIZE / WRITE_SIZE readings give the scale of those counters."""
@@ -615,7 +706,7 @@ def main(argv=None):
     ap.add_argument("--suite", metavar="PATH",
                     help="instead of the one-line benchmark, run the Gated DeltaNet batch sweep and the "
                          "40-layer stack and write JSON lines to PATH")
-    ap.add_argument("--suite-only", choices=["gdn", "stack", "spec"], default=None,
+    ap.add_argument("--suite-only", choices=["gdn", "stack", "spec", "continuous"], default=None,
                     help="with --suite: run one part of it")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
@@ -634,6 +725,8 @@ def main(argv=None):
                 suite_stack(out)
             if args.suite_only in (None, "spec"):
                 suite_spec(out)
+            if args.suite_only in (None, "continuous"):
+                suite_continuous(out)
         print(open(args.suite).read(), end="")
         return 0
 
