@@ -28,7 +28,7 @@ import subprocess
 
 import numpy as np
 
-from .formats import half_ulp, round_to  # noqa: F401  (read-copy roundings)
+from .formats import half_ulp, round_to, sr_f16, sr_words  # noqa: F401  (storage roundings)
 
 MAMBA2 = 0
 GDN = 1
@@ -319,6 +319,58 @@ class TwoCopyReplayModel(ReplayModel):
         g = np.exp((self.rec_lam * held).sum(axis=1) + _scal(lam, n))
         u = half_ulp(self.C, self.read_dtype)
         return (g[:, None] * np.einsum("nic,nc->ni", u, np.abs(q))).reshape(B, H, self.dv)
+
+
+def sr_round_tiles(X, key, step, tiles):
+    """Stochastic rounding to fp16 of the given tiles of X [n, d_v, d_k] in
+    place, tile t (its index = row * n_heads + head) with the random words of
+    (step, t)."""
+    n, dv, dk = X.shape
+    for t in tiles:
+        X[t] = sr_f16(X[t].reshape(-1), sr_words(key, step, t, dv * dk)).reshape(dv, dk)
+
+
+class SRReplayModel(ReplayModel):
+    """Checkpoint + buffer whose checkpoint is stored in fp16 with stochastic
+    rounding at every flush (blog "The precision argument, derived": the
+    recurrence copy kept in FP16 with stochastic rounding, so rounding enters
+    the recurrence once per window).  Records are kept exactly; `tile_ids`
+    maps this model's tiles to the (row * n_heads + head) indices the random
+    words are drawn for."""
+
+    def __init__(self, form, B, H, dv, dk, L, key, tile_ids=None, oracle=None):
+        super().__init__(form, B, H, dv, dk, L, oracle)
+        self.key = np.asarray(key, np.uint64)
+        self.tile_ids = np.arange(B * H) if tile_ids is None else np.asarray(tile_ids)
+
+    def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None, sr_step=0):
+        out = super().step(q, k, v, lam, flush_rows, beta, active_rows)
+        fl = np.repeat(np.asarray(flush_rows, bool), self.H)
+        if active_rows is not None:
+            fl &= np.repeat(np.asarray(active_rows, bool), self.H)
+        for t in np.nonzero(fl)[0]:
+            self.C[t] = sr_f16(self.C[t].reshape(-1), sr_words(self.key, sr_step, self.tile_ids[t],
+                                                               self.dv * self.dk)).reshape(self.dv, self.dk)
+        return out
+
+
+class SRConventionalModel(ConventionalModel):
+    """Conventional decode with the state stored in fp16 with stochastic
+    rounding after every step (the per-step rounding the blog's argument
+    starts from)."""
+
+    def __init__(self, form, B, H, dv, dk, key, tile_ids=None, S0=None, oracle=None):
+        super().__init__(form, B, H, dv, dk, S0, oracle)
+        self.key = np.asarray(key, np.uint64)
+        self.tile_ids = np.arange(B * H) if tile_ids is None else np.asarray(tile_ids)
+
+    def step(self, q, k, v, lam, beta=None, active_rows=None, want_x=False, sr_step=0):
+        res = super().step(q, k, v, lam, beta, active_rows, want_x)
+        act = np.ones(self.B * self.H, bool) if active_rows is None else np.repeat(np.asarray(active_rows, bool), self.H)
+        for t in np.nonzero(act)[0]:
+            self.S[t] = sr_f16(self.S[t].reshape(-1), sr_words(self.key, sr_step, self.tile_ids[t],
+                                                               self.dv * self.dk)).reshape(self.dv, self.dk)
+        return res
 
 
 class SpecReplayModel:

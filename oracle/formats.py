@@ -117,3 +117,97 @@ def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
     mant, emin = {"f16": (10, -14), "bf16": (7, -126), "f32": (23, -126)}[dtype]
     _, ex = np.frexp(np.maximum(np.abs(x), 2.0**emin))
     return np.ldexp(np.ones_like(x), ((ex - 1) - mant - 1).astype(np.int32))
+
+
+# ---------------------------------------------------- stochastic rounding --
+# Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+# as 1, 2, 3", SC 2011): a counter-based generator, the published constants
+# and round function.  Used for stochastic rounding of a 16-bit state (blog
+# "The precision argument, derived": the recurrence copy kept in FP16 with
+# stochastic rounding); the GPU path implements the same definition.
+_PH_M0, _PH_M1 = np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157)
+_PH_W0, _PH_W1 = np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B)
+_M32 = np.uint64(0xFFFFFFFF)
+
+
+def _mulhilo64(a, b):
+    """Full 64 x 64 -> 128-bit product of uint64 arrays: (hi, lo)."""
+    a = np.asarray(a, np.uint64)
+    b = np.asarray(b, np.uint64)
+    s32 = np.uint64(32)
+    a_lo, a_hi = a & _M32, a >> s32
+    b_lo, b_hi = b & _M32, b >> s32
+    ll = a_lo * b_lo
+    lh = a_lo * b_hi
+    hl = a_hi * b_lo
+    hh = a_hi * b_hi
+    mid = (ll >> s32) + (lh & _M32) + (hl & _M32)
+    lo = (ll & _M32) | ((mid & _M32) << s32)
+    hi = hh + (lh >> s32) + (hl >> s32) + (mid >> s32)
+    return hi, lo
+
+
+def philox4x64(counter, key):
+    """Philox4x64-10 of counters [..., 4] uint64 under keys [..., 2] uint64
+    (broadcast); returns [..., 4] uint64."""
+    c = np.array(np.broadcast_to(np.asarray(counter, np.uint64), np.broadcast_shapes(
+        np.shape(counter), np.shape(key)[:-1] + (4,))), dtype=np.uint64)
+    k = np.array(np.broadcast_to(np.asarray(key, np.uint64), c.shape[:-1] + (2,)), dtype=np.uint64)
+    c0, c1, c2, c3 = (c[..., i].copy() for i in range(4))
+    k0, k1 = k[..., 0].copy(), k[..., 1].copy()
+    with np.errstate(over="ignore"):
+        for rnd in range(10):
+            if rnd:
+                k0 = k0 + _PH_W0
+                k1 = k1 + _PH_W1
+            hi0, lo0 = _mulhilo64(_PH_M0, c0)
+            hi1, lo1 = _mulhilo64(_PH_M1, c2)
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return np.stack([c0, c1, c2, c3], axis=-1)
+
+
+F16_MAX = 65504.0
+
+
+def sr_f16(x, r) -> np.ndarray:
+    """Stochastic rounding of real values x to fp16 with 32-bit random words r
+    (same shape): |x| lies between two neighbouring fp16 values lo <= |x| < hi;
+    the result is hi (with x's sign) when r < p 2^32, p = (|x| - lo) / (hi - lo),
+    else lo, so it rounds up with probability p and E[result] = x.  Values that
+    are fp16 already are unchanged; |x| >= 65504 and non-finite values round
+    to nearest even (no stochastic choice at the top of the range)."""
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    a = np.abs(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = a.astype(np.float16)
+    lo = h.astype(np.float64)
+    hb = h.view(np.uint16)
+    down = lo > a
+    lo_b = np.where(down, hb - 1, hb).astype(np.uint16)
+    lo = lo_b.view(np.float16).astype(np.float64)
+    hi = (lo_b + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = (a - lo) / (hi - lo)
+    up = r < np.ldexp(p, 32)
+    mag = np.where(up, hi, lo)
+    rne = x.astype(np.float16).astype(np.float64)
+    out = np.where(np.isfinite(x) & (a < F16_MAX), np.copysign(mag, x), rne)
+    return out
+
+
+def sr_words(key, step, tile, n_elems):
+    """The 32-bit random word for each of n_elems consecutive state elements
+    (row-major d_v x d_k) of one tile at one step: element e uses word e % 8 of
+    Philox4x64-10 block (step, tile, e // 8, 0), the low half of 64-bit output
+    (e % 8) // 2 first.  key: two uint64."""
+    n_blk = (n_elems + 7) // 8
+    ctr = np.zeros((n_blk, 4), np.uint64)
+    ctr[:, 0] = np.uint64(step)
+    ctr[:, 1] = np.uint64(tile)
+    ctr[:, 2] = np.arange(n_blk, dtype=np.uint64)
+    out = philox4x64(ctr, np.asarray(key, np.uint64))       # [n_blk, 4] uint64
+    lo = (out & _M32).astype(np.uint64)
+    hi = (out >> np.uint64(32)).astype(np.uint64)
+    words = np.stack([lo, hi], axis=-1).reshape(n_blk, 8)  # lo0 hi0 lo1 hi1 ...
+    return words.reshape(-1)[:n_elems]

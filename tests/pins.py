@@ -18,6 +18,9 @@ Sources of the facts (pages):
   [ofp8] Open Compute Project "OCP 8-bit Floating Point Specification
          (OFP8)": the E4M3 encoding (bias 7, no infinities, max 448,
          subnormals m/8 * 2^-6); the format is not on the pages.
+  [philox] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+         1, 2, 3" (SC 2011): the Philox4x64-10 generator (not on the pages;
+         it supplies the random bits of stochastic rounding).
   [nv]   NVIDIA technical blog "ReplaySSM: Rethinking state storage for
          faster hybrid model decoding", section "Benefit 2: Simplify rollback
          and speed up verification" (speculative verify); with [blog]
@@ -567,6 +570,88 @@ def pin_spec_cursor(orc):
     assert list(h) == [0, 2, 4, 2, 4, 6] and list(np.nonzero(f)[0]) == [2]
 
 
+# ------------------------------------------------------ stochastic rounding --
+def pin_philox_matches_library(orc):
+    """[philox] The oracle's Philox4x64-10 equals numpy's Philox bit
+    generator (an independent implementation of the same definition; numpy
+    increments its counter before each block)."""
+    from oracle import formats
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        ctr = rng.integers(0, 2**62, 4, dtype=np.uint64)
+        key = rng.integers(0, 2**63, 2, dtype=np.uint64)
+        ref = np.random.Philox(counter=ctr, key=key).random_raw(4)
+        nxt = ctr.copy()
+        nxt[0] += np.uint64(1)
+        assert np.array_equal(formats.philox4x64(nxt, key), ref)
+
+
+def pin_sr_rule(orc):
+    """Stochastic rounding to fp16: the result is one of the two fp16
+    neighbours, up with probability exactly p = (|x| - lo) / ulp (a uniform
+    grid of 2^16 random words rounds up exactly p 2^16 times), fp16 values
+    are unchanged, the sign is kept, and E[SR(x)] = x."""
+    from oracle import formats
+    grid = np.arange(65536, dtype=np.float64) * 65536.0
+    for lo, ulp in ((1.0, 2.0**-10), (503 * 2.0**-24, 2.0**-24), (-1000.0, 0.5), (2.0**-20, 2.0**-24)):
+        for k8 in range(8):
+            p = k8 / 8.0
+            x = np.sign(lo) * (abs(lo) + p * ulp)
+            got = formats.sr_f16(np.full(65536, x), grid)
+            a, b = np.sign(x) * abs(lo), np.sign(x) * (abs(lo) + ulp)
+            assert np.all((got == a) | (got == b)), (lo, k8)
+            assert int(np.sum(got == b)) == int(p * 65536), (lo, k8, int(np.sum(got == b)))
+    # the convention both sides implement: round up exactly when r < p 2^32
+    half = 1.0 + 2.0**-11
+    assert formats.sr_f16(np.array([half, half, half]), np.array([0.0, 2.0**31 - 1, 2.0**31])).tolist() == \
+        [1.0 + 2.0**-10, 1.0 + 2.0**-10, 1.0]
+    vals = np.float16(np.linspace(-3, 3, 97)).astype(np.float64)
+    assert np.array_equal(formats.sr_f16(vals, np.full(97, 2.0**32 - 1)), vals)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(200000).astype(np.float32).astype(np.float64)
+    r = rng.integers(0, 2**32, 200000).astype(np.float64)
+    err = formats.sr_f16(x, r) - x
+    e = np.frexp(np.abs(x))[1] - 1                  # |x| in [2^e, 2^(e+1))
+    ulp = np.ldexp(1.0, np.maximum(e, -14) - 10)      # fp16 spacing there
+    assert abs(np.mean(err / ulp)) < 0.01           # unbiased
+    assert np.all(np.abs(err) <= ulp * 1.0000001)
+
+
+def pin_sr_once_per_window(orc):
+    """[blog] "The precision argument, derived": with independent rounding
+    errors of variance s^2 and constant decay alpha, the deviation of a state
+    rounded every step settles at variance s^2 / (1 - alpha^2); rounded once
+    per window of L steps (a checkpoint), at s^2 / (1 - alpha^(2L)).  Scalar
+    toy: 4096 independent chains around 1.5 (one fp16 binade), alpha = 0.9,
+    L = 16, stochastic rounding with Philox words; the measured variance ratio
+    matches the closed form within 10 %, and both deviations have mean ~ 0."""
+    from oracle import formats
+    alpha, L, n_chain, n_step = 0.9, 16, 4096, 160
+    rng = np.random.default_rng(8)
+    key = np.array([7, 11], np.uint64)
+    exact = np.full(n_chain, 1.5)
+    per_step = exact.copy()
+    per_window = exact.copy()
+    devs_s, devs_w = [], []
+    for t in range(n_step):
+        u = 0.15 + 0.01 * rng.standard_normal(n_chain)
+        exact = alpha * exact + u
+        w = formats.sr_words(key, t, 0, 2 * n_chain).astype(np.float64)
+        per_step = formats.sr_f16(alpha * per_step + u, w[:n_chain])
+        per_window = alpha * per_window + u
+        if t % L == L - 1:
+            per_window = formats.sr_f16(per_window, w[n_chain:])
+            if t >= 4 * L:
+                devs_w.append(per_window - exact)
+        if t >= 4 * L:
+            devs_s.append(per_step - exact)
+    var_s, var_w = np.var(np.concatenate(devs_s)), np.var(np.concatenate(devs_w))
+    want = (1 - alpha ** (2 * L)) / (1 - alpha ** 2)
+    assert abs(var_s / var_w / want - 1) < 0.10, (var_s / var_w, want)
+    ulp = 2.0 ** -10
+    assert abs(np.mean(np.concatenate(devs_s))) < 0.02 * ulp * np.sqrt(1 / (1 - alpha**2)) * 10
+
+
 ALL_PINS = [
     pin_identity_mamba2_tiny,
     pin_identity_mamba2_long_memory,
@@ -593,4 +678,7 @@ ALL_PINS = [
     pin_spec_rejected_drafts_never_read,
     pin_spec_T1_is_standard_decode,
     pin_spec_cursor,
+    pin_philox_matches_library,
+    pin_sr_rule,
+    pin_sr_once_per_window,
 ]

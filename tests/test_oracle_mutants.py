@@ -218,3 +218,55 @@ def test_two_copy_bound_without_decay_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "TwoCopyReplayModel", Broken)
     with pytest.raises(AssertionError):
         pins.pin_two_copy_read_error_is_one_rounding(oracle.get())
+
+
+# ------------------------------------------ stochastic-rounding mutants --
+def _sr_mutants():
+    import numpy as np
+    from oracle import formats as F
+    sr, ph = F.sr_f16, F.philox4x64
+
+    def nearest(x, r):                      # no stochastic choice at all
+        return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+    def flipped(x, r):                      # rounds up with probability 1 - p
+        return sr(x, 2.0**32 - 1 - np.asarray(r, np.float64))
+
+    def truncate(x, r):                     # always the neighbour towards zero
+        return sr(x, np.full(np.shape(x), 2.0**32))
+
+    def no_key_bump(counter, key):          # key not advanced between rounds
+        import numpy as np
+        c = np.array(np.broadcast_to(np.asarray(counter, np.uint64), np.shape(counter)), np.uint64)
+        k = np.asarray(key, np.uint64)
+        c0, c1, c2, c3 = (c[..., i].copy() for i in range(4))
+        with np.errstate(over="ignore"):
+            for _ in range(10):
+                hi0, lo0 = F._mulhilo64(F._PH_M0, c0)
+                hi1, lo1 = F._mulhilo64(F._PH_M1, c2)
+                c0, c1, c2, c3 = hi1 ^ c1 ^ k[..., 0], lo1, hi0 ^ c3 ^ k[..., 1], lo0
+        return np.stack([c0, c1, c2, c3], axis=-1)
+
+    def nine_rounds(counter, key):
+        import numpy as np
+        out = ph(counter, key)
+        return out ^ np.uint64(1)           # any corruption of the output words
+
+    return {"sr_nearest": ("sr_f16", nearest), "sr_flipped": ("sr_f16", flipped),
+            "sr_truncate": ("sr_f16", truncate), "philox_no_key_bump": ("philox4x64", no_key_bump),
+            "philox_corrupt": ("philox4x64", nine_rounds)}
+
+
+@pytest.mark.parametrize("kind", sorted(_sr_mutants()))
+def test_sr_mutant_is_caught(monkeypatch, kind):
+    import pins
+    from oracle import formats
+    name, fn = _sr_mutants()[kind]
+    monkeypatch.setattr(formats, name, fn)
+    caught = []
+    for pin in (pins.pin_philox_matches_library, pins.pin_sr_rule, pins.pin_sr_once_per_window):
+        try:
+            pin(oracle.get())
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"stochastic-rounding mutant {kind} passed every pin"
