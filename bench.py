@@ -106,6 +106,8 @@ def workload_key(name, cfg) -> str:
     key = f"{name}-B{cfg['B']}-L{cfg['L']}-{cfg['state']}"
     if cfg.get("groups"):
         key += f"-g{cfg['groups']}"
+    if cfg.get("sr"):
+        key += "-sr"
     return key + (f"-read{cfg['read']}" if cfg.get("read") else "")
 
 
@@ -197,11 +199,11 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     read = cfg["read"] if kind == "replay" else None
     groups = cfg.get("groups", 0)
     lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"], read,
-                   0, groups)
+                   0, groups, stochastic=bool(cfg.get("sr")))
     B = cfg["B"]
     layers = []
     for p in range(n_pools):
-        d = DecodeLayer(lay, B, B, dev)
+        d = DecodeLayer(lay, B, B, dev, sr_key=(0x5EED0000 + p, 0x243F6A8885A308D3))
         for b in range(B):
             d.assign(b, b)
         d.reset_rows(range(B))
@@ -639,6 +641,20 @@ def _read_counter_csv(path):
     return rows
 
 
+def config_from_args(args):
+    """The workload's configuration with the command line's overrides."""
+    cfg = dict(WORKLOADS[args.workload])
+    if args.batch:
+        cfg["B"] = args.batch
+    if args.L:
+        cfg["L"] = args.L
+    if args.state:
+        cfg["state"] = args.state
+    cfg["read"] = args.read
+    cfg["sr"] = args.rounding == "stochastic"
+    return cfg
+
+
 def summarize_counters(args, fetch_csv, write_csv):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
     (known bytes of the calibration copy) / (its reading), then averaged per
@@ -661,14 +677,7 @@ def summarize_counters(args, fetch_csv, write_csv):
         res[label] = {"scale": scale,
                       "replay": float(np.mean([v for n, vs in per.items() if "k_replay_step" in n for v in vs])) * 1024 * scale,
                       "conventional": float(np.mean([v for n, vs in per.items() if "k_conventional_step" in n for v in vs])) * 1024 * scale}
-    cfg = dict(WORKLOADS[args.workload])
-    if args.batch:
-        cfg["B"] = args.batch
-    if args.L:
-        cfg["L"] = args.L
-    if args.state:
-        cfg["state"] = args.state
-    cfg["read"] = args.read
+    cfg = config_from_args(args)
     key = workload_key(args.workload, cfg)
     entry = {"kernel_source": kernel_source_hash(),
              "bytes_per_launch": round(res["fetch"]["replay"] + res["write"]["replay"]),
@@ -698,6 +707,8 @@ def main(argv=None):
     ap.add_argument("--state", default=None, choices=["f32", "f16"])
     ap.add_argument("--read", default=None, choices=["f16", "bf16", "e4m3"],
                     help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy")
+    ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
+                    help="state stores: nearest even, or stochastic rounding (fp16 state)")
     ap.add_argument("--pools", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
@@ -735,14 +746,7 @@ def main(argv=None):
               f"GPU runs its own rows or heads independently (--gpus {args.gpus} is not supported).",
               file=sys.stderr)
         return 2
-    cfg = dict(WORKLOADS[args.workload])
-    if args.batch:
-        cfg["B"] = args.batch
-    if args.L:
-        cfg["L"] = args.L
-    if args.state:
-        cfg["state"] = args.state
-    cfg["read"] = args.read
+    cfg = config_from_args(args)
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
@@ -756,6 +760,7 @@ def main(argv=None):
                         "conventional", groups=groups)
     form_name = "mamba2" if cfg["form"] == 0 else "gdn"
     state_desc = f"{cfg['state']} state" + (f" + {cfg['read']} read copy" if cfg["read"] else "")
+    state_desc += " (stochastic rounding)" if cfg["sr"] else ""
     keys = f", keys shared by {groups} groups" if groups else ""
     workload = (f"{form_name} layer, {cfg['H']} heads{keys}, d_v={cfg['dv']}, d_k={cfg['dk']}, {state_desc}, "
                 f"{cfg['rec']} records, {cfg['io']} q/k/v, batch {cfg['B']}, L={cfg['L']}")
@@ -777,7 +782,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": workload, "global_batch": cfg["B"], "seq_len": None, "heads": cfg["H"],
                    "d_v": cfg["dv"], "d_k": cfg["dk"], "L": cfg["L"], "state_dtype": cfg["state"],
-                   "read_copy_dtype": cfg["read"],
+                   "read_copy_dtype": cfg["read"], "state_rounding": args.rounding,
                    "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": args.pools,
                    "key_groups": groups or cfg["H"],
                    "parallelism": "none (1 GPU)"},

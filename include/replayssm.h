@@ -92,6 +92,28 @@ typedef enum {
  *               kernel: values and decays per value head, keys per group):
  *               q and k inputs are [n_rows][G][d_k] and the ring keeps one
  *               key record per group.  Standard decoding only (spec_T = 0).
+ * state_rounding: RS_ROUND_NEAREST (nearest even) for every store.
+ *               RS_ROUND_STOCHASTIC, with state_dtype RS_F16 and a single
+ *               checkpoint only: every store of the 16-bit checkpoint or
+ *               state (a flush, a token-less flush, a conventional step,
+ *               the flush of a speculative verify)
+ *               rounds each value x up to the next fp16 neighbour exactly
+ *               when the value's 16-bit random word r is below p 2^16,
+ *               p = (|x| - lo) / (hi - lo) for the fp16 neighbours
+ *               lo <= |x| < hi (so E[stored] = x for every fp32 value from
+ *               2^-17 up, where p is a multiple of 2^-13 or finer; fp16
+ *               values, |x| >= 65504 and non-finite values round to nearest
+ *               even).  Words come from Philox4x64-10 (Salmon et al.,
+ *               "Parallel random numbers: as easy as 1, 2, 3", SC 2011)
+ *               under key (batch->sr_key0, batch->sr_key1): element e
+ *               (row-major within its (row, head) tile t = row * n_heads +
+ *               head) uses 16-bit word e mod 16 (the 64-bit outputs split
+ *               least significant half-word first) of the block for counter
+ *               (batch->sr_step, t, e / 16, 0).  Launches that store must
+ *               not repeat an sr_step under one key.  The blog ("The
+ *               precision argument, derived") keeps the recurrence copy in
+ *               FP16 with stochastic rounding, so that rounding enters the
+ *               recurrence unbiased and once per window.
  * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16,
  *               RS_BF16 or RS_E4M3 for a two-precision checkpoint (blog "The
  *               precision argument, derived"): state_dtype RS_F32 is the
@@ -121,7 +143,11 @@ typedef struct {
                          see replay_spec_verify */
     int32_t n_groups; /* 0 (= n_heads): one key and query per head; else the
                          number of key groups, see below */
+    int32_t state_rounding; /* RS_ROUND_NEAREST or RS_ROUND_STOCHASTIC, see below */
 } rs_layer;
+
+/* Rounding of state stores (rs_layer.state_rounding). */
+typedef enum { RS_ROUND_NEAREST = 0, RS_ROUND_STOCHASTIC = 1 } rs_rounding;
 
 /*
  * Byte layout of one paged block = the whole per-request state of one layer
@@ -192,6 +218,9 @@ typedef struct {
     const uint8_t* flush;
     int32_t* err_count;
     int32_t* next_write_pos;
+    uint64_t sr_key0, sr_key1;  /* stochastic rounding: Philox key          */
+    uint64_t sr_step;           /* stochastic rounding: first counter word,
+                                   a new value for every launch that stores */
 } rs_batch;
 
 /*

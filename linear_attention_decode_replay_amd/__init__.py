@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplays
 MAMBA2, GDN = 0, 1
 F32, F16, BF16, E4M3 = 0, 1, 2, 3
 RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
+RS_ROUND_NEAREST, RS_ROUND_STOCHASTIC = 0, 1
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -36,7 +37,7 @@ class RsLayer(_c.Structure):
     _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
                 ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
                 ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32),
-                ("spec_T", _c.c_int32), ("n_groups", _c.c_int32)]
+                ("spec_T", _c.c_int32), ("n_groups", _c.c_int32), ("state_rounding", _c.c_int32)]
 
 
 class RsBlockLayout(_c.Structure):
@@ -48,7 +49,8 @@ class RsBlockLayout(_c.Structure):
 class RsBatch(_c.Structure):
     _fields_ = [("n_rows", _c.c_int32), ("reserved", _c.c_int32), ("n_blocks", _c.c_int64),
                 ("pool", _vp), ("block_table", _vp), ("write_pos", _vp), ("flush", _vp),
-                ("err_count", _vp), ("next_write_pos", _vp)]
+                ("err_count", _vp), ("next_write_pos", _vp), ("sr_key0", _c.c_uint64),
+                ("sr_key1", _c.c_uint64), ("sr_step", _c.c_uint64)]
 
 
 class RsStepIO(_c.Structure):
@@ -123,17 +125,20 @@ _DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
 
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
-          record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0, n_groups: int = 0) -> RsLayer:
+          record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0, n_groups: int = 0,
+          stochastic: bool = False) -> RsLayer:
     """read_dtype: None for a single checkpoint, "f16" / "bf16" / "e4m3" for
     a two-precision checkpoint (fp32 recurrence copy + read copy; E4M3 with a
     power-of-two scale per state row).  spec_T: 0 for standard decoding, T
     for a speculative layer verifying T drafts per step.  n_groups: 0 for a
     key and query per head, else the number of key groups (q, k inputs then
-    [rows, n_groups, d_k], one key record per group)."""
+    [rows, n_groups, d_k], one key record per group).  stochastic: store an
+    fp16 state with stochastic rounding (the key and counter travel in the
+    batch: sr_key0/sr_key1, sr_step)."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
                    code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype),
-                   int(spec_T), int(n_groups))
+                   int(spec_T), int(n_groups), RS_ROUND_STOCHASTIC if stochastic else RS_ROUND_NEAREST)
 
 
 def block_layout(lay: RsLayer) -> RsBlockLayout:
@@ -151,12 +156,14 @@ def _ptr(t) -> int | None:
 
 
 def make_batch(pool, n_blocks: int, block_table, write_pos=None, flush=None, err_count=None,
-               next_write_pos=None) -> RsBatch:
+               next_write_pos=None, sr_key=(0, 0), sr_step=0) -> RsBatch:
     """pool: uint8 device tensor; block_table/write_pos/next_write_pos: int32
-    [n_rows]; flush: uint8 [n_rows]; err_count: int32 [1].  The tensors must
+    [n_rows]; flush: uint8 [n_rows]; err_count: int32 [1]; sr_key: two
+    uint64, sr_step: uint64 (stochastic rounding only).  The tensors must
     outlive the launches that use the returned struct."""
     return RsBatch(int(block_table.numel()), 0, int(n_blocks), _ptr(pool), _ptr(block_table),
-                   _ptr(write_pos), _ptr(flush), _ptr(err_count), _ptr(next_write_pos))
+                   _ptr(write_pos), _ptr(flush), _ptr(err_count), _ptr(next_write_pos),
+                   int(sr_key[0]), int(sr_key[1]), int(sr_step))
 
 
 def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:

@@ -60,6 +60,10 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
             return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy only");
     }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
+    if (L->state_rounding != RS_ROUND_NEAREST && L->state_rounding != RS_ROUND_STOCHASTIC)
+        return fail(RS_EINVAL, "unknown state rounding %d", L->state_rounding);
+    if (L->state_rounding == RS_ROUND_STOCHASTIC && (L->state_dtype != RS_F16 || two_precision(*L)))
+        return fail(RS_EUNSUPPORTED, "stochastic rounding: a single fp16 checkpoint / state only");
     if (L->n_groups < 0 || (L->n_groups > 0 && L->n_heads % L->n_groups != 0))
         return fail(RS_EINVAL, "n_groups (%d) must be 0 or divide n_heads (%d)", L->n_groups, L->n_heads);
     if (L->spec_T != 0 && groups_of(*L) != L->n_heads)
@@ -195,6 +199,10 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.L = L.L;
     p.slots = lay.slots;
     p.heads_per_group = L.n_heads / groups_of(L);
+    p.sr = L.state_rounding == RS_ROUND_STOCHASTIC;
+    p.sr_key0 = b.sr_key0;
+    p.sr_key1 = b.sr_key1;
+    p.sr_step = b.sr_step;
     return p;
 }
 

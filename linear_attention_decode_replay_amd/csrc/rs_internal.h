@@ -33,6 +33,8 @@ struct StepParams {
     float* out;
     int32_t n_rows, n_heads, L, slots;
     int32_t heads_per_group;   // heads sharing one key / query (1: per-head keys)
+    int32_t sr;                // stochastic rounding of 16-bit state stores
+    uint64_t sr_key0, sr_key1, sr_step;
     // speculative verify / commit
     int32_t spec_T;
     int64_t qs_t, ks_t, vs_t;  // token strides (elements)

@@ -209,6 +209,102 @@ __device__ __forceinline__ void store_read_row(const float* x, typename TL::S* d
     }
 }
 
+
+// ------------------------------------------------------ stochastic rounding --
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): the published multipliers, Weyl key increments and
+// round function; the key is advanced between rounds.
+constexpr uint64_t kPhM0 = 0xD2E7470EE14C6C93ull, kPhM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhW0 = 0x9E3779B97F4A7C15ull, kPhW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        if (rnd) {
+            k0 += kPhW0;
+            k1 += kPhW1;
+        }
+        const uint64_t lo0 = kPhM0 * c[0], hi0 = __umul64hi(kPhM0, c[0]);
+        const uint64_t lo1 = kPhM1 * c[2], hi1 = __umul64hi(kPhM1, c[2]);
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
+
+// fp32 -> fp16 bits with stochastic rounding by a 16-bit random word r:
+// between the fp16 neighbours lo <= |x| < hi, take hi exactly when
+// r < p 2^16, p = (|x| - lo) / (hi - lo).  For 2^-14 <= |x| < 65504 the
+// fp32 value carries 13 bits m below the fp16 mantissa, p = m / 2^13, and
+// r < 8 m is (r >> 3) < m: truncate, then add the carry (which may step into
+// the next binade).  Below 2^-14 the neighbours are multiples of 2^-24:
+// t = |x| 2^24 (exact), lo = floor(t), p = t - lo, and p 2^16 is exact.
+// |x| >= 65504 and non-finite values round to nearest even.
+__device__ __forceinline__ uint16_t sr_f16_bits(float x, uint32_t r) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t sign = (u >> 16) & 0x8000u;
+    if (a >= 0x38800000u && a < 0x477FE000u) {  // 2^-14 <= |x| < 65504
+        const uint32_t up = (r >> 3) < (a & 0x1FFFu) ? 1u : 0u;
+        return (uint16_t)((((a >> 13) - 0x1C000u) + up) | sign);
+    }
+    if (a >= 0x477FE000u) return __builtin_bit_cast(uint16_t, (_Float16)x);
+    const float t = __uint_as_float(a) * 16777216.0f;
+    const float lo = floorf(t);
+    const uint32_t up = (float)r < __builtin_amdgcn_ldexpf(t - lo, 16) ? 1u : 0u;
+    return (uint16_t)(((uint32_t)lo + up) | sign);
+}
+
+// Exchange with the adjacent lane (lane ^ 1), a DPP quad permutation.
+__device__ __forceinline__ uint64_t xswap64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, 0xB1, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), 0xB1, 0xF, 0xF,
+                                               false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Random words for a lane's 8-element chunks (columns 8 cc .. 8 cc + 7) of
+// state rows row_first + r row_step, r < NR.  Element e of a (row, head)
+// tile (row-major) uses 16-bit word e mod 16 of the Philox4x64-10 block for
+// counter (sr_step, tile, e / 16, 0), the 64-bit outputs split least
+// significant half-word first; a chunk is half a block, so w[r] = the two
+// 64-bit outputs of its half.  Adjacent lanes cc = 2j, 2j + 1 hold the two
+// halves of the same blocks: with NR even each lane of the pair generates
+// the block of one of two rows and hands the other half to its partner.
+// Every lane of the wave must execute this.
+template <int NR>
+__device__ __forceinline__ void sr_lane_words(const StepParams& p, int64_t tile, int row_first, int row_step,
+                                              int dk, int cc, uint64_t (&w)[NR][2]) {
+    const bool odd = cc & 1;
+    const int64_t cblk = cc >> 1;
+    const int64_t bpr = dk / 16;  // blocks per state row
+    if constexpr (NR % 2 == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; r += 2) {
+            const int row = row_first + (r + (odd ? 1 : 0)) * row_step;
+            uint64_t c[4] = {p.sr_step, (uint64_t)tile, (uint64_t)(row * bpr + cblk), 0};
+            philox4x64_10(c, p.sr_key0, p.sr_key1);
+            const uint64_t k0 = odd ? c[2] : c[0], k1 = odd ? c[3] : c[1];
+            const uint64_t g0 = xswap64(odd ? c[0] : c[2]), g1 = xswap64(odd ? c[1] : c[3]);
+            w[r][0] = odd ? g0 : k0;
+            w[r][1] = odd ? g1 : k1;
+            w[r + 1][0] = odd ? k0 : g0;
+            w[r + 1][1] = odd ? k1 : g1;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int row = row_first + r * row_step;
+            uint64_t c[4] = {p.sr_step, (uint64_t)tile, (uint64_t)(row * bpr + cblk), 0};
+            philox4x64_10(c, p.sr_key0, p.sr_key1);
+            w[r][0] = odd ? c[2] : c[0];
+            w[r][1] = odd ? c[3] : c[1];
+        }
+    }
+}
+
 // ------------------------------------------------------- lane-group sums --
 // Partner exchange for the butterfly sums below, inside aligned groups of
 // 2 * OFF lanes.  The sums only need, at level OFF, a pairing of each lane
@@ -375,6 +471,29 @@ __device__ __forceinline__ u32x4 ld_stream(const void* p) {
 }
 __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Stores a lane's 8-element chunks of an fp16 state in rows
+// row_first + r row_step (dst: the chunk in the first of them, rows
+// row_step d_k elements apart) with stochastic rounding.
+template <int NR>
+__device__ __forceinline__ void sr_store_rows(const float (&cf)[NR][8], _Float16* dst, const StepParams& p,
+                                              int64_t tile, int row_first, int row_step, int dk, int cc) {
+    uint64_t w[NR][2];
+    sr_lane_words<NR>(p, tile, row_first, row_step, dk, cc, w);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t wi = w[r][i >> 1];
+            const int sh = 32 * (i & 1);
+            const uint32_t b0 = sr_f16_bits(cf[r][2 * i], (uint32_t)(wi >> sh) & 0xFFFFu);
+            const uint32_t b1 = sr_f16_bits(cf[r][2 * i + 1], (uint32_t)(wi >> (sh + 16)) & 0xFFFFu);
+            o[i] = b0 | (b1 << 16);
+        }
+        st_stream(dst + (int64_t)r * row_step * dk, u32x4{o[0], o[1], o[2], o[3]});
+    }
 }
 // LDS carve-up shared by the step and flush kernels (DVW = rows owned).
 template <class R>
@@ -767,6 +886,12 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
             for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
         }
     }
+    if constexpr (std::is_same<TS, tF16>::value) {
+        if (p.sr) {
+            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, cc);
+            return;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const int64_t rowoff = (int64_t)(r * RPP + rg) * DK;
@@ -873,6 +998,18 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 
     // S_t = alpha S_{t-1} + u k^T, stored every step.
     const float* u = FORM == kMamba2 ? s_v : s_u;
+    if constexpr (std::is_same<TS, tF16>::value) {
+        if (p.sr) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float ur = u[r * RPP + rg];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] = alpha * cf[r][c] + ur * kv[c];
+            }
+            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, row0 + rg, RPP, DK, cc);
+            return;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const float ur = u[r * RPP + rg];
@@ -955,6 +1092,12 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
             const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
 #pragma unroll
             for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+        }
+    }
+    if constexpr (std::is_same<TS, tF16>::value) {
+        if (p.sr) {
+            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, cc);
+            return;
         }
     }
 #pragma unroll
@@ -1289,8 +1432,17 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
                 for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
             }
         }
+        bool stored = false;
+        if constexpr (std::is_same<TS, tF16>::value) {
+            if (p.sr) {
+                sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc);
+                stored = true;
+            }
+        }
+        if (!stored) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+            for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+        }
     }
     // drafts become records base .. base + T - 1
 #pragma unroll

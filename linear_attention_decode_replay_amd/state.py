@@ -60,7 +60,7 @@ class _Stage:
 
 class DecodeLayer:
     def __init__(self, lay: RsLayer, n_slots: int, n_blocks: int | None = None, device="cuda",
-                 staging: int = 4):
+                 staging: int = 4, sr_key=(0, 0)):
         self.layer = lay
         self.L = int(lay.L)
         self.n_slots = n = int(n_slots)
@@ -75,7 +75,10 @@ class DecodeLayer:
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
         # batch[i] reads cursor i and writes the next cursors into cursor 1-i
         self.batch = [make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.cursor[i],
-                                 self.flush, self.err, next_write_pos=self.cursor[1 - i]) for i in (0, 1)]
+                                 self.flush, self.err, next_write_pos=self.cursor[1 - i], sr_key=sr_key)
+                      for i in (0, 1)]
+        # stochastic rounding: the counter's first word, one value per launch
+        self.sr_step = 0
         self._cur = 0
         self._stages = [_Stage(n) for _ in range(staging)]
         self._next = 0
@@ -130,6 +133,14 @@ class DecodeLayer:
             st.event.record(stream)
         self.uploads += 1
 
+    def _batch(self):
+        """The batch struct for the next launch, stamped with a fresh
+        stochastic-rounding counter word."""
+        b = self.batch[self._cur]
+        b.sr_step = self.sr_step
+        self.sr_step += 1
+        return b
+
     # ----------------------------------------------------------------- steps --
     def step(self, io, force: np.ndarray | None = None, stream=None, events=None):
         """One checkpoint + buffer decode step.  Returns the host (write_pos,
@@ -148,7 +159,7 @@ class DecodeLayer:
             self._dirty = False
         if events:
             events[0].record(stream)
-        replay_decode_step(self.layer, self.batch[self._cur], io, stream)
+        replay_decode_step(self.layer, self._batch(), io, stream)
         if events:
             events[1].record(stream)
         self._cur ^= 1
@@ -163,7 +174,7 @@ class DecodeLayer:
             self._dirty = False
         if events:
             events[0].record(stream)
-        conventional_decode_step(self.layer, self.batch[self._cur], io, stream)
+        conventional_decode_step(self.layer, self._batch(), io, stream)
         if events:
             events[1].record(stream)
 
@@ -176,7 +187,7 @@ class DecodeLayer:
         sel &= self.live()
         wp, _ = rs_meta_step(self.L, self.anchor)
         self._upload(stream, wp, sel.astype(np.uint8))
-        replay_flush(self.layer, self.batch[self._cur], stream)
+        replay_flush(self.layer, self._batch(), stream)
         self.anchor[sel] = 0
         self._dirty = True
 
@@ -204,7 +215,8 @@ class SpecDecodeLayer:
     copies the cursor back to the host.  Joining or leaving rows is an upload
     of the block table with the new rows' counts set to 0."""
 
-    def __init__(self, lay: RsLayer, n_slots: int, n_blocks: int | None = None, device="cuda"):
+    def __init__(self, lay: RsLayer, n_slots: int, n_blocks: int | None = None, device="cuda",
+                 sr_key=(0, 0)):
         if lay.spec_T < 1:
             raise ValueError("SpecDecodeLayer needs a speculative layer (spec_T > 0)")
         self.layer = lay
@@ -221,7 +233,9 @@ class SpecDecodeLayer:
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
         self._cur = 0
         self.batch = [make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.committed[i],
-                                 self.flag[i], self.err, next_write_pos=self.committed[1 - i]) for i in (0, 1)]
+                                 self.flag[i], self.err, next_write_pos=self.committed[1 - i], sr_key=sr_key)
+                      for i in (0, 1)]
+        self.sr_step = 0  # stochastic rounding: one counter word per verify launch
 
     def assign(self, slot: int, block: int) -> None:
         if not 0 <= block < self.pool.n_blocks:
@@ -251,7 +265,10 @@ class SpecDecodeLayer:
         stream = stream or torch.cuda.current_stream(self.device)
         if events:
             events[0].record(stream)
-        replay_spec_verify(self.layer, self.batch[self._cur], io, stream)
+        b = self.batch[self._cur]
+        b.sr_step = self.sr_step
+        self.sr_step += 1
+        replay_spec_verify(self.layer, b, io, stream)
         if events:
             events[1].record(stream)
 

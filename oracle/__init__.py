@@ -354,6 +354,15 @@ class SRReplayModel(ReplayModel):
         return out
 
 
+    def fold(self, rows_mask, sr_step=0):
+        """Token-less flush; the folded checkpoints are stored with
+        stochastic rounding like a flush's."""
+        super().fold(rows_mask)
+        for t in np.nonzero(np.repeat(np.asarray(rows_mask, bool), self.H))[0]:
+            self.C[t] = sr_f16(self.C[t].reshape(-1), sr_words(self.key, sr_step, self.tile_ids[t],
+                                                               self.dv * self.dk)).reshape(self.dv, self.dk)
+
+
 class SRConventionalModel(ConventionalModel):
     """Conventional decode with the state stored in fp16 with stochastic
     rounding after every step (the per-step rounding the blog's argument

@@ -169,13 +169,19 @@ def philox4x64(counter, key):
 F16_MAX = 65504.0
 
 
+SR_BITS = 16   # width of the random word one stochastic rounding consumes
+
+
 def sr_f16(x, r) -> np.ndarray:
-    """Stochastic rounding of real values x to fp16 with 32-bit random words r
+    """Stochastic rounding of real values x to fp16 with 16-bit random words r
     (same shape): |x| lies between two neighbouring fp16 values lo <= |x| < hi;
-    the result is hi (with x's sign) when r < p 2^32, p = (|x| - lo) / (hi - lo),
-    else lo, so it rounds up with probability p and E[result] = x.  Values that
-    are fp16 already are unchanged; |x| >= 65504 and non-finite values round
-    to nearest even (no stochastic choice at the top of the range)."""
+    the result is hi (with x's sign) when r < p 2^16, p = (|x| - lo) / (hi - lo),
+    else lo, so it rounds up with probability ceil(p 2^16) / 2^16: exactly p
+    when p is a multiple of 2^-16, as it is for every fp32 value from 2^-17
+    up (at most 13 bits lie below the fp16 grid there), so E[result] = x for
+    them.  Values that are fp16 already are unchanged; |x| >= 65504 and
+    non-finite values round to nearest even (no stochastic choice at the top
+    of the range)."""
     x = np.asarray(x, np.float64)
     r = np.asarray(r, np.float64)
     a = np.abs(x)
@@ -189,25 +195,26 @@ def sr_f16(x, r) -> np.ndarray:
     hi = (lo_b + 1).astype(np.uint16).view(np.float16).astype(np.float64)
     with np.errstate(invalid="ignore", divide="ignore"):
         p = (a - lo) / (hi - lo)
-    up = r < np.ldexp(p, 32)
+    up = r < np.ldexp(p, SR_BITS)
     mag = np.where(up, hi, lo)
-    rne = x.astype(np.float16).astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        rne = x.astype(np.float16).astype(np.float64)
     out = np.where(np.isfinite(x) & (a < F16_MAX), np.copysign(mag, x), rne)
     return out
 
 
 def sr_words(key, step, tile, n_elems):
-    """The 32-bit random word for each of n_elems consecutive state elements
-    (row-major d_v x d_k) of one tile at one step: element e uses word e % 8 of
-    Philox4x64-10 block (step, tile, e // 8, 0), the low half of 64-bit output
-    (e % 8) // 2 first.  key: two uint64."""
-    n_blk = (n_elems + 7) // 8
+    """The 16-bit random word for each of n_elems consecutive state elements
+    (row-major d_v x d_k) of one tile at one step: element e uses word e % 16
+    of Philox4x64-10 block (step, tile, e // 16, 0), whose four 64-bit outputs
+    are split into 16-bit words least significant first (output 0 bits 0-15,
+    16-31, 32-47, 48-63, then output 1, ...).  key: two uint64."""
+    n_blk = (n_elems + 15) // 16
     ctr = np.zeros((n_blk, 4), np.uint64)
     ctr[:, 0] = np.uint64(step)
     ctr[:, 1] = np.uint64(tile)
     ctr[:, 2] = np.arange(n_blk, dtype=np.uint64)
     out = philox4x64(ctr, np.asarray(key, np.uint64))       # [n_blk, 4] uint64
-    lo = (out & _M32).astype(np.uint64)
-    hi = (out >> np.uint64(32)).astype(np.uint64)
-    words = np.stack([lo, hi], axis=-1).reshape(n_blk, 8)  # lo0 hi0 lo1 hi1 ...
+    shifts = np.arange(4, dtype=np.uint64) * np.uint64(16)
+    words = (out[..., None] >> shifts) & np.uint64(0xFFFF)  # [n_blk, 4 outputs, 4 half-words]
     return words.reshape(-1)[:n_elems]

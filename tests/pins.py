@@ -587,13 +587,15 @@ def pin_philox_matches_library(orc):
 
 
 def pin_sr_rule(orc):
-    """Stochastic rounding to fp16: the result is one of the two fp16
-    neighbours, up with probability exactly p = (|x| - lo) / ulp (a uniform
-    grid of 2^16 random words rounds up exactly p 2^16 times), fp16 values
-    are unchanged, the sign is kept, and E[SR(x)] = x."""
+    """Stochastic rounding to fp16 with 16-bit words: the result is one of the
+    two fp16 neighbours, up with probability exactly p = (|x| - lo) / ulp (all
+    2^16 random words round up exactly p 2^16 times), fp16 values are
+    unchanged, the sign is kept, E[SR(x)] = x, and the fp16 subnormal range
+    (spacing 2^-24) and the top of the range behave the same way."""
     from oracle import formats
-    grid = np.arange(65536, dtype=np.float64) * 65536.0
-    for lo, ulp in ((1.0, 2.0**-10), (503 * 2.0**-24, 2.0**-24), (-1000.0, 0.5), (2.0**-20, 2.0**-24)):
+    grid = np.arange(65536, dtype=np.float64)
+    for lo, ulp in ((1.0, 2.0**-10), (503 * 2.0**-24, 2.0**-24), (-1000.0, 0.5), (2.0**-20, 2.0**-24),
+                    (65472.0, 32.0), (2.0**-14, 2.0**-24)):
         for k8 in range(8):
             p = k8 / 8.0
             x = np.sign(lo) * (abs(lo) + p * ulp)
@@ -601,20 +603,51 @@ def pin_sr_rule(orc):
             a, b = np.sign(x) * abs(lo), np.sign(x) * (abs(lo) + ulp)
             assert np.all((got == a) | (got == b)), (lo, k8)
             assert int(np.sum(got == b)) == int(p * 65536), (lo, k8, int(np.sum(got == b)))
-    # the convention both sides implement: round up exactly when r < p 2^32
+    # p = m / 2^13 for fp32 values (13 bits below the fp16 mantissa): every
+    # m rounds up exactly m 2^3 times out of 2^16
+    m = np.arange(0, 8192, 37)
+    x = 1.0 + m * 2.0**-23
+    ups = [int(np.sum(formats.sr_f16(np.full(65536, xi), grid) > 1.0)) for xi in x]
+    assert ups == list(8 * m)
+    # the convention both sides implement: round up exactly when r < p 2^16
     half = 1.0 + 2.0**-11
-    assert formats.sr_f16(np.array([half, half, half]), np.array([0.0, 2.0**31 - 1, 2.0**31])).tolist() == \
+    assert formats.sr_f16(np.array([half, half, half]), np.array([0.0, 2.0**15 - 1, 2.0**15])).tolist() == \
         [1.0 + 2.0**-10, 1.0 + 2.0**-10, 1.0]
     vals = np.float16(np.linspace(-3, 3, 97)).astype(np.float64)
-    assert np.array_equal(formats.sr_f16(vals, np.full(97, 2.0**32 - 1)), vals)
+    assert np.array_equal(formats.sr_f16(vals, np.full(97, 2.0**16 - 1)), vals)
+    assert np.array_equal(formats.sr_f16(np.array([0.0, -0.0]), np.zeros(2)), np.array([0.0, -0.0]))
+    assert np.signbit(formats.sr_f16(np.array([-0.0]), np.zeros(1))[0])
+    # at and above 65504, and for non-finite values: nearest even
+    top = np.array([65504.0, 65519.0, 65520.0, -70000.0, np.inf, -np.inf])
+    assert np.array_equal(formats.sr_f16(top, np.zeros(6)), np.array([65504.0, 65504.0, np.inf, -np.inf, np.inf, -np.inf]))
+    assert np.isnan(formats.sr_f16(np.array([np.nan]), np.zeros(1))[0])
     rng = np.random.default_rng(2)
     x = rng.standard_normal(200000).astype(np.float32).astype(np.float64)
-    r = rng.integers(0, 2**32, 200000).astype(np.float64)
+    r = rng.integers(0, 2**16, 200000).astype(np.float64)
     err = formats.sr_f16(x, r) - x
     e = np.frexp(np.abs(x))[1] - 1                  # |x| in [2^e, 2^(e+1))
     ulp = np.ldexp(1.0, np.maximum(e, -14) - 10)      # fp16 spacing there
     assert abs(np.mean(err / ulp)) < 0.01           # unbiased
     assert np.all(np.abs(err) <= ulp * 1.0000001)
+
+
+def pin_sr_words_layout(orc):
+    """The word layout: element e of a tile takes 16-bit word e % 16 of the
+    Philox4x64-10 block for counter (step, tile, e // 16, 0), least
+    significant half-word of output 0 first; checked against numpy's Philox
+    (whose counter is incremented before each block) for a few elements."""
+    from oracle import formats
+    key = np.array([0x243F6A8885A308D3, 0x13198A2E03707344], np.uint64)
+    w = formats.sr_words(key, 5, 9, 8192)
+    assert w.dtype == np.uint64 and w.max() < 2**16 and len(w) == 8192
+    for e in (0, 1, 3, 4, 7, 15, 16, 33, 8191):
+        ctr = np.array([4, 9, e // 16, 0], np.uint64)   # numpy adds 1 to word 0 first
+        out = np.random.Philox(counter=ctr, key=key).random_raw(4)
+        want = (int(out[(e % 16) // 4]) >> (16 * (e % 4))) & 0xFFFF
+        assert int(w[e]) == want, e
+    # distinct (step, tile) pairs draw distinct words
+    assert not np.array_equal(w[:64], formats.sr_words(key, 6, 9, 64))
+    assert not np.array_equal(w[:64], formats.sr_words(key, 5, 10, 64))
 
 
 def pin_sr_once_per_window(orc):
@@ -680,5 +713,6 @@ ALL_PINS = [
     pin_spec_cursor,
     pin_philox_matches_library,
     pin_sr_rule,
+    pin_sr_words_layout,
     pin_sr_once_per_window,
 ]

@@ -291,3 +291,39 @@ def test_grouped_io_strides():
     with pytest.raises(rs.ReplaySSMError) as e:                    # k rows shorter than 8 groups
         rs.replay_decode_step(layer, batch, io, stream=0)
     assert "row strides" in rs.last_error()
+
+
+# ------------------------------------------------------ stochastic rounding --
+def _rounded(mode, **kw):
+    lay = _c2(**kw)
+    lay.state_rounding = mode
+    return lay
+
+
+@pytest.mark.parametrize("mode,kw,code", [
+    (2, dict(), rs.RS_EINVAL), (-1, dict(), rs.RS_EINVAL),
+    (rs.RS_ROUND_STOCHASTIC, dict(), rs.RS_EUNSUPPORTED),                      # fp32 state
+    (rs.RS_ROUND_STOCHASTIC, dict(state_dtype="f16", read_dtype="e4m3"), rs.RS_EUNSUPPORTED),
+])
+def test_rounding_validation(mode, kw, code):
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.block_layout(_rounded(mode, **kw))
+    assert e.value.code == code
+
+
+def test_stochastic_rounding_layers_accepted():
+    """An fp16 state with stochastic rounding: standard, grouped and
+    speculative layers; the block layout is the nearest-even one's."""
+    for extra in (dict(), dict(n_groups=8), dict(spec_T=4)):
+        lay = rs.block_layout(_c2(state_dtype="f16", stochastic=True, **extra))
+        ref = rs.block_layout(_c2(state_dtype="f16", **extra))
+        assert (lay.block_bytes, lay.ckpt_off, lay.rec_k_off) == (ref.block_bytes, ref.ckpt_off, ref.rec_k_off)
+        assert rs.layer_supported(_c2(state_dtype="f16", stochastic=True, **extra)) == rs.RS_OK
+
+
+def test_batch_struct_carries_key_and_counter():
+    b = rs.RsBatch(4, 0, 4, None, None, None, None, None, None, 2**64 - 1, 5, 2**63 + 7)
+    assert (b.sr_key0, b.sr_key1, b.sr_step) == (2**64 - 1, 5, 2**63 + 7)
+    # 2 int32 + int64 + 6 pointers + 3 uint64; 12 int32
+    assert ctypes.sizeof(rs.RsBatch) == 88
+    assert ctypes.sizeof(rs.RsLayer) == 48

@@ -230,10 +230,10 @@ def _sr_mutants():
         return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
 
     def flipped(x, r):                      # rounds up with probability 1 - p
-        return sr(x, 2.0**32 - 1 - np.asarray(r, np.float64))
+        return sr(x, 2.0**16 - 1 - np.asarray(r, np.float64))
 
     def truncate(x, r):                     # always the neighbour towards zero
-        return sr(x, np.full(np.shape(x), 2.0**32))
+        return sr(x, np.full(np.shape(x), 2.0**16))
 
     def no_key_bump(counter, key):          # key not advanced between rounds
         import numpy as np
@@ -252,9 +252,30 @@ def _sr_mutants():
         out = ph(counter, key)
         return out ^ np.uint64(1)           # any corruption of the output words
 
+    def _words(key, step, tile, n, per_block, order):
+        n_blk = (n + per_block - 1) // per_block
+        ctr = np.zeros((n_blk, 4), np.uint64)
+        ctr[:, 0], ctr[:, 1] = np.uint64(step), np.uint64(tile)
+        ctr[:, 2] = np.arange(n_blk, dtype=np.uint64)
+        out = ph(ctr, np.asarray(key, np.uint64))
+        sh = np.arange(4, dtype=np.uint64)[::order] * np.uint64(16)
+        w = ((out[..., None] >> sh) & np.uint64(0xFFFF)).reshape(n_blk, 16)[:, :per_block]
+        return w.reshape(-1)[:n]
+
+    def words_high_first(key, step, tile, n):     # most significant half-word first
+        return _words(key, step, tile, n, 16, -1)
+
+    def words_eight_per_block(key, step, tile, n):  # a block per 8 elements
+        return _words(key, step, tile, n, 8, 1)
+
+    def words_step_tile_swapped(key, step, tile, n):
+        return _words(key, tile, step, n, 16, 1)
+
     return {"sr_nearest": ("sr_f16", nearest), "sr_flipped": ("sr_f16", flipped),
             "sr_truncate": ("sr_f16", truncate), "philox_no_key_bump": ("philox4x64", no_key_bump),
-            "philox_corrupt": ("philox4x64", nine_rounds)}
+            "philox_corrupt": ("philox4x64", nine_rounds), "words_high_first": ("sr_words", words_high_first),
+            "words_eight_per_block": ("sr_words", words_eight_per_block),
+            "words_step_tile_swapped": ("sr_words", words_step_tile_swapped)}
 
 
 @pytest.mark.parametrize("kind", sorted(_sr_mutants()))
@@ -264,7 +285,8 @@ def test_sr_mutant_is_caught(monkeypatch, kind):
     name, fn = _sr_mutants()[kind]
     monkeypatch.setattr(formats, name, fn)
     caught = []
-    for pin in (pins.pin_philox_matches_library, pins.pin_sr_rule, pins.pin_sr_once_per_window):
+    for pin in (pins.pin_philox_matches_library, pins.pin_sr_rule, pins.pin_sr_words_layout,
+                pins.pin_sr_once_per_window):
         try:
             pin(oracle.get())
         except AssertionError:

@@ -29,7 +29,7 @@ import torch
 _TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # independent random streams
-_S_TOKENS, _S_HEADS, _S_INIT, _S_SCHED, _S_POOL = 1, 2, 3, 4, 5
+_S_TOKENS, _S_HEADS, _S_INIT, _S_SCHED, _S_POOL, _S_DYADIC = 1, 2, 3, 4, 5, 6
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -86,6 +86,20 @@ def gdn_tokens(seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str =
     beta = torch.sigmoid(torch.randn((B, H), generator=g, dtype=torch.float64)).float()
     lam = (-_softplus(torch.randn((B, H), generator=g, dtype=torch.float64))).float()
     return Tokens(q, k, v, lam, beta)
+
+
+def dyadic_tokens(seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str = "bf16",
+                  bits: int = 6) -> Tokens:
+    """Mamba-2 tokens on which fp32 and fp64 arithmetic agree exactly: q, k,
+    v uniform on the integer multiples of 2^-bits in [-1, 1] (exact in bf16
+    and fp16 for bits <= 7), log-decay 0 (alpha = 1), so every product is a
+    multiple of 2^-2bits and short sums of them are exact in fp32."""
+    g = _gen(seed, _S_DYADIC, step)
+    dt = _TORCH_DT[io]
+    m = 1 << bits
+    draw = lambda d: (torch.randint(-m, m + 1, (B, H, d), generator=g).double() / m).to(dt)
+    q, k, v = draw(dk), draw(dk), draw(dv)
+    return Tokens(q, k, v, torch.zeros((B, H)), None)
 
 
 def tokens(form: int, seed: int, step: int, B: int, H: int, dv: int, dk: int, io: str,
