@@ -93,10 +93,11 @@ typedef enum {
  *               q and k inputs are [n_rows][G][d_k] and the ring keeps one
  *               key record per group.  Standard decoding only (spec_T = 0).
  * state_rounding: RS_ROUND_NEAREST (nearest even) for every store.
- *               RS_ROUND_STOCHASTIC, with state_dtype RS_F16 and a single
- *               checkpoint only: every store of the 16-bit checkpoint or
- *               state (a flush, a token-less flush, a conventional step,
- *               the flush of a speculative verify)
+ *               RS_ROUND_STOCHASTIC, with state_dtype RS_F16 only: every
+ *               store of the fp16 checkpoint, state or recurrence copy (a
+ *               flush, a token-less flush, a conventional step, the flush of
+ *               a speculative verify; an E4M3 read copy is still rounded to
+ *               nearest even, from the same unrounded values)
  *               rounds each value x up to the next fp16 neighbour exactly
  *               when the value's 16-bit random word r is below p 2^16,
  *               p = (|x| - lo) / (hi - lo) for the fp16 neighbours
@@ -114,16 +115,19 @@ typedef enum {
  *               precision argument, derived") keeps the recurrence copy in
  *               FP16 with stochastic rounding, so that rounding enters the
  *               recurrence unbiased and once per window.
- * read_dtype:   -1 (or state_dtype) for a single checkpoint; RS_F16,
- *               RS_BF16 or RS_E4M3 for a two-precision checkpoint (blog "The
- *               precision argument, derived"): state_dtype RS_F32 is the
- *               recurrence copy, read by flushes only; a second copy in
+ * read_dtype:   -1 (or state_dtype) for a single checkpoint; for a
+ *               two-precision checkpoint (blog "The precision argument,
+ *               derived") RS_F16, RS_BF16 or RS_E4M3 over an RS_F32
+ *               recurrence copy (state_dtype), or RS_E4M3 over an RS_F16
+ *               one (the pages' preferred pairing: an FP16 recurrence copy
+ *               with stochastic rounding and a coarse read copy): the
+ *               recurrence copy is read by flushes only; a second copy in
  *               read_dtype is what non-flush steps read.  A flush folds from
  *               the recurrence copy and rewrites both copies from the same
  *               unrounded values, so the read copy's rounding never enters
  *               the recurrence.  Mamba-2 form only (RS_EUNSUPPORTED for GDN:
  *               its buffered corrections would carry the read copy's error).
- *               All roundings are to nearest even.  An RS_E4M3 read copy
+ *               Read copies round to nearest even.  An RS_E4M3 read copy
  *               scales each state row (the d_k entries of one output
  *               component) by its own power of two 2^e, e the smallest
  *               integer with max|row| * 2^-e <= 448 (and at least -100): it

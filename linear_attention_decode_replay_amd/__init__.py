@@ -270,13 +270,14 @@ def rs_meta_advance(L: int, steps_since_anchor: np.ndarray, flush: np.ndarray) -
 
 def read_copy_columns(lay: RsLayer) -> np.ndarray:
     """For a two-precision layer: the column held by each stored position of
-    a read-copy row.  With n read elements per 16 bytes, position p (chunk
-    c = p // n, e = p % n) holds column 4 (c + (d_k // n) (e // 4)) + e % 4
-    (4 = fp32 recurrence-copy elements per 16 bytes)."""
+    a read-copy row.  With n read elements and m recurrence-copy elements per
+    16 bytes (m = 4 for fp32, 8 for fp16), position p (chunk c = p // n,
+    e = p % n) holds column m (c + (d_k // n) (e // m)) + e % m."""
     n = {F16: 8, BF16: 8, E4M3: 16}[lay.read_dtype]
+    m = {F32: 4, F16: 8}[lay.state_dtype]
     p = np.arange(lay.d_k)
     c, e = p // n, p % n
-    return 4 * (c + (lay.d_k // n) * (e // 4)) + e % 4
+    return m * (c + (lay.d_k // n) * (e // m)) + e % m
 
 
 # ------------------------------------------------------------ device memory --

@@ -56,14 +56,15 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
         if (L->form != RS_MAMBA2)
             return fail(RS_EUNSUPPORTED, "two-precision checkpoint: Mamba-2 form only (a GDN read copy would "
                                          "leak into the buffered corrected values)");
-        if (L->state_dtype != RS_F32)
-            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: fp32 recurrence copy only");
+        if (L->state_dtype != RS_F32 && !(L->state_dtype == RS_F16 && L->read_dtype == RS_E4M3))
+            return fail(RS_EUNSUPPORTED, "two-precision checkpoint: an fp32 recurrence copy, or an fp16 one with "
+                                         "an E4M3 read copy");
     }
     if (L->record_dtype == RS_BF16) return fail(RS_EUNSUPPORTED, "bf16 records are not supported");
     if (L->state_rounding != RS_ROUND_NEAREST && L->state_rounding != RS_ROUND_STOCHASTIC)
         return fail(RS_EINVAL, "unknown state rounding %d", L->state_rounding);
-    if (L->state_rounding == RS_ROUND_STOCHASTIC && (L->state_dtype != RS_F16 || two_precision(*L)))
-        return fail(RS_EUNSUPPORTED, "stochastic rounding: a single fp16 checkpoint / state only");
+    if (L->state_rounding == RS_ROUND_STOCHASTIC && L->state_dtype != RS_F16)
+        return fail(RS_EUNSUPPORTED, "stochastic rounding: an fp16 checkpoint / state (recurrence copy) only");
     if (L->n_groups < 0 || (L->n_groups > 0 && L->n_heads % L->n_groups != 0))
         return fail(RS_EINVAL, "n_groups (%d) must be 0 or divide n_heads (%d)", L->n_groups, L->n_heads);
     if (L->spec_T != 0 && groups_of(*L) != L->n_heads)

@@ -265,20 +265,21 @@ __device__ __forceinline__ uint64_t xswap64(uint64_t v) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Random words for a lane's 8-element chunks (columns 8 cc .. 8 cc + 7) of
-// state rows row_first + r row_step, r < NR.  Element e of a (row, head)
-// tile (row-major) uses 16-bit word e mod 16 of the Philox4x64-10 block for
-// counter (sr_step, tile, e / 16, 0), the 64-bit outputs split least
-// significant half-word first; a chunk is half a block, so w[r] = the two
-// 64-bit outputs of its half.  Adjacent lanes cc = 2j, 2j + 1 hold the two
-// halves of the same blocks: with NR even each lane of the pair generates
-// the block of one of two rows and hands the other half to its partner.
-// Every lane of the wave must execute this.
+// Random words for a lane's 8-element chunks (columns col .. col + 7, col a
+// multiple of 8) of state rows row_first + r row_step, r < NR.  Element e of
+// a (row, head) tile (row-major) uses 16-bit word e mod 16 of the
+// Philox4x64-10 block for counter (sr_step, tile, e / 16, 0), the 64-bit
+// outputs split least significant half-word first; a chunk is half a block,
+// so w[r] = the two 64-bit outputs of its half.  The lane holding the other
+// half of the same 16 columns is the adjacent one (lane ^ 1, column col ^ 8):
+// with NR even each lane of the pair generates the block of one of two rows
+// and hands the other half to its partner.  Every lane of the wave must
+// execute this.
 template <int NR>
 __device__ __forceinline__ void sr_lane_words(const StepParams& p, int64_t tile, int row_first, int row_step,
-                                              int dk, int cc, uint64_t (&w)[NR][2]) {
-    const bool odd = cc & 1;
-    const int64_t cblk = cc >> 1;
+                                              int dk, int col, uint64_t (&w)[NR][2]) {
+    const bool odd = (col >> 3) & 1;
+    const int64_t cblk = col >> 4;
     const int64_t bpr = dk / 16;  // blocks per state row
     if constexpr (NR % 2 == 0) {
 #pragma unroll
@@ -473,26 +474,32 @@ __device__ __forceinline__ void st_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// Stores a lane's 8-element chunks of an fp16 state in rows
-// row_first + r row_step (dst: the chunk in the first of them, rows
-// row_step d_k elements apart) with stochastic rounding.
-template <int NR>
-__device__ __forceinline__ void sr_store_rows(const float (&cf)[NR][8], _Float16* dst, const StepParams& p,
-                                              int64_t tile, int row_first, int row_step, int dk, int cc) {
-    uint64_t w[NR][2];
-    sr_lane_words<NR>(p, tile, row_first, row_step, dk, cc, w);
+// Stores a lane's share of an fp16 state with stochastic rounding: HPC
+// 8-element chunks per row, chunk h at column col0 + 8 LPR h (the lane order
+// of a two-precision checkpoint; HPC = 1 for a single one), in rows
+// row_first + r row_step (dst: the first chunk of the first of them, rows
+// row_step d_k elements apart).  cf[r][8 h + i] is element i of chunk h.
+template <int NR, int HPC, int LPR>
+__device__ __forceinline__ void sr_store_rows(const float (&cf)[NR][8 * HPC], _Float16* dst, const StepParams& p,
+                                              int64_t tile, int row_first, int row_step, int dk, int col0) {
+    static_assert(HPC == 1 || LPR % 2 == 0, "the two halves of a block sit in adjacent lanes");
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        uint32_t o[4];
+    for (int h = 0; h < HPC; ++h) {
+        uint64_t w[NR][2];
+        sr_lane_words<NR>(p, tile, row_first, row_step, dk, col0 + 8 * LPR * h, w);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint64_t wi = w[r][i >> 1];
-            const int sh = 32 * (i & 1);
-            const uint32_t b0 = sr_f16_bits(cf[r][2 * i], (uint32_t)(wi >> sh) & 0xFFFFu);
-            const uint32_t b1 = sr_f16_bits(cf[r][2 * i + 1], (uint32_t)(wi >> (sh + 16)) & 0xFFFFu);
-            o[i] = b0 | (b1 << 16);
+        for (int r = 0; r < NR; ++r) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t wi = w[r][i >> 1];
+                const int sh = 32 * (i & 1);
+                const uint32_t b0 = sr_f16_bits(cf[r][8 * h + 2 * i], (uint32_t)(wi >> sh) & 0xFFFFu);
+                const uint32_t b1 = sr_f16_bits(cf[r][8 * h + 2 * i + 1], (uint32_t)(wi >> (sh + 16)) & 0xFFFFu);
+                o[i] = b0 | (b1 << 16);
+            }
+            st_stream(dst + (int64_t)r * row_step * dk + 8 * LPR * h, u32x4{o[0], o[1], o[2], o[3]});
         }
-        st_stream(dst + (int64_t)r * row_step * dk, u32x4{o[0], o[1], o[2], o[3]});
     }
 }
 // LDS carve-up shared by the step and flush kernels (DVW = rows owned).
@@ -888,7 +895,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     }
     if constexpr (std::is_same<TS, tF16>::value) {
         if (p.sr) {
-            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, cc);
+            sr_store_rows<NR, HPC, LPR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, col0);
+            if constexpr (TWO) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    store_read_row<TL, VEC, LPR>(cf[r], cl + (int64_t)(r * RPP + rg) * DK + cc * VEC,
+                                                 cs + r * RPP + rg, cc);
+            }
             return;
         }
     }
@@ -1006,7 +1019,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) cf[r][c] = alpha * cf[r][c] + ur * kv[c];
             }
-            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, row0 + rg, RPP, DK, cc);
+            sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, row0 + rg, RPP, DK, cc * VEC);
             return;
         }
     }
@@ -1096,7 +1109,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     }
     if constexpr (std::is_same<TS, tF16>::value) {
         if (p.sr) {
-            sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, cc);
+            sr_store_rows<NR, HPC, LPR>(cf, ck + (int64_t)rg * DK + col0, p, id.tile, row0 + rg, RPP, DK, col0);
+            if constexpr (TWO) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    store_read_row<TL, VEC, LPR>(cf[r], cl + (int64_t)(r * RPP + rg) * DK + cc * VEC,
+                                                 cs + r * RPP + rg, cc);
+            }
             return;
         }
     }
@@ -1435,7 +1454,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
         bool stored = false;
         if constexpr (std::is_same<TS, tF16>::value) {
             if (p.sr) {
-                sr_store_rows<NR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc);
+                sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
                 stored = true;
             }
         }
@@ -1616,16 +1635,18 @@ bool with_form(int form, F&& f) {
     return false;
 }
 
-// The read copy's type: the state type itself (one checkpoint), or fp16 /
-// bf16 / E4M3 for a two-precision checkpoint over an fp32 recurrence copy.
-// E4M3 needs a head of at least one wave of 16-byte code chunks (64 x 128
-// and 128 x 128; not 16 x 32).
+// The read copy's type: the state type itself (one checkpoint), or, for a
+// two-precision checkpoint, fp16 / bf16 / E4M3 over an fp32 recurrence copy
+// and E4M3 over an fp16 one.  E4M3 needs a head of at least one wave of
+// 16-byte code chunks (64 x 128 and 128 x 128; not 16 x 32).
 template <int DV, int DK, class TS, class F>
 bool with_read(int read_dt, int state_dt, F&& f) {
     if (read_dt < 0 || read_dt == state_dt) { f(TS{}); return true; }
     if constexpr (std::is_same<TS, tF32>::value) {
         if (read_dt == RS_F16) { f(tF16{}); return true; }
         if (read_dt == RS_BF16) { f(tBF16{}); return true; }
+    }
+    if constexpr (std::is_same<TS, tF32>::value || std::is_same<TS, tF16>::value) {
         if constexpr (tile_ok<DV, DK, tE4M3, split_for<DV, DK>()>()) {
             if (read_dt == RS_E4M3) { f(tE4M3{}); return true; }
         }

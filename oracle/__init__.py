@@ -275,18 +275,38 @@ class ReplayModel:
 
 class TwoCopyReplayModel(ReplayModel):
     """Checkpoint + buffer with two checkpoint copies (blog, section "The
-    precision argument, derived"): the recurrence copy
-    C is exact (float64) and is read only by flushes; the read copy C_lo is C
-    rounded to `read_dtype` (formats.round_to: f16, bf16 or e4m3 with a
-    power-of-two scale per state row) at each flush, from the same unrounded
-    fold, and is what non-flush steps read.  Mamba-2 form."""
+    precision argument, derived"): the recurrence copy C is read only by
+    flushes; the read copy C_lo is what non-flush steps read.  A flush folds
+    from C and casts the same unrounded fold into both copies: C_lo rounded
+    to `read_dtype` (formats.round_to: f16, bf16 or e4m3 with a power-of-two
+    scale per state row), C kept exact (rec_dtype None) or stored in fp16
+    (rec_dtype "f16"), to nearest even or, given a Philox key, with
+    stochastic rounding (the paper's preferred recurrence copy, in the
+    blog's account); `tile_ids` as in SRReplayModel.  Mamba-2 form."""
 
-    def __init__(self, B, H, dv, dk, L, read_dtype="f16", oracle=None):
+    def __init__(self, B, H, dv, dk, L, read_dtype="f16", oracle=None, rec_dtype=None, key=None, tile_ids=None):
         super().__init__(MAMBA2, B, H, dv, dk, L, oracle)
         self.read_dtype = read_dtype
         self.C_lo = np.zeros_like(self.C)
+        if rec_dtype not in (None, "f16"):
+            raise ValueError(f"recurrence copy dtype {rec_dtype!r}: None (exact) or 'f16'")
+        self.rec_dtype = rec_dtype
+        self.key = None if key is None else np.asarray(key, np.uint64)
+        self.tile_ids = np.arange(B * H) if tile_ids is None else np.asarray(tile_ids)
 
-    def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None):
+    def _store(self, mask, sr_step):
+        """Both copies of the masked tiles from the unrounded fold in C."""
+        self.C_lo[mask] = round_to(self.C[mask], self.read_dtype)
+        if self.rec_dtype is None:
+            return
+        for t in np.nonzero(mask)[0]:
+            if self.key is None:
+                self.C[t] = round_to(self.C[t], "f16")
+            else:
+                self.C[t] = sr_f16(self.C[t].reshape(-1), sr_words(self.key, sr_step, self.tile_ids[t],
+                                                                   self.dv * self.dk)).reshape(self.dv, self.dk)
+
+    def step(self, q, k, v, lam, flush_rows, beta=None, active_rows=None, sr_step=0):
         B, H = self.B, self.H
         n = B * H
         fl = np.repeat(np.asarray(flush_rows, bool), H)
@@ -298,14 +318,12 @@ class TwoCopyReplayModel(ReplayModel):
         # flush rows: fold from the recurrence copy, then re-round the read copy
         out += self.o.replay_step(MAMBA2, self.C, self.rec_lam, self.rec_x, self.rec_k, self.w, fl, *args,
                                   act & fl)
-        f = act & fl
-        self.C_lo[f] = round_to(self.C[f], self.read_dtype)
+        self._store(act & fl, sr_step)
         return out.reshape(B, H, self.dv)
 
-    def fold(self, rows_mask):
+    def fold(self, rows_mask, sr_step=0):
         super().fold(rows_mask)
-        mask = np.repeat(np.asarray(rows_mask, bool), self.H)
-        self.C_lo[mask] = round_to(self.C[mask], self.read_dtype)
+        self._store(np.repeat(np.asarray(rows_mask, bool), self.H), sr_step)
 
     def read_error_bound(self, q, lam):
         """Before step(q, ..., lam, ...): per output component, the most the

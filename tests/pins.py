@@ -374,6 +374,40 @@ def pin_two_copy_error_does_not_accumulate(orc):
     assert late_single > 2 * late_two, (late_single, late_two)
 
 
+def pin_two_copy_f16_recurrence(orc):
+    """[blog] "The precision argument, derived": a flush casts the same
+    unrounded fold into both copies.  With an fp16 recurrence copy under
+    stochastic rounding and an E4M3 read copy, three windows: after each
+    flush the read copy is the E4M3 rounding of the fold computed (by a
+    separate exact model started from the stored recurrence copy) before any
+    rounding, the recurrence copy is that fold under the Philox words of
+    (flush step, tile), and the non-flush outputs are those of the exact
+    model from the read copy."""
+    from oracle import formats
+    B, H, dv, dk, L = 2, 3, 16, 32, 4
+    key = np.array([3, 5], np.uint64)
+    tiles = np.arange(B * H) + 40
+    two = oracle.TwoCopyReplayModel(B, H, dv, dk, L, "e4m3", oracle=orc, rec_dtype="f16", key=key, tile_ids=tiles)
+    ws, fls = orc.cursor_run(L, 0, 3 * L)
+    for s in range(3 * L):
+        q, k, v, lam, _ = _tok(M2, 31, s, B, H, dv, dk)
+        ref = oracle.ReplayModel(M2, B, H, dv, dk, L, oracle=orc)
+        ref.C, ref.rec_lam, ref.rec_x, ref.rec_k, ref.w = (two.C.copy(), two.rec_lam.copy(), two.rec_x.copy(),
+                                                       two.rec_k.copy(), two.w.copy())
+        if not fls[s]:
+            ref.C = two.C_lo.copy()      # a non-flush step reads the read copy
+        o_ref = ref.step(q, k, v, lam, np.full(B, fls[s]))
+        o = two.step(q, k, v, lam, np.full(B, fls[s]), sr_step=100 + s)
+        assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12 * np.abs(o_ref).max()), s
+        if fls[s]:
+            assert np.array_equal(two.C_lo, formats.round_to(ref.C, "e4m3")), s
+            for t in range(B * H):
+                want = formats.sr_f16(ref.C[t].reshape(-1), formats.sr_words(key, 100 + s, tiles[t], dv * dk))
+                assert np.array_equal(two.C[t].reshape(-1), want), (s, t)
+            assert not np.array_equal(two.C, oracle.round_to(ref.C, "f16"))   # not nearest even
+    assert int(fls.sum()) == 3
+
+
 def pin_e4m3_matches_library_cast(orc):
     """[ofp8] E4M3 codes with round to nearest even: equal to torch's
     float8_e4m3fn cast (a library routine) on fp32 values spread over the
@@ -702,6 +736,7 @@ ALL_PINS = [
     pin_cursor_forced_flush,
     pin_two_copy_read_error_is_one_rounding,
     pin_two_copy_error_does_not_accumulate,
+    pin_two_copy_f16_recurrence,
     pin_e4m3_matches_library_cast,
     pin_e4m3_spec_values,
     pin_read_rounding_within_half_ulp,

@@ -303,7 +303,7 @@ def _rounded(mode, **kw):
 @pytest.mark.parametrize("mode,kw,code", [
     (2, dict(), rs.RS_EINVAL), (-1, dict(), rs.RS_EINVAL),
     (rs.RS_ROUND_STOCHASTIC, dict(), rs.RS_EUNSUPPORTED),                      # fp32 state
-    (rs.RS_ROUND_STOCHASTIC, dict(state_dtype="f16", read_dtype="e4m3"), rs.RS_EUNSUPPORTED),
+    (rs.RS_ROUND_STOCHASTIC, dict(state_dtype="f16", read_dtype="bf16"), rs.RS_EUNSUPPORTED),
 ])
 def test_rounding_validation(mode, kw, code):
     with pytest.raises(rs.ReplaySSMError) as e:
@@ -311,10 +311,28 @@ def test_rounding_validation(mode, kw, code):
     assert e.value.code == code
 
 
+@pytest.mark.parametrize("state,read,code", [
+    ("f32", "f16", rs.RS_OK), ("f32", "bf16", rs.RS_OK), ("f32", "e4m3", rs.RS_OK), ("f16", "e4m3", rs.RS_OK),
+    ("f16", "bf16", rs.RS_EUNSUPPORTED), ("f16", "f32", rs.RS_EUNSUPPORTED),
+])
+def test_two_precision_pairings(state, read, code):
+    """Recurrence copy / read copy pairs: fp32 under any read copy, fp16
+    under E4M3 only."""
+    lay = _c2(state_dtype=state, read_dtype=read)
+    assert rs.layer_supported(lay) == code
+    if code == rs.RS_OK:
+        b = rs.block_layout(lay)
+        elem = 128 * 64 * 128
+        assert b.ckpt_lo_off >= b.ckpt_off + elem * (4 if state == "f32" else 2)
+        if read == "e4m3":
+            assert b.ckpt_scale_off >= b.ckpt_lo_off + elem
+
+
 def test_stochastic_rounding_layers_accepted():
     """An fp16 state with stochastic rounding: standard, grouped and
-    speculative layers; the block layout is the nearest-even one's."""
-    for extra in (dict(), dict(n_groups=8), dict(spec_T=4)):
+    speculative layers and an fp16 recurrence copy under an E4M3 read copy;
+    the block layout is the nearest-even one's."""
+    for extra in (dict(), dict(n_groups=8), dict(spec_T=4), dict(read_dtype="e4m3")):
         lay = rs.block_layout(_c2(state_dtype="f16", stochastic=True, **extra))
         ref = rs.block_layout(_c2(state_dtype="f16", **extra))
         assert (lay.block_bytes, lay.ckpt_off, lay.rec_k_off) == (ref.block_bytes, ref.ckpt_off, ref.rec_k_off)
@@ -327,3 +345,16 @@ def test_batch_struct_carries_key_and_counter():
     # 2 int32 + int64 + 6 pointers + 3 uint64; 12 int32
     assert ctypes.sizeof(rs.RsBatch) == 88
     assert ctypes.sizeof(rs.RsLayer) == 48
+
+
+@pytest.mark.parametrize("state,read", [("f32", "f16"), ("f32", "bf16"), ("f32", "e4m3"), ("f16", "e4m3")])
+def test_read_copy_columns_permutation(state, read):
+    """The read copy's lane order is a permutation of the columns, with each
+    16-byte read chunk holding whole recurrence-copy chunks (contiguous runs
+    of 16 / element size columns)."""
+    lay = _c2(state_dtype=state, read_dtype=read)
+    cols = rs.read_copy_columns(lay)
+    assert sorted(cols) == list(range(128))
+    m = 4 if state == "f32" else 2
+    run = 16 // m
+    assert all(cols[i + 1] == cols[i] + 1 for i in range(128) if (i + 1) % run and i + 1 < 128)

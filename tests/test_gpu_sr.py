@@ -20,6 +20,7 @@ import torch
 import linear_attention_decode_replay_amd as rs
 import oracle
 import workloads
+from oracle import formats
 from gpu_harness import TOL_F32, TOL_LOW, rel_err, say
 from linear_attention_decode_replay_amd.state import DecodeLayer, SpecDecodeLayer
 
@@ -241,3 +242,114 @@ def test_sr_spec_flush_exact():
         rs.rs_spec_meta_advance(L, T, h, fl, a)
     assert flushes >= 3 and int(d.err.item()) == 0
     say("[sr] speculative flush rounds bit for bit")
+
+
+def _run_two_copy(B, H, L, steps, seed, exact, stochastic=True, sample=None):
+    """A two-precision checkpoint with an fp16 recurrence copy (stochastic
+    or nearest rounding) under an E4M3 read copy, Nemotron head shape,
+    against oracle.TwoCopyReplayModel.  Both copies of a flushed tile come
+    from the same unrounded fold: exact inputs make both bit-exact; random
+    inputs check the recurrence copy as above and the read copy's codes and
+    row scales against the oracle's encoding of its fp64 fold, then
+    resynchronise the model to the GPU's copies."""
+    dv, dk = 64, 128
+    tag = f"two-copy f16/e4m3 B={B} H={H} L={L} steps={steps} exact={exact} sr={stochastic} seed={seed}"
+    say(f"[case] {tag}")
+    lay = rs.layer(rs.MAMBA2, H, dv, dk, L, "f16", "f16", "bf16", "e4m3", stochastic=stochastic)
+    n_blocks = B + 3
+    rep = DecodeLayer(lay, B, n_blocks, "cuda", sr_key=KEY)
+    rep.pool.raw.fill_(0xFF)
+    blocks = workloads.shuffled_blocks(seed, B, n_blocks)
+    for b in range(B):
+        rep.assign(b, int(blocks[b]))
+    rep.reset_rows(range(B))
+    sample = list(range(B)) if sample is None else sample
+    ns = len(sample)
+    tiles = np.array([b * H + h for b in sample for h in range(H)])
+    model = oracle.TwoCopyReplayModel(ns, H, dv, dk, L, "e4m3", rec_dtype="f16", key=KEY if stochastic else None,
+                                      tile_ids=tiles)
+    blk = torch.as_tensor(blocks[sample], device="cuda", dtype=torch.long)
+    inv = np.argsort(rep.pool.ckpt_lo_columns())   # stored position of each column
+    stats = StoreStats()
+    n_rne = n_rne_diff = 0
+    code_diff = code_n = scale_diff = scale_n = 0
+    tie_off = 0.0
+    err, flushes = 0.0, 0
+    for s in range(steps):
+        tok = (workloads.dyadic_tokens(seed, s, B, H, dv, dk) if exact
+               else workloads.mamba2_tokens(seed, s, B, H, dv, dk, "bf16"))
+        q, k, v, lam = (t.to("cuda") for t in (tok.q, tok.k, tok.v, tok.lam))
+        out = torch.empty(B, H, dv, device="cuda")
+        step_r = rep.sr_step
+        _, fl = rep.step(rs.make_io(q, k, v, lam, out))
+        a64 = [t[sample].double().numpy() for t in (tok.q, tok.k, tok.v, tok.lam)]
+        flr = np.asarray(fl)[sample].astype(bool)
+        pre = oracle.ReplayModel(rs.MAMBA2, ns, H, dv, dk, L)   # the unrounded fold of flushing tiles
+        pre.C, pre.rec_lam, pre.rec_x, pre.rec_k, pre.w = (model.C.copy(), model.rec_lam.copy(),
+                                                         model.rec_x.copy(), model.rec_k.copy(), model.w.copy())
+        pre.step(*a64, flr)
+        o = model.step(*a64, flr, sr_step=step_r)
+        torch.cuda.synchronize()
+        err = max(err, rel_err(out[sample].double().cpu().numpy(), o))
+        assert err <= (TOL_F32 if exact else TOL_LOW), (s, err)
+        fl_t = np.repeat(flr, H)
+        if not fl_t.any():
+            continue
+        flushes += 1
+        got_hi = rep.pool.ckpt()[blk].double().cpu().numpy().reshape(ns * H, dv, dk)[fl_t]
+        codes = rep.pool.ckpt_lo()[blk].cpu().numpy().reshape(ns * H, dv, dk)[fl_t][..., inv]
+        scales = rep.pool.ckpt_scale()[blk].cpu().numpy().reshape(ns * H, dv)[fl_t].astype(np.float64)
+        want_codes, want_e = formats.e4m3_quantize_rows(pre.C[fl_t])
+        if exact:
+            assert np.array_equal(got_hi, model.C[fl_t]), f"recurrence copy, step {s}"
+            assert np.array_equal(codes, want_codes), f"read-copy codes, step {s}"
+            assert np.array_equal(scales, np.ldexp(1.0, want_e)), f"read-copy scales, step {s}"
+            continue
+        if stochastic:
+            stats.add(got_hi, pre.C[fl_t], model.C[fl_t])
+        else:
+            x, ref = pre.C[fl_t], model.C[fl_t]
+            assert np.all(np.abs(got_hi - x) <= _f16_ulp(x) + 1e-5 * np.abs(x).max())
+            bad = got_hi != ref
+            n_rne += got_hi.size
+            n_rne_diff += int(bad.sum())
+            if bad.any():
+                # the other neighbour only where the fp64 value lies within
+                # the fp32 sums' error (bounded by 1e-5 of the tile's largest
+                # value, as above) of the midpoint between the two
+                scale = np.broadcast_to(np.abs(x).max(axis=(1, 2), keepdims=True), x.shape)[bad]
+                off = np.abs(x[bad] - 0.5 * (got_hi[bad] + ref[bad])) / scale
+                tie_off = max(tie_off, float(off.max()))
+        same_row = scales == np.ldexp(1.0, want_e)
+        scale_diff += int(np.sum(~same_row))
+        scale_n += same_row.size
+        cd = codes != want_codes
+        code_diff += int(np.sum(cd[same_row]))
+        code_n += int(np.sum(same_row)) * dk
+        # continue from the GPU's copies
+        model.C[fl_t] = got_hi
+        model.C_lo[fl_t] = formats.e4m3_dequantize_rows(codes, np.log2(scales).astype(np.int64))
+    assert int(rep.err.item()) == 0
+    assert flushes >= 2
+    if not exact:
+        say(f"[two-copy] {tag}: read-copy rows with another scale {scale_diff}/{scale_n}, "
+            f"codes differing {code_diff}/{code_n}, nearest-even recurrence values differing {n_rne_diff}/{n_rne} "
+            f"(at most {tie_off:.2e} of the tile's largest value from a tie)")
+        assert scale_diff <= max(1, scale_n // 1000) and code_diff <= max(2, code_n // 10000)
+        if stochastic:
+            stats.check(tag)
+        else:
+            assert n_rne_diff <= max(2, n_rne // 500) and tie_off < 1e-5, (n_rne_diff, tie_off)
+    say(f"[errors] {tag}: out={err:.3g}, flushes={flushes}")
+
+
+@pytest.mark.parametrize("stochastic", [True, False])
+def test_two_copy_f16_recurrence_exact(stochastic):
+    """fp16 recurrence copy + E4M3 read copy, dyadic inputs: both copies
+    bit-exact against the oracle, outputs from the read copy."""
+    _run_two_copy(B=4, H=8, L=4, steps=10, seed=31, exact=True, stochastic=stochastic)
+
+
+@pytest.mark.parametrize("stochastic", [True, False])
+def test_two_copy_f16_recurrence_generic(stochastic):
+    _run_two_copy(B=8, H=32, L=4, steps=10, seed=33, exact=False, stochastic=stochastic, sample=[1, 6])

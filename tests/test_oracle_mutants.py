@@ -155,6 +155,35 @@ def test_two_copy_mutant_is_caught(monkeypatch, kind):
     assert caught, f"two-copy mutant {kind} passed both pins"
 
 
+@pytest.mark.parametrize("kind", ["read_copy_from_rounded_recurrence", "recurrence_nearest_even",
+                                  "recurrence_words_of_step_zero"])
+def test_two_copy_store_mutant_is_caught(monkeypatch, kind):
+    """Mistakes in how a flush stores the two copies of an fp16 recurrence
+    copy must fail the two-copy pins."""
+    import numpy as np
+    import pins
+    from oracle import formats
+
+    def broken_store(self, mask, sr_step):
+        for t in np.nonzero(mask)[0]:
+            step = 0 if kind == "recurrence_words_of_step_zero" else sr_step
+            if kind == "read_copy_from_rounded_recurrence":
+                self.C[t] = formats.sr_f16(self.C[t].reshape(-1), formats.sr_words(
+                    self.key, step, self.tile_ids[t], self.dv * self.dk)).reshape(self.dv, self.dk)
+                self.C_lo[t] = formats.round_to(self.C[t], self.read_dtype)
+                continue
+            self.C_lo[t] = formats.round_to(self.C[t], self.read_dtype)
+            if kind == "recurrence_nearest_even":
+                self.C[t] = formats.round_to(self.C[t], "f16")
+            else:
+                self.C[t] = formats.sr_f16(self.C[t].reshape(-1), formats.sr_words(
+                    self.key, step, self.tile_ids[t], self.dv * self.dk)).reshape(self.dv, self.dk)
+
+    monkeypatch.setattr(oracle.TwoCopyReplayModel, "_store", broken_store)
+    with pytest.raises(AssertionError):
+        pins.pin_two_copy_f16_recurrence(oracle.get())
+
+
 # ---------------------------------------------- read-format mutants --
 def _format_mutants():
     import numpy as np
