@@ -289,11 +289,11 @@ def _inputs(cfg, B, n, dev, seed=11):
     return ios, keep
 
 
-def _layer_stack(cfg, B, n_layers, dev):
+def _layer_stack(cfg, B, n_layers, dev, reconstruct=False):
     import linear_attention_decode_replay_amd as rs
     from linear_attention_decode_replay_amd.state import DecodeLayer
     lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"],
-                   cfg["read"])
+                   cfg["read"], reconstruct=reconstruct)
     layers = []
     for _ in range(n_layers):
         d = DecodeLayer(lay, B, B, dev)
@@ -305,8 +305,9 @@ def _layer_stack(cfg, B, n_layers, dev):
 
 
 def suite_gdn_sweep(out, steps=32):
-    """Gated DeltaNet, 32 heads, 128x128, L=16: replay vs conventional kernel
-    time per launch over batch sizes, fp32 and fp16 state.  Reading a 1 GiB
+    """Gated DeltaNet, 32 heads, 128x128, L=16: replay (output-only route),
+    replay (state-reconstruction route) and conventional kernel time per
+    launch over batch sizes, fp32 and fp16 state.  Reading a 1 GiB
     buffer between launches (outside the timed events) evicts the state from
     the 256 MB Infinity Cache and the L2s without leaving dirty lines behind,
     so every launch is cold."""
@@ -318,13 +319,13 @@ def suite_gdn_sweep(out, steps=32):
             cfg = dict(WORKLOADS["gdn"], B=B, state=state)
             ios, keep = _inputs(cfg, B, 16, dev)
             res = {}
-            for kind in ("replay", "conventional"):
-                d = _layer_stack(cfg, B, 1, dev)[0]
+            for kind in ("replay", "reconstruct", "conventional"):
+                d = _layer_stack(cfg, B, 1, dev, reconstruct=kind == "reconstruct")[0]
                 times, nbytes = [], []
                 for s in range(16 + steps):
                     scrub.sum()
                     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    if kind == "replay":
+                    if kind != "conventional":
                         wp, fl = d.step(ios[s % 16], events=ev)
                         w, f = int(wp[0]), bool(fl[0])
                     else:
@@ -333,15 +334,17 @@ def suite_gdn_sweep(out, steps=32):
                     if s >= 16:
                         times.append(ev)
                         nbytes.append(step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, state, cfg["rec"],
-                                                 cfg["io"], w, f, kind))
+                                                 cfg["io"], w, f, "conventional" if kind == "conventional" else "replay"))
                 torch.cuda.synchronize()
                 us = float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e3
                 res[kind] = {"us": round(us, 2), "tbs": round(float(np.mean(nbytes)) / (us * 1e-6) / 1e12, 3)}
                 del d
             line = {"suite": "gdn_batch_sweep", "state": state, "batch": B, "L": 16,
                     "replay_us": res["replay"]["us"], "replay_tbs": res["replay"]["tbs"],
+                    "reconstruct_us": res["reconstruct"]["us"], "reconstruct_tbs": res["reconstruct"]["tbs"],
                     "conventional_us": res["conventional"]["us"], "conventional_tbs": res["conventional"]["tbs"],
-                    "speedup": round(res["conventional"]["us"] / res["replay"]["us"], 3)}
+                    "speedup": round(res["conventional"]["us"] / res["replay"]["us"], 3),
+                    "speedup_reconstruct": round(res["conventional"]["us"] / res["reconstruct"]["us"], 3)}
             print(json.dumps(line), file=out, flush=True)
             del ios, keep
             torch.cuda.empty_cache()

@@ -115,6 +115,16 @@ typedef enum {
  *               precision argument, derived") keeps the recurrence copy in
  *               FP16 with stochastic rounding, so that rounding enters the
  *               recurrence unbiased and once per window.
+ * gdn_route:    Gated DeltaNet only.  RS_GDN_OUTPUT_ONLY (the PR reviewer's
+ *               form): S_{t-1} q and S_{t-1} k come from C q, C k and the
+ *               scalars k_j . q, k_j . k of the buffered keys, and the state
+ *               is never formed on a non-flush step.  RS_GDN_RECONSTRUCT
+ *               (the PR's kernel, "Core concept": the state is rebuilt from
+ *               the checkpoint and the buffer): every step rebuilds
+ *               S_{t-1} = P C + sum_j p_j d_j k_j^T in registers and reads
+ *               both products from it.  Both routes store the same records
+ *               and checkpoints and agree in real arithmetic; the second
+ *               does w d_v d_k more multiply-adds per tile per step.
  * read_dtype:   -1 (or state_dtype) for a single checkpoint; for a
  *               two-precision checkpoint (blog "The precision argument,
  *               derived") RS_F16, RS_BF16 or RS_E4M3 over an RS_F32
@@ -148,10 +158,15 @@ typedef struct {
     int32_t n_groups; /* 0 (= n_heads): one key and query per head; else the
                          number of key groups, see below */
     int32_t state_rounding; /* RS_ROUND_NEAREST or RS_ROUND_STOCHASTIC, see below */
+    int32_t gdn_route;      /* RS_GDN_OUTPUT_ONLY or RS_GDN_RECONSTRUCT, see below */
 } rs_layer;
 
 /* Rounding of state stores (rs_layer.state_rounding). */
 typedef enum { RS_ROUND_NEAREST = 0, RS_ROUND_STOCHASTIC = 1 } rs_rounding;
+
+/* How a Gated DeltaNet non-flush step forms S_{t-1} q and S_{t-1} k
+ * (rs_layer.gdn_route; must be RS_GDN_OUTPUT_ONLY for Mamba-2). */
+typedef enum { RS_GDN_OUTPUT_ONLY = 0, RS_GDN_RECONSTRUCT = 1 } rs_gdn_route;
 
 /*
  * Byte layout of one paged block = the whole per-request state of one layer

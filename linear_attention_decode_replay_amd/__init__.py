@@ -28,6 +28,7 @@ MAMBA2, GDN = 0, 1
 F32, F16, BF16, E4M3 = 0, 1, 2, 3
 RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
 RS_ROUND_NEAREST, RS_ROUND_STOCHASTIC = 0, 1
+RS_GDN_OUTPUT_ONLY, RS_GDN_RECONSTRUCT = 0, 1
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -37,7 +38,8 @@ class RsLayer(_c.Structure):
     _fields_ = [("form", _c.c_int32), ("n_heads", _c.c_int32), ("d_v", _c.c_int32),
                 ("d_k", _c.c_int32), ("L", _c.c_int32), ("state_dtype", _c.c_int32),
                 ("record_dtype", _c.c_int32), ("io_dtype", _c.c_int32), ("read_dtype", _c.c_int32),
-                ("spec_T", _c.c_int32), ("n_groups", _c.c_int32), ("state_rounding", _c.c_int32)]
+                ("spec_T", _c.c_int32), ("n_groups", _c.c_int32), ("state_rounding", _c.c_int32),
+                ("gdn_route", _c.c_int32)]
 
 
 class RsBlockLayout(_c.Structure):
@@ -126,7 +128,7 @@ _DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "e4m3": E4M3}
 
 def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32",
           record_dtype="f16", io_dtype="bf16", read_dtype=None, spec_T: int = 0, n_groups: int = 0,
-          stochastic: bool = False) -> RsLayer:
+          stochastic: bool = False, reconstruct: bool = False) -> RsLayer:
     """read_dtype: None for a single checkpoint, "f16" / "bf16" / "e4m3" for
     a two-precision checkpoint (fp32 recurrence copy + read copy; E4M3 with a
     power-of-two scale per state row).  spec_T: 0 for standard decoding, T
@@ -134,11 +136,13 @@ def layer(form: int, n_heads: int, d_v: int, d_k: int, L: int, state_dtype="f32"
     key and query per head, else the number of key groups (q, k inputs then
     [rows, n_groups, d_k], one key record per group).  stochastic: store an
     fp16 state with stochastic rounding (the key and counter travel in the
-    batch: sr_key0/sr_key1, sr_step)."""
+    batch: sr_key0/sr_key1, sr_step).  reconstruct: Gated DeltaNet only, the
+    state-reconstruction route instead of the output-only one."""
     code = lambda d: _DT_CODE[d] if isinstance(d, str) else int(d)
     return RsLayer(int(form), int(n_heads), int(d_v), int(d_k), int(L), code(state_dtype),
                    code(record_dtype), code(io_dtype), -1 if read_dtype is None else code(read_dtype),
-                   int(spec_T), int(n_groups), RS_ROUND_STOCHASTIC if stochastic else RS_ROUND_NEAREST)
+                   int(spec_T), int(n_groups), RS_ROUND_STOCHASTIC if stochastic else RS_ROUND_NEAREST,
+                   RS_GDN_RECONSTRUCT if reconstruct else RS_GDN_OUTPUT_ONLY)
 
 
 def block_layout(lay: RsLayer) -> RsBlockLayout:

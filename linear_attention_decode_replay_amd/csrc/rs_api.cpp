@@ -65,6 +65,10 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
         return fail(RS_EINVAL, "unknown state rounding %d", L->state_rounding);
     if (L->state_rounding == RS_ROUND_STOCHASTIC && L->state_dtype != RS_F16)
         return fail(RS_EUNSUPPORTED, "stochastic rounding: an fp16 checkpoint / state (recurrence copy) only");
+    if (L->gdn_route != RS_GDN_OUTPUT_ONLY && L->gdn_route != RS_GDN_RECONSTRUCT)
+        return fail(RS_EINVAL, "unknown Gated DeltaNet route %d", L->gdn_route);
+    if (L->gdn_route == RS_GDN_RECONSTRUCT && L->form != RS_GDN)
+        return fail(RS_EINVAL, "the state-reconstruction route is a Gated DeltaNet option");
     if (L->n_groups < 0 || (L->n_groups > 0 && L->n_heads % L->n_groups != 0))
         return fail(RS_EINVAL, "n_groups (%d) must be 0 or divide n_heads (%d)", L->n_groups, L->n_heads);
     if (L->spec_T != 0 && groups_of(*L) != L->n_heads)
@@ -201,6 +205,7 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.slots = lay.slots;
     p.heads_per_group = L.n_heads / groups_of(L);
     p.sr = L.state_rounding == RS_ROUND_STOCHASTIC;
+    p.reconstruct = L.gdn_route == RS_GDN_RECONSTRUCT;
     p.sr_key0 = b.sr_key0;
     p.sr_key1 = b.sr_key1;
     p.sr_step = b.sr_step;

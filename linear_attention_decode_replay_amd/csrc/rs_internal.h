@@ -34,6 +34,7 @@ struct StepParams {
     int32_t n_rows, n_heads, L, slots;
     int32_t heads_per_group;   // heads sharing one key / query (1: per-head keys)
     int32_t sr;                // stochastic rounding of 16-bit state stores
+    int32_t reconstruct;       // Gated DeltaNet: rebuild S_{t-1} on every step
     uint64_t sr_key0, sr_key1, sr_step;
     // speculative verify / commit
     int32_t spec_T;

@@ -654,7 +654,9 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // i < EPC, EPC = recurrence-copy elements per 16 bytes).  q, k and buffered
 // keys are read in that order too, so every dot product is unchanged.  With
 // a single checkpoint HPC = 1 and the order is the natural one.
-template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL>
+// RECON (Gated DeltaNet only): the state-reconstruction route, a separate
+// instantiation so that the output-only route keeps its register budget.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false>
 __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(const StepParams p) {
     using T = Tile<DV, DK, TL, SPLIT>;
     using S = typename TS::S;
@@ -747,13 +749,18 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
 
     decay_weights(lam_j, s.e, s.sc, w, FORM == kMamba2 ? lam : 0.0f);
 
+    // Gated DeltaNet, state-reconstruction route: S_{t-1} is rebuilt in
+    // registers below, so no record dot products are needed.
+    constexpr bool recon = FORM == kGdn && RECON;
+    const int wd = recon ? 0 : w;  // records whose dot products are taken
+
     // Record dot products: lane group rg takes records rg, rg + RPP, ...;
-    // index w stands for the current token (k . q).
-    const int rounds = (w + RPP) / RPP;
+    // index wd stands for the current token (k . q).
+    const int rounds = (wd + RPP) / RPP;
     for (int it = 0; it < rounds; ++it) {
         const int j = it * RPP + rg;
         float kj[VEC];
-        if (j < w) {
+        if (j < wd) {
 #pragma unroll
             for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(s.k + (int64_t)j * DK + col(h), kj + h * EPC);
         } else {
@@ -768,8 +775,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
         }
         pq = group_sum<LPR>(pq);
         if constexpr (FORM == kGdn) pk = group_sum<LPR>(pk);
-        if (cc == 0 && j <= w) {
-            if (j < w) {
+        if (cc == 0 && j <= wd) {
+            if (j < wd) {
                 s.cq[j] = pq;
                 if constexpr (FORM == kGdn) s.ck[j] = pk;
             } else {
@@ -789,6 +796,26 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
 #pragma unroll
         for (int r = 0; r < NR; ++r) unpack_n<TL, VEC>(&cb[r * HPC], cf[r]);
     }
+    if constexpr (FORM == kGdn) {
+        if constexpr (recon) {  // S_{t-1} = G C + sum_j e_j d_j k_j^T
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] *= G;
+            for (int j = 0; j < w; ++j) {
+                float kj[VEC];
+                load_f<TR, VEC>(s.k + (int64_t)j * DK + col0, kj);
+                const float ej = s.e[j];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+                }
+            }
+        }
+    }
+    const float gs = recon ? 1.0f : G;  // the checkpoint's weight in the products below
     float acc[NV];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -802,11 +829,11 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
             if constexpr (SC) a = fl ? a : rsc[r] * a;
             acc[r] = G * a;
         } else {
-            acc[2 * r] = G * a;
-            acc[2 * r + 1] = G * b;
+            acc[2 * r] = gs * a;
+            acc[2 * r + 1] = gs * b;
         }
     }
-    for (int j = cc; j < w; j += LPR) {
+    for (int j = cc; j < wd; j += LPR) {
         const float wq = s.e[j] * s.cq[j];
         const float wk = FORM == kGdn ? s.e[j] * s.ck[j] : 0.f;
 #pragma unroll
@@ -871,7 +898,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     //   Mamba-2:  C' = G C + sum_j e_j x_j k_j^T + v k^T
     //   GDN:      C' = alpha P C + sum_j alpha p_j d_j k_j^T + d k^T
     if constexpr (FORM == kGdn) __syncthreads();  // d in LDS
-    const float gc = FORM == kMamba2 ? G : alpha * G;
+    // (reconstruction route: the registers already hold S_{t-1}, records folded)
+    const float gc = FORM == kMamba2 ? G : alpha * gs;
     const float ge = FORM == kMamba2 ? 1.0f : alpha;
     const float* u = FORM == kMamba2 ? s.v : s.u;
 #pragma unroll
@@ -880,7 +908,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
 #pragma unroll
         for (int c = 0; c < VEC; ++c) cf[r][c] = gc * cf[r][c] + ur * kv[c];
     }
-    for (int j = 0; j < w; ++j) {
+    for (int j = 0; j < wd; ++j) {
         float kj[VEC];
         const R* kr = s.k + (int64_t)j * DK + col0;
 #pragma unroll
@@ -1756,6 +1784,14 @@ struct Dispatch {
                                         // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
                                         constexpr int SP = split_for<DV, DK>();
                                         const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                        if constexpr (FORM == kGdn) {
+                                            if (p->reconstruct) {
+                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, true>),
+                                                                   grid<SP>(), dim3(Tile<DV, DK, TL, SP>::NT), lds,
+                                                                   stream, *p);
+                                                return;
+                                            }
+                                        }
                                         hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
                                                            dim3(Tile<DV, DK, TL, SP>::NT), lds, stream, *p);
                                     }

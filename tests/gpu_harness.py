@@ -73,12 +73,14 @@ class Case:
     force_every: int = 0             # > 0: force a flush on row 0 every n steps
     read_dt: str | None = None       # two-precision checkpoint: read copy dtype
     groups: int = 0                  # key groups (0: a key and query per head)
+    reconstruct: bool = False        # Gated DeltaNet: the state-reconstruction route
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"{f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
-                f"strided={self.strided} pad={self.pad_rows} groups={self.groups} seed={self.seed}")
+                f"strided={self.strided} pad={self.pad_rows} groups={self.groups} "
+                f"route={'reconstruct' if self.reconstruct else 'output-only'} seed={self.seed}")
 
 
 def grouped(tok, hg: int):
@@ -114,7 +116,8 @@ def run_case(c: Case, dev="cuda") -> dict:
     Returns the worst errors seen; raises AssertionError on any bit-exact
     mismatch (cursor, flush flag, copied record fields, untouched pad rows)."""
     say(f"[case] {c.name()}")
-    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt, 0, c.groups)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt, 0, c.groups,
+                   reconstruct=c.reconstruct)
     hg = c.H // c.groups if c.groups else 1
     n_blocks = c.n_blocks or (c.B + 3)
     rep = DecodeLayer(lay, c.B, n_blocks, dev)

@@ -342,9 +342,9 @@ def test_stochastic_rounding_layers_accepted():
 def test_batch_struct_carries_key_and_counter():
     b = rs.RsBatch(4, 0, 4, None, None, None, None, None, None, 2**64 - 1, 5, 2**63 + 7)
     assert (b.sr_key0, b.sr_key1, b.sr_step) == (2**64 - 1, 5, 2**63 + 7)
-    # 2 int32 + int64 + 6 pointers + 3 uint64; 12 int32
+    # 2 int32 + int64 + 6 pointers + 3 uint64; 13 int32
     assert ctypes.sizeof(rs.RsBatch) == 88
-    assert ctypes.sizeof(rs.RsLayer) == 48
+    assert ctypes.sizeof(rs.RsLayer) == 52
 
 
 @pytest.mark.parametrize("state,read", [("f32", "f16"), ("f32", "bf16"), ("f32", "e4m3"), ("f16", "e4m3")])
@@ -358,3 +358,16 @@ def test_read_copy_columns_permutation(state, read):
     m = 4 if state == "f32" else 2
     run = 16 // m
     assert all(cols[i + 1] == cols[i] + 1 for i in range(128) if (i + 1) % run and i + 1 < 128)
+
+
+@pytest.mark.parametrize("route,form,code", [
+    (rs.RS_GDN_RECONSTRUCT, rs.GDN, rs.RS_OK), (rs.RS_GDN_OUTPUT_ONLY, rs.GDN, rs.RS_OK),
+    (rs.RS_GDN_RECONSTRUCT, rs.MAMBA2, rs.RS_EINVAL), (2, rs.GDN, rs.RS_EINVAL), (-1, rs.GDN, rs.RS_EINVAL),
+])
+def test_gdn_route_validation(route, form, code):
+    lay = rs.layer(form, 32, 128, 128, 16, "f32", "f16", "bf16")
+    lay.gdn_route = route
+    assert rs.layer_supported(lay) == code
+    if code == rs.RS_OK:   # the route changes no layout
+        assert rs.block_layout(lay).block_bytes == rs.block_layout(rs.layer(form, 32, 128, 128, 16, "f32", "f16",
+                                                                            "bf16")).block_bytes

@@ -177,3 +177,27 @@ def test_grouped_keys_gdn_production():
     """Gated DeltaNet 128x128 with 2 value heads per key head."""
     _go(Case(form=rs.GDN, B=16, H=32, groups=16, dv=128, dk=128, L=16, steps=20, rec_dt="f16", io_dt="bf16",
              sample=[0, 15], seed=74))
+
+
+# ------------------------------------------ GDN state-reconstruction route --
+@pytest.mark.parametrize("L", [1, 4, 16])
+def test_gdn_reconstruct_tiny(L):
+    """The PR's route: every step rebuilds S_{t-1} from the checkpoint and
+    the buffered (d, k, g) records; outputs, records and checkpoints against
+    the conventional recurrence, like the output-only route."""
+    err = _go(Case(form=rs.GDN, L=L, steps=max(3 * L + 5, 24), reconstruct=True, seed=70 + L))
+    assert err["flushes"] >= 2
+
+
+@pytest.mark.parametrize("sdt,rdt,io", [("f16", "f16", "bf16"), ("f32", "f16", "f16")])
+def test_gdn_reconstruct_dtypes_strided(sdt, rdt, io):
+    _go(Case(form=rs.GDN, B=6, pad_rows=[2], n_blocks=9, strided=True, force_every=5, state_dt=sdt,
+             rec_dt=rdt, io_dt=io, reconstruct=True, seed=75))
+
+
+@pytest.mark.parametrize("state_dt", ["f32", "f16"])
+def test_gdn_reconstruct_production_shape(state_dt):
+    """32 heads, 128 x 128 (split over two workgroups per tile), batch 64,
+    L = 16, 20 steps with one flush; 3 rows sampled."""
+    _go(Case(form=rs.GDN, B=64, H=32, dv=128, dk=128, L=16, steps=20, state_dt=state_dt, rec_dt="f16",
+             io_dt="bf16", sample=[0, 31, 63], reconstruct=True, seed=77))
