@@ -181,11 +181,13 @@ typedef enum { RS_GDN_OUTPUT_ONLY = 0, RS_GDN_RECONSTRUCT = 1 } rs_gdn_route;
  *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
  *                                   ckpt_lo_off is 0 otherwise), each row of
  *                                   d_k elements in lane order: with n read
- *                                   elements per 16 bytes, stored position p
- *                                   (chunk c = p / n, e = p mod n) holds
- *                                   column 4 (c + (d_k / n) floor(e / 4)) +
- *                                   e mod 4, so that both copies are read
- *                                   and written with contiguous accesses
+ *                                   and m recurrence-copy elements per 16
+ *                                   bytes (m = 4 for fp32, 8 for fp16),
+ *                                   stored position p (chunk c = p / n,
+ *                                   e = p mod n) holds column
+ *                                   m (c + (d_k / n) floor(e / m)) + e mod m,
+ *                                   so that both copies are read and
+ *                                   written with contiguous accesses
  *   ckpt_sc  [n_heads][d_v]         fp32 row scales of an RS_E4M3 read copy
  *                                   (ckpt_scale_off is 0 otherwise)
  * slots = L - 1 (a speculative layer: slots = L).  block_bytes is a multiple
@@ -226,10 +228,29 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               rs_meta_advance).  Passing it as the next step's write_pos
  *               lets a caller skip the per-step host -> device copy while
  *               the batch is unchanged.  Must not alias write_pos.
+ *   flush_hint  replay_decode_step with a two-precision checkpoint only
+ *               (other layers ignore it and process every row): what the
+ *               caller knows of this step's flushing rows (rs_flush_hint).
+ *               RS_FLUSH_UNKNOWN (0) runs one kernel over all rows.
+ *               RS_FLUSH_NONE promises that no row flushes and runs a kernel
+ *               built without the fold (fewer registers, more waves in
+ *               flight on the small read copy); RS_FLUSH_ALL promises that
+ *               every non-padding row flushes; RS_FLUSH_MIXED runs the
+ *               no-fold kernel over the rows that do not flush and then the
+ *               full kernel over those that do.  A row that breaks a
+ *               promise is skipped and counted in err_count (never computed
+ *               wrongly).
  */
+typedef enum {
+    RS_FLUSH_UNKNOWN = 0,
+    RS_FLUSH_NONE = 1,
+    RS_FLUSH_ALL = 2,
+    RS_FLUSH_MIXED = 3
+} rs_flush_hint;
+
 typedef struct {
     int32_t n_rows;
-    int32_t reserved;
+    int32_t flush_hint;
     int64_t n_blocks;
     void* pool;
     const int32_t* block_table;

@@ -29,6 +29,7 @@ F32, F16, BF16, E4M3 = 0, 1, 2, 3
 RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
 RS_ROUND_NEAREST, RS_ROUND_STOCHASTIC = 0, 1
 RS_GDN_OUTPUT_ONLY, RS_GDN_RECONSTRUCT = 0, 1
+RS_FLUSH_UNKNOWN, RS_FLUSH_NONE, RS_FLUSH_ALL, RS_FLUSH_MIXED = 0, 1, 2, 3
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -49,7 +50,7 @@ class RsBlockLayout(_c.Structure):
 
 
 class RsBatch(_c.Structure):
-    _fields_ = [("n_rows", _c.c_int32), ("reserved", _c.c_int32), ("n_blocks", _c.c_int64),
+    _fields_ = [("n_rows", _c.c_int32), ("flush_hint", _c.c_int32), ("n_blocks", _c.c_int64),
                 ("pool", _vp), ("block_table", _vp), ("write_pos", _vp), ("flush", _vp),
                 ("err_count", _vp), ("next_write_pos", _vp), ("sr_key0", _c.c_uint64),
                 ("sr_key1", _c.c_uint64), ("sr_step", _c.c_uint64)]

@@ -35,6 +35,7 @@ struct StepParams {
     int32_t heads_per_group;   // heads sharing one key / query (1: per-head keys)
     int32_t sr;                // stochastic rounding of 16-bit state stores
     int32_t reconstruct;       // Gated DeltaNet: rebuild S_{t-1} on every step
+    int32_t flush_hint;        // rs_flush_hint of the launch (see k_replay_step)
     uint64_t sr_key0, sr_key1, sr_step;
     // speculative verify / commit
     int32_t spec_T;

@@ -656,7 +656,15 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // a single checkpoint HPC = 1 and the order is the natural one.
 // RECON (Gated DeltaNet only): the state-reconstruction route, a separate
 // instantiation so that the output-only route keeps its register budget.
-template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false>
+// ROWS: kAllRows, or kNonFlushRows: an instantiation without the fold, which
+// carries none of the flush path's registers and so keeps more waves in
+// flight.  The caller's flush hint picks the kernels (RS_FLUSH_NONE: the
+// second alone; RS_FLUSH_MIXED: the second over the rows that do not flush,
+// then the first over those that do) and decides what a row that breaks it
+// means: skipped, and counted as an error.
+constexpr int kAllRows = 0, kNonFlushRows = 1;
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false,
+          int ROWS = kAllRows>
 __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(const StepParams p) {
     using T = Tile<DV, DK, TL, SPLIT>;
     using S = typename TS::S;
@@ -681,9 +689,23 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     const bool pad = blk < 0;
     const bool bad = !pad && (blk >= p.n_blocks || w < 0 || w > p.slots);
     if (pad || bad) {
-        if (bad) count_error(p, id);
+        // a pair of launches counts a bad tile once, in the first
+        if (bad && !(ROWS == kAllRows && p.flush_hint == RS_FLUSH_MIXED)) count_error(p, id);
         return;
     }
+    const bool fl_row = (w == p.slots) || flag;
+    if constexpr (ROWS == kNonFlushRows) {
+        if (fl_row) {
+            if (p.flush_hint == RS_FLUSH_NONE) count_error(p, id);  // the hint was wrong
+            return;
+        }
+    } else {
+        if (!fl_row && (p.flush_hint == RS_FLUSH_ALL || p.flush_hint == RS_FLUSH_MIXED)) {
+            if (p.flush_hint == RS_FLUSH_ALL) count_error(p, id);
+            return;
+        }
+    }
+    const bool fl = ROWS == kNonFlushRows ? false : fl_row;
 
     const int tid = threadIdx.x;
     const int cc = tid % LPR;  // column chunk
@@ -704,7 +726,6 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
     const float lam = p.lam[id.tile];
-    const bool fl = (w == p.slots) || flag;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
@@ -1784,16 +1805,25 @@ struct Dispatch {
                                         // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
                                         constexpr int SP = split_for<DV, DK>();
                                         const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                        const dim3 block(Tile<DV, DK, TL, SP>::NT);
                                         if constexpr (FORM == kGdn) {
-                                            if (p->reconstruct) {
+                                            if (p->reconstruct) {  // (the hint is cleared for it)
                                                 hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, true>),
-                                                                   grid<SP>(), dim3(Tile<DV, DK, TL, SP>::NT), lds,
-                                                                   stream, *p);
+                                                                   grid<SP>(), block, lds, stream, *p);
                                                 return;
                                             }
                                         }
-                                        hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
-                                                           dim3(Tile<DV, DK, TL, SP>::NT), lds, stream, *p);
+                                        // (the hint is cleared unless the checkpoint has two copies)
+                                        const int hint = p->flush_hint;
+                                        if constexpr (TWO) {
+                                            if (hint == RS_FLUSH_NONE || hint == RS_FLUSH_MIXED)
+                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
+                                                                                  kNonFlushRows>),
+                                                                   grid<SP>(), block, lds, stream, *p);
+                                        }
+                                        if (hint != RS_FLUSH_NONE)
+                                            hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
+                                                               block, lds, stream, *p);
                                     }
                                 });
                             }

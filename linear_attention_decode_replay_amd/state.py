@@ -26,9 +26,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (Pool, RsLayer, conventional_decode_step, make_batch, replay_decode_step,
-               replay_flush, replay_spec_commit, replay_spec_verify, replay_state_reset, rs_meta_advance,
-               rs_meta_step)
+from . import (RS_FLUSH_ALL, RS_FLUSH_MIXED, RS_FLUSH_NONE, RS_FLUSH_UNKNOWN, Pool, RsLayer,
+               conventional_decode_step, make_batch, replay_decode_step, replay_flush, replay_spec_commit,
+               replay_spec_verify, replay_state_reset, rs_meta_advance, rs_meta_step)
 
 
 def _layout(n: int):
@@ -79,6 +79,9 @@ class DecodeLayer:
                       for i in (0, 1)]
         # stochastic rounding: the counter's first word, one value per launch
         self.sr_step = 0
+        # tell the library which rows flush (it then runs the kernel built
+        # without the fold wherever it can); False: RS_FLUSH_UNKNOWN always
+        self.flush_hints = True
         self._cur = 0
         self._stages = [_Stage(n) for _ in range(staging)]
         self._next = 0
@@ -133,13 +136,23 @@ class DecodeLayer:
             st.event.record(stream)
         self.uploads += 1
 
-    def _batch(self):
+    def _batch(self, hint=RS_FLUSH_UNKNOWN):
         """The batch struct for the next launch, stamped with a fresh
-        stochastic-rounding counter word."""
+        stochastic-rounding counter word and the flush hint."""
         b = self.batch[self._cur]
         b.sr_step = self.sr_step
+        b.flush_hint = hint
         self.sr_step += 1
         return b
+
+    def _hint(self, fl) -> int:
+        live = self.live()
+        if not self.flush_hints or not live.any():
+            return RS_FLUSH_UNKNOWN
+        n = int(np.count_nonzero(np.asarray(fl)[live]))
+        if n == 0:
+            return RS_FLUSH_NONE
+        return RS_FLUSH_ALL if n == int(live.sum()) else RS_FLUSH_MIXED
 
     # ----------------------------------------------------------------- steps --
     def step(self, io, force: np.ndarray | None = None, stream=None, events=None):
@@ -159,7 +172,7 @@ class DecodeLayer:
             self._dirty = False
         if events:
             events[0].record(stream)
-        replay_decode_step(self.layer, self._batch(), io, stream)
+        replay_decode_step(self.layer, self._batch(self._hint(fl)), io, stream)
         if events:
             events[1].record(stream)
         self._cur ^= 1

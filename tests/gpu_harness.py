@@ -74,13 +74,15 @@ class Case:
     read_dt: str | None = None       # two-precision checkpoint: read copy dtype
     groups: int = 0                  # key groups (0: a key and query per head)
     reconstruct: bool = False        # Gated DeltaNet: the state-reconstruction route
+    flush_hints: bool = True         # pass the host's flush hint (False: RS_FLUSH_UNKNOWN)
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"{f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
                 f"strided={self.strided} pad={self.pad_rows} groups={self.groups} "
-                f"route={'reconstruct' if self.reconstruct else 'output-only'} seed={self.seed}")
+                f"route={'reconstruct' if self.reconstruct else 'output-only'} hints={self.flush_hints} "
+                f"seed={self.seed}")
 
 
 def grouped(tok, hg: int):
@@ -121,6 +123,7 @@ def run_case(c: Case, dev="cuda") -> dict:
     hg = c.H // c.groups if c.groups else 1
     n_blocks = c.n_blocks or (c.B + 3)
     rep = DecodeLayer(lay, c.B, n_blocks, dev)
+    rep.flush_hints = c.flush_hints
     conv = DecodeLayer(lay, c.B, n_blocks, dev) if c.check_conventional else None
     for d in (rep, conv):
         if d is not None:

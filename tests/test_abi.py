@@ -371,3 +371,15 @@ def test_gdn_route_validation(route, form, code):
     if code == rs.RS_OK:   # the route changes no layout
         assert rs.block_layout(lay).block_bytes == rs.block_layout(rs.layer(form, 32, 128, 128, 16, "f32", "f16",
                                                                             "bf16")).block_bytes
+
+
+def test_flush_hint_validation():
+    layer = _c2()
+    buf = (ctypes.c_uint8 * 512)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    io = rs.RsStepIO(base, base, base, 128 * 128, 128, 128 * 128, 128, 128 * 64, 64, base, None, base)
+    for bad in (-1, 4):
+        batch = rs.RsBatch(4, bad, 4, base, base, base, None, None)
+        with pytest.raises(rs.ReplaySSMError) as e:
+            rs.replay_decode_step(layer, batch, io, stream=0)
+        assert e.value.code == rs.RS_EINVAL and "flush_hint" in rs.last_error()

@@ -87,12 +87,15 @@ TWO_COPY_TOL = 1e-3
 
 @pytest.mark.parametrize("read_dt", ["f16", "bf16"])
 @pytest.mark.parametrize("rec_dt,io", [("f32", "f32"), ("f16", "bf16")])
-def test_two_precision_checkpoint_tiny(read_dt, rec_dt, io):
+@pytest.mark.parametrize("hints", [True, False])
+def test_two_precision_checkpoint_tiny(read_dt, rec_dt, io, hints):
     """fp32 recurrence copy + fp16/bf16 read copy (Mamba-2), tiny heads with
     strided inputs, padding and forced flushes; compared with the oracle's
-    two-copy model (outputs) and its exact recurrence (flushed checkpoints)."""
+    two-copy model (outputs) and its exact recurrence (flushed checkpoints).
+    With the host's flush hints, non-flush steps run the kernel without the
+    fold and forced-flush steps a pair of launches; without, one kernel."""
     err = run_case(Case(B=5, pad_rows=[3], strided=True, force_every=5, rec_dt=rec_dt, io_dt=io,
-                        read_dt=read_dt, seed=60))
+                        read_dt=read_dt, seed=60, flush_hints=hints))
     _check_two_precision(err, read_dt)
 
 
@@ -201,3 +204,49 @@ def test_gdn_reconstruct_production_shape(state_dt):
     L = 16, 20 steps with one flush; 3 rows sampled."""
     _go(Case(form=rs.GDN, B=64, H=32, dv=128, dk=128, L=16, steps=20, state_dt=state_dt, rec_dt="f16",
              io_dt="bf16", sample=[0, 31, 63], reconstruct=True, seed=77))
+
+
+# ------------------------------------------------------------- flush hints --
+@pytest.mark.parametrize("hint", ["none", "all"])
+def test_flush_hint_broken_promise(hint):
+    """A row that breaks the caller's flush hint is skipped (its outputs and
+    checkpoint untouched) and counted once per tile; the other rows are
+    computed as without a hint."""
+    import numpy as np
+    import torch
+    import workloads
+    from gpu_harness import say
+    from linear_attention_decode_replay_amd.state import DecodeLayer
+
+    H, L = 4, 4
+    lay = rs.layer(rs.MAMBA2, H, 16, 32, L, "f32", "f32", "f32", "f16")   # hints apply to two-copy layers
+    tok = workloads.tokens(rs.MAMBA2, 5, 0, 3, H, 16, 32, "f32")
+    outs, ckpts, errs = [], [], []
+    for use in (rs.RS_FLUSH_UNKNOWN, rs.RS_FLUSH_NONE if hint == "none" else rs.RS_FLUSH_ALL):
+        d = DecodeLayer(lay, 3, 3, "cuda")
+        d.pool.raw.zero_()              # zero records in the slots the rows read
+        for b in range(3):
+            d.assign(b, b)
+        d.reset_rows(range(3))
+        d.anchor[:] = [L - 1, 1, 1]     # row 0 flushes this step, rows 1 and 2 do not
+        d._dirty = True
+        d._hint = lambda fl, use=use: use
+        out = torch.full((3, H, 16), float("nan"), device="cuda")
+        _, fl = d.step(rs.make_io(tok.q.cuda(), tok.k.cuda(), tok.v.cuda(), tok.lam.cuda(), out))
+        assert list(fl) == [1, 0, 0]
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+        ckpts.append(d.pool.ckpt()[:3].cpu())
+        errs.append(int(d.err.item()))
+    ref, got = outs
+    assert errs[0] == 0
+    broken = [0] if hint == "none" else [1, 2]
+    kept = [b for b in range(3) if b not in broken]
+    assert errs[1] == H * len(broken)
+    assert torch.isnan(got[broken]).all()
+    assert torch.allclose(got[kept], ref[kept], rtol=1e-6, atol=1e-6)
+    if hint == "none":  # the skipped flush left the zero checkpoint alone
+        assert torch.count_nonzero(ckpts[1][0]) == 0 and torch.count_nonzero(ckpts[0][0]) > 0
+    else:
+        assert torch.allclose(ckpts[1][0], ckpts[0][0], rtol=1e-6, atol=1e-7)
+    say(f"[hint] broken '{hint}' promise: {errs[1]} tiles skipped and counted")
