@@ -409,7 +409,7 @@ __device__ __forceinline__ void group_max(float& x) {
 // A (row, head) tile of d_v x d_k state is covered by SPLIT workgroups, each
 // owning DVW = d_v / SPLIT consecutive state rows (everything the step does is
 // row-local except the record dot products, which each workgroup recomputes).
-template <int DV, int DK, class TS, int SPLIT>
+template <int DV, int DK, class TS, int SPLIT, int PER_ = 0>
 struct Tile {
     using S = typename TS::S;
     static constexpr int DVW = DV / SPLIT;                     // state rows per workgroup
@@ -417,8 +417,8 @@ struct Tile {
     static constexpr int LPR = DK / VEC;                       // lanes per state row
     static constexpr int LOADS = DVW * LPR;                    // 16-B chunks per workgroup
     // at least 4 chunks per thread, 2 for an E4M3 read copy (whose flush rows
-    // hold 4 fp32 recurrence-copy chunks per code chunk)
-    static constexpr int PER = kScaled<TS> ? 2 : 4;
+    // hold 4 fp32 recurrence-copy chunks per code chunk), or PER_ if given
+    static constexpr int PER = PER_ ? PER_ : (kScaled<TS> ? 2 : 4);
     static constexpr int NT = LOADS / PER >= 256 ? 256 : (LOADS / PER >= 128 ? 128 : 64);
     static constexpr int RPP = NT / LPR;                       // rows per pass
     static constexpr int NR = DVW / RPP;                       // passes per thread
@@ -663,10 +663,18 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // then the first over those that do) and decides what a row that breaks it
 // means: skipped, and counted as an error.
 constexpr int kAllRows = 0, kNonFlushRows = 1;
+// The instantiation without the fold gives each thread 4 read-copy chunks
+// (an E4M3 tile then takes 128 threads instead of 256): the fold's registers
+// are gone, and twice the bytes per wave are in flight.
+template <int DV, int DK, class TL, int SPLIT, int ROWS>
+using StepTile = Tile<DV, DK, TL, SPLIT, ROWS == kNonFlushRows ? 4 : 0>;
+
 template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false,
           int ROWS = kAllRows>
-__global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(const StepParams p) {
-    using T = Tile<DV, DK, TL, SPLIT>;
+__global__ __launch_bounds__((StepTile<DV, DK, TL, SPLIT, ROWS>::NT),
+                             1)
+void k_replay_step(const StepParams p) {
+    using T = StepTile<DV, DK, TL, SPLIT, ROWS>;
     using S = typename TS::S;
     using RL = typename TL::S;
     using R = typename TR::S;
@@ -740,6 +748,20 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
         load_f<TI, EPC>(kp + col(h), kv + h * EPC);
     }
     const float vi = to_f<TI>(vp[min(tid, DVW - 1)]);
+    // a non-flush row's record: log-decay, key (one per group), value
+    // (Mamba-2; Gated DeltaNet stores its corrected value with the output)
+    auto append_record = [&](int slot) {
+        if (id.part == 0) {
+            if (tid == 0) rl[slot] = lam;
+            if (rg == 0 && key_owner) {
+                R* kd = rk + (int64_t)slot * DK + col0;
+#pragma unroll
+                for (int h = 0; h < HPC; ++h) store_f<TR, EPC>(kd + EPC * LPR * h, kv + h * EPC);
+            }
+        }
+        if constexpr (FORM == kMamba2)
+            if (tid < DVW) rx[(int64_t)slot * DV + tid] = from_f<TR>(vi);
+    };
     float lam_j = 0.f;
     if (w > 0) lam_j = rl[min(tid, w - 1)];
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
@@ -766,6 +788,15 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
 
     if (tid < DVW) s.v[tid] = vi;
     rec.commit(rk, rx, s.k, s.x);
+    // The kernel without the fold appends the record (slot w, which this
+    // step does not read) and takes this lane's share of k . q now, so that
+    // k is not held through the checkpoint products.
+    float kq_lane = 0.f;
+    if constexpr (ROWS == kNonFlushRows) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) kq_lane += kv[c] * qv[c];
+        append_record(w);
+    }
     __syncthreads();
 
     decay_weights(lam_j, s.e, s.sc, w, FORM == kMamba2 ? lam : 0.0f);
@@ -784,15 +815,19 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
         if (j < wd) {
 #pragma unroll
             for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(s.k + (int64_t)j * DK + col(h), kj + h * EPC);
-        } else {
+        } else if constexpr (ROWS != kNonFlushRows) {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) kj[c] = kv[c];
         }
         float pq = 0.f, pk = 0.f;
+        if (ROWS == kNonFlushRows && j >= wd) {
+            pq = kq_lane;
+        } else {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            pq += kj[c] * qv[c];
-            if constexpr (FORM == kGdn) pk += kj[c] * kv[c];
+            for (int c = 0; c < VEC; ++c) {
+                pq += kj[c] * qv[c];
+                if constexpr (FORM == kGdn) pk += kj[c] * kv[c];
+            }
         }
         pq = group_sum<LPR>(pq);
         if constexpr (FORM == kGdn) pk = group_sum<LPR>(pk);
@@ -813,7 +848,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     if (!TWO || fl) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) unpack_n<TS, VEC>(&cb[r * HPC], cf[r]);
-    } else {
+    } else if constexpr (!(ROWS == kNonFlushRows && SC)) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) unpack_n<TL, VEC>(&cb[r * HPC], cf[r]);
     }
@@ -841,10 +876,22 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         float a = 0.f, b = 0.f;
+        if constexpr (ROWS == kNonFlushRows && SC) {
+            // codes widened four at a time straight into the product, so
+            // that the tile is never held as floats
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            a += cf[r][c] * qv[c];
-            if constexpr (FORM == kGdn) b += cf[r][c] * kv[c];
+            for (int i = 0; i < VEC / 4; ++i) {
+                const int word = (int)cb[r * HPC + i / 4][i % 4];
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+                a += lo[0] * qv[4 * i] + lo[1] * qv[4 * i + 1] + hi[0] * qv[4 * i + 2] + hi[1] * qv[4 * i + 3];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                a += cf[r][c] * qv[c];
+                if constexpr (FORM == kGdn) b += cf[r][c] * kv[c];
+            }
         }
         if constexpr (FORM == kMamba2) {
             if constexpr (SC) a = fl ? a : rsc[r] * a;
@@ -901,16 +948,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_step(c
     }
 
     if (!fl) {  // uniform across the workgroup
-        if (id.part == 0) {
-            if (tid == 0) rl[w] = lam;
-            if (rg == 0 && key_owner) {
-                R* kd = rk + (int64_t)w * DK + col0;
-#pragma unroll
-                for (int h = 0; h < HPC; ++h) store_f<TR, EPC>(kd + EPC * LPR * h, kv + h * EPC);
-            }
-        }
-        if constexpr (FORM == kMamba2)
-            if (tid < DVW) rx[(int64_t)w * DV + tid] = from_f<TR>(vi);
+        if constexpr (ROWS != kNonFlushRows) append_record(w);  // (else appended above)
         return;
     }
 
@@ -1819,7 +1857,9 @@ struct Dispatch {
                                             if (hint == RS_FLUSH_NONE || hint == RS_FLUSH_MIXED)
                                                 hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
                                                                                   kNonFlushRows>),
-                                                                   grid<SP>(), block, lds, stream, *p);
+                                                                   grid<SP>(),
+                                                                   dim3(StepTile<DV, DK, TL, SP, kNonFlushRows>::NT),
+                                                                   lds, stream, *p);
                                         }
                                         if (hint != RS_FLUSH_NONE)
                                             hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
