@@ -172,6 +172,21 @@ def cpu_baseline(cfg, n_steps=None, rows=None, min_seconds=10.0, max_windows=32)
     for _ in range(n_win):
         window(conv, False)
     t_conv = time.perf_counter() - t0
+    # the same route on one thread, over a sixteenth of the rows (one window)
+    b1 = max(1, B // 16)
+    one = (oracle.TwoCopyReplayModel(b1, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["read"]) if cfg.get("read")
+           else oracle.ReplayModel(cfg["form"], b1, cfg["H"], cfg["dv"], cfg["dk"], cfg["L"]))
+    f64_all = f64
+    f64 = [tuple(None if a is None else a[:b1] for a in t) for t in f64_all]
+    o.set_num_threads(1)
+    Bsave, B = B, b1
+    t0 = time.perf_counter()
+    window(one, True)
+    t_one = time.perf_counter() - t0
+    B = Bsave
+    o.set_num_threads(threads)
+    del one
+    one_thread = n_steps * (b1 / cfg["B"]) / t_one
     scale = B / cfg["B"]
     total = n_win * n_steps
     route = "two-copy checkpoint+buffer" if cfg.get("read") else "checkpoint+buffer"
@@ -182,7 +197,9 @@ def cpu_baseline(cfg, n_steps=None, rows=None, min_seconds=10.0, max_windows=32)
         "kind": "oracle",
         "sample": (f"fp64 oracle, {route} route, {total} steps ({n_win} windows of {n_steps}) over "
                    f"{B} of {cfg['B']} rows x {cfg['H']} heads; conventional route "
-                   f"{round(total * scale / t_conv, 4)} steps/s; {t_rep + t_conv:.1f} s of CPU time"),
+                   f"{round(total * scale / t_conv, 4)} steps/s; the checkpoint+buffer route on 1 thread "
+                   f"({b1} rows, one window, scaled to the batch) {round(one_thread, 4)} steps/s; "
+                   f"{t_rep + t_conv + t_one:.1f} s of CPU time"),
     }
 
 
