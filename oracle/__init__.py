@@ -90,6 +90,9 @@ class Oracle:
         lib.oc_spec_verify.argtypes = [i64, c_int, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P, _I32P,
                                        _U8P, _F64P, _F64P, _F64P, _F64P, _opt(_U8P), _F64P]
         lib.oc_spec_verify.restype = i64
+        lib.oc_spec_verify_gdn.argtypes = [i64, c_int, c_int, c_int, c_int, _F64P, _F64P, _F64P, _F64P, _I32P,
+                                           _U8P, _F64P, _F64P, _F64P, _F64P, _F64P, _opt(_U8P), _F64P]
+        lib.oc_spec_verify_gdn.restype = i64
         lib.oc_spec_commit.argtypes = [i64, _I32P, _I32P, _opt(_U8P)]
         lib.oc_spec_commit.restype = None
         lib.oc_spec_cursor_run.argtypes = [c_int, c_int, i32, i64, _I32P, _opt(_U8P), _I32P, _U8P]
@@ -142,19 +145,25 @@ class Oracle:
         return w, f.astype(bool)
 
     # -- speculative verify (Mamba-2 form) ---------------------------------
-    def spec_verify(self, C, rec_lam, rec_x, rec_k, h, flush, q, k, v, lam, active=None):
-        """q, k: [n, T, dk]; v: [n, T, dv]; lam: [n, T].  Returns out [n, T, dv]."""
+    def spec_verify(self, C, rec_lam, rec_x, rec_k, h, flush, q, k, v, lam, active=None, beta=None):
+        """q, k: [n, T, dk]; v: [n, T, dv]; lam: [n, T]; beta: [n, T] for the
+        Gated DeltaNet form (None: Mamba-2).  Returns out [n, T, dv]."""
         n, dv, dk = C.shape
         cap = rec_lam.shape[1]
         T = q.shape[1]
         assert rec_x.shape == (n, cap, dv) and rec_k.shape == (n, cap, dk)
         assert h.dtype == np.int32 and h.shape == (n,)
-        for a in (C, q, k, v, lam):
+        for a in (C, q, k, v, lam) + (() if beta is None else (beta,)):
             assert a.dtype == np.float64 and a.flags.c_contiguous
         assert q.shape == (n, T, dk) and k.shape == (n, T, dk) and v.shape == (n, T, dv) and lam.shape == (n, T)
         out = np.zeros((n, T, dv), np.float64)
-        ovf = self.lib.oc_spec_verify(n, dv, dk, cap, T, C, rec_lam, rec_x, rec_k, h, _u8(flush), q, k, v, lam,
-                                      _u8(active), out)
+        if beta is None:
+            ovf = self.lib.oc_spec_verify(n, dv, dk, cap, T, C, rec_lam, rec_x, rec_k, h, _u8(flush), q, k, v,
+                                          lam, _u8(active), out)
+        else:
+            assert beta.shape == (n, T)
+            ovf = self.lib.oc_spec_verify_gdn(n, dv, dk, cap, T, C, rec_lam, rec_x, rec_k, h, _u8(flush), q, k,
+                                              v, lam, beta, _u8(active), out)
         if ovf:
             raise ValueError(f"{ovf} tiles would overflow the record ring (cap={cap}, T={T})")
         return out
@@ -403,12 +412,15 @@ class SRConventionalModel(ConventionalModel):
 class SpecReplayModel:
     """Speculative verify from a checkpoint plus a ring of L committed records
     (blog, "Speculative decoding: rollback becomes a pointer"), B rows x H
-    heads, fp64, Mamba-2 form.  verify() computes the T draft outputs and
-    stores the drafts as records behind the committed ones (after folding the
-    committed records on flush rows); commit() advances the committed pointer."""
+    heads, fp64, Mamba-2 form or (form=GDN, blog "The delta-rule wrinkle")
+    Gated DeltaNet, whose records hold corrected values.  verify() computes
+    the T draft outputs and stores the drafts as records behind the committed
+    ones (after folding the committed records on flush rows); commit()
+    advances the committed pointer."""
 
-    def __init__(self, B, H, dv, dk, L, T, oracle=None):
+    def __init__(self, B, H, dv, dk, L, T, oracle=None, form=MAMBA2):
         self.o = oracle or get()
+        self.form = form
         self.B, self.H, self.dv, self.dk, self.L, self.T = B, H, dv, dk, L, T
         n = B * H
         self.cap = L
@@ -418,17 +430,20 @@ class SpecReplayModel:
         self.rec_k = np.zeros((n, L, dk))
         self.h = np.zeros(n, np.int32)
 
-    def verify(self, q, k, v, lam, flush_rows, active_rows=None):
-        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam: [B, H, T]; flush_rows [B].
-        Returns o [B, H, T, dv]."""
+    def verify(self, q, k, v, lam, flush_rows, active_rows=None, beta=None):
+        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam, beta: [B, H, T];
+        flush_rows [B].  Returns o [B, H, T, dv]."""
         B, H, T = self.B, self.H, self.T
         n = B * H
         fl = np.repeat(np.asarray(flush_rows, bool), H)
         act = None if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
         f = lambda a, d: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T, d))
+        sc = lambda a: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T))
+        if (self.form == GDN) != (beta is not None):
+            raise ValueError("beta is given for the Gated DeltaNet form and only for it")
         out = self.o.spec_verify(self.C, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, f(q, self.dk),
-                                 f(k, self.dk), f(v, self.dv),
-                                 np.ascontiguousarray(np.asarray(lam, np.float64).reshape(n, T)), act)
+                                 f(k, self.dk), f(v, self.dv), sc(lam), act,
+                                 None if beta is None else sc(beta))
         return out.reshape(B, H, T, self.dv)
 
     def commit(self, accepted_rows, active_rows=None):
@@ -454,32 +469,39 @@ class SpecTokenByToken:
     accepted drafts; verify() runs the T drafts on a copy of S and returns
     every draft's output (Mamba-2 form)."""
 
-    def __init__(self, B, H, dv, dk, T, S0=None, oracle=None):
-        self.conv = ConventionalModel(MAMBA2, B, H, dv, dk, S0, oracle)
+    def __init__(self, B, H, dv, dk, T, S0=None, oracle=None, form=MAMBA2):
+        self.conv = ConventionalModel(form, B, H, dv, dk, S0, oracle)
         self.B, self.H, self.dv, self.dk, self.T = B, H, dv, dk, T
+        self.form = form
         self._drafts = None
+        self.drafts_x = None  # [B, H, T, dv]: the value each draft writes (v, or GDN's corrected value)
 
-    def verify(self, q, k, v, lam):
-        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam: [B, H, T]."""
+    def verify(self, q, k, v, lam, beta=None):
+        """q, k: [B, H, T, dk]; v: [B, H, T, dv]; lam, beta: [B, H, T] (beta:
+        Gated DeltaNet only)."""
         q, k, v, lam = (np.asarray(a, np.float64) for a in (q, k, v, lam))
+        beta = None if beta is None else np.asarray(beta, np.float64)
         S = self.conv.S.copy()
-        outs = []
+        outs, xs = [], []
         for i in range(self.T):
-            outs.append(self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i]))
-        committed = self.conv.S
+            o, x = self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i],
+                                  None if beta is None else beta[:, :, i], want_x=True)
+            outs.append(o)
+            xs.append(x)
         self.conv.S = S  # the committed state is unchanged until commit()
-        self._drafts = (q, k, v, lam)
-        del committed
+        self._drafts = (q, k, v, lam, beta)
+        self.drafts_x = np.stack(xs, axis=2)
         return np.stack(outs, axis=2)
 
     def commit(self, accepted_rows):
         """Advance each row's committed state by its first `accepted` drafts."""
-        q, k, v, lam = self._drafts
+        q, k, v, lam, beta = self._drafts
         acc = np.asarray(accepted_rows)
         for i in range(self.T):
             rows = acc > i
             if rows.any():
-                self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i], active_rows=rows)
+                self.conv.step(q[:, :, i], k[:, :, i], v[:, :, i], lam[:, :, i],
+                               None if beta is None else beta[:, :, i], active_rows=rows)
 
     def state(self):
         return self.conv.state()

@@ -414,6 +414,113 @@ int64_t oc_spec_verify(int64_t n, int dv, int dk, int cap, int T, double* C, dou
 }
 
 /*
+ * Speculative verify, Gated DeltaNet form.  [blog] "The delta-rule wrinkle":
+ * each token's corrected value u = beta (v - alpha S_{t-1} k) depends on the
+ * state before it, so the T drafts' corrections come from a T x T
+ * lower-triangular solve; [blog] "Speculative decoding": the checkpoint is
+ * read against every draft, drafts become records behind the h committed
+ * ones, a flush folds only the committed records.  Per tile, with committed
+ * records (lam_j, u_j, k_j), j = 1..h, gamma over committed alphas and D over
+ * draft alphas (D_{a:b} = prod_{l=a..b} alpha_l, 1 when empty):
+ *   S_h x = gamma_{1:h} C x + sum_j gamma_{j+1:h} (k_j . x) u_j     (x = k_i, q_i)
+ *   u_i + beta_i sum_{m<i} D_{m+1:i} (k_m . k_i) u_m = beta_i (v_i - D_{1:i} S_h k_i)
+ *   o_i = D_{1:i} S_h q_i + sum_{m<=i} D_{m+1:i} (k_m . q_i) u_m
+ * The system is solved by forward substitution, i = 1..T, one d_v-vector at
+ * a time.  Then the committed records are folded on a flushing tile (as in
+ * oc_spec_verify) and the drafts are stored as records (lam_i, u_i, k_i)
+ * from slot (flush ? 0 : h).  rec_x holds u.
+ */
+int64_t oc_spec_verify_gdn(int64_t n, int dv, int dk, int cap, int T, double* C, double* rec_lam,
+                           double* rec_x, double* rec_k, int32_t* h, const uint8_t* flush,
+                           const double* q, const double* k, const double* v, const double* lam,
+                           const double* beta, const uint8_t* active, double* out) {
+    int64_t overflow = 0;
+#pragma omp parallel reduction(+ : overflow)
+    {
+        double* ac = (double*)malloc(sizeof(double) * (size_t)(cap + 2));
+        double* ad = (double*)malloc(sizeof(double) * (size_t)(T + 2));
+        double* y = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* shk = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* shq = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* u = (double*)malloc(sizeof(double) * (size_t)T * dv); /* u[(i-1)*dv + r] */
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n; ++t) {
+            if (active && !active[t]) continue;
+            const int ht = h[t];
+            const int base = flush[t] ? 0 : ht;
+            if (base + T > cap) { overflow += 1; continue; }
+            double* Ct = C + t * (int64_t)dv * dk;
+            double* lamt = rec_lam + t * (int64_t)cap;
+            double* xt = rec_x + t * (int64_t)cap * dv;
+            double* krt = rec_k + t * (int64_t)cap * dk;
+            const double* qt = q + t * (int64_t)T * dk;
+            const double* kt = k + t * (int64_t)T * dk;
+            const double* vt = v + t * (int64_t)T * dv;
+            const double* lt = lam + t * (int64_t)T;
+            const double* bt = beta + t * (int64_t)T;
+            double* ot = out + t * (int64_t)T * dv;
+            for (int j = 1; j <= ht; ++j) ac[j] = exp(lamt[j - 1]);
+            for (int i = 1; i <= T; ++i) ad[i] = exp(lt[i - 1]);
+            const double gh = gamma_range(ac, 1, ht);
+            for (int i = 1; i <= T; ++i) {
+                const double* qi = qt + (int64_t)(i - 1) * dk;
+                const double* ki = kt + (int64_t)(i - 1) * dk;
+                /* the committed state S_h read at k_i and at q_i */
+                matvec(Ct, ki, dv, dk, y);
+                for (int r = 0; r < dv; ++r) shk[r] = gh * y[r];
+                matvec(Ct, qi, dv, dk, y);
+                for (int r = 0; r < dv; ++r) shq[r] = gh * y[r];
+                for (int j = 1; j <= ht; ++j) {
+                    const double g = gamma_range(ac, j + 1, ht);
+                    const double* kj = krt + (int64_t)(j - 1) * dk;
+                    const double wk = g * dot(kj, ki, dk), wq = g * dot(kj, qi, dk);
+                    for (int r = 0; r < dv; ++r) {
+                        shk[r] += wk * xt[(int64_t)(j - 1) * dv + r];
+                        shq[r] += wq * xt[(int64_t)(j - 1) * dv + r];
+                    }
+                }
+                /* row i of the triangular system, earlier drafts known */
+                const double Di = gamma_range(ad, 1, i);
+                double* ui = u + (int64_t)(i - 1) * dv;
+                for (int r = 0; r < dv; ++r) ui[r] = bt[i - 1] * (vt[(int64_t)(i - 1) * dv + r] - Di * shk[r]);
+                for (int m = 1; m < i; ++m) {
+                    const double a = bt[i - 1] * gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, ki, dk);
+                    for (int r = 0; r < dv; ++r) ui[r] -= a * u[(int64_t)(m - 1) * dv + r];
+                }
+                /* output of draft i */
+                for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] = Di * shq[r];
+                for (int m = 1; m <= i; ++m) {
+                    const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);
+                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * u[(int64_t)(m - 1) * dv + r];
+                }
+            }
+            if (flush[t]) {
+                for (int r = 0; r < dv; ++r)
+                    for (int c = 0; c < dk; ++c) {
+                        double s = gh * Ct[(int64_t)r * dk + c];
+                        for (int j = 1; j <= ht; ++j)
+                            s += gamma_range(ac, j + 1, ht) * xt[(int64_t)(j - 1) * dv + r] * krt[(int64_t)(j - 1) * dk + c];
+                        Ct[(int64_t)r * dk + c] = s;
+                    }
+                h[t] = 0;
+            }
+            for (int i = 0; i < T; ++i) {
+                lamt[base + i] = lt[i];
+                memcpy(xt + (int64_t)(base + i) * dv, u + (int64_t)i * dv, sizeof(double) * (size_t)dv);
+                memcpy(krt + (int64_t)(base + i) * dk, kt + (int64_t)i * dk, sizeof(double) * (size_t)dk);
+            }
+        }
+        free(ac);
+        free(ad);
+        free(y);
+        free(shk);
+        free(shq);
+        free(u);
+    }
+    return overflow;
+}
+
+/*
  * Commit after a speculative verify ([blog]: "after sampling advances the
  * committed pointer by a"): h <- h + accepted for each selected tile.  The
  * verify step has already set h to 0 on a flushing tile.

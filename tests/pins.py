@@ -469,23 +469,41 @@ def _spec_tok(seed, step, B, H, T, dv, dk, a_lo=0.05, a_hi=1.0):
     return st(0), st(1), st(2), st(3)
 
 
-def run_spec(orc, B, H, dv, dk, L, T, n_steps, accept, seed=0, a_lo=0.05, a_hi=1.0):
+def _spec_tok_gdn(seed, step, B, H, T, dv, dk):
+    """Gated DeltaNet drafts: q, k [B, H, T, dk] unit-norm, v [B, H, T, dv],
+    lam, beta [B, H, T]."""
+    toks = [_tok(GDN, seed, 1000 * step + i, B, H, dv, dk) for i in range(T)]
+    st = lambda idx: np.stack([t[idx] for t in toks], axis=2)
+    return st(0), st(1), st(2), st(3), st(4)
+
+
+def run_spec(orc, B, H, dv, dk, L, T, n_steps, accept, seed=0, a_lo=0.05, a_hi=1.0, form=M2):
     """Speculative verify against the token-by-token recurrence.  accept(s)
     gives the accepted counts [B] of step s.  Returns (max output deviation,
     max deviation of a flushed checkpoint from the committed state, number of
-    flushing row-steps)."""
-    spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc)
-    ref = oracle.SpecTokenByToken(B, H, dv, dk, T, oracle=orc)
+    flushing row-steps); for the Gated DeltaNet form also checks that the
+    drafts' stored records hold the token-by-token corrected values."""
+    spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc, form=form)
+    ref = oracle.SpecTokenByToken(B, H, dv, dk, T, oracle=orc, form=form)
     h = np.zeros(B, np.int32)
     worst_o = worst_s = 0.0
     n_flush = 0
     for s in range(n_steps):
-        q, k, v, lam = _spec_tok(seed, s, B, H, T, dv, dk, a_lo, a_hi)
+        beta = None
+        if form == M2:
+            q, k, v, lam = _spec_tok(seed, s, B, H, T, dv, dk, a_lo, a_hi)
+        else:
+            q, k, v, lam, beta = _spec_tok_gdn(seed, s, B, H, T, dv, dk)
         fl = np.array([orc.spec_cursor_run(L, T, int(h[b]), np.zeros(1, np.int32))[1][0] for b in range(B)])
         assert np.array_equal(spec.committed()[:, 0], h), "the ring holds a different committed count"
-        o_s = spec.verify(q, k, v, lam, fl)
-        o_r = ref.verify(q, k, v, lam)
+        o_s = spec.verify(q, k, v, lam, fl, beta=beta)
+        o_r = ref.verify(q, k, v, lam, beta)
         worst_o = max(worst_o, _rel(o_s, o_r))
+        if form != M2:
+            base = np.where(fl, 0, h)
+            for b in range(B):
+                x = spec.rec_x.reshape(B, H, L, dv)[b, :, base[b]:base[b] + T]
+                worst_o = max(worst_o, _rel(x, ref.drafts_x[b]))
         if fl.any():
             n_flush += int(fl.sum())
             worst_s = max(worst_s, _rel(spec.checkpoint()[fl], ref.state()[fl]))
@@ -508,6 +526,63 @@ def pin_spec_identity(orc):
         o, st, nf = run_spec(orc, 3, 2, 8, 12, 8, T, 30, lambda s: rng.integers(0, T + 1, 3), seed=T)
         assert nf >= 3, (T, nf)
         assert o < 1e-12 and st < 1e-12, (T, o, st)
+
+
+def pin_spec_gdn_identity(orc):
+    """[blog] "The delta-rule wrinkle" and "Speculative decoding": Gated
+    DeltaNet drafts through the T x T triangular solve, from checkpoint plus
+    committed records, equal running the drafts token by token through the
+    recurrence (outputs, the corrected values stored as records, flushed
+    checkpoints); T = 1, 2, 4, random accepted counts, several flushes."""
+    rng = np.random.default_rng(12)
+    for T in (1, 2, 4):
+        o, st, nf = run_spec(orc, 3, 2, 8, 12, 8, T, 30, lambda s: rng.integers(0, T + 1, 3), seed=40 + T, form=GDN)
+        assert o < 1e-12 and st < 1e-12, (T, o, st)
+        assert nf >= 3, (T, nf)
+
+
+def pin_spec_gdn_T1_is_standard_decode(orc):
+    """A one-draft Gated DeltaNet verify with every draft accepted is the
+    standard step's output-only route (ReplayModel, an independent code
+    path), flushes included (ring of L, flush when h + 1 > L)."""
+    B, H, dv, dk, L = 2, 3, 8, 12, 4
+    spec = oracle.SpecReplayModel(B, H, dv, dk, L, 1, oracle=orc, form=GDN)
+    std = oracle.ReplayModel(GDN, B, H, dv, dk, L + 1, oracle=orc)   # L records + the current token
+    h = 0
+    for s in range(3 * L + 2):
+        q, k, v, lam, beta = _spec_tok_gdn(51, s, B, H, 1, dv, dk)
+        fl = h + 1 > L
+        o_s = spec.verify(q, k, v, lam, np.full(B, fl), beta=beta)[:, :, 0]
+        # the standard step flushes the records with the current token; the
+        # speculative one folds the committed records and keeps the draft
+        if fl:
+            std.fold(np.ones(B, bool))
+        o_r = std.step(q[:, :, 0], k[:, :, 0], v[:, :, 0], lam[:, :, 0], np.zeros(B, bool), beta[:, :, 0])
+        assert _rel(o_s, o_r) < 1e-12, s
+        spec.commit(np.ones(B, np.int32))
+        h = (0 if fl else h) + 1
+
+
+def pin_spec_gdn_zero_beta(orc):
+    """beta = 0 writes nothing: every corrected value is 0 and draft i's
+    output is the decayed committed state read at q_i, D_{1:i} S_h q_i."""
+    B, H, dv, dk, L, T = 2, 2, 8, 12, 8, 4
+    spec = oracle.SpecReplayModel(B, H, dv, dk, L, T, oracle=orc, form=GDN)
+    ref = oracle.SpecTokenByToken(B, H, dv, dk, T, oracle=orc, form=GDN)
+    for s in range(2):   # some committed history first (h = 4, room for T = 4)
+        q, k, v, lam, beta = _spec_tok_gdn(61, s, B, H, T, dv, dk)
+        spec.verify(q, k, v, lam, np.zeros(B, bool), beta=beta)
+        ref.verify(q, k, v, lam, beta)
+        spec.commit(np.full(B, 2))
+        ref.commit(np.full(B, 2))
+    q, k, v, lam, beta = _spec_tok_gdn(62, 9, B, H, T, dv, dk)
+    o = spec.verify(q, k, v, lam, np.zeros(B, bool), beta=np.zeros_like(beta))
+    Sh = ref.state()
+    D = np.exp(np.cumsum(lam, axis=2))
+    want = D[..., None] * np.einsum("bhvk,bhtk->bhtv", Sh, q)
+    assert _rel(o, want) < 1e-12
+    held = spec.committed()[0, 0]
+    assert np.all(spec.rec_x.reshape(B, H, L, dv)[:, :, held:held + T] == 0)
 
 
 def pin_spec_long_memory(orc):
@@ -741,6 +816,9 @@ ALL_PINS = [
     pin_e4m3_spec_values,
     pin_read_rounding_within_half_ulp,
     pin_spec_identity,
+    pin_spec_gdn_identity,
+    pin_spec_gdn_T1_is_standard_decode,
+    pin_spec_gdn_zero_beta,
     pin_spec_long_memory,
     pin_spec_causal,
     pin_spec_rejected_drafts_never_read,

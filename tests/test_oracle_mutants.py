@@ -90,6 +90,24 @@ MUTANTS = [
     ("spec_flush_rule_inclusive",
      "const int f = (room < T) || (forced && forced[s]);",
      "const int f = (room <= T) || (forced && forced[s]);"),
+    ("spec_gdn_solve_sign",
+     "for (int r = 0; r < dv; ++r) ui[r] -= a * u[(int64_t)(m - 1) * dv + r];",
+     "for (int r = 0; r < dv; ++r) ui[r] += a * u[(int64_t)(m - 1) * dv + r];"),
+    ("spec_gdn_no_triangular_solve",
+     "for (int m = 1; m < i; ++m) {\n                    const double a = bt[i - 1]",
+     "for (int m = 1; m < 1; ++m) {\n                    const double a = bt[i - 1]"),
+    ("spec_gdn_solve_decay_off_by_one",
+     "const double a = bt[i - 1] * gamma_range(ad, m + 1, i) * dot(",
+     "const double a = bt[i - 1] * gamma_range(ad, m, i) * dot("),
+    ("spec_gdn_drop_beta",
+     "ui[r] = bt[i - 1] * (vt[(int64_t)(i - 1) * dv + r] - Di * shk[r]);",
+     "ui[r] = (vt[(int64_t)(i - 1) * dv + r] - Di * shk[r]);"),
+    ("spec_gdn_state_read_at_q",
+     "matvec(Ct, ki, dv, dk, y);",
+     "matvec(Ct, qi, dv, dk, y);"),
+    ("spec_gdn_drafts_store_v",
+     "memcpy(xt + (int64_t)(base + i) * dv, u + (int64_t)i * dv, sizeof(double) * (size_t)dv);",
+     "memcpy(xt + (int64_t)(base + i) * dv, vt + (int64_t)i * dv, sizeof(double) * (size_t)dv);"),
     ("spec_commit_one_short",
      "if (!active || active[t]) h[t] += accepted[t];",
      "if (!active || active[t]) h[t] += accepted[t] > 0 ? accepted[t] - 1 : 0;"),
