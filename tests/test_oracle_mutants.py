@@ -73,20 +73,37 @@ MUTANTS = [
      "const int f = (w == L - 1) || (forced && forced[s]);",
      "const int f = (w == L - 1);"),
     ("spec_no_causal_mask",
-     "for (int m = 1; m <= i; ++m) {",
-     "for (int m = 1; m <= T; ++m) {"),
+     "for (int m = 1; m <= i; ++m) {\n                    const double wgt = gamma_range(ad, m + 1, i) * dot(kt + "
+     "(int64_t)(m - 1) * dk, qi, dk);\n                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] "
+     "+= wgt * vt[",
+     "for (int m = 1; m <= T; ++m) {\n                    const double wgt = gamma_range(ad, m + 1, i) * dot(kt + "
+     "(int64_t)(m - 1) * dk, qi, dk);\n                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] "
+     "+= wgt * vt["),
     ("spec_draft_decay_short",
-     "const double Di = gamma_range(ad, 1, i);",
-     "const double Di = gamma_range(ad, 1, i - 1);"),
+     "const double Di = gamma_range(ad, 1, i);\n                matvec(Ct, qi, dv, dk, cq);",
+     "const double Di = gamma_range(ad, 1, i - 1);\n                matvec(Ct, qi, dv, dk, cq);"),
+    ("spec_gdn_draft_decay_short",
+     "const double Di = gamma_range(ad, 1, i);\n                double* ui",
+     "const double Di = gamma_range(ad, 1, i - 1);\n                double* ui"),
     ("spec_W_off_by_one",
-     "const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);",
-     "const double wgt = gamma_range(ad, m, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);"),
+     "const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);\n"
+     "                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * vt[",
+     "const double wgt = gamma_range(ad, m, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);\n"
+     "                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * vt["),
+    ("spec_gdn_W_off_by_one",
+     "const double wgt = gamma_range(ad, m + 1, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);\n"
+     "                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * u[",
+     "const double wgt = gamma_range(ad, m, i) * dot(kt + (int64_t)(m - 1) * dk, qi, dk);\n"
+     "                    for (int r = 0; r < dv; ++r) ot[(int64_t)(i - 1) * dv + r] += wgt * u["),
     ("spec_committed_drop_draft_decay",
      "const double wgt = gamma_range(ac, j + 1, ht) * Di * dot(krt + (int64_t)(j - 1) * dk, qi, dk);",
      "const double wgt = gamma_range(ac, j + 1, ht) * dot(krt + (int64_t)(j - 1) * dk, qi, dk);"),
     ("spec_drafts_after_flushed_records",
-     "const int base = flush[t] ? 0 : ht;",
-     "const int base = ht;"),
+     "const int base = flush[t] ? 0 : ht; /* first slot",
+     "const int base = ht; /* first slot"),
+    ("spec_gdn_drafts_after_flushed_records",
+     "const int base = flush[t] ? 0 : ht;\n",
+     "const int base = ht;\n"),
     ("spec_flush_rule_inclusive",
      "const int f = (room < T) || (forced && forced[s]);",
      "const int f = (room <= T) || (forced && forced[s]);"),
