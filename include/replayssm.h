@@ -82,9 +82,9 @@ typedef enum {
  *               speculative layer (blog "Speculative decoding: rollback
  *               becomes a pointer"): its ring holds up to L committed records
  *               and each step verifies T draft tokens per row with
- *               replay_spec_verify; replay_decode_step rejects it.  Mamba-2
- *               form, single fp32 or fp16 checkpoint, (d_v, d_k) = (16, 32)
- *               or (64, 128).
+ *               replay_spec_verify; replay_decode_step rejects it.  Single
+ *               fp32 or fp16 checkpoint, one key per head; (d_v, d_k) =
+ *               (16, 32) or (64, 128), and (128, 128) for Gated DeltaNet.
  * n_groups:     0 or n_heads for a key and a query per head.  A divisor
  *               G < n_heads shares one key and one query among each run of
  *               n_heads / G consecutive heads, the released grouped-key
@@ -384,9 +384,18 @@ int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, cons
  * the number of drafts accepted; records past it are never read and get
  * overwritten.
  *
+ * Gated DeltaNet (blog "The delta-rule wrinkle"): records hold corrected
+ * values u, and a draft's u_i = beta_i (v_i - alpha_i S_{i-1} k_i) depends on
+ * the drafts before it, a T x T triangular system.  With S_h the committed
+ * state (checkpoint plus committed records, never formed) read at k_i and q_i:
+ *     u_i = beta_i (v_i - D_i S_h k_i) - beta_i sum_{m<i} W_im (k_m . k_i) u_m
+ *     o_i = D_i S_h q_i + sum_{m<=i} W_im (k_m . q_i) u_m
+ * solved draft by draft; the drafts' u_i are stored as their records.
+ * Heads of 16 x 32, 64 x 128 (both forms) and 128 x 128 (Gated DeltaNet).
+ *
  * q, k: [n_rows][T][n_heads][d_k]; v: [n_rows][T][n_heads][d_v], io_dtype,
  * unit stride along the last dimension, row / token / head strides in
- * elements; log_decay: [n_rows][T][n_heads] fp32 contiguous; out:
+ * elements; log_decay (and beta): [n_rows][T][n_heads] fp32 contiguous; out:
  * [n_rows][T][n_heads][d_v] fp32 contiguous.
  */
 typedef struct {
@@ -398,6 +407,7 @@ typedef struct {
     int64_t v_row_stride, v_token_stride, v_head_stride;
     const float* log_decay;
     float* out;
+    const float* beta;  /* Gated DeltaNet: [n_rows][T][n_heads] fp32 contiguous; NULL for Mamba-2 */
 } rs_spec_io;
 
 /*

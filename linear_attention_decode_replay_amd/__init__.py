@@ -69,7 +69,7 @@ class RsSpecIO(_c.Structure):
                 ("q_row_stride", _c.c_int64), ("q_token_stride", _c.c_int64), ("q_head_stride", _c.c_int64),
                 ("k_row_stride", _c.c_int64), ("k_token_stride", _c.c_int64), ("k_head_stride", _c.c_int64),
                 ("v_row_stride", _c.c_int64), ("v_token_stride", _c.c_int64), ("v_head_stride", _c.c_int64),
-                ("log_decay", _vp), ("out", _vp)]
+                ("log_decay", _vp), ("out", _vp), ("beta", _vp)]
 
 
 class ReplaySSMError(RuntimeError):
@@ -185,19 +185,19 @@ def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:
                     v.stride(0), v.stride(1), _ptr(log_decay), _ptr(beta), _ptr(out))
 
 
-def make_spec_io(q, k, v, log_decay, out) -> RsSpecIO:
+def make_spec_io(q, k, v, log_decay, out, beta=None) -> RsSpecIO:
     """q, k: [n_rows, T, n_heads, d_k]; v: [n_rows, T, n_heads, d_v] (any
-    row/token/head strides, unit last stride); log_decay: fp32
-    [n_rows, T, n_heads] contiguous; out: fp32 [n_rows, T, n_heads, d_v]
-    contiguous."""
+    row/token/head strides, unit last stride); log_decay, beta (Gated
+    DeltaNet only): fp32 [n_rows, T, n_heads] contiguous; out: fp32
+    [n_rows, T, n_heads, d_v] contiguous."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4 or t.stride(3) != 1:
             raise ValueError(f"{name} must be [rows, T, heads, d] with unit last stride")
-    for name, t in (("log_decay", log_decay), ("out", out)):
-        if not t.is_contiguous():
+    for name, t in (("log_decay", log_decay), ("out", out), ("beta", beta)):
+        if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     return RsSpecIO(_ptr(q), _ptr(k), _ptr(v), q.stride(0), q.stride(1), q.stride(2), k.stride(0), k.stride(1),
-                    k.stride(2), v.stride(0), v.stride(1), v.stride(2), _ptr(log_decay), _ptr(out))
+                    k.stride(2), v.stride(0), v.stride(1), v.stride(2), _ptr(log_decay), _ptr(out), _ptr(beta))
 
 
 def _stream(stream):

@@ -79,7 +79,6 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
         if (T < 1 || T > L->L) return fail(RS_EINVAL, "spec_T must be in 1..L (got %d, L=%d)", T, L->L);
         if (T != 1 && T != 2 && T != 4 && T != 8)
             return fail(RS_EUNSUPPORTED, "spec_T must be 1, 2, 4 or 8 (got %d)", T);
-        if (L->form != RS_MAMBA2) return fail(RS_EUNSUPPORTED, "speculative verify: Mamba-2 form only");
         if (two_precision(*L))
             return fail(RS_EUNSUPPORTED, "speculative verify: single checkpoint only (no read copy)");
         if (kind == rs::Kind::ReplayStep)
@@ -89,8 +88,8 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
     }
     if (!rs::compiled(kind, *L)) {
         if (spec_kind)
-            return fail(RS_EUNSUPPORTED, "no speculative kernel for d_v=%d d_k=%d (supported: 16x32, 64x128)",
-                        L->d_v, L->d_k);
+            return fail(RS_EUNSUPPORTED, "no speculative kernel for d_v=%d d_k=%d (supported: 16x32, 64x128%s)",
+                        L->d_v, L->d_k, L->form == RS_GDN ? ", 128x128" : "");
         if (L->read_dtype == RS_E4M3)
             return fail(RS_EUNSUPPORTED, "no kernel for an E4M3 read copy with d_v=%d d_k=%d (supported: 64x128, "
                                          "128x128)", L->d_v, L->d_k);
@@ -368,8 +367,11 @@ int replay_spec_verify(const rs_layer* layer, const rs_batch* batch, const rs_sp
     if (!io->log_decay || !aligned(io->log_decay, 16))
         return fail(RS_EINVAL, "log_decay must be non-NULL and 16-byte aligned");
     if (!io->out || !aligned(io->out, 16)) return fail(RS_EINVAL, "out must be non-NULL and 16-byte aligned");
+    if (layer->form == RS_GDN && (!io->beta || !aligned(io->beta, 16)))
+        return fail(RS_EINVAL, "beta must be non-NULL and 16-byte aligned for Gated DeltaNet");
     rs::StepParams p = params(*layer, *batch);
     p.spec_T = T;
+    p.beta = io->beta;
     p.q = io->q;
     p.k = io->k;
     p.v = io->v;

@@ -1570,6 +1570,340 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     if (tid < T) rl[base + tid] = s.lamd[tid];
 }
 
+// ---------------------------------- speculative verify, Gated DeltaNet form --
+// A draft's corrected value u_i = beta_i (v_i - alpha_i S_{i-1} k_i) depends
+// on the drafts before it (blog "The delta-rule wrinkle": a T x T triangular
+// solve), so after the dot products the drafts are finished one at a time.
+// With D_{a:b} the product of draft decays a..b and S_h the committed state
+// (checkpoint plus committed records):
+//   u_i = beta_i (v_i - D_{1:i} S_h k_i) - beta_i sum_{m<i} D_{m+1:i} (k_m . k_i) u_m
+//   o_i = D_{1:i} S_h q_i + sum_{m<=i} D_{m+1:i} (k_m . q_i) u_m
+// One workgroup per (row, head) tile (split 1, as k_spec_verify).
+template <class R>
+struct SpecGdnLds {
+    R* kc;         // [slots][DK] committed keys
+    R* xc;         // [DV][slots] committed corrected values, transposed so
+                   // that lanes holding consecutive records read consecutive
+                   // words (record-major would put a row group in one bank)
+    float* qd;     // [T][DK] draft queries
+    float* kd;     // [T][DK] draft keys
+    float* vd;     // [T][DV] draft values
+    float* lamd;   // [T] draft log-decays
+    float* betad;  // [T] draft write strengths
+    float* ec;     // [slots] exp(sum of the committed log-decays after record j)
+    float* dexp;   // [T] D_{1:i}
+    float* wdd;    // [T][T] D_{m+1:i} at [m * T + i], m <= i
+    float* kq;     // [slots + T][T] key . q_i (committed keys, then drafts)
+    float* kk;     // [slots + T][T] key . k_i
+    float* sc;     // [4] total committed log-decay, its exponential
+};
+
+template <int DV, int DK, class R>
+__device__ __forceinline__ SpecGdnLds<R> spec_gdn_carve(char* smem, int slots, int T) {
+    SpecGdnLds<R> s;
+    s.kc = reinterpret_cast<R*>(smem);
+    s.xc = s.kc + (int64_t)slots * DK;
+    float* f = reinterpret_cast<float*>(s.xc + (int64_t)slots * DV);
+    s.qd = f;
+    s.kd = s.qd + T * DK;
+    s.vd = s.kd + T * DK;
+    s.lamd = s.vd + T * DV;
+    s.betad = s.lamd + T;
+    s.ec = s.betad + T;
+    s.dexp = s.ec + slots;
+    s.wdd = s.dexp + T;
+    s.kq = s.wdd + T * T;
+    s.kk = s.kq + (slots + T) * T;
+    s.sc = s.kk + (slots + T) * T;
+    return s;
+}
+
+size_t spec_gdn_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes) {
+    return (size_t)slots * (dk + dv) * rec_bytes +
+           sizeof(float) * (2 * (size_t)T * dk + (size_t)T * dv + 2 * (size_t)T + (size_t)slots + (size_t)T +
+                            (size_t)T * T + 2 * ((size_t)slots + T) * T + 4);
+}
+
+template <int DV, int DK, class TS, class TR, class TI, int T>
+__global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(const StepParams p) {
+    using Tl = Tile<DV, DK, TS, 1>;
+    using S = typename TS::S;
+    using R = typename TR::S;
+    using I = typename TI::S;
+    constexpr int NT = Tl::NT, VEC = Tl::VEC, LPR = Tl::LPR, RPP = Tl::RPP, NR = Tl::NR;
+    constexpr int QN = (T * DK / 4 + NT - 1) / NT;    // 4-element pieces of draft q / k per thread
+    constexpr int VN = (T * DV + NT - 1) / NT;        // draft v elements per thread
+    constexpr int KCH = DK * (int)sizeof(R) / 16, XCH = DV * (int)sizeof(R) / 16, XE = 16 / (int)sizeof(R);
+    constexpr int RC = 2;                             // record chunks per thread in registers
+    constexpr int NV = 2 * NR;                        // (S_h q_i, S_h k_i) partial sums of the owned rows
+    static_assert(DK % 4 == 0 && VEC % 4 == 0, "4-element pieces");
+
+    const TileIds id = tile_ids<1>(p);
+    const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
+    const bool flag = row_flag(fsrc, id.row) && p.flush;
+    const int blk = p.block_table[id.row];
+    const int h = p.write_pos[id.row];
+    const bool pad = blk < 0;
+    const bool bad = !pad && (blk >= p.n_blocks || h < 0 || h > p.slots);
+    if (pad || bad) {
+        if (bad) count_error(p, id);
+        return;
+    }
+    const bool fl = flag || (h + T > p.L);  // no room for T more records: flush first
+    const int base = fl ? 0 : h;            // slot of this step's first draft
+    const int tid = threadIdx.x;
+    const int cc = tid % LPR;
+    const int rg = tid / LPR;
+
+    char* bp = p.pool + (int64_t)blk * p.block_bytes;
+    S* ck = reinterpret_cast<S*>(bp + p.ckpt_off) + (int64_t)id.head * (DV * DK);
+    R* rx = reinterpret_cast<R*>(bp + p.recx_off) + (int64_t)id.head * p.slots * DV;
+    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    float* rl = reinterpret_cast<float*>(bp + p.reclam_off) + (int64_t)id.head * p.slots;
+    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
+    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const I* vb = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
+    const int64_t tok0 = (int64_t)id.row * T;
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const SpecGdnLds<R> s = spec_gdn_carve<DV, DK, R>(smem, p.slots, T);
+
+    // 1. small loads, then the checkpoint stream
+    Raw4<TI> qr[QN], kr[QN];
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = min((u * NT + tid) * 4, T * DK - 4);  // clamped: every thread loads
+        const int i = e / DK, c = e - i * DK;
+        qr[u].load(qb + i * p.qs_t + c);
+        kr[u].load(kb + i * p.ks_t + c);
+    }
+    I vr[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) {
+        const int e = min(u * NT + tid, T * DV - 1);
+        const int i = e / DV;
+        vr[u] = vb[i * p.vs_t + (e - i * DV)];
+    }
+    const int64_t dtok = (tok0 + min(tid, T - 1)) * p.n_heads + id.head;
+    const float lam_d = p.lam[dtok];
+    const float beta_d = p.beta[dtok];
+    float lam_c = 0.f;
+    if (h > 0) lam_c = rl[min(tid, h - 1)];
+    const int nk = h * KCH, nrec = nk + h * XCH;
+    auto rsrc = [&](int i) -> const R* {
+        if (i < nk) return rk + (int64_t)i * XE;
+        const int t2 = i - nk, j = t2 / XCH;
+        return rx + (int64_t)j * DV + (t2 - j * XCH) * XE;
+    };
+    auto put = [&](int i, u32x4 v) {  // keys as chunks, corrected values transposed
+        if (i < nk) {
+            reinterpret_cast<u32x4*>(s.kc)[i] = v;
+            return;
+        }
+        const int t2 = i - nk, j = t2 / XCH, e0 = (t2 - j * XCH) * XE;
+        R e[XE];
+        __builtin_memcpy(e, &v, 16);
+#pragma unroll
+        for (int x = 0; x < XE; ++x) s.xc[(e0 + x) * p.slots + j] = e[x];
+    };
+    u32x4 rb[RC];
+    if (nrec > 0) {
+#pragma unroll
+        for (int u = 0; u < RC; ++u) rb[u] = ld_stream(rsrc(min(u * NT + tid, nrec - 1)));
+    }
+    for (int i = RC * NT + tid; i < nrec; i += NT) put(i, ld_stream(rsrc(i)));
+    u32x4 cb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+
+    // 2. to LDS
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = (u * NT + tid) * 4;
+        if (e < T * DK) {
+            qr[u].to(s.qd + e);
+            kr[u].to(s.kd + e);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < VN; ++u)
+        if (u * NT + tid < T * DV) s.vd[u * NT + tid] = to_f<TI>(vr[u]);
+    if (tid < T) {
+        s.lamd[tid] = lam_d;
+        s.betad[tid] = beta_d;
+    }
+#pragma unroll
+    for (int u = 0; u < RC; ++u)
+        if (u * NT + tid < nrec) put(u * NT + tid, rb[u]);
+    __syncthreads();
+
+    // 3. decay weights (wave 0)
+    if (tid < 64) {
+        const int lane = tid;
+        float sfx = lane < h ? lam_c : 0.f;  // inclusive suffix sum of the committed log-decays
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float t = __shfl_down(sfx, off);
+            if (lane + off < 64) sfx += t;
+        }
+        float after = __shfl_down(sfx, 1);
+        if (lane == 63) after = 0.f;
+        if (lane < h) s.ec[lane] = expf(after);
+        if (lane == 0) {
+            s.sc[0] = sfx;
+            s.sc[1] = expf(sfx);
+        }
+        if (lane < T) {  // D_{1:i} and D_{m+1:i} from the draft log-decays
+            float c = 0.f;
+            for (int m = 0; m <= lane; ++m) c += s.lamd[m];
+            s.dexp[lane] = expf(c);
+            for (int m = 0; m <= lane; ++m) {
+                float sm = 0.f;
+                for (int l = m + 1; l <= lane; ++l) sm += s.lamd[l];
+                s.wdd[m * T + lane] = expf(sm);
+            }
+        }
+    }
+
+    // 4. every key (committed, then draft) against every draft's q and k
+    const int nkeys = h + T;
+    for (int j0 = 0; j0 < nkeys; j0 += RPP) {
+        const int j = j0 + rg;
+        float kj[VEC];
+        if (j < h) {
+            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+        } else {
+            const int m = min(j - h, T - 1);
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) kj[c] = s.kd[m * DK + cc * VEC + c];
+        }
+        float part[2 * T];
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                a += kj[c] * s.qd[i * DK + cc * VEC + c];
+                b += kj[c] * s.kd[i * DK + cc * VEC + c];
+            }
+            part[i] = a;
+            part[T + i] = b;
+        }
+        xsum<2 * T, LPR / 2, 1>(part, cc);
+        constexpr int left = xsum_left<2 * T, LPR, 1>();
+        if (j < nkeys && (cc & xsum_dup_mask<2 * T, LPR, 1>()) == 0) {
+            const int b0 = xsum_base<2 * T, LPR, 1>(cc);
+#pragma unroll
+            for (int x = 0; x < left; ++x) {
+                const int v = b0 + x;
+                if (v < T) s.kq[j * T + v] = part[x];
+                else s.kk[j * T + v - T] = part[x];
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. drafts in order: S_h q_i, S_h k_i for the owned rows, then the
+    //    substitution and the output at the lanes that own each row
+    float cf[NR][VEC];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+    const float P = s.sc[1];
+    constexpr int left = xsum_left<NV, LPR, 2>();
+    constexpr int NOWN = left / 2;  // rows this lane ends up with
+    const int b0 = xsum_base<NV, LPR, 2>(cc);
+    const bool owner = (cc & xsum_dup_mask<NV, LPR, 2>()) == 0;
+    float ur[T][NOWN];  // corrected values of the owned rows, drafts so far
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+        float acc[NV];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                a += cf[r][c] * s.qd[i * DK + cc * VEC + c];
+                b += cf[r][c] * s.kd[i * DK + cc * VEC + c];
+            }
+            acc[2 * r] = P * a;
+            acc[2 * r + 1] = P * b;
+        }
+        for (int j = cc; j < h; j += LPR) {
+            const float wq = s.ec[j] * s.kq[j * T + i], wk = s.ec[j] * s.kk[j * T + i];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float u = to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
+                acc[2 * r] += wq * u;
+                acc[2 * r + 1] += wk * u;
+            }
+        }
+        xsum<NV, LPR / 2, 2>(acc, cc);
+        const float D = s.dexp[i], bt = s.betad[i];
+#pragma unroll
+        for (int x = 0; x < NOWN; ++x) {
+            const int row = ((b0 + 2 * x) / 2) * RPP + rg;
+            float u = bt * (s.vd[i * DV + row] - D * acc[2 * x + 1]);
+            float o = D * acc[2 * x];
+#pragma unroll
+            for (int m = 0; m < i; ++m) {
+                const float w = s.wdd[m * T + i];
+                u -= bt * w * s.kk[(h + m) * T + i] * ur[m][x];
+                o += w * s.kq[(h + m) * T + i] * ur[m][x];
+            }
+            o += s.kq[(h + i) * T + i] * u;  // m = i, weight 1
+            ur[i][x] = u;
+            if (owner) p.out[((tok0 + i) * p.n_heads + id.head) * DV + row] = o;
+        }
+    }
+
+    // 6. flush: fold the committed records (only those), store once
+    if (fl) {  // uniform
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) cf[r][c] *= P;
+        for (int j = 0; j < h; ++j) {
+            float kj[VEC];
+            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+            const float ej = s.ec[j];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float f = ej * to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+            }
+        }
+        bool stored = false;
+        if constexpr (std::is_same<TS, tF16>::value) {
+            if (p.sr) {
+                sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
+                stored = true;
+            }
+        }
+        if (!stored) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+        }
+    }
+    // 7. drafts become records base .. base + T - 1: keys, corrected values, log-decays
+#pragma unroll
+    for (int u = 0; u < QN; ++u) {
+        const int e = (u * NT + tid) * 4;
+        if (e < T * DK) {
+            const int i = e / DK, c = e - i * DK;
+            store_f<TR, 4>(rk + (int64_t)(base + i) * DK + c, s.kd + e);
+        }
+    }
+    if (owner) {
+#pragma unroll
+        for (int i = 0; i < T; ++i)
+#pragma unroll
+            for (int x = 0; x < NOWN; ++x)
+                rx[(int64_t)(base + i) * DV + ((b0 + 2 * x) / 2) * RPP + rg] = from_f<TR>(ur[i][x]);
+    }
+    if (tid < T) rl[base + tid] = s.lamd[tid];
+}
+
 // Commit after a verify: one thread per row (see replay_spec_commit).
 __global__ __launch_bounds__(256) void k_spec_commit(const StepParams p) {
     const int row = blockIdx.x * 256 + threadIdx.x;
@@ -1777,23 +2111,35 @@ struct Dispatch {
                     return;
                 }
                 if (kind == Kind::SpecVerify) {
-                    if constexpr (tile_ok<DV, DK, TS, 1>() && split_for<DV, DK>() == 1) {
-                        with_record(L.record_dtype, [&](auto tr) {
-                            using TR = decltype(tr);
-                            with_io(L.io_dtype, [&](auto ti) {
-                                using TI = decltype(ti);
-                                with_spec_T(L.spec_T, [&](auto t_c) {
-                                    constexpr int T = decltype(t_c)::value;
-                                    ok = true;
-                                    if (p) {
-                                        const size_t lds = spec_lds_bytes(L.L, T, DV, DK, (int)sizeof(typename TR::S));
-                                        hipLaunchKernelGGL((k_spec_verify<DV, DK, TS, TR, TI, T>), grid<1>(),
-                                                           dim3(Tile<DV, DK, TS, 1>::NT), lds, stream, *p);
-                                    }
+                    with_form(L.form, [&](auto f_c) {
+                        constexpr int FORM = decltype(f_c)::value;
+                        // Mamba-2: heads of one workgroup's size (64 x 128, 16 x 32);
+                        // Gated DeltaNet: also 128 x 128 in one workgroup
+                        constexpr bool have = FORM == kMamba2 ? (tile_ok<DV, DK, TS, 1>() && split_for<DV, DK>() == 1)
+                                                              : tile_ok<DV, DK, TS, 1>();
+                        if constexpr (have) {
+                            with_record(L.record_dtype, [&](auto tr) {
+                                using TR = decltype(tr);
+                                with_io(L.io_dtype, [&](auto ti) {
+                                    using TI = decltype(ti);
+                                    with_spec_T(L.spec_T, [&](auto t_c) {
+                                        constexpr int T = decltype(t_c)::value;
+                                        ok = true;
+                                        if (!p) return;
+                                        const int rb = (int)sizeof(typename TR::S);
+                                        const dim3 block(Tile<DV, DK, TS, 1>::NT);
+                                        if constexpr (FORM == kMamba2)
+                                            hipLaunchKernelGGL((k_spec_verify<DV, DK, TS, TR, TI, T>), grid<1>(), block,
+                                                               spec_lds_bytes(L.L, T, DV, DK, rb), stream, *p);
+                                        else
+                                            hipLaunchKernelGGL((k_spec_verify_gdn<DV, DK, TS, TR, TI, T>), grid<1>(),
+                                                               block, spec_gdn_lds_bytes(L.L, T, DV, DK, rb), stream,
+                                                               *p);
+                                    });
                                 });
                             });
-                        });
-                    }
+                        }
+                    });
                     return;
                 }
                 if (kind == Kind::SpecCommit) {
@@ -1882,7 +2228,8 @@ struct Dispatch {
 // Upper bound over the splits (a workgroup owning all d_v rows).
 size_t lds_bytes(Kind kind, const rs_layer& layer) {
     if (kind == Kind::SpecVerify)
-        return spec_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, layer.record_dtype == RS_F32 ? 4 : 2);
+        return (layer.form == RS_GDN ? spec_gdn_lds_bytes : spec_lds_bytes)(layer.L, layer.spec_T, layer.d_v, layer.d_k,
+                                                                           layer.record_dtype == RS_F32 ? 4 : 2);
     if (kind != Kind::ReplayStep && kind != Kind::Flush) return 0;
     const int slots = layer.spec_T > 0 ? layer.L : layer.L - 1;
     const size_t rb = layer.record_dtype == RS_F32 ? 4 : 2;

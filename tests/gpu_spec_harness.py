@@ -24,6 +24,7 @@ from linear_attention_decode_replay_amd.state import SpecDecodeLayer
 
 @dataclass
 class SpecCase:
+    form: int = rs.MAMBA2
     B: int = 2
     H: int = 4
     dv: int = 16
@@ -44,7 +45,8 @@ class SpecCase:
     force_row0_every: int = 0        # > 0: force a flush on row 0 every n steps
 
     def name(self):
-        return (f"spec B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
+        f = "gdn" if self.form == rs.GDN else "mamba2"
+        return (f"spec {f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} accept={self.accept} "
                 f"strided={self.strided} pad={self.pad_rows} seed={self.seed}")
 
@@ -61,7 +63,7 @@ def _device(t: torch.Tensor, strided: bool, dev):
 
 def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     say(f"[case] {c.name()}")
-    lay = rs.layer(rs.MAMBA2, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T)
     n_blocks = c.B + 3
     d = SpecDecodeLayer(lay, c.B, n_blocks, dev)
     d.pool.raw.fill_(0xFF)  # NaN in every dtype: a slot read before it is written shows up
@@ -72,14 +74,14 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     d.upload(rows=live)
     sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live]
     ns = len(sample)
-    spec = oracle.SpecReplayModel(ns, c.H, c.dv, c.dk, c.L, c.T)
-    ref = oracle.SpecTokenByToken(ns, c.H, c.dv, c.dk, c.T)
+    spec = oracle.SpecReplayModel(ns, c.H, c.dv, c.dk, c.L, c.T, form=c.form)
+    ref = oracle.SpecTokenByToken(ns, c.H, c.dv, c.dk, c.T, form=c.form)
     h = np.full(c.B, -1, np.int32)
     h[live] = 0
     rdt = workloads.torch_dtype(c.rec_dt)
-    err = {"out_spec": 0.0, "out_vs_tokens": 0.0, "ckpt_flush": 0.0, "flushes": 0, "accepted": 0}
+    err = {"out_spec": 0.0, "out_vs_tokens": 0.0, "ckpt_flush": 0.0, "rec_u": 0.0, "flushes": 0, "accepted": 0}
     for s in range(c.steps):
-        tok = workloads.spec_tokens(c.seed, s, c.B, c.H, c.T, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
+        tok = workloads.spec_tokens(c.seed, s, c.B, c.H, c.T, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi, c.form)
         force = np.zeros(c.B, np.uint8)
         if c.force_row0_every and (s + 1) % c.force_row0_every == 0 and 0 in live:
             force[0] = 1
@@ -92,15 +94,17 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
         assert np.array_equal(dflag[live].astype(bool), fl[live].astype(bool)), f"device flags, step {s}"
         q, k, v = (_device(t, c.strided, dev) for t in (tok.q, tok.k, tok.v))
         lam = tok.lam.to(dev)
+        beta = tok.beta.to(dev) if tok.beta is not None else None
         out = torch.full((c.B, c.T, c.H, c.dv), float("nan"), device=dev)
-        d.verify(rs.make_spec_io(q, k, v, lam, out))
+        d.verify(rs.make_spec_io(q, k, v, lam, out, beta))
         # oracle routes on the sampled rows, tile-major [rows, H, T, d]
         tm = lambda t: t[sample].double().numpy().transpose(0, 2, 1, 3)
         q64, k64, v64 = tm(tok.q), tm(tok.k), tm(tok.v)
         lam64 = tok.lam[sample].double().numpy().transpose(0, 2, 1)
+        beta64 = None if tok.beta is None else tok.beta[sample].double().numpy().transpose(0, 2, 1)
         flr = fl[sample].astype(bool)
-        o_spec = spec.verify(q64, k64, v64, lam64, flr)
-        o_tok = ref.verify(q64, k64, v64, lam64)
+        o_spec = spec.verify(q64, k64, v64, lam64, flr, beta=beta64)
+        o_tok = ref.verify(q64, k64, v64, lam64, beta64)
         torch.cuda.synchronize()
         got = out[sample].double().cpu().numpy().transpose(0, 2, 1, 3)
         err["out_spec"] = max(err["out_spec"], rel_err(got, o_spec))
@@ -115,7 +119,10 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
             got_k = d.pool.rec_k()[blk[i_row], :, sl].cpu()          # [H, T, dk]
             assert torch.equal(got_k, tok.k[b].transpose(0, 1).to(rdt)), f"k records, row {b}, step {s}"
             got_v = d.pool.rec_x()[blk[i_row], :, sl].cpu()
-            assert torch.equal(got_v, tok.v[b].transpose(0, 1).to(rdt)), f"v records, row {b}, step {s}"
+            if c.form == rs.MAMBA2:
+                assert torch.equal(got_v, tok.v[b].transpose(0, 1).to(rdt)), f"v records, row {b}, step {s}"
+            else:  # the drafts' corrected values, against running them token by token
+                err["rec_u"] = max(err["rec_u"], rel_err(got_v.double().numpy(), ref.drafts_x[i_row]))
             got_l = d.pool.rec_lam()[blk[i_row], :, sl].cpu()
             assert torch.equal(got_l, tok.lam[b].transpose(0, 1)), f"lam records, row {b}, step {s}"
         flushed = [i for i, b in enumerate(sample) if fl[b]]

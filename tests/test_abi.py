@@ -181,8 +181,8 @@ def test_spec_block_layout_ring_of_L():
 
 @pytest.mark.parametrize("bad,code", [
     (dict(spec_T=3), rs.RS_EUNSUPPORTED), (dict(spec_T=8, L=4), rs.RS_EINVAL),
-    (dict(spec_T=-1), rs.RS_EINVAL), (dict(spec_T=4, form=rs.GDN), rs.RS_EUNSUPPORTED),
-    (dict(spec_T=4, d_v=128, d_k=128), rs.RS_EUNSUPPORTED),
+    (dict(spec_T=-1), rs.RS_EINVAL), (dict(spec_T=4, d_v=128, d_k=128), rs.RS_EUNSUPPORTED),   # Mamba-2
+    (dict(spec_T=4, form=rs.GDN, d_v=32, d_k=64), rs.RS_EUNSUPPORTED),
     (dict(spec_T=4, read_dtype="f16"), rs.RS_EUNSUPPORTED),
 ])
 def test_spec_layer_validation(bad, code):
@@ -383,3 +383,21 @@ def test_flush_hint_validation():
         with pytest.raises(rs.ReplaySSMError) as e:
             rs.replay_decode_step(layer, batch, io, stream=0)
         assert e.value.code == rs.RS_EINVAL and "flush_hint" in rs.last_error()
+
+
+def test_gdn_spec_layers_accepted():
+    """Gated DeltaNet speculative layers at 16 x 32, 64 x 128 and 128 x 128;
+    the verify needs beta."""
+    for dv, dk in ((16, 32), (64, 128), (128, 128)):
+        lay = rs.layer(rs.GDN, 4, dv, dk, 16, "f32", "f16", "bf16", None, 4)
+        assert rs.layer_supported(lay) == rs.RS_OK
+        assert rs.block_layout(lay).slots == 16
+    layer = rs.layer(rs.GDN, 2, 16, 32, 8, "f32", "f32", "f32", None, 2)
+    buf = (ctypes.c_uint8 * 4096)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    batch = rs.RsBatch(1, 0, 1, base, base, base, None, None)
+    io = rs.RsSpecIO(base, base, base, 2 * 2 * 32, 2 * 32, 32, 2 * 2 * 32, 2 * 32, 32, 2 * 2 * 16, 2 * 16, 16,
+                     base, base, None)
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_spec_verify(layer, batch, io, stream=0)
+    assert e.value.code == rs.RS_EINVAL and "beta" in rs.last_error()

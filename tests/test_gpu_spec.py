@@ -102,3 +102,46 @@ def test_spec_layer_rejects_standard_step():
     with pytest.raises(rs.ReplaySSMError) as e:
         rs.replay_decode_step(lay, d.batch[0], io)
     assert e.value.code == rs.RS_EINVAL
+
+
+# ------------------------------------------------------- Gated DeltaNet form --
+def _check_gdn(err, tol):
+    _check(err, tol)
+    assert err["rec_u"] <= tol, err   # the drafts' corrected values, stored as records
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_spec_gdn_tiny_fp32(T):
+    """Gated DeltaNet drafts through the triangular solve: tiny heads, fp32,
+    random accepted counts, L = 8."""
+    err = run_spec_case(SpecCase(form=rs.GDN, T=T, steps=40, seed=30 + T))
+    assert err["flushes"] >= 3
+    _check_gdn(err, TOL_F32)
+
+
+@pytest.mark.parametrize("accept", ["all", "none"])
+def test_spec_gdn_accept_policies(accept):
+    err = run_spec_case(SpecCase(form=rs.GDN, T=4, L=16, steps=30, accept=accept, seed=37))
+    _check_gdn(err, TOL_F32)
+
+
+def test_spec_gdn_strided_padding_forced_lowprec():
+    err = run_spec_case(SpecCase(form=rs.GDN, B=4, T=4, L=8, steps=30, rec_dt="f16", io_dt="bf16", strided=True,
+                                 pad_rows=[1], force_row0_every=4, seed=38))
+    _check_gdn(err, TOL_LOW)
+
+
+@pytest.mark.parametrize("state_dt", ["f32", "f16"])
+def test_spec_gdn_128x128(state_dt):
+    """The Gated DeltaNet head (32 heads, 128 x 128, one workgroup per tile),
+    batch 64, L = 16, T = 4, bf16 inputs, fp16 records; 3 rows sampled."""
+    err = run_spec_case(SpecCase(form=rs.GDN, B=64, H=32, dv=128, dk=128, L=16, T=4, steps=16, state_dt=state_dt,
+                                 rec_dt="f16", io_dt="bf16", sample=[0, 31, 63], seed=39))
+    assert err["flushes"] >= 1
+    _check_gdn(err, TOL_LOW)
+
+
+def test_spec_gdn_T8_64x128():
+    err = run_spec_case(SpecCase(form=rs.GDN, B=16, H=16, dv=64, dk=128, L=16, T=8, steps=12, rec_dt="f16",
+                                 io_dt="bf16", sample=[0, 15], seed=40))
+    _check_gdn(err, TOL_LOW)

@@ -197,16 +197,20 @@ class SpecTokens:
     k: torch.Tensor      # [B, T, H, dk] io dtype
     v: torch.Tensor      # [B, T, H, dv] io dtype
     lam: torch.Tensor    # [B, T, H] float32
+    beta: torch.Tensor | None = None  # [B, T, H] float32 (Gated DeltaNet) or None
 
 
 def spec_tokens(seed: int, step: int, B: int, H: int, T: int, dv: int, dk: int, io: str = "bf16",
-                a_lo: float = 1.0, a_hi: float = 8.0) -> SpecTokens:
-    """T draft tokens per row for speculative step `step` (Mamba-2 recipe);
-    draft i of step s is the Mamba-2 token of step T s + i, so the same
-    per-head decay scales apply."""
-    toks = [mamba2_tokens(seed, T * step + i, B, H, dv, dk, io, a_lo, a_hi) for i in range(T)]
+                a_lo: float = 1.0, a_hi: float = 8.0, form: int = 0) -> SpecTokens:
+    """T draft tokens per row for speculative step `step`; draft i of step s
+    is the token of step T s + i of the form's recipe (Mamba-2: the same
+    per-head decay scales apply; Gated DeltaNet: unit-norm q, k and beta)."""
+    if form == 0:
+        toks = [mamba2_tokens(seed, T * step + i, B, H, dv, dk, io, a_lo, a_hi) for i in range(T)]
+    else:
+        toks = [gdn_tokens(seed, T * step + i, B, H, dv, dk, io) for i in range(T)]
     st = lambda name: torch.stack([getattr(t, name) for t in toks], dim=1).contiguous()
-    return SpecTokens(st("q"), st("k"), st("v"), st("lam"))
+    return SpecTokens(st("q"), st("k"), st("v"), st("lam"), st("beta") if form else None)
 
 
 def spec_accepted(seed: int, step: int, B: int, T: int, policy: str = "random") -> np.ndarray:
