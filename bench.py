@@ -426,7 +426,7 @@ def suite_stack(out, n_layers=40):
             print(json.dumps(line), file=out, flush=True)
 
 
-def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush):
+def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0):
     """Algorithmic HBM bytes of one speculative verify launch (rows with h
     committed records, flushing or not) plus its commit launch.  Per (row,
     head): read the checkpoint and the h committed records, read T draft
@@ -438,13 +438,14 @@ def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush):
     flush = np.asarray(flush, bool)
     ms = dv * dk * _ES[state]
     r = (dv + dk) * _ES[rec] + 4
-    tok = (2 * dk + dv) * _ES[io] + 4
+    tok = (2 * dk + dv) * _ES[io] + 4 + (4 if form == 1 else 0)  # q, k, v, log-decay (and beta)
     per_head = ms + h * r + T * (tok + r + 4 * dv) + np.where(flush, ms, 0)
     return float(np.sum(H * per_head + 9) + B * 18)
 
 
-def suite_spec(out, steps=48, n_pools=4):
-    """Speculative verify at the Nemotron-3-Super layer shape, batch 256,
+def suite_spec(out, steps=48, n_pools=4, workload="nemotron"):
+    """Speculative verify at the Nemotron-3-Super layer shape (or, workload
+    "gdn", the Gated DeltaNet layer: 32 heads, 128 x 128), batch 256,
     L = 16, fp32 checkpoint, fp16 records, bf16 inputs, T in {4, 8}, with
     every draft accepted, one token per step, and uniform 0..T acceptance.
     One step = one verify launch + one commit launch (the committed counts
@@ -457,8 +458,9 @@ def suite_spec(out, steps=48, n_pools=4):
     import workloads
     from linear_attention_decode_replay_amd.state import SpecDecodeLayer
     dev = torch.device("cuda", 0)
-    base = dict(WORKLOADS["nemotron"])
+    base = dict(WORKLOADS[workload])
     B, H, dv, dk, L = base["B"], base["H"], base["dv"], base["dk"], base["L"]
+    form = base["form"]
     # standard steps for reference (one token per row per step)
     ios, keep = _inputs(base, B, 16, dev)
     ref_us = {}
@@ -483,13 +485,14 @@ def suite_spec(out, steps=48, n_pools=4):
         torch.cuda.empty_cache()
     del ios, keep
     for T in (4, 8):
-        lay = rs.layer(0, H, dv, dk, L, "f32", "f16", "bf16", None, T)
+        lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", None, T)
         drafts = []
         for s in range(8):
-            t = workloads.spec_tokens(11, s, B, H, T, dv, dk, "bf16")
+            t = workloads.spec_tokens(11, s, B, H, T, dv, dk, "bf16", form=form)
             q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
+            beta = t.beta.to(dev) if t.beta is not None else None
             o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-            drafts.append(((q, k, v, lam, o), rs.make_spec_io(q, k, v, lam, o)))
+            drafts.append(((q, k, v, lam, o, beta), rs.make_spec_io(q, k, v, lam, o, beta)))
         for policy in ("all", "one", "random"):
             pools = []
             for _ in range(n_pools):
@@ -513,7 +516,7 @@ def suite_spec(out, steps=48, n_pools=4):
                 a = acc_host[s % steps]
                 fl = rs.rs_spec_meta_step(L, T, hm)
                 if s >= n_warm:
-                    nbytes += spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl)
+                    nbytes += spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form)
                     tokens += int(a.sum())
                     n_flush += int(fl.sum())
                 d.verify(drafts[s % 8][1])
@@ -528,7 +531,7 @@ def suite_spec(out, steps=48, n_pools=4):
                 raise RuntimeError(f"{errs} tiles or rows flagged by the speculative kernels' checks")
             gb = nbytes / steps / 1e9
             tok_per_row = tokens / steps / B
-            line = {"suite": "spec_verify", "T": T, "accept": policy, "batch": B, "L": L,
+            line = {"suite": "spec_verify", "workload": workload, "T": T, "accept": policy, "batch": B, "L": L,
                     "us_per_step": round(us, 2), "gb_per_step": round(gb, 4), "tbs": round(gb / (us * 1e-6) / 1e3, 3),
                     "committed_tokens_per_row_step": round(tok_per_row, 3),
                     "flush_fraction": round(n_flush / (steps * B), 4),
@@ -756,6 +759,7 @@ def main(argv=None):
                 suite_stack(out)
             if args.suite_only in (None, "spec"):
                 suite_spec(out)
+                suite_spec(out, workload="gdn")
             if args.suite_only in (None, "continuous"):
                 suite_continuous(out)
         print(open(args.suite).read(), end="")
