@@ -179,6 +179,42 @@ class DecodeLayer:
         rs_meta_advance(self.L, self.anchor, fl)
         return wp, fl
 
+    def capture_steps(self, ios, stream=None):
+        """Capture consecutive checkpoint + buffer steps into a HIP graph
+        (PR "CUDA graphs and continuous batching": the cursor and the flush
+        decision live on the device, so a steady decode loop can be
+        captured).  ios: one rs_step_io per step, an even number of them (the
+        graph returns the cursor arrays to the parity it started from); the
+        caller refreshes the buffers behind them before each replay and calls
+        advance_host(len(ios)) after it.  The batch must be steady: no upload
+        pending, no forced flush, no stochastic rounding (its counter would be
+        fixed in the graph).  Every step runs one kernel over all rows."""
+        if len(ios) % 2:
+            raise ValueError("capture an even number of steps")
+        if self.layer.state_rounding:
+            raise ValueError("stochastic rounding draws a fresh counter per launch: no graph capture")
+        if self._dirty or self._forced_last:
+            raise ValueError("metadata upload pending: run an eager step first")
+        stream = stream or torch.cuda.Stream(self.device)
+        stream.wait_stream(torch.cuda.current_stream(self.device))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cur = self._cur
+            for io in ios:
+                b = self.batch[cur]
+                b.flush_hint = RS_FLUSH_UNKNOWN
+                replay_decode_step(self.layer, b, io, stream)
+                cur ^= 1
+        torch.cuda.current_stream(self.device).wait_stream(stream)
+        return g
+
+    def advance_host(self, n_steps: int) -> None:
+        """The host cursor after n_steps steps run outside step() (graph
+        replays): no row forced, every live row one token per step."""
+        for _ in range(n_steps):
+            _, fl = rs_meta_step(self.L, self.anchor)
+            rs_meta_advance(self.L, self.anchor, fl)
+
     def conventional_step(self, io, stream=None, events=None) -> None:
         stream = stream or torch.cuda.current_stream(self.device)
         if self._dirty:
@@ -290,6 +326,30 @@ class SpecDecodeLayer:
         stream = stream or torch.cuda.current_stream(self.device)
         replay_spec_commit(self.layer, self.batch[self._cur], accepted, self.flag[1 - self._cur], stream)
         self._cur ^= 1
+
+    def capture_steps(self, ios, accepted, stream=None):
+        """Capture verify + commit steps into a HIP graph (the blog,
+        "Speculative decoding": the flush rule depends only on h and T, so
+        the decision lives inside a captured graph).  ios: one rs_spec_io per
+        step, an even number of them; accepted: one device int32 [n_slots]
+        tensor per step, which the caller fills (from sampling on the
+        device) before each replay.  No stochastic rounding (its counter
+        would be fixed in the graph)."""
+        if len(ios) % 2 or len(ios) != len(accepted):
+            raise ValueError("an even number of steps, one accepted-count tensor per step")
+        if self.layer.state_rounding:
+            raise ValueError("stochastic rounding draws a fresh counter per launch: no graph capture")
+        stream = stream or torch.cuda.Stream(self.device)
+        stream.wait_stream(torch.cuda.current_stream(self.device))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cur = self._cur
+            for io, acc in zip(ios, accepted):
+                replay_spec_verify(self.layer, self.batch[cur], io, stream)
+                replay_spec_commit(self.layer, self.batch[cur], acc, self.flag[1 - cur], stream)
+                cur ^= 1
+        torch.cuda.current_stream(self.device).wait_stream(stream)
+        return g
 
     def device_committed(self):
         """(committed counts, flags) the next verify will read (synchronises)."""
