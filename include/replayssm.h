@@ -228,18 +228,21 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               rs_meta_advance).  Passing it as the next step's write_pos
  *               lets a caller skip the per-step host -> device copy while
  *               the batch is unchanged.  Must not alias write_pos.
- *   flush_hint  replay_decode_step with a two-precision checkpoint only
- *               (other layers ignore it and process every row): what the
- *               caller knows of this step's flushing rows (rs_flush_hint).
- *               RS_FLUSH_UNKNOWN (0) runs one kernel over all rows.
- *               RS_FLUSH_NONE promises that no row flushes and runs a kernel
- *               built without the fold (fewer registers, more waves in
- *               flight on the small read copy); RS_FLUSH_ALL promises that
- *               every non-padding row flushes; RS_FLUSH_MIXED runs the
- *               no-fold kernel over the rows that do not flush and then the
- *               full kernel over those that do.  A row that breaks a
- *               promise is skipped and counted in err_count (never computed
- *               wrongly).
+ *   flush_hint  replay_decode_step only: what the caller knows of this
+ *               step's flushing rows (rs_flush_hint).  RS_FLUSH_UNKNOWN (0)
+ *               runs one kernel over all rows.
+ *               Two-precision checkpoints: RS_FLUSH_NONE promises that no row
+ *               flushes and runs a kernel built without the fold;
+ *               RS_FLUSH_ALL promises that every non-padding row flushes;
+ *               RS_FLUSH_MIXED runs the no-fold kernel over the rows that do
+ *               not flush and then the full kernel over those that do.
+ *               Mamba-2 with one fp32 checkpoint: RS_FLUSH_NONE runs a
+ *               persistent kernel without the fold that streams the
+ *               checkpoint tiles with the next tile's loads in flight and
+ *               stores the outputs and records after the stream; the other
+ *               hints are not used.  Other layers do not use the hint.
+ *               Where a hint is used, a row that breaks its promise is
+ *               skipped and counted in err_count (never computed wrongly).
  */
 typedef enum {
     RS_FLUSH_UNKNOWN = 0,

@@ -207,11 +207,8 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.heads_per_group = L.n_heads / groups_of(L);
     p.sr = L.state_rounding == RS_ROUND_STOCHASTIC;
     p.reconstruct = L.gdn_route == RS_GDN_RECONSTRUCT;
-    // the hint picks kernels for two-precision layers only (measured: the
-    // kernel without the fold gains 27 % on an E4M3 read copy's non-flush
-    // steps and loses 1-2 % on a single checkpoint, where the stream is
-    // already bandwidth-bound)
-    p.flush_hint = two_precision(L) ? b.flush_hint : RS_FLUSH_UNKNOWN;
+    // (the state-reconstruction route has one kernel for every row)
+    p.flush_hint = p.reconstruct ? RS_FLUSH_UNKNOWN : b.flush_hint;
     p.sr_key0 = b.sr_key0;
     p.sr_key1 = b.sr_key1;
     p.sr_step = b.sr_step;

@@ -36,6 +36,9 @@ struct StepParams {
     int32_t sr;                // stochastic rounding of 16-bit state stores
     int32_t reconstruct;       // Gated DeltaNet: rebuild S_{t-1} on every step
     int32_t flush_hint;        // rs_flush_hint of the launch (see k_replay_step)
+    int32_t meta_off;          // persistent replay step: LDS byte offsets of the rows' metadata
+    int32_t defer_off;         //   and of the deferred writes,
+    int32_t defer_cap;         //   and the items these hold
     uint64_t sr_key0, sr_key1, sr_step;
     // speculative verify / commit
     int32_t spec_T;

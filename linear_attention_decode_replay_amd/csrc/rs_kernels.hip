@@ -36,7 +36,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "rs_internal.h"
 
@@ -554,6 +557,14 @@ struct RecordCopy {
         const int t = i - nk, j = t / XCH;
         return rx + (int64_t)j * DV + (t - j * XCH) * XE;
     }
+    // the same with no branch: w = 0 loads (and commit ignores) the first
+    // chunk, so the ring must have a slot
+    __device__ __forceinline__ void issue_always(const R* rk, const R* rx, int w) {
+        nk = w * KCH;
+        n = nk + w * XCH;
+#pragma unroll
+        for (int u = 0; u < RC; ++u) buf[u] = ld_stream(src(rk, rx, min(u * NT + (int)threadIdx.x, max(n - 1, 0))));
+    }
     __device__ __forceinline__ void issue(const R* rk, const R* rx, int w) {
         nk = w * KCH;
         n = nk + w * XCH;
@@ -562,6 +573,10 @@ struct RecordCopy {
             for (int u = 0; u < RC; ++u) buf[u] = ld_stream(src(rk, rx, min(u * NT + (int)threadIdx.x, n - 1)));
         }
     }
+    // TAIL = false: the records fit the first RC * NT chunks (the caller
+    // checked), so the remainder loop, whose loads would make the compiler
+    // wait for every outstanding load, is left out.
+    template <bool TAIL = true>
     __device__ __forceinline__ void commit(const R* rk, const R* rx, R* sk, R* sx) {
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
@@ -571,6 +586,7 @@ struct RecordCopy {
                 else reinterpret_cast<u32x4*>(sx)[i - nk] = buf[u];
             }
         }
+        if constexpr (TAIL)
         for (int i = RC * NT + (int)threadIdx.x; i < n; i += NT) {
             const u32x4 c = ld_stream(src(rk, rx, i));
             if (i < nk) reinterpret_cast<u32x4*>(sk)[i] = c;
@@ -663,131 +679,328 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // then the first over those that do) and decides what a row that breaks it
 // means: skipped, and counted as an error.
 constexpr int kAllRows = 0, kNonFlushRows = 1;
+constexpr int kMaxRecords = 63;  // a ring holds at most L - 1 <= 63 records
 // The instantiation without the fold gives each thread 4 read-copy chunks
 // (an E4M3 tile then takes 128 threads instead of 256): the fold's registers
 // are gone, and twice the bytes per wave are in flight.
 template <int DV, int DK, class TL, int SPLIT, int ROWS>
 using StepTile = Tile<DV, DK, TL, SPLIT, ROWS == kNonFlushRows ? 4 : 0>;
 
-template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false,
-          int ROWS = kAllRows>
-__global__ __launch_bounds__((StepTile<DV, DK, TL, SPLIT, ROWS>::NT),
-                             1)
-void k_replay_step(const StepParams p) {
-    using T = StepTile<DV, DK, TL, SPLIT, ROWS>;
-    using S = typename TS::S;
-    using RL = typename TL::S;
-    using R = typename TR::S;
-    using I = typename TI::S;
-    constexpr int NT = T::NT, VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
-    constexpr int KEEP = FORM == kGdn ? 2 : 1;  // Gated DeltaNet keeps (C q, C k) of a row together
-    constexpr int NV = KEEP * NR;
-    constexpr bool TWO = !std::is_same<TS, TL>::value;
-    constexpr bool SC = kScaled<TL>;                // read copy with per-row scales
-    constexpr int HPC = VEC * (int)sizeof(S) / 16;  // recurrence-copy chunks per lane chunk
-    constexpr int EPC = VEC / HPC;                  // elements per recurrence-copy chunk
+// One non-flush tile's writes, held in LDS by a persistent workgroup until
+// its tiles are done (see k_replay_step): the owned output rows, the record
+// (key, owned value or corrected-value rows, log-decay) and where they go
+// (work item = tile * SPLIT + part, block, cursor; cursor -1: nothing).
+template <int DVW, int DK, class R>
+struct Deferred {
+    static constexpr int OUT = DVW * 4, KB = DK * (int)sizeof(R), XB = DVW * (int)sizeof(R);
+    static constexpr int BYTES = OUT + KB + XB + 16;  // + work item, block, cursor, log-decay
+    static_assert(OUT % 16 == 0 && KB % 16 == 0 && XB % 16 == 0, "16-byte pieces");
+    float* out;
+    R* k;
+    R* x;
+    int* meta;
+    float* lam;
+    __device__ __forceinline__ explicit Deferred(char* e)
+        : out(reinterpret_cast<float*>(e)), k(reinterpret_cast<R*>(e + OUT)), x(reinterpret_cast<R*>(e + OUT + KB)),
+          meta(reinterpret_cast<int*>(e + OUT + KB + XB)), lam(reinterpret_cast<float*>(e + OUT + KB + XB + 12)) {}
+};
 
-    const TileIds id = tile_ids<SPLIT>(p);
-    // Without a flag array the (always present) cursor array is read in its
-    // place and the result discarded, so that the load is unconditional.
-    const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
-    const bool flag = row_flag(fsrc, id.row) && p.flush;
-    const int blk = p.block_table[id.row];
-    const int w = p.write_pos[id.row];
-    const bool pad = blk < 0;
-    const bool bad = !pad && (blk >= p.n_blocks || w < 0 || w > p.slots);
-    if (pad || bad) {
+// N io elements of one lane, held as raw words from the load until they are
+// used, so that a tile issued ahead of its arithmetic keeps its loads in
+// flight.
+template <class T, int N>
+struct RawIo {
+    using S = typename T::S;
+    static constexpr int BYTES = N * (int)sizeof(S);
+    static_assert(BYTES == 8 || BYTES % 16 == 0, "8 bytes or whole 16-byte chunks");
+    uint32_t w[BYTES / 4];
+    __device__ __forceinline__ void load(const S* __restrict__ p) {
+        if constexpr (BYTES == 8) {
+            const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+            w[0] = r[0];
+            w[1] = r[1];
+        } else {
+#pragma unroll
+            for (int i = 0; i < BYTES / 16; ++i) {
+                const u32x4 r = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[4 * i + j] = r[j];
+            }
+        }
+    }
+    __device__ __forceinline__ void to_float(float* out) const {
+        S tmp[N];
+        __builtin_memcpy(tmp, w, BYTES);
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = to_f<T>(tmp[i]);
+    }
+};
+
+// Where one (row, head, part) tile's data lives.
+template <int DV, int DK, class TS, class TR, class TI, class TL, int DVW>
+struct TilePtrs {
+    typename TS::S* ck;        // checkpoint (recurrence copy), owned rows
+    typename TL::S* cl;        // read copy (two-precision checkpoint)
+    float* cs;                 // read-copy row scales (scaled formats)
+    typename TR::S* rx;        // value records, owned rows
+    typename TR::S* rk;        // key records of the head's group
+    float* rl;                 // log-decay records
+    const typename TI::S* qp;  // this row's query, key and value tokens
+    const typename TI::S* kp;
+    const typename TI::S* vp;
+    bool key_owner;            // the tile appends its group's key
+    __device__ __forceinline__ TilePtrs(const StepParams& p, const TileIds& id, int blk) {
+        using S = typename TS::S;
+        using RL = typename TL::S;
+        using R = typename TR::S;
+        using I = typename TI::S;
+        const int row0 = id.part * DVW;
+        char* base = p.pool + (int64_t)blk * p.block_bytes;
+        ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+        cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
+        cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;
+        rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
+        // keys and queries per group of heads_per_group heads (1: per head)
+        const int grp = id.head / p.heads_per_group;
+        key_owner = id.head == grp * p.heads_per_group;
+        rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.slots * DK;
+        rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
+        qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
+        kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
+        vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
+    }
+};
+
+// A tile's loads (tile_issue_small, tile_issue_stream) and whether it runs; tile_finish
+// does its arithmetic and stores.  The two halves let a persistent
+// workgroup issue the next tile's loads before it computes the current one.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS>
+struct TileIn {
+    using T = StepTile<DV, DK, TL, SPLIT, ROWS>;
+    static constexpr int VEC = T::VEC, NR = T::NR, NT = T::NT, DVW = T::DVW;
+    static constexpr int HPC = VEC * (int)sizeof(typename TS::S) / 16;  // recurrence-copy chunks per lane chunk
+    static constexpr int EPC = VEC / HPC;                               // elements per recurrence-copy chunk
+    TileIds id;
+    int blk, w;
+    bool run, fl;  // the tile is computed here; it flushes
+    RawIo<TI, EPC> qr[HPC], kr[HPC];
+    typename TI::S vr;
+    float lam, lam_j;
+    RecordCopy<DV, DVW, DK, typename TR::S, NT, 2> rec;
+    float rsc[NR];  // scales of the owned read-copy rows (scaled formats)
+    u32x4 cb[NR * HPC];
+};
+
+// Whether a tile runs in this launch, and whether it flushes, from its row's
+// metadata; a skipped tile is counted as an error where the flush hint's
+// rules say so.  ERR_LDS (persistent workgroups, one item per thread while
+// they stage their items): counted in LDS, so that no global write is
+// pending in the loop that issues ahead (the compiler then waits for every
+// outstanding load at once).
+template <int ROWS, bool ERR_LDS = false>
+__device__ __forceinline__ bool tile_runs(const StepParams& p, const TileIds& id, int blk, int w, bool flag, bool& fl,
+                                          int* err_lds = nullptr) {
+    fl = false;
+    if (blk < 0) return false;  // padding
+    auto error = [&]() {
+        if constexpr (ERR_LDS) {
+            if (id.part == 0) atomicAdd(err_lds, 1);
+        } else {
+            count_error(p, id);
+        }
+    };
+    if (blk >= p.n_blocks || w < 0 || w > p.slots) {
         // a pair of launches counts a bad tile once, in the first
-        if (bad && !(ROWS == kAllRows && p.flush_hint == RS_FLUSH_MIXED)) count_error(p, id);
-        return;
+        if (!(ROWS == kAllRows && p.flush_hint == RS_FLUSH_MIXED)) error();
+        return false;
     }
     const bool fl_row = (w == p.slots) || flag;
     if constexpr (ROWS == kNonFlushRows) {
         if (fl_row) {
-            if (p.flush_hint == RS_FLUSH_NONE) count_error(p, id);  // the hint was wrong
-            return;
+            if (p.flush_hint == RS_FLUSH_NONE) error();  // the hint was wrong
+            return false;
         }
+        return true;
     } else {
         if (!fl_row && (p.flush_hint == RS_FLUSH_ALL || p.flush_hint == RS_FLUSH_MIXED)) {
-            if (p.flush_hint == RS_FLUSH_ALL) count_error(p, id);
-            return;
+            if (p.flush_hint == RS_FLUSH_ALL) error();
+            return false;
+        }
+        fl = fl_row;
+        return true;
+    }
+}
+
+// The small loads of a tile that runs (tokens, buffered decays and records;
+// the checkpoint stream is tile_issue_stream's), issued before the stream so
+// that waiting for them never waits for the stream.  UNCOND (tiles that do
+// not flush, so the ring has a slot 0): no branch around any load, a ring
+// with no records yet reading slot 0 and ignoring it, so that a loop that
+// issues ahead has none either.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS, bool UNCOND = false>
+__device__ __forceinline__ void tile_issue_small(const StepParams& p, const TileIds id, int blk, int w, bool fl,
+                                                 TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in) {
+    using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
+    using T = typename In::T;
+    constexpr int LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr bool SC = kScaled<TL>;
+    constexpr int HPC = In::HPC, EPC = In::EPC;
+    static_assert(!UNCOND || ROWS == kNonFlushRows, "unconditional loads: non-flush tiles only");
+
+    in.id = id;
+    in.blk = blk;
+    in.w = w;
+    in.run = true;
+    in.fl = fl;
+    const int tid = threadIdx.x;
+    const int cc = tid % LPR;  // column chunk
+    const int rg = tid / LPR;  // row within a pass
+    const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, id, blk);
+    in.lam = p.lam[id.tile];
+    // column of element h * EPC + i of this lane's share of a row
+    const int col0 = EPC * cc;
+#pragma unroll
+    for (int h = 0; h < HPC; ++h) {
+        in.qr[h].load(P.qp + col0 + EPC * LPR * h);
+        in.kr[h].load(P.kp + col0 + EPC * LPR * h);
+    }
+    in.vr = P.vp[min(tid, DVW - 1)];
+    if constexpr (UNCOND) {
+        in.lam_j = P.rl[min(tid, max(w - 1, 0))];
+        in.rec.issue_always(P.rk, P.rx, w);
+    } else {
+        in.lam_j = w > 0 ? P.rl[min(tid, w - 1)] : 0.f;
+        in.rec.issue(P.rk, P.rx, w);
+    }
+    if constexpr (SC) {
+        if (!fl) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) in.rsc[r] = P.cs[r * RPP + rg];
         }
     }
-    const bool fl = ROWS == kNonFlushRows ? false : fl_row;
+}
+
+// The checkpoint stream of a tile whose small loads tile_issue_small issued.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS>
+__device__ __forceinline__ void tile_issue_stream(const StepParams& p,
+                                                  TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in) {
+    using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
+    using T = typename In::T;
+    using S = typename TS::S;
+    constexpr int VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr int HPC = In::HPC, EPC = In::EPC;
+    const bool fl = in.fl;
+    const int tid = threadIdx.x;
+    const int cc = tid % LPR;
+    const int rg = tid / LPR;
+    const int col0 = EPC * cc;
+    const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, in.id, in.blk);
+    if (!TWO || fl) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const S* rowp = P.ck + (int64_t)(r * RPP + rg) * DK + col0;
+#pragma unroll
+            for (int h = 0; h < HPC; ++h) in.cb[r * HPC + h] = ld_stream(rowp + EPC * LPR * h);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) in.cb[r * HPC] = ld_stream(P.cl + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+    }
+}
+
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON, int ROWS,
+          bool DEFER>
+__device__ __forceinline__ void tile_finish(const StepParams& p,
+                                            const TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in, char* smem,
+                                            char* dslot) {
+    using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
+    using T = typename In::T;
+    using S = typename TS::S;
+    using R = typename TR::S;
+    constexpr int VEC = T::VEC, LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
+    constexpr int KEEP = FORM == kGdn ? 2 : 1;  // Gated DeltaNet keeps (C q, C k) of a row together
+    constexpr int NV = KEEP * NR;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr bool SC = kScaled<TL>;                // read copy with per-row scales
+    constexpr int HPC = In::HPC, EPC = In::EPC;
+
+    static_assert(!DEFER || ROWS == kNonFlushRows, "deferred writes: non-flush rows only");
+    using D = Deferred<DVW, DK, R>;
+    D df(dslot);
+    if (!in.run) {
+        if constexpr (DEFER)
+            if (threadIdx.x == 0) df.meta[2] = -1;  // nothing to write
+        return;
+    }
+    const TileIds id = in.id;
+    const int blk = in.blk, w = in.w;
+    const bool fl = in.fl;
+    if constexpr (DEFER) {
+        if (threadIdx.x == 0) {
+            df.meta[0] = (int)id.tile * SPLIT + id.part;
+            df.meta[1] = blk;
+            df.meta[2] = w;
+        }
+    }
 
     const int tid = threadIdx.x;
     const int cc = tid % LPR;  // column chunk
     const int rg = tid / LPR;  // row within a pass
     const int row0 = id.part * DVW;
+    const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, id, blk);
+    S* ck = P.ck;
+    typename TL::S* cl = P.cl;
+    float* cs = P.cs;
+    R* rx = P.rx;
+    R* rk = P.rk;
+    float* rl = P.rl;
+    const bool key_owner = P.key_owner;
+    const float lam = in.lam;
 
-    char* base = p.pool + (int64_t)blk * p.block_bytes;
-    S* ck = reinterpret_cast<S*>(base + p.ckpt_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
-    RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
-    float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;  // row scales
-    R* rx = reinterpret_cast<R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
-    // keys and queries per group of heads_per_group heads (1: per head)
-    const int grp = id.head / p.heads_per_group;
-    const bool key_owner = id.head == grp * p.heads_per_group;  // appends the group's key
-    R* rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.slots * DK;
-    float* rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
-    const I* qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
-    const I* kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
-    const I* vp = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h + row0;
-    const float lam = p.lam[id.tile];
-
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     const Lds<R> s = carve<DVW, DK, R>(smem, p.slots, p.L);
 
-    // column of element h * EPC + i of this lane's share of a row
     const int col0 = EPC * cc;
     auto col = [col0](int h) { return col0 + EPC * LPR * h; };
     float qv[VEC], kv[VEC];
 #pragma unroll
     for (int h = 0; h < HPC; ++h) {
-        load_f<TI, EPC>(qp + col(h), qv + h * EPC);
-        load_f<TI, EPC>(kp + col(h), kv + h * EPC);
+        in.qr[h].to_float(qv + h * EPC);
+        in.kr[h].to_float(kv + h * EPC);
     }
-    const float vi = to_f<TI>(vp[min(tid, DVW - 1)]);
+    const float vi = to_f<TI>(in.vr);
     // a non-flush row's record: log-decay, key (one per group), value
     // (Mamba-2; Gated DeltaNet stores its corrected value with the output)
     auto append_record = [&](int slot) {
         if (id.part == 0) {
-            if (tid == 0) rl[slot] = lam;
+            if (tid == 0) {
+                if constexpr (DEFER) *df.lam = lam;
+                else rl[slot] = lam;
+            }
             if (rg == 0 && key_owner) {
-                R* kd = rk + (int64_t)slot * DK + col0;
+                R* kd = DEFER ? df.k + col0 : rk + (int64_t)slot * DK + col0;
 #pragma unroll
                 for (int h = 0; h < HPC; ++h) store_f<TR, EPC>(kd + EPC * LPR * h, kv + h * EPC);
             }
         }
-        if constexpr (FORM == kMamba2)
-            if (tid < DVW) rx[(int64_t)slot * DV + tid] = from_f<TR>(vi);
+        if constexpr (FORM == kMamba2) {
+            if (tid < DVW) {
+                if constexpr (DEFER) df.x[tid] = from_f<TR>(vi);
+                else rx[(int64_t)slot * DV + tid] = from_f<TR>(vi);
+            }
+        }
     };
-    float lam_j = 0.f;
-    if (w > 0) lam_j = rl[min(tid, w - 1)];
-    RecordCopy<DV, DVW, DK, R, NT, 2> rec;
-    rec.issue(rk, rx, w);
-    float rsc[NR];  // scales of the owned read-copy rows (scaled formats)
-    if constexpr (SC) {
-        if (!fl) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) rsc[r] = cs[r * RPP + rg];
-        }
-    }
+    const float lam_j = in.lam_j;
+    RecordCopy<DV, DVW, DK, R, T::NT, 2> rec = in.rec;
+    float rsc[NR];
     u32x4 cb[NR * HPC];
-    if (!TWO || fl) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const S* rowp = ck + (int64_t)(r * RPP + rg) * DK + col0;
+    for (int r = 0; r < NR; ++r) rsc[r] = in.rsc[r];
 #pragma unroll
-            for (int h = 0; h < HPC; ++h) cb[r * HPC + h] = ld_stream(rowp + EPC * LPR * h);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) cb[r * HPC] = ld_stream(cl + (int64_t)(r * RPP + rg) * DK + cc * VEC);
-    }
+    for (int i = 0; i < NR * HPC; ++i) cb[i] = in.cb[i];
 
     if (tid < DVW) s.v[tid] = vi;
-    rec.commit(rk, rx, s.k, s.x);
+    rec.template commit<!DEFER>(rk, rx, s.k, s.x);
     // The kernel without the fold appends the record (slot w, which this
     // step does not read) and takes this lane's share of k . q now, so that
     // k is not held through the checkpoint products.
@@ -901,7 +1114,7 @@ void k_replay_step(const StepParams p) {
             acc[2 * r + 1] = gs * b;
         }
     }
-    for (int j = cc; j < wd; j += LPR) {
+    auto record_terms = [&](int j) {
         const float wq = s.e[j] * s.cq[j];
         const float wk = FORM == kGdn ? s.e[j] * s.ck[j] : 0.f;
 #pragma unroll
@@ -914,6 +1127,15 @@ void k_replay_step(const StepParams p) {
                 acc[2 * r + 1] += wk * xj;
             }
         }
+    };
+    if constexpr (DEFER) {
+        // (unrolled to its bound, at most 63 records: a per-lane loop here
+        // makes the compiler wait for the prefetched loads)
+#pragma unroll
+        for (int it = 0; it < (kMaxRecords + LPR - 1) / LPR; ++it)
+            if (cc + it * LPR < wd) record_terms(cc + it * LPR);
+    } else {
+        for (int j = cc; j < wd; j += LPR) record_terms(j);
     }
     if constexpr (FORM == kMamba2) {
         if (cc == LPR - 1) {
@@ -923,9 +1145,10 @@ void k_replay_step(const StepParams p) {
     }
     xsum<NV, LPR / 2, KEEP>(acc, cc);
 
-    if (p.next_wp && id.head == 0 && id.part == 0 && tid == 0) p.next_wp[id.row] = fl ? 0 : w + 1;
+    if constexpr (!DEFER)  // (deferred: stored with the item's other writes)
+        if (p.next_wp && id.head == 0 && id.part == 0 && tid == 0) p.next_wp[id.row] = fl ? 0 : w + 1;
     const float alpha = expf(lam);  // Gated DeltaNet only
-    float* o = p.out + id.tile * DV + row0;
+    float* o = DEFER ? df.out : p.out + id.tile * DV + row0;
     {
         constexpr int left = xsum_left<NV, LPR, KEEP>();
         const int b0 = xsum_base<NV, LPR, KEEP>(cc);
@@ -941,6 +1164,7 @@ void k_replay_step(const StepParams p) {
                     const float d = bt * (s.v[row] - alpha * acc[i + 1]);
                     o[row] = alpha * acc[i] + kq * d;
                     if (fl) s.u[row] = d;
+                    else if constexpr (DEFER) df.x[row] = from_f<TR>(d);
                     else rx[(int64_t)w * DV + row] = from_f<TR>(d);
                 }
             }
@@ -1001,6 +1225,197 @@ void k_replay_step(const StepParams p) {
 #pragma unroll
         for (int h = 0; h < HPC; ++h) st_stream(rowp + EPC * LPR * h, hp[h]);
         if constexpr (TWO) store_read_row<TL, VEC, LPR>(cf[r], cl + rowoff + cc * VEC, cs + r * RPP + rg, cc);
+    }
+}
+
+// One tile, loads then arithmetic.
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON, int ROWS,
+          bool DEFER>
+__device__ __forceinline__ void replay_tile(const StepParams& p, const TileIds id, char* smem, char* dslot) {
+    // Without a flag array the (always present) cursor array is read in its
+    // place and the result discarded, so that the load is unconditional.
+    const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
+    const bool flag = row_flag(fsrc, id.row) && p.flush;
+    const int blk = p.block_table[id.row];
+    const int w = p.write_pos[id.row];
+    bool fl;
+    TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS> in;
+    in.run = tile_runs<ROWS>(p, id, blk, w, flag, fl);
+    if (in.run) {
+        tile_issue_small(p, id, blk, w, fl, in);
+        tile_issue_stream(p, in);
+    }
+    tile_finish<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, DEFER>(p, in, smem, dslot);
+}
+
+// Store the n deferred tiles at dbase, 16 bytes per thread and step.
+template <int DV, int DK, class R, int SPLIT>
+__device__ __forceinline__ void drain_deferred(const StepParams& p, char* dbase, int n) {
+    constexpr int DVW = DV / SPLIT;
+    using D = Deferred<DVW, DK, R>;
+    constexpr int OCH = D::OUT / 16, KCH = D::KB / 16, XCH = D::XB / 16, CPE = OCH + KCH + XCH + 1;
+    for (int c = threadIdx.x; c < n * CPE; c += blockDim.x) {
+        const int e = c / CPE, j = c - e * CPE;
+        char* ent = dbase + e * D::BYTES;
+        const D df(ent);
+        const int w = df.meta[2];
+        if (w < 0) continue;
+        const int tile = df.meta[0] / SPLIT, part = df.meta[0] - tile * SPLIT, blk = df.meta[1];
+        const int row = tile / p.n_heads, head = tile - row * p.n_heads;
+        char* base = p.pool + (int64_t)blk * p.block_bytes;
+        if (j < OCH) {
+            reinterpret_cast<u32x4*>(p.out + (int64_t)tile * DV + part * DVW)[j] =
+                reinterpret_cast<const u32x4*>(df.out)[j];
+        } else if (j < OCH + KCH) {
+            const int grp = head / p.heads_per_group;
+            if (part == 0 && head == grp * p.heads_per_group) {
+                R* rk = reinterpret_cast<R*>(base + p.reck_off) + ((int64_t)grp * p.slots + w) * DK;
+                reinterpret_cast<u32x4*>(rk)[j - OCH] = reinterpret_cast<const u32x4*>(df.k)[j - OCH];
+            }
+        } else if (j < OCH + KCH + XCH) {
+            R* rx = reinterpret_cast<R*>(base + p.recx_off) + ((int64_t)head * p.slots + w) * DV + part * DVW;
+            reinterpret_cast<u32x4*>(rx)[j - OCH - KCH] = reinterpret_cast<const u32x4*>(df.x)[j - OCH - KCH];
+        } else if (part == 0) {
+            reinterpret_cast<float*>(base + p.reclam_off)[(int64_t)head * p.slots + w] = *df.lam;
+            if (head == 0 && p.next_wp) p.next_wp[row] = w + 1;  // (non-flush rows only)
+        }
+    }
+}
+
+// PERSIST (non-flush rows only): a one-dimensional grid of a few workgroups
+// per compute unit, each taking the work items (tile * SPLIT + part)
+// blockIdx.x, blockIdx.x + gridDim.x, ...  It first stages the items that
+// run (in order, with their rows' block and cursor) in LDS at p.meta_off,
+// then issues each item's loads ahead of the item before it, so that two
+// workgroups per compute unit keep enough bytes in flight.  The outputs and
+// appended records wait in LDS (p.defer_cap items from byte p.defer_off) and
+// are stored after the workgroup's last item (or when full), so that the
+// step's small writes follow the checkpoint stream instead of being
+// interleaved with it.  Measured on MI355X: ~640 bytes of writes per 32 KiB
+// tile read cost a 1 GiB read stream about 26 us when interleaved and about
+// 6 us as one burst at the end; on the Nemotron-3-Super layer at batch 256
+// this form takes the non-flush steps from 183-212 to 170-201 us (A/B
+// harness, back-to-back launches).
+template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, bool RECON = false,
+          int ROWS = kAllRows, bool PERSIST = false>
+__global__ __launch_bounds__((StepTile<DV, DK, TL, SPLIT, ROWS>::NT),
+                             1)
+void k_replay_step(const StepParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    if constexpr (!PERSIST) {
+        replay_tile<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, false>(p, tile_ids<SPLIT>(p), smem, smem);
+    } else {
+        using R = typename TR::S;
+        using D = Deferred<DV / SPLIT, DK, R>;
+        using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
+        constexpr int NT = StepTile<DV, DK, TL, SPLIT, ROWS>::NT;
+        const int G = (int)gridDim.x;
+        const int items = p.n_rows * p.n_heads * SPLIT;
+        const int mine = (items - (int)blockIdx.x + G - 1) / G;  // >= 1: the grid is at most the items
+        auto ids = [&](int t) {
+            TileIds id;
+            id.tile = t / SPLIT;
+            id.part = t - (int)id.tile * SPLIT;
+            id.row = (int)id.tile / p.n_heads;
+            id.head = (int)id.tile - id.row * p.n_heads;
+            return id;
+        };
+        // Staging: the items of this workgroup that run, in order, each with
+        // its row's block and cursor (3 ints), after an error counter, the
+        // running count and one total per wave.
+        int* err_lds = reinterpret_cast<int*>(smem + p.meta_off);
+        int* cnt_lds = err_lds + 1;
+        int* wave_n = err_lds + 4;
+        int* list = err_lds + 8;
+        static_assert(NT / 64 <= 4, "wave totals");
+        if (threadIdx.x == 0) *err_lds = *cnt_lds = 0;
+        __syncthreads();
+        for (int c = 0; c < mine; c += NT) {
+            const int i = c + (int)threadIdx.x;
+            const int t = (int)blockIdx.x + i * G;
+            int blk = -1, w = 0;
+            bool run = false;
+            if (i < mine) {
+                const TileIds id = ids(t);
+                blk = p.block_table[id.row];
+                w = p.write_pos[id.row];
+                const bool flag = p.flush && row_flag(p.flush, id.row);
+                bool fl;
+                run = tile_runs<ROWS, true>(p, id, blk, w, flag, fl, err_lds);
+            }
+            const uint64_t ball = __ballot(run);
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+            if (lane == 0) wave_n[wave] = __popcll(ball);
+            __syncthreads();
+            int k = *cnt_lds + __popcll(ball & ((1ull << lane) - 1));
+            for (int v = 0; v < wave; ++v) k += wave_n[v];
+            if (run) {
+                list[3 * k] = t;
+                list[3 * k + 1] = blk;
+                list[3 * k + 2] = w;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0)
+                for (int v = 0; v < NT / 64; ++v) *cnt_lds += wave_n[v];
+            __syncthreads();
+        }
+        const int cnt = __builtin_amdgcn_readfirstlane(*cnt_lds);
+        // running item j (in scalar registers: the branches on them are uniform)
+        auto issue = [&](int j, In& in) {
+            const int t = __builtin_amdgcn_readfirstlane(list[3 * j]);
+            const int blk = __builtin_amdgcn_readfirstlane(list[3 * j + 1]);
+            const int w = __builtin_amdgcn_readfirstlane(list[3 * j + 2]);
+            tile_issue_small<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS, true>(p, ids(t), blk, w, false, in);
+        };
+        char* dbase = smem + p.defer_off;
+        int n = 0;
+        auto finish = [&](const In& in) {
+            tile_finish<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, true>(p, in, smem, dbase + n * D::BYTES);
+            __syncthreads();  // the item's LDS is free and its deferred writes are visible
+            if (++n == p.defer_cap) {
+                drain_deferred<DV, DK, R, SPLIT>(p, dbase, n);
+                n = 0;
+                // Wait for the drain's stores here: a global write still
+                // pending at the loop's next waits would make the compiler
+                // wait for every outstanding load there, the prefetched ones
+                // included (vmcnt(0) only; the other counters are left).
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                __syncthreads();
+            }
+        };
+        // Two sets of loads that trade places (no register copies, which
+        // would wait for the loads): item j's small loads are issued two
+        // items ahead and its stream one item ahead, so that the loads an
+        // item waits for are all older than the next item's.  The steady
+        // loop has no branch around a load and issues in the same order as
+        // the prologue (small a, stream a, small b), so that the compiler's
+        // waits there count exactly; the last one to three items follow it.
+        if (cnt > 0) {
+            In a, b;
+            issue(0, a);
+            tile_issue_stream(p, a);
+            issue(min(1, cnt - 1), b);
+            int j = 0;
+            for (; j + 3 < cnt; j += 2) {
+                tile_issue_stream(p, b);
+                finish(a);
+                issue(j + 2, a);
+                tile_issue_stream(p, a);
+                finish(b);
+                issue(j + 3, b);
+            }
+            // items j .. cnt - 1: a (small and stream issued), b (small issued)
+            if (j + 1 < cnt) tile_issue_stream(p, b);
+            finish(a);
+            if (j + 2 < cnt) {
+                issue(j + 2, a);
+                tile_issue_stream(p, a);
+            }
+            if (j + 1 < cnt) finish(b);
+            if (j + 2 < cnt) finish(a);
+        }
+        drain_deferred<DV, DK, R, SPLIT>(p, dbase, n);
+        if (threadIdx.x == 0 && *err_lds && p.err) atomicAdd(p.err, *err_lds);
     }
 }
 
@@ -2008,6 +2423,66 @@ constexpr int wide_split() {
 constexpr int64_t kFillWorkgroups = 1024;
 
 // -------------------------------------------------------------- dispatch --
+// Persistent launch shape of a replay step: the grid (0: launch the
+// one-workgroup-per-tile form instead), where the deferred writes start in
+// LDS, how many tiles they hold, and the LDS size.
+struct PersistShape {
+    unsigned grid = 0;
+    int meta_off = 0, defer_off = 0, defer_cap = 0;
+    size_t lds = 0;
+};
+constexpr int kMaxDefer = 64;
+// Workgroups per compute unit (measured on MI355X, Nemotron-3-Super shape,
+// batch 256: 2 beat 3 and 4; fewer workgroups also make the deferred writes'
+// end-of-launch burst shorter).
+constexpr int kPersistPerCU = 2;
+
+// Workgroups of fn (nt threads, lds bytes) resident per compute unit, cached
+// per device (the occupancy query reads the kernel's register counts).
+int resident_per_cu(const void* fn, int nt, size_t lds, int dev) {
+    struct Entry {
+        const void* fn;
+        size_t lds;
+        int dev, nb;
+    };
+    static std::mutex m;
+    static std::vector<Entry> cache;
+    std::lock_guard<std::mutex> g(m);
+    for (const Entry& e : cache)
+        if (e.fn == fn && e.lds == lds && e.dev == dev) return e.nb;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, nt, lds) != hipSuccess) nb = 0;
+    cache.push_back({fn, lds, dev, nb});
+    return nb;
+}
+
+PersistShape persist_shape(const void* fn, int nt, size_t lds0, int entry_bytes, int64_t items) {
+    PersistShape r;
+    int dev = 0, cus = 0, lds_cu = 0;
+    if (items < 1 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        cus < 1)
+        return r;
+    const int off = (int)((lds0 + 15) / 16 * 16);
+    const int per_cu = std::min(kPersistPerCU, resident_per_cu(fn, nt, (size_t)off, dev));
+    if (per_cu < 1) return r;
+    const int64_t grid = std::min<int64_t>(items, (int64_t)per_cu * cus);
+    const int64_t mine = (items + grid - 1) / grid;  // most items of one workgroup
+    const int64_t meta = 32 + (mine * 12 + 15) / 16 * 16;  // counters, then 3 ints per running item
+    const int64_t room = (int64_t)lds_cu / per_cu - off - meta;
+    const int64_t cap = std::min<int64_t>({room / entry_bytes, mine, kMaxDefer});
+    if (cap < 1) return r;
+    const size_t lds = (size_t)(off + meta + cap * entry_bytes);
+    if (resident_per_cu(fn, nt, lds, dev) < per_cu) return r;
+    r.grid = (unsigned)grid;
+    r.meta_off = off;
+    r.defer_off = (int)(off + meta);
+    r.defer_cap = (int)cap;
+    r.lds = lds;
+    return r;
+}
+
 template <int DV, int DK, class TS, class F>
 void with_split(const StepParams* p, F&& f) {
     constexpr int base = split_for<DV, DK>();
@@ -2197,19 +2672,57 @@ struct Dispatch {
                                                 return;
                                             }
                                         }
-                                        // (the hint is cleared unless the checkpoint has two copies)
                                         const int hint = p->flush_hint;
-                                        if constexpr (TWO) {
+                                        // The persistent form (steps with no flushing row)
+                                        // for Mamba-2 with one fp32 checkpoint, where it
+                                        // measured faster; with 16-bit tiles, read copies or
+                                        // Gated DeltaNet two workgroups per compute unit keep
+                                        // too little in flight and it measured slower.
+                                        constexpr bool persist_form =
+                                            FORM == kMamba2 && !TWO && std::is_same<TS, tF32>::value;
+                                        if constexpr (persist_form) {
+                                            if (hint == RS_FLUSH_NONE) {
+                                                constexpr int NT = StepTile<DV, DK, TL, SP, kNonFlushRows>::NT;
+                                                const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
+                                                                              kNonFlushRows, true>;
+                                                // (it copies the records to LDS in one pass:
+                                                // 2 chunks per thread)
+                                                constexpr int rec_chunks = (DK + DV / SP) * (int)sizeof(R) / 16;
+                                                const PersistShape ps =
+                                                    slots * rec_chunks <= 2 * NT
+                                                        ? persist_shape(reinterpret_cast<const void*>(fn), NT, lds,
+                                                                        Deferred<DV / SP, DK, R>::BYTES,
+                                                                        (int64_t)p->n_rows * p->n_heads * SP)
+                                                        : PersistShape{};
+                                                if (ps.grid) {
+                                                    StepParams q = *p;
+                                                    q.meta_off = ps.meta_off;
+                                                    q.defer_off = ps.defer_off;
+                                                    q.defer_cap = ps.defer_cap;
+                                                    hipLaunchKernelGGL(fn, dim3(ps.grid), dim3(NT), ps.lds, stream, q);
+                                                    return;
+                                                }
+                                            }
+                                        }
+                                        if constexpr (!TWO) {
+                                            // one launch over every row; the hint is not used
+                                            // (a pair of launches on mixed steps and the kernel
+                                            // without the fold measured slower here)
+                                            StepParams q = *p;
+                                            q.flush_hint = RS_FLUSH_UNKNOWN;
+                                            hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
+                                                               block, lds, stream, q);
+                                        } else {
                                             if (hint == RS_FLUSH_NONE || hint == RS_FLUSH_MIXED)
                                                 hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
                                                                                   kNonFlushRows>),
                                                                    grid<SP>(),
                                                                    dim3(StepTile<DV, DK, TL, SP, kNonFlushRows>::NT),
                                                                    lds, stream, *p);
+                                            if (hint != RS_FLUSH_NONE)
+                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>),
+                                                                   grid<SP>(), block, lds, stream, *p);
                                         }
-                                        if (hint != RS_FLUSH_NONE)
-                                            hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
-                                                               block, lds, stream, *p);
                                     }
                                 });
                             }

@@ -207,11 +207,14 @@ def test_gdn_reconstruct_production_shape(state_dt):
 
 
 # ------------------------------------------------------------- flush hints --
+@pytest.mark.parametrize("read", ["f16", None])
 @pytest.mark.parametrize("hint", ["none", "all"])
-def test_flush_hint_broken_promise(hint):
+def test_flush_hint_broken_promise(hint, read):
     """A row that breaks the caller's flush hint is skipped (its outputs and
     checkpoint untouched) and counted once per tile; the other rows are
-    computed as without a hint."""
+    computed as without a hint.  Two-copy checkpoints use every hint; a
+    single fp32 Mamba-2 checkpoint uses RS_FLUSH_NONE only (its persistent
+    kernel) and computes every row under RS_FLUSH_ALL."""
     import numpy as np
     import torch
     import workloads
@@ -219,7 +222,7 @@ def test_flush_hint_broken_promise(hint):
     from linear_attention_decode_replay_amd.state import DecodeLayer
 
     H, L = 4, 4
-    lay = rs.layer(rs.MAMBA2, H, 16, 32, L, "f32", "f32", "f32", "f16")   # hints apply to two-copy layers
+    lay = rs.layer(rs.MAMBA2, H, 16, 32, L, "f32", "f32", "f32", read)
     tok = workloads.tokens(rs.MAMBA2, 5, 0, 3, H, 16, 32, "f32")
     outs, ckpts, errs = [], [], []
     for use in (rs.RS_FLUSH_UNKNOWN, rs.RS_FLUSH_NONE if hint == "none" else rs.RS_FLUSH_ALL):
@@ -240,6 +243,10 @@ def test_flush_hint_broken_promise(hint):
         errs.append(int(d.err.item()))
     ref, got = outs
     assert errs[0] == 0
+    if read is None and hint == "all":   # not used: every row computed
+        assert errs[1] == 0 and torch.allclose(got, ref, rtol=1e-6, atol=1e-6)
+        assert torch.allclose(ckpts[1], ckpts[0], rtol=1e-6, atol=1e-7)
+        return
     broken = [0] if hint == "none" else [1, 2]
     kept = [b for b in range(3) if b not in broken]
     assert errs[1] == H * len(broken)
@@ -249,4 +256,18 @@ def test_flush_hint_broken_promise(hint):
         assert torch.count_nonzero(ckpts[1][0]) == 0 and torch.count_nonzero(ckpts[0][0]) > 0
     else:
         assert torch.allclose(ckpts[1][0], ckpts[0][0], rtol=1e-6, atol=1e-7)
-    say(f"[hint] broken '{hint}' promise: {errs[1]} tiles skipped and counted")
+    say(f"[hint] broken '{hint}' promise (read copy {read}): {errs[1]} tiles skipped and counted")
+
+
+# ------------------------------------------- persistent non-flush kernel --
+@pytest.mark.parametrize("B,H,pad,force", [(40, 40, [3, 17], 3), (1024, 40, [5, 600], 0)])
+def test_persistent_step_item_counts(B, H, pad, force):
+    """Steps with no flushing row of a Mamba-2 layer with one fp32 checkpoint
+    run as a persistent grid of two workgroups per compute unit.  More
+    (row, head) tiles than the grid: every workgroup takes several, in odd
+    and even numbers (1600 tiles: 3 or 4 each, fewer where padding rows
+    drop out), with forced flushes every third step in between (those steps
+    run the one-launch kernel); 40960 tiles: 80 per workgroup, more than the
+    64 whose writes it holds back at once."""
+    _go(Case(form=rs.MAMBA2, B=B, H=H, dv=16, dk=32, L=4, steps=12, state_dt="f32", rec_dt="f16", io_dt="bf16",
+             pad_rows=pad, force_every=force, check_conventional=False, seed=81 + B))
