@@ -236,7 +236,8 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               RS_FLUSH_ALL promises that every non-padding row flushes;
  *               RS_FLUSH_MIXED runs the no-fold kernel over the rows that do
  *               not flush and then the full kernel over those that do.
- *               Mamba-2 with one fp32 checkpoint: RS_FLUSH_NONE runs a
+ *               Mamba-2 with one fp32 checkpoint and a key per head
+ *               (n_groups 0 or n_heads): RS_FLUSH_NONE runs a
  *               persistent kernel without the fold that streams the
  *               checkpoint tiles with the next tile's loads in flight and
  *               stores the outputs and records after the stream; the other

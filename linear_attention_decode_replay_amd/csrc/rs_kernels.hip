@@ -2674,14 +2674,17 @@ struct Dispatch {
                                         }
                                         const int hint = p->flush_hint;
                                         // The persistent form (steps with no flushing row)
-                                        // for Mamba-2 with one fp32 checkpoint, where it
-                                        // measured faster; with 16-bit tiles, read copies or
-                                        // Gated DeltaNet two workgroups per compute unit keep
-                                        // too little in flight and it measured slower.
+                                        // for Mamba-2 with one fp32 checkpoint and a key per
+                                        // head, where it measured faster; with 16-bit tiles,
+                                        // read copies or Gated DeltaNet two workgroups per
+                                        // compute unit keep too little in flight, and with
+                                        // grouped keys (a key append in one tile of a group)
+                                        // there is less interleaved writing to take out: it
+                                        // measured slower there.
                                         constexpr bool persist_form =
                                             FORM == kMamba2 && !TWO && std::is_same<TS, tF32>::value;
                                         if constexpr (persist_form) {
-                                            if (hint == RS_FLUSH_NONE) {
+                                            if (hint == RS_FLUSH_NONE && p->heads_per_group == 1) {
                                                 constexpr int NT = StepTile<DV, DK, TL, SP, kNonFlushRows>::NT;
                                                 const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
                                                                               kNonFlushRows, true>;
