@@ -389,6 +389,75 @@ constexpr int xsum_dup_mask() {
     return m;
 }
 
+// Lane-bit mask that xpartner<OFF> flips: its pairs are lane ^ mask inside
+// the group (row mirrors flip every lower bit too).
+constexpr int flip_of(int off) { return off == 8 ? 15 : (off == 4 ? 7 : off); }
+constexpr int parity(int x) { return __builtin_popcount(x) & 1; }
+
+// Select-free first levels.  A lane whose N values are stored with their
+// top index bits XOR-permuted can keep its lower half and send the upper half
+// at each of the first PL levels, where xsum selects by the lane's own bit.
+// Level l's permutation bit is m_l = parity(lane & A_l), with A_l chosen so
+// that m_l differs between the lane and its partner at level l (they keep
+// opposite halves) and is equal between the partners of every other level
+// (earlier ones: the pair agrees on the order of what is left; later ones:
+// the pair kept the same indices).  The pairings' lane masks are independent,
+// so A_l is the dual basis vector, unique.  The kept original indices then
+// have top bits m_0 m_1 ..., which xsum_perm_base accounts for; after the PL
+// levels the remaining values are in natural order and xsum finishes.
+template <int G, int L>
+constexpr int xsum_perm_sel() {
+    for (int a = 1; a < G; ++a) {
+        bool ok = parity(flip_of((G / 2) >> L) & a) == 1;
+        for (int k = 0; (G / 2) >> k > 0; ++k)
+            if (k != L) ok = ok && parity(flip_of((G / 2) >> k) & a) == 0;
+        if (ok) return a;
+    }
+    return 0;
+}
+template <int N, int OFF, int PL>
+__device__ __forceinline__ void xsum_perm(float* v, int gl) {
+    if constexpr (PL > 0 && OFF > 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) v[i] += xpartner<OFF>(v[i + N / 2]);
+        xsum_perm<N / 2, OFF / 2, PL - 1>(v, gl);
+    } else {
+        xsum<N, OFF, 1>(v, gl);
+    }
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// Levels of a group of G lanes that split an index of T values (a power of
+// two, the top index bits first), and the XOR mask a lane applies to that
+// index: bit (log2 T - 1 - l) is the lane's m_l.
+template <int T, int G>
+constexpr int xsum_perm_levels() {
+    return ilog2(T) < ilog2(G) ? ilog2(T) : ilog2(G);
+}
+template <int T, int G>
+__device__ __forceinline__ int xsum_perm_mask(int gl) {
+    constexpr int LT = ilog2(T), PL = xsum_perm_levels<T, G>();
+    static_assert(PL == 0 || xsum_perm_sel<G, 0>() != 0, "no select-free mask for this group");
+    int m = 0;
+    if constexpr (PL > 0) m |= parity(gl & xsum_perm_sel<G, 0>()) << (LT - 1);
+    if constexpr (PL > 1) m |= parity(gl & xsum_perm_sel<G, 1>()) << (LT - 2);
+    if constexpr (PL > 2) m |= parity(gl & xsum_perm_sel<G, 2>()) << (LT - 3);
+    if constexpr (PL > 3) m |= parity(gl & xsum_perm_sel<G, 3>()) << (LT - 4);
+    if constexpr (PL > 4) m |= parity(gl & xsum_perm_sel<G, 4>()) << (LT - 5);
+    static_assert(PL <= 5, "levels");
+    return m;
+}
+// First original index left in a lane after xsum_perm over N values whose
+// top log2(T) bits are the permuted query index (mask xsum_perm_mask).
+template <int N, int G, int T>
+__device__ __forceinline__ int xsum_perm_base(int gl) {
+    constexpr int PL = xsum_perm_levels<T, G>();
+    constexpr int LT = ilog2(T);
+    const int top = xsum_perm_mask<T, G>(gl) >> (LT - PL);  // the PL kept bits
+    return top * (N >> PL) + xsum_base<(N >> PL), (G >> PL), 1>(gl);
+}
+
 // Plain butterfly sum of one value over the group; every lane gets the sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
@@ -1847,11 +1916,16 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     __syncthreads();
 
     // 3. weighted K^T Q
+    // The lane holds query i at position i ^ mq (mq from its lane-group
+    // bits), so that the reductions over the query index need no selects
+    // (xsum_perm); weights indexed by query are read at i ^ mq.
+    constexpr int PL = xsum_perm_levels<T, LPR>();
+    const int mq = xsum_perm_mask<T, LPR>(cc);
     float qv[T][VEC];
 #pragma unroll
     for (int i = 0; i < T; ++i)
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) qv[i][c] = s.qd[i * DK + cc * VEC + c];
+        for (int c = 0; c < VEC; ++c) qv[i][c] = s.qd[(i ^ mq) * DK + cc * VEC + c];
     if (tid < T) s.gck[tid] = expf(s.sc[0] + s.cum[tid]);
     const int nkeys = h + T;
     for (int j0 = 0; j0 < nkeys; j0 += RPP) {
@@ -1872,10 +1946,10 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
             for (int c = 0; c < VEC; ++c) a += kj[c] * qv[i][c];
             part[i] = a;
         }
-        xsum<T, LPR / 2, 1>(part, cc);
+        xsum_perm<T, LPR / 2, PL>(part, cc);
         constexpr int left = xsum_left<T, LPR, 1>();
         if (j < nkeys && (cc & xsum_dup_mask<T, LPR, 1>()) == 0) {
-            const int b0 = xsum_base<T, LPR, 1>(cc);
+            const int b0 = xsum_perm_base<T, LPR, T>(cc);
 #pragma unroll
             for (int k = 0; k < left; ++k) {
                 const int i = b0 + k;
@@ -1901,7 +1975,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-        const float g = s.gck[i];
+        const float g = s.gck[i ^ mq];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             float a = 0.f;
@@ -1917,16 +1991,16 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
             xj[r] = j < h ? to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]) : s.vd[(j - h) * DV + r * RPP + rg];
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-            const float wg = s.wq[j * T + i];
+            const float wg = s.wq[j * T + (i ^ mq)];
 #pragma unroll
             for (int r = 0; r < NR; ++r) acc[i * NR + r] += wg * xj[r];
         }
     }
-    xsum<NV, LPR / 2, 1>(acc, cc);
+    xsum_perm<NV, LPR / 2, PL>(acc, cc);
     {
         constexpr int left = xsum_left<NV, LPR, 1>();
         if ((cc & xsum_dup_mask<NV, LPR, 1>()) == 0) {
-            const int b0 = xsum_base<NV, LPR, 1>(cc);
+            const int b0 = xsum_perm_base<NV, LPR, T>(cc);
 #pragma unroll
             for (int k = 0; k < left; ++k) {
                 const int v = b0 + k, i = v / NR, r = v - i * NR;
