@@ -1968,7 +1968,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     }
     __syncthreads();
 
-    // 4. outputs
+    // 4. outputs (each query scaled by its checkpoint weight first: T * VEC
+    // multiplies instead of T * NR)
     float cf[NR][VEC];
 #pragma unroll
     for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
@@ -1977,11 +1978,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     for (int i = 0; i < T; ++i) {
         const float g = s.gck[i ^ mq];
 #pragma unroll
+        for (int c = 0; c < VEC; ++c) qv[i][c] *= g;
+#pragma unroll
         for (int r = 0; r < NR; ++r) {
             float a = 0.f;
 #pragma unroll
             for (int c = 0; c < VEC; ++c) a += cf[r][c] * qv[i][c];
-            acc[i * NR + r] = g * a;
+            acc[i * NR + r] = a;
         }
     }
     for (int j = cc; j < nkeys; j += LPR) {
