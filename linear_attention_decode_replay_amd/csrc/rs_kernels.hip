@@ -1438,10 +1438,16 @@ void k_replay_step(const StepParams p) {
         };
         char* dbase = smem + p.defer_off;
         int n = 0;
-        auto finish = [&](const In& in) {
-            tile_finish<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, true>(p, in, smem, dbase + n * D::BYTES);
-            __syncthreads();  // the item's LDS is free and its deferred writes are visible
+        // Consecutive items use the two halves of the records area in turn
+        // (a: the first, b: the second), so an item's LDS is free again once
+        // the next item has passed its own barriers and no barrier is needed
+        // between items; one comes before every drain.
+        const int carve = (int)((lds_need<DV / SPLIT, DK, R>(p.slots, p.L) + 15) / 16 * 16);
+        auto finish = [&](const In& in, int half) {
+            tile_finish<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, true>(p, in, smem + half * carve,
+                                                                                 dbase + n * D::BYTES);
             if (++n == p.defer_cap) {
+                __syncthreads();  // the items' deferred writes are visible
                 drain_deferred<DV, DK, R, SPLIT>(p, dbase, n);
                 n = 0;
                 // Wait for the drain's stores here: a global write still
@@ -1467,22 +1473,23 @@ void k_replay_step(const StepParams p) {
             int j = 0;
             for (; j + 3 < cnt; j += 2) {
                 tile_issue_stream(p, b);
-                finish(a);
+                finish(a, 0);
                 issue(j + 2, a);
                 tile_issue_stream(p, a);
-                finish(b);
+                finish(b, 1);
                 issue(j + 3, b);
             }
             // items j .. cnt - 1: a (small and stream issued), b (small issued)
             if (j + 1 < cnt) tile_issue_stream(p, b);
-            finish(a);
+            finish(a, 0);
             if (j + 2 < cnt) {
                 issue(j + 2, a);
                 tile_issue_stream(p, a);
             }
-            if (j + 1 < cnt) finish(b);
-            if (j + 2 < cnt) finish(a);
+            if (j + 1 < cnt) finish(b, 1);
+            if (j + 2 < cnt) finish(a, 0);
         }
+        __syncthreads();  // the items' deferred writes are visible
         drain_deferred<DV, DK, R, SPLIT>(p, dbase, n);
         if (threadIdx.x == 0 && *err_lds && p.err) atomicAdd(p.err, *err_lds);
     }
@@ -2533,6 +2540,7 @@ int resident_per_cu(const void* fn, int nt, size_t lds, int dev) {
     return nb;
 }
 
+// lds0: the records area of one item; the persistent step keeps two.
 PersistShape persist_shape(const void* fn, int nt, size_t lds0, int entry_bytes, int64_t items) {
     PersistShape r;
     int dev = 0, cus = 0, lds_cu = 0;
@@ -2541,7 +2549,7 @@ PersistShape persist_shape(const void* fn, int nt, size_t lds0, int entry_bytes,
         hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
         cus < 1)
         return r;
-    const int off = (int)((lds0 + 15) / 16 * 16);
+    const int off = 2 * (int)((lds0 + 15) / 16 * 16);
     const int per_cu = std::min(kPersistPerCU, resident_per_cu(fn, nt, (size_t)off, dev));
     if (per_cu < 1) return r;
     const int64_t grid = std::min<int64_t>(items, (int64_t)per_cu * cus);
