@@ -855,6 +855,7 @@ struct TileIn {
     RawIo<TI, EPC> qr[HPC], kr[HPC];
     typename TI::S vr;
     float lam, lam_j;
+    float beta;  // Gated DeltaNet
     RecordCopy<DV, DVW, DK, typename TR::S, NT, 2> rec;
     float rsc[NR];  // scales of the owned read-copy rows (scaled formats)
     u32x4 cb[NR * HPC];
@@ -926,6 +927,7 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
     const int rg = tid / LPR;  // row within a pass
     const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, id, blk);
     in.lam = p.lam[id.tile];
+    if constexpr (FORM == kGdn) in.beta = p.beta[id.tile];
     // column of element h * EPC + i of this lane's share of a row
     const int col0 = EPC * cc;
 #pragma unroll
@@ -1226,7 +1228,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
 #pragma unroll
                 for (int i = 0; i < left; ++i) o[(b0 + i) * RPP + rg] = acc[i];
             } else {
-                const float bt = p.beta[id.tile];
+                const float bt = in.beta;
 #pragma unroll
                 for (int i = 0; i < left; i += 2) {
                     const int row = ((b0 + i) / 2) * RPP + rg;
@@ -1534,6 +1536,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 #pragma unroll
     for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     const float alpha = expf(p.lam[id.tile]);
+    const float bt = FORM == kGdn ? p.beta[id.tile] : 0.f;  // loaded with the others, used at the end
     if (tid < DVW) s_v[tid] = vi;
 
     float kq = 0.f;
@@ -1574,7 +1577,6 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, SPLIT>::NT)) void k_conventional_
 #pragma unroll
                 for (int i = 0; i < left; ++i) o[(b0 + i) * RPP + rg] = acc[i];
             } else {
-                const float bt = p.beta[id.tile];
 #pragma unroll
                 for (int i = 0; i < left; i += 2) {
                     const int row = ((b0 + i) / 2) * RPP + rg;
