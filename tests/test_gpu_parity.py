@@ -260,6 +260,23 @@ def test_flush_hint_broken_promise(hint, read):
 
 
 # ------------------------------------------- persistent non-flush kernel --
+@pytest.mark.parametrize("B,H,shape,L,pad,force,sample", [
+    (1, 1, (64, 128), 16, [], 0, None),           # one tile: a grid of one workgroup
+    (3, 5, (16, 32), 4, [1], 0, None),
+    (17, 128, (64, 128), 16, [], 0, [0, 8, 16]),  # 2,176 tiles: 4 or 5 per workgroup
+    (300, 40, (16, 32), 8, [7, 299], 5, None),    # 12,000 tiles: 23 or 24 per workgroup
+    (513, 64, (16, 32), 2, [], 0, None),          # L = 2: every other step flushes
+])
+def test_persistent_step_shapes(B, H, shape, L, pad, force, sample):
+    """The persistent non-flush step (Mamba-2, one fp32 checkpoint) over odd
+    shapes: grids from one workgroup up, uneven item counts, padding rows and
+    forced flushes, the shortest ring."""
+    dv, dk = shape
+    _go(Case(form=rs.MAMBA2, B=B, H=H, dv=dv, dk=dk, L=L, steps=3 * L + 1, state_dt="f32", rec_dt="f16",
+             io_dt="bf16", pad_rows=pad, force_every=force, sample=sample, check_conventional=False,
+             seed=90 + B))
+
+
 @pytest.mark.parametrize("B,H,pad,force", [(40, 40, [3, 17], 3), (1024, 40, [5, 600], 0)])
 def test_persistent_step_item_counts(B, H, pad, force):
     """Steps with no flushing row of a Mamba-2 layer with one fp32 checkpoint
