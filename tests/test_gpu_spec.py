@@ -68,9 +68,13 @@ def test_spec_nemotron_shape(state_dt):
     _check(err, TOL_LOW)
 
 
-def test_spec_T8_nemotron_shape():
-    err = run_spec_case(SpecCase(B=64, H=128, dv=64, dk=128, L=16, T=8, steps=12, rec_dt="f16", io_dt="bf16",
-                                 a_lo=1.0, a_hi=8.0, sample=[0, 63], seed=22))
+@pytest.mark.parametrize("state_dt", ["f32", "f16"])
+def test_spec_T8_nemotron_shape(state_dt):
+    """T = 8 at 64 x 128: lane groups of 32 (fp32 state) and 16 (fp16 state)
+    lanes, so the reductions over the draft index use both sets of
+    select-free levels."""
+    err = run_spec_case(SpecCase(B=64, H=128, dv=64, dk=128, L=16, T=8, steps=12, state_dt=state_dt, rec_dt="f16",
+                                 io_dt="bf16", a_lo=1.0, a_hi=8.0, sample=[0, 63], seed=22))
     _check(err, TOL_LOW)
 
 
