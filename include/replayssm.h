@@ -24,9 +24,12 @@
  * current token into C, writes C once and empties the buffer.
  *
  * Conventions for every function below:
- *   - Memory: the caller owns all host and device memory, including the
- *     block pool.  The library allocates nothing and keeps no mutable global
- *     state; it may be called from several host threads.
+ *   - Memory: the caller owns all device memory, including the block pool;
+ *     the library allocates no device or pinned host memory.  Its only
+ *     mutable global state is a mutex-guarded host cache of occupancy
+ *     queries (resident workgroups per compute unit, per kernel and device:
+ *     facts that do not change while the process runs), so it may be called
+ *     from several host threads.
  *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL means
  *     the default stream) and never synchronise the host.  All device
  *     pointers must stay valid until the work on `stream` has completed.
