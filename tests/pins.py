@@ -365,7 +365,7 @@ def pin_two_copy_error_does_not_accumulate(orc):
         o_s = single.step(q, k, v, lam, np.full(B, fls[s]))
         if fls[s]:
             single.C[:] = oracle.round_to(single.C, "f16")
-        scale = np.abs(o_e).max()
+        scale = max(np.abs(o_e).max(), 1e-300)
         err_two.append(np.abs(o_t - o_e).max() / scale)
         err_single.append(np.abs(o_s - o_e).max() / scale)
     late_two, late_single = max(err_two[-50:]), max(err_single[-50:])

@@ -10,13 +10,14 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "byte_model_facts.txt
 
 def _facts():
     rows = []
-    for line in open(GOLDEN):
-        line = line.strip()
-        if not line or line.startswith("#"):
-            continue
-        name, args, value, tol, cite = [x.strip() for x in line.split("|")]
-        rows.append((name, [float(a) if "." in a else int(a) for a in args.split()], float(value),
-                     float(tol), cite))
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, args, value, tol, cite = [x.strip() for x in line.split("|")]
+            rows.append((name, [float(a) if "." in a else int(a) for a in args.split()], float(value),
+                         float(tol), cite))
     return rows
 
 

@@ -133,7 +133,8 @@ MUTANTS = [
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
-    src = open(SRC).read()
+    with open(SRC) as f:
+        src = f.read()
     assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
     mut_src = tmp_path / "mutant.c"
     mut_src.write_text(src.replace(old, new))
