@@ -5,25 +5,35 @@
 
 Default workload: one Mamba-2 layer at the Nemotron-3-Super shape (128 heads,
 d_v=64, d_k=128, fp32 state, 4 MiB per sequence), batch 256, L=16, bf16
-v/k/q, fp16 records, fp32 log-decay.  A step is one pass of the whole hot
-path over the batch: host cursor/flush metadata, its async upload, and one
-kernel launch that serves flush and non-flush rows.  K defaults to 64 after
-W=64 warm-up steps: with 4 state pools in rotation both are exactly one
-window of 16 tokens per pool, so every cursor position is weighted equally.
+v/k/q, fp16 records, fp32 log-decay, every row of a pool at the same cursor.
+A step is one pass of the whole hot path over the batch: host cursor/flush
+metadata, its async upload when it changed, and one kernel launch that
+serves flush and non-flush rows.
+
+Cursor schedule.  The method's cost is per window of L tokens (L - 1
+appends and one checkpoint write), so a step's cost depends on its cursor.
+P state pools (default L + 1, like P layers of a model; P = 1 mod L) are
+used in rotation, launch s on pool s mod P, and pool p starts at cursor
+(p + phi) mod L, so launch s runs at cursor (s + phi) mod L: any L
+consecutive launches visit every cursor once, the flush included.  phi is
+chosen from W and K so that the K timed launches are floor(K / L) whole
+windows plus a run of K mod L consecutive cursors whose algorithmic bytes
+are as close as possible to the window average (exactly whole windows when
+L divides K).  Bringing a pool to its starting cursor takes untimed decode
+steps before the warm-up.  No launch reuses the previous P - 1 launches'
+state, so none finds it in the 256 MB Infinity Cache.
 
 Inputs are seeded synthetic tensors (16 distinct token batches, cycled),
-resident in HBM before the timed region.  P independent state pools (default
-4, like P layers of a model) are used in rotation so that consecutive steps
-never find their state in the 256 MB Infinity Cache.
+resident in HBM before the timed region.
 
 Prints ONE JSON line.  `value` is the decode steps/s of the checkpoint +
 buffer path (wall clock over K steps); the conventional kernel is timed the
 same way under "conventional".  "roofline" describes the dominant kernel
-(the checkpoint + buffer step): algorithmic bytes per launch / mean launch
-time, where the mean is the time between one pair of HIP events recorded on
-the launch stream around the K timed launches, divided by K; against
-8 TB/s.  The per-cursor times ("us_by_cursor") come from one more window per
-pool after the timed region, with events around each launch.
+(the checkpoint + buffer step): algorithmic bytes of the timed launches /
+their time, the time between one pair of HIP events recorded on the launch
+stream around the K timed launches; against 8 TB/s.  The per-cursor times
+("us_by_cursor") come from 2 L more launches after the timed region, with
+events around each launch.
 """
 from __future__ import annotations
 
@@ -51,6 +61,17 @@ WORKLOADS = {
 }
 
 _ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+# Launch log: when enabled (a list), every timed-suite launch of one of the
+# library's kernels is appended in launch order as (kernel, label, algorithmic
+# bytes), so that rocprofv3's per-dispatch counters of the same run can be
+# lined up with the launches (summarize_counters).
+_LAUNCH_LOG = None
+
+
+def log_launch(kernel, label, nbytes):
+    if _LAUNCH_LOG is not None:
+        _LAUNCH_LOG.append((kernel, label, float(nbytes)))
 
 
 # ----------------------------------------------------------- byte accounting --
@@ -93,6 +114,55 @@ def read_copy_bytes(dv, dk, read):
 
 def window_bytes(form, H, dv, dk, B, state, rec, io, L, kind="replay", read=None, groups=0):
     return sum(step_bytes(form, H, dv, dk, B, state, rec, io, w, w == L - 1, kind, read, groups) for w in range(L))
+
+
+def cursor_bytes(cfg, L=None):
+    """Algorithmic bytes of one replay launch at each cursor 0..L-1 (the
+    last one flushes)."""
+    L = L or cfg["L"]
+    return [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"],
+                       w, w == L - 1, "replay", cfg.get("read"), cfg.get("groups", 0)) for w in range(L)]
+
+
+def timed_phase(per_cursor, steps):
+    """The cursor c0 of the first timed launch: the K timed launches run at
+    cursors c0, c0 + 1, ... (mod L); c0 minimises the distance between their
+    mean algorithmic bytes and the window average (smallest c0 on ties).
+    With L dividing K every c0 gives whole windows and c0 = 0."""
+    L = len(per_cursor)
+    if steps < 1:
+        return 0
+    win = sum(per_cursor) / L
+    best, best_d = 0, None
+    for c0 in range(L):
+        m = sum(per_cursor[(c0 + i) % L] for i in range(steps)) / steps
+        d = abs(m - win)
+        if best_d is None or d < best_d * (1 - 1e-12):
+            best, best_d = c0, d
+    return best
+
+
+def cursor_schedule(L, n_pools, warmup, steps, per_cursor):
+    """The launch schedule of the replay benchmark.  Returns (phi, starts):
+    launch s (counted from the first warm-up launch) runs on pool s mod P at
+    cursor (s + phi) mod L, and pool p starts at cursor starts[p] = (p + phi)
+    mod L.  Needs P = 1 (mod L): pool p is visited at launches p, p + P, ...
+    and its cursor moves by one per visit, which stays (s + phi) mod L only
+    when P = 1 (mod L)."""
+    if n_pools < 1 or n_pools % L != 1 % L:
+        raise ValueError(f"the number of state pools must be 1 mod L (L={L}, got {n_pools})")
+    c0 = timed_phase(per_cursor, steps)
+    phi = (c0 - warmup) % L
+    return phi, [(p + phi) % L for p in range(n_pools)]
+
+
+def window_us(by_cursor, L):
+    """Mean launch time over the L cursor positions (events around each
+    launch), or None if a position is missing."""
+    keys = [f"w{w}" for w in range(L - 1)] + ["flush"]
+    if any(k not in by_cursor for k in keys):
+        return None
+    return round(float(np.mean([by_cursor[k] for k in keys])), 2)
 
 
 def kernel_source_hash() -> str:
@@ -205,6 +275,10 @@ def cpu_baseline(cfg, n_steps=None, rows=None, min_seconds=10.0, max_windows=32)
 
 # ------------------------------------------------------------------------ GPU --
 def run_gpu(cfg, steps, warmup, n_pools, kind):
+    """Time K steps of one kernel kind on the cursor schedule above.  Returns
+    the timings plus `launches`: (cursor, flush, algorithmic bytes) of every
+    launch in launch order (pool preparation, warm-up, timed, breakdown),
+    which lines the launches up with rocprofv3's per-dispatch counters."""
     import torch
     import linear_attention_decode_replay_amd as rs
     import workloads
@@ -212,12 +286,15 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    L = cfg["L"]
     # the conventional step has one state copy whatever the replay layout
     read = cfg["read"] if kind == "replay" else None
     groups = cfg.get("groups", 0)
-    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"], read,
+    lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], L, cfg["state"], cfg["rec"], cfg["io"], read,
                    0, groups, stochastic=bool(cfg.get("sr")))
     B = cfg["B"]
+    per_cursor = cursor_bytes(cfg)
+    phi, starts = cursor_schedule(L, n_pools, warmup, steps, per_cursor)
     layers = []
     for p in range(n_pools):
         d = DecodeLayer(lay, B, B, dev, sr_key=(0x5EED0000 + p, 0x243F6A8885A308D3))
@@ -238,15 +315,36 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
         keep.append((q, k, v, lam, beta, out))
         ios.append(rs.make_io(q, k, v, lam, out, beta))
     torch.cuda.synchronize()
+    launches = []
 
-    def one(s, events=None):
-        d = layers[s % n_pools]
-        io = ios[s % n_inputs]
+    def launch(d, io, events=None):
         if kind == "replay":
             wp, fl = d.step(io, events=events)
-            return int(wp[0]), bool(fl[0])
-        d.conventional_step(io, events=events)
-        return None, None
+            w, f = int(wp[0]), bool(fl[0])
+        else:
+            d.conventional_step(io, events=events)
+            w, f = 0, False
+        nb = step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"], w, f,
+                        kind, cfg["read"], groups)
+        launches.append((w, f, nb))
+        if kind == "replay":
+            log_launch("k_replay_step", "flush" if f else f"w{w}", nb)
+        else:
+            log_launch("k_conventional_step", "conventional", nb)
+        return w, f
+
+    # pool preparation (untimed): pool p decodes starts[p] tokens
+    if kind == "replay":
+        for p, n in enumerate(starts):
+            for i in range(n):
+                launch(layers[p], ios[i % n_inputs])
+    torch.cuda.synchronize()
+
+    def one(s, events=None):
+        w, f = launch(layers[s % n_pools], ios[s % n_inputs], events)
+        if kind == "replay" and w != (s + phi) % L:
+            raise RuntimeError(f"launch {s} ran at cursor {w}, the schedule says {(s + phi) % L}")
+        return w, f
 
     for s in range(warmup):
         one(s)
@@ -255,38 +353,46 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     # on the launch stream (no event between launches, so none of their
     # overhead lands inside a launch).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cursors = []
+    first = len(launches)
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
-        cursors.append(one(warmup + i))
+        one(warmup + i)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = start.elapsed_time(end)
+    timed = launches[first:]
     errs = sum(int(d.err.item()) for d in layers)
     if errs:
         raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
-    nbytes = [step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, cfg["state"], cfg["rec"], cfg["io"],
-                         w or 0, bool(f), kind, cfg["read"], groups) for (w, f) in cursors]
+    nbytes = [b for (_, _, b) in timed]
     # Breakdown by cursor position (after the timed region, not part of it):
-    # one more window per pool with events around every launch.
+    # 2 L more launches (every cursor twice) with events around each.
     by_pos = {}
     if kind == "replay":
-        n_brk = cfg["L"] * n_pools
+        n_brk = 2 * L
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_brk)]
         brk = [one(warmup + steps + i, ev[i]) for i in range(n_brk)]
         torch.cuda.synchronize()
         for (w, f), (a, b) in zip(brk, ev):
             by_pos.setdefault("flush" if f else f"w{w}", []).append(a.elapsed_time(b))
+    mix = {}
+    for (w, f, _) in timed:
+        key = "flush" if f else f"w{w}"
+        mix[key] = mix.get(key, 0) + 1
     return {
         "wall_s": wall,
         "steps_per_s": steps / wall,
         "ms_per_step": 1e3 * wall / steps,
         "kernel_ms_mean": region_ms / steps,
         "bytes_per_launch_mean": float(np.mean(nbytes)),
+        "window_bytes_per_launch": float(np.mean(per_cursor)),
         "achieved_gbs": float(np.sum(nbytes) / (region_ms * 1e-3) / 1e9),
         "by_position_us": {k: round(1e3 * float(np.mean(v)), 1) for k, v in sorted(by_pos.items())},
+        "timed_cursor_counts": dict(sorted(mix.items())),
+        "first_timed_cursor": (warmup + phi) % L,
+        "launches": launches,
     }
 
 
@@ -367,7 +473,7 @@ def suite_gdn_sweep(out, steps=32):
             torch.cuda.empty_cache()
 
 
-def suite_stack(out, n_layers=40):
+def suite_stack(out, n_layers=40, quick=False):
     """40 Mamba-2 layers at the Nemotron-3-Super shape, batch 256: time and
     algorithmic bytes of one decode step over all layers (one launch per
     layer), replay for L in {8, 16, 32} with fp32 and fp16 checkpoints, replay
@@ -382,6 +488,8 @@ def suite_stack(out, n_layers=40):
     runs = [("conventional", 16, "f32", None), ("conventional", 16, "f16", None)]
     runs += [("replay", L, st, None) for st in ("f32", "f16") for L in (8, 16, 32)]
     runs += [("replay", 16, "f32", rd) for rd in ("f16", "bf16", "e4m3")]
+    if quick:  # the fp32 conventional step and the L = 16 fp32 replay step only
+        runs = [("conventional", 16, "f32", None), ("replay", 16, "f32", None)]
     for kind, L, state, read in runs:
         cfg = dict(base, L=L, state=state, read=read)
         layers = _layer_stack(cfg, base["B"], n_layers, dev)
@@ -401,9 +509,12 @@ def suite_stack(out, n_layers=40):
                 else:
                     d.conventional_step(io)
                     w, f = 0, False
+                nb = step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], state, cfg["rec"], cfg["io"],
+                                w, f, kind, read)
+                log_launch("k_replay_step" if kind == "replay" else "k_conventional_step",
+                           f"stack40 {kind} L={L} {state}" + (f" read {read}" if read else ""), nb)
                 if s >= n_warm:
-                    nbytes += step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], state, cfg["rec"],
-                                         cfg["io"], w, f, kind, read)
+                    nbytes += nb
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         torch.cuda.synchronize()
@@ -443,7 +554,7 @@ def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0):
     return float(np.sum(H * per_head + 9) + B * 18)
 
 
-def suite_spec(out, steps=48, n_pools=4, workload="nemotron"):
+def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
     """Speculative verify at the Nemotron-3-Super layer shape (or, workload
     "gdn", the Gated DeltaNet layer: 32 heads, 128 x 128), batch 256,
     L = 16, fp32 checkpoint, fp16 records, bf16 inputs, T in {4, 8}, with
@@ -474,9 +585,13 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron"):
                 e0.record()
             d = layers[s % n_pools]
             if kind == "replay":
-                d.step(ios[s % 16])
+                wp, fl = d.step(ios[s % 16])
+                w, f = int(wp[0]), bool(fl[0])
             else:
                 d.conventional_step(ios[s % 16])
+                w, f = 0, False
+            log_launch("k_replay_step" if kind == "replay" else "k_conventional_step", f"spec reference {kind}",
+                       step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind))
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         torch.cuda.synchronize()
@@ -484,7 +599,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron"):
         del layers
         torch.cuda.empty_cache()
     del ios, keep
-    for T in (4, 8):
+    for T in Ts:
         lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", None, T)
         drafts = []
         for s in range(8):
@@ -515,12 +630,16 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron"):
                 d, hm = pools[pi], hmirror[pi]
                 a = acc_host[s % steps]
                 fl = rs.rs_spec_meta_step(L, T, hm)
+                nb = spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form)
                 if s >= n_warm:
-                    nbytes += spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form)
+                    nbytes += nb
                     tokens += int(a.sum())
                     n_flush += int(fl.sum())
                 d.verify(drafts[s % 8][1])
                 d.commit(acc[s % steps])
+                log_launch("k_spec_verify" if form == 0 else "k_spec_verify_gdn", f"T={T} accept {policy}",
+                           nb - B * 18)
+                log_launch("k_spec_commit", f"T={T} accept {policy}", B * 18)
                 rs.rs_spec_meta_advance(L, T, hm, fl, a)
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record()
@@ -652,16 +771,27 @@ def calibrate_copy(mib: int) -> None:
 
 def _read_counter_csv(path):
     """Per-dispatch counter values from a rocprofv3 counter_collection.csv:
-    returns [(kernel_name, counter_name, value)]."""
+    returns [(dispatch id, kernel_name, counter_name, value)] in dispatch
+    order."""
     import csv
     rows = []
     with open(path, newline="") as f:
-        for r in csv.DictReader(f):
+        for i, r in enumerate(csv.DictReader(f)):
             name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("kernel_name") or ""
             cname = r.get("Counter_Name") or r.get("Counter-Name") or ""
             val = r.get("Counter_Value") or r.get("Counter-Value") or "0"
-            rows.append((name, cname, float(val)))
+            did = r.get("Dispatch_Id") or r.get("Dispatch-Id") or r.get("dispatch_id") or i
+            rows.append((int(did), name, cname, float(val)))
+    rows.sort(key=lambda t: t[0])
     return rows
+
+
+def kernel_family(name: str) -> str:
+    """The function name of a (demangled) kernel: 'k_replay_step' for
+    'void rs::(anonymous namespace)::k_replay_step<0, 64, ...>(rs::StepParams)'."""
+    import re
+    m = re.search(r"(k_[A-Za-z0-9_]+)\s*[<(]", name)
+    return m.group(1) if m else name
 
 
 def config_from_args(args):
@@ -678,44 +808,99 @@ def config_from_args(args):
     return cfg
 
 
+def counter_scale(rows, mib, what):
+    """Bytes per counter unit: the counters are KiB per dispatch; the
+    calibration copy of `mib` MiB (three dispatches, the largest copies of the
+    run) gives the scale."""
+    copy = sorted((v for (_, n, _, v) in rows if "copy" in n.lower() and not n.lstrip().startswith("void rs::")),
+                  reverse=True)[:3]
+    if not copy or copy[-1] * 1024 < 0.25 * mib * 2**20:
+        raise SystemExit(f"no calibration copy of ~{mib} MiB found in the {what} counters")
+    return mib * 2**20 / (float(np.median(copy)) * 1024)
+
+
+def line_up(rows, log, scale):
+    """Measured bytes per logged launch: the dispatches of each kernel
+    family, in dispatch order, against that family's logged launches, in
+    launch order.  Returns {(family, label): [(measured, algorithmic), ...]}."""
+    disp = {}
+    for (_, name, _, v) in rows:
+        disp.setdefault(kernel_family(name), []).append(v * 1024 * scale)
+    logged = {}
+    for fam, label, nb in log:
+        logged.setdefault(fam, []).append((label, nb))
+    out = {}
+    for fam, launches in logged.items():
+        got = disp.get(fam, [])
+        if len(got) != len(launches):
+            raise SystemExit(f"{fam}: {len(got)} dispatches in the counters, {len(launches)} launches logged")
+        for (label, nb), m in zip(launches, got):
+            out.setdefault((fam, label), []).append((m, nb))
+    return out
+
+
 def summarize_counters(args, fetch_csv, write_csv):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
-    (known bytes of the calibration copy) / (its reading), then averaged per
-    launch of the checkpoint + buffer kernel and of the conventional kernel."""
-    out = {}
+    (known bytes of the calibration copy) / (its reading).  The dispatches
+    are lined up with the launch log that the profiled run wrote
+    (--launch-log), which gives each launch's label (cursor, suite case) and
+    algorithmic bytes.  Prints one JSON line per (kernel, label) with the
+    mean measured fetch, write and total per launch and the ratio to the
+    algorithmic bytes.  For the one-line benchmark (labels = cursors), the
+    window average over cursors is stored in profiles/counters.json under
+    the workload's key."""
     mib = args.calibrate_copy
     if not mib:
         raise SystemExit("--summarize-counters needs --calibrate-copy MIB (the size used in the profiled run)")
-    res = {}
+    if not args.launch_log:
+        raise SystemExit("--summarize-counters needs --launch-log PATH (written by the profiled run)")
+    log = json.load(open(args.launch_log))
+    per = {}
+    scales = {}
     for label, path in (("fetch", fetch_csv), ("write", write_csv)):
-        per = {}
-        for name, cname, val in _read_counter_csv(path):
-            per.setdefault(name, []).append(val)
-        # the calibration copy is the largest copy dispatch of the run (three of them)
-        copy = sorted((v for n, vs in per.items() if "copy" in n.lower() and "rs::" not in n for v in vs),
-                      reverse=True)[:3]
-        if not copy or copy[-1] * 1024 < 0.25 * mib * 2**20:
-            raise SystemExit(f"no calibration copy of ~{mib} MiB found in {path}")
-        scale = mib * 2**20 / (float(np.median(copy)) * 1024)
-        res[label] = {"scale": scale,
-                      "replay": float(np.mean([v for n, vs in per.items() if "k_replay_step" in n for v in vs])) * 1024 * scale,
-                      "conventional": float(np.mean([v for n, vs in per.items() if "k_conventional_step" in n for v in vs])) * 1024 * scale}
-    cfg = config_from_args(args)
-    key = workload_key(args.workload, cfg)
-    entry = {"kernel_source": kernel_source_hash(),
-             "bytes_per_launch": round(res["fetch"]["replay"] + res["write"]["replay"]),
-             "replay": {"fetch": round(res["fetch"]["replay"]), "write": round(res["write"]["replay"])},
-             "conventional": {"fetch": round(res["fetch"]["conventional"]), "write": round(res["write"]["conventional"]),
-                              "bytes_per_launch": round(res["fetch"]["conventional"] + res["write"]["conventional"])},
-             "scale": {"fetch": round(res["fetch"]["scale"], 4), "write": round(res["write"]["scale"], 4)},
-             "calibration_copy_mib": mib}
-    path = os.path.join(ROOT, "profiles", "counters.json")
-    data = json.load(open(path)) if os.path.exists(path) else {}
-    data[key] = entry
-    with open(path, "w") as f:
-        json.dump(data, f, indent=1, sort_keys=True)
-        f.write("\n")
-    print(json.dumps({key: entry}))
+        rows = _read_counter_csv(path)
+        scales[label] = counter_scale(rows, mib, label)
+        per[label] = line_up(rows, log["launches"], scales[label])
+    table = {}
+    for key in per["fetch"]:
+        f = np.array([m for m, _ in per["fetch"][key]])
+        w = np.array([m for m, _ in per["write"][key]])
+        alg = np.array([nb for _, nb in per["fetch"][key]])
+        table[key] = {"kernel": key[0], "label": key[1], "launches": len(f), "fetch": float(f.mean()),
+                      "write": float(w.mean()), "total": float((f + w).mean()), "algorithmic": float(alg.mean()),
+                      "ratio": float((f + w).sum() / alg.sum())}
+        print(json.dumps({k: (round(v) if isinstance(v, float) and k != "ratio" else
+                              (round(v, 4) if k == "ratio" else v)) for k, v in table[key].items()}))
+    # the one-line benchmark's launches: window averages over the cursors
+    L = log.get("L")
+    if L and log.get("workload_key"):
+        def window(fam):
+            labels = [f"w{w}" for w in range(L - 1)] + ["flush"]
+            if fam == "k_conventional_step":
+                labels = ["conventional"]
+            rows = [table.get((fam, lb)) for lb in labels]
+            if any(r is None for r in rows):
+                raise SystemExit(f"{fam}: not every cursor position was profiled")
+            return {k: float(np.mean([r[k] for r in rows])) for k in ("fetch", "write", "total", "algorithmic")}
+        rep, conv = window("k_replay_step"), window("k_conventional_step")
+        entry = {"kernel_source": kernel_source_hash(),
+                 "bytes_per_launch": round(rep["total"]),
+                 "basis": "window average: mean over the L cursor positions of the mean per launch",
+                 "replay": {"fetch": round(rep["fetch"]), "write": round(rep["write"]),
+                            "algorithmic": round(rep["algorithmic"]),
+                            "by_cursor": {lb: round(table[("k_replay_step", lb)]["total"])
+                                          for lb in [f"w{w}" for w in range(L - 1)] + ["flush"]}},
+                 "conventional": {"fetch": round(conv["fetch"]), "write": round(conv["write"]),
+                                  "bytes_per_launch": round(conv["total"]), "algorithmic": round(conv["algorithmic"])},
+                 "scale": {"fetch": round(scales["fetch"], 4), "write": round(scales["write"], 4)},
+                 "calibration_copy_mib": mib}
+        path = os.path.join(ROOT, "profiles", "counters.json")
+        data = json.load(open(path)) if os.path.exists(path) else {}
+        data[log["workload_key"]] = entry
+        with open(path, "w") as fo:
+            json.dump(data, fo, indent=1, sort_keys=True)
+            fo.write("\n")
+        print(json.dumps({log["workload_key"]: entry}))
     return 0
 
 
@@ -732,7 +917,8 @@ def main(argv=None):
                     help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="state stores: nearest even, or stochastic rounding (fp16 state)")
-    ap.add_argument("--pools", type=int, default=4)
+    ap.add_argument("--pools", type=int, default=None,
+                    help="state pools in rotation (default L + 1; must be 1 mod L)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows in the CPU-baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -742,12 +928,24 @@ def main(argv=None):
                          "40-layer stack and write JSON lines to PATH")
     ap.add_argument("--suite-only", choices=["gdn", "stack", "spec", "continuous"], default=None,
                     help="with --suite: run one part of it")
+    ap.add_argument("--spec-T", type=int, action="append", default=None,
+                    help="with --suite-only spec: the draft counts to run (default 4 and 8)")
+    ap.add_argument("--spec-workload", choices=["nemotron", "gdn"], action="append", default=None,
+                    help="with --suite-only spec: the layers to run (default both)")
+    ap.add_argument("--stack-quick", action="store_true",
+                    help="with --suite-only stack: only the fp32 conventional and the L = 16 fp32 replay stacks")
+    ap.add_argument("--launch-log", metavar="PATH",
+                    help="write every launch of the library's kernels (kernel, label, algorithmic bytes) in launch "
+                         "order to PATH (for --summarize-counters); with --summarize-counters: read it")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                          "into per-launch HBM bytes in profiles/counters.json and print them; runs nothing on the GPU")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         return summarize_counters(args, *args.summarize_counters)
+    global _LAUNCH_LOG
+    if args.launch_log:
+        _LAUNCH_LOG = []
     if args.suite:
         if args.gpus != 1:
             print("the suite runs on one GPU", file=sys.stderr)
@@ -756,13 +954,16 @@ def main(argv=None):
             if args.suite_only in (None, "gdn"):
                 suite_gdn_sweep(out)
             if args.suite_only in (None, "stack"):
-                suite_stack(out)
+                suite_stack(out, quick=args.stack_quick)
             if args.suite_only in (None, "spec"):
-                suite_spec(out)
-                suite_spec(out, workload="gdn")
+                for wl in args.spec_workload or ["nemotron", "gdn"]:
+                    suite_spec(out, workload=wl, Ts=tuple(args.spec_T or (4, 8)))
             if args.suite_only in (None, "continuous"):
                 suite_continuous(out)
         print(open(args.suite).read(), end="")
+        if args.launch_log:
+            with open(args.launch_log, "w") as f:
+                json.dump({"launches": _LAUNCH_LOG}, f)
         return 0
 
     if args.gpus != 1:
@@ -771,11 +972,17 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     cfg = config_from_args(args)
+    pools = args.pools or cfg["L"] + 1
+    try:
+        cursor_schedule(cfg["L"], pools, args.warmup, args.steps, cursor_bytes(cfg))
+    except ValueError as e:
+        print(f"bench.py: {e}", file=sys.stderr)
+        return 2
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
-    rep = run_gpu(cfg, args.steps, args.warmup, args.pools, "replay")
-    conv = run_gpu(cfg, args.steps, args.warmup, args.pools, "conventional")
+    rep = run_gpu(cfg, args.steps, args.warmup, pools, "replay")
+    conv = run_gpu(cfg, args.steps, args.warmup, pools, "conventional")
 
     groups = cfg.get("groups", 0)
     wb_r = window_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["B"], cfg["state"], cfg["rec"], cfg["io"], cfg["L"],
@@ -807,17 +1014,23 @@ def main(argv=None):
         "config": {"workload": workload, "global_batch": cfg["B"], "seq_len": None, "heads": cfg["H"],
                    "d_v": cfg["dv"], "d_k": cfg["dk"], "L": cfg["L"], "state_dtype": cfg["state"],
                    "read_copy_dtype": cfg["read"], "state_rounding": args.rounding,
-                   "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": args.pools,
+                   "record_dtype": cfg["rec"], "io_dtype": cfg["io"], "state_pools": pools,
                    "key_groups": groups or cfg["H"],
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "k_replay_step", "bytes_per_launch": round(rep["bytes_per_launch_mean"]),
+                     "window_bytes_per_launch": round(rep["window_bytes_per_launch"]),
+                     "basis": "timed launches: floor(K/L) whole windows plus K mod L consecutive cursors; "
+                              "traffic: window average over the L cursors (rocprofv3 counters)",
                      "launch_us": round(1e3 * rep["kernel_ms_mean"], 2)},
         "replay": {"steps_per_s": round(rep["steps_per_s"], 2), "kernel_us": round(1e3 * rep["kernel_ms_mean"], 2),
                    "kernel_steps_per_s": round(1e3 / rep["kernel_ms_mean"], 2),
                    "achieved_tbs": round(achieved / 1e3, 3), "pct_peak": round(100 * achieved / HBM_PEAK_GBS, 1),
-                   "us_by_cursor": rep["by_position_us"]},
+                   "timed_cursor_counts": rep["timed_cursor_counts"],
+                   "first_timed_cursor": rep["first_timed_cursor"],
+                   "us_by_cursor": rep["by_position_us"],
+                   "window_us_from_cursors": window_us(rep["by_position_us"], cfg["L"])},
         "conventional": {"steps_per_s": round(conv["steps_per_s"], 2), "kernel_us": round(1e3 * conv["kernel_ms_mean"], 2),
                          "kernel_steps_per_s": round(1e3 / conv["kernel_ms_mean"], 2),
                          "achieved_tbs": round(conv["achieved_gbs"] / 1e3, 3),
@@ -827,6 +1040,9 @@ def main(argv=None):
         "algorithmic_bytes_ratio": round(wb_r / wb_c, 4),
         "kernel_source": kernel_source_hash(),
     }
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            json.dump({"launches": _LAUNCH_LOG, "L": cfg["L"], "workload_key": key}, f)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, rows=args.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -69,3 +69,92 @@ def test_grouped_window_bytes_match_model(L):
     assert conv == pytest.approx(c["B"] * H * bm.conventional_window_bytes(L, ms), rel=1e-12)
     if L == 16:  # the blog's "about 0.55 of conventional traffic"
         assert abs(got / conv - 0.5503) < 5e-4
+
+
+def _simulate(L, pools, warmup, steps, per_cursor):
+    """Drive the host cursor rule (rs_meta_step / rs_meta_advance, what
+    DecodeLayer calls) over the benchmark's schedule: pool preparation, W
+    warm-up and K timed launches.  Returns the timed launches' cursors."""
+    import numpy as np
+    import linear_attention_decode_replay_amd as rs
+    phi, starts = bench.cursor_schedule(L, pools, warmup, steps, per_cursor)
+    anchors = [np.zeros(3, np.int32) for _ in range(pools)]   # three rows per pool, all in phase
+    for p, n in enumerate(starts):
+        for _ in range(n):
+            _, fl = rs.rs_meta_step(L, anchors[p])
+            rs.rs_meta_advance(L, anchors[p], fl)
+    timed = []
+    for s in range(warmup + steps):
+        a = anchors[s % pools]
+        wp, fl = rs.rs_meta_step(L, a)
+        assert len(set(wp.tolist())) == 1 and int(wp[0]) == (s + phi) % L
+        assert bool(fl[0]) == (int(wp[0]) == L - 1)
+        rs.rs_meta_advance(L, a, fl)
+        if s >= warmup:
+            timed.append(int(wp[0]))
+    return timed
+
+
+@pytest.mark.parametrize("L,pools,warmup,steps", [
+    (16, 17, 5, 20), (16, 17, 64, 64), (16, 17, 0, 64), (16, 33, 3, 50), (16, 17, 16, 1),
+    (16, 17, 7, 15), (16, 17, 9, 8), (8, 9, 5, 20), (32, 33, 5, 20), (4, 5, 1, 9), (1, 1, 2, 3)])
+def test_timed_cursor_mix(L, pools, warmup, steps):
+    """The K timed launches are floor(K/L) whole windows plus one run of
+    K mod L consecutive cursors, for any warm-up; whole windows exactly when
+    L divides K; the run is the one whose mean algorithmic bytes are closest
+    to the window average."""
+    c = dict(bench.WORKLOADS["nemotron"], L=L)
+    per = bench.cursor_bytes(c)
+    timed = _simulate(L, pools, warmup, steps, per)
+    counts = [timed.count(w) for w in range(L)]
+    full, extra = divmod(steps, L)
+    assert sorted(counts) == [full] * (L - extra) + [full + 1] * extra
+    c0 = timed[0]
+    assert c0 == bench.timed_phase(per, steps)
+    assert all(timed[i] == (c0 + i) % L for i in range(steps))
+    win = sum(per) / L
+    got = sum(per[w] for w in timed) / steps
+    for alt in range(L):   # no other start is closer to the window average
+        m = sum(per[(alt + i) % L] for i in range(steps)) / steps
+        assert abs(got - win) <= abs(m - win) * (1 + 1e-12)
+    if extra == 0:
+        assert c0 == 0 and got == pytest.approx(win, rel=1e-15)
+
+
+def test_driver_schedule_is_near_the_window_average():
+    """--steps 20 --warmup 5 at the headline shape: one flush among the 20
+    timed launches, and their algorithmic bytes within 0.1 % of the window
+    average (the flush-free 6/16 of a window that a plain rotation of
+    in-phase pools would time is 9 % below it)."""
+    c = dict(bench.WORKLOADS["nemotron"])
+    per = bench.cursor_bytes(c)
+    timed = _simulate(16, 17, 5, 20, per)
+    assert timed.count(15) == 1
+    win = sum(per) / 16
+    assert abs(sum(per[w] for w in timed) / 20 / win - 1) < 1e-3
+    assert sum(per[w] for w in range(1, 7)) / 6 / win < 0.92
+
+
+def test_pool_count_must_be_one_mod_L():
+    c = dict(bench.WORKLOADS["nemotron"])
+    with pytest.raises(ValueError):
+        bench.cursor_schedule(16, 4, 5, 20, bench.cursor_bytes(c))
+    assert bench.main(["--pools", "4", "--steps", "20"]) == 2
+
+
+def test_counter_lineup():
+    """Counter dispatches are matched to logged launches per kernel, in order;
+    the counters' KiB are scaled by the calibration copy."""
+    rows = [(0, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)] * 3
+    rows += [(1, "void rs::(anonymous namespace)::k_replay_step<0, 64>(rs::StepParams)", "FETCH_SIZE", 10.0),
+             (2, "void rs::(anonymous namespace)::k_conventional_step<0>(rs::StepParams)", "FETCH_SIZE", 7.0),
+             (3, "void rs::(anonymous namespace)::k_replay_step<0, 64, true>(rs::StepParams)", "FETCH_SIZE", 12.0)]
+    scale = bench.counter_scale(rows, 1, "fetch")
+    assert scale == 2.0
+    got = bench.line_up(rows, [("k_replay_step", "w0", 20480.0), ("k_conventional_step", "conventional", 1.0),
+                               ("k_replay_step", "flush", 24576.0)], scale)
+    assert got[("k_replay_step", "w0")] == [(20480.0, 20480.0)]
+    assert got[("k_replay_step", "flush")] == [(24576.0, 24576.0)]
+    assert got[("k_conventional_step", "conventional")] == [(14336.0, 1.0)]
+    with pytest.raises(SystemExit):
+        bench.line_up(rows, [("k_replay_step", "w0", 1.0)], scale)
