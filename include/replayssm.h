@@ -44,7 +44,12 @@
  *     aligned; block_table, write_pos, flush and reset masks 4 bytes (the
  *     byte arrays are read in aligned 32-bit words, never past the word that
  *     holds the last entry).
- *   - Sizes: n_rows <= 65535 per launch.
+ *   - Sizes: n_rows <= 65535 per launch.  A layer's buffered records are
+ *     staged in LDS and must fit one gfx950 workgroup's 160 KiB (every
+ *     supported shape does, up to L = 64); a launch whose workgroups need
+ *     more than 64 KiB also checks the device's own limit
+ *     (hipDeviceAttributeMaxSharedMemoryPerBlock) and returns
+ *     RS_EUNSUPPORTED if it is lower.
  */
 #ifndef REPLAYSSM_H
 #define REPLAYSSM_H
@@ -319,6 +324,9 @@ int replay_decode_step(const rs_layer* layer, const rs_batch* batch, const rs_st
  * are untouched.  This materialises the exact state at any step: before a row
  * is retired or preempted, or at a prefix-cache block boundary (vLLM pull
  * request, "What this PR adds", align mode).  batch->flush must not be NULL.
+ * On a speculative layer (spec_T > 0) write_pos is the row's committed count
+ * h (0..L) and its h committed records are folded; the caller then sets h to
+ * 0 in the count array its next verify reads.
  */
 int replay_flush(const rs_layer* layer, const rs_batch* batch, hipStream_t stream);
 
@@ -446,7 +454,9 @@ int replay_spec_commit(const rs_layer* layer, const rs_batch* batch, const int32
  * force[r] != 0 (force may be NULL), 0 for padding rows (committed < 0).
  * rs_spec_meta_advance: committed[r] = (flush[r] ? 0 : committed[r]) +
  * accepted[r] for non-padding rows, in place.  RS_EINVAL on NULL arrays,
- * n_rows < 0, L outside 1..64 or T outside 1..L.
+ * n_rows < 0, L outside 1..64, T outside 1..L, or an accepted count of a
+ * non-padding row outside 0..T (checked for every row first: on error no
+ * row is updated; the device commit skips and counts such a row).
  */
 int rs_spec_meta_step(int32_t L, int32_t T, int32_t n_rows, const int32_t* committed,
                       const uint8_t* force, uint8_t* flush);

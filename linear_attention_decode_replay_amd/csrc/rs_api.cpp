@@ -1,6 +1,10 @@
 // Host side of the C ABI declared in replayssm.h: argument validation, the
 // paged block layout, the per-row cursor/flush metadata and kernel launch.
-// No allocation, no global mutable state (the error text is thread-local).
+// The entry points allocate no device memory.  Global state: the error text
+// (thread-local) and, in rs_kernels.hip, a mutex-guarded cache of occupancy
+// queries (workgroups per compute unit of the persistent replay step, per
+// device and LDS size), which grows on the host heap the first time each
+// (kernel, LDS size, device) is launched.
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -40,7 +44,11 @@ bool two_precision(const rs_layer& L) { return L.read_dtype >= 0 && L.read_dtype
 
 // Key groups: n_groups, or one per head.
 int groups_of(const rs_layer& L) { return L.n_groups > 0 ? L.n_groups : L.n_heads; }
-const size_t kMaxLds = 64 * 1024;
+// LDS of one workgroup on gfx950, the one target the kernels are built for;
+// a launch also checks the device's own limit (do_launch).
+const size_t kMaxLds = 160 * 1024;
+// LDS any gfx9 workgroup can have without asking the device.
+const size_t kBaseLds = 64 * 1024;
 
 int check_layer(const rs_layer* L, rs::Kind kind) {
     if (!L) return fail(RS_EINVAL, "layer is NULL");
@@ -231,6 +239,16 @@ void set_io(rs::StepParams& p, const rs_step_io& io) {
 }
 
 int do_launch(rs::Kind kind, const rs_layer& L, const rs::StepParams& p, hipStream_t stream) {
+    const size_t lds = rs::lds_bytes(kind, L);
+    if (lds > kBaseLds) {
+        int dev = 0, max_lds = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return fail(RS_EHIP, "cannot query the device's LDS per workgroup");
+        if (lds > (size_t)max_lds)
+            return fail(RS_EUNSUPPORTED, "buffer of L=%d records needs %zu bytes of LDS; device %d allows %d",
+                        L.L, lds, dev, max_lds);
+    }
     (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
     const hipError_t e = rs::launch(kind, L, p, stream);
     if (e != hipSuccess) return fail(RS_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -424,6 +442,11 @@ int rs_spec_meta_advance(int32_t L, int32_t T, int32_t n_rows, int32_t* committe
     if (n_rows < 0) return fail(RS_EINVAL, "n_rows must be >= 0");
     if (n_rows == 0) return ok();
     if (!committed || !flush || !accepted) return fail(RS_EINVAL, "NULL array");
+    // every count is checked before any row moves, so a bad count leaves the
+    // mirror as it was (the device commit skips and counts such a row)
+    for (int32_t r = 0; r < n_rows; ++r)
+        if (committed[r] >= 0 && (accepted[r] < 0 || accepted[r] > T))
+            return fail(RS_EINVAL, "accepted[%d] = %d is outside 0..T (T=%d)", r, accepted[r], T);
     for (int32_t r = 0; r < n_rows; ++r)
         if (committed[r] >= 0) committed[r] = (flush[r] ? 0 : committed[r]) + accepted[r];
     return ok();

@@ -2650,7 +2650,9 @@ struct Dispatch {
     }
 
     bool run() {
-        const int slots = L.L - 1;
+        // record slots per head: the block layout's (a speculative ring holds
+        // L committed records, a standard buffer L - 1)
+        const int slots = L.spec_T > 0 ? L.L : L.L - 1;
         bool ok = false;
         with_shape(L.d_v, L.d_k, [&](auto dv_c, auto dk_c) {
             constexpr int DV = decltype(dv_c)::value, DK = decltype(dk_c)::value;

@@ -26,8 +26,12 @@ TOL_F32 = 1e-4   # fp32 state and fp32 records
 TOL_LOW = 2e-2   # fp16/bf16 records or checkpoint
 
 
-def tolerance(state_dt, rec_dt, io_dt):
-    return TOL_F32 if (state_dt, rec_dt, io_dt) == ("f32", "f32", "f32") else TOL_LOW
+def tolerance(state_dt, rec_dt, io_dt=None):
+    """The gate for a layer's state and record dtypes: 1e-4 with an fp32
+    state and fp32 records, 2e-2 with fp16/bf16 records or checkpoint.  The
+    io dtype does not enter: the oracle is given the same (bf16/fp16-valued)
+    inputs as the kernels."""
+    return TOL_F32 if (state_dt, rec_dt) == ("f32", "f32") else TOL_LOW
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray, tile_dims: int = 1) -> float:
@@ -75,6 +79,7 @@ class Case:
     groups: int = 0                  # key groups (0: a key and query per head)
     reconstruct: bool = False        # Gated DeltaNet: the state-reconstruction route
     flush_hints: bool = True         # pass the host's flush hint (False: RS_FLUSH_UNKNOWN)
+    forget_every: int = 0            # > 0: every n-th (step, row, head) has lam = -inf (alpha = 0)
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
@@ -82,7 +87,17 @@ class Case:
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
                 f"strided={self.strided} pad={self.pad_rows} groups={self.groups} "
                 f"route={'reconstruct' if self.reconstruct else 'output-only'} hints={self.flush_hints} "
-                f"seed={self.seed}")
+                f"forget_every={self.forget_every} seed={self.seed}")
+
+
+def full_forgetting(lam: torch.Tensor, every: int, step: int) -> None:
+    """Set every `every`-th log-decay of this step to -inf (alpha = 0, a
+    legal decay: the blog's weights are products of the alphas), counting
+    over (step, row, ...) in row-major order, in place."""
+    if every > 0:
+        n = lam.numel()
+        idx = torch.arange(n).reshape(lam.shape) + step * n
+        lam[(idx % every) == 0] = float("-inf")
 
 
 def grouped(tok, hg: int):
@@ -151,6 +166,7 @@ def run_case(c: Case, dev="cuda") -> dict:
            "out_replay_step": 0.0, "out_replay_vs_exact": 0.0, "flushes": 0}
     for s in range(c.steps):
         tok = workloads.tokens(c.form, c.seed, s, c.B, c.H, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi)
+        full_forgetting(tok.lam, c.forget_every, s)
         tok, qg, kg = grouped(tok, hg)
         q, k, v = _device_tokens(tok, c.strided, dev, (qg, kg))
         lam = tok.lam.to(dev)

@@ -71,13 +71,26 @@ def test_block_layout_regions_disjoint(L, shape, sdt, rdt):
     (dict(L=0), rs.RS_EINVAL), (dict(L=65), rs.RS_EINVAL), (dict(form=7), rs.RS_EINVAL),
     (dict(n_heads=0), rs.RS_EINVAL), (dict(d_v=32, d_k=32), rs.RS_EUNSUPPORTED),
     (dict(state_dtype="bf16"), rs.RS_EUNSUPPORTED), (dict(io_dtype=9), rs.RS_EINVAL),
-    (dict(d_v=128, d_k=128, L=64, record_dtype="f32"), rs.RS_EUNSUPPORTED),
 ])
 def test_layer_validation(bad, code):
     with pytest.raises(rs.ReplaySSMError) as e:
         rs.block_layout(_c2(**bad))
     assert e.value.code == code
     assert rs.last_error()
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+@pytest.mark.parametrize("spec_T", [0, 8])
+def test_largest_buffers_fit_the_workgroup_lds(form, spec_T):
+    """L = 64 with fp32 records at 128 x 128 (the largest record area) is
+    supported: its records fit one gfx950 workgroup's LDS."""
+    if spec_T and form == rs.MAMBA2:
+        shape = dict(d_v=64, d_k=128)   # the Mamba-2 verify's largest head
+    else:
+        shape = dict(d_v=128, d_k=128)
+    layer = _c2(form=form, L=64, record_dtype="f32", state_dtype="f32", io_dtype="f32", spec_T=spec_T, **shape)
+    assert rs.layer_supported(layer) == rs.RS_OK, rs.last_error()
+    assert rs.block_layout(layer).slots == (64 if spec_T else 63)
 
 
 def test_empty_batch_launches_nothing():
@@ -260,6 +273,17 @@ def test_spec_meta_pad_rows_and_bad_arguments():
         rs.rs_spec_meta_step(16, 17, h)
     with pytest.raises(rs.ReplaySSMError):
         rs.rs_spec_meta_step(16, 0, h)
+    # an accepted count outside 0..T is an error and moves no row (a padding
+    # row's count is not looked at)
+    for bad in ([0, 5, 1], [0, 1, -1]):
+        h2 = np.array([-1, 3, 7], np.int32)
+        with pytest.raises(rs.ReplaySSMError) as e:
+            rs.rs_spec_meta_advance(16, 4, h2, np.zeros(3, np.uint8), np.array(bad, np.int32))
+        assert e.value.code == rs.RS_EINVAL and "accepted" in rs.last_error()
+        assert list(h2) == [-1, 3, 7]
+    h3 = np.array([-1, 3], np.int32)
+    rs.rs_spec_meta_advance(16, 4, h3, np.zeros(2, np.uint8), np.array([99, 4], np.int32))
+    assert list(h3) == [-1, 7]
 
 
 # ------------------------------------------------------------ grouped keys --
