@@ -20,7 +20,11 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
-    # no packed-fp32 instructions: plain float code only
+    # No packed-fp32 instructions (v_pk_fma/mul/add_f32) in the gfx950 code:
+    # turn the target feature off for the device pass.  hipcc hands the same
+    # flag to the host (x86) pass, which warns that it does not know the
+    # feature and ignores it; the device pass honours it
+    # (tests/test_build_flags.py disassembles the built library to check).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
