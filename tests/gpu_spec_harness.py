@@ -18,7 +18,7 @@ import torch
 import linear_attention_decode_replay_amd as rs
 import oracle
 import workloads
-from gpu_harness import rel_err, say
+from gpu_harness import full_forgetting, rel_err, say
 from linear_attention_decode_replay_amd.state import SpecDecodeLayer
 
 
@@ -43,12 +43,13 @@ class SpecCase:
     pad_rows: list = field(default_factory=list)
     strided: bool = False            # q/k/v as strided views of wider buffers
     force_row0_every: int = 0        # > 0: force a flush on row 0 every n steps
+    forget_every: int = 0            # > 0: every n-th (step, row, draft, head) has lam = -inf
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"spec {f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} accept={self.accept} "
-                f"strided={self.strided} pad={self.pad_rows} seed={self.seed}")
+                f"strided={self.strided} pad={self.pad_rows} forget_every={self.forget_every} seed={self.seed}")
 
 
 def _device(t: torch.Tensor, strided: bool, dev):
@@ -82,6 +83,7 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     err = {"out_spec": 0.0, "out_vs_tokens": 0.0, "ckpt_flush": 0.0, "rec_u": 0.0, "flushes": 0, "accepted": 0}
     for s in range(c.steps):
         tok = workloads.spec_tokens(c.seed, s, c.B, c.H, c.T, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi, c.form)
+        full_forgetting(tok.lam, c.forget_every, s)
         force = np.zeros(c.B, np.uint8)
         if c.force_row0_every and (s + 1) % c.force_row0_every == 0 and 0 in live:
             force[0] = 1

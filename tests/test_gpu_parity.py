@@ -43,6 +43,30 @@ def test_tiny_buffer_lengths(form, L):
 
 
 @pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+def test_largest_buffer_128x128_fp32_records(form):
+    """L = 64 with fp32 records at 128 x 128, the largest record area (63
+    slots of 1 KiB per head, staged in LDS): 70 steps, one flush, fp32
+    throughout."""
+    err = _go(Case(form=form, B=2, H=2, dv=128, dk=128, L=64, steps=70, seed=64))
+    assert err["flushes"] == 1
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+@pytest.mark.parametrize("shape,dts", [((16, 32), ("f32", "f32", "f32")), ((64, 128), ("f32", "f16", "bf16")),
+                                       ((128, 128), ("f16", "f16", "bf16"))])
+def test_full_forgetting(form, shape, dts):
+    """alpha = 0 (lam = -inf) on every 5th (step, row, head): the checkpoint
+    and the records before it drop out of the output (oracle pin
+    pin_full_forgetting), in flush and non-flush steps, appended records
+    carry lam = -inf bit for bit, and nothing turns into NaN."""
+    dv, dk = shape
+    sdt, rdt, io = dts
+    err = _go(Case(form=form, B=3, H=3, dv=dv, dk=dk, L=4, steps=24, state_dt=sdt, rec_dt=rdt, io_dt=io,
+                   forget_every=5, force_every=7, seed=70))
+    assert err["flushes"] >= 6
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
 @pytest.mark.parametrize("sdt,rdt,io", [("f32", "f16", "bf16"), ("f16", "f16", "bf16"),
                                         ("f16", "f32", "f16"), ("f32", "f32", "bf16")])
 def test_tiny_dtypes(form, sdt, rdt, io):

@@ -207,7 +207,7 @@ def test_continuous_batching():
     assert int(rep.err.item()) == 0 and int(conv.err.item()) == 0
 
 
-@pytest.mark.parametrize("L,state_dt", [(8, "f32"), (16, "f32"), (32, "f32"), (16, "f16")])
+@pytest.mark.parametrize("L,state_dt", [(8, "f32"), (16, "f32"), (32, "f32"), (8, "f16"), (16, "f16"), (32, "f16")])
 def test_stack_of_40_layers(L, state_dt):
     """40 Mamba-2 layers at the Nemotron-3-Super shape, batch 256, one pool
     per layer; one window plus three steps.  All layers run on the GPU with
@@ -255,3 +255,55 @@ def test_stack_of_40_layers(L, state_dt):
     assert all(int(d.err.item()) == 0 for d in layers)
     del layers
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("form,shape", [(rs.MAMBA2, (16, 32)), (rs.MAMBA2, (64, 128)), (rs.GDN, (128, 128))])
+def test_token_less_flush_of_speculative_layer(form, shape):
+    """replay_flush on a speculative layer (a ring of L committed records):
+    after verify + commit steps with random acceptance, every row's h
+    committed records are folded into its checkpoint, which must equal the
+    committed state (the oracle, token by token).  At 64 x 128 with fp16
+    records and L = 16 the flush's LDS holds L (not L - 1) record slots."""
+    from linear_attention_decode_replay_amd.state import SpecDecodeLayer
+    dv, dk = shape
+    B, H, L, T = 3, 2, 16, 4
+    lowp = shape != (16, 32)
+    rdt, io = ("f16", "bf16") if lowp else ("f32", "f32")
+    lay = rs.layer(form, H, dv, dk, L, "f32", rdt, io, None, T)
+    d = SpecDecodeLayer(lay, B, B + 1, DEV)
+    d.pool.raw.fill_(0xFF)
+    for b in range(B):
+        d.assign(b, b + 1)
+    d.upload(rows=range(B))
+    ref = oracle.SpecTokenByToken(B, H, dv, dk, T, form=form)
+    h = np.zeros(B, np.int32)
+    for s in range(7):
+        tok = workloads.spec_tokens(91, s, B, H, T, dv, dk, io, 0.05, 1.0, form)
+        fl = rs.rs_spec_meta_step(L, T, h)
+        q, k, v, lam = (x.to(DEV) for x in (tok.q, tok.k, tok.v, tok.lam))
+        beta = tok.beta.to(DEV) if tok.beta is not None else None
+        out = torch.empty((B, T, H, dv), device=DEV)
+        d.verify(rs.make_spec_io(q, k, v, lam, out, beta))
+        tm = lambda t: t.double().numpy().transpose(0, 2, 1, 3)
+        ref.verify(tm(tok.q), tm(tok.k), tm(tok.v), tok.lam.double().numpy().transpose(0, 2, 1),
+                   None if tok.beta is None else tok.beta.double().numpy().transpose(0, 2, 1))
+        a = workloads.spec_accepted(91, s, B, T, "random")
+        d.commit(torch.from_numpy(a).to(DEV))
+        ref.commit(a)
+        rs.rs_spec_meta_advance(L, T, h, fl, a)
+    assert (h > 0).any()
+    # materialise: flag every row, cursor = committed count (the device's)
+    dh, _ = d.device_committed()
+    assert np.array_equal(dh, h)
+    n4 = d.flag[0].numel()
+    flags = torch.ones(n4, dtype=torch.uint8, device=DEV)
+    batch = rs.make_batch(d.pool.raw, d.pool.n_blocks, d.block_table, d.committed[d._cur], flags, d.err)
+    rs.replay_flush(lay, batch)
+    torch.cuda.synchronize()
+    blk = torch.arange(1, B + 1, device=DEV)
+    ck = d.pool.ckpt()[blk].double().cpu().numpy()
+    e = rel_err(ck, ref.state(), 2)
+    tol = TOL_LOW if lowp else TOL_F32
+    say(f"[errors] token-less flush of a speculative layer form={form} shape={shape}: ckpt={e:.3g} h={list(h)}")
+    assert e <= tol
+    assert int(d.err.item()) == 0

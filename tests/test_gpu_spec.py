@@ -149,3 +149,15 @@ def test_spec_gdn_T8_64x128():
     err = run_spec_case(SpecCase(form=rs.GDN, B=16, H=16, dv=64, dk=128, L=16, T=8, steps=12, rec_dt="f16",
                                  io_dt="bf16", sample=[0, 15], seed=40))
     _check_gdn(err, TOL_LOW)
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+@pytest.mark.parametrize("T", [4, 8])
+def test_spec_full_forgetting(form, T):
+    """lam = -inf (alpha = 0) on every 7th (step, row, draft, head), committed
+    records included: the masked draft weights and the committed decay sums
+    stay sums of log-decays, so a -inf draft zeroes what comes before it and
+    nothing becomes NaN; outputs and flushes against the oracle."""
+    err = run_spec_case(SpecCase(form=form, T=T, L=16, steps=24, accept="random", forget_every=7, seed=17 + T))
+    assert err["flushes"] >= 1
+    _check(err, TOL_F32)
