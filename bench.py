@@ -531,9 +531,10 @@ def suite_stack(out, n_layers=40, quick=False):
         torch.cuda.empty_cache()
     for (kind, L, state, read), ms in results.items():
         if kind == "replay":
+            c16 = results.get(("conventional", 16, "f16", None))
             line = {"suite": "stack40_ratio", "L": L, "state": state, "read_copy": read,
                     "speedup_vs_conventional_f32": round(results[("conventional", 16, "f32", None)] / ms, 3),
-                    "speedup_vs_conventional_f16": round(results[("conventional", 16, "f16", None)] / ms, 3)}
+                    "speedup_vs_conventional_f16": round(c16 / ms, 3) if c16 else None}
             print(json.dumps(line), file=out, flush=True)
 
 
@@ -904,6 +905,55 @@ def summarize_counters(args, fetch_csv, write_csv):
     return 0
 
 
+def summarize_trace(trace_csv, launch_log):
+    """Kernel durations from a rocprofv3 --kernel-trace csv, lined up with the
+    launch log of the same run (dispatches of each kernel in dispatch order
+    against its logged launches in launch order).  Prints one JSON line per
+    (kernel, label): launches, mean / min / max duration in us, and the
+    algorithmic bytes over the summed duration; for the one-line benchmark
+    (labels = cursors) also the window average over cursors."""
+    import csv
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Dispatch_Id"]), kernel_family(r["Kernel_Name"]),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    log = json.load(open(launch_log))
+    disp = {}
+    for _, fam, us in rows:
+        disp.setdefault(fam, []).append(us)
+    logged = {}
+    for fam, label, nb in log["launches"]:
+        logged.setdefault(fam, []).append((label, nb))
+    table = {}
+    for fam, launches in logged.items():
+        got = disp.get(fam, [])
+        if len(got) != len(launches):
+            raise SystemExit(f"{fam}: {len(got)} dispatches in the trace, {len(launches)} launches logged")
+        for (label, nb), us in zip(launches, got):
+            table.setdefault((fam, label), []).append((us, nb))
+    for (fam, label), v in table.items():
+        us = np.array([a for a, _ in v])
+        nb = np.array([b for _, b in v])
+        print(json.dumps({"kernel": fam, "label": label, "launches": len(v), "us_mean": round(float(us.mean()), 2),
+                          "us_min": round(float(us.min()), 2), "us_max": round(float(us.max()), 2),
+                          "tbs": round(float(nb.sum() / us.sum() / 1e6), 3)}))
+    L = log.get("L")
+    if L:
+        labels = [f"w{w}" for w in range(L - 1)] + ["flush"]
+        if all(("k_replay_step", lb) in table for lb in labels):
+            means = [float(np.mean([a for a, _ in table[("k_replay_step", lb)]])) for lb in labels]
+            nbs = [float(np.mean([b for _, b in table[("k_replay_step", lb)]])) for lb in labels]
+            win = float(np.mean(means))
+            print(json.dumps({"kernel": "k_replay_step", "label": "window average over cursors",
+                              "us": round(win, 2), "non_flush_us": round(float(np.mean(means[:-1])), 2),
+                              "flush_us": round(means[-1], 2), "bytes": round(float(np.mean(nbs))),
+                              "tbs": round(float(np.mean(nbs)) / win / 1e6, 3),
+                              "frac_of_8tbs": round(float(np.mean(nbs)) / win / 1e6 / 8.0, 4)}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -934,6 +984,9 @@ def main(argv=None):
                     help="with --suite-only spec: the layers to run (default both)")
     ap.add_argument("--stack-quick", action="store_true",
                     help="with --suite-only stack: only the fp32 conventional and the L = 16 fp32 replay stacks")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="kernel durations from a rocprofv3 --kernel-trace csv, per launch-log label (needs "
+                         "--launch-log of the same run); runs nothing on the GPU")
     ap.add_argument("--launch-log", metavar="PATH",
                     help="write every launch of the library's kernels (kernel, label, algorithmic bytes) in launch "
                          "order to PATH (for --summarize-counters); with --summarize-counters: read it")
@@ -943,6 +996,10 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.summarize_counters:
         return summarize_counters(args, *args.summarize_counters)
+    if args.summarize_trace:
+        if not args.launch_log:
+            raise SystemExit("--summarize-trace needs --launch-log PATH")
+        return summarize_trace(args.summarize_trace, args.launch_log)
     global _LAUNCH_LOG
     if args.launch_log:
         _LAUNCH_LOG = []
@@ -950,6 +1007,8 @@ def main(argv=None):
         if args.gpus != 1:
             print("the suite runs on one GPU", file=sys.stderr)
             return 2
+        if args.calibrate_copy:
+            calibrate_copy(args.calibrate_copy)
         with open(args.suite, "w") as out:
             if args.suite_only in (None, "gdn"):
                 suite_gdn_sweep(out)

@@ -158,3 +158,32 @@ def test_counter_lineup():
     assert got[("k_conventional_step", "conventional")] == [(14336.0, 1.0)]
     with pytest.raises(SystemExit):
         bench.line_up(rows, [("k_replay_step", "w0", 1.0)], scale)
+
+
+def test_trace_summary_per_cursor(tmp_path, capsys):
+    """--summarize-trace lines the kernel trace up with the launch log and
+    averages each cursor position first, then the window."""
+    import csv
+    import json
+    L = 2
+    log = {"L": L, "launches": [("k_replay_step", "w0", 100.0), ("k_conventional_step", "conventional", 50.0),
+                                ("k_replay_step", "flush", 300.0), ("k_replay_step", "w0", 100.0)]}
+    durations = {1: ("k_replay_step<0>", 10_000), 2: ("k_conventional_step<0>", 7_000),
+                 3: ("k_replay_step<1>", 30_000), 4: ("k_replay_step<0>", 20_000)}
+    path = tmp_path / "kt.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for did, (name, ns) in durations.items():
+            w.writerow({"Dispatch_Id": did, "Kernel_Name": f"void rs::{name}(rs::StepParams)",
+                        "Start_Timestamp": 1000 * did, "End_Timestamp": 1000 * did + ns})
+    lp = tmp_path / "log.json"
+    lp.write_text(json.dumps(log))
+    assert bench.main(["--summarize-trace", str(path), "--launch-log", str(lp)]) == 0
+    lines = [json.loads(x) for x in capsys.readouterr().out.splitlines()]
+    by = {(d["kernel"], d["label"]): d for d in lines}
+    assert by[("k_replay_step", "w0")]["us_mean"] == 15.0
+    assert by[("k_replay_step", "flush")]["us_mean"] == 30.0
+    assert by[("k_conventional_step", "conventional")]["us_mean"] == 7.0
+    win = by[("k_replay_step", "window average over cursors")]
+    assert win["us"] == 22.5 and win["bytes"] == 200
