@@ -110,3 +110,13 @@ def spec_replay_state_bytes_per_token(L: int, T: int, accepted: int, m_state: in
             tokens += accepted
         h = (0 if flush else h) + accepted
     return (reads + writes) * m_state / tokens
+
+
+def spec_replay_bytes_per_token(L: int, T: int, accepted: int, m_state: int, rec_layer: int,
+                                n_steps: int = 100000) -> float:
+    """spec_replay_state_bytes_per_token plus the record writes: every verify
+    step stores its T draft records (rec_layer bytes each for the whole
+    layer), accepted or not ("appends all T draft records behind the h
+    committed ones")."""
+    per_token = spec_replay_state_bytes_per_token(L, T, accepted, m_state, n_steps)
+    return per_token + T * rec_layer / accepted

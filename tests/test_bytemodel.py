@@ -81,12 +81,32 @@ def test_spec_state_bytes_closed_form():
     is 4 steps (h = 4, 8, 12, 16, the last flushing) committing 16 tokens:
     5 state transfers per 16 tokens; with one token committed per step a
     flush comes every 13 steps: 14 transfers per 13 tokens.  (The blog's
-    interactive widget prints 1.30 and 4.47 MiB for these cases; its
-    accounting is not stated in the text, so those two figures are not
-    reproduced here.)"""
+    interactive widget prints 1.30 and 4.47 MiB for these cases; see
+    test_spec_widget_figures.)"""
     m = bm.layer_state_bytes(128, 64, 128, 4)
     assert bm.spec_replay_state_bytes_per_token(16, 4, 4, m, 4000) == 5 * m / 16
     got = bm.spec_replay_state_bytes_per_token(16, 4, 1, m, 13 * 300)
     assert abs(got - 14 * m / 13) < 1e-9 * m
     # both far below the snapshot scheme (5 and 20 MiB) and plain decoding (8 MiB)
     assert 5 * m / 16 < bm.snapshot_verify_step_bytes(4, m) / 4 < bm.plain_decode_token_bytes(m)
+
+
+def test_spec_widget_figures():
+    """The blog's widget ("Speculative decoding: rollback becomes a pointer",
+    T = 4, Nemotron-3-Super layer) prints 1.30 MiB per committed token with
+    every draft accepted and 4.47 MiB with every draft rejected.  Counting
+    the state transfers of the stated rule plus the T draft records each
+    step writes (388 B per head, 128 heads) reproduces the first figure to
+    the digits printed (1.297).  The same count gives 4.497 for the second,
+    not 4.47: that figure is not reproduced, and no single counting of state
+    transfers, record writes and record reads gives both (a reading in which
+    a flush also folds the step's own accepted token gives 4.475, but then
+    1.247 for the first)."""
+    m = bm.layer_state_bytes(128, 64, 128, 4)
+    rec = 128 * bm.record_bytes(64, 128)
+    assert rec == 128 * 388
+    all_acc = bm.spec_replay_bytes_per_token(16, 4, 4, m, rec, 4000) / 2**20
+    assert round(all_acc, 2) == 1.30
+    rejected = bm.spec_replay_bytes_per_token(16, 4, 1, m, rec, 13 * 300) / 2**20
+    assert abs(rejected - (14 * 4 / 13 + 4 * rec / 2**20)) < 1e-9
+    assert round(rejected, 2) == 4.50   # the widget prints 4.47 (unpinned)
