@@ -2491,6 +2491,17 @@ constexpr int split_for() {
     return s < 1 ? 1 : s;
 }
 
+// The replay step's split for a single checkpoint: whole tiles up to 32 KiB
+// of state per workgroup.  Measured on MI355X, Gated DeltaNet 128 x 128 with
+// an fp16 state, batch 256: window average 64.6 -> 58.7 us per launch
+// unsplit (fp32 state, 64 KiB per tile, keeps split_for).  The read-modify-
+// write kernels keep split_for: the conventional step measured 5 % slower
+// unsplit (90.1 -> 95.2 us).
+template <int DV, int DK, class TS>
+constexpr int replay_split() {
+    return DV * DK * (int)sizeof(typename TS::S) <= 32768 ? 1 : split_for<DV, DK>();
+}
+
 // Whether Tile<DV, DK, TS, SPLIT> is a valid decomposition (the conditions
 // its static_asserts check, plus at least 8 owned rows so that an owned value
 // record is a whole number of 16-byte chunks).
@@ -2764,73 +2775,85 @@ struct Dispatch {
                                     using TI = decltype(ti);
                                     ok = true;
                                     if (p) {
-                                        // The replay step keeps the base split at any batch:
+                                        // Unsplit tiles of up to 32 KiB (replay_split) when the
+                                        // grid fills the chip, else split_for; never wider:
                                         // measured, a wider split at small batch repeats the
                                         // record work in more workgroups and is slower
                                         // (Gated DeltaNet batch 1: 9.1 -> 10.3 us).
-                                        constexpr int SP = split_for<DV, DK>();
-                                        const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
-                                        const dim3 block(Tile<DV, DK, TL, SP>::NT);
-                                        if constexpr (FORM == kGdn) {
-                                            if (p->reconstruct) {  // (the hint is cleared for it)
-                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, true>),
-                                                                   grid<SP>(), block, lds, stream, *p);
-                                                return;
-                                            }
-                                        }
-                                        const int hint = p->flush_hint;
-                                        // The persistent form (steps with no flushing row)
-                                        // for Mamba-2 with one fp32 checkpoint and a key per
-                                        // head, where it measured faster; with 16-bit tiles,
-                                        // read copies or Gated DeltaNet two workgroups per
-                                        // compute unit keep too little in flight, and with
-                                        // grouped keys (a key append in one tile of a group)
-                                        // there is less interleaved writing to take out: it
-                                        // measured slower there.
-                                        constexpr bool persist_form =
-                                            FORM == kMamba2 && !TWO && std::is_same<TS, tF32>::value;
-                                        if constexpr (persist_form) {
-                                            if (hint == RS_FLUSH_NONE && p->heads_per_group == 1) {
-                                                constexpr int NT = StepTile<DV, DK, TL, SP, kNonFlushRows>::NT;
-                                                const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
-                                                                              kNonFlushRows, true>;
-                                                // (it copies the records to LDS in one pass:
-                                                // 2 chunks per thread)
-                                                constexpr int rec_chunks = (DK + DV / SP) * (int)sizeof(R) / 16;
-                                                const PersistShape ps =
-                                                    slots * rec_chunks <= 2 * NT
-                                                        ? persist_shape(reinterpret_cast<const void*>(fn), NT, lds,
-                                                                        Deferred<DV / SP, DK, R>::BYTES,
-                                                                        (int64_t)p->n_rows * p->n_heads * SP)
-                                                        : PersistShape{};
-                                                if (ps.grid) {
-                                                    StepParams q = *p;
-                                                    q.meta_off = ps.meta_off;
-                                                    q.defer_off = ps.defer_off;
-                                                    q.defer_cap = ps.defer_cap;
-                                                    hipLaunchKernelGGL(fn, dim3(ps.grid), dim3(NT), ps.lds, stream, q);
+                                        constexpr int SPW = TWO ? split_for<DV, DK>() : replay_split<DV, DK, TS>();
+                                        constexpr int SPB = split_for<DV, DK>();
+                                        const bool whole = (int64_t)p->n_rows * p->n_heads >= kFillWorkgroups;
+                                        auto go = [&](auto sp_c) {
+                                            constexpr int SP = decltype(sp_c)::value;
+                                            const size_t lds = lds_need<DV / SP, DK, R>(slots, L.L);
+                                            const dim3 block(Tile<DV, DK, TL, SP>::NT);
+                                            if constexpr (FORM == kGdn) {
+                                                if (p->reconstruct) {  // (the hint is cleared for it)
+                                                    hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, true>),
+                                                                       grid<SP>(), block, lds, stream, *p);
                                                     return;
                                                 }
                                             }
-                                        }
-                                        if constexpr (!TWO) {
-                                            // one launch over every row; the hint is not used
-                                            // (a pair of launches on mixed steps and the kernel
-                                            // without the fold measured slower here)
-                                            StepParams q = *p;
-                                            q.flush_hint = RS_FLUSH_UNKNOWN;
-                                            hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
-                                                               block, lds, stream, q);
+                                            const int hint = p->flush_hint;
+                                            // The persistent form (steps with no flushing row)
+                                            // for Mamba-2 with one fp32 checkpoint and a key per
+                                            // head, where it measured faster; with 16-bit tiles,
+                                            // read copies or Gated DeltaNet two workgroups per
+                                            // compute unit keep too little in flight, and with
+                                            // grouped keys (a key append in one tile of a group)
+                                            // there is less interleaved writing to take out: it
+                                            // measured slower there.
+                                            constexpr bool persist_form =
+                                                FORM == kMamba2 && !TWO && std::is_same<TS, tF32>::value;
+                                            if constexpr (persist_form) {
+                                                if (hint == RS_FLUSH_NONE && p->heads_per_group == 1) {
+                                                    constexpr int NT = StepTile<DV, DK, TL, SP, kNonFlushRows>::NT;
+                                                    const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
+                                                                                  kNonFlushRows, true>;
+                                                    // (it copies the records to LDS in one pass:
+                                                    // 2 chunks per thread)
+                                                    constexpr int rec_chunks = (DK + DV / SP) * (int)sizeof(R) / 16;
+                                                    const PersistShape ps =
+                                                        slots * rec_chunks <= 2 * NT
+                                                            ? persist_shape(reinterpret_cast<const void*>(fn), NT, lds,
+                                                                            Deferred<DV / SP, DK, R>::BYTES,
+                                                                            (int64_t)p->n_rows * p->n_heads * SP)
+                                                            : PersistShape{};
+                                                    if (ps.grid) {
+                                                        StepParams q = *p;
+                                                        q.meta_off = ps.meta_off;
+                                                        q.defer_off = ps.defer_off;
+                                                        q.defer_cap = ps.defer_cap;
+                                                        hipLaunchKernelGGL(fn, dim3(ps.grid), dim3(NT), ps.lds, stream, q);
+                                                        return;
+                                                    }
+                                                }
+                                            }
+                                            if constexpr (!TWO) {
+                                                // one launch over every row; the hint is not used
+                                                // (a pair of launches on mixed steps and the kernel
+                                                // without the fold measured slower here)
+                                                StepParams q = *p;
+                                                q.flush_hint = RS_FLUSH_UNKNOWN;
+                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>), grid<SP>(),
+                                                                   block, lds, stream, q);
+                                            } else {
+                                                if (hint == RS_FLUSH_NONE || hint == RS_FLUSH_MIXED)
+                                                    hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
+                                                                                      kNonFlushRows>),
+                                                                       grid<SP>(),
+                                                                       dim3(StepTile<DV, DK, TL, SP, kNonFlushRows>::NT),
+                                                                       lds, stream, *p);
+                                                if (hint != RS_FLUSH_NONE)
+                                                    hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>),
+                                                                       grid<SP>(), block, lds, stream, *p);
+                                            }
+                                        };
+                                        if constexpr (SPW != SPB) {
+                                            if (whole) go(std::integral_constant<int, SPW>{});
+                                            else go(std::integral_constant<int, SPB>{});
                                         } else {
-                                            if (hint == RS_FLUSH_NONE || hint == RS_FLUSH_MIXED)
-                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
-                                                                                  kNonFlushRows>),
-                                                                   grid<SP>(),
-                                                                   dim3(StepTile<DV, DK, TL, SP, kNonFlushRows>::NT),
-                                                                   lds, stream, *p);
-                                            if (hint != RS_FLUSH_NONE)
-                                                hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL>),
-                                                                   grid<SP>(), block, lds, stream, *p);
+                                            go(std::integral_constant<int, SPB>{});
                                         }
                                     }
                                 });
