@@ -671,13 +671,17 @@ def suite_continuous(out, steps=200, n_layers=4):
     """Continuous batching at the Nemotron-3-Super layer shape: 256 request
     slots over a shuffled pool of 384 blocks, rows starting mid-window (cursor
     U{0..15}), each live row retiring with p = 1/32 per step and each empty
-    slot taking a new row with p = 1/2 (a joining row's checkpoint is zeroed
-    by replay_state_reset, inside the timed region).  n_layers independent
-    layer pools share the schedule, as the layers of one model do, so that no
-    launch finds its state in the caches.  Reports the per-launch time
-    distribution (events around each launch) and the average over the whole
-    run (one event pair), for the checkpoint + buffer step and for the
-    conventional step on the same schedule."""
+    slot taking a new request with p = 1/2.  n_layers layers of one model
+    share the slots (one block table, one set of cursors and flags: one
+    metadata upload per step when rows retire or join) and each has its own
+    pool, so that no launch finds its state in the caches.  A joining row of
+    the checkpoint + buffer layers starts with a zero checkpoint that is not
+    read until its first flush (RS_CURSOR_ZERO_CKPT: no launch); the
+    conventional layers zero a joining row's state with replay_state_reset
+    (its launches are in the timed region).  Each kind runs the schedule
+    twice on fresh pools: once timed as a whole (one event pair around the
+    run), once with events around every launch (the per-launch
+    distribution)."""
     import torch
     import linear_attention_decode_replay_amd as rs
     import workloads
@@ -692,70 +696,81 @@ def suite_continuous(out, steps=200, n_layers=4):
     rec = (dv + dk) * _ES[cfg["rec"]] + 4
     io_b = (2 * dk + dv) * _ES[cfg["io"]] + 4 + 4 * dv
     for kind in ("replay", "conventional"):
-        layers = []
-        for _ in range(n_layers):
-            d = DecodeLayer(lay, B, NB, dev)
+        res = {}
+        for per_launch_events in (False, True):
+            d = DecodeLayer(lay, B, NB, dev, n_layers=n_layers)
             for slot in range(B):
                 d.assign(slot, int(blocks0[slot]))
             d.reset_rows(range(B))
             for slot in range(B):  # mid-window starts (the records' values do not matter for timing)
                 d.assign(slot, int(blocks0[slot]), int(w0s[slot]))
-            layers.append(d)
-        torch.cuda.synchronize()
-        per_launch, flush_frac, live_rows, nbytes = [], [], [], 0.0
-        ev = []
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for s in range(steps):
-            e = events[s]
-            for d in layers:
+            torch.cuda.synchronize()
+            flush_frac, live_rows, nbytes, ev, uploads0 = [], [], 0.0, [], d.uploads
+            e0 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record()
+            for s in range(steps):
+                e = events[s]
                 for slot in e.retire:
                     d.retire(slot)
                 for slot, b in e.join:
                     d.assign(slot, int(b))
-                if e.join:
-                    d.reset_rows([slot for slot, _ in e.join])
-            for li, d in enumerate(layers):
-                pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                io = ios[(s + li) % 16]
+                joined = [slot for slot, _ in e.join]
+                if joined:
+                    if kind == "replay":
+                        d.join_rows(joined)
+                    else:
+                        d.reset_rows(joined)
+                pairs = None
+                if per_launch_events:
+                    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                             for _ in range(n_layers)]
+                    ev.extend(pairs)
+                step_ios = [ios[(s + li) % 16] for li in range(n_layers)]
+                live = d.live()
                 if kind == "replay":
-                    wp, fl = d.step(io, events=pair)
-                    live = d.live()
-                    if li == 0:
-                        flush_frac.append(float(np.mean(fl[live])) if live.any() else 0.0)
-                        live_rows.append(int(live.sum()))
+                    zc = d.zero_ckpt & live
+                    wp, fl = d.step(step_ios, events=pairs)
+                    flush_frac.append(float(np.mean(fl[live])) if live.any() else 0.0)
+                    live_rows.append(int(live.sum()))
                     f = fl[live].astype(bool)
                     w = wp[live]
-                    nbytes += float(np.sum(H * (ms_state + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
-                    nbytes += 4.0 * int((~live).sum())
+                    # a zero checkpoint is not read (its flush still writes it)
+                    ck_read = np.where(zc[live], 0, ms_state)
+                    nbytes += n_layers * float(np.sum(H * (ck_read + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
+                    nbytes += n_layers * 4.0 * int((~live).sum())
                 else:
-                    d.conventional_step(io, events=pair)
-                    live = d.live()
-                    nbytes += float(live.sum()) * (H * (2 * ms_state + io_b) + 4) + 4.0 * int((~live).sum())
-                ev.append(pair)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e1.record()
-        torch.cuda.synchronize()
-        per_launch = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-        total_us = e0.elapsed_time(e1) * 1e3
-        errs = sum(int(d.err.item()) for d in layers)
-        if errs:
-            raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
-        n = steps * n_layers
+                    d.conventional_step(step_ios, events=pairs)
+                    nbytes += n_layers * (float(live.sum()) * (H * (2 * ms_state + io_b) + 4) + 4.0 * int((~live).sum()))
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            total_us = e0.elapsed_time(e1) * 1e3
+            errs = int(d.err.item())
+            if errs:
+                raise RuntimeError(f"{errs} tiles skipped by the kernel's bounds checks")
+            n = steps * n_layers
+            if per_launch_events:
+                per_launch = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+                res.update({"us_per_launch_mean": round(float(per_launch.mean()), 2),
+                            "us_per_launch_p50": round(float(np.percentile(per_launch, 50)), 2),
+                            "us_per_launch_p90": round(float(np.percentile(per_launch, 90)), 2),
+                            "us_per_launch_max": round(float(per_launch.max()), 2)})
+            else:
+                res.update({"us_per_launch_region": round(total_us / n, 2),
+                            "wall_us_per_launch": round(1e6 * wall / n, 2),
+                            "gb_per_launch": round(nbytes / n / 1e9, 4),
+                            "tbs_region": round(nbytes / (total_us * 1e-6) / 1e12, 3),
+                            "metadata_uploads": d.uploads - uploads0})
+                if kind == "replay":
+                    res["flushing_rows_mean"] = round(float(np.mean(flush_frac)), 4)
+                    res["live_rows_mean"] = round(float(np.mean(live_rows)), 1)
+            del d
+            torch.cuda.empty_cache()
         line = {"suite": "continuous_batching", "kind": kind, "slots": B, "pool_blocks": NB, "steps": steps,
-                "layers": n_layers, "us_per_launch_region": round(total_us / n, 2),
-                "us_per_launch_mean": round(float(per_launch.mean()), 2),
-                "us_per_launch_p50": round(float(np.percentile(per_launch, 50)), 2),
-                "us_per_launch_p90": round(float(np.percentile(per_launch, 90)), 2),
-                "us_per_launch_max": round(float(per_launch.max()), 2),
-                "gb_per_launch": round(nbytes / n / 1e9, 4),
-                "tbs_region": round(nbytes / (total_us * 1e-6) / 1e12, 3)}
-        if kind == "replay":
-            line["flushing_rows_mean"] = round(float(np.mean(flush_frac)), 4)
-            line["live_rows_mean"] = round(float(np.mean(live_rows)), 1)
+                "layers": n_layers, **res}
         print(json.dumps(line), file=out, flush=True)
-        del layers
-        torch.cuda.empty_cache()
 
 
 def calibrate_copy(mib: int) -> None:

@@ -224,7 +224,17 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               which is neither read nor written (its outputs are left as
  *               they were).
  *   write_pos   records held by the row, 0..L-1 (the write cursor of the
- *               vLLM pull request, "CUDA graphs and continuous batching").
+ *               vLLM pull request, "CUDA graphs and continuous batching"),
+ *               optionally with RS_CURSOR_ZERO_CKPT set: the row's checkpoint
+ *               is zero and is not read (a request that joined the batch and
+ *               has not flushed yet; its block's checkpoint region may hold
+ *               anything).  replay_decode_step and replay_flush treat the
+ *               checkpoint as zero for such a row; its first flush writes the
+ *               checkpoint, and next_write_pos carries the bit until then.
+ *               This replaces replay_state_reset for a joining row (one launch
+ *               fewer, and no checkpoint read until the row's first flush).
+ *               Not for speculative layers (their counts must be 0..L) or
+ *               conventional_decode_step (which reads no cursor).
  *   flush       nonzero: this step folds the row into its checkpoint.  A row
  *               at write_pos == L-1 flushes whatever its flag says.  May be
  *               NULL (no forced flushes).
@@ -233,7 +243,8 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *   next_write_pos  optional (may be NULL), replay_decode_step only: receives
  *               each non-padding row's cursor for the next step, 0 after a
  *               flush and write_pos + 1 otherwise (the host rule of
- *               rs_meta_advance).  Passing it as the next step's write_pos
+ *               rs_meta_advance), with RS_CURSOR_ZERO_CKPT kept on a row
+ *               that did not flush.  Passing it as the next step's write_pos
  *               lets a caller skip the per-step host -> device copy while
  *               the batch is unchanged.  Must not alias write_pos.
  *   flush_hint  replay_decode_step only: what the caller knows of this
@@ -253,6 +264,9 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *               Where a hint is used, a row that breaks its promise is
  *               skipped and counted in err_count (never computed wrongly).
  */
+/* write_pos flag: the row's checkpoint is zero and is not read (above). */
+#define RS_CURSOR_ZERO_CKPT (1 << 30)
+
 typedef enum {
     RS_FLUSH_UNKNOWN = 0,
     RS_FLUSH_NONE = 1,

@@ -30,6 +30,8 @@ RS_OK, RS_EINVAL, RS_EUNSUPPORTED, RS_EHIP = 0, -1, -2, -3
 RS_ROUND_NEAREST, RS_ROUND_STOCHASTIC = 0, 1
 RS_GDN_OUTPUT_ONLY, RS_GDN_RECONSTRUCT = 0, 1
 RS_FLUSH_UNKNOWN, RS_FLUSH_NONE, RS_FLUSH_ALL, RS_FLUSH_MIXED = 0, 1, 2, 3
+# write_pos flag: the row's checkpoint is zero and is not read (replayssm.h)
+RS_CURSOR_ZERO_CKPT = 1 << 30
 
 _c = ctypes
 _vp = _c.c_void_p

@@ -532,6 +532,13 @@ __device__ __forceinline__ bool row_flag(const uint8_t* flags, int row) {
     return ((word >> (8 * (row & 3))) & 0xffu) != 0;
 }
 
+// A row's cursor word: the number of buffered records, and whether its
+// checkpoint is zero and not to be read (RS_CURSOR_ZERO_CKPT: a row that
+// joined and has not flushed yet).  A negative word stays negative, so the
+// range checks still see it.
+__device__ __forceinline__ int cursor_of(int word) { return word >= 0 ? (word & ~RS_CURSOR_ZERO_CKPT) : word; }
+__device__ __forceinline__ bool zero_ckpt_of(int word) { return word >= 0 && (word & RS_CURSOR_ZERO_CKPT) != 0; }
+
 // Counted once per (row, head) tile, by the workgroup owning its first rows.
 __device__ __forceinline__ void count_error(const StepParams& p, const TileIds& id) {
     if (threadIdx.x == 0 && id.part == 0 && p.err) atomicAdd(p.err, 1);
@@ -868,6 +875,7 @@ struct TileIn {
     TileIds id;
     int blk, w;
     bool run, fl;  // the tile is computed here; it flushes
+    bool zc;       // the row's checkpoint is zero (RS_CURSOR_ZERO_CKPT): not read
     RawIo<TI, EPC> qr[HPC], kr[HPC];
     typename TI::S vr;
     float lam, lam_j;
@@ -924,7 +932,7 @@ __device__ __forceinline__ bool tile_runs(const StepParams& p, const TileIds& id
 // with no records yet reading slot 0 and ignoring it, so that a loop that
 // issues ahead has none either.
 template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS, bool UNCOND = false>
-__device__ __forceinline__ void tile_issue_small(const StepParams& p, const TileIds id, int blk, int w, bool fl,
+__device__ __forceinline__ void tile_issue_small(const StepParams& p, const TileIds id, int blk, int w, bool fl, bool zc,
                                                  TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in) {
     using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
     using T = typename In::T;
@@ -938,6 +946,7 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
     in.w = w;
     in.run = true;
     in.fl = fl;
+    in.zc = zc;
     const int tid = threadIdx.x;
     const int cc = tid % LPR;  // column chunk
     const int rg = tid / LPR;  // row within a pass
@@ -968,9 +977,13 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
 }
 
 // The checkpoint stream of a tile whose small loads tile_issue_small issued.
+// always: issue the loads even for a zero checkpoint (its values are then
+// replaced by zeros in tile_finish), so that a loop issuing ahead has no
+// branch around them; otherwise a zero checkpoint is not read.
 template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS>
 __device__ __forceinline__ void tile_issue_stream(const StepParams& p,
-                                                  TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in) {
+                                                  TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in,
+                                                  bool always = false) {
     using In = TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>;
     using T = typename In::T;
     using S = typename TS::S;
@@ -983,6 +996,7 @@ __device__ __forceinline__ void tile_issue_stream(const StepParams& p,
     const int rg = tid / LPR;
     const int col0 = EPC * cc;
     const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, in.id, in.blk);
+    if (in.zc && !always) return;
     if (!TWO || fl) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -1027,7 +1041,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
         if (threadIdx.x == 0) {
             df.meta[0] = (int)id.tile * SPLIT + id.part;
             df.meta[1] = blk;
-            df.meta[2] = w;
+            df.meta[2] = w | (in.zc ? RS_CURSOR_ZERO_CKPT : 0);
         }
     }
 
@@ -1085,6 +1099,12 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     for (int r = 0; r < NR; ++r) rsc[r] = in.rsc[r];
 #pragma unroll
     for (int i = 0; i < NR * HPC; ++i) cb[i] = in.cb[i];
+    if (in.zc) {  // a zero checkpoint: zero bits are +0 in every state and read format
+#pragma unroll
+        for (int r = 0; r < NR; ++r) rsc[r] = 1.0f;
+#pragma unroll
+        for (int i = 0; i < NR * HPC; ++i) cb[i] = u32x4{0u, 0u, 0u, 0u};
+    }
 
     if (tid < DVW) s.v[tid] = vi;
     rec.template commit<!DEFER>(rk, rx, s.k, s.x);
@@ -1234,7 +1254,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
 
     if constexpr (!DEFER)  // (deferred: stored with the item's other writes)
         if (p.next_wp && id.head == 0 && id.part == 0 && tid == 0)
-            st_nt<kNtSmall<FORM>>(p.next_wp + id.row, fl ? 0 : w + 1);
+            st_nt<kNtSmall<FORM>>(p.next_wp + id.row, fl ? 0 : (w + 1) | (in.zc ? RS_CURSOR_ZERO_CKPT : 0));
     const float alpha = expf(lam);  // Gated DeltaNet only
     float* o = DEFER ? df.out : p.out + id.tile * DV + row0;
     {
@@ -1325,12 +1345,13 @@ __device__ __forceinline__ void replay_tile(const StepParams& p, const TileIds i
     const uint8_t* fsrc = p.flush ? p.flush : reinterpret_cast<const uint8_t*>(p.write_pos);
     const bool flag = row_flag(fsrc, id.row) && p.flush;
     const int blk = p.block_table[id.row];
-    const int w = p.write_pos[id.row];
+    const int word = p.write_pos[id.row];
+    const int w = cursor_of(word);
     bool fl;
     TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS> in;
     in.run = tile_runs<ROWS>(p, id, blk, w, flag, fl);
     if (in.run) {
-        tile_issue_small(p, id, blk, w, fl, in);
+        tile_issue_small(p, id, blk, w, fl, zero_ckpt_of(word), in);
         tile_issue_stream(p, in);
     }
     tile_finish<FORM, DV, DK, TS, TR, TI, SPLIT, TL, RECON, ROWS, DEFER>(p, in, smem, dslot);
@@ -1346,8 +1367,9 @@ __device__ __forceinline__ void drain_deferred(const StepParams& p, char* dbase,
         const int e = c / CPE, j = c - e * CPE;
         char* ent = dbase + e * D::BYTES;
         const D df(ent);
-        const int w = df.meta[2];
-        if (w < 0) continue;
+        const int word = df.meta[2];
+        if (word < 0) continue;
+        const int w = cursor_of(word);
         const int tile = df.meta[0] / SPLIT, part = df.meta[0] - tile * SPLIT, blk = df.meta[1];
         const int row = tile / p.n_heads, head = tile - row * p.n_heads;
         char* base = p.pool + (int64_t)blk * p.block_bytes;
@@ -1365,7 +1387,8 @@ __device__ __forceinline__ void drain_deferred(const StepParams& p, char* dbase,
             st_stream(reinterpret_cast<u32x4*>(rx) + (j - OCH - KCH), reinterpret_cast<const u32x4*>(df.x)[j - OCH - KCH]);
         } else if (part == 0) {
             st_nt(reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)head * p.slots + w, *df.lam);
-            if (head == 0 && p.next_wp) st_nt(p.next_wp + row, w + 1);  // (non-flush rows only)
+            if (head == 0 && p.next_wp)  // (non-flush rows only)
+                st_nt(p.next_wp + row, (w + 1) | (word & RS_CURSOR_ZERO_CKPT));
         }
     }
 }
@@ -1426,10 +1449,10 @@ void k_replay_step(const StepParams p) {
             if (i < mine) {
                 const TileIds id = ids(t);
                 blk = p.block_table[id.row];
-                w = p.write_pos[id.row];
+                w = p.write_pos[id.row];  // the cursor word (RS_CURSOR_ZERO_CKPT kept)
                 const bool flag = p.flush && row_flag(p.flush, id.row);
                 bool fl;
-                run = tile_runs<ROWS, true>(p, id, blk, w, flag, fl, err_lds);
+                run = tile_runs<ROWS, true>(p, id, blk, cursor_of(w), flag, fl, err_lds);
             }
             const uint64_t ball = __ballot(run);
             const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1453,7 +1476,8 @@ void k_replay_step(const StepParams p) {
             const int t = __builtin_amdgcn_readfirstlane(list[3 * j]);
             const int blk = __builtin_amdgcn_readfirstlane(list[3 * j + 1]);
             const int w = __builtin_amdgcn_readfirstlane(list[3 * j + 2]);
-            tile_issue_small<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS, true>(p, ids(t), blk, w, false, in);
+            tile_issue_small<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS, true>(p, ids(t), blk, cursor_of(w), false,
+                                                                           zero_ckpt_of(w), in);
         };
         char* dbase = smem + p.defer_off;
         int n = 0;
@@ -1487,23 +1511,23 @@ void k_replay_step(const StepParams p) {
         if (cnt > 0) {
             In a, b;
             issue(0, a);
-            tile_issue_stream(p, a);
+            tile_issue_stream(p, a, true);
             issue(min(1, cnt - 1), b);
             int j = 0;
             for (; j + 3 < cnt; j += 2) {
-                tile_issue_stream(p, b);
+                tile_issue_stream(p, b, true);
                 finish(a, 0);
                 issue(j + 2, a);
-                tile_issue_stream(p, a);
+                tile_issue_stream(p, a, true);
                 finish(b, 1);
                 issue(j + 3, b);
             }
             // items j .. cnt - 1: a (small and stream issued), b (small issued)
-            if (j + 1 < cnt) tile_issue_stream(p, b);
+            if (j + 1 < cnt) tile_issue_stream(p, b, true);
             finish(a, 0);
             if (j + 2 < cnt) {
                 issue(j + 2, a);
-                tile_issue_stream(p, a);
+                tile_issue_stream(p, a, true);
             }
             if (j + 1 < cnt) finish(b, 1);
             if (j + 2 < cnt) finish(a, 0);
@@ -1646,13 +1670,15 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     const TileIds id = tile_ids<SPLIT>(p);
     const bool flag = row_flag(p.flush, id.row);
     const int blk = p.block_table[id.row];
-    const int w = p.write_pos[id.row];
+    const int word = p.write_pos[id.row];
+    const int w = cursor_of(word);
+    const bool zc = zero_ckpt_of(word);  // the checkpoint is zero: not read, written as the fold
     if (blk < 0 || !flag) return;
     if (blk >= p.n_blocks || w < 0 || w > p.slots) {
         count_error(p, id);
         return;
     }
-    if (w == 0) return;  // nothing buffered: the checkpoint is the state
+    if (w == 0 && !zc) return;  // nothing buffered: the checkpoint is the state
 
     const int tid = threadIdx.x;
     const int cc = tid % LPR;
@@ -1671,14 +1697,19 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
 
     const int col0 = EPC * cc;
     auto col = [col0](int h) { return col0 + EPC * LPR * h; };
-    const float lam_j = rl[min(tid, w - 1)];
+    const float lam_j = w > 0 ? rl[min(tid, w - 1)] : 0.f;
     RecordCopy<DV, DVW, DK, R, NT, 2> rec;
     rec.issue(rk, rx, w);
     u32x4 cb[NR * HPC];
+    if (!zc) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int h = 0; h < HPC; ++h) cb[r * HPC + h] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + col(h));
+            for (int h = 0; h < HPC; ++h) cb[r * HPC + h] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + col(h));
+    } else {
+#pragma unroll
+        for (int i = 0; i < NR * HPC; ++i) cb[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     rec.commit(rk, rx, s.k, s.x);
     decay_weights(lam_j, s.e, s.sc, w, 0.0f);
     __syncthreads();

@@ -26,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (RS_FLUSH_ALL, RS_FLUSH_MIXED, RS_FLUSH_NONE, RS_FLUSH_UNKNOWN, Pool, RsLayer,
+from . import (RS_CURSOR_ZERO_CKPT, RS_FLUSH_ALL, RS_FLUSH_MIXED, RS_FLUSH_NONE, RS_FLUSH_UNKNOWN, Pool, RsLayer,
                conventional_decode_step, make_batch, replay_decode_step, replay_flush, replay_spec_commit,
                replay_spec_verify, replay_state_reset, rs_meta_advance, rs_meta_step)
 
@@ -59,24 +59,36 @@ class _Stage:
 
 
 class DecodeLayer:
+    """n_layers > 1: that many layers of the same shape (one pool each) over
+    the same request slots, as the layers of a model are: they share the
+    block table, the cursors and the flags (one metadata buffer, one upload
+    per step), and step() takes one rs_step_io per layer and launches them in
+    order; each launch writes the same next cursors."""
+
     def __init__(self, lay: RsLayer, n_slots: int, n_blocks: int | None = None, device="cuda",
-                 staging: int = 4, sr_key=(0, 0)):
+                 staging: int = 4, sr_key=(0, 0), n_layers: int = 1):
         self.layer = lay
         self.L = int(lay.L)
         self.n_slots = n = int(n_slots)
-        self.pool = Pool(lay, n_blocks or n_slots, device)
+        self.pools = [Pool(lay, n_blocks or n_slots, device) for _ in range(int(n_layers))]
+        self.pool = self.pools[0]
         self.device = self.pool.raw.device
         self.anchor = np.full(n, -1, np.int32)   # -1: empty slot (padding row)
         self.blocks = np.full(n, -1, np.int32)
+        # rows whose checkpoint is zero and not read until their first flush
+        # (joined with join_rows; RS_CURSOR_ZERO_CKPT in the cursor word)
+        self.zero_ckpt = np.zeros(n, bool)
         _, size = _layout(n)
         self.meta = torch.zeros(size, dtype=torch.uint8, device=self.device)
         self.block_table, self.flush, self.mask, c0, c1 = _views(self.meta, n)
         self.cursor = (c0, c1)
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
-        # batch[i] reads cursor i and writes the next cursors into cursor 1-i
-        self.batch = [make_batch(self.pool.raw, self.pool.n_blocks, self.block_table, self.cursor[i],
-                                 self.flush, self.err, next_write_pos=self.cursor[1 - i], sr_key=sr_key)
-                      for i in (0, 1)]
+        # batches[layer][i] reads cursor i and writes the next cursors into
+        # cursor 1-i (each layer its own stochastic-rounding key)
+        self.batches = [[make_batch(pl.raw, pl.n_blocks, self.block_table, self.cursor[i], self.flush, self.err,
+                                    next_write_pos=self.cursor[1 - i], sr_key=(sr_key[0] + li, sr_key[1]))
+                         for i in (0, 1)] for li, pl in enumerate(self.pools)]
+        self.batch = self.batches[0]
         # stochastic rounding: the counter's first word, one value per launch
         self.sr_step = 0
         # tell the library which rows flush (it then runs the kernel built
@@ -96,20 +108,31 @@ class DecodeLayer:
             raise ValueError(f"block {block} outside the pool of {self.pool.n_blocks}")
         self.blocks[slot] = block
         self.anchor[slot] = steps_since_anchor
+        self.zero_ckpt[slot] = False
         self._dirty = True
 
     def retire(self, slot: int) -> None:
         self.blocks[slot] = -1
         self.anchor[slot] = -1
+        self.zero_ckpt[slot] = False
         self._dirty = True
 
     def live(self) -> np.ndarray:
         return self.blocks >= 0
 
-    def device_cursor(self) -> np.ndarray:
-        """The device's cursors for the next step (synchronises; for tests)."""
+    def device_cursor(self, words: bool = False) -> np.ndarray:
+        """The device's cursors for the next step (synchronises; for tests):
+        the record counts, or with words=True the cursor words
+        (RS_CURSOR_ZERO_CKPT included)."""
         torch.cuda.synchronize(self.device)
-        return self.cursor[self._cur].cpu().numpy()
+        c = self.cursor[self._cur].cpu().numpy()
+        return c if words else np.where(c >= 0, c & ~RS_CURSOR_ZERO_CKPT, c)
+
+    def _words(self, wp) -> np.ndarray:
+        """Cursor words of the rows: the record count, with
+        RS_CURSOR_ZERO_CKPT on live rows whose checkpoint is still zero."""
+        return np.where(self.zero_ckpt & self.live(), np.asarray(wp, np.int32) | RS_CURSOR_ZERO_CKPT,
+                        np.asarray(wp, np.int32)).astype(np.int32)
 
     # ------------------------------------------------------------- transfers --
     def _upload(self, stream, wp, flags=None, mask=None) -> None:
@@ -122,7 +145,7 @@ class DecodeLayer:
         st.bt[:] = self.blocks
         st.fl[:] = 0 if flags is None else flags
         st.mk[:] = 0 if mask is None else mask
-        st.c[self._cur][:] = wp
+        st.c[self._cur][:] = self._words(wp)
         off, _ = _layout(self.n_slots)
         with torch.cuda.stream(stream):
             if self._cur == 0:
@@ -136,10 +159,10 @@ class DecodeLayer:
             st.event.record(stream)
         self.uploads += 1
 
-    def _batch(self, hint=RS_FLUSH_UNKNOWN):
+    def _batch(self, hint=RS_FLUSH_UNKNOWN, layer: int = 0):
         """The batch struct for the next launch, stamped with a fresh
         stochastic-rounding counter word and the flush hint."""
-        b = self.batch[self._cur]
+        b = self.batches[layer][self._cur]
         b.sr_step = self.sr_step
         b.flush_hint = hint
         self.sr_step += 1
@@ -155,11 +178,20 @@ class DecodeLayer:
         return RS_FLUSH_ALL if n == int(live.sum()) else RS_FLUSH_MIXED
 
     # ----------------------------------------------------------------- steps --
+    def _per_layer(self, io, events):
+        if len(self.pools) == 1:
+            return [io], [events]
+        if len(io) != len(self.pools):
+            raise ValueError(f"{len(self.pools)} layers: one rs_step_io per layer")
+        return list(io), list(events) if events else [None] * len(io)
+
     def step(self, io, force: np.ndarray | None = None, stream=None, events=None):
         """One checkpoint + buffer decode step.  Returns the host (write_pos,
         flush) arrays that were used.  `events` = (start, end) torch events
-        recorded on the stream right around the kernel launch."""
+        recorded on the stream right around the kernel launch (with several
+        layers: io and events are lists, one entry per layer)."""
         stream = stream or torch.cuda.current_stream(self.device)
+        ios, evs = self._per_layer(io, events)
         wp, fl = rs_meta_step(self.L, self.anchor, force)
         forced = None
         if force is not None:
@@ -170,13 +202,16 @@ class DecodeLayer:
             self._upload(stream, wp, forced)
             self._forced_last = forced is not None
             self._dirty = False
-        if events:
-            events[0].record(stream)
-        replay_decode_step(self.layer, self._batch(self._hint(fl)), io, stream)
-        if events:
-            events[1].record(stream)
+        hint = self._hint(fl)
+        for li, (io_l, ev) in enumerate(zip(ios, evs)):
+            if ev:
+                ev[0].record(stream)
+            replay_decode_step(self.layer, self._batch(hint, li), io_l, stream)
+            if ev:
+                ev[1].record(stream)
         self._cur ^= 1
         rs_meta_advance(self.L, self.anchor, fl)
+        self.zero_ckpt &= ~(np.asarray(fl, bool) & self.live())  # a flush wrote the checkpoint
         return wp, fl
 
     def capture_steps(self, ios, stream=None):
@@ -193,6 +228,8 @@ class DecodeLayer:
             raise ValueError("capture an even number of steps")
         if self.layer.state_rounding:
             raise ValueError("stochastic rounding draws a fresh counter per launch: no graph capture")
+        if len(self.pools) != 1:
+            raise ValueError("graph capture of one layer at a time")
         if self._dirty or self._forced_last:
             raise ValueError("metadata upload pending: run an eager step first")
         stream = stream or torch.cuda.Stream(self.device)
@@ -217,15 +254,17 @@ class DecodeLayer:
 
     def conventional_step(self, io, stream=None, events=None) -> None:
         stream = stream or torch.cuda.current_stream(self.device)
+        ios, evs = self._per_layer(io, events)
         if self._dirty:
             wp, _ = rs_meta_step(self.L, self.anchor)
             self._upload(stream, wp)
             self._dirty = False
-        if events:
-            events[0].record(stream)
-        conventional_decode_step(self.layer, self._batch(), io, stream)
-        if events:
-            events[1].record(stream)
+        for li, (io_l, ev) in enumerate(zip(ios, evs)):
+            if ev:
+                ev[0].record(stream)
+            conventional_decode_step(self.layer, self._batch(layer=li), io_l, stream)
+            if ev:
+                ev[1].record(stream)
 
     def flush_rows(self, rows, stream=None) -> None:
         """Token-less flush of the given slots (materialise their state, e.g.
@@ -236,8 +275,23 @@ class DecodeLayer:
         sel &= self.live()
         wp, _ = rs_meta_step(self.L, self.anchor)
         self._upload(stream, wp, sel.astype(np.uint8))
-        replay_flush(self.layer, self._batch(), stream)
+        for li in range(len(self.pools)):
+            replay_flush(self.layer, self._batch(layer=li), stream)
         self.anchor[sel] = 0
+        self.zero_ckpt[sel] = False
+        self._dirty = True
+
+    def join_rows(self, rows) -> None:
+        """New requests in the given slots, without a launch: their
+        checkpoints count as zero (RS_CURSOR_ZERO_CKPT) and are not read until
+        each row's first flush writes it; anchored at 0.  The metadata goes
+        up with the next step's upload.  (The conventional step reads no
+        cursor: its rows need reset_rows.)"""
+        sel = np.zeros(self.n_slots, bool)
+        sel[np.asarray(rows, dtype=np.int64)] = True
+        sel &= self.live()
+        self.anchor[sel] = 0
+        self.zero_ckpt[sel] = True
         self._dirty = True
 
     def reset_rows(self, rows, stream=None) -> None:
@@ -249,8 +303,10 @@ class DecodeLayer:
         sel &= self.live()
         wp, _ = rs_meta_step(self.L, self.anchor)
         self._upload(stream, wp, mask=sel.astype(np.uint8))
-        replay_state_reset(self.layer, self.batch[self._cur], self.mask, stream)
+        for li in range(len(self.pools)):
+            replay_state_reset(self.layer, self.batches[li][self._cur], self.mask, stream)
         self.anchor[sel] = 0
+        self.zero_ckpt[sel] = False
         self._dirty = True
 
 

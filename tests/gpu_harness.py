@@ -80,6 +80,7 @@ class Case:
     reconstruct: bool = False        # Gated DeltaNet: the state-reconstruction route
     flush_hints: bool = True         # pass the host's flush hint (False: RS_FLUSH_UNKNOWN)
     forget_every: int = 0            # > 0: every n-th (step, row, head) has lam = -inf (alpha = 0)
+    join: bool = False               # replay rows join with a zero checkpoint (join_rows) instead of a reset
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
@@ -87,7 +88,7 @@ class Case:
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} read={self.read_dt} "
                 f"strided={self.strided} pad={self.pad_rows} groups={self.groups} "
                 f"route={'reconstruct' if self.reconstruct else 'output-only'} hints={self.flush_hints} "
-                f"forget_every={self.forget_every} seed={self.seed}")
+                f"forget_every={self.forget_every} join={self.join} seed={self.seed}")
 
 
 def full_forgetting(lam: torch.Tensor, every: int, step: int) -> None:
@@ -150,7 +151,10 @@ def run_case(c: Case, dev="cuda") -> dict:
             continue
         for b in live_rows:
             d.assign(b, int(blocks[b]))
-        d.reset_rows(live_rows)
+        if c.join and d is rep:
+            d.join_rows(live_rows)   # the checkpoints stay NaN-filled: never read until written
+        else:
+            d.reset_rows(live_rows)
     sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live_rows]
     ns = len(sample)
     ref = oracle.ConventionalModel(c.form, ns, c.H, c.dv, c.dk)
@@ -184,6 +188,9 @@ def run_case(c: Case, dev="cuda") -> dict:
         nxt = rep.device_cursor()
         lv = rep.live()
         assert np.array_equal(nxt[lv], rep.anchor[lv] % c.L), f"device cursor, step {s}"
+        # the zero-checkpoint flag the device carries equals the host's
+        zbit = (rep.device_cursor(words=True) & rs.RS_CURSOR_ZERO_CKPT) != 0
+        assert np.array_equal(zbit[lv], rep.zero_ckpt[lv]), f"zero-checkpoint flags, step {s}"
         for b in live_rows[1:]:
             assert wp[b] == s % c.L and bool(fl[b]) == (s % c.L == c.L - 1), (s, b)
         for b in c.pad_rows:

@@ -312,3 +312,31 @@ def test_persistent_step_item_counts(B, H, pad, force):
     64 whose writes it holds back at once."""
     _go(Case(form=rs.MAMBA2, B=B, H=H, dv=16, dk=32, L=4, steps=12, state_dt="f32", rec_dt="f16", io_dt="bf16",
              pad_rows=pad, force_every=force, check_conventional=False, seed=81 + B))
+
+
+@pytest.mark.parametrize("name,case", [
+    ("mamba2-tiny", dict()),
+    ("gdn-tiny", dict(form=rs.GDN)),
+    ("mamba2-nemotron-heads", dict(B=5, H=3, dv=64, dk=128, L=8, steps=20, rec_dt="f16", io_dt="bf16",
+                                   pad_rows=[2], force_every=3)),
+    ("mamba2-no-hints", dict(B=3, H=3, dv=64, dk=128, L=4, steps=12, rec_dt="f16", io_dt="bf16",
+                             flush_hints=False)),
+    ("e4m3-read-copy", dict(B=3, H=3, dv=64, dk=128, L=4, steps=12, rec_dt="f16", io_dt="bf16", read_dt="e4m3")),
+    ("f16-read-copy", dict(B=3, H=3, dv=64, dk=128, L=4, steps=12, rec_dt="f16", io_dt="bf16", read_dt="f16")),
+    ("gdn-128-f16-state", dict(form=rs.GDN, B=3, H=2, dv=128, dk=128, L=8, steps=20, state_dt="f16",
+                               rec_dt="f16", io_dt="bf16", force_every=5)),
+    ("gdn-reconstruct", dict(form=rs.GDN, B=3, H=3, L=4, steps=12, reconstruct=True)),
+])
+def test_join_with_zero_checkpoint(name, case):
+    """Rows join with RS_CURSOR_ZERO_CKPT instead of a state reset: their
+    checkpoints stay NaN-filled in the pool and must never be read before
+    the row's first flush writes them (any read would turn the outputs into
+    NaN); the flag the device carries in its cursors is bit-exact against the
+    host's, and is cleared by each row's first flush."""
+    c = Case(join=True, seed=80, **case)
+    if c.read_dt:
+        err = run_case(c)
+        assert err["out_replay"] <= TWO_COPY_TOL and err["ckpt_flush"] <= tolerance(c.state_dt, c.rec_dt)
+        assert err["read_bound_excess"] <= 0
+    else:
+        _go(c)

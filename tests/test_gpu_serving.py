@@ -131,14 +131,16 @@ def _load_row_start(d: DecodeLayer, block: int, C0, rec_lam, rec_x, rec_k, w0):
         rl[block, :, :w0] = torch.from_numpy(rec_lam[:, :w0]).float().to(DEV)
 
 
-def test_continuous_batching():
+@pytest.mark.parametrize("join", [False, True])
+def test_continuous_batching(join):
     """Nemotron-3-Super layer shapes, 256 request slots over a shuffled pool
     of 384 blocks, each starting mid-window (cursor ~ U{0..15}, random
     checkpoint and records); 200 steps in which each live row retires with
-    p = 1/32 and each empty slot takes a new request with p = 1/2.  Every
-    step checks 32 sampled slots against the oracle (through their retires
-    and joins), the host and device cursors, and that empty slots are not
-    written."""
+    p = 1/32 and each empty slot takes a new request with p = 1/2 (its state
+    zeroed by a reset launch, or, join=True, joined with a zero checkpoint
+    that is not read until the row's first flush).  Every step checks 32
+    sampled slots against the oracle (through their retires and joins), the
+    host and device cursors, and that empty slots are not written."""
     H, dv, dk, L, B, NB, steps = 128, 64, 128, 16, 256, 384, 200
     seed = 4
     lay = rs.layer(rs.MAMBA2, H, dv, dk, L, "f32", "f16", "bf16")
@@ -181,7 +183,10 @@ def test_continuous_batching():
                 ref.S[i * H:(i + 1) * H] = 0.0
         joined = [slot for slot, _ in ev.join]
         if joined:
-            rep.reset_rows(joined)
+            if join:
+                rep.join_rows(joined)
+            else:
+                rep.reset_rows(joined)
             conv.reset_rows(joined)
         tok = workloads.tokens(rs.MAMBA2, seed, s, B, H, dv, dk, "bf16")
         iod, out_r, keep = _dev_io(tok, B, H, dv)
@@ -306,4 +311,91 @@ def test_token_less_flush_of_speculative_layer(form, shape):
     tol = TOL_LOW if lowp else TOL_F32
     say(f"[errors] token-less flush of a speculative layer form={form} shape={shape}: ckpt={e:.3g} h={list(h)}")
     assert e <= tol
+    assert int(d.err.item()) == 0
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+def test_token_less_flush_of_joining_rows(form):
+    """Rows joined with a zero checkpoint (never written, NaN-filled pool):
+    a token-less flush of one at w = 6 writes the fold of its records into
+    zero, of one that has just joined (w = 0) writes zeros; both equal the
+    conventional state, the other joined row keeps its flag until its own
+    first flush, and decoding continues from all of them."""
+    B, H, dv, dk, L = 3, 2, 16, 32, 8
+    lay = rs.layer(form, H, dv, dk, L, "f32", "f32", "f32")
+    d = DecodeLayer(lay, B, B, DEV)
+    d.pool.raw.fill_(0xFF)
+    for b in (0, 1):
+        d.assign(b, b)
+    d.join_rows([0, 1])
+    ref = oracle.ConventionalModel(form, B, H, dv, dk)
+    worst = 0.0
+    for s in range(12):
+        if s == 6:  # row 2 joins, then rows 0 (6 records) and 2 (none) are materialised
+            d.assign(2, 2)
+            d.join_rows([2])
+            d.flush_rows([0, 2])
+            torch.cuda.synchronize()
+            ck = d.pool.ckpt()[torch.tensor([0, 2], device=DEV)].double().cpu().numpy()
+            e = rel_err(ck, ref.state()[[0, 2]], 2)
+            say(f"[flush] joined rows form={form}: ckpt err {e:.3g}")
+            assert e <= TOL_F32 and np.all(np.isfinite(ck)) and not ck[1].any()
+            assert list(d.zero_ckpt) == [False, True, False]
+            assert list(d.anchor) == [0, 6, 0]
+        tok = workloads.tokens(form, 91, s, B, H, dv, dk, "f32")
+        if s < 6:  # row 2 is empty: the oracle's row 2 stays at zero state
+            tok.v[2] = 0.0
+        iod, out, keep = _dev_io(tok, B, H, dv)
+        d.step(iod)
+        o_ref = ref.step(*_f64(tok, slice(None)))
+        torch.cuda.synchronize()
+        rows = [0, 1, 2] if s >= 6 else [0, 1]
+        worst = max(worst, rel_err(out[rows].double().cpu().numpy(), o_ref[rows]))
+        if s == 7:  # row 1's first flush (w = L - 1) wrote its checkpoint
+            assert not d.zero_ckpt.any()
+    say(f"[errors] joined rows + token-less flush form={form}: out={worst:.3g}")
+    assert worst <= TOL_F32
+    assert int(d.err.item()) == 0
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+def test_layers_sharing_metadata(form):
+    """Three layers over the same slots share one block table and one set of
+    cursors (DecodeLayer with n_layers = 3: one upload per step, each launch
+    writing the same next cursors): every layer matches its own oracle
+    through a retire, a join with a zero checkpoint and a forced flush."""
+    B, H, dv, dk, L, NL = 4, 2, 16, 32, 4, 3
+    lay = rs.layer(form, H, dv, dk, L, "f32", "f32", "f32")
+    d = DecodeLayer(lay, B, B + 1, DEV, n_layers=NL)
+    for pl in d.pools:
+        pl.raw.fill_(0xFF)
+    for b in range(B):
+        d.assign(b, b)
+    d.join_rows(range(B))
+    refs = [oracle.ConventionalModel(form, B, H, dv, dk) for _ in range(NL)]
+    worst = 0.0
+    uploads = []
+    for s in range(14):
+        if s == 5:  # row 1 retires; a new request takes its slot on the spare block
+            d.retire(1)
+            d.assign(1, B)
+            d.join_rows([1])
+            for r in refs:
+                r.S.reshape(B, H, dv, dk)[1] = 0.0
+        force = np.zeros(B, np.uint8)
+        if s == 8:
+            force[2] = 1
+        toks = [workloads.tokens(form, 200 + li, s, B, H, dv, dk, "f32") for li in range(NL)]
+        devs = [_dev_io(t, B, H, dv) for t in toks]
+        u0 = d.uploads
+        d.step([x[0] for x in devs], force)
+        uploads.append(d.uploads - u0)
+        torch.cuda.synchronize()
+        for li in range(NL):
+            o_ref = refs[li].step(*_f64(toks[li], slice(None)))
+            worst = max(worst, rel_err(devs[li][1].double().cpu().numpy(), o_ref))
+        assert np.array_equal(d.device_cursor()[d.live()], d.anchor[d.live()] % L)
+    say(f"[errors] {NL} layers sharing metadata form={form}: out={worst:.3g} uploads={uploads}")
+    assert worst <= TOL_F32
+    assert max(uploads) == 1 and sum(uploads) <= 4   # first step, the join, the forced flush and the step after
     assert int(d.err.item()) == 0
