@@ -62,6 +62,10 @@ WORKLOADS = {
 
 _ES = {"f32": 4, "f16": 2, "bf16": 2}
 
+# measured HBM bytes per launch (--summarize-counters writes, the roofline's
+# `traffic` reads)
+COUNTERS_PATH = os.path.join(ROOT, "profiles", "counters.json")
+
 # Launch log: when enabled (a list), every timed-suite launch of one of the
 # library's kernels is appended in launch order as (kernel, label, algorithmic
 # bytes), so that rocprofv3's per-dispatch counters of the same run can be
@@ -184,7 +188,7 @@ def workload_key(name, cfg) -> str:
 def load_traffic(workload_key: str):
     """HBM traffic per launch measured with rocprofv3 counters, if a summary
     for the current kernel source exists under profiles/."""
-    path = os.path.join(ROOT, "profiles", "counters.json")
+    path = COUNTERS_PATH
     if not os.path.exists(path):
         return None
     try:
@@ -402,8 +406,11 @@ def _inputs(cfg, B, n, dev, seed=11):
     import torch
     import workloads
     ios, keep = [], []
+    hg = cfg["H"] // cfg["groups"] if cfg.get("groups") else 1
     for s in range(n):
         t = workloads.tokens(cfg["form"], seed, s, B, cfg["H"], cfg["dv"], cfg["dk"], cfg["io"])
+        if hg > 1:  # the group's key and query: those drawn for its first head
+            t = workloads.Tokens(t.q[:, ::hg].contiguous(), t.k[:, ::hg].contiguous(), t.v, t.lam, t.beta)
         q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
         beta = t.beta.to(dev) if t.beta is not None else None
         out = torch.empty((B, cfg["H"], cfg["dv"]), dtype=torch.float32, device=dev)
@@ -416,7 +423,7 @@ def _layer_stack(cfg, B, n_layers, dev, reconstruct=False):
     import linear_attention_decode_replay_amd as rs
     from linear_attention_decode_replay_amd.state import DecodeLayer
     lay = rs.layer(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], cfg["L"], cfg["state"], cfg["rec"], cfg["io"],
-                   cfg["read"], reconstruct=reconstruct)
+                   cfg["read"], 0, cfg.get("groups", 0), reconstruct=reconstruct)
     layers = []
     for _ in range(n_layers):
         d = DecodeLayer(lay, B, B, dev)
@@ -454,10 +461,13 @@ def suite_gdn_sweep(out, steps=32):
                     else:
                         d.conventional_step(ios[s % 16], events=ev)
                         w, f = 0, False
+                    nb = step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, state, cfg["rec"], cfg["io"], w,
+                                    f, "conventional" if kind == "conventional" else "replay")
+                    log_launch("k_conventional_step" if kind == "conventional" else "k_replay_step",
+                               f"gdn B={B} {state} {kind}" + ("" if s >= 16 else " warm-up"), nb)
                     if s >= 16:
                         times.append(ev)
-                        nbytes.append(step_bytes(cfg["form"], cfg["H"], cfg["dv"], cfg["dk"], B, state, cfg["rec"],
-                                                 cfg["io"], w, f, "conventional" if kind == "conventional" else "replay"))
+                        nbytes.append(nb)
                 torch.cuda.synchronize()
                 us = float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e3
                 res[kind] = {"us": round(us, 2), "tbs": round(float(np.mean(nbytes)) / (us * 1e-6) / 1e12, 3)}
@@ -538,26 +548,44 @@ def suite_stack(out, n_layers=40, quick=False):
             print(json.dumps(line), file=out, flush=True)
 
 
-def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0):
+def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0, groups=0, accepted=None):
     """Algorithmic HBM bytes of one speculative verify launch (rows with h
     committed records, flushing or not) plus its commit launch.  Per (row,
     head): read the checkpoint and the h committed records, read T draft
     tokens (q, k, v, log-decay), write T records and T fp32 outputs; a
     flushing row also writes the checkpoint.  Per row: block id, count and
     flag read by the verify; the commit reads block id, count, flag and the
-    accepted count and writes the next count and flag."""
+    accepted count and writes the next count and flag.  With `groups` key
+    groups the key records and q, k inputs of a group are counted once,
+    spread over its heads, and the commit moves each flushed row's accepted
+    keys (`accepted`) out of the staging slots: read and write once per
+    group (see spec_commit_key_bytes)."""
     h = np.asarray(h)
     flush = np.asarray(flush, bool)
+    hg = H // groups if groups else 1
     ms = dv * dk * _ES[state]
-    r = (dv + dk) * _ES[rec] + 4
-    tok = (2 * dk + dv) * _ES[io] + 4 + (4 if form == 1 else 0)  # q, k, v, log-decay (and beta)
+    r = (dv + dk / hg) * _ES[rec] + 4
+    tok = (2 * dk / hg + dv) * _ES[io] + 4 + (4 if form == 1 else 0)  # q, k, v, log-decay (and beta)
     per_head = ms + h * r + T * (tok + r + 4 * dv) + np.where(flush, ms, 0)
-    return float(np.sum(H * per_head + 9) + B * 18)
+    moved = spec_commit_key_bytes(dk, rec, flush, accepted, groups) if hg > 1 else 0.0
+    return float(np.sum(H * per_head + 9) + B * 18 + moved)
+
+
+def spec_commit_key_bytes(dk, rec, flush, accepted, groups):
+    """Bytes the commit moves for grouped keys: each flushed row's accepted
+    draft keys, read from the staging slots and written to slot 0, per
+    group (block id, count and flag re-read per (row, group) are counted
+    with the commit's per-row bytes)."""
+    if accepted is None:
+        raise ValueError("grouped keys: the accepted counts decide the commit's key moves")
+    a = np.where(np.asarray(flush, bool), np.asarray(accepted), 0)
+    return float(2 * groups * dk * _ES[rec] * np.sum(a))
 
 
 def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
-    """Speculative verify at the Nemotron-3-Super layer shape (or, workload
-    "gdn", the Gated DeltaNet layer: 32 heads, 128 x 128), batch 256,
+    """Speculative verify at the Nemotron-3-Super layer shape (workload
+    "nemotron-grouped": with its 8 key groups; "gdn": the Gated DeltaNet
+    layer, 32 heads, 128 x 128), batch 256,
     L = 16, fp32 checkpoint, fp16 records, bf16 inputs, T in {4, 8}, with
     every draft accepted, one token per step, and uniform 0..T acceptance.
     One step = one verify launch + one commit launch (the committed counts
@@ -573,6 +601,8 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
     base = dict(WORKLOADS[workload])
     B, H, dv, dk, L = base["B"], base["H"], base["dv"], base["dk"], base["L"]
     form = base["form"]
+    groups = base.get("groups", 0)
+    hg = H // groups if groups else 1
     # standard steps for reference (one token per row per step)
     ios, keep = _inputs(base, B, 16, dev)
     ref_us = {}
@@ -592,7 +622,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 d.conventional_step(ios[s % 16])
                 w, f = 0, False
             log_launch("k_replay_step" if kind == "replay" else "k_conventional_step", f"spec reference {kind}",
-                       step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind))
+                       step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind, groups=groups))
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         torch.cuda.synchronize()
@@ -601,10 +631,12 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
         torch.cuda.empty_cache()
     del ios, keep
     for T in Ts:
-        lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", None, T)
+        lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", None, T, groups)
         drafts = []
         for s in range(8):
             t = workloads.spec_tokens(11, s, B, H, T, dv, dk, "bf16", form=form)
+            if hg > 1:  # the group's key and query: those drawn for its first head
+                t.q, t.k = t.q[:, :, ::hg].contiguous(), t.k[:, :, ::hg].contiguous()
             q, k, v, lam = (x.to(dev) for x in (t.q, t.k, t.v, t.lam))
             beta = t.beta.to(dev) if t.beta is not None else None
             o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
@@ -631,7 +663,8 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 d, hm = pools[pi], hmirror[pi]
                 a = acc_host[s % steps]
                 fl = rs.rs_spec_meta_step(L, T, hm)
-                nb = spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form)
+                nb = spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form, groups, a)
+                moved = spec_commit_key_bytes(dk, "f16", fl, a, groups) if hg > 1 else 0.0
                 if s >= n_warm:
                     nbytes += nb
                     tokens += int(a.sum())
@@ -639,7 +672,9 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 d.verify(drafts[s % 8][1])
                 d.commit(acc[s % steps])
                 log_launch("k_spec_verify" if form == 0 else "k_spec_verify_gdn", f"T={T} accept {policy}",
-                           nb - B * 18)
+                           nb - B * 18 - moved)
+                if hg > 1:
+                    log_launch("k_spec_commit_keys", f"T={T} accept {policy}", moved)
                 log_launch("k_spec_commit", f"T={T} accept {policy}", B * 18)
                 rs.rs_spec_meta_advance(L, T, hm, fl, a)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -855,6 +890,16 @@ def line_up(rows, log, scale):
     return out
 
 
+def suite_key(args) -> str:
+    """The counters.json key of a suite run: which suite and its options."""
+    parts = ["suite", args.suite_only or "all"]
+    if args.suite_only == "spec":
+        parts += [f"T{t}" for t in (args.spec_T or (4, 8))] + list(args.spec_workload or ["nemotron", "gdn"])
+    if args.suite_only == "stack" and args.stack_quick:
+        parts.append("quick")
+    return "-".join(str(x) for x in parts)
+
+
 def summarize_counters(args, fetch_csv, write_csv):
     """FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
     (known bytes of the calibration copy) / (its reading).  The dispatches
@@ -887,6 +932,22 @@ def summarize_counters(args, fetch_csv, write_csv):
                       "ratio": float((f + w).sum() / alg.sum())}
         print(json.dumps({k: (round(v) if isinstance(v, float) and k != "ratio" else
                               (round(v, 4) if k == "ratio" else v)) for k, v in table[key].items()}))
+    path = COUNTERS_PATH
+    if log.get("suite_key"):  # a suite: every (kernel, case) as measured
+        data = json.load(open(path)) if os.path.exists(path) else {}
+        data[log["suite_key"]] = {
+            "kernel_source": kernel_source_hash(),
+            "basis": "mean per launch of each (kernel, case) label",
+            "by_label": {f"{t['kernel']} {t['label']}": {"launches": t["launches"], "fetch": round(t["fetch"]),
+                                                         "write": round(t["write"]), "total": round(t["total"]),
+                                                         "algorithmic": round(t["algorithmic"]),
+                                                         "ratio": round(t["ratio"], 4)}
+                         for t in table.values()},
+            "scale": {"fetch": round(scales["fetch"], 4), "write": round(scales["write"], 4)},
+            "calibration_copy_mib": mib}
+        with open(path, "w") as fo:
+            json.dump(data, fo, indent=1, sort_keys=True)
+            fo.write("\n")
     # the one-line benchmark's launches: window averages over the cursors
     L = log.get("L")
     if L and log.get("workload_key"):
@@ -910,7 +971,6 @@ def summarize_counters(args, fetch_csv, write_csv):
                                   "bytes_per_launch": round(conv["total"]), "algorithmic": round(conv["algorithmic"])},
                  "scale": {"fetch": round(scales["fetch"], 4), "write": round(scales["write"], 4)},
                  "calibration_copy_mib": mib}
-        path = os.path.join(ROOT, "profiles", "counters.json")
         data = json.load(open(path)) if os.path.exists(path) else {}
         data[log["workload_key"]] = entry
         with open(path, "w") as fo:
@@ -969,7 +1029,7 @@ def summarize_trace(trace_csv, launch_log):
     return 0
 
 
-def main(argv=None):
+def build_parser():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
@@ -995,7 +1055,7 @@ def main(argv=None):
                     help="with --suite: run one part of it")
     ap.add_argument("--spec-T", type=int, action="append", default=None,
                     help="with --suite-only spec: the draft counts to run (default 4 and 8)")
-    ap.add_argument("--spec-workload", choices=["nemotron", "gdn"], action="append", default=None,
+    ap.add_argument("--spec-workload", choices=["nemotron", "nemotron-grouped", "gdn"], action="append", default=None,
                     help="with --suite-only spec: the layers to run (default both)")
     ap.add_argument("--stack-quick", action="store_true",
                     help="with --suite-only stack: only the fp32 conventional and the L = 16 fp32 replay stacks")
@@ -1008,7 +1068,11 @@ def main(argv=None):
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
                          "into per-launch HBM bytes in profiles/counters.json and print them; runs nothing on the GPU")
-    args = ap.parse_args(argv)
+    return ap
+
+
+def main(argv=None):
+    args = build_parser().parse_args(argv)
     if args.summarize_counters:
         return summarize_counters(args, *args.summarize_counters)
     if args.summarize_trace:
@@ -1037,7 +1101,7 @@ def main(argv=None):
         print(open(args.suite).read(), end="")
         if args.launch_log:
             with open(args.launch_log, "w") as f:
-                json.dump({"launches": _LAUNCH_LOG}, f)
+                json.dump({"launches": _LAUNCH_LOG, "suite_key": suite_key(args)}, f)
         return 0
 
     if args.gpus != 1:

@@ -91,15 +91,16 @@ typedef enum {
  *               becomes a pointer"): its ring holds up to L committed records
  *               and each step verifies T draft tokens per row with
  *               replay_spec_verify; replay_decode_step rejects it.  Single
- *               fp32 or fp16 checkpoint, one key per head; (d_v, d_k) =
- *               (16, 32) or (64, 128), and (128, 128) for Gated DeltaNet.
+ *               fp32 or fp16 checkpoint; keys per head or grouped
+ *               (n_groups); (d_v, d_k) = (16, 32), (64, 128) or (128, 128).
  * n_groups:     0 or n_heads for a key and a query per head.  A divisor
  *               G < n_heads shares one key and one query among each run of
  *               n_heads / G consecutive heads, the released grouped-key
  *               layout (blog "The identity", the paragraph on the released
  *               kernel: values and decays per value head, keys per group):
- *               q and k inputs are [n_rows][G][d_k] and the ring keeps one
- *               key record per group.  Standard decoding only (spec_T = 0).
+ *               q and k inputs are [n_rows][G][d_k] ([n_rows][T][G][d_k]
+ *               for a speculative layer) and the ring keeps one key record
+ *               per group, written by the group's first head.
  * state_rounding: RS_ROUND_NEAREST (nearest even) for every store.
  *               RS_ROUND_STOCHASTIC, with state_dtype RS_F16 only: every
  *               store of the fp16 checkpoint, state or recurrence copy (a
@@ -183,8 +184,9 @@ typedef enum { RS_GDN_OUTPUT_ONLY = 0, RS_GDN_RECONSTRUCT = 1 } rs_gdn_route;
  * Offsets are from the block start; every region starts 256-byte aligned.
  *   ckpt     [n_heads][d_v][d_k]    state_dtype, row-major per head
  *   rec_x    [n_heads][slots][d_v]  record_dtype
- *   rec_k    [n_groups][slots][d_k] record_dtype (n_groups = n_heads
- *                                   unless the layer groups its keys)
+ *   rec_k    [n_groups][key_slots][d_k] record_dtype (n_groups =
+ *                                   n_heads unless the layer groups its
+ *                                   keys)
  *   rec_lam  [n_heads][slots]       fp32 log-decay
  *   ckpt_lo  [n_heads][d_v][d_k]    read_dtype (two-precision checkpoint only;
  *                                   ckpt_lo_off is 0 otherwise), each row of
@@ -198,8 +200,12 @@ typedef enum { RS_GDN_OUTPUT_ONLY = 0, RS_GDN_RECONSTRUCT = 1 } rs_gdn_route;
  *                                   written with contiguous accesses
  *   ckpt_sc  [n_heads][d_v]         fp32 row scales of an RS_E4M3 read copy
  *                                   (ckpt_scale_off is 0 otherwise)
- * slots = L - 1 (a speculative layer: slots = L).  block_bytes is a multiple
- * of 256.
+ * slots = L - 1 (a speculative layer: slots = L).  key_slots = slots, except
+ * on a speculative layer with grouped keys (n_groups < n_heads): L + T, the
+ * last T holding the drafts of a row that flushed in its verify until
+ * replay_spec_commit moves the accepted ones to slots 0.. (the verify cannot
+ * write them there itself: other heads of the group may still be reading the
+ * committed keys).  block_bytes is a multiple of 256.
  */
 typedef struct {
     int64_t ckpt_off;
@@ -208,7 +214,7 @@ typedef struct {
     int64_t rec_lam_off;
     int64_t block_bytes;
     int32_t slots;
-    int32_t reserved;
+    int32_t key_slots;
     int64_t ckpt_lo_off;
     int64_t ckpt_scale_off;
 } rs_block_layout;
@@ -408,7 +414,9 @@ int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, cons
  * A row whose ring has no room for T more records (h + T > L), or whose flag
  * is set, flushes first: its h committed records (only those) are folded into
  * the checkpoint, which is written once, and the drafts are stored from slot
- * 0.  This needs no acceptance count, so it happens in the same launch.
+ * 0 (with grouped keys, the drafts' keys go to the staging slots L..L+T-1
+ * until the commit; see key_slots).  This needs no acceptance count, so it
+ * happens in the same launch.
  * After sampling, replay_spec_commit advances each row's committed count by
  * the number of drafts accepted; records past it are never read and get
  * overwritten.
@@ -420,9 +428,10 @@ int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, cons
  *     u_i = beta_i (v_i - D_i S_h k_i) - beta_i sum_{m<i} W_im (k_m . k_i) u_m
  *     o_i = D_i S_h q_i + sum_{m<=i} W_im (k_m . q_i) u_m
  * solved draft by draft; the drafts' u_i are stored as their records.
- * Heads of 16 x 32, 64 x 128 (both forms) and 128 x 128 (Gated DeltaNet).
+ * Heads of 16 x 32, 64 x 128 and 128 x 128, both forms.
  *
- * q, k: [n_rows][T][n_heads][d_k]; v: [n_rows][T][n_heads][d_v], io_dtype,
+ * q, k: [n_rows][T][n_heads][d_k] ([n_rows][T][n_groups][d_k] with grouped
+ * keys); v: [n_rows][T][n_heads][d_v], io_dtype,
  * unit stride along the last dimension, row / token / head strides in
  * elements; log_decay (and beta): [n_rows][T][n_heads] fp32 contiguous; out:
  * [n_rows][T][n_heads][d_v] fp32 contiguous.
@@ -456,7 +465,11 @@ int replay_spec_verify(const rs_layer* layer, const rs_batch* batch, const rs_sp
  * batch->next_write_pos and next_flush[row] = (h' + T > L).  Passing
  * (next_write_pos, next_flush) as the next verify's (write_pos, flush) keeps
  * the cursor on the device.  accepted: device int32 [n_rows], 0..T; a row
- * with another value commits nothing and is counted in err_count.
+ * with another value commits nothing and is counted in err_count.  With
+ * grouped keys, a row that flushed also has its accepted drafts' keys moved
+ * from the staging slots L.. to slots 0.. of each group (see key_slots): the
+ * verify of a flushing row leaves them there, so the commit must run before
+ * the row's next verify or token-less flush, on the same stream.
  * batch->next_write_pos and next_flush must not alias write_pos / flush.
  */
 int replay_spec_commit(const rs_layer* layer, const rs_batch* batch, const int32_t* accepted,

@@ -48,7 +48,7 @@ class RsLayer(_c.Structure):
 class RsBlockLayout(_c.Structure):
     _fields_ = [("ckpt_off", _c.c_int64), ("rec_x_off", _c.c_int64), ("rec_k_off", _c.c_int64),
                 ("rec_lam_off", _c.c_int64), ("block_bytes", _c.c_int64), ("slots", _c.c_int32),
-                ("reserved", _c.c_int32), ("ckpt_lo_off", _c.c_int64), ("ckpt_scale_off", _c.c_int64)]
+                ("key_slots", _c.c_int32), ("ckpt_lo_off", _c.c_int64), ("ckpt_scale_off", _c.c_int64)]
 
 
 class RsBatch(_c.Structure):
@@ -188,8 +188,9 @@ def make_io(q, k, v, log_decay, out, beta=None) -> RsStepIO:
 
 
 def make_spec_io(q, k, v, log_decay, out, beta=None) -> RsSpecIO:
-    """q, k: [n_rows, T, n_heads, d_k]; v: [n_rows, T, n_heads, d_v] (any
-    row/token/head strides, unit last stride); log_decay, beta (Gated
+    """q, k: [n_rows, T, n_heads, d_k] ([n_rows, T, n_groups, d_k] with
+    grouped keys); v: [n_rows, T, n_heads, d_v] (any row/token/head strides,
+    unit last stride); log_decay, beta (Gated
     DeltaNet only): fp32 [n_rows, T, n_heads] contiguous; out: fp32
     [n_rows, T, n_heads, d_v] contiguous."""
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -320,9 +321,10 @@ class Pool:
                             self._tdt[L.record_dtype], (L.n_heads, s, L.d_v))
 
     def rec_k(self):
-        """[n_blocks, G, slots, d_k] in the record dtype (G = key groups,
-        n_heads unless the layer groups its keys)."""
-        L, s = self.layer, self.layout.slots
+        """[n_blocks, G, key_slots, d_k] in the record dtype (G = key groups,
+        n_heads unless the layer groups its keys; key_slots = slots, plus T
+        staging slots on a speculative layer with grouped keys)."""
+        L, s = self.layer, self.layout.key_slots
         es = 4 if L.record_dtype == F32 else 2
         G = L.n_groups if L.n_groups > 0 else L.n_heads
         return self._region(self.layout.rec_k_off, G * s * L.d_k * es,

@@ -44,6 +44,14 @@ bool two_precision(const rs_layer& L) { return L.read_dtype >= 0 && L.read_dtype
 
 // Key groups: n_groups, or one per head.
 int groups_of(const rs_layer& L) { return L.n_groups > 0 ? L.n_groups : L.n_heads; }
+// Key record slots per group: the ring's, plus, on a speculative layer whose
+// keys are shared by several heads, T more that hold the drafts of a flushing
+// row until replay_spec_commit moves them to slot 0 (the other heads of the
+// group may still be reading the committed keys there during the verify).
+int key_slots_of(const rs_layer& L) {
+    const int slots = L.spec_T > 0 ? L.L : L.L - 1;
+    return L.spec_T > 0 && groups_of(L) != L.n_heads ? slots + L.spec_T : slots;
+}
 // LDS of one workgroup on gfx950, the one target the kernels are built for;
 // a launch also checks the device's own limit (do_launch).
 const size_t kMaxLds = 160 * 1024;
@@ -79,8 +87,6 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
         return fail(RS_EINVAL, "the state-reconstruction route is a Gated DeltaNet option");
     if (L->n_groups < 0 || (L->n_groups > 0 && L->n_heads % L->n_groups != 0))
         return fail(RS_EINVAL, "n_groups (%d) must be 0 or divide n_heads (%d)", L->n_groups, L->n_heads);
-    if (L->spec_T != 0 && groups_of(*L) != L->n_heads)
-        return fail(RS_EUNSUPPORTED, "speculative verify: one key per head only (n_groups = 0)");
     const bool spec_kind = kind == rs::Kind::SpecVerify || kind == rs::Kind::SpecCommit;
     if (L->spec_T != 0) {
         const int T = L->spec_T;
@@ -96,8 +102,8 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
     }
     if (!rs::compiled(kind, *L)) {
         if (spec_kind)
-            return fail(RS_EUNSUPPORTED, "no speculative kernel for d_v=%d d_k=%d (supported: 16x32, 64x128%s)",
-                        L->d_v, L->d_k, L->form == RS_GDN ? ", 128x128" : "");
+            return fail(RS_EUNSUPPORTED, "no speculative kernel for d_v=%d d_k=%d (supported: 16x32, 64x128, 128x128)",
+                        L->d_v, L->d_k);
         if (L->read_dtype == RS_E4M3)
             return fail(RS_EUNSUPPORTED, "no kernel for an E4M3 read copy with d_v=%d d_k=%d (supported: 64x128, "
                                          "128x128)", L->d_v, L->d_k);
@@ -119,7 +125,7 @@ void layout_of(const rs_layer& L, rs_block_layout* o) {
     o->ckpt_off = 0;
     o->rec_x_off = align_up(H * L.d_v * L.d_k * sb, 256);
     o->rec_k_off = align_up(o->rec_x_off + H * slots * L.d_v * rb, 256);
-    o->rec_lam_off = align_up(o->rec_k_off + (int64_t)groups_of(L) * slots * L.d_k * rb, 256);
+    o->rec_lam_off = align_up(o->rec_k_off + (int64_t)groups_of(L) * key_slots_of(L) * L.d_k * rb, 256);
     o->block_bytes = align_up(o->rec_lam_off + H * slots * 4, 256);
     o->ckpt_lo_off = 0;
     o->ckpt_scale_off = 0;
@@ -132,7 +138,7 @@ void layout_of(const rs_layer& L, rs_block_layout* o) {
         }
     }
     o->slots = (int32_t)slots;
-    o->reserved = 0;
+    o->key_slots = key_slots_of(L);
 }
 
 int check_batch(const rs_layer& L, const rs_batch* b, bool needs_cursor, bool needs_flush) {
@@ -212,6 +218,8 @@ rs::StepParams params(const rs_layer& L, const rs_batch& b) {
     p.n_heads = L.n_heads;
     p.L = L.L;
     p.slots = lay.slots;
+    p.key_slots = lay.key_slots;
+    p.key_bytes = L.d_k * dtype_bytes(L.record_dtype);
     p.heads_per_group = L.n_heads / groups_of(L);
     p.sr = L.state_rounding == RS_ROUND_STOCHASTIC;
     p.reconstruct = L.gdn_route == RS_GDN_RECONSTRUCT;
@@ -367,14 +375,15 @@ int replay_spec_verify(const rs_layer* layer, const rs_batch* batch, const rs_sp
     if (!io) return fail(RS_EINVAL, "io is NULL");
     if (batch->n_rows == 0) return ok();
     const int T = layer->spec_T, e = dtype_bytes(layer->io_dtype);
-    struct { const char* name; const void* p; int64_t rs, ts, hs; int d; } v3[] = {
-        {"q", io->q, io->q_row_stride, io->q_token_stride, io->q_head_stride, layer->d_k},
-        {"k", io->k, io->k_row_stride, io->k_token_stride, io->k_head_stride, layer->d_k},
-        {"v", io->v, io->v_row_stride, io->v_token_stride, io->v_head_stride, layer->d_v}};
+    const int64_t G = groups_of(*layer);  // q and k: one per key group
+    struct { const char* name; const void* p; int64_t rs, ts, hs; int d; int64_t heads; } v3[] = {
+        {"q", io->q, io->q_row_stride, io->q_token_stride, io->q_head_stride, layer->d_k, G},
+        {"k", io->k, io->k_row_stride, io->k_token_stride, io->k_head_stride, layer->d_k, G},
+        {"v", io->v, io->v_row_stride, io->v_token_stride, io->v_head_stride, layer->d_v, layer->n_heads}};
     for (const auto& a : v3) {
         if ((rc = check_vec(a.name, a.p, a.rs, a.hs, a.d, e))) return rc;
         if ((a.ts * e) % 16) return fail(RS_EINVAL, "%s token stride must keep 16-byte alignment", a.name);
-        if (a.ts < (int64_t)layer->n_heads * a.hs)
+        if (a.ts < a.heads * a.hs)
             return fail(RS_EINVAL, "%s token stride overlaps the heads of the previous token", a.name);
         if (batch->n_rows > 1 && a.rs < (int64_t)T * a.ts)
             return fail(RS_EINVAL, "%s row stride overlaps the tokens of the previous row", a.name);

@@ -855,7 +855,7 @@ struct TilePtrs {
         // keys and queries per group of heads_per_group heads (1: per head)
         const int grp = id.head / p.heads_per_group;
         key_owner = id.head == grp * p.heads_per_group;
-        rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.slots * DK;
+        rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.key_slots * DK;
         rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
         qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
         kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
@@ -1379,7 +1379,7 @@ __device__ __forceinline__ void drain_deferred(const StepParams& p, char* dbase,
         } else if (j < OCH + KCH) {
             const int grp = head / p.heads_per_group;
             if (part == 0 && head == grp * p.heads_per_group) {
-                R* rk = reinterpret_cast<R*>(base + p.reck_off) + ((int64_t)grp * p.slots + w) * DK;
+                R* rk = reinterpret_cast<R*>(base + p.reck_off) + ((int64_t)grp * p.key_slots + w) * DK;
                 st_stream(reinterpret_cast<u32x4*>(rk) + (j - OCH), reinterpret_cast<const u32x4*>(df.k)[j - OCH]);
             }
         } else if (j < OCH + KCH + XCH) {
@@ -1689,7 +1689,8 @@ __global__ __launch_bounds__((Tile<DV, DK, TL, SPLIT>::NT)) void k_replay_flush(
     RL* cl = reinterpret_cast<RL*>(base + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK) + (int64_t)row0 * DK;
     float* cs = reinterpret_cast<float*>(base + p.ckpt_sc_off) + id.head * DV + row0;
     const R* rx = reinterpret_cast<const R*>(base + p.recx_off) + (int64_t)id.head * p.slots * DV + row0;
-    const R* rk = reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)(id.head / p.heads_per_group) * p.slots * DK;
+    const R* rk =
+        reinterpret_cast<const R*>(base + p.reck_off) + (int64_t)(id.head / p.heads_per_group) * p.key_slots * DK;
     const float* rl = reinterpret_cast<const float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1871,14 +1872,20 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     const int tid = threadIdx.x;
     const int cc = tid % LPR;
     const int rg = tid / LPR;
+    // keys and queries per group of heads_per_group heads (1: per head); the
+    // group's first head stores its draft keys, a flushing row's in the
+    // staging slots (the other heads may still read the committed ones)
+    const int grp = id.head / p.heads_per_group;
+    const bool key_owner = id.head == grp * p.heads_per_group;
+    const int kbase = fl && p.heads_per_group > 1 ? p.slots : base;
 
     char* bp = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(bp + p.ckpt_off) + (int64_t)id.head * (DV * DK);
     R* rx = reinterpret_cast<R*>(bp + p.recx_off) + (int64_t)id.head * p.slots * DV;
-    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)grp * p.key_slots * DK;
     float* rl = reinterpret_cast<float*>(bp + p.reclam_off) + (int64_t)id.head * p.slots;
-    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
-    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
+    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vb = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
     const int64_t tok0 = (int64_t)id.row * T;  // this row's first token in [row][T] arrays
 
@@ -2099,13 +2106,15 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
             for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
         }
     }
-    // drafts become records base .. base + T - 1
+    // drafts become records base .. base + T - 1 (keys: kbase .., the group's first head)
+    if (key_owner) {
 #pragma unroll
-    for (int u = 0; u < QN; ++u) {
-        const int e = (u * NT + tid) * 4;
-        if (e < T * DK) {
-            const int i = e / DK, c = e - i * DK;
-            store_f<TR, 4>(rk + (int64_t)(base + i) * DK + c, s.kd + e);
+        for (int u = 0; u < QN; ++u) {
+            const int e = (u * NT + tid) * 4;
+            if (e < T * DK) {
+                const int i = e / DK, c = e - i * DK;
+                store_f<TR, 4>(rk + (int64_t)(kbase + i) * DK + c, s.kd + e);
+            }
         }
     }
 #pragma unroll
@@ -2203,14 +2212,18 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(c
     const int tid = threadIdx.x;
     const int cc = tid % LPR;
     const int rg = tid / LPR;
+    // keys and queries per group (as k_spec_verify)
+    const int grp = id.head / p.heads_per_group;
+    const bool key_owner = id.head == grp * p.heads_per_group;
+    const int kbase = fl && p.heads_per_group > 1 ? p.slots : base;
 
     char* bp = p.pool + (int64_t)blk * p.block_bytes;
     S* ck = reinterpret_cast<S*>(bp + p.ckpt_off) + (int64_t)id.head * (DV * DK);
     R* rx = reinterpret_cast<R*>(bp + p.recx_off) + (int64_t)id.head * p.slots * DV;
-    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)id.head * p.slots * DK;
+    R* rk = reinterpret_cast<R*>(bp + p.reck_off) + (int64_t)grp * p.key_slots * DK;
     float* rl = reinterpret_cast<float*>(bp + p.reclam_off) + (int64_t)id.head * p.slots;
-    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + id.head * p.qs_h;
-    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + id.head * p.ks_h;
+    const I* qb = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
+    const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vb = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
     const int64_t tok0 = (int64_t)id.row * T;
 
@@ -2434,13 +2447,16 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(c
             for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
         }
     }
-    // 7. drafts become records base .. base + T - 1: keys, corrected values, log-decays
+    // 7. drafts become records base .. base + T - 1: keys (kbase .., the
+    // group's first head), corrected values, log-decays
+    if (key_owner) {
 #pragma unroll
-    for (int u = 0; u < QN; ++u) {
-        const int e = (u * NT + tid) * 4;
-        if (e < T * DK) {
-            const int i = e / DK, c = e - i * DK;
-            store_f<TR, 4, kNtSmall<kGdn>>(rk + (int64_t)(base + i) * DK + c, s.kd + e);
+        for (int u = 0; u < QN; ++u) {
+            const int e = (u * NT + tid) * 4;
+            if (e < T * DK) {
+                const int i = e / DK, c = e - i * DK;
+                store_f<TR, 4, kNtSmall<kGdn>>(rk + (int64_t)(kbase + i) * DK + c, s.kd + e);
+            }
         }
     }
     if (owner) {
@@ -2451,6 +2467,27 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(c
                 st_nt<kNtSmall<kGdn>>(rx + (int64_t)(base + i) * DV + ((b0 + 2 * x) / 2) * RPP + rg, from_f<TR>(ur[i][x]));
     }
     if (tid < T) st_nt<kNtSmall<kGdn>>(rl + base + tid, s.lamd[tid]);
+}
+
+// Grouped keys: a row that flushed in its verify has its drafts' keys in the
+// staging slots (slots .. slots + T - 1 of each group); move the accepted
+// ones to slots 0 .. a - 1.  One workgroup per (row, group), 16-byte chunks.
+// Reads the same metadata as k_spec_commit, which writes other arrays.
+__global__ __launch_bounds__(64) void k_spec_commit_keys(const StepParams p) {
+    const int row = blockIdx.y, grp = blockIdx.x;
+    const int blk = p.block_table[row];
+    if (blk < 0) return;
+    const int h = p.write_pos[row];
+    const int T = p.spec_T;
+    if (blk >= p.n_blocks || h < 0 || h > p.slots) return;  // counted by k_spec_commit
+    const bool fl = (p.flush && p.flush[row]) || (h + T > p.L);
+    const int a = p.accepted[row];
+    if (!fl || a < 1 || a > T) return;
+    char* keys = p.pool + (int64_t)blk * p.block_bytes + p.reck_off + (int64_t)grp * p.key_slots * p.key_bytes;
+    const int n = a * p.key_bytes / 16;  // key_bytes is a multiple of 16
+    const u32x4* src = reinterpret_cast<const u32x4*>(keys + (int64_t)p.slots * p.key_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(keys);
+    for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
 }
 
 // Commit after a verify: one thread per row (see replay_spec_commit).
@@ -2736,10 +2773,8 @@ struct Dispatch {
                 if (kind == Kind::SpecVerify) {
                     with_form(L.form, [&](auto f_c) {
                         constexpr int FORM = decltype(f_c)::value;
-                        // Mamba-2: heads of one workgroup's size (64 x 128, 16 x 32);
-                        // Gated DeltaNet: also 128 x 128 in one workgroup
-                        constexpr bool have = FORM == kMamba2 ? (tile_ok<DV, DK, TS, 1>() && split_for<DV, DK>() == 1)
-                                                              : tile_ok<DV, DK, TS, 1>();
+                        // one workgroup per (row, head) tile, 128 x 128 included
+                        constexpr bool have = tile_ok<DV, DK, TS, 1>();
                         if constexpr (have) {
                             with_record(L.record_dtype, [&](auto tr) {
                                 using TR = decltype(tr);
@@ -2767,6 +2802,10 @@ struct Dispatch {
                 }
                 if (kind == Kind::SpecCommit) {
                     ok = true;
+                    if (p && p->heads_per_group > 1)
+                        hipLaunchKernelGGL(k_spec_commit_keys, dim3((unsigned)(p->n_heads / p->heads_per_group),
+                                                                    (unsigned)p->n_rows),
+                                           dim3(64), 0, stream, *p);
                     if (p)
                         hipLaunchKernelGGL(k_spec_commit, dim3((unsigned)((p->n_rows + 255) / 256)), dim3(256), 0,
                                            stream, *p);

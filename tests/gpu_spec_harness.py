@@ -44,12 +44,14 @@ class SpecCase:
     strided: bool = False            # q/k/v as strided views of wider buffers
     force_row0_every: int = 0        # > 0: force a flush on row 0 every n steps
     forget_every: int = 0            # > 0: every n-th (step, row, draft, head) has lam = -inf
+    groups: int = 0                  # key groups (0: a key and query per head)
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"spec {f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} accept={self.accept} "
-                f"strided={self.strided} pad={self.pad_rows} forget_every={self.forget_every} seed={self.seed}")
+                f"strided={self.strided} pad={self.pad_rows} forget_every={self.forget_every} groups={self.groups} "
+                f"seed={self.seed}")
 
 
 def _device(t: torch.Tensor, strided: bool, dev):
@@ -64,7 +66,8 @@ def _device(t: torch.Tensor, strided: bool, dev):
 
 def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     say(f"[case] {c.name()}")
-    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T, c.groups)
+    hg = c.H // c.groups if c.groups else 1  # heads per key group
     n_blocks = c.B + 3
     d = SpecDecodeLayer(lay, c.B, n_blocks, dev)
     d.pool.raw.fill_(0xFF)  # NaN in every dtype: a slot read before it is written shows up
@@ -84,6 +87,10 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     for s in range(c.steps):
         tok = workloads.spec_tokens(c.seed, s, c.B, c.H, c.T, c.dv, c.dk, c.io_dt, c.a_lo, c.a_hi, c.form)
         full_forgetting(tok.lam, c.forget_every, s)
+        # grouped keys: the device takes one q and k per group (its first
+        # head's draw), the oracle every head's copy of its group's
+        qg, kg = tok.q[:, :, ::hg].contiguous(), tok.k[:, :, ::hg].contiguous()
+        tok.q, tok.k = qg.repeat_interleave(hg, dim=2), kg.repeat_interleave(hg, dim=2)
         force = np.zeros(c.B, np.uint8)
         if c.force_row0_every and (s + 1) % c.force_row0_every == 0 and 0 in live:
             force[0] = 1
@@ -94,7 +101,7 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
         dh, dflag = d.device_committed()
         assert np.array_equal(dh[live], h[live]), f"device committed counts, step {s}"
         assert np.array_equal(dflag[live].astype(bool), fl[live].astype(bool)), f"device flags, step {s}"
-        q, k, v = (_device(t, c.strided, dev) for t in (tok.q, tok.k, tok.v))
+        q, k, v = (_device(t, c.strided, dev) for t in (qg, kg, tok.v))
         lam = tok.lam.to(dev)
         beta = tok.beta.to(dev) if tok.beta is not None else None
         out = torch.full((c.B, c.T, c.H, c.dv), float("nan"), device=dev)
@@ -114,12 +121,15 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
         for b in c.pad_rows:
             assert torch.isnan(out[b]).all(), f"padding row {b} written, step {s}"
         blk = torch.as_tensor(blocks[sample], device=dev, dtype=torch.long)
-        # drafts stored as records from slot (flushed ? 0 : h)
+        # drafts stored as records from slot (flushed ? 0 : h); with grouped
+        # keys, a flushing row's keys from the staging slot L until the commit
         base = np.where(fl[sample] != 0, 0, h[sample])
+        kbase = np.where(fl[sample] != 0, c.L, h[sample]) if hg > 1 else base
         for i_row, b in enumerate(sample):
             sl = torch.arange(int(base[i_row]), int(base[i_row]) + c.T, device=dev)
-            got_k = d.pool.rec_k()[blk[i_row], :, sl].cpu()          # [H, T, dk]
-            assert torch.equal(got_k, tok.k[b].transpose(0, 1).to(rdt)), f"k records, row {b}, step {s}"
+            ksl = torch.arange(int(kbase[i_row]), int(kbase[i_row]) + c.T, device=dev)
+            got_k = d.pool.rec_k()[blk[i_row], :, ksl].cpu()         # [G, T, dk]
+            assert torch.equal(got_k, kg[b].transpose(0, 1).to(rdt)), f"k records, row {b}, step {s}"
             got_v = d.pool.rec_x()[blk[i_row], :, sl].cpu()
             if c.form == rs.MAMBA2:
                 assert torch.equal(got_v, tok.v[b].transpose(0, 1).to(rdt)), f"v records, row {b}, step {s}"
@@ -135,6 +145,12 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
         a = workloads.spec_accepted(c.seed, s, c.B, c.T, c.accept)
         a[c.pad_rows] = 0
         d.commit(torch.from_numpy(a).to(dev))
+        if hg > 1:  # the commit moved a flushed row's accepted keys to slots 0 .. a - 1
+            for i_row, b in enumerate(sample):
+                if fl[b] and a[b]:
+                    got_k = d.pool.rec_k()[blk[i_row], :, :int(a[b])].cpu()
+                    assert torch.equal(got_k, kg[b, :int(a[b])].transpose(0, 1).to(rdt)), \
+                        f"committed keys of flushed row {b}, step {s}"
         spec.commit(a[sample])
         ref.commit(a[sample])
         rs.rs_spec_meta_advance(c.L, c.T, h, fl, a)

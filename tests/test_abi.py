@@ -195,7 +195,7 @@ def test_spec_block_layout_ring_of_L():
 
 @pytest.mark.parametrize("bad,code", [
     (dict(spec_T=3), rs.RS_EUNSUPPORTED), (dict(spec_T=8, L=4), rs.RS_EINVAL),
-    (dict(spec_T=-1), rs.RS_EINVAL), (dict(spec_T=4, d_v=128, d_k=128), rs.RS_EUNSUPPORTED),   # Mamba-2
+    (dict(spec_T=-1), rs.RS_EINVAL),
     (dict(spec_T=4, form=rs.GDN, d_v=32, d_k=64), rs.RS_EUNSUPPORTED),
     (dict(spec_T=4, read_dtype="f16"), rs.RS_EUNSUPPORTED),
 ])
@@ -203,6 +203,13 @@ def test_spec_layer_validation(bad, code):
     with pytest.raises(rs.ReplaySSMError) as e:
         rs.block_layout(_c2(**bad))
     assert e.value.code == code and rs.last_error()
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+@pytest.mark.parametrize("state", ["f32", "f16"])
+def test_spec_layer_128x128_is_supported(form, state):
+    lay = rs.block_layout(_c2(spec_T=8, form=form, d_v=128, d_k=128, state_dtype=state))
+    assert lay.slots == 16
 
 
 def test_spec_device_calls_reject_bad_arguments_on_host():
@@ -296,9 +303,22 @@ def test_grouped_block_layout():
     assert per.rec_lam_off - per.rec_k_off == 16 * (lay.rec_lam_off - lay.rec_k_off)
 
 
+def test_grouped_speculative_block_layout():
+    """A speculative layer with 8 key groups: each group's key ring holds L
+    committed records plus T staging slots (the drafts of a row that flushed
+    in its verify, until the commit moves them); per-head keys need none."""
+    lay = rs.block_layout(_c2(n_groups=8, spec_T=4))
+    assert lay.slots == 16 and lay.key_slots == 20
+    assert lay.rec_lam_off == lay.rec_k_off + 8 * 20 * 128 * 2
+    per = rs.block_layout(_c2(spec_T=4))
+    assert per.key_slots == per.slots == 16
+    std = rs.block_layout(_c2(n_groups=8))
+    assert std.key_slots == std.slots == 15
+
+
 @pytest.mark.parametrize("bad,code", [
     (dict(n_groups=3), rs.RS_EINVAL), (dict(n_groups=-1), rs.RS_EINVAL),
-    (dict(n_groups=8, spec_T=4), rs.RS_EUNSUPPORTED),
+    (dict(n_groups=3, spec_T=4), rs.RS_EINVAL),
 ])
 def test_grouped_layer_validation(bad, code):
     with pytest.raises(rs.ReplaySSMError) as e:
@@ -316,6 +336,20 @@ def test_grouped_io_strides():
     with pytest.raises(rs.ReplaySSMError) as e:                    # k rows shorter than 8 groups
         rs.replay_decode_step(layer, batch, io, stream=0)
     assert "row strides" in rs.last_error()
+
+
+def test_grouped_speculative_io_strides():
+    """Draft q / k tokens of a grouped speculative layer hold n_groups
+    vectors (v tokens n_heads): a token stride of 7 groups is rejected."""
+    layer = _c2(n_groups=8, spec_T=4)
+    buf = (ctypes.c_uint8 * 1024)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    batch = rs.RsBatch(4, 0, 4, base, base, base, None, None, base + 256)
+    io = rs.RsSpecIO(base, base, base, 4 * 8 * 128, 8 * 128, 128, 4 * 7 * 128, 7 * 128, 128,
+                     4 * 128 * 64, 128 * 64, 64, base, base)
+    with pytest.raises(rs.ReplaySSMError) as e:
+        rs.replay_spec_verify(layer, batch, io, stream=0)
+    assert e.value.code == rs.RS_EINVAL and "k token stride" in rs.last_error()
 
 
 # ------------------------------------------------------ stochastic rounding --

@@ -1,4 +1,5 @@
 """bench.py's algorithmic byte accounting against the oracle's traffic model."""
+import numpy as np
 import pytest
 
 import bench
@@ -160,6 +161,36 @@ def test_counter_lineup():
         bench.line_up(rows, [("k_replay_step", "w0", 1.0)], scale)
 
 
+def test_suite_counters_are_stored(tmp_path, monkeypatch, capsys):
+    """A suite run's counters (speculative verify, layer stack) are stored in
+    counters.json under the suite's key, one entry per (kernel, case)."""
+    import csv
+    import json
+    monkeypatch.setattr(bench, "COUNTERS_PATH", str(tmp_path / "counters.json"))
+    key = bench.suite_key(bench.build_parser().parse_args(["--suite", "x", "--suite-only", "spec", "--spec-T", "8"]))
+    assert key == "suite-spec-T8-nemotron-gdn"
+    log = {"launches": [("k_spec_verify", "T=8 accept all", 3000.0), ("k_spec_commit", "commit", 10.0)],
+           "suite_key": key}
+    (tmp_path / "log.json").write_text(json.dumps(log))
+    for counter, vals in (("FETCH_SIZE", (2.0, 0.01)), ("WRITE_SIZE", (1.0, 0.0))):
+        with open(tmp_path / f"{counter}.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for i in range(3):
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": counter,
+                            "Counter_Value": 1024.0})
+            w.writerow({"Dispatch_Id": 5, "Kernel_Name": "void rs::k_spec_verify<64>(rs::StepParams)",
+                        "Counter_Name": counter, "Counter_Value": vals[0]})
+            w.writerow({"Dispatch_Id": 6, "Kernel_Name": "void rs::k_spec_commit(rs::StepParams)",
+                        "Counter_Name": counter, "Counter_Value": vals[1]})
+    assert bench.main(["--summarize-counters", str(tmp_path / "FETCH_SIZE.csv"), str(tmp_path / "WRITE_SIZE.csv"),
+                       "--calibrate-copy", "1", "--launch-log", str(tmp_path / "log.json")]) == 0
+    entry = json.load(open(tmp_path / "counters.json"))[key]
+    assert entry["kernel_source"] == bench.kernel_source_hash()
+    v = entry["by_label"]["k_spec_verify T=8 accept all"]
+    assert (v["fetch"], v["write"], v["total"], v["algorithmic"], v["ratio"]) == (2048, 1024, 3072, 3000, 1.024)
+
+
 def test_trace_summary_per_cursor(tmp_path, capsys):
     """--summarize-trace lines the kernel trace up with the launch log and
     averages each cursor position first, then the window."""
@@ -187,3 +218,21 @@ def test_trace_summary_per_cursor(tmp_path, capsys):
     assert by[("k_conventional_step", "conventional")]["us_mean"] == 7.0
     win = by[("k_replay_step", "window average over cursors")]
     assert win["us"] == 22.5 and win["bytes"] == 200
+
+
+def test_grouped_spec_step_bytes():
+    """Grouped keys: a group's key records and draft q, k are counted once,
+    and the commit moves each flushed row's accepted keys (read + write per
+    group); per-head keys move nothing."""
+    H, G, dv, dk, B, T = 128, 8, 64, 128, 2, 4
+    h = np.array([3, 14])
+    fl = np.array([False, True])
+    a = np.array([2, 3])
+    per = bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0)
+    grp = bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0, G, a)
+    shared = (H - G) * (int(h.sum()) * dk * 2 + B * T * (dk * 2 + 2 * dk * 2))
+    moved = 2 * G * dk * 2 * 3          # row 1 flushed with 3 accepted drafts
+    assert grp == per - shared + moved
+    assert bench.spec_commit_key_bytes(dk, "f16", fl, a, G) == moved
+    with pytest.raises(ValueError):
+        bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0, G)

@@ -262,19 +262,24 @@ def test_stack_of_40_layers(L, state_dt):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("form,shape", [(rs.MAMBA2, (16, 32)), (rs.MAMBA2, (64, 128)), (rs.GDN, (128, 128))])
-def test_token_less_flush_of_speculative_layer(form, shape):
+@pytest.mark.parametrize("form,shape,groups", [(rs.MAMBA2, (16, 32), 0), (rs.MAMBA2, (64, 128), 0),
+                                               (rs.GDN, (128, 128), 0), (rs.MAMBA2, (16, 32), 2),
+                                               (rs.GDN, (64, 128), 2)])
+def test_token_less_flush_of_speculative_layer(form, shape, groups):
     """replay_flush on a speculative layer (a ring of L committed records):
     after verify + commit steps with random acceptance, every row's h
     committed records are folded into its checkpoint, which must equal the
     committed state (the oracle, token by token).  At 64 x 128 with fp16
-    records and L = 16 the flush's LDS holds L (not L - 1) record slots."""
+    records and L = 16 the flush's LDS holds L (not L - 1) record slots.
+    With grouped keys (4 heads in 2 groups) the flush reads each group's
+    keys, which the commits of flushed rows moved out of the staging slots."""
     from linear_attention_decode_replay_amd.state import SpecDecodeLayer
     dv, dk = shape
-    B, H, L, T = 3, 2, 16, 4
+    B, H, L, T = 3, 4 if groups else 2, 16, 4
+    hg = H // groups if groups else 1
     lowp = shape != (16, 32)
     rdt, io = ("f16", "bf16") if lowp else ("f32", "f32")
-    lay = rs.layer(form, H, dv, dk, L, "f32", rdt, io, None, T)
+    lay = rs.layer(form, H, dv, dk, L, "f32", rdt, io, None, T, groups)
     d = SpecDecodeLayer(lay, B, B + 1, DEV)
     d.pool.raw.fill_(0xFF)
     for b in range(B):
@@ -284,8 +289,10 @@ def test_token_less_flush_of_speculative_layer(form, shape):
     h = np.zeros(B, np.int32)
     for s in range(7):
         tok = workloads.spec_tokens(91, s, B, H, T, dv, dk, io, 0.05, 1.0, form)
+        qg, kg = tok.q[:, :, ::hg].contiguous(), tok.k[:, :, ::hg].contiguous()
+        tok.q, tok.k = qg.repeat_interleave(hg, dim=2), kg.repeat_interleave(hg, dim=2)
         fl = rs.rs_spec_meta_step(L, T, h)
-        q, k, v, lam = (x.to(DEV) for x in (tok.q, tok.k, tok.v, tok.lam))
+        q, k, v, lam = (x.to(DEV) for x in (qg, kg, tok.v, tok.lam))
         beta = tok.beta.to(DEV) if tok.beta is not None else None
         out = torch.empty((B, T, H, dv), device=DEV)
         d.verify(rs.make_spec_io(q, k, v, lam, out, beta))

@@ -22,6 +22,11 @@ def _check(err, tol):
     assert err["ckpt_flush"] <= tol, err
 
 
+def _check_gdn(err, tol):
+    _check(err, tol)
+    assert err["rec_u"] <= tol, err   # the drafts' corrected values, stored as records
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 8])
 def test_spec_tiny_fp32(T):
     """Tiny shapes, everything fp32, random accepted counts 0..T, L = 8."""
@@ -108,10 +113,46 @@ def test_spec_layer_rejects_standard_step():
     assert e.value.code == rs.RS_EINVAL
 
 
+@pytest.mark.parametrize("state_dt,T", [("f32", 4), ("f16", 4), ("f32", 8)])
+def test_spec_mamba2_128x128(state_dt, T):
+    """Mamba-2 with 128 x 128 heads in one workgroup per tile: batch 32,
+    16 heads, L = 16, bf16 inputs, fp16 records; 3 rows sampled."""
+    err = run_spec_case(SpecCase(B=32, H=16, dv=128, dk=128, L=16, T=T, steps=16, state_dt=state_dt, rec_dt="f16",
+                                 io_dt="bf16", sample=[0, 17, 31], seed=41 + T))
+    assert err["flushes"] >= 1
+    _check(err, TOL_LOW)
+
+
+@pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
+@pytest.mark.parametrize("T", [2, 4])
+def test_spec_grouped_keys_tiny(form, T):
+    """Keys and queries shared by pairs of heads (4 heads, 2 groups), fp32,
+    random acceptance with forced flushes: the group's first head stores the
+    draft keys, a flushing row's in the staging slots until the commit moves
+    the accepted ones to slot 0; every head reads its group's keys."""
+    err = run_spec_case(SpecCase(form=form, B=3, H=4, L=8, T=T, steps=40, groups=2, force_row0_every=5,
+                                 seed=60 + T))
+    assert err["flushes"] >= 3
+    (_check_gdn if form == rs.GDN else _check)(err, TOL_F32)
+
+
+@pytest.mark.parametrize("form,H,groups,shape,T,state_dt", [
+    (rs.MAMBA2, 16, 2, (64, 128), 8, "f32"),     # 8 heads per group, as the released Nemotron-H layout
+    (rs.MAMBA2, 16, 2, (64, 128), 4, "f16"),
+    (rs.GDN, 8, 4, (128, 128), 4, "f32"),
+])
+def test_spec_grouped_keys(form, H, groups, shape, T, state_dt):
+    """Grouped keys at full head sizes: batch 32, L = 16, bf16 inputs,
+    fp16 records, strided inputs and a padding row; 3 rows sampled."""
+    dv, dk = shape
+    err = run_spec_case(SpecCase(form=form, B=32, H=H, dv=dv, dk=dk, L=16, T=T, steps=16, groups=groups,
+                                 state_dt=state_dt, rec_dt="f16", io_dt="bf16", strided=True, pad_rows=[5],
+                                 sample=[0, 17, 31], seed=70 + T))
+    assert err["flushes"] >= 1
+    (_check_gdn if form == rs.GDN else _check)(err, TOL_LOW)
+
+
 # ------------------------------------------------------- Gated DeltaNet form --
-def _check_gdn(err, tol):
-    _check(err, tol)
-    assert err["rec_u"] <= tol, err   # the drafts' corrected values, stored as records
 
 
 @pytest.mark.parametrize("T", [1, 2, 4, 8])
