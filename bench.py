@@ -772,11 +772,15 @@ def suite_continuous(out, steps=200, n_layers=4):
                     w = wp[live]
                     # a zero checkpoint is not read (its flush still writes it)
                     ck_read = np.where(zc[live], 0, ms_state)
-                    nbytes += n_layers * float(np.sum(H * (ck_read + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
-                    nbytes += n_layers * 4.0 * int((~live).sum())
+                    nb = float(np.sum(H * (ck_read + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
+                    nb += 4.0 * int((~live).sum())
                 else:
                     d.conventional_step(step_ios, events=pairs)
-                    nbytes += n_layers * (float(live.sum()) * (H * (2 * ms_state + io_b) + 4) + 4.0 * int((~live).sum()))
+                    nb = float(live.sum()) * (H * (2 * ms_state + io_b) + 4) + 4.0 * int((~live).sum())
+                nbytes += n_layers * nb
+                for _ in range(n_layers):
+                    log_launch("k_replay_step" if kind == "replay" else "k_conventional_step",
+                               f"continuous {kind}" + (" (events per launch)" if per_launch_events else ""), nb)
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record()
             torch.cuda.synchronize()

@@ -206,6 +206,19 @@ def test_grouped_keys_gdn_production():
              sample=[0, 15], seed=74))
 
 
+@pytest.mark.parametrize("name,case", [
+    ("mamba2-groups-of-4", dict(B=7, H=8, groups=2)),                       # 56 tiles: 32 mapped, 24 in the tail
+    ("gdn-128-fp32-parts", dict(form=rs.GDN, B=5, H=3, dv=128, dk=128)),     # 30 half tiles: 16 mapped
+    ("gdn-128-fp32-groups", dict(form=rs.GDN, B=4, H=4, groups=2, dv=128, dk=128)),  # units of 4: all mapped
+])
+def test_xcd_unit_map_covers_every_tile(name, case):
+    """Workgroups that share bytes (a tile's parts, a key group's heads)
+    are mapped to one XCD in blocks of 8 units, with the identity on a last
+    partial block: every row of the batch is checked, so a tile computed
+    twice or never shows up."""
+    _go(Case(L=4, steps=13, seed=75, **case))
+
+
 # ------------------------------------------ GDN state-reconstruction route --
 @pytest.mark.parametrize("L", [1, 4, 16])
 def test_gdn_reconstruct_tiny(L):
