@@ -32,9 +32,6 @@ struct StepParams {
     const float* beta;
     float* out;
     int32_t n_rows, n_heads, L, slots;
-    int32_t key_slots;         // key record slots per group (slots, or L + T on a
-                               // speculative layer with grouped keys)
-    int32_t key_bytes;         // bytes of one key record (d_k * record size)
     int32_t heads_per_group;   // heads sharing one key / query (1: per-head keys)
     int32_t sr;                // stochastic rounding of 16-bit state stores
     int32_t reconstruct;       // Gated DeltaNet: rebuild S_{t-1} on every step
@@ -48,6 +45,9 @@ struct StepParams {
     int64_t qs_t, ks_t, vs_t;  // token strides (elements)
     const int32_t* accepted;   // commit: drafts accepted per row
     uint8_t* next_flush;       // commit: next step's flag per row
+    int32_t key_slots;         // key record slots per group (slots, or L + T on a
+                               // speculative layer with grouped keys)
+    int32_t key_bytes;         // bytes of one key record (d_k * record size)
 };
 
 enum class Kind { ReplayStep, ConventionalStep, Flush, Reset, SpecVerify, SpecCommit };

@@ -887,7 +887,8 @@ struct TilePtrs {
         // keys and queries per group of heads_per_group heads (1: per head)
         const int grp = id.head / p.heads_per_group;
         key_owner = id.head == grp * p.heads_per_group;
-        rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.key_slots * DK;
+        // (the step kernels run standard layers only, where key_slots == slots)
+        rk = reinterpret_cast<R*>(base + p.reck_off) + (int64_t)grp * p.slots * DK;
         rl = reinterpret_cast<float*>(base + p.reclam_off) + (int64_t)id.head * p.slots;
         qp = static_cast<const I*>(p.q) + id.row * p.qs_r + grp * p.qs_h;
         kp = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
@@ -1411,7 +1412,7 @@ __device__ __forceinline__ void drain_deferred(const StepParams& p, char* dbase,
         } else if (j < OCH + KCH) {
             const int grp = head / p.heads_per_group;
             if (part == 0 && head == grp * p.heads_per_group) {
-                R* rk = reinterpret_cast<R*>(base + p.reck_off) + ((int64_t)grp * p.key_slots + w) * DK;
+                R* rk = reinterpret_cast<R*>(base + p.reck_off) + ((int64_t)grp * p.slots + w) * DK;
                 st_stream(reinterpret_cast<u32x4*>(rk) + (j - OCH), reinterpret_cast<const u32x4*>(df.k)[j - OCH]);
             }
         } else if (j < OCH + KCH + XCH) {
@@ -2929,6 +2930,30 @@ struct Dispatch {
                                                         hipLaunchKernelGGL(fn, dim3(ps.grid), dim3(NT), ps.lds, stream, q);
                                                         return;
                                                     }
+                                                }
+                                            }
+                                            // A step where every row flushes, with one fp32
+                                            // checkpoint, runs its tiles in twice as many parts:
+                                            // each workgroup folds half the rows, so the fold's
+                                            // arithmetic hides behind more loads in flight.
+                                            // Measured on MI355X at batch 256 (outputs and
+                                            // checkpoints bit-identical): the Nemotron-3-Super
+                                            // layer's flush step 429.9 -> 393.7 us, grouped keys
+                                            // 393.5 -> 372.2, Gated DeltaNet 128 x 128 206.4 ->
+                                            // 191.8; with an fp16 state (123.1 -> 126.7) or an
+                                            // E4M3 read copy (458.8 -> 467.4) it is slower.
+                                            if constexpr (!TWO && std::is_same<TS, tF32>::value &&
+                                                          tile_ok<DV, DK, TL, 2 * SP>()) {
+                                                if (hint == RS_FLUSH_ALL) {
+                                                    constexpr int FSP = 2 * SP;
+                                                    StepParams q = *p;
+                                                    q.flush_hint = RS_FLUSH_UNKNOWN;
+                                                    const dim3 fg = this->template grid<FSP>();
+                                                    const dim3 fb(Tile<DV, DK, TL, FSP>::NT);
+                                                    const size_t fl_lds = lds_need<DV / FSP, DK, R>(slots, L.L);
+                                                    hipLaunchKernelGGL((k_replay_step<FORM, DV, DK, TS, TR, TI, FSP, TL>), fg, fb,
+                                                                       fl_lds, stream, q);
+                                                    return;
                                                 }
                                             }
                                             if constexpr (!TWO) {
