@@ -621,7 +621,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
             else:
                 d.conventional_step(ios[s % 16])
                 w, f = 0, False
-            log_launch("k_replay_step" if kind == "replay" else "k_conventional_step", f"spec reference {kind}",
+            log_launch("k_replay_step" if kind == "replay" else "k_conventional_step", f"{workload} reference {kind}",
                        step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind, groups=groups))
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
@@ -671,11 +671,11 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                     n_flush += int(fl.sum())
                 d.verify(drafts[s % 8][1])
                 d.commit(acc[s % steps])
-                log_launch("k_spec_verify" if form == 0 else "k_spec_verify_gdn", f"T={T} accept {policy}",
-                           nb - B * 18 - moved)
+                label = f"{workload} T={T} accept {policy}"
+                log_launch("k_spec_verify" if form == 0 else "k_spec_verify_gdn", label, nb - B * 18 - moved)
                 if hg > 1:
-                    log_launch("k_spec_commit_keys", f"T={T} accept {policy}", moved)
-                log_launch("k_spec_commit", f"T={T} accept {policy}", B * 18)
+                    log_launch("k_spec_commit_keys", label, moved)
+                log_launch("k_spec_commit", label, B * 18)
                 rs.rs_spec_meta_advance(L, T, hm, fl, a)
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record()
