@@ -802,13 +802,18 @@ __device__ __forceinline__ void store_f(typename T::S* __restrict__ p, const flo
 // second alone; RS_FLUSH_MIXED: the second over the rows that do not flush,
 // then the first over those that do) and decides what a row that breaks it
 // means: skipped, and counted as an error.
-constexpr int kAllRows = 0, kNonFlushRows = 1;
+// kNonFlushRowsLong: the same without the fold, staging the records in 3
+// chunks per thread instead of 2 (the persistent form copies them in one
+// pass: rings of up to 32 records at 64 x 128 with fp16 records).
+constexpr int kAllRows = 0, kNonFlushRows = 1, kNonFlushRowsLong = 2;
+constexpr bool nonflush_rows(int rows) { return rows != kAllRows; }
+constexpr int record_chunks(int rows) { return rows == kNonFlushRowsLong ? 3 : 2; }
 constexpr int kMaxRecords = 63;  // a ring holds at most L - 1 <= 63 records
 // The instantiation without the fold gives each thread 4 read-copy chunks
 // (an E4M3 tile then takes 128 threads instead of 256): the fold's registers
 // are gone, and twice the bytes per wave are in flight.
 template <int DV, int DK, class TL, int SPLIT, int ROWS>
-using StepTile = Tile<DV, DK, TL, SPLIT, ROWS == kNonFlushRows ? 4 : 0>;
+using StepTile = Tile<DV, DK, TL, SPLIT, nonflush_rows(ROWS) ? 4 : 0>;
 
 // One non-flush tile's writes, held in LDS by a persistent workgroup until
 // its tiles are done (see k_replay_step): the owned output rows, the record
@@ -913,7 +918,7 @@ struct TileIn {
     typename TI::S vr;
     float lam, lam_j;
     float beta;  // Gated DeltaNet
-    RecordCopy<DV, DVW, DK, typename TR::S, NT, 2> rec;
+    RecordCopy<DV, DVW, DK, typename TR::S, NT, record_chunks(ROWS)> rec;
     float rsc[NR];  // scales of the owned read-copy rows (scaled formats)
     u32x4 cb[NR * HPC];
 };
@@ -942,7 +947,7 @@ __device__ __forceinline__ bool tile_runs(const StepParams& p, const TileIds& id
         return false;
     }
     const bool fl_row = (w == p.slots) || flag;
-    if constexpr (ROWS == kNonFlushRows) {
+    if constexpr (nonflush_rows(ROWS)) {
         if (fl_row) {
             if (p.flush_hint == RS_FLUSH_NONE) error();  // the hint was wrong
             return false;
@@ -972,7 +977,7 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
     constexpr int LPR = T::LPR, RPP = T::RPP, NR = T::NR, DVW = T::DVW;
     constexpr bool SC = kScaled<TL>;
     constexpr int HPC = In::HPC, EPC = In::EPC;
-    static_assert(!UNCOND || ROWS == kNonFlushRows, "unconditional loads: non-flush tiles only");
+    static_assert(!UNCOND || nonflush_rows(ROWS), "unconditional loads: non-flush tiles only");
 
     in.id = id;
     in.blk = blk;
@@ -1059,7 +1064,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     constexpr bool SC = kScaled<TL>;                // read copy with per-row scales
     constexpr int HPC = In::HPC, EPC = In::EPC;
 
-    static_assert(!DEFER || ROWS == kNonFlushRows, "deferred writes: non-flush rows only");
+    static_assert(!DEFER || nonflush_rows(ROWS), "deferred writes: non-flush rows only");
     using D = Deferred<DVW, DK, R>;
     D df(dslot);
     if (!in.run) {
@@ -1125,7 +1130,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
         }
     };
     const float lam_j = in.lam_j;
-    RecordCopy<DV, DVW, DK, R, T::NT, 2> rec = in.rec;
+    auto rec = in.rec;
     float rsc[NR];
     u32x4 cb[NR * HPC];
 #pragma unroll
@@ -1145,7 +1150,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     // step does not read) and takes this lane's share of k . q now, so that
     // k is not held through the checkpoint products.
     float kq_lane = 0.f;
-    if constexpr (ROWS == kNonFlushRows) {
+    if constexpr (nonflush_rows(ROWS)) {
 #pragma unroll
         for (int c = 0; c < VEC; ++c) kq_lane += kv[c] * qv[c];
         append_record(w);
@@ -1168,12 +1173,12 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
         if (j < wd) {
 #pragma unroll
             for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(s.k + (int64_t)j * DK + col(h), kj + h * EPC);
-        } else if constexpr (ROWS != kNonFlushRows) {
+        } else if constexpr (!nonflush_rows(ROWS)) {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) kj[c] = kv[c];
         }
         float pq = 0.f, pk = 0.f;
-        if (ROWS == kNonFlushRows && j >= wd) {
+        if (nonflush_rows(ROWS) && j >= wd) {
             pq = kq_lane;
         } else {
 #pragma unroll
@@ -1201,7 +1206,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     if (!TWO || fl) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) unpack_n<TS, VEC>(&cb[r * HPC], cf[r]);
-    } else if constexpr (!(ROWS == kNonFlushRows && SC)) {
+    } else if constexpr (!(nonflush_rows(ROWS) && SC)) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) unpack_n<TL, VEC>(&cb[r * HPC], cf[r]);
     }
@@ -1229,7 +1234,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         float a = 0.f, b = 0.f;
-        if constexpr (ROWS == kNonFlushRows && SC) {
+        if constexpr (nonflush_rows(ROWS) && SC) {
             // codes widened four at a time straight into the product, so
             // that the tile is never held as floats
 #pragma unroll
@@ -1313,7 +1318,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     }
 
     if (!fl) {  // uniform across the workgroup
-        if constexpr (ROWS != kNonFlushRows) append_record(w);  // (else appended above)
+        if constexpr (!nonflush_rows(ROWS)) append_record(w);  // (else appended above)
         return;
     }
 
@@ -2910,25 +2915,31 @@ struct Dispatch {
                                                 FORM == kMamba2 && !TWO && std::is_same<TS, tF32>::value;
                                             if constexpr (persist_form) {
                                                 if (hint == RS_FLUSH_NONE && p->heads_per_group == 1) {
+                                                    // It copies the records to LDS in one pass: 2 chunks
+                                                    // per thread, or 3 for longer rings (kNonFlushRowsLong).
                                                     constexpr int NT = StepTile<DV, DK, TL, SP, kNonFlushRows>::NT;
-                                                    const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
-                                                                                  kNonFlushRows, true>;
-                                                    // (it copies the records to LDS in one pass:
-                                                    // 2 chunks per thread)
+                                                    static_assert(NT == StepTile<DV, DK, TL, SP, kNonFlushRowsLong>::NT, "");
                                                     constexpr int rec_chunks = (DK + DV / SP) * (int)sizeof(R) / 16;
-                                                    const PersistShape ps =
-                                                        slots * rec_chunks <= 2 * NT
-                                                            ? persist_shape(reinterpret_cast<const void*>(fn), NT, lds,
-                                                                            Deferred<DV / SP, DK, R>::BYTES,
-                                                                            (int64_t)p->n_rows * p->n_heads * SP)
-                                                            : PersistShape{};
-                                                    if (ps.grid) {
+                                                    auto run = [&](auto rows_c) {
+                                                        constexpr int ROWSP = decltype(rows_c)::value;
+                                                        const auto fn = k_replay_step<FORM, DV, DK, TS, TR, TI, SP, TL, false,
+                                                                                      ROWSP, true>;
+                                                        const PersistShape ps =
+                                                            persist_shape(reinterpret_cast<const void*>(fn), NT, lds,
+                                                                          Deferred<DV / SP, DK, R>::BYTES,
+                                                                          (int64_t)p->n_rows * p->n_heads * SP);
+                                                        if (!ps.grid) return false;
                                                         StepParams q = *p;
                                                         q.meta_off = ps.meta_off;
                                                         q.defer_off = ps.defer_off;
                                                         q.defer_cap = ps.defer_cap;
                                                         hipLaunchKernelGGL(fn, dim3(ps.grid), dim3(NT), ps.lds, stream, q);
-                                                        return;
+                                                        return true;
+                                                    };
+                                                    if (slots * rec_chunks <= record_chunks(kNonFlushRows) * NT) {
+                                                        if (run(std::integral_constant<int, kNonFlushRows>{})) return;
+                                                    } else if (slots * rec_chunks <= record_chunks(kNonFlushRowsLong) * NT) {
+                                                        if (run(std::integral_constant<int, kNonFlushRowsLong>{})) return;
                                                     }
                                                 }
                                             }

@@ -327,6 +327,16 @@ def test_persistent_step_item_counts(B, H, pad, force):
              pad_rows=pad, force_every=force, check_conventional=False, seed=81 + B))
 
 
+@pytest.mark.parametrize("rec_dt,L", [("f16", 32), ("f32", 16)])
+def test_persistent_step_long_ring(rec_dt, L):
+    """Rings whose records take 3 chunks per thread to stage (31 fp16
+    records, or 15 fp32 records, of a 64 x 128 head) run the persistent
+    non-flush form's long-ring instantiation: 17 rows x 128 heads (4 or 5
+    tiles per workgroup), two windows and a flush."""
+    _go(Case(B=17, H=128, dv=64, dk=128, L=L, steps=2 * L + 3, state_dt="f32", rec_dt=rec_dt, io_dt="bf16",
+             sample=[0, 9, 16], check_conventional=False, seed=95 + L))
+
+
 @pytest.mark.parametrize("name,case", [
     ("mamba2-tiny", dict()),
     ("gdn-tiny", dict(form=rs.GDN)),
