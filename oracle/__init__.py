@@ -463,6 +463,44 @@ class SpecReplayModel:
         return self.C.reshape(self.B, self.H, self.dv, self.dk)
 
 
+class SpecTwoCopyModel(SpecReplayModel):
+    """Speculative verify over a two-precision checkpoint (blog, "The
+    precision argument, derived", and "Speculative decoding: rollback becomes
+    a pointer"), Mamba-2 form: a row that does not flush reads the read copy
+    C_lo for its outputs; a flushing row folds its committed records into the
+    recurrence copy C (exact, fp64) and computes its outputs from it, and the
+    read copy is then the same fold rounded to `read_dtype`
+    (formats.round_to: f16, bf16, or e4m3 with a power-of-two scale per
+    state row)."""
+
+    def __init__(self, B, H, dv, dk, L, T, read_dtype, oracle=None):
+        super().__init__(B, H, dv, dk, L, T, oracle, MAMBA2)
+        self.read_dtype = read_dtype
+        self.C_lo = np.zeros_like(self.C)
+
+    def verify(self, q, k, v, lam, flush_rows, active_rows=None, beta=None):
+        if beta is not None:
+            raise ValueError("two-precision checkpoints are Mamba-2 only")
+        B, H, T = self.B, self.H, self.T
+        n = B * H
+        fl = np.repeat(np.asarray(flush_rows, bool), H)
+        act = np.ones(n, bool) if active_rows is None else np.repeat(np.asarray(active_rows, bool), H)
+        f = lambda a, d: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T, d))
+        sc = lambda a: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T))
+        args = (f(q, self.dk), f(k, self.dk), f(v, self.dv), sc(lam))
+        # rows that do not flush: outputs from the read copy, drafts appended
+        out = self.o.spec_verify(self.C_lo, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, *args, act & ~fl)
+        # flushing rows: fold into the recurrence copy, outputs from it
+        out += self.o.spec_verify(self.C, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, *args, act & fl)
+        self.C_lo[act & fl] = round_to(self.C[act & fl], self.read_dtype)
+        return out.reshape(B, H, T, self.dv)
+
+    def fold(self, rows_mask):
+        super().fold(rows_mask)
+        mask = np.repeat(np.asarray(rows_mask, bool), self.H)
+        self.C_lo[mask] = round_to(self.C[mask], self.read_dtype)
+
+
 class SpecTokenByToken:
     """The definition a speculative verify must reproduce: the conventional
     recurrence run token by token.  The committed state S advances only by

@@ -528,6 +528,51 @@ def pin_spec_identity(orc):
         assert o < 1e-12 and st < 1e-12, (T, o, st)
 
 
+def pin_spec_two_copy(orc):
+    """[blog] "The precision argument, derived" with "Speculative
+    decoding": over a two-precision checkpoint, a flushing row's outputs come
+    from the exact recurrence copy (they equal the drafts run token by token
+    from the committed state), and afterwards the read copy is that fold
+    rounded to the read format; a row that does not flush reads the read
+    copy: right after a flush that committed nothing, its outputs equal the
+    drafts run token by token from the read copy.  f16 and E4M3, T = 2,
+    every third step forced to flush with nothing accepted."""
+    B, H, dv, dk, L, T = 2, 2, 8, 12, 8, 2
+    rng = np.random.default_rng(61)
+    for rd in ("f16", "e4m3"):
+        two = oracle.SpecTwoCopyModel(B, H, dv, dk, L, T, rd, oracle=orc)
+        ref = oracle.SpecTokenByToken(B, H, dv, dk, T, oracle=orc)
+        h = np.zeros(B, np.int32)
+        checked_lo = checked_fl = 0
+        shows = False
+        for s in range(24):
+            q, k, v, lam = _spec_tok(61, s, B, H, T, dv, dk)
+            forced = s % 3 == 1
+            fl = np.array([forced or orc.spec_cursor_run(L, T, int(h[b]), np.zeros(1, np.int32))[1][0]
+                           for b in range(B)], bool)
+            from_lo = None
+            if s % 3 == 2:  # after a forced flush that committed nothing: h = 0 on every row
+                assert not h.any() and not fl.any()
+                from_lo = oracle.SpecTokenByToken(B, H, dv, dk, T, S0=two.C_lo.copy(), oracle=orc).verify(q, k, v, lam)
+            o = two.verify(q, k, v, lam, fl)
+            o_exact = ref.verify(q, k, v, lam)
+            if fl.any():
+                assert _rel(o[fl], o_exact[fl]) < 1e-12, (rd, s)
+                C = two.checkpoint()[fl]
+                assert _rel(C, ref.state()[fl]) < 1e-12, (rd, s)
+                assert np.array_equal(two.C_lo.reshape(B, H, dv, dk)[fl], oracle.round_to(C, rd)), (rd, s)
+                checked_fl += 1
+            if from_lo is not None:
+                assert _rel(o, from_lo) < 1e-12, (rd, s)
+                shows = shows or _rel(o, o_exact) > 1e-6  # the read copy's rounding shows
+                checked_lo += 1
+            a = np.zeros(B, np.int32) if forced else rng.integers(0, T + 1, B).astype(np.int32)
+            two.commit(a)
+            ref.commit(a)
+            h = np.where(fl, 0, h) + a
+        assert checked_lo >= 6 and checked_fl >= 8 and shows, (rd, checked_lo, checked_fl, shows)
+
+
 def pin_spec_gdn_identity(orc):
     """[blog] "The delta-rule wrinkle" and "Speculative decoding": Gated
     DeltaNet drafts through the T x T triangular solve, from checkpoint plus
@@ -816,6 +861,7 @@ ALL_PINS = [
     pin_e4m3_spec_values,
     pin_read_rounding_within_half_ulp,
     pin_spec_identity,
+    pin_spec_two_copy,
     pin_spec_gdn_identity,
     pin_spec_gdn_T1_is_standard_decode,
     pin_spec_gdn_zero_beta,

@@ -191,6 +191,46 @@ def test_two_copy_mutant_is_caught(monkeypatch, kind):
     assert caught, f"two-copy mutant {kind} passed both pins"
 
 
+def _broken_spec_two_copy(kind):
+    """A SpecTwoCopyModel with one planted mistake (Python level)."""
+    import numpy as np
+    from oracle import MAMBA2, SpecTwoCopyModel, round_to
+
+    class Broken(SpecTwoCopyModel):
+        def verify(self, q, k, v, lam, flush_rows, active_rows=None, beta=None):
+            B, H, T = self.B, self.H, self.T
+            n = B * H
+            fl = np.repeat(np.asarray(flush_rows, bool), H)
+            act = np.ones(n, bool)
+            f = lambda a, d: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T, d))
+            sc = lambda a: np.ascontiguousarray(np.asarray(a, np.float64).reshape(n, T))
+            args = (f(q, self.dk), f(k, self.dk), f(v, self.dv), sc(lam))
+            if kind == "read_copy_refreshed_before_the_fold":
+                self.C_lo[fl] = round_to(self.C[fl], self.read_dtype)
+            read = self.C if kind == "nonflush_reads_recurrence_copy" else self.C_lo
+            fold = self.C_lo if kind == "flush_reads_read_copy" else self.C
+            out = self.o.spec_verify(read, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, *args, act & ~fl)
+            out += self.o.spec_verify(fold, self.rec_lam, self.rec_x, self.rec_k, self.h, fl, *args, act & fl)
+            if kind == "flush_reads_read_copy":
+                self.C[fl] = fold[fl]
+            if kind not in ("read_copy_not_refreshed", "read_copy_refreshed_before_the_fold"):
+                self.C_lo[fl] = round_to(self.C[fl], self.read_dtype)
+            return out.reshape(B, H, T, self.dv)
+
+    return Broken
+
+
+@pytest.mark.parametrize("kind", ["nonflush_reads_recurrence_copy", "flush_reads_read_copy",
+                                  "read_copy_not_refreshed", "read_copy_refreshed_before_the_fold"])
+def test_spec_two_copy_mutant_is_caught(monkeypatch, kind):
+    """Mistakes in which copy a speculative verify reads, or in when the read
+    copy is refreshed, must fail pin_spec_two_copy."""
+    import pins
+    monkeypatch.setattr(oracle, "SpecTwoCopyModel", _broken_spec_two_copy(kind))
+    with pytest.raises(AssertionError):
+        pins.pin_spec_two_copy(oracle.get())
+
+
 @pytest.mark.parametrize("kind", ["read_copy_from_rounded_recurrence", "recurrence_nearest_even",
                                   "recurrence_words_of_step_zero"])
 def test_two_copy_store_mutant_is_caught(monkeypatch, kind):
