@@ -548,7 +548,7 @@ def suite_stack(out, n_layers=40, quick=False):
             print(json.dumps(line), file=out, flush=True)
 
 
-def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0, groups=0, accepted=None):
+def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0, groups=0, accepted=None, read=None):
     """Algorithmic HBM bytes of one speculative verify launch (rows with h
     committed records, flushing or not) plus its commit launch.  Per (row,
     head): read the checkpoint and the h committed records, read T draft
@@ -559,14 +559,21 @@ def spec_step_bytes(H, dv, dk, B, T, state, rec, io, h, flush, form=0, groups=0,
     groups the key records and q, k inputs of a group are counted once,
     spread over its heads, and the commit moves each flushed row's accepted
     keys (`accepted`) out of the staging slots: read and write once per
-    group (see spec_commit_key_bytes)."""
+    group (see spec_commit_key_bytes).  With a two-precision checkpoint
+    (`read` = the read copy's dtype) a row that does not flush reads the read
+    copy; a flushing row reads the recurrence copy and writes both."""
     h = np.asarray(h)
     flush = np.asarray(flush, bool)
     hg = H // groups if groups else 1
     ms = dv * dk * _ES[state]
     r = (dv + dk / hg) * _ES[rec] + 4
     tok = (2 * dk / hg + dv) * _ES[io] + 4 + (4 if form == 1 else 0)  # q, k, v, log-decay (and beta)
-    per_head = ms + h * r + T * (tok + r + 4 * dv) + np.where(flush, ms, 0)
+    if read:
+        ml = read_copy_bytes(dv, dk, read)
+        ck = np.where(flush, ms + ms + ml, ml)
+    else:
+        ck = np.where(flush, ms + ms, ms)
+    per_head = ck + h * r + T * (tok + r + 4 * dv)
     moved = spec_commit_key_bytes(dk, rec, flush, accepted, groups) if hg > 1 else 0.0
     return float(np.sum(H * per_head + 9) + B * 18 + moved)
 
@@ -582,7 +589,7 @@ def spec_commit_key_bytes(dk, rec, flush, accepted, groups):
     return float(2 * groups * dk * _ES[rec] * np.sum(a))
 
 
-def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
+def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8), read=None):
     """Speculative verify at the Nemotron-3-Super layer shape (workload
     "nemotron-grouped": with its 8 key groups; "gdn": the Gated DeltaNet
     layer, 32 heads, 128 x 128), batch 256,
@@ -607,7 +614,9 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
     ios, keep = _inputs(base, B, 16, dev)
     ref_us = {}
     for kind in ("replay", "conventional"):
-        layers = _layer_stack(base, B, n_pools, dev)
+        # the reference replay step keeps the same read copy; the conventional one has one state copy
+        kread = read if kind == "replay" else None
+        layers = _layer_stack(dict(base, read=kread), B, n_pools, dev)
         n_warm, n_time = L * n_pools, 2 * L * n_pools
         for s in range(n_warm + n_time):
             if s == n_warm:
@@ -622,7 +631,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 d.conventional_step(ios[s % 16])
                 w, f = 0, False
             log_launch("k_replay_step" if kind == "replay" else "k_conventional_step", f"{workload} reference {kind}",
-                       step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind, groups=groups))
+                       step_bytes(form, H, dv, dk, B, "f32", base["rec"], base["io"], w, f, kind, kread, groups))
         e1 = torch.cuda.Event(enable_timing=True)
         e1.record()
         torch.cuda.synchronize()
@@ -631,7 +640,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
         torch.cuda.empty_cache()
     del ios, keep
     for T in Ts:
-        lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", None, T, groups)
+        lay = rs.layer(form, H, dv, dk, L, "f32", "f16", "bf16", read, T, groups)
         drafts = []
         for s in range(8):
             t = workloads.spec_tokens(11, s, B, H, T, dv, dk, "bf16", form=form)
@@ -663,7 +672,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 d, hm = pools[pi], hmirror[pi]
                 a = acc_host[s % steps]
                 fl = rs.rs_spec_meta_step(L, T, hm)
-                nb = spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form, groups, a)
+                nb = spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", hm, fl, form, groups, a, read)
                 moved = spec_commit_key_bytes(dk, "f16", fl, a, groups) if hg > 1 else 0.0
                 if s >= n_warm:
                     nbytes += nb
@@ -671,7 +680,7 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                     n_flush += int(fl.sum())
                 d.verify(drafts[s % 8][1])
                 d.commit(acc[s % steps])
-                label = f"{workload} T={T} accept {policy}"
+                label = f"{workload}{' read ' + read if read else ''} T={T} accept {policy}"
                 log_launch("k_spec_verify" if form == 0 else "k_spec_verify_gdn", label, nb - B * 18 - moved)
                 if hg > 1:
                     log_launch("k_spec_commit_keys", label, moved)
@@ -686,7 +695,8 @@ def suite_spec(out, steps=48, n_pools=4, workload="nemotron", Ts=(4, 8)):
                 raise RuntimeError(f"{errs} tiles or rows flagged by the speculative kernels' checks")
             gb = nbytes / steps / 1e9
             tok_per_row = tokens / steps / B
-            line = {"suite": "spec_verify", "workload": workload, "T": T, "accept": policy, "batch": B, "L": L,
+            line = {"suite": "spec_verify", "workload": workload, "read_copy": read, "T": T, "accept": policy,
+                    "batch": B, "L": L,
                     "us_per_step": round(us, 2), "gb_per_step": round(gb, 4), "tbs": round(gb / (us * 1e-6) / 1e3, 3),
                     "committed_tokens_per_row_step": round(tok_per_row, 3),
                     "flush_fraction": round(n_flush / (steps * B), 4),
@@ -899,6 +909,8 @@ def suite_key(args) -> str:
     parts = ["suite", args.suite_only or "all"]
     if args.suite_only == "spec":
         parts += [f"T{t}" for t in (args.spec_T or (4, 8))] + list(args.spec_workload or ["nemotron", "gdn"])
+        if args.read:
+            parts.append(f"read{args.read}")
     if args.suite_only == "stack" and args.stack_quick:
         parts.append("quick")
     return "-".join(str(x) for x in parts)
@@ -1043,7 +1055,8 @@ def build_parser():
     ap.add_argument("--L", type=int, default=None)
     ap.add_argument("--state", default=None, choices=["f32", "f16"])
     ap.add_argument("--read", default=None, choices=["f16", "bf16", "e4m3"],
-                    help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy")
+                    help="two-precision checkpoint (Mamba-2, fp32 state): dtype of the read copy (also for the "
+                         "Mamba-2 layers of --suite-only spec)")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="state stores: nearest even, or stochastic rounding (fp16 state)")
     ap.add_argument("--pools", type=int, default=None,
@@ -1099,7 +1112,8 @@ def main(argv=None):
                 suite_stack(out, quick=args.stack_quick)
             if args.suite_only in (None, "spec"):
                 for wl in args.spec_workload or ["nemotron", "gdn"]:
-                    suite_spec(out, workload=wl, Ts=tuple(args.spec_T or (4, 8)))
+                    suite_spec(out, workload=wl, Ts=tuple(args.spec_T or (4, 8)),
+                               read=args.read if wl != "gdn" else None)
             if args.suite_only in (None, "continuous"):
                 suite_continuous(out)
         print(open(args.suite).read(), end="")

@@ -90,9 +90,11 @@ typedef enum {
  *               speculative layer (blog "Speculative decoding: rollback
  *               becomes a pointer"): its ring holds up to L committed records
  *               and each step verifies T draft tokens per row with
- *               replay_spec_verify; replay_decode_step rejects it.  Single
- *               fp32 or fp16 checkpoint; keys per head or grouped
- *               (n_groups); (d_v, d_k) = (16, 32), (64, 128) or (128, 128).
+ *               replay_spec_verify; replay_decode_step rejects it.  An
+ *               fp32 or fp16 checkpoint, or (Mamba-2) an fp32 recurrence
+ *               copy with an RS_F16, RS_BF16 or RS_E4M3 read copy; keys per
+ *               head or grouped (n_groups); (d_v, d_k) = (16, 32),
+ *               (64, 128) or (128, 128) (an E4M3 read copy: not 16 x 32).
  * n_groups:     0 or n_heads for a key and a query per head.  A divisor
  *               G < n_heads shares one key and one query among each run of
  *               n_heads / G consecutive heads, the released grouped-key
@@ -416,7 +418,11 @@ int rs_meta_advance(int32_t L, int32_t n_rows, int32_t* steps_since_anchor, cons
  * the checkpoint, which is written once, and the drafts are stored from slot
  * 0 (with grouped keys, the drafts' keys go to the staging slots L..L+T-1
  * until the commit; see key_slots).  This needs no acceptance count, so it
- * happens in the same launch.
+ * happens in the same launch.  With a two-precision checkpoint a row that
+ * does not flush reads the read copy (and its row scales) for the C q_i
+ * term, and a flushing row reads the recurrence copy, folds in fp32 and
+ * rewrites both copies from the same unrounded values, as in
+ * replay_decode_step.
  * After sampling, replay_spec_commit advances each row's committed count by
  * the number of drafts accepted; records past it are never read and get
  * overwritten.

@@ -93,8 +93,9 @@ int check_layer(const rs_layer* L, rs::Kind kind) {
         if (T < 1 || T > L->L) return fail(RS_EINVAL, "spec_T must be in 1..L (got %d, L=%d)", T, L->L);
         if (T != 1 && T != 2 && T != 4 && T != 8)
             return fail(RS_EUNSUPPORTED, "spec_T must be 1, 2, 4 or 8 (got %d)", T);
-        if (two_precision(*L))
-            return fail(RS_EUNSUPPORTED, "speculative verify: single checkpoint only (no read copy)");
+        if (two_precision(*L) && (L->form != RS_MAMBA2 || L->state_dtype != RS_F32))
+            return fail(RS_EUNSUPPORTED, "speculative verify with a read copy: Mamba-2 with an fp32 recurrence "
+                                         "copy only");
         if (kind == rs::Kind::ReplayStep)
             return fail(RS_EINVAL, "a speculative layer (spec_T=%d) is stepped with replay_spec_verify", T);
     } else if (spec_kind) {

@@ -1880,12 +1880,77 @@ struct Raw4 {
     }
 };
 
-template <int DV, int DK, class TS, class TR, class TI, int T>
+// Four consecutive elements of a read copy: 8 bytes of fp16 / bf16, or 4
+// bytes of E4M3 codes whose row scale the caller applies (speculative verify
+// over a two-precision checkpoint, one lane's four columns of a row).
+template <class TL>
+struct Quad {
+    using RL = typename TL::S;
+    using W = typename std::conditional<sizeof(RL) == 2, u32x2, uint32_t>::type;
+    W w;
+    __device__ __forceinline__ void load(const RL* p) { w = __builtin_nontemporal_load(reinterpret_cast<const W*>(p)); }
+    __device__ __forceinline__ void to(float* out, float scale) const {
+        if constexpr (kScaled<TL>) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+            out[0] = lo[0] * scale;
+            out[1] = lo[1] * scale;
+            out[2] = hi[0] * scale;
+            out[3] = hi[1] * scale;
+        } else {
+            RL tmp[4];
+            __builtin_memcpy(tmp, &w, sizeof(tmp));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = to_f<TL>(tmp[i]);
+        }
+    }
+};
+
+// Store four values of a read-copy row, rounded to nearest even; E4M3: the
+// row (G lanes, 4 values each) shares one power-of-two scale, chosen as in
+// encode_e4m3_row, which lane 0 of the group stores.
+template <class TL, int G>
+__device__ __forceinline__ void store_read_quad(const float* x, typename TL::S* dst, float* scale, int lane_in_row) {
+    using W = typename Quad<TL>::W;
+    W w;
+    if constexpr (kScaled<TL>) {
+        float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+        group_max<G>(amax);
+        const uint32_t b = __float_as_uint(amax);
+        int e = (int)((b >> 23) & 0xffu) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+        e = max(e, -100);
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[0], -e), __builtin_amdgcn_ldexpf(x[1], -e), 0,
+                                                false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[2], -e), __builtin_amdgcn_ldexpf(x[3], -e), c, true);
+        w = (uint32_t)c;
+        if (lane_in_row == 0) st_nt(scale, __builtin_amdgcn_ldexpf(1.0f, e));
+    } else {
+        typename TL::S tmp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmp[i] = from_f<TL>(x[i]);
+        __builtin_memcpy(&w, tmp, sizeof(tmp));
+    }
+    __builtin_nontemporal_store(w, reinterpret_cast<W*>(dst));
+}
+
+// TL != TS: a two-precision checkpoint (fp32 recurrence copy TS, read copy
+// TL; blog "The precision argument, derived").  A row that does not flush
+// reads only the read copy for its outputs; a flushing row reads the
+// recurrence copy, folds in fp32 and stores both copies from the same
+// unrounded values.  The read copy keeps the lane order of the standard
+// step's layout (rs_block_layout): this lane's four columns 4 cc .. 4 cc + 3
+// sit at position n (cc mod (DK / n)) + 4 (cc div (DK / n)) of the row, n
+// read elements per 16 bytes.
+template <int DV, int DK, class TS, class TR, class TI, int T, class TL = TS>
 __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const StepParams p) {
     using Tl = Tile<DV, DK, TS, 1>;
     using S = typename TS::S;
     using R = typename TR::S;
     using I = typename TI::S;
+    using RL = typename TL::S;
+    constexpr bool TWO = !std::is_same<TS, TL>::value;
+    constexpr bool SC = kScaled<TL>;
+    static_assert(!TWO || std::is_same<TS, tF32>::value, "a read copy under an fp32 recurrence copy");
     constexpr int NT = Tl::NT, VEC = Tl::VEC, LPR = Tl::LPR, RPP = Tl::RPP, NR = Tl::NR;
     constexpr int NV = T * NR;                        // partial sums per lane: (draft, owned row)
     constexpr int QN = (T * DK / 4 + NT - 1) / NT;    // 4-element pieces of draft q / k per thread
@@ -1926,6 +1991,12 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     const I* kb = static_cast<const I*>(p.k) + id.row * p.ks_r + grp * p.ks_h;
     const I* vb = static_cast<const I*>(p.v) + id.row * p.vs_r + id.head * p.vs_h;
     const int64_t tok0 = (int64_t)id.row * T;  // this row's first token in [row][T] arrays
+    // read copy (two-precision checkpoint): this lane's columns in a row
+    RL* cl = reinterpret_cast<RL*>(bp + p.ckpt_lo_off) + (int64_t)id.head * (DV * DK);
+    float* cs = reinterpret_cast<float*>(bp + p.ckpt_sc_off) + (int64_t)id.head * DV;
+    constexpr int RN = 16 / (int)sizeof(RL), RCH = DK / RN;  // read elements per 16 bytes, chunks per row
+    const int lpos = RN * (cc % RCH) + 4 * (cc / RCH);
+    static_assert(!TWO || (VEC == 4 && DK % RN == 0), "four fp32 columns per lane");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const SpecLds<R> s = spec_carve<DV, DK, R>(smem, p.slots, T);
@@ -1969,8 +2040,18 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     // for the stream
     for (int i = RC * NT + tid; i < nrec; i += NT) *rdst(i) = ld_stream(rsrc(i));
     u32x4 cb[NR];
+    Quad<TL> lq[NR];  // two-precision, a row that does not flush: the read copy instead
+    float lsc[NR];
+    if (!TWO || fl) {  // uniform
 #pragma unroll
-    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+        for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            lq[r].load(cl + (int64_t)(r * RPP + rg) * DK + lpos);
+            lsc[r] = SC ? cs[r * RPP + rg] : 1.0f;
+        }
+    }
 
     // 2. to LDS
 #pragma unroll
@@ -2073,8 +2154,13 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     // 4. outputs (each query scaled by its checkpoint weight first: T * VEC
     // multiplies instead of T * NR)
     float cf[NR][VEC];
+    if (!TWO || fl) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+        for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) lq[r].to(cf[r], lsc[r]);
+    }
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < T; ++i) {
@@ -2142,6 +2228,11 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
         if (!stored) {
 #pragma unroll
             for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+        }
+        if constexpr (TWO) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                store_read_quad<TL, LPR>(cf[r], cl + (int64_t)(r * RPP + rg) * DK + lpos, cs + r * RPP + rg, cc);
         }
     }
     // drafts become records base .. base + T - 1 (keys: kbase .., the group's first head)
@@ -2820,17 +2911,28 @@ struct Dispatch {
                                     using TI = decltype(ti);
                                     with_spec_T(L.spec_T, [&](auto t_c) {
                                         constexpr int T = decltype(t_c)::value;
-                                        ok = true;
-                                        if (!p) return;
                                         const int rb = (int)sizeof(typename TR::S);
                                         const dim3 block(Tile<DV, DK, TS, 1>::NT);
-                                        if constexpr (FORM == kMamba2)
-                                            hipLaunchKernelGGL((k_spec_verify<DV, DK, TS, TR, TI, T>), grid<1>(), block,
-                                                               spec_lds_bytes(L.L, T, DV, DK, rb), stream, *p);
-                                        else
+                                        if constexpr (FORM == kMamba2) {
+                                            // a read copy only under an fp32 recurrence copy
+                                            with_read<DV, DK, TS>(L.read_dtype, L.state_dtype, [&](auto tl) {
+                                                using TL = decltype(tl);
+                                                if constexpr (std::is_same<TS, TL>::value ||
+                                                              std::is_same<TS, tF32>::value) {
+                                                    ok = true;
+                                                    if (!p) return;
+                                                    hipLaunchKernelGGL((k_spec_verify<DV, DK, TS, TR, TI, T, TL>), grid<1>(),
+                                                                       block, spec_lds_bytes(L.L, T, DV, DK, rb), stream,
+                                                                       *p);
+                                                }
+                                            });
+                                        } else if (L.read_dtype < 0 || L.read_dtype == L.state_dtype) {
+                                            ok = true;
+                                            if (!p) return;
                                             hipLaunchKernelGGL((k_spec_verify_gdn<DV, DK, TS, TR, TI, T>), grid<1>(),
                                                                block, spec_gdn_lds_bytes(L.L, T, DV, DK, rb), stream,
                                                                *p);
+                                        }
                                     });
                                 });
                             });

@@ -19,6 +19,7 @@ import linear_attention_decode_replay_amd as rs
 import oracle
 import workloads
 from gpu_harness import full_forgetting, rel_err, say
+from oracle import formats as oracle_formats
 from linear_attention_decode_replay_amd.state import SpecDecodeLayer
 
 
@@ -45,13 +46,14 @@ class SpecCase:
     force_row0_every: int = 0        # > 0: force a flush on row 0 every n steps
     forget_every: int = 0            # > 0: every n-th (step, row, draft, head) has lam = -inf
     groups: int = 0                  # key groups (0: a key and query per head)
+    read_dt: str | None = None       # two-precision checkpoint: read copy dtype (fp32 recurrence copy)
 
     def name(self):
         f = "gdn" if self.form == rs.GDN else "mamba2"
         return (f"spec {f} B={self.B} H={self.H} {self.dv}x{self.dk} L={self.L} T={self.T} steps={self.steps} "
                 f"state={self.state_dt} rec={self.rec_dt} io={self.io_dt} accept={self.accept} "
                 f"strided={self.strided} pad={self.pad_rows} forget_every={self.forget_every} groups={self.groups} "
-                f"seed={self.seed}")
+                f"read={self.read_dt} seed={self.seed}")
 
 
 def _device(t: torch.Tensor, strided: bool, dev):
@@ -66,7 +68,7 @@ def _device(t: torch.Tensor, strided: bool, dev):
 
 def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     say(f"[case] {c.name()}")
-    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, None, c.T, c.groups)
+    lay = rs.layer(c.form, c.H, c.dv, c.dk, c.L, c.state_dt, c.rec_dt, c.io_dt, c.read_dt, c.T, c.groups)
     hg = c.H // c.groups if c.groups else 1  # heads per key group
     n_blocks = c.B + 3
     d = SpecDecodeLayer(lay, c.B, n_blocks, dev)
@@ -78,7 +80,11 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
     d.upload(rows=live)
     sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live]
     ns = len(sample)
-    spec = oracle.SpecReplayModel(ns, c.H, c.dv, c.dk, c.L, c.T, form=c.form)
+    if c.read_dt:
+        spec = oracle.SpecTwoCopyModel(ns, c.H, c.dv, c.dk, c.L, c.T, c.read_dt)
+        cols = d.pool.ckpt_lo_columns()  # the read copy keeps each row in lane order
+    else:
+        spec = oracle.SpecReplayModel(ns, c.H, c.dv, c.dk, c.L, c.T, form=c.form)
     ref = oracle.SpecTokenByToken(ns, c.H, c.dv, c.dk, c.T, form=c.form)
     h = np.full(c.B, -1, np.int32)
     h[live] = 0
@@ -140,8 +146,30 @@ def run_spec_case(c: SpecCase, dev="cuda") -> dict:
         flushed = [i for i, b in enumerate(sample) if fl[b]]
         if flushed:
             err["flushes"] += len(flushed)
-            ck = d.pool.ckpt()[blk[flushed]].double().cpu().numpy()
+            ckt = d.pool.ckpt()[blk[flushed]]
+            ck = ckt.double().cpu().numpy()
             err["ckpt_flush"] = max(err["ckpt_flush"], rel_err(ck, ref.state()[flushed], 2))
+            if c.read_dt:
+                # the read copy is the cast of the kernel's own fp32 fold, bit
+                # for bit; the oracle then reads the device's read copy (its
+                # own, cast from the fp64 fold, may sit one rounding away)
+                lo = d.pool.ckpt_lo()[blk[flushed]].cpu()
+                if c.read_dt == "e4m3":
+                    sc = d.pool.ckpt_scale()[blk[flushed]].cpu().numpy()
+                    codes, e = oracle_formats.e4m3_quantize_rows(ck)
+                    assert np.array_equal(lo.numpy(), codes[..., cols]), f"E4M3 codes, step {s}"
+                    assert np.array_equal(sc, np.ldexp(1.0, e).astype(np.float32)), f"E4M3 scales, step {s}"
+                    got = oracle_formats.e4m3_dequantize_rows(lo.numpy(), np.log2(sc).astype(np.int64))
+                else:
+                    want = ckt.cpu()[..., torch.as_tensor(cols)].to(workloads.torch_dtype(c.read_dt))
+                    assert torch.equal(lo, want), f"read copy, step {s}"
+                    got = lo.double().numpy()
+                nat = np.empty_like(got)
+                nat[..., cols] = got
+                C_lo = spec.C_lo.reshape(ns, c.H, c.dv, c.dk)
+                C_lo[flushed] = nat
+                err["read_resync"] = max(err.get("read_resync", 0.0),
+                                         rel_err(nat, oracle.round_to(ref.state()[flushed], c.read_dt), 2))
         a = workloads.spec_accepted(c.seed, s, c.B, c.T, c.accept)
         a[c.pad_rows] = 0
         d.commit(torch.from_numpy(a).to(dev))

@@ -197,12 +197,22 @@ def test_spec_block_layout_ring_of_L():
     (dict(spec_T=3), rs.RS_EUNSUPPORTED), (dict(spec_T=8, L=4), rs.RS_EINVAL),
     (dict(spec_T=-1), rs.RS_EINVAL),
     (dict(spec_T=4, form=rs.GDN, d_v=32, d_k=64), rs.RS_EUNSUPPORTED),
-    (dict(spec_T=4, read_dtype="f16"), rs.RS_EUNSUPPORTED),
+    (dict(spec_T=4, form=rs.GDN, read_dtype="f16"), rs.RS_EUNSUPPORTED),
+    (dict(spec_T=4, state_dtype="f16", read_dtype="e4m3"), rs.RS_EUNSUPPORTED),
 ])
 def test_spec_layer_validation(bad, code):
     with pytest.raises(rs.ReplaySSMError) as e:
         rs.block_layout(_c2(**bad))
     assert e.value.code == code and rs.last_error()
+
+
+@pytest.mark.parametrize("read", ["f16", "bf16", "e4m3"])
+def test_spec_layer_with_read_copy(read):
+    """A speculative Mamba-2 layer over an fp32 recurrence copy may keep a
+    read copy: the block holds both copies (and E4M3 row scales)."""
+    lay = rs.block_layout(_c2(spec_T=4, read_dtype=read))
+    assert lay.ckpt_lo_off >= lay.rec_lam_off + 128 * 16 * 4
+    assert (lay.ckpt_scale_off > 0) == (read == "e4m3")
 
 
 @pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])

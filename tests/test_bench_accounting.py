@@ -236,3 +236,17 @@ def test_grouped_spec_step_bytes():
     assert bench.spec_commit_key_bytes(dk, "f16", fl, a, G) == moved
     with pytest.raises(ValueError):
         bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0, G)
+
+
+def test_spec_step_bytes_with_read_copy():
+    """A two-precision speculative layer: rows that do not flush read the
+    read copy instead of the checkpoint; flushing rows read the recurrence
+    copy and write both copies."""
+    H, dv, dk, B, T = 128, 64, 128, 2, 4
+    h = np.array([3, 14])
+    fl = np.array([False, True])
+    one = bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0)
+    two = bench.spec_step_bytes(H, dv, dk, B, T, "f32", "f16", "bf16", h, fl, 0, read="e4m3")
+    ms, ml = dv * dk * 4, dv * dk + 4 * dv
+    assert two - one == H * ((ml - ms) + ml)   # row 0 reads the read copy; row 1 also writes it
+

@@ -152,6 +152,41 @@ def test_spec_grouped_keys(form, H, groups, shape, T, state_dt):
     (_check_gdn if form == rs.GDN else _check)(err, TOL_LOW)
 
 
+def _check_read_copy(err, tol):
+    """A read copy moves non-flush outputs away from the exact recurrence by
+    its rounding: they are compared with the oracle's two-copy model (which
+    reads the device's read copy), the flushed recurrence copy with the
+    exact committed state."""
+    assert err["out_spec"] <= tol, err
+    assert err["ckpt_flush"] <= tol, err
+
+
+@pytest.mark.parametrize("read_dt", ["f16", "bf16"])
+@pytest.mark.parametrize("T", [2, 4])
+def test_spec_two_copy_tiny(read_dt, T):
+    """Speculative verify over an fp32 recurrence copy and a 16-bit read copy
+    (tiny heads, fp32 records and inputs, forced flushes): non-flush outputs
+    from the read copy, flushes fold the recurrence copy and store both; the
+    read copy is the nearest-even cast of the fp32 fold, bit for bit."""
+    err = run_spec_case(SpecCase(B=3, H=4, L=8, T=T, steps=40, read_dt=read_dt, force_row0_every=5, seed=80 + T))
+    assert err["flushes"] >= 3
+    _check_read_copy(err, TOL_F32)
+
+
+@pytest.mark.parametrize("read_dt,T,groups,state", [("e4m3", 8, 0, "f32"), ("f16", 4, 0, "f32"),
+                                                    ("e4m3", 4, 2, "f32")])
+def test_spec_two_copy_nemotron_heads(read_dt, T, groups, state):
+    """Nemotron heads (64 x 128), batch 32 x 16 heads, L = 16, bf16 inputs,
+    fp16 records, strided inputs and a padding row: E4M3 codes and row
+    scales of the read copy are the oracle's encoding of the kernel's fp32
+    fold, bit for bit; one case with keys in 2 groups."""
+    err = run_spec_case(SpecCase(B=32, H=16, dv=64, dk=128, L=16, T=T, steps=16, groups=groups, state_dt=state,
+                                 rec_dt="f16", io_dt="bf16", read_dt=read_dt, strided=True, pad_rows=[5],
+                                 sample=[0, 17, 31], seed=85 + T))
+    assert err["flushes"] >= 1
+    _check_read_copy(err, TOL_LOW)
+
+
 # ------------------------------------------------------- Gated DeltaNet form --
 
 
