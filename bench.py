@@ -73,9 +73,11 @@ COUNTERS_PATH = os.path.join(ROOT, "profiles", "counters.json")
 _LAUNCH_LOG = None
 
 
-def log_launch(kernel, label, nbytes):
+def log_launch(kernel, label, nbytes, phase=""):
+    """phase (the one-line benchmark): "prepare", "warm-up", "timed" or
+    "events" (the per-cursor breakdown with events around each launch)."""
     if _LAUNCH_LOG is not None:
-        _LAUNCH_LOG.append((kernel, label, float(nbytes)))
+        _LAUNCH_LOG.append((kernel, label, float(nbytes), phase))
 
 
 # ----------------------------------------------------------- byte accounting --
@@ -321,6 +323,8 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     torch.cuda.synchronize()
     launches = []
 
+    phase = ["prepare"]
+
     def launch(d, io, events=None):
         if kind == "replay":
             wp, fl = d.step(io, events=events)
@@ -332,9 +336,9 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
                         kind, cfg["read"], groups)
         launches.append((w, f, nb))
         if kind == "replay":
-            log_launch("k_replay_step", "flush" if f else f"w{w}", nb)
+            log_launch("k_replay_step", "flush" if f else f"w{w}", nb, phase[0])
         else:
-            log_launch("k_conventional_step", "conventional", nb)
+            log_launch("k_conventional_step", "conventional", nb, phase[0])
         return w, f
 
     # pool preparation (untimed): pool p decodes starts[p] tokens
@@ -350,9 +354,11 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
             raise RuntimeError(f"launch {s} ran at cursor {w}, the schedule says {(s + phi) % L}")
         return w, f
 
+    phase[0] = "warm-up"
     for s in range(warmup):
         one(s)
     torch.cuda.synchronize()
+    phase[0] = "timed"
     # Timed region: K back-to-back steps, bracketed by one pair of HIP events
     # on the launch stream (no event between launches, so none of their
     # overhead lands inside a launch).
@@ -374,6 +380,7 @@ def run_gpu(cfg, steps, warmup, n_pools, kind):
     # Breakdown by cursor position (after the timed region, not part of it):
     # 2 L more launches (every cursor twice) with events around each.
     by_pos = {}
+    phase[0] = "events"
     if kind == "replay":
         n_brk = 2 * L
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_brk)]
@@ -892,7 +899,7 @@ def line_up(rows, log, scale):
     for (_, name, _, v) in rows:
         disp.setdefault(kernel_family(name), []).append(v * 1024 * scale)
     logged = {}
-    for fam, label, nb in log:
+    for fam, label, nb, *_ in log:
         logged.setdefault(fam, []).append((label, nb))
     out = {}
     for fam, launches in logged.items():
@@ -1015,21 +1022,32 @@ def summarize_trace(trace_csv, launch_log):
     for _, fam, us in rows:
         disp.setdefault(fam, []).append(us)
     logged = {}
-    for fam, label, nb in log["launches"]:
-        logged.setdefault(fam, []).append((label, nb))
-    table = {}
+    for fam, label, nb, *rest in log["launches"]:
+        logged.setdefault(fam, []).append((label, nb, rest[0] if rest else ""))
+    table, phases = {}, {}
     for fam, launches in logged.items():
         got = disp.get(fam, [])
         if len(got) != len(launches):
             raise SystemExit(f"{fam}: {len(got)} dispatches in the trace, {len(launches)} launches logged")
-        for (label, nb), us in zip(launches, got):
+        for (label, nb, ph), us in zip(launches, got):
             table.setdefault((fam, label), []).append((us, nb))
+            if ph:
+                phases.setdefault((fam, ph), []).append((us, nb))
     for (fam, label), v in table.items():
         us = np.array([a for a, _ in v])
         nb = np.array([b for _, b in v])
         print(json.dumps({"kernel": fam, "label": label, "launches": len(v), "us_mean": round(float(us.mean()), 2),
                           "us_min": round(float(us.min()), 2), "us_max": round(float(us.max()), 2),
                           "tbs": round(float(nb.sum() / us.sum() / 1e6), 3)}))
+    # the one-line benchmark's timed launches alone (the phase its log records):
+    # bench.py's launch_us is their mean plus the gaps between them
+    for (fam, ph), v in phases.items():
+        if ph == "timed":
+            us = np.array([a for a, _ in v])
+            nb = np.array([b for _, b in v])
+            print(json.dumps({"kernel": fam, "label": "timed launches", "launches": len(v),
+                              "us_mean": round(float(us.mean()), 2), "tbs": round(float(nb.sum() / us.sum() / 1e6), 3),
+                              "frac_of_8tbs": round(float(nb.sum() / us.sum() / 1e6) / 8.0, 4)}))
     L = log.get("L")
     if L:
         labels = [f"w{w}" for w in range(L - 1)] + ["flush"]

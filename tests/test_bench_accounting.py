@@ -250,3 +250,26 @@ def test_spec_step_bytes_with_read_copy():
     ms, ml = dv * dk * 4, dv * dk + 4 * dv
     assert two - one == H * ((ml - ms) + ml)   # row 0 reads the read copy; row 1 also writes it
 
+
+def test_trace_summary_of_timed_launches(tmp_path, capsys):
+    """The one-line benchmark logs each launch's phase; --summarize-trace
+    reports the mean of the timed launches, which is what bench.py's
+    launch_us measures (plus the gaps between launches)."""
+    import csv
+    import json
+    log = {"L": 2, "launches": [("k_replay_step", "w0", 100.0, "prepare"), ("k_replay_step", "flush", 300.0, "timed"),
+                                ("k_replay_step", "w0", 100.0, "timed"), ("k_replay_step", "flush", 300.0, "events")]}
+    path = tmp_path / "kt.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for did, ns in enumerate((50_000, 30_000, 10_000, 90_000)):
+            w.writerow({"Dispatch_Id": did, "Kernel_Name": "void rs::k_replay_step<0>(rs::StepParams)",
+                        "Start_Timestamp": 1000 * did, "End_Timestamp": 1000 * did + ns})
+    lp = tmp_path / "log.json"
+    lp.write_text(json.dumps(log))
+    assert bench.main(["--summarize-trace", str(path), "--launch-log", str(lp)]) == 0
+    lines = [json.loads(x) for x in capsys.readouterr().out.splitlines()]
+    timed = [d for d in lines if d.get("label") == "timed launches"]
+    assert len(timed) == 1 and timed[0]["launches"] == 2 and timed[0]["us_mean"] == 20.0
+
