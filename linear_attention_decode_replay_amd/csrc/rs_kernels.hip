@@ -697,6 +697,15 @@ struct RecordCopy {
             for (int u = 0; u < RC; ++u) buf[u] = ld_stream(src(rk, rx, min(u * NT + (int)threadIdx.x, n - 1)));
         }
     }
+    // the same with no branch around the loads: with no records every lane
+    // reads the 16 bytes at safe, which commit ignores
+    __device__ __forceinline__ void issue_or(const R* rk, const R* rx, int w, const R* safe) {
+        nk = w * KCH;
+        n = nk + w * XCH;
+#pragma unroll
+        for (int u = 0; u < RC; ++u)
+            buf[u] = ld_stream(n > 0 ? src(rk, rx, min(u * NT + (int)threadIdx.x, n - 1)) : safe);
+    }
     // TAIL = false: the records fit the first RC * NT chunks (the caller
     // checked), so the remainder loop, whose loads would make the compiler
     // wait for every outstanding load, is left out.
@@ -1003,8 +1012,12 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
         in.lam_j = P.rl[min(tid, max(w - 1, 0))];
         in.rec.issue_always(P.rk, P.rx, w);
     } else {
-        in.lam_j = w > 0 ? P.rl[min(tid, w - 1)] : 0.f;
-        in.rec.issue(P.rk, P.rx, w);
+        // no branch around these loads either: an empty ring reads a valid
+        // address and ignores the value (see tile_issue_stream)
+        const float* lp = w > 0 ? P.rl + min(tid, w - 1) : p.lam + id.tile;
+        const float lj = *lp;
+        in.lam_j = w > 0 ? lj : 0.f;
+        in.rec.issue_or(P.rk, P.rx, w, reinterpret_cast<const typename TR::S*>(P.ck));
     }
     if constexpr (SC) {
         if (!fl) {
@@ -1034,13 +1047,19 @@ __device__ __forceinline__ void tile_issue_stream(const StepParams& p,
     const int rg = tid / LPR;
     const int col0 = EPC * cc;
     const TilePtrs<DV, DK, TS, TR, TI, TL, DVW> P(p, in.id, in.blk);
-    if (in.zc && !always) return;
+    if constexpr (TWO)
+        if (in.zc && !always) return;
+    // A single checkpoint's stream is issued even for a zero checkpoint, every
+    // lane then reading the tile's first 16 bytes (one cache line, ignored):
+    // with a branch around these loads the compiler makes the record copy
+    // wait for the whole stream (its wait counts cover both paths).
+    const bool skip = !TWO && in.zc && !always;
     if (!TWO || fl) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const S* rowp = P.ck + (int64_t)(r * RPP + rg) * DK + col0;
 #pragma unroll
-            for (int h = 0; h < HPC; ++h) in.cb[r * HPC + h] = ld_stream(rowp + EPC * LPR * h);
+            for (int h = 0; h < HPC; ++h) in.cb[r * HPC + h] = ld_stream(skip ? P.ck : rowp + EPC * LPR * h);
         }
     } else {
 #pragma unroll
@@ -1137,7 +1156,10 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     for (int r = 0; r < NR; ++r) rsc[r] = in.rsc[r];
 #pragma unroll
     for (int i = 0; i < NR * HPC; ++i) cb[i] = in.cb[i];
-    if (in.zc) {  // a zero checkpoint: zero bits are +0 in every state and read format
+    // A zero checkpoint: zero bits are +0 in every state and read format.  The
+    // one-workgroup kernel clears its registers after the record work below,
+    // since overwriting them here would wait for the checkpoint stream.
+    if (DEFER && in.zc) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) rsc[r] = 1.0f;
 #pragma unroll
@@ -1200,6 +1222,12 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     }
     __syncthreads();
 
+    if (!DEFER && in.zc) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) rsc[r] = 1.0f;
+#pragma unroll
+        for (int i = 0; i < NR * HPC; ++i) cb[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     const float G = s.sc[0];
     const float kq = s.sc[1];
     float cf[NR][VEC];
@@ -1295,25 +1323,60 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
             st_nt<kNtSmall<FORM>>(p.next_wp + id.row, fl ? 0 : (w + 1) | (in.zc ? RS_CURSOR_ZERO_CKPT : 0));
     const float alpha = expf(lam);  // Gated DeltaNet only
     float* o = DEFER ? df.out : p.out + id.tile * DV + row0;
+    // One-workgroup tiles stage the output rows (and Gated DeltaNet's
+    // corrected values) in LDS and store them below in whole 16-byte chunks:
+    // the lanes holding the reduced rows cover rows RPP apart, and storing
+    // from them scatters small pieces into the checkpoint read stream.
+    // Mamba-2 stages its outputs in u (unused by that form); Gated DeltaNet
+    // stages them in v (a row's v is read just before, by the same lane) and
+    // its corrected values in u, where the flush fold reads them.
+    constexpr bool STAGE = !DEFER && DVW % 4 == 0 && (DVW * (int)sizeof(R)) % 16 == 0;
+    float* so = FORM == kMamba2 ? s.u : s.v;
     {
         constexpr int left = xsum_left<NV, LPR, KEEP>();
         const int b0 = xsum_base<NV, LPR, KEEP>(cc);
         if ((cc & xsum_dup_mask<NV, LPR, KEEP>()) == 0) {
             if constexpr (FORM == kMamba2) {
 #pragma unroll
-                for (int i = 0; i < left; ++i) st_nt(o + (b0 + i) * RPP + rg, acc[i]);
+                for (int i = 0; i < left; ++i) {
+                    if constexpr (STAGE) so[(b0 + i) * RPP + rg] = acc[i];
+                    else st_nt(o + (b0 + i) * RPP + rg, acc[i]);
+                }
             } else {
                 const float bt = in.beta;
 #pragma unroll
                 for (int i = 0; i < left; i += 2) {
                     const int row = ((b0 + i) / 2) * RPP + rg;
                     const float d = bt * (s.v[row] - alpha * acc[i + 1]);
-                    st_nt<kNtSmall<FORM>>(o + row, alpha * acc[i] + kq * d);
-                    if (fl) s.u[row] = d;
-                    else if constexpr (DEFER) df.x[row] = from_f<TR>(d);
-                    else st_nt<kNtSmall<FORM>>(rx + (int64_t)w * DV + row, from_f<TR>(d));
+                    if constexpr (STAGE) {
+                        so[row] = alpha * acc[i] + kq * d;
+                        s.u[row] = d;
+                    } else {
+                        st_nt<kNtSmall<FORM>>(o + row, alpha * acc[i] + kq * d);
+                        if (fl) s.u[row] = d;
+                        else if constexpr (DEFER) df.x[row] = from_f<TR>(d);
+                        else st_nt<kNtSmall<FORM>>(rx + (int64_t)w * DV + row, from_f<TR>(d));
+                    }
                 }
             }
+        }
+    }
+    if constexpr (STAGE) {
+        __syncthreads();
+        constexpr int OC = DVW / 4;                     // output chunks
+        constexpr int XE = 16 / (int)sizeof(R);         // record elements per chunk
+        constexpr int XC = FORM == kGdn ? DVW / XE : 0;  // corrected-value chunks
+        static_assert(OC + XC <= T::NT, "one chunk per thread");
+        if (tid < OC) {
+            st_nt<kNtSmall<FORM>>(reinterpret_cast<u32x4*>(o) + tid,
+                                  u32x4{__float_as_uint(so[4 * tid]), __float_as_uint(so[4 * tid + 1]),
+                                        __float_as_uint(so[4 * tid + 2]), __float_as_uint(so[4 * tid + 3])});
+        } else if (FORM == kGdn && !fl && tid < OC + XC) {
+            const int c = tid - OC;
+            float dv[XE];
+#pragma unroll
+            for (int e = 0; e < XE; ++e) dv[e] = s.u[c * XE + e];
+            store_f<TR, XE, kNtSmall<FORM>>(rx + (int64_t)w * DV + c * XE, dv);
         }
     }
 
@@ -1326,7 +1389,7 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
     // the owned rows, store once.
     //   Mamba-2:  C' = G C + sum_j e_j x_j k_j^T + v k^T
     //   GDN:      C' = alpha P C + sum_j alpha p_j d_j k_j^T + d k^T
-    if constexpr (FORM == kGdn) __syncthreads();  // d in LDS
+    if constexpr (FORM == kGdn && !STAGE) __syncthreads();  // d in LDS (staged: stored above)
     // (reconstruction route: the registers already hold S_{t-1}, records folded)
     const float gc = FORM == kMamba2 ? G : alpha * gs;
     const float ge = FORM == kMamba2 ? 1.0f : alpha;
