@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -171,10 +172,24 @@ def window_us(by_cursor, L):
     return round(float(np.mean([by_cursor[k] for k in keys])), 2)
 
 
+# C/C++ comments and string or character literals (kept: they can hold //)
+_CPP_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with comments removed and whitespace runs collapsed, so
+    that editing a comment does not change what counts as the same code."""
+    out = _CPP_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(out.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's code (comments and layout excluded): stored
+    counters are reported only for the code they were measured on."""
     h = hashlib.sha256()
     for f in ("rs_kernels.hip", "rs_api.cpp", "rs_internal.h"):
-        h.update(open(os.path.join(ROOT, "linear_attention_decode_replay_amd", "csrc", f), "rb").read())
+        with open(os.path.join(ROOT, "linear_attention_decode_replay_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

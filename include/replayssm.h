@@ -234,13 +234,16 @@ int rs_block_layout_get(const rs_layer* layer, rs_block_layout* out);
  *   write_pos   records held by the row, 0..L-1 (the write cursor of the
  *               vLLM pull request, "CUDA graphs and continuous batching"),
  *               optionally with RS_CURSOR_ZERO_CKPT set: the row's checkpoint
- *               is zero and is not read (a request that joined the batch and
- *               has not flushed yet; its block's checkpoint region may hold
- *               anything).  replay_decode_step and replay_flush treat the
- *               checkpoint as zero for such a row; its first flush writes the
- *               checkpoint, and next_write_pos carries the bit until then.
- *               This replaces replay_state_reset for a joining row (one launch
- *               fewer, and no checkpoint read until the row's first flush).
+ *               is zero and its stored values are never used (a request that
+ *               joined the batch and has not flushed yet; its block's
+ *               checkpoint region may hold anything).  replay_decode_step and
+ *               replay_flush treat the checkpoint as zero for such a row; its
+ *               first flush writes the checkpoint, and next_write_pos carries
+ *               the bit until then.  This replaces replay_state_reset for a
+ *               joining row (one launch fewer).  The one-workgroup kernels
+ *               read only the first 16 bytes of such a checkpoint (one cache
+ *               line, so that no load sits under a branch); the persistent
+ *               non-flush form streams it and discards it.
  *               Not for speculative layers (their counts must be 0..L) or
  *               conventional_decode_step (which reads no cursor).
  *   flush       nonzero: this step folds the row into its checkpoint.  A row

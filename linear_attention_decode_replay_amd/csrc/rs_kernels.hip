@@ -1030,7 +1030,8 @@ __device__ __forceinline__ void tile_issue_small(const StepParams& p, const Tile
 // The checkpoint stream of a tile whose small loads tile_issue_small issued.
 // always: issue the loads even for a zero checkpoint (its values are then
 // replaced by zeros in tile_finish), so that a loop issuing ahead has no
-// branch around them; otherwise a zero checkpoint is not read.
+// branch around them; otherwise a zero checkpoint's loads all read the
+// tile's first 16 bytes (one checkpoint) or are skipped (two copies).
 template <int FORM, int DV, int DK, class TS, class TR, class TI, int SPLIT, class TL, int ROWS>
 __device__ __forceinline__ void tile_issue_stream(const StepParams& p,
                                                   TileIn<FORM, DV, DK, TS, TR, TI, SPLIT, TL, ROWS>& in,

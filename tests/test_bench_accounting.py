@@ -273,3 +273,13 @@ def test_trace_summary_of_timed_launches(tmp_path, capsys):
     timed = [d for d in lines if d.get("label") == "timed launches"]
     assert len(timed) == 1 and timed[0]["launches"] == 2 and timed[0]["us_mean"] == 20.0
 
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The stored counters follow the code, not its comments: removing
+    comments and collapsing whitespace keeps string and character literals
+    (which may hold //) and every token of code."""
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "a//b /*c*/"; char c = \'/\'; x = a / 2;'
+    assert bench.code_text(src) == 'int a = 1; const char* s = "a//b /*c*/"; char c = \'/\'; x = a / 2;'
+    assert bench.code_text(src.replace("// note", "// other words")) == bench.code_text(src)
+    assert bench.code_text(src.replace("a / 2", "a / 3")) != bench.code_text(src)
