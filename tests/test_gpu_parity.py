@@ -349,6 +349,12 @@ def test_persistent_step_long_ring(rec_dt, L):
     ("gdn-128-f16-state", dict(form=rs.GDN, B=3, H=2, dv=128, dk=128, L=8, steps=20, state_dt="f16",
                                rec_dt="f16", io_dt="bf16", force_every=5)),
     ("gdn-reconstruct", dict(form=rs.GDN, B=3, H=3, L=4, steps=12, reconstruct=True)),
+    # rings with no slot (L = 1: every step flushes) or one; the one-workgroup
+    # kernel's loads for an empty ring and a zero checkpoint read fallback
+    # addresses whose values are discarded
+    ("mamba2-L1", dict(L=1, steps=8)),
+    ("gdn-L1", dict(form=rs.GDN, L=1, steps=8)),
+    ("mamba2-L2-f16-state", dict(L=2, steps=9, state_dt="f16", rec_dt="f16", io_dt="bf16")),
 ])
 def test_join_with_zero_checkpoint(name, case):
     """Rows join with RS_CURSOR_ZERO_CKPT instead of a state reset: their
