@@ -802,7 +802,7 @@ def suite_continuous(out, steps=200, n_layers=4):
                     live_rows.append(int(live.sum()))
                     f = fl[live].astype(bool)
                     w = wp[live]
-                    # a zero checkpoint is not read (its flush still writes it)
+                    # a zero checkpoint counts no read (one cache line per tile at most; its flush still writes it)
                     ck_read = np.where(zc[live], 0, ms_state)
                     nb = float(np.sum(H * (ck_read + w * rec + np.where(f, ms_state, rec) + io_b) + 9))
                     nb += 4.0 * int((~live).sum())

@@ -75,7 +75,7 @@ class DecodeLayer:
         self.device = self.pool.raw.device
         self.anchor = np.full(n, -1, np.int32)   # -1: empty slot (padding row)
         self.blocks = np.full(n, -1, np.int32)
-        # rows whose checkpoint is zero and not read until their first flush
+        # rows whose checkpoint counts as zero until their first flush
         # (joined with join_rows; RS_CURSOR_ZERO_CKPT in the cursor word)
         self.zero_ckpt = np.zeros(n, bool)
         _, size = _layout(n)
@@ -283,8 +283,8 @@ class DecodeLayer:
 
     def join_rows(self, rows) -> None:
         """New requests in the given slots, without a launch: their
-        checkpoints count as zero (RS_CURSOR_ZERO_CKPT) and are not read until
-        each row's first flush writes it; anchored at 0.  The metadata goes
+        checkpoints count as zero (RS_CURSOR_ZERO_CKPT) and their stored values
+        are not used until each row's first flush writes them; anchored at 0.  The metadata goes
         up with the next step's upload.  (The conventional step reads no
         cursor: its rows need reset_rows.)"""
         sel = np.zeros(self.n_slots, bool)

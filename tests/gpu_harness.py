@@ -152,7 +152,7 @@ def run_case(c: Case, dev="cuda") -> dict:
         for b in live_rows:
             d.assign(b, int(blocks[b]))
         if c.join and d is rep:
-            d.join_rows(live_rows)   # the checkpoints stay NaN-filled: never read until written
+            d.join_rows(live_rows)   # the checkpoints stay NaN-filled: never used until written
         else:
             d.reset_rows(live_rows)
     sample = [b for b in (c.sample if c.sample is not None else range(c.B)) if b in live_rows]

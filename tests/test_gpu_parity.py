@@ -358,10 +358,10 @@ def test_persistent_step_long_ring(rec_dt, L):
 ])
 def test_join_with_zero_checkpoint(name, case):
     """Rows join with RS_CURSOR_ZERO_CKPT instead of a state reset: their
-    checkpoints stay NaN-filled in the pool and must never be read before
-    the row's first flush writes them (any read would turn the outputs into
-    NaN); the flag the device carries in its cursors is bit-exact against the
-    host's, and is cleared by each row's first flush."""
+    checkpoints stay NaN-filled in the pool and their values must never be
+    used before the row's first flush writes them (any use would turn the
+    outputs into NaN); the flag the device carries in its cursors is
+    bit-exact against the host's, and is cleared by each row's first flush."""
     c = Case(join=True, seed=80, **case)
     if c.read_dt:
         err = run_case(c)
