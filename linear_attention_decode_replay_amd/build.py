@@ -26,6 +26,13 @@ HIPCC_FLAGS = [
     # feature and ignores it; the device pass honours it
     # (tests/test_build_flags.py disassembles the built library to check).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core (MFMA) operands and results in ordinary VGPRs, not AGPRs:
+    # the one MFMA in the library (the fp16-state flush fold) then accumulates
+    # in the registers that already hold the tile, instead of copying it to
+    # accumulation registers that count against the same budget (measured:
+    # the Gated DeltaNet 128 x 128 fp16 kernel at 126 VGPRs + 64 AGPRs, two
+    # waves per SIMD, against 126 VGPRs and four).
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

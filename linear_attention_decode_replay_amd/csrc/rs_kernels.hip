@@ -1401,17 +1401,74 @@ __device__ __forceinline__ void tile_finish(const StepParams& p,
 #pragma unroll
         for (int c = 0; c < VEC; ++c) cf[r][c] = gc * cf[r][c] + ur * kv[c];
     }
-    for (int j = 0; j < wd; ++j) {
-        float kj[VEC];
-        const R* kr = s.k + (int64_t)j * DK + col0;
+    // fp16 state and records: the records' rank-w update on the matrix
+    // cores.  With D = the 16 x 16 block whose element (m, n) is tile row
+    // 16 (R0 + m % 4) + 4 wave + m / 4 and column 8 n + c, each lane's block
+    // elements are exactly its registers cf[R0 .. R0 + 3][c] (the layout of
+    // v_mfma_f32_16x16x16_f16: lane l holds D rows 4 (l / 16) + i, column
+    // l % 16), so the update accumulates in place.  The records' weighted
+    // values f = e_j x_j (fp32) enter as fp16 pairs hi + lo with
+    // hi = fp16(f), lo = fp16(f - hi) (two passes, |f - hi - lo| <= 2^-22 |f|
+    // in fp16's normal range), the keys as they are stored (fp16); products
+    // are exact and sums fp32.  |f| <= |x_j| (weights <= 1), so hi never
+    // overflows.
+    constexpr bool MF = std::is_same<TS, tF16>::value && std::is_same<TR, tF16>::value && !TWO && DK == 128 &&
+                        LPR == 16 && RPP == 16 && NR % 4 == 0 && VEC == 8 && HPC == 1;
+    if constexpr (MF) {
+        typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        const int l = tid & 63;
+        const int kq = 4 * (l >> 4);  // this lane's 4 of the block's 16 records (operands A and B)
+        const int arow = 16 * (l & 3) + 4 * (tid >> 6) + ((l & 15) >> 2);  // its operand-A row, R0 = 0
+        for (int jc = 0; jc < wd; jc += 16) {
+            h4_t bk[VEC];  // keys: bk[c][i] = k_{jc + kq + i}[8 cc + c]
 #pragma unroll
-        for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(kr + EPC * LPR * h, kj + h * EPC);
-        const float ej = ge * s.e[j];
+            for (int i = 0; i < 4; ++i) {
+                const int j = jc + kq + i;
+                u32x4 kw = u32x4{0u, 0u, 0u, 0u};
+                if (j < wd) kw = *reinterpret_cast<const u32x4*>(s.k + (int64_t)j * DK + col0);
+                _Float16 kh[VEC];
+                __builtin_memcpy(kh, &kw, 16);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
+                for (int c = 0; c < VEC; ++c) bk[c][i] = kh[c];
+            }
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+            for (int R0 = 0; R0 < NR; R0 += 4) {
+                h4_t ahi, alo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jc + kq + i;
+                    float f = 0.f;
+                    if (j < wd) f = ge * s.e[j] * (float)s.x[(int64_t)j * DVW + 16 * R0 + arow];
+                    const _Float16 hi = (_Float16)f;
+                    ahi[i] = hi;
+                    alo[i] = (_Float16)(f - (float)hi);
+                }
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+                    f4_t acc = {cf[R0][c], cf[R0 + 1][c], cf[R0 + 2][c], cf[R0 + 3][c]};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bk[c], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bk[c], acc, 0, 0, 0);
+                    cf[R0][c] = acc[0];
+                    cf[R0 + 1][c] = acc[1];
+                    cf[R0 + 2][c] = acc[2];
+                    cf[R0 + 3][c] = acc[3];
+                }
+            }
+        }
+    } else {
+        for (int j = 0; j < wd; ++j) {
+            float kj[VEC];
+            const R* kr = s.k + (int64_t)j * DK + col0;
+#pragma unroll
+            for (int h = 0; h < HPC; ++h) load_f<TR, EPC>(kr + EPC * LPR * h, kj + h * EPC);
+            const float ej = ge * s.e[j];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float f = ej * to_f<TR>(s.x[(int64_t)j * DVW + r * RPP + rg]);
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+            }
         }
     }
     if constexpr (std::is_same<TS, tF16>::value) {

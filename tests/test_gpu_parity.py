@@ -337,6 +337,16 @@ def test_persistent_step_long_ring(rec_dt, L):
              sample=[0, 9, 16], check_conventional=False, seed=95 + L))
 
 
+@pytest.mark.parametrize("form,dv,L", [(rs.MAMBA2, 64, 4), (rs.MAMBA2, 64, 64), (rs.GDN, 128, 4), (rs.GDN, 128, 64)])
+def test_fp16_state_fold_on_matrix_cores(form, dv, L):
+    """An fp16 state with fp16 records at d_k = 128 folds its records on the
+    matrix cores at every flush (16 records per pass, the weights as fp16
+    hi + lo pairs): rings of 3 records (one partial pass) and 63 (four
+    passes), forced flushes on row 0 at other cursors, a padding row."""
+    _go(Case(form=form, B=3, H=2, dv=dv, dk=128, L=L, steps=L + 8, state_dt="f16", rec_dt="f16", io_dt="bf16",
+             pad_rows=[1], force_every=5, seed=120 + L + dv))
+
+
 @pytest.mark.parametrize("name,case", [
     ("mamba2-tiny", dict()),
     ("gdn-tiny", dict(form=rs.GDN)),
