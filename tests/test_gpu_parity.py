@@ -337,14 +337,16 @@ def test_persistent_step_long_ring(rec_dt, L):
              sample=[0, 9, 16], check_conventional=False, seed=95 + L))
 
 
-@pytest.mark.parametrize("form,dv,L", [(rs.MAMBA2, 64, 4), (rs.MAMBA2, 64, 64), (rs.GDN, 128, 4), (rs.GDN, 128, 64)])
-def test_fp16_state_fold_on_matrix_cores(form, dv, L):
+@pytest.mark.parametrize("form,dv,L,groups", [(rs.MAMBA2, 64, 4, 0), (rs.MAMBA2, 64, 64, 0), (rs.GDN, 128, 4, 0),
+                                             (rs.GDN, 128, 64, 0), (rs.MAMBA2, 64, 16, 2), (rs.GDN, 128, 16, 2)])
+def test_fp16_state_fold_on_matrix_cores(form, dv, L, groups):
     """An fp16 state with fp16 records at d_k = 128 folds its records on the
     matrix cores at every flush (16 records per pass, the weights as fp16
-    hi + lo pairs): rings of 3 records (one partial pass) and 63 (four
-    passes), forced flushes on row 0 at other cursors, a padding row."""
-    _go(Case(form=form, B=3, H=2, dv=dv, dk=128, L=L, steps=L + 8, state_dt="f16", rec_dt="f16", io_dt="bf16",
-             pad_rows=[1], force_every=5, seed=120 + L + dv))
+    hi + lo pairs): rings of 3 records (one partial pass), 15 with keys
+    shared by pairs of heads, and 63 (four passes); forced flushes on row 0
+    at other cursors, a padding row."""
+    _go(Case(form=form, B=3, H=4 if groups else 2, dv=dv, dk=128, L=L, steps=L + 8, state_dt="f16", rec_dt="f16",
+             io_dt="bf16", pad_rows=[1], force_every=5, groups=groups, seed=120 + L + dv + groups))
 
 
 @pytest.mark.parametrize("name,case", [
