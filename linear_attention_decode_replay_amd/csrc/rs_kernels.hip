@@ -2404,7 +2404,13 @@ struct SpecGdnLds {
     float* kq;     // [slots + T][T] key . q_i (committed keys, then drafts)
     float* kk;     // [slots + T][T] key . k_i
     float* sc;     // [4] total committed log-decay, its exponential
+    float* y;      // [DV][spec_y_stride(T)] S_h q_i (columns i < T), S_h k_i
+                   // (T + i): the matrix-core form only
 };
+
+// Row stride of SpecGdnLds::y: 2T products, 16-byte rows, 4 words of padding
+// (the four lane groups of a wave write rows four apart).
+constexpr int spec_y_stride(int T) { return (2 * T + 3) / 4 * 4 + 4; }
 
 template <int DV, int DK, class R>
 __device__ __forceinline__ SpecGdnLds<R> spec_gdn_carve(char* smem, int slots, int T) {
@@ -2423,18 +2429,33 @@ __device__ __forceinline__ SpecGdnLds<R> spec_gdn_carve(char* smem, int slots, i
     s.kq = s.wdd + T * T;
     s.kk = s.kq + (slots + T) * T;
     s.sc = s.kk + (slots + T) * T;
+    // 16-byte aligned, by arithmetic on the LDS pointer itself (a pointer
+    // rebuilt from an integer is generic, and its loads wait like global ones)
+    const size_t yoff = (size_t)(reinterpret_cast<char*>(s.sc + 4) - smem);
+    s.y = reinterpret_cast<float*>(smem + ((yoff + 15) & ~size_t(15)));
     return s;
 }
 
-size_t spec_gdn_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes) {
+// The matrix-core form (spec_gdn_mf) adds the y rows and up to 12 bytes of
+// alignment before them.
+size_t spec_gdn_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes, bool mf) {
     return (size_t)slots * (dk + dv) * rec_bytes +
            sizeof(float) * (2 * (size_t)T * dk + (size_t)T * dv + 2 * (size_t)T + (size_t)slots + (size_t)T +
-                            (size_t)T * T + 2 * ((size_t)slots + T) * T + 4);
+                            (size_t)T * T + 2 * ((size_t)slots + T) * T + 4) +
+           (mf ? 12 + sizeof(float) * (size_t)dv * spec_y_stride(T) : 0);
+}
+
+// Whether the Gated DeltaNet verify of this shape runs its state products on
+// the matrix cores: an fp32 state whose d_v rows fill four waves' 16-row
+// blocks and whose d_k columns come in 16-column slices.
+constexpr bool spec_gdn_mf(int dv, int dk, bool f32_state) {
+    return f32_state && dv % 64 == 0 && dk % 16 == 0 && (size_t)dv * dk / 4 / 4 >= 256;
 }
 
 template <int DV, int DK, class TS, class TR, class TI, int T>
 __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(const StepParams p) {
     using Tl = Tile<DV, DK, TS, 1>;
+    constexpr bool MF = spec_gdn_mf(DV, DK, std::is_same<TS, tF32>::value);
     using S = typename TS::S;
     using R = typename TR::S;
     using I = typename TI::S;
@@ -2524,9 +2545,27 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(c
         for (int u = 0; u < RC; ++u) rb[u] = ld_stream(rsrc(min(u * NT + tid, nrec - 1)));
     }
     for (int i = RC * NT + tid; i < nrec; i += NT) put(i, ld_stream(rsrc(i)));
+    // Matrix-core form: wave wv owns the 16-row blocks wv NB .. wv NB + NB - 1;
+    // in block b, lane (rm, cg) holds row 16 (wv NB + b) + rm, columns
+    // 16 q + 4 cg .. + 3 of every 16-column slice q (one 64-byte piece of 16
+    // rows per load).  That is the A operand of the 16 x 16 x 4 fp32 matrix
+    // product, one column per lane group, so S_h [q, k] needs no exchange.
+    // Plain loads: the two halves of a 128-byte line come from two loads,
+    // and non-temporal ones measured 2-5 % slower here.
+    constexpr int NB = DV / 64, NP = DK / 16;
+    [[maybe_unused]] const int wv = tid >> 6, rm = tid & 15, cg = (tid >> 4) & 3;
     u32x4 cb[NR];
+    if constexpr (MF) {
+        static_assert(NB * NP == NR && NT == 256, "four waves of 16-row blocks");
 #pragma unroll
-    for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+                cb[b * NP + q] = *reinterpret_cast<const u32x4*>(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
+    }
 
     // 2. to LDS
 #pragma unroll
@@ -2615,106 +2654,219 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(c
     }
     __syncthreads();
 
-    // 5. drafts in order: S_h q_i, S_h k_i for the owned rows, then the
-    //    substitution and the output at the lanes that own each row
-    float cf[NR][VEC];
+    if constexpr (MF) {
+        using f4 = __attribute__((ext_vector_type(4))) float;
+        constexpr int YS = spec_y_stride(T);
+        const float P = s.sc[1];
+        f4 cf[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
-    const float P = s.sc[1];
-    constexpr int left = xsum_left<NV, LPR, 2>();
-    constexpr int NOWN = left / 2;  // rows this lane ends up with
-    const int b0 = xsum_base<NV, LPR, 2>(cc);
-    const bool owner = (cc & xsum_dup_mask<NV, LPR, 2>()) == 0;
-    float ur[T][NOWN];  // corrected values of the owned rows, drafts so far
+        for (int r = 0; r < NR; ++r) cf[r] = __builtin_bit_cast(f4, cb[r]);
+        // 5. Y = P S_h W + X G on the matrix cores, W = [q_1 .. q_T, k_1 .. k_T]
+        //    (d_k x 2T, zero beyond), X the committed corrected values, G_jn =
+        //    e_j (k_j . w_n).  Each 16 x 16 x 4 product takes four columns of
+        //    16 rows (lane group cg holds column 4 cg + e of slice q) against
+        //    the same columns of W (lane (rm, cg): column n = rm); lane (rm, cg)
+        //    ends with rows 4 cg .. + 3 of the block at column n = rm.
+        const int nq = min(rm, T - 1), nkd = min(max(rm - T, 0), T - 1);
+        const float* wsrc = (rm < T ? s.qd + nq * DK : s.kd + nkd * DK) + 4 * cg;
+        const float wsc = rm < 2 * T ? P : 0.f;
+        f4 y[NB];
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-        float acc[NV];
+        for (int b = 0; b < NB; ++b) y[b] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            float a = 0.f, b = 0.f;
+        for (int q = 0; q < NP; ++q) {
+            const f4 w = *reinterpret_cast<const f4*>(wsrc + 16 * q) * wsc;
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                a += cf[r][c] * s.qd[i * DK + cc * VEC + c];
-                b += cf[r][c] * s.kd[i * DK + cc * VEC + c];
-            }
-            acc[2 * r] = P * a;
-            acc[2 * r + 1] = P * b;
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[b * NP + q][e], w[e], y[b], 0, 0, 0);
         }
-        for (int j = cc; j < h; j += LPR) {
-            const float wq = s.ec[j] * s.kq[j * T + i], wk = s.ec[j] * s.kk[j * T + i];
+        // records four at a time; a slot past h takes slot 0's (finite) value
+        // with weight zero
+        for (int j0 = 0; j0 < h; j0 += 4) {
+            const int jj = j0 + cg;
+            const int jc = jj < h ? jj : 0;
+            const float g = jj < h && rm < 2 * T ? s.ec[jc] * (rm < T ? s.kq[jc * T + nq] : s.kk[jc * T + nkd]) : 0.f;
 #pragma unroll
+            for (int b = 0; b < NB; ++b)
+                y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f<TR>(s.xc[(16 * (wv * NB + b) + rm) * p.slots + jc]), g,
+                                                            y[b], 0, 0, 0);
+        }
+        if (rm < 2 * T) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s.y[(16 * (wv * NB + b) + 4 * cg + i) * YS + rm] = y[b][i];
+        }
+        // 6. flush (before the substitution, so that the tile's registers are
+        //    free there): S_h = P C + sum_j e_j x_j k_j^T on the matrix cores, in
+        //    place: as C^T += K^T F^T a lane's four values of slice q are rows
+        //    4 cg .. + 3 of the product at column rm, A = keys (slot j0 + cg,
+        //    column 16 q + rm), B = F (row rm of the block, slot j0 + cg)
+        if (fl) {  // uniform
+#pragma unroll
+            for (int r = 0; r < NR; ++r) cf[r] *= P;
+            for (int j0 = 0; j0 < h; j0 += 4) {
+                const int jj = j0 + cg;
+                const int jc = jj < h ? jj : 0;
+                const float ej = jj < h ? s.ec[jc] : 0.f;
+                float fx[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) fx[b] = ej * to_f<TR>(s.xc[(16 * (wv * NB + b) + rm) * p.slots + jc]);
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    const float ka = to_f<TR>(s.kc[(int64_t)jc * DK + 16 * q + rm]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        cf[b * NP + q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, fx[b], cf[b * NP + q], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    st_stream(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg,
+                              __builtin_bit_cast(u32x4, cf[b * NP + q]));
+        }
+        __syncthreads();
+        // substitution, one thread per state row; outputs and the drafts'
+        // corrected values (records base .. base + T - 1)
+        if (tid < DV) {
+            const int row = tid;
+            float yv[2 * T];
+#pragma unroll
+            for (int n = 0; n < 2 * T; ++n) yv[n] = s.y[row * YS + n];
+            float ur[T];
+#pragma unroll
+            for (int i = 0; i < T; ++i) {
+                const float D = s.dexp[i], bt = s.betad[i];
+                float u = bt * (s.vd[i * DV + row] - D * yv[T + i]);
+                float o = D * yv[i];
+#pragma unroll
+                for (int m = 0; m < i; ++m) {
+                    const float w = s.wdd[m * T + i];
+                    u -= bt * w * s.kk[(h + m) * T + i] * ur[m];
+                    o += w * s.kq[(h + m) * T + i] * ur[m];
+                }
+                o += s.kq[(h + i) * T + i] * u;  // m = i, weight 1
+                ur[i] = u;
+                st_nt<kNtSmall<kGdn>>(p.out + ((tok0 + i) * p.n_heads + id.head) * DV + row, o);
+                st_nt<kNtSmall<kGdn>>(rx + (int64_t)(base + i) * DV + row, from_f<TR>(u));
+            }
+        }
+        // 7. the drafts' keys (kbase .., the group's first head)
+        if (key_owner) {
+#pragma unroll
+            for (int u = 0; u < QN; ++u) {
+                const int e = (u * NT + tid) * 4;
+                if (e < T * DK) {
+                    const int i = e / DK, c = e - i * DK;
+                    store_f<TR, 4, kNtSmall<kGdn>>(rk + (int64_t)(kbase + i) * DK + c, s.kd + e);
+                }
+            }
+        }
+    } else {
+        // 5. drafts in order: S_h q_i, S_h k_i for the owned rows, then the
+        //    substitution and the output at the lanes that own each row
+        float cf[NR][VEC];
+    #pragma unroll
+        for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+        const float P = s.sc[1];
+        constexpr int left = xsum_left<NV, LPR, 2>();
+        constexpr int NOWN = left / 2;  // rows this lane ends up with
+        const int b0 = xsum_base<NV, LPR, 2>(cc);
+        const bool owner = (cc & xsum_dup_mask<NV, LPR, 2>()) == 0;
+        float ur[T][NOWN];  // corrected values of the owned rows, drafts so far
+    #pragma unroll
+        for (int i = 0; i < T; ++i) {
+            float acc[NV];
+    #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                const float u = to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
-                acc[2 * r] += wq * u;
-                acc[2 * r + 1] += wk * u;
+                float a = 0.f, b = 0.f;
+    #pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+                    a += cf[r][c] * s.qd[i * DK + cc * VEC + c];
+                    b += cf[r][c] * s.kd[i * DK + cc * VEC + c];
+                }
+                acc[2 * r] = P * a;
+                acc[2 * r + 1] = P * b;
+            }
+            for (int j = cc; j < h; j += LPR) {
+                const float wq = s.ec[j] * s.kq[j * T + i], wk = s.ec[j] * s.kk[j * T + i];
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float u = to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
+                    acc[2 * r] += wq * u;
+                    acc[2 * r + 1] += wk * u;
+                }
+            }
+            xsum<NV, LPR / 2, 2>(acc, cc);
+            const float D = s.dexp[i], bt = s.betad[i];
+    #pragma unroll
+            for (int x = 0; x < NOWN; ++x) {
+                const int row = ((b0 + 2 * x) / 2) * RPP + rg;
+                float u = bt * (s.vd[i * DV + row] - D * acc[2 * x + 1]);
+                float o = D * acc[2 * x];
+    #pragma unroll
+                for (int m = 0; m < i; ++m) {
+                    const float w = s.wdd[m * T + i];
+                    u -= bt * w * s.kk[(h + m) * T + i] * ur[m][x];
+                    o += w * s.kq[(h + m) * T + i] * ur[m][x];
+                }
+                o += s.kq[(h + i) * T + i] * u;  // m = i, weight 1
+                ur[i][x] = u;
+                if (owner) st_nt<kNtSmall<kGdn>>(p.out + ((tok0 + i) * p.n_heads + id.head) * DV + row, o);
             }
         }
-        xsum<NV, LPR / 2, 2>(acc, cc);
-        const float D = s.dexp[i], bt = s.betad[i];
-#pragma unroll
-        for (int x = 0; x < NOWN; ++x) {
-            const int row = ((b0 + 2 * x) / 2) * RPP + rg;
-            float u = bt * (s.vd[i * DV + row] - D * acc[2 * x + 1]);
-            float o = D * acc[2 * x];
-#pragma unroll
-            for (int m = 0; m < i; ++m) {
-                const float w = s.wdd[m * T + i];
-                u -= bt * w * s.kk[(h + m) * T + i] * ur[m][x];
-                o += w * s.kq[(h + m) * T + i] * ur[m][x];
-            }
-            o += s.kq[(h + i) * T + i] * u;  // m = i, weight 1
-            ur[i][x] = u;
-            if (owner) st_nt<kNtSmall<kGdn>>(p.out + ((tok0 + i) * p.n_heads + id.head) * DV + row, o);
-        }
-    }
 
-    // 6. flush: fold the committed records (only those), store once
-    if (fl) {  // uniform
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) cf[r][c] *= P;
-        for (int j = 0; j < h; ++j) {
-            float kj[VEC];
-            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
-            const float ej = s.ec[j];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const float f = ej * to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+        // 6. flush: fold the committed records (only those), store once
+        if (fl) {  // uniform
+    #pragma unroll
+            for (int r = 0; r < NR; ++r)
+    #pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] *= P;
+            for (int j = 0; j < h; ++j) {
+                float kj[VEC];
+                load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+                const float ej = s.ec[j];
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float f = ej * to_f<TR>(s.xc[(r * RPP + rg) * p.slots + j]);
+    #pragma unroll
+                    for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+                }
+            }
+            bool stored = false;
+            if constexpr (std::is_same<TS, tF16>::value) {
+                if (p.sr) {
+                    sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
+                    stored = true;
+                }
+            }
+            if (!stored) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
             }
         }
-        bool stored = false;
-        if constexpr (std::is_same<TS, tF16>::value) {
-            if (p.sr) {
-                sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
-                stored = true;
+        // 7. drafts become records base .. base + T - 1: keys (kbase .., the
+        // group's first head), corrected values, log-decays
+        if (key_owner) {
+    #pragma unroll
+            for (int u = 0; u < QN; ++u) {
+                const int e = (u * NT + tid) * 4;
+                if (e < T * DK) {
+                    const int i = e / DK, c = e - i * DK;
+                    store_f<TR, 4, kNtSmall<kGdn>>(rk + (int64_t)(kbase + i) * DK + c, s.kd + e);
+                }
             }
         }
-        if (!stored) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+        if (owner) {
+    #pragma unroll
+            for (int i = 0; i < T; ++i)
+    #pragma unroll
+                for (int x = 0; x < NOWN; ++x)
+                    st_nt<kNtSmall<kGdn>>(rx + (int64_t)(base + i) * DV + ((b0 + 2 * x) / 2) * RPP + rg, from_f<TR>(ur[i][x]));
         }
-    }
-    // 7. drafts become records base .. base + T - 1: keys (kbase .., the
-    // group's first head), corrected values, log-decays
-    if (key_owner) {
-#pragma unroll
-        for (int u = 0; u < QN; ++u) {
-            const int e = (u * NT + tid) * 4;
-            if (e < T * DK) {
-                const int i = e / DK, c = e - i * DK;
-                store_f<TR, 4, kNtSmall<kGdn>>(rk + (int64_t)(kbase + i) * DK + c, s.kd + e);
-            }
-        }
-    }
-    if (owner) {
-#pragma unroll
-        for (int i = 0; i < T; ++i)
-#pragma unroll
-            for (int x = 0; x < NOWN; ++x)
-                st_nt<kNtSmall<kGdn>>(rx + (int64_t)(base + i) * DV + ((b0 + 2 * x) / 2) * RPP + rg, from_f<TR>(ur[i][x]));
     }
     if (tid < T) st_nt<kNtSmall<kGdn>>(rl + base + tid, s.lamd[tid]);
 }
@@ -3051,7 +3203,10 @@ struct Dispatch {
                                             ok = true;
                                             if (!p) return;
                                             hipLaunchKernelGGL((k_spec_verify_gdn<DV, DK, TS, TR, TI, T>), grid<1>(),
-                                                               block, spec_gdn_lds_bytes(L.L, T, DV, DK, rb), stream,
+                                                               block,
+                                                               spec_gdn_lds_bytes(L.L, T, DV, DK, rb,
+                                                                                  spec_gdn_mf(DV, DK, std::is_same<TS, tF32>::value)),
+                                                               stream,
                                                                *p);
                                         }
                                     });
@@ -3234,8 +3389,13 @@ struct Dispatch {
 // Upper bound over the splits (a workgroup owning all d_v rows).
 size_t lds_bytes(Kind kind, const rs_layer& layer) {
     if (kind == Kind::SpecVerify)
-        return (layer.form == RS_GDN ? spec_gdn_lds_bytes : spec_lds_bytes)(layer.L, layer.spec_T, layer.d_v, layer.d_k,
-                                                                           layer.record_dtype == RS_F32 ? 4 : 2);
+    {
+        const int rb = layer.record_dtype == RS_F32 ? 4 : 2;
+        if (layer.form == RS_GDN)
+            return spec_gdn_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, rb,
+                                      spec_gdn_mf(layer.d_v, layer.d_k, layer.state_dtype == RS_F32));
+        return spec_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, rb);
+    }
     if (kind != Kind::ReplayStep && kind != Kind::Flush) return 0;
     const int slots = layer.spec_T > 0 ? layer.L : layer.L - 1;
     const size_t rb = layer.record_dtype == RS_F32 ? 4 : 2;

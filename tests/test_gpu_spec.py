@@ -227,6 +227,38 @@ def test_spec_gdn_T8_64x128():
     _check_gdn(err, TOL_LOW)
 
 
+_GDN_MF = {
+    "T8-strided-pad-forced": dict(T=8, L=16, rec_dt="f16", io_dt="bf16", strided=True, pad_rows=[5],
+                                  force_row0_every=3),
+    "T8-fp32-all": dict(T=8, L=16, rec_dt="f32", io_dt="f32", accept="all"),
+    "T8-fp32-none": dict(T=8, L=16, rec_dt="f32", io_dt="f32", accept="none"),
+    "T1-fp32": dict(T=1, L=8, rec_dt="f32", io_dt="f32"),
+    "T2": dict(T=2, L=8, rec_dt="f16", io_dt="bf16"),
+    "T4-L4": dict(T=4, L=4, rec_dt="f16", io_dt="bf16"),
+    "T8-full-forgetting": dict(T=8, L=16, rec_dt="f16", io_dt="bf16", forget_every=7),
+    "T4-L64-fp32-records": dict(T=4, L=64, rec_dt="f32", io_dt="f32", steps=48),
+    "64x128-T8-fp32": dict(dv=64, T=8, L=16, rec_dt="f32", io_dt="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(_GDN_MF))
+def test_spec_gdn_fp32_state_on_matrix_cores(name):
+    """fp32 state at 128 x 128 (and 64 x 128): the verify's state products
+    S_h [q_1 .. q_T, k_1 .. k_T], the committed records' share of them and the
+    flush fold run as 16 x 16 x 4 fp32 matrix products.  Draft counts 1 to 8
+    (2T = 2 .. 16 of the 16 product columns), flushes every step (L = 4) or
+    with 63 slots of fp32 records (L = 64, more than four 16-record blocks),
+    nothing / everything accepted, lam = -inf drafts, strided inputs, padding
+    and forced flushes; batch 16, 8 heads, 2 rows sampled."""
+    c = dict(dv=128, steps=20, accept="random")
+    c.update(_GDN_MF[name])
+    err = run_spec_case(SpecCase(form=rs.GDN, B=16, H=8, dk=128, state_dt="f32", sample=[0, 15],
+                                 seed=90 + len(name), **c))
+    if c["accept"] != "none":
+        assert err["flushes"] >= 1
+    _check_gdn(err, TOL_F32 if c["rec_dt"] == "f32" and c["io_dt"] == "f32" else TOL_LOW)
+
+
 @pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
 @pytest.mark.parametrize("T", [4, 8])
 def test_spec_full_forgetting(form, T):
