@@ -2054,6 +2054,18 @@ __device__ __forceinline__ void store_read_quad(const float* x, typename TL::S* 
     __builtin_nontemporal_store(w, reinterpret_cast<W*>(dst));
 }
 
+// Whether the speculative verify runs its state products on the matrix
+// cores: an fp32 state whose d_v rows fill four waves' 16-row blocks and
+// whose d_k columns come in 16-column slices, at the draft counts where that
+// measured faster (batch 256: Gated DeltaNet T = 4 and 8, Mamba-2 T = 8; at
+// fewer drafts the T (Mamba-2) or 2T columns fill a fraction of each 16-column
+// product: Mamba-2 at T = 4 and Gated DeltaNet at T = 2 were 7-12 % and 5-10 %
+// slower than the VALU form).
+constexpr bool spec_mf(int form, int dv, int dk, bool f32_state, int T) {
+    return f32_state && dv % 64 == 0 && dk % 16 == 0 && (size_t)dv * dk / 4 / 4 >= 256 &&
+           (form == kGdn ? T >= 4 : T == 8);
+}
+
 // TL != TS: a two-precision checkpoint (fp32 recurrence copy TS, read copy
 // TL; blog "The precision argument, derived").  A row that does not flush
 // reads only the read copy for its outputs; a flushing row reads the
@@ -2074,6 +2086,7 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     static_assert(!TWO || std::is_same<TS, tF32>::value, "a read copy under an fp32 recurrence copy");
     constexpr int NT = Tl::NT, VEC = Tl::VEC, LPR = Tl::LPR, RPP = Tl::RPP, NR = Tl::NR;
     constexpr int NV = T * NR;                        // partial sums per lane: (draft, owned row)
+    constexpr bool MF = !TWO && spec_mf(kMamba2, DV, DK, std::is_same<TS, tF32>::value, T);
     constexpr int QN = (T * DK / 4 + NT - 1) / NT;    // 4-element pieces of draft q / k per thread
     constexpr int VN = (T * DV + NT - 1) / NT;        // draft v elements per thread
     constexpr int KCH = DK * (int)sizeof(R) / 16, XCH = DV * (int)sizeof(R) / 16, XE = 16 / (int)sizeof(R);
@@ -2163,7 +2176,19 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     u32x4 cb[NR];
     Quad<TL> lq[NR];  // two-precision, a row that does not flush: the read copy instead
     float lsc[NR];
-    if (!TWO || fl) {  // uniform
+    // Matrix-core form: the load layout of k_spec_verify_gdn's (wave wv, its
+    // 16-row blocks b, lane (rm, cg): row 16 (wv NB + b) + rm, columns
+    // 16 q + 4 cg .. + 3), the A operand of the 16 x 16 x 4 fp32 product
+    constexpr int NB = DV / 64, NP = DK / 16;
+    [[maybe_unused]] const int wv = tid >> 6, rm = tid & 15, cg = (tid >> 4) & 3;
+    if constexpr (MF) {
+        static_assert(NB * NP == NR && NT == 256, "four waves of 16-row blocks");
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+                cb[b * NP + q] = *reinterpret_cast<const u32x4*>(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg);
+    } else if (!TWO || fl) {  // uniform
 #pragma unroll
         for (int r = 0; r < NR; ++r) cb[r] = ld_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC);
     } else {
@@ -2272,88 +2297,161 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
     }
     __syncthreads();
 
-    // 4. outputs (each query scaled by its checkpoint weight first: T * VEC
-    // multiplies instead of T * NR)
-    float cf[NR][VEC];
-    if (!TWO || fl) {
+    if constexpr (MF) {
+        using f4 = __attribute__((ext_vector_type(4))) float;
+        f4 cf[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+        for (int r = 0; r < NR; ++r) cf[r] = __builtin_bit_cast(f4, cb[r]);
+        // 4. O = C Qg + X Wq on the matrix cores: Qg = [g_1 q_1 .. g_T q_T]
+        //    (d_k x T, zero beyond), X the committed values then the drafts'
+        //    (x_j at row, column j), Wq the weighted key products; lane (rm,
+        //    cg) ends with rows 4 cg .. + 3 of each block for draft n = rm
+        const float* wsrc = s.qd + min(rm, T - 1) * DK + 4 * cg;
+        const float wsc = rm < T ? s.gck[min(rm, T - 1)] : 0.f;
+        f4 y[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) y[b] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const f4 w = *reinterpret_cast<const f4*>(wsrc + 16 * q) * wsc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[b * NP + q][e], w[e], y[b], 0, 0, 0);
+        }
+        // committed records then drafts, four at a time; a slot past them
+        // takes slot 0's (finite) value with weight zero
+        for (int j0 = 0; j0 < nkeys; j0 += 4) {
+            const int jj = j0 + cg;
+            const int jc = jj < nkeys ? jj : 0;
+            const float g = jj < nkeys && rm < T ? s.wq[jc * T + min(rm, T - 1)] : 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int row = 16 * (wv * NB + b) + rm;
+                const float xa = jc < h ? to_f<TR>(s.xc[(int64_t)(jc < h ? jc : 0) * DV + row]) : s.vd[max(jc - h, 0) * DV + row];
+                y[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, g, y[b], 0, 0, 0);
+            }
+        }
+        if (rm < T) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                __builtin_nontemporal_store(
+                    y[b], reinterpret_cast<f4*>(p.out + ((tok0 + rm) * p.n_heads + id.head) * DV + 16 * (wv * NB + b) + 4 * cg));
+        }
+        // 5. flush: C = G C + sum_j e_j x_j k_j^T on the matrix cores, in
+        //    place (as C^T += K^T F^T: keys as A, F = e_j x_j as B; the
+        //    product's rows 4 cg .. + 3 at column rm are the lane's four
+        //    values of slice q), stored from where it was loaded
+        if (fl) {  // uniform
+            const float G = s.sc[1];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) cf[r] *= G;
+            for (int j0 = 0; j0 < h; j0 += 4) {
+                const int jj = j0 + cg;
+                const int jc = jj < h ? jj : 0;
+                const float ej = jj < h ? s.ec[jc] : 0.f;
+                float fx[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) fx[b] = ej * to_f<TR>(s.xc[(int64_t)jc * DV + 16 * (wv * NB + b) + rm]);
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    const float ka = to_f<TR>(s.kc[(int64_t)jc * DK + 16 * q + rm]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        cf[b * NP + q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, fx[b], cf[b * NP + q], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    st_stream(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg,
+                              __builtin_bit_cast(u32x4, cf[b * NP + q]));
+        }
     } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) lq[r].to(cf[r], lsc[r]);
-    }
-    float acc[NV];
-#pragma unroll
-    for (int i = 0; i < T; ++i) {
-        const float g = s.gck[i ^ mq];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) qv[i][c] *= g;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            float a = 0.f;
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) a += cf[r][c] * qv[i][c];
-            acc[i * NR + r] = a;
+        // 4. outputs (each query scaled by its checkpoint weight first: T * VEC
+        // multiplies instead of T * NR)
+        float cf[NR][VEC];
+        if (!TWO || fl) {
+    #pragma unroll
+            for (int r = 0; r < NR; ++r) unpack16<TS>(cb[r], cf[r]);
+        } else {
+    #pragma unroll
+            for (int r = 0; r < NR; ++r) lq[r].to(cf[r], lsc[r]);
         }
-    }
-    for (int j = cc; j < nkeys; j += LPR) {
-        float xj[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-            xj[r] = j < h ? to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]) : s.vd[(j - h) * DV + r * RPP + rg];
-#pragma unroll
+        float acc[NV];
+    #pragma unroll
         for (int i = 0; i < T; ++i) {
-            const float wg = s.wq[j * T + (i ^ mq)];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) acc[i * NR + r] += wg * xj[r];
-        }
-    }
-    xsum_perm<NV, LPR / 2, PL>(acc, cc);
-    {
-        constexpr int left = xsum_left<NV, LPR, 1>();
-        if ((cc & xsum_dup_mask<NV, LPR, 1>()) == 0) {
-            const int b0 = xsum_perm_base<NV, LPR, T>(cc);
-#pragma unroll
-            for (int k = 0; k < left; ++k) {
-                const int v = b0 + k, i = v / NR, r = v - i * NR;
-                st_nt(p.out + ((tok0 + i) * p.n_heads + id.head) * DV + r * RPP + rg, acc[k]);
-            }
-        }
-    }
-
-    // 5. flush: fold the committed records (only those), store once
-    if (fl) {  // uniform
-        const float G = s.sc[1];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) cf[r][c] *= G;
-        for (int j = 0; j < h; ++j) {
-            float kj[VEC];
-            load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
-            const float ej = s.ec[j];
-#pragma unroll
+            const float g = s.gck[i ^ mq];
+    #pragma unroll
+            for (int c = 0; c < VEC; ++c) qv[i][c] *= g;
+    #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                const float f = ej * to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]);
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+                float a = 0.f;
+    #pragma unroll
+                for (int c = 0; c < VEC; ++c) a += cf[r][c] * qv[i][c];
+                acc[i * NR + r] = a;
             }
         }
-        bool stored = false;
-        if constexpr (std::is_same<TS, tF16>::value) {
-            if (p.sr) {
-                sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
-                stored = true;
-            }
-        }
-        if (!stored) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
-        }
-        if constexpr (TWO) {
-#pragma unroll
+        for (int j = cc; j < nkeys; j += LPR) {
+            float xj[NR];
+    #pragma unroll
             for (int r = 0; r < NR; ++r)
-                store_read_quad<TL, LPR>(cf[r], cl + (int64_t)(r * RPP + rg) * DK + lpos, cs + r * RPP + rg, cc);
+                xj[r] = j < h ? to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]) : s.vd[(j - h) * DV + r * RPP + rg];
+    #pragma unroll
+            for (int i = 0; i < T; ++i) {
+                const float wg = s.wq[j * T + (i ^ mq)];
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) acc[i * NR + r] += wg * xj[r];
+            }
+        }
+        xsum_perm<NV, LPR / 2, PL>(acc, cc);
+        {
+            constexpr int left = xsum_left<NV, LPR, 1>();
+            if ((cc & xsum_dup_mask<NV, LPR, 1>()) == 0) {
+                const int b0 = xsum_perm_base<NV, LPR, T>(cc);
+    #pragma unroll
+                for (int k = 0; k < left; ++k) {
+                    const int v = b0 + k, i = v / NR, r = v - i * NR;
+                    st_nt(p.out + ((tok0 + i) * p.n_heads + id.head) * DV + r * RPP + rg, acc[k]);
+                }
+            }
+        }
+
+        // 5. flush: fold the committed records (only those), store once
+        if (fl) {  // uniform
+            const float G = s.sc[1];
+    #pragma unroll
+            for (int r = 0; r < NR; ++r)
+    #pragma unroll
+                for (int c = 0; c < VEC; ++c) cf[r][c] *= G;
+            for (int j = 0; j < h; ++j) {
+                float kj[VEC];
+                load_f<TR, VEC>(s.kc + (int64_t)j * DK + cc * VEC, kj);
+                const float ej = s.ec[j];
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float f = ej * to_f<TR>(s.xc[(int64_t)j * DV + r * RPP + rg]);
+    #pragma unroll
+                    for (int c = 0; c < VEC; ++c) cf[r][c] += f * kj[c];
+                }
+            }
+            bool stored = false;
+            if constexpr (std::is_same<TS, tF16>::value) {
+                if (p.sr) {
+                    sr_store_rows<NR, 1, LPR>(cf, ck + (int64_t)rg * DK + cc * VEC, p, id.tile, rg, RPP, DK, cc * VEC);
+                    stored = true;
+                }
+            }
+            if (!stored) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r) st_stream(ck + (int64_t)(r * RPP + rg) * DK + cc * VEC, pack16<TS>(cf[r]));
+            }
+            if constexpr (TWO) {
+    #pragma unroll
+                for (int r = 0; r < NR; ++r)
+                    store_read_quad<TL, LPR>(cf[r], cl + (int64_t)(r * RPP + rg) * DK + lpos, cs + r * RPP + rg, cc);
+            }
         }
     }
     // drafts become records base .. base + T - 1 (keys: kbase .., the group's first head)
@@ -2436,7 +2534,7 @@ __device__ __forceinline__ SpecGdnLds<R> spec_gdn_carve(char* smem, int slots, i
     return s;
 }
 
-// The matrix-core form (spec_gdn_mf) adds the y rows and up to 12 bytes of
+// The matrix-core form (spec_mf) adds the y rows and up to 12 bytes of
 // alignment before them.
 size_t spec_gdn_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes, bool mf) {
     return (size_t)slots * (dk + dv) * rec_bytes +
@@ -2445,17 +2543,11 @@ size_t spec_gdn_lds_bytes(int slots, int T, int dv, int dk, int rec_bytes, bool 
            (mf ? 12 + sizeof(float) * (size_t)dv * spec_y_stride(T) : 0);
 }
 
-// Whether the Gated DeltaNet verify of this shape runs its state products on
-// the matrix cores: an fp32 state whose d_v rows fill four waves' 16-row
-// blocks and whose d_k columns come in 16-column slices.
-constexpr bool spec_gdn_mf(int dv, int dk, bool f32_state) {
-    return f32_state && dv % 64 == 0 && dk % 16 == 0 && (size_t)dv * dk / 4 / 4 >= 256;
-}
 
 template <int DV, int DK, class TS, class TR, class TI, int T>
 __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify_gdn(const StepParams p) {
     using Tl = Tile<DV, DK, TS, 1>;
-    constexpr bool MF = spec_gdn_mf(DV, DK, std::is_same<TS, tF32>::value);
+    constexpr bool MF = spec_mf(kGdn, DV, DK, std::is_same<TS, tF32>::value, T);
     using S = typename TS::S;
     using R = typename TR::S;
     using I = typename TI::S;
@@ -3205,7 +3297,7 @@ struct Dispatch {
                                             hipLaunchKernelGGL((k_spec_verify_gdn<DV, DK, TS, TR, TI, T>), grid<1>(),
                                                                block,
                                                                spec_gdn_lds_bytes(L.L, T, DV, DK, rb,
-                                                                                  spec_gdn_mf(DV, DK, std::is_same<TS, tF32>::value)),
+                                                                                  spec_mf(kGdn, DV, DK, std::is_same<TS, tF32>::value, T)),
                                                                stream,
                                                                *p);
                                         }
@@ -3393,7 +3485,7 @@ size_t lds_bytes(Kind kind, const rs_layer& layer) {
         const int rb = layer.record_dtype == RS_F32 ? 4 : 2;
         if (layer.form == RS_GDN)
             return spec_gdn_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, rb,
-                                      spec_gdn_mf(layer.d_v, layer.d_k, layer.state_dtype == RS_F32));
+                                      spec_mf(kGdn, layer.d_v, layer.d_k, layer.state_dtype == RS_F32, layer.spec_T));
         return spec_lds_bytes(layer.L, layer.spec_T, layer.d_v, layer.d_k, rb);
     }
     if (kind != Kind::ReplayStep && kind != Kind::Flush) return 0;

@@ -243,10 +243,10 @@ _GDN_MF = {
 
 @pytest.mark.parametrize("name", list(_GDN_MF))
 def test_spec_gdn_fp32_state_on_matrix_cores(name):
-    """fp32 state at 128 x 128 (and 64 x 128): the verify's state products
-    S_h [q_1 .. q_T, k_1 .. k_T], the committed records' share of them and the
-    flush fold run as 16 x 16 x 4 fp32 matrix products.  Draft counts 1 to 8
-    (2T = 2 .. 16 of the 16 product columns), flushes every step (L = 4) or
+    """fp32 state at 128 x 128 (and 64 x 128): at T = 4 and 8 the verify's
+    state products S_h [q_1 .. q_T, k_1 .. k_T], the committed records' share
+    of them and the flush fold run as 16 x 16 x 4 fp32 matrix products (T = 1
+    and 2 take the VALU form), flushes every step (L = 4) or
     with 63 slots of fp32 records (L = 64, more than four 16-record blocks),
     nothing / everything accepted, lam = -inf drafts, strided inputs, padding
     and forced flushes; batch 16, 8 heads, 2 rows sampled."""
@@ -257,6 +257,36 @@ def test_spec_gdn_fp32_state_on_matrix_cores(name):
     if c["accept"] != "none":
         assert err["flushes"] >= 1
     _check_gdn(err, TOL_F32 if c["rec_dt"] == "f32" and c["io_dt"] == "f32" else TOL_LOW)
+
+
+_M2_MF = {
+    "strided-pad-forced": dict(rec_dt="f16", io_dt="bf16", strided=True, pad_rows=[5], force_row0_every=3),
+    "fp32-all": dict(rec_dt="f32", io_dt="f32", accept="all"),
+    "fp32-none": dict(rec_dt="f32", io_dt="f32", accept="none"),
+    "full-forgetting": dict(rec_dt="f16", io_dt="bf16", forget_every=7, steps=24),
+    "L8-every-step": dict(rec_dt="f32", io_dt="f32", L=8),
+    "L64-fp32-records": dict(rec_dt="f32", io_dt="f32", L=64, steps=24, accept="all"),
+    "128x128": dict(dv=128, rec_dt="f16", io_dt="bf16"),
+    "grouped-2": dict(rec_dt="f16", io_dt="bf16", groups=2, H=8, strided=True, pad_rows=[3]),
+}
+
+
+@pytest.mark.parametrize("name", list(_M2_MF))
+def test_spec_mamba2_fp32_state_on_matrix_cores(name):
+    """Mamba-2 verify at T = 8 over an fp32 state: C [g_1 q_1 .. g_8 q_8], the
+    committed and draft values' share (X Wq) and the flush fold run as
+    16 x 16 x 4 fp32 matrix products, the outputs stored from the product
+    registers.  Strided / padded / forced-flush rows, everything or nothing
+    accepted, lam = -inf drafts, a flush every step (L = 8), 63 slots of fp32
+    records, 128 x 128 heads, keys shared by pairs of heads; batch 16, 2 rows
+    sampled."""
+    c = dict(dv=64, H=8, L=16, steps=20, accept="random")
+    c.update(_M2_MF[name])
+    err = run_spec_case(SpecCase(form=rs.MAMBA2, B=16, dk=128, T=8, state_dt="f32", sample=[0, 15],
+                                 seed=120 + len(name), **c))
+    if c["accept"] != "none":
+        assert err["flushes"] >= 1
+    _check(err, TOL_F32 if c["rec_dt"] == "f32" and c["io_dt"] == "f32" else TOL_LOW)
 
 
 @pytest.mark.parametrize("form", [rs.MAMBA2, rs.GDN])
