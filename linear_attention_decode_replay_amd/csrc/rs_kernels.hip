@@ -2361,12 +2361,14 @@ __global__ __launch_bounds__((Tile<DV, DK, TS, 1>::NT)) void k_spec_verify(const
                         cf[b * NP + q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, fx[b], cf[b * NP + q], 0, 0, 0);
                 }
             }
+            // plain stores (the two halves of a 128-byte line come from two
+            // stores): 0-3 % faster per step than non-temporal ones here
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int q = 0; q < NP; ++q)
-                    st_stream(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg,
-                              __builtin_bit_cast(u32x4, cf[b * NP + q]));
+                    *reinterpret_cast<u32x4*>(ck + (int64_t)(16 * (wv * NB + b) + rm) * DK + 16 * q + 4 * cg) =
+                        __builtin_bit_cast(u32x4, cf[b * NP + q]);
         }
     } else {
         // 4. outputs (each query scaled by its checkpoint weight first: T * VEC
